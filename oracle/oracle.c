@@ -1,0 +1,311 @@
+/*
+ * CPU reference ("oracle") for the paged KV-cache varlen attention path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or
+ * calls this file; only the test suite, the smoke entry point and the CPU
+ * baseline leg of the benchmark do.  It shares no source, header or helper
+ * with the HIP path.
+ *
+ * Plain, slow, obviously correct: loops in the order the definitions state
+ * them, floating point in fp64.  bf16 inputs are widened exactly (the 16 bits
+ * become the top half of an IEEE binary32, which converts exactly to binary64).
+ *
+ * Sources (the pages this build follows):
+ *  - "Inside vLLM ... Part 3 Runtime", Aside "KV cache and prefix caching"
+ *    (supercharleszhu.github.io): a forward writes each new token's K/V into
+ *    the physical slot block_id*block_size + offset given by slot_mapping, and
+ *    reads K/V back per request through its block_table; a prefill query
+ *    attends causally over cached prefix + new tokens, a decode query over all
+ *    of its blocks, one launch for the whole batch.
+ *  - Same page, "Step 4c - Mixed batches": query_start_loc is the prefix sum
+ *    of per-request scheduled token counts.
+ *  - "vLLM internals study" (anthony-chaudhary.github.io) section 2.1
+ *    "PagedAttention & the block manager" (block table maps logical block
+ *    index to physical block id; write slot = block number * block_size +
+ *    offset) and section 2.4 "Attention kernels & backends" (query heads that
+ *    share one KV head are processed together).
+ *
+ * Readings taken where the pages are silent (each listed in the design notes):
+ *  - attention is softmax(scale * q.k^T) v, the scale a caller argument;
+ *  - seq_lens counts cached + new tokens, and the new tokens are the last
+ *    Q_b positions, so query i of a Q_b-token chunk sits at p = L_b - Q_b + i
+ *    and sees keys 0..p (bottom-right causal alignment);
+ *  - query head h reads KV head floor(h / (Hq/Hkv));
+ *  - slot_mapping entries < 0 are skipped;
+ *  - the pool layout is the one documented with the C ABI (see k_index and
+ *    v_index below: 16-token blocks, per (block, kv head) one K tile and one
+ *    V tile of 16*D bf16 each, permuted inside the tile).
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#include "oracle.h"
+
+/* ---- bf16 <-> fp64 (exact widening) ---------------------------------- */
+
+static double bf16_to_double(uint16_t bits) {
+  uint32_t u = ((uint32_t)bits) << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* ---- pool layout (as documented with the C ABI) ----------------------- */
+
+/* Element offset of K (block n, kv head g, token slot t, dim d).
+ * Tile (n, g) starts at (n*Hkv + g) * bs * D; inside it K is stored as
+ * D/8 chunks of [bs tokens][8 dims]. */
+static size_t k_index(int64_t n, int64_t g, int64_t t, int64_t d, int64_t Hkv,
+                      int64_t bs, int64_t D) {
+  size_t tile = (size_t)((n * Hkv + g) * bs * D);
+  size_t chunk = (size_t)(d / 8);
+  return tile + (chunk * (size_t)bs + (size_t)t) * 8 + (size_t)(d % 8);
+}
+
+/* Element offset of V (block n, kv head g, token slot t, dim d).
+ * Inside a tile, with H = D/2: dim d pairs with dim d+H, tokens come in groups
+ * of 4; order is [d mod H][t / 4][d / H][t mod 4]. */
+static size_t v_index(int64_t n, int64_t g, int64_t t, int64_t d, int64_t Hkv,
+                      int64_t bs, int64_t D) {
+  size_t tile = (size_t)((n * Hkv + g) * bs * D);
+  int64_t H = D / 2;
+  int64_t dl = d % H, dh = d / H;
+  int64_t tg = t / 4, tl = t % 4;
+  return tile + (size_t)((((dl * (bs / 4) + tg) * 2 + dh) * 4) + tl);
+}
+
+size_t oracle_k_index(int64_t n, int64_t g, int64_t t, int64_t d, int64_t Hkv,
+                      int64_t bs, int64_t D) {
+  return k_index(n, g, t, d, Hkv, bs, D);
+}
+
+size_t oracle_v_index(int64_t n, int64_t g, int64_t t, int64_t d, int64_t Hkv,
+                      int64_t bs, int64_t D) {
+  return v_index(n, g, t, d, Hkv, bs, D);
+}
+
+/* ---- KV scatter (reshape-and-cache) ---------------------------------- */
+
+/* For each new token t with slot s = slot_mapping[t] >= 0: block s / bs,
+ * offset s % bs; copy the bits of k[t][g][d], v[t][g][d] there.  Every other
+ * pool element is left as it was. */
+void oracle_write_kv(uint16_t *k_cache, uint16_t *v_cache, const uint16_t *k,
+                     const uint16_t *v, const int64_t *slot_mapping,
+                     int64_t num_tokens, int64_t Hkv, int64_t bs, int64_t D) {
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    int64_t s = slot_mapping[t];
+    if (s < 0) continue;
+    int64_t n = s / bs, off = s % bs;
+    for (int64_t g = 0; g < Hkv; ++g) {
+      for (int64_t d = 0; d < D; ++d) {
+        size_t src = (size_t)((t * Hkv + g) * D + d);
+        k_cache[k_index(n, g, off, d, Hkv, bs, D)] = k[src];
+        v_cache[v_index(n, g, off, d, Hkv, bs, D)] = v[src];
+      }
+    }
+  }
+}
+
+/* ---- logical gather through the block tables -------------------------- */
+
+/* Dense [sum L_b][Hkv][D]: row (start_b + j) holds logical token j of
+ * sequence b, read from block block_tables[b][j / bs] at offset j % bs. */
+void oracle_gather_kv(const uint16_t *k_cache, const uint16_t *v_cache,
+                      const int32_t *block_tables, int64_t bt_stride,
+                      const int32_t *seq_lens, int64_t num_seqs, int64_t Hkv,
+                      int64_t bs, int64_t D, uint16_t *k_out, uint16_t *v_out) {
+  int64_t row = 0;
+  for (int64_t b = 0; b < num_seqs; ++b) {
+    for (int64_t j = 0; j < seq_lens[b]; ++j, ++row) {
+      int64_t n = block_tables[b * bt_stride + j / bs];
+      for (int64_t g = 0; g < Hkv; ++g) {
+        for (int64_t d = 0; d < D; ++d) {
+          size_t dst = (size_t)((row * Hkv + g) * D + d);
+          k_out[dst] = k_cache[k_index(n, g, j % bs, d, Hkv, bs, D)];
+          v_out[dst] = v_cache[v_index(n, g, j % bs, d, Hkv, bs, D)];
+        }
+      }
+    }
+  }
+}
+
+/* ---- attention ---------------------------------------------------------- */
+
+/* Softmax-weighted sum over keys 0..p of one (query row, head), given the
+ * scores s[0..p] already computed; v_at(j, d) supplies V.  Shared by the paged
+ * and the dense form: the two differ only in how K and V are addressed. */
+typedef double (*v_fetch_fn)(const void *ctx, int64_t j, int64_t d);
+
+static void softmax_weighted_sum(const double *s, int64_t p, v_fetch_fn v_at,
+                                 const void *ctx, int64_t D, double *out) {
+  double m = s[0];
+  for (int64_t j = 1; j <= p; ++j)
+    if (s[j] > m) m = s[j];
+  double denom = 0.0;
+  for (int64_t d = 0; d < D; ++d) out[d] = 0.0;
+  for (int64_t j = 0; j <= p; ++j) {
+    double w = exp(s[j] - m);
+    denom += w;
+    for (int64_t d = 0; d < D; ++d) out[d] += w * v_at(ctx, j, d);
+  }
+  for (int64_t d = 0; d < D; ++d) out[d] /= denom;
+}
+
+typedef struct {
+  const uint16_t *k_cache, *v_cache;
+  const int32_t *bt_row;
+  int64_t g, Hkv, bs, D;
+} paged_ctx;
+
+static double paged_k(const paged_ctx *c, int64_t j, int64_t d) {
+  int64_t n = c->bt_row[j / c->bs];
+  return bf16_to_double(
+      c->k_cache[k_index(n, c->g, j % c->bs, d, c->Hkv, c->bs, c->D)]);
+}
+
+static double paged_v(const void *ctx, int64_t j, int64_t d) {
+  const paged_ctx *c = (const paged_ctx *)ctx;
+  int64_t n = c->bt_row[j / c->bs];
+  return bf16_to_double(
+      c->v_cache[v_index(n, c->g, j % c->bs, d, c->Hkv, c->bs, c->D)]);
+}
+
+/* One output row: query token t (global index) of sequence b, query head h. */
+static void paged_row(const uint16_t *q, const uint16_t *k_cache,
+                      const uint16_t *v_cache, const int32_t *block_tables,
+                      int64_t bt_stride, const int32_t *seq_lens,
+                      const int32_t *query_start_loc, int64_t b, int64_t t,
+                      int64_t h, int64_t Hq, int64_t Hkv, int64_t bs, int64_t D,
+                      double sigma, double *scores, double *out) {
+  int64_t L = seq_lens[b];
+  int64_t Q = query_start_loc[b + 1] - query_start_loc[b];
+  int64_t i = t - query_start_loc[b];
+  int64_t p = L - Q + i; /* position of this query; it sees keys 0..p */
+  paged_ctx c = {k_cache, v_cache, block_tables + b * bt_stride,
+                 h / (Hq / Hkv), Hkv, bs, D};
+  const uint16_t *qrow = q + (size_t)((t * Hq + h) * D);
+  for (int64_t j = 0; j <= p; ++j) {
+    double dot = 0.0;
+    for (int64_t d = 0; d < D; ++d)
+      dot += bf16_to_double(qrow[d]) * paged_k(&c, j, d);
+    scores[j] = sigma * dot;
+  }
+  softmax_weighted_sum(scores, p, paged_v, &c, D, out);
+}
+
+/* Sequence that owns global query token t (query_start_loc is
+ * non-decreasing). */
+static int64_t seq_of_token(const int32_t *query_start_loc, int64_t num_seqs,
+                            int64_t t) {
+  for (int64_t b = 0; b < num_seqs; ++b)
+    if (t < query_start_loc[b + 1]) return b;
+  return -1;
+}
+
+/* out[t][h][d] (fp64) for every query token of every sequence. */
+void oracle_attend(const uint16_t *q, const uint16_t *k_cache,
+                   const uint16_t *v_cache, const int32_t *block_tables,
+                   int64_t bt_stride, const int32_t *seq_lens,
+                   const int32_t *query_start_loc, int64_t num_seqs,
+                   int64_t Hq, int64_t Hkv, int64_t bs, int64_t D, float scale,
+                   int64_t max_seq_len, double *scratch, double *out,
+                   int nthreads) {
+  int64_t T = query_start_loc[num_seqs];
+  double sigma = (double)scale;
+  (void)nthreads;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+  for (int64_t r = 0; r < T * Hq; ++r) {
+    int64_t t = r / Hq, h = r % Hq;
+    int tid = 0;
+#ifdef _OPENMP
+    tid = omp_get_thread_num();
+#endif
+    int64_t b = seq_of_token(query_start_loc, num_seqs, t);
+    paged_row(q, k_cache, v_cache, block_tables, bt_stride, seq_lens,
+              query_start_loc, b, t, h, Hq, Hkv, bs, D, sigma,
+              scratch + (size_t)tid * (size_t)max_seq_len,
+              out + (size_t)((t * Hq + h) * D));
+  }
+}
+
+/* Selected rows only: rows[2r] = query token t, rows[2r+1] = query head h;
+ * out_rows[r][d]. */
+void oracle_attend_rows(const uint16_t *q, const uint16_t *k_cache,
+                        const uint16_t *v_cache, const int32_t *block_tables,
+                        int64_t bt_stride, const int32_t *seq_lens,
+                        const int32_t *query_start_loc, int64_t num_seqs,
+                        int64_t Hq, int64_t Hkv, int64_t bs, int64_t D,
+                        float scale, int64_t max_seq_len, const int64_t *rows,
+                        int64_t num_rows, double *scratch, double *out_rows,
+                        int nthreads) {
+  double sigma = (double)scale;
+  (void)nthreads;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+  for (int64_t r = 0; r < num_rows; ++r) {
+    int tid = 0;
+#ifdef _OPENMP
+    tid = omp_get_thread_num();
+#endif
+    int64_t t = rows[2 * r], h = rows[2 * r + 1];
+    int64_t b = seq_of_token(query_start_loc, num_seqs, t);
+    paged_row(q, k_cache, v_cache, block_tables, bt_stride, seq_lens,
+              query_start_loc, b, t, h, Hq, Hkv, bs, D, sigma,
+              scratch + (size_t)tid * (size_t)max_seq_len,
+              out_rows + (size_t)(r * D));
+  }
+}
+
+/* Dense form: K/V of sequence b are rows kv_start_b .. kv_start_b + L_b - 1
+ * of contiguous [sum L][Hkv][D] arrays (kv_start = prefix sum of seq_lens).
+ * No block tables; same scores and softmax. */
+typedef struct {
+  const uint16_t *v_dense;
+  int64_t row0, g, Hkv, D;
+} dense_ctx;
+
+static double dense_v(const void *ctx, int64_t j, int64_t d) {
+  const dense_ctx *c = (const dense_ctx *)ctx;
+  return bf16_to_double(c->v_dense[(size_t)(((c->row0 + j) * c->Hkv + c->g) *
+                                                c->D + d)]);
+}
+
+void oracle_attend_dense(const uint16_t *q, const uint16_t *k_dense,
+                         const uint16_t *v_dense, const int32_t *seq_lens,
+                         const int32_t *query_start_loc, int64_t num_seqs,
+                         int64_t Hq, int64_t Hkv, int64_t D, float scale,
+                         int64_t max_seq_len, double *scratch, double *out) {
+  double sigma = (double)scale;
+  int64_t row0 = 0;
+  for (int64_t b = 0; b < num_seqs; ++b) {
+    int64_t L = seq_lens[b];
+    int64_t Q = query_start_loc[b + 1] - query_start_loc[b];
+    for (int64_t i = 0; i < Q; ++i) {
+      int64_t t = query_start_loc[b] + i;
+      int64_t p = L - Q + i;
+      for (int64_t h = 0; h < Hq; ++h) {
+        int64_t g = h / (Hq / Hkv);
+        const uint16_t *qrow = q + (size_t)((t * Hq + h) * D);
+        for (int64_t j = 0; j <= p; ++j) {
+          double dot = 0.0;
+          for (int64_t d = 0; d < D; ++d)
+            dot += bf16_to_double(qrow[d]) *
+                   bf16_to_double(
+                       k_dense[(size_t)(((row0 + j) * Hkv + g) * D + d)]);
+          scratch[j] = sigma * dot;
+        }
+        dense_ctx c = {v_dense, row0, g, Hkv, D};
+        softmax_weighted_sum(scratch, p, dense_v, &c, D,
+                             out + (size_t)((t * Hq + h) * D));
+      }
+    }
+    row0 += L;
+  }
+  (void)max_seq_len;
+}
+
+int oracle_abi_version(void) { return 1; }
