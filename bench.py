@@ -1,0 +1,212 @@
+#!/usr/bin/env python3
+"""Benchmark of one paged-attention layer step on one MI355X.
+
+A step is the whole hot path for one layer over one batch: pa_write_kv of
+the step's new K/V rows, then pa_attend (work plan, unified varlen paged
+attention, split-K merge) over every query row.  Inputs are seeded synthetic
+tensors already resident in HBM.  Several copies of the KV pool (one per
+simulated layer, >= 2 GiB in total) are cycled so that no step reads K/V left
+in the caches by the previous one.
+
+Prints one JSON line:
+  value    paged-attention KV read GB/s of the headline workload (Llama-3-8B
+           decode layer: 64 sequences, contexts U[128, 4096], 32 q / 8 kv
+           heads, head_dim 128, 16-token blocks) = valid-token K+V bytes per
+           step / step time;
+  roofline the attention kernel against the 8 TB/s HBM peak, its duration
+           from HIP events on the launch stream;
+  mixed_step  mixed chunked-prefill step (1920-token chunk on 1536 cached
+           tokens + 128 decodes): tokens/s per layer;
+  cpu_baseline  the CPU oracle (fp64) on the same headline workload.
+
+    python bench.py [--steps K] [--warmup W] [--config 2] [--no-mixed]
+                    [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--no-mixed", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--min-working-set-gib", type=float, default=2.0)
+    return ap.parse_args()
+
+
+def algorithmic(w):
+    """Bytes and flops one attention launch needs at minimum."""
+    L = w.seq_lens.astype(np.int64)
+    Q = w.query_lens.astype(np.int64)
+    kv = int(L.sum()) * 2 * w.num_kv_heads * w.head_dim * 2
+    qo = 2 * w.num_q_tokens * w.num_q_heads * w.head_dim * 2
+    tables = int(((L + 15) // 16).sum()) * 4
+    meta = w.num_seqs * 4 + (w.num_seqs + 1) * 4
+    # visible (query, key) pairs per head: query i of a chunk sees L-Q+i+1 keys
+    pairs = int((Q * (L - Q) + Q * (Q + 1) // 2).sum())
+    flops = 4 * w.head_dim * w.num_q_heads * pairs
+    write = 2 * 2 * w.num_q_tokens * w.num_kv_heads * w.head_dim * 2  # read + write
+    return {"kv_bytes": kv, "attend_bytes": kv + qo + tables + meta,
+            "write_bytes": write, "flops": flops, "pairs_per_head": pairs}
+
+
+class Runner:
+    """Pools for several simulated layers plus the step's inputs, on the GPU."""
+
+    def __init__(self, w, min_ws_gib):
+        import torch
+        import paged_kv_cache_varlen_amd as pa
+        from tests.gpu_util import Uploaded
+        self.torch, self.pa, self.w = torch, pa, w
+        base = Uploaded(w, sentinel=False)
+        pool_bytes = 2 * base.k_cache.numel() * 2
+        n = max(1, min(8, int(np.ceil(min_ws_gib * 2**30 / pool_bytes))))
+        self.layers = [(base.k_cache, base.v_cache)]
+        for _ in range(n - 1):
+            self.layers.append((base.k_cache.clone(), base.v_cache.clone()))
+        self.u = base
+        self.stream = torch.cuda.current_stream()
+
+    def step(self, i, ev=None):
+        pa, u, w = self.pa, self.u, self.w
+        kc, vc = self.layers[i % len(self.layers)]
+        pa.write_kv(u.k_new, u.v_new, u.new_slots, kc, vc)
+        if ev is not None:
+            ev[0].record(self.stream)
+        pa.attend(u.q, kc, vc, u.block_tables, u.seq_lens, u.qsl, w.scale,
+                  w.max_query_len, w.max_seq_len, num_kv_heads=w.num_kv_heads,
+                  out=u.out, workspace=u.workspace)
+        if ev is not None:
+            ev[1].record(self.stream)
+
+    def run(self, steps, warmup):
+        torch = self.torch
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True),
+                torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(i, evs[i])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        attend_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        return (t1 - t0) * 1e3 / steps, attend_ms
+
+
+def cpu_baseline(w, budget_s=20.0):
+    """The oracle on the same workload: as many whole sequences as fit the
+    time budget (all heads), scaled to KV GB/s."""
+    import oracle
+    kc = np.zeros(w.pool_elems(), np.uint16)
+    vc = np.zeros(w.pool_elems(), np.uint16)
+    oracle.write_kv(kc, vc, w.k_dense[w.fill_rows], w.v_dense[w.fill_rows], w.fill_slots)
+    oracle.write_kv(kc, vc, w.k_new, w.v_new, w.new_slots)
+    threads = oracle.default_threads()
+    done_seqs, kv_bytes, spent = 0, 0, 0.0
+    per_tok = 2 * w.num_kv_heads * w.head_dim * 2
+    order = list(range(w.num_seqs))
+    for b in order:
+        t0, t1 = int(w.query_start_loc[b]), int(w.query_start_loc[b + 1])
+        rows = np.array([(t, h) for t in range(t0, t1) for h in range(w.num_q_heads)],
+                        np.int64)
+        s = time.perf_counter()
+        oracle.attend_rows(w.q, kc, vc, w.block_tables, w.seq_lens,
+                           w.query_start_loc, w.num_kv_heads, w.scale, rows,
+                           nthreads=threads)
+        spent += time.perf_counter() - s
+        done_seqs += 1
+        kv_bytes += int(w.seq_lens[b]) * per_tok
+        if spent >= budget_s:
+            break
+    return {"value": round(kv_bytes / spent / 1e9, 4), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "sample": "%d of %d sequences of the headline workload, all %d query "
+                      "heads, fp64 C oracle with OpenMP, %.1f s"
+                      % (done_seqs, w.num_seqs, w.num_q_heads, spent)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the paged-attention path here is a "
+              "single-GPU kernel (no multi-GPU sharding is built); use --gpus 1",
+              file=sys.stderr)
+        return 2
+    import torch
+    import workloads as W
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    w = W.make_config(args.config)
+    alg = algorithmic(w)
+    r = Runner(w, args.min_working_set_gib)
+    ms_step, attend_ms = r.run(args.steps, args.warmup)
+    kv_gbs = alg["kv_bytes"] / (ms_step * 1e-3) / 1e9
+    achieved = alg["attend_bytes"] / (attend_ms * 1e-3) / 1e9
+    line = {
+        "metric": "paged-attn KV read GB/s (% HBM peak) + mixed-step tokens/s per layer",
+        "value": round(kv_gbs, 2),
+        "unit": "GB/s",
+        "hbm_peak_frac": round(kv_gbs / HBM_PEAK_GBS, 4),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 q/K/V, seeded block tables)",
+        "config": dict(W.Workload.describe(w), layers_cycled=len(r.layers)),
+        "decode_tokens_per_s": round(w.num_q_tokens / (ms_step * 1e-3), 1),
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None, "kernel": "pa_attend (plan + attend + merge)",
+            "attend_ms": round(attend_ms, 5),
+            "algorithmic_bytes": alg["attend_bytes"]},
+    }
+    del r
+    torch.cuda.empty_cache()
+
+    if not args.no_mixed and args.config != 3:
+        w3 = W.make_config(3)
+        a3 = algorithmic(w3)
+        r3 = Runner(w3, args.min_working_set_gib)
+        ms3, att3 = r3.run(max(20, args.steps // 4), max(5, args.warmup // 2))
+        line["mixed_step"] = {
+            "workload": w3.name, "tokens_per_s_per_layer": round(w3.num_q_tokens / (ms3 * 1e-3), 1),
+            "ms_per_step": round(ms3, 5), "attend_ms": round(att3, 5),
+            "kv_read_gbs": round(a3["kv_bytes"] / (ms3 * 1e-3) / 1e9, 2),
+            "attend_tflops": round(a3["flops"] / (att3 * 1e-3) / 1e12, 2)}
+        del r3
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

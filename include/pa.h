@@ -1,0 +1,249 @@
+/*
+ * pa.h - C ABI of the MI355X (gfx950) paged KV-cache varlen attention library
+ * (libpa.so).
+ *
+ * The library implements the per-layer attention step of a paged KV cache:
+ *
+ *   pa_write_kv  scatter this step's new K/V rows into their physical slots of
+ *                one global pool of 16-token blocks;
+ *   pa_attend    varlen causal attention of every query token of a mixed batch
+ *                (chunked-prefill chunks and single-token decodes together, one
+ *                call) over each request's cached + new tokens, read through
+ *                its block table.
+ *
+ * Where the operations are defined:
+ *   - "Inside vLLM" (supercharleszhu.github.io), Part 3 Runtime, Aside "KV
+ *     cache and prefix caching": the pool of fixed-size blocks; slot_mapping
+ *     gives, per new token of the flattened batch, the slot
+ *     block_id * block_size + offset that its K/V is written to; attention
+ *     takes the per-request block tables, seq_lens and query_start_loc and,
+ *     in one launch, gives a prefill query a causal mask over its cached
+ *     prefix + new tokens and a decode query all of its blocks.
+ *   - Same page, Step 4c "Mixed batches": query_start_loc is the prefix sum of
+ *     per-request scheduled token counts over the flattened batch.
+ *   - "vLLM internals study" (anthony-chaudhary.github.io) section 2.1: the
+ *     block table maps logical block index to physical block id; the write
+ *     slot is block number * block_size + block offset.  Section 2.4: query
+ *     heads that share one KV head are processed together (GQA).
+ *   - "Inside the vLLM Engine" (rohitghumare.com), "A memory problem wearing a
+ *     throughput costume": 16-token blocks, ceil(N/16) blocks for N tokens.
+ *
+ * Semantics (readings where the pages are silent):
+ *   - Attention of query token t (head h) of request b is
+ *       out = sum_j softmax_j(scale * q.K_j) V_j   over keys j = 0 .. p,
+ *     where seq_lens[b] = L counts cached + new tokens, the request's
+ *     Q = query_start_loc[b+1] - query_start_loc[b] new tokens are its last Q
+ *     positions, and query i of the request sits at p = L - Q + i.
+ *   - Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *   - pa_write_kv is called before pa_attend for the same step, so the new
+ *     tokens' K/V are in the pool when attention reads them.
+ *
+ * Data types: q, k, v, out and the pools are bf16 (IEEE binary32 truncated to
+ * its upper 16 bits).  Attention computes in fp32 with bf16 MFMA operands and
+ * rounds the output to bf16 (nearest even).
+ *
+ * KV pool layout (the pages leave it open; this library fixes it):
+ *   k_cache and v_cache are two separate arrays of
+ *     num_blocks x num_kv_heads tiles, each tile 16 * head_dim bf16;
+ *   tile (block n, kv head g) starts at element (n * num_kv_heads + g) * 16 * D.
+ *   Inside a tile, for token slot t in [0,16) and dim d in [0,D), H = D/2:
+ *     K(t, d) is at ((d / 8) * 16 + t) * 8 + d % 8
+ *     V(t, d) is at (((d % H) * 4 + t / 4) * 2 + d / H) * 4 + t % 4
+ *   (K: 8-dim chunks of all 16 tokens; V: dims d and d+H of 4 consecutive
+ *   tokens side by side.)  Only pa_write_kv, pa_attend and pa_gather_kv are
+ *   meant to touch the pools.
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE memory that the caller allocates, owns
+ *     and keeps alive until the call's work on `stream` has finished.  The
+ *     library never allocates, frees or keeps pointers across calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     pa_write_kv, pa_attend and pa_gather_kv only enqueue work: no host
+ *     synchronisation, no device allocation.
+ *   - Host-side argument errors (NULL pointer, negative size, unsupported
+ *     head_dim / block shape, num_q_heads not a multiple of num_kv_heads, too
+ *     small workspace) are detected before anything is enqueued and returned
+ *     as a pa_status; pa_last_error() then holds a message.
+ *   - Metadata CONTENT (block ids, slots, lengths) is not checked on the fast
+ *     path: invalid content is a caller error whose output is undefined.  The
+ *     kernels still never read or write outside the buffers whose sizes they
+ *     are given (out-of-range block ids and slots are clamped or skipped, and
+ *     requests with inconsistent lengths are skipped).  pa_validate_metadata
+ *     reports such content errors.
+ *   - Launch failures return PA_ERR_HIP with the HIP error text in
+ *     pa_last_error().
+ *   - Thread safety: the library holds no mutable global state except a
+ *     per-device cache of the compute-unit count and the thread-local error
+ *     string; calls from several host threads are safe.  Calls that share a
+ *     workspace must be ordered on one stream.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+#define PA_BLOCK_SIZE 16
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,        /* a required pointer is NULL                    */
+  PA_ERR_SHAPE = 2,       /* a size is negative or sizes are inconsistent  */
+  PA_ERR_UNSUPPORTED = 3, /* head_dim not 64/128, group size > 16, ...     */
+  PA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required    */
+  PA_ERR_METADATA = 5,    /* pa_validate_metadata found invalid content    */
+  PA_ERR_HIP = 6          /* a HIP runtime call or launch failed           */
+} pa_status;
+
+/* Library ABI version (PA_ABI_VERSION). */
+int pa_abi_version(void);
+
+/* Static text for a status code. */
+const char *pa_status_string(int status);
+
+/* Message of the last failed call on this host thread ("" if none). */
+const char *pa_last_error(void);
+
+/*
+ * pa_write_kv - scatter new K/V rows into the pool ("reshape and cache").
+ *
+ * For every token i in [0, num_tokens) with s = slot_mapping[i] >= 0:
+ *   for every kv head g and dim d,
+ *     K(block s/16, head g, slot s%16, d) = k[i*k_token_stride + g*D + d]
+ *     V(block s/16, head g, slot s%16, d) = v[i*v_token_stride + g*D + d]
+ * as exact bit copies.  Tokens with s < 0 are skipped (padding); slots
+ * >= num_blocks*16 are skipped too (caller error).  Two tokens with the same
+ * slot race (caller error).  Every other pool element is left unchanged.
+ *
+ *   k, v            device bf16, row i at k + i*k_token_stride (elements),
+ *                   num_kv_heads*head_dim contiguous elements per row
+ *   k_token_stride, v_token_stride   >= num_kv_heads*head_dim
+ *   slot_mapping    device int64 [num_tokens]
+ *   k_cache, v_cache device bf16 pools, num_blocks tiles per kv head (layout
+ *                   above)
+ *   head_dim        64 or 128
+ *
+ * Source: "Inside vLLM", Aside "KV cache and prefix caching" (slot_mapping,
+ * the phase-agnostic scatter); "vLLM internals study" section 2.1.
+ */
+pa_status pa_write_kv(const void *k, const void *v, int64_t k_token_stride,
+                      int64_t v_token_stride, const int64_t *slot_mapping,
+                      int64_t num_tokens, int32_t num_kv_heads,
+                      int32_t head_dim, void *k_cache, void *v_cache,
+                      int64_t num_blocks, void *stream);
+
+/*
+ * pa_attend_workspace_size - bytes of device workspace pa_attend needs for a
+ * batch within these bounds (work list, per-token split records and split-K
+ * partial results).  Returns 0 for invalid arguments.
+ */
+size_t pa_attend_workspace_size(int32_t num_seqs, int64_t num_q_tokens,
+                                int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_query_len,
+                                int32_t max_seq_len);
+
+/*
+ * pa_attend - paged varlen causal attention over a mixed batch.
+ *
+ *   q                device bf16 [num_q_tokens][num_q_heads][head_dim],
+ *                    rows of request b at query_start_loc[b] ..
+ *                    query_start_loc[b+1]-1
+ *   k_cache, v_cache device bf16 pools (layout above), num_blocks blocks
+ *   block_tables     device int32 [num_seqs][max_blocks_per_seq]; entry j of
+ *                    row b is the physical block of logical tokens
+ *                    16j .. 16j+15 of request b; entries past ceil(L_b/16) are
+ *                    never read.  Several rows may name the same block
+ *                    (shared prefix blocks are read-only here).
+ *   seq_lens         device int32 [num_seqs], L_b = cached + new tokens
+ *   query_start_loc  device int32 [num_seqs+1], 0 = qsl[0] <= qsl[1] <= ...,
+ *                    qsl[num_seqs] = num_q_tokens; 0 <= Q_b <= L_b
+ *   max_query_len, max_seq_len  host-side upper bounds of Q_b and L_b (used
+ *                    for workspace sizing; requests beyond them are skipped)
+ *   scale            softmax scale (e.g. 1/sqrt(head_dim))
+ *   out              device bf16 [num_q_tokens][num_q_heads][head_dim]
+ *   workspace        device buffer of >= pa_attend_workspace_size(...) bytes,
+ *                    256-byte aligned; contents need no initialisation and
+ *                    are scratch after the call
+ *   num_q_heads % num_kv_heads == 0, num_q_heads/num_kv_heads <= 16,
+ *   head_dim 64 or 128.
+ *
+ * The reduction order of every output depends only on that request's own
+ * (Q_b, L_b) and the logical positions of its keys: outputs are bitwise
+ * independent of physical block ids, of block sharing and of the rest of the
+ * batch.
+ *
+ * Source: "Inside vLLM", Step 4c and the Aside "KV cache and prefix caching";
+ * "vLLM internals study" sections 2.1 and 2.4.
+ */
+pa_status pa_attend(const void *q, const void *k_cache, const void *v_cache,
+                    int64_t num_blocks, const int32_t *block_tables,
+                    int32_t max_blocks_per_seq, const int32_t *seq_lens,
+                    const int32_t *query_start_loc, int32_t num_seqs,
+                    int64_t num_q_tokens, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim,
+                    int32_t max_query_len, int32_t max_seq_len, float scale,
+                    void *out, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/*
+ * pa_gather_kv - logical gather through the block tables (a checking aid).
+ *
+ * Writes k_out/v_out, device bf16 [sum_b L_b][num_kv_heads][head_dim]: row
+ * kv_start[b] + j holds token j < L_b of request b, read from block
+ * block_tables[b][j/16], slot j%16.  kv_start: device int64 [num_seqs+1],
+ * prefix sum of seq_lens; total_rows = kv_start[num_seqs].
+ *
+ * Source: "Deep Dive - vLLM" (leetllm.com), "The historical idea: page KV
+ * memory" (a kernel follows the table to load the right physical blocks);
+ * "vLLM internals study" section 2.1.
+ */
+pa_status pa_gather_kv(const void *k_cache, const void *v_cache,
+                       int64_t num_blocks, const int32_t *block_tables,
+                       int32_t max_blocks_per_seq, const int32_t *seq_lens,
+                       const int64_t *kv_start, int32_t num_seqs,
+                       int64_t total_rows, int32_t num_kv_heads,
+                       int32_t head_dim, void *k_out, void *v_out,
+                       void *stream);
+
+/*
+ * pa_validate_metadata_host - check the CONTENT of one step's metadata, all
+ * pointers HOST memory.  Returns PA_OK or PA_ERR_METADATA (message in
+ * pa_last_error()) for: query_start_loc not starting at 0, decreasing, or not
+ * ending at num_q_tokens; Q_b > L_b or L_b < 0; L_b > max_seq_len or
+ * Q_b > max_query_len; ceil(L_b/16) > max_blocks_per_seq; a used block-table
+ * entry outside [0, num_blocks); a slot >= num_blocks*16; two tokens with the
+ * same slot.  slot_mapping may be NULL (num_slots ignored).
+ */
+pa_status pa_validate_metadata_host(const int32_t *block_tables,
+                                    int32_t max_blocks_per_seq,
+                                    const int32_t *seq_lens,
+                                    const int32_t *query_start_loc,
+                                    int32_t num_seqs, int64_t num_q_tokens,
+                                    int32_t max_query_len, int32_t max_seq_len,
+                                    int64_t num_blocks,
+                                    const int64_t *slot_mapping,
+                                    int64_t num_slots);
+
+/*
+ * pa_validate_metadata - the same checks on DEVICE metadata.  Synchronous:
+ * copies the arrays to host memory (blocking hipMemcpy) first.
+ */
+pa_status pa_validate_metadata(const int32_t *block_tables,
+                               int32_t max_blocks_per_seq,
+                               const int32_t *seq_lens,
+                               const int32_t *query_start_loc,
+                               int32_t num_seqs, int64_t num_q_tokens,
+                               int32_t max_query_len, int32_t max_seq_len,
+                               int64_t num_blocks, const int64_t *slot_mapping,
+                               int64_t num_slots);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,208 @@
+"""MI355X-native paged KV-cache varlen attention (PagedAttention hot path).
+
+Python binding of libpa.so (include/pa.h).  Argument marshalling only: every
+step of the path runs in the library's HIP kernels; torch supplies device
+memory and the current stream.  There is no fallback: if libpa.so is missing
+or a tensor is not on a GPU, the calls raise.
+
+    k_cache, v_cache = alloc_pool(num_blocks, num_kv_heads, head_dim)
+    write_kv(k_new, v_new, slot_mapping, k_cache, v_cache)
+    out = attend(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
+                 scale, max_query_len, max_seq_len)
+
+Sources: "Inside vLLM" (supercharleszhu.github.io), Part 3, Step 4c and the
+Aside "KV cache and prefix caching"; "vLLM internals study"
+(anthony-chaudhary.github.io) sections 2.1 and 2.4.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import PAError  # noqa: F401
+
+BLOCK_SIZE = 16
+
+
+def _need_cuda(t: torch.Tensor, name: str) -> None:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+
+
+def _dtype(t: torch.Tensor, dt, name: str) -> None:
+    if t.dtype != dt:
+        raise TypeError("%s must be %s, got %s" % (name, dt, t.dtype))
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def alloc_pool(num_blocks: int, num_kv_heads: int, head_dim: int,
+               device="cuda", fill: Optional[float] = None
+               ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Two bf16 pools (K, V), each [num_blocks][num_kv_heads][16 * head_dim]
+    in the library's tile layout."""
+    shape = (num_blocks, num_kv_heads, BLOCK_SIZE * head_dim)
+    if fill is None:
+        k = torch.empty(shape, dtype=torch.bfloat16, device=device)
+        v = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    else:
+        k = torch.full(shape, fill, dtype=torch.bfloat16, device=device)
+        v = torch.full(shape, fill, dtype=torch.bfloat16, device=device)
+    return k, v
+
+
+def _pool_blocks(cache: torch.Tensor, num_kv_heads: int, head_dim: int) -> int:
+    per_block = num_kv_heads * BLOCK_SIZE * head_dim
+    if not cache.is_contiguous() or cache.numel() % per_block:
+        raise ValueError("pool must be contiguous with a multiple of "
+                         "num_kv_heads*16*head_dim elements")
+    return cache.numel() // per_block
+
+
+def write_kv(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+             k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
+    """Scatter k, v ([T][Hkv][D] bf16, rows may be strided) into their slots."""
+    for t, n in ((k, "k"), (v, "v"), (slot_mapping, "slot_mapping"),
+                 (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need_cuda(t, n)
+    _dtype(k, torch.bfloat16, "k")
+    _dtype(v, torch.bfloat16, "v")
+    _dtype(slot_mapping, torch.int64, "slot_mapping")
+    _dtype(k_cache, torch.bfloat16, "k_cache")
+    _dtype(v_cache, torch.bfloat16, "v_cache")
+    if k.dim() != 3 or v.shape != k.shape:
+        raise ValueError("k and v must be [num_tokens][num_kv_heads][head_dim]")
+    T, Hkv, D = k.shape
+    for t, n in ((k, "k"), (v, "v")):
+        if t.stride(2) != 1 or t.stride(1) != D:
+            raise ValueError("%s rows must be contiguous [num_kv_heads][head_dim]" % n)
+    if not slot_mapping.is_contiguous() or slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be contiguous [num_tokens]")
+    nb = _pool_blocks(k_cache, Hkv, D)
+    if _pool_blocks(v_cache, Hkv, D) != nb:
+        raise ValueError("k_cache and v_cache differ in size")
+    lib = _lib.load()
+    st = lib.pa_write_kv(_ptr(k), _ptr(v), k.stride(0), v.stride(0),
+                         _ptr(slot_mapping), T, Hkv, D, _ptr(k_cache),
+                         _ptr(v_cache), nb, _stream(k))
+    _lib.check(st, "pa_write_kv")
+
+
+def workspace_size(num_seqs: int, num_q_tokens: int, num_q_heads: int,
+                   num_kv_heads: int, head_dim: int, max_query_len: int,
+                   max_seq_len: int) -> int:
+    n = _lib.load().pa_attend_workspace_size(num_seqs, num_q_tokens, num_q_heads,
+                                            num_kv_heads, head_dim,
+                                            max_query_len, max_seq_len)
+    if n == 0:
+        raise ValueError("invalid arguments for pa_attend_workspace_size")
+    return int(n)
+
+
+def alloc_workspace(num_seqs, num_q_tokens, num_q_heads, num_kv_heads, head_dim,
+                    max_query_len, max_seq_len, device="cuda") -> torch.Tensor:
+    n = workspace_size(num_seqs, num_q_tokens, num_q_heads, num_kv_heads,
+                       head_dim, max_query_len, max_seq_len)
+    # torch's caching allocator returns 512-byte aligned blocks
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def attend(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+           block_tables: torch.Tensor, seq_lens: torch.Tensor,
+           query_start_loc: torch.Tensor, scale: float, max_query_len: int,
+           max_seq_len: int, num_kv_heads: Optional[int] = None,
+           out: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Paged varlen causal attention of every query row of a mixed batch.
+
+    q [T][Hq][D] bf16; block_tables [B][max_blocks] int32; seq_lens [B] int32;
+    query_start_loc [B+1] int32; pools from alloc_pool.  Returns out
+    [T][Hq][D] bf16 (written in place when ``out`` is given)."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                 (block_tables, "block_tables"), (seq_lens, "seq_lens"),
+                 (query_start_loc, "query_start_loc")):
+        _need_cuda(t, n)
+    _dtype(q, torch.bfloat16, "q")
+    _dtype(k_cache, torch.bfloat16, "k_cache")
+    _dtype(v_cache, torch.bfloat16, "v_cache")
+    _dtype(block_tables, torch.int32, "block_tables")
+    _dtype(seq_lens, torch.int32, "seq_lens")
+    _dtype(query_start_loc, torch.int32, "query_start_loc")
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be contiguous [num_q_tokens][num_q_heads][head_dim]")
+    T, Hq, D = q.shape
+    if num_kv_heads is None:
+        if k_cache.dim() != 3:
+            raise ValueError("pass num_kv_heads or a [blocks][kv_heads][16*D] pool")
+        num_kv_heads = k_cache.shape[1]
+    nb = _pool_blocks(k_cache, num_kv_heads, D)
+    if block_tables.dim() != 2 or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be contiguous [num_seqs][max_blocks]")
+    B = block_tables.shape[0]
+    if seq_lens.shape != (B,) or query_start_loc.shape != (B + 1,):
+        raise ValueError("seq_lens must be [B] and query_start_loc [B+1]")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need_cuda(out, "out")
+        _dtype(out, torch.bfloat16, "out")
+        if out.shape != q.shape or not out.is_contiguous():
+            raise ValueError("out must be contiguous and shaped like q")
+    if workspace is None:
+        workspace = alloc_workspace(B, T, Hq, num_kv_heads, D, max_query_len,
+                                    max_seq_len, device=q.device)
+    lib = _lib.load()
+    st = lib.pa_attend(_ptr(q), _ptr(k_cache), _ptr(v_cache), nb,
+                       _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens),
+                       _ptr(query_start_loc), B, T, Hq, num_kv_heads, D,
+                       int(max_query_len), int(max_seq_len), float(scale),
+                       _ptr(out), _ptr(workspace), workspace.numel(), _stream(q))
+    _lib.check(st, "pa_attend")
+    return out
+
+
+def gather_kv(k_cache: torch.Tensor, v_cache: torch.Tensor,
+              block_tables: torch.Tensor, seq_lens: torch.Tensor,
+              kv_start: torch.Tensor, total_rows: int, num_kv_heads: int,
+              head_dim: int) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Logical gather through the block tables: dense [sum L][Hkv][D] K, V."""
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache"),
+                 (block_tables, "block_tables"), (seq_lens, "seq_lens"),
+                 (kv_start, "kv_start")):
+        _need_cuda(t, n)
+    _dtype(kv_start, torch.int64, "kv_start")
+    nb = _pool_blocks(k_cache, num_kv_heads, head_dim)
+    B = block_tables.shape[0]
+    ko = torch.empty((total_rows, num_kv_heads, head_dim), dtype=torch.bfloat16,
+                     device=k_cache.device)
+    vo = torch.empty_like(ko)
+    lib = _lib.load()
+    st = lib.pa_gather_kv(_ptr(k_cache), _ptr(v_cache), nb, _ptr(block_tables),
+                          block_tables.shape[1], _ptr(seq_lens), _ptr(kv_start),
+                          B, total_rows, num_kv_heads, head_dim, _ptr(ko),
+                          _ptr(vo), _stream(k_cache))
+    _lib.check(st, "pa_gather_kv")
+    return ko, vo
+
+
+def validate_metadata(block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                      query_start_loc: torch.Tensor, num_q_tokens: int,
+                      max_query_len: int, max_seq_len: int, num_blocks: int,
+                      slot_mapping: Optional[torch.Tensor] = None) -> None:
+    """Synchronous content check of device metadata; raises PAError."""
+    B = block_tables.shape[0]
+    lib = _lib.load()
+    st = lib.pa_validate_metadata(
+        _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens),
+        _ptr(query_start_loc), B, num_q_tokens, max_query_len, max_seq_len,
+        num_blocks, _ptr(slot_mapping),
+        0 if slot_mapping is None else slot_mapping.numel())
+    _lib.check(st, "pa_validate_metadata")

@@ -1,0 +1,150 @@
+// KV scatter into the block pool, and the logical gather back out of it.
+//
+// Scatter ("reshape and cache"): every new token of the flattened batch is
+// written to the physical slot slot_mapping[i] = block_id * 16 + offset
+// ("Inside vLLM", Aside "KV cache and prefix caching"; "vLLM internals study"
+// section 2.1, "Reaching the kernel").  One kernel for prefill chunks and
+// decodes alike: the slot is all it needs.
+//
+// Pool tile layout (block n, kv head g), 16*D bf16, H = D/2:
+//   K(t, d) at ((d/8)*16 + t)*8 + d%8      -> 16 bytes per (t, 8-dim chunk)
+//   V(t, d) at (((d%H)*4 + t/4)*2 + d/H)*4 + t%4
+// The attention kernel loads each tile with fully contiguous 1 KiB wave loads
+// that land directly in MFMA operand order.
+#include "pa_device.h"
+
+namespace pa {
+
+namespace {
+
+// One thread per (token, kv head, 8-dim chunk): a 16-byte K copy and eight
+// 2-byte V stores.  Copies are integer moves: exact bits.
+template <int D>
+__global__ __launch_bounds__(256) void write_kv_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    int64_t k_stride, int64_t v_stride, const int64_t* __restrict__ slots,
+    int64_t num_tokens, int Hkv, uint16_t* __restrict__ k_cache,
+    uint16_t* __restrict__ v_cache, int64_t num_slots) {
+  constexpr int kChunks = D / 8;
+  constexpr int H = D / 2;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_token = (int64_t)Hkv * kChunks;
+  if (gid >= num_tokens * per_token) return;
+  const int64_t tok = gid / per_token;
+  const int rem = (int)(gid - tok * per_token);
+  const int g = rem / kChunks;
+  const int c = rem - g * kChunks;
+  const int64_t s = slots[tok];
+  if (s < 0 || s >= num_slots) return;
+  const int64_t blk = s >> 4;
+  const int t = (int)(s & 15);
+  const int64_t tile = (blk * Hkv + g) * (int64_t)(kBlock * D);
+
+  const uint4 kv = *reinterpret_cast<const uint4*>(k + tok * k_stride + g * D + c * 8);
+  *reinterpret_cast<uint4*>(k_cache + tile + ((int64_t)c * 16 + t) * 8) = kv;
+
+  const uint4 vv = *reinterpret_cast<const uint4*>(v + tok * v_stride + g * D + c * 8);
+  const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int d = c * 8 + j;
+    const uint16_t bits = (uint16_t)(w[j >> 1] >> ((j & 1) * 16));
+    const int off = (((d % H) * 4 + (t >> 2)) * 2 + d / H) * 4 + (t & 3);
+    v_cache[tile + off] = bits;
+  }
+}
+
+// One thread per (dense row, kv head, 8-dim chunk).
+template <int D>
+__global__ __launch_bounds__(256) void gather_kv_kernel(
+    const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
+    int64_t num_blocks, const int32_t* __restrict__ bt, int32_t bt_stride,
+    const int32_t* __restrict__ seq_lens, const int64_t* __restrict__ kv_start,
+    int32_t num_seqs, int64_t total_rows, int Hkv, uint16_t* __restrict__ k_out,
+    uint16_t* __restrict__ v_out) {
+  constexpr int kChunks = D / 8;
+  constexpr int H = D / 2;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_row = (int64_t)Hkv * kChunks;
+  if (gid >= total_rows * per_row) return;
+  const int64_t row = gid / per_row;
+  const int rem = (int)(gid - row * per_row);
+  const int g = rem / kChunks;
+  const int c = rem - g * kChunks;
+  // request owning this row: last b with kv_start[b] <= row
+  int lo = 0, hi = num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (kv_start[mid] <= row) lo = mid; else hi = mid - 1;
+  }
+  const int b = lo;
+  const int64_t j = row - kv_start[b];
+  if (j < 0 || j >= seq_lens[b] || (j >> 4) >= bt_stride) return;
+  int64_t blk = bt[(int64_t)b * bt_stride + (j >> 4)];
+  if (blk < 0 || blk >= num_blocks) return;
+  const int t = (int)(j & 15);
+  const int64_t tile = (blk * Hkv + g) * (int64_t)(kBlock * D);
+  const int64_t dst = (row * Hkv + g) * D + c * 8;
+  *reinterpret_cast<uint4*>(k_out + dst) =
+      *reinterpret_cast<const uint4*>(k_cache + tile + ((int64_t)c * 16 + t) * 8);
+  uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    const int d = c * 8 + jj;
+    const int off = (((d % H) * 4 + (t >> 2)) * 2 + d / H) * 4 + (t & 3);
+    w[jj >> 1] |= (uint32_t)v_cache[tile + off] << ((jj & 1) * 16);
+  }
+  *reinterpret_cast<uint4*>(v_out + dst) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+}  // namespace
+
+hipError_t launch_write_kv(const uint16_t* k, const uint16_t* v,
+                           int64_t k_stride, int64_t v_stride,
+                           const int64_t* slot_mapping, int64_t num_tokens,
+                           int num_kv_heads, int head_dim, uint16_t* k_cache,
+                           uint16_t* v_cache, int64_t num_blocks,
+                           hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const int64_t threads = num_tokens * num_kv_heads * (head_dim / 8);
+  const dim3 block(256);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  const int64_t num_slots = num_blocks * kBlock;
+  if (head_dim == 128) {
+    hipLaunchKernelGGL(write_kv_kernel<128>, grid, block, 0, stream, k, v,
+                       k_stride, v_stride, slot_mapping, num_tokens,
+                       num_kv_heads, k_cache, v_cache, num_slots);
+  } else {
+    hipLaunchKernelGGL(write_kv_kernel<64>, grid, block, 0, stream, k, v,
+                       k_stride, v_stride, slot_mapping, num_tokens,
+                       num_kv_heads, k_cache, v_cache, num_slots);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_kv(const uint16_t* k_cache, const uint16_t* v_cache,
+                            int64_t num_blocks, const int32_t* block_tables,
+                            int32_t bt_stride, const int32_t* seq_lens,
+                            const int64_t* kv_start, int32_t num_seqs,
+                            int64_t total_rows, int num_kv_heads, int head_dim,
+                            uint16_t* k_out, uint16_t* v_out,
+                            hipStream_t stream) {
+  if (total_rows == 0 || num_seqs == 0) return hipSuccess;
+  const int64_t threads = total_rows * num_kv_heads * (head_dim / 8);
+  const dim3 block(256);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (head_dim == 128) {
+    hipLaunchKernelGGL(gather_kv_kernel<128>, grid, block, 0, stream, k_cache,
+                       v_cache, num_blocks, block_tables, bt_stride, seq_lens,
+                       kv_start, num_seqs, total_rows, num_kv_heads, k_out,
+                       v_out);
+  } else {
+    hipLaunchKernelGGL(gather_kv_kernel<64>, grid, block, 0, stream, k_cache,
+                       v_cache, num_blocks, block_tables, bt_stride, seq_lens,
+                       kv_start, num_seqs, total_rows, num_kv_heads, k_out,
+                       v_out);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,300 @@
+// C ABI of libpa.so: argument checks, workspace sizing and launches.  The
+// operations and their sources are documented in include/pa.h.
+#include "../../include/pa.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <mutex>
+#include <string>
+#include <unordered_set>
+#include <vector>
+
+#include "pa_device.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pa_status fail(pa_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+pa_status ok() {
+  g_last_error.clear();
+  return PA_OK;
+}
+
+pa_status hip_fail(hipError_t e, const char* what) {
+  return fail(PA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Compute-unit count per device, read once.
+int num_cus_of_current_device(hipError_t* err) {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int n = 0;
+    *err = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (*err != hipSuccess) return 0;
+    cache[dev] = n > 0 ? n : 1;
+  }
+  return cache[dev];
+}
+
+bool supported_head_dim(int32_t d) { return d == 64 || d == 128; }
+
+pa_status check_heads(int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim) {
+  if (num_q_heads <= 0 || num_kv_heads <= 0)
+    return fail(PA_ERR_SHAPE, "num_q_heads and num_kv_heads must be > 0");
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PA_ERR_SHAPE, "num_q_heads must be a multiple of num_kv_heads");
+  if (num_q_heads / num_kv_heads > pa::kMaxGroup)
+    return fail(PA_ERR_UNSUPPORTED,
+                "more than 16 query heads per kv head is not supported");
+  if (!supported_head_dim(head_dim))
+    return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_abi_version(void) { return PA_ABI_VERSION; }
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "null pointer";
+    case PA_ERR_SHAPE: return "invalid shape";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_WORKSPACE: return "workspace too small";
+    case PA_ERR_METADATA: return "invalid metadata";
+    case PA_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+pa_status pa_write_kv(const void* k, const void* v, int64_t k_token_stride,
+                      int64_t v_token_stride, const int64_t* slot_mapping,
+                      int64_t num_tokens, int32_t num_kv_heads,
+                      int32_t head_dim, void* k_cache, void* v_cache,
+                      int64_t num_blocks, void* stream) {
+  if (num_tokens < 0 || num_blocks < 0)
+    return fail(PA_ERR_SHAPE, "num_tokens and num_blocks must be >= 0");
+  if (num_kv_heads <= 0) return fail(PA_ERR_SHAPE, "num_kv_heads must be > 0");
+  if (!supported_head_dim(head_dim))
+    return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (k_token_stride < row || v_token_stride < row)
+    return fail(PA_ERR_SHAPE, "token strides must be >= num_kv_heads*head_dim");
+  if ((k_token_stride % 8) || (v_token_stride % 8))
+    return fail(PA_ERR_SHAPE, "token strides must be multiples of 8 elements");
+  if (num_tokens == 0) return ok();
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache)
+    return fail(PA_ERR_NULL, "pa_write_kv: NULL pointer");
+  if (((uintptr_t)k | (uintptr_t)v | (uintptr_t)k_cache | (uintptr_t)v_cache) & 15)
+    return fail(PA_ERR_SHAPE, "k, v and the pools must be 16-byte aligned");
+  hipError_t e = pa::launch_write_kv(
+      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+      k_token_stride, v_token_stride, slot_mapping, num_tokens, num_kv_heads,
+      head_dim, static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
+      num_blocks, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pa_write_kv launch");
+  return ok();
+}
+
+size_t pa_attend_workspace_size(int32_t num_seqs, int64_t num_q_tokens,
+                                int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_query_len,
+                                int32_t max_seq_len) {
+  if (num_seqs < 0 || num_q_tokens < 0 || max_query_len < 0 || max_seq_len < 0)
+    return 0;
+  if (check_heads(num_q_heads, num_kv_heads, head_dim) != PA_OK) return 0;
+  return pa::workspace_layout(num_seqs, num_q_tokens, num_q_heads, num_kv_heads,
+                              head_dim, max_query_len, max_seq_len)
+      .total;
+}
+
+pa_status pa_attend(const void* q, const void* k_cache, const void* v_cache,
+                    int64_t num_blocks, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                    const int32_t* query_start_loc, int32_t num_seqs,
+                    int64_t num_q_tokens, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim,
+                    int32_t max_query_len, int32_t max_seq_len, float scale,
+                    void* out, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  if (num_seqs < 0 || num_q_tokens < 0 || num_blocks < 0 ||
+      max_blocks_per_seq < 0 || max_query_len < 0 || max_seq_len < 0)
+    return fail(PA_ERR_SHAPE, "pa_attend: negative size");
+  if (num_q_tokens > INT32_MAX / 2)
+    return fail(PA_ERR_SHAPE, "pa_attend: num_q_tokens too large");
+  pa_status s = check_heads(num_q_heads, num_kv_heads, head_dim);
+  if (s != PA_OK) return s;
+  if (num_q_tokens == 0 || num_seqs == 0) return ok();
+  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens ||
+      !query_start_loc || !out)
+    return fail(PA_ERR_NULL, "pa_attend: NULL pointer");
+  if (num_blocks == 0 || max_blocks_per_seq == 0)
+    return fail(PA_ERR_SHAPE, "pa_attend: empty pool or block table");
+  if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out) & 15)
+    return fail(PA_ERR_SHAPE, "q, out and the pools must be 16-byte aligned");
+  pa::WorkspaceLayout ws =
+      pa::workspace_layout(num_seqs, num_q_tokens, num_q_heads, num_kv_heads,
+                           head_dim, max_query_len, max_seq_len);
+  if (!workspace || workspace_bytes < ws.total)
+    return fail(PA_ERR_WORKSPACE,
+                "pa_attend: workspace needs " + std::to_string(ws.total) +
+                    " bytes, got " + std::to_string(workspace_bytes));
+  if ((uintptr_t)workspace & 255)
+    return fail(PA_ERR_WORKSPACE, "pa_attend: workspace must be 256-byte aligned");
+  hipError_t e = hipSuccess;
+  const int cus = num_cus_of_current_device(&e);
+  if (e != hipSuccess) return hip_fail(e, "pa_attend device query");
+  pa::AttendArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = static_cast<const uint16_t*>(k_cache);
+  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.num_blocks = num_blocks;
+  a.block_tables = block_tables;
+  a.bt_stride = max_blocks_per_seq;
+  a.seq_lens = seq_lens;
+  a.qsl = query_start_loc;
+  a.num_seqs = num_seqs;
+  a.num_q_tokens = num_q_tokens;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.max_query_len = max_query_len;
+  a.max_seq_len = max_seq_len;
+  a.scale = scale;
+  a.out = static_cast<uint16_t*>(out);
+  a.workspace = workspace;
+  a.ws = ws;
+  a.num_cus = cus;
+  e = pa::launch_attend(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pa_attend launch");
+  return ok();
+}
+
+pa_status pa_gather_kv(const void* k_cache, const void* v_cache,
+                       int64_t num_blocks, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                       const int64_t* kv_start, int32_t num_seqs,
+                       int64_t total_rows, int32_t num_kv_heads,
+                       int32_t head_dim, void* k_out, void* v_out,
+                       void* stream) {
+  if (num_seqs < 0 || total_rows < 0 || num_blocks < 0 || max_blocks_per_seq < 0)
+    return fail(PA_ERR_SHAPE, "pa_gather_kv: negative size");
+  if (num_kv_heads <= 0) return fail(PA_ERR_SHAPE, "num_kv_heads must be > 0");
+  if (!supported_head_dim(head_dim))
+    return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (total_rows == 0 || num_seqs == 0) return ok();
+  if (!k_cache || !v_cache || !block_tables || !seq_lens || !kv_start ||
+      !k_out || !v_out)
+    return fail(PA_ERR_NULL, "pa_gather_kv: NULL pointer");
+  hipError_t e = pa::launch_gather_kv(
+      static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache),
+      num_blocks, block_tables, max_blocks_per_seq, seq_lens, kv_start, num_seqs,
+      total_rows, num_kv_heads, head_dim, static_cast<uint16_t*>(k_out),
+      static_cast<uint16_t*>(v_out), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pa_gather_kv launch");
+  return ok();
+}
+
+pa_status pa_validate_metadata_host(const int32_t* block_tables,
+                                    int32_t max_blocks_per_seq,
+                                    const int32_t* seq_lens,
+                                    const int32_t* query_start_loc,
+                                    int32_t num_seqs, int64_t num_q_tokens,
+                                    int32_t max_query_len, int32_t max_seq_len,
+                                    int64_t num_blocks,
+                                    const int64_t* slot_mapping,
+                                    int64_t num_slots) {
+  if (num_seqs < 0 || num_q_tokens < 0 || max_blocks_per_seq < 0 || num_blocks < 0)
+    return fail(PA_ERR_SHAPE, "validate: negative size");
+  if (num_seqs > 0 && (!block_tables || !seq_lens || !query_start_loc))
+    return fail(PA_ERR_NULL, "validate: NULL pointer");
+  if (num_seqs > 0 && query_start_loc[0] != 0)
+    return fail(PA_ERR_METADATA, "query_start_loc[0] != 0");
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int64_t q0 = query_start_loc[b], q1 = query_start_loc[b + 1];
+    const int64_t L = seq_lens[b];
+    const std::string at = " (request " + std::to_string(b) + ")";
+    if (q1 < q0) return fail(PA_ERR_METADATA, "query_start_loc decreases" + at);
+    if (L < 0) return fail(PA_ERR_METADATA, "seq_len < 0" + at);
+    if (q1 - q0 > L) return fail(PA_ERR_METADATA, "query length > seq_len" + at);
+    if (L > max_seq_len) return fail(PA_ERR_METADATA, "seq_len > max_seq_len" + at);
+    if (q1 - q0 > max_query_len)
+      return fail(PA_ERR_METADATA, "query length > max_query_len" + at);
+    const int64_t nb = (L + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE;
+    if (nb > max_blocks_per_seq)
+      return fail(PA_ERR_METADATA, "block table row too short" + at);
+    for (int64_t j = 0; j < nb; ++j) {
+      const int64_t id = block_tables[(int64_t)b * max_blocks_per_seq + j];
+      if (id < 0 || id >= num_blocks)
+        return fail(PA_ERR_METADATA, "block id out of range" + at);
+    }
+  }
+  if (num_seqs > 0 && query_start_loc[num_seqs] != num_q_tokens)
+    return fail(PA_ERR_METADATA, "query_start_loc[num_seqs] != num_q_tokens");
+  if (slot_mapping && num_slots > 0) {
+    std::unordered_set<int64_t> seen;
+    seen.reserve((size_t)num_slots * 2);
+    for (int64_t i = 0; i < num_slots; ++i) {
+      const int64_t s = slot_mapping[i];
+      if (s < 0) continue;
+      if (s >= num_blocks * PA_BLOCK_SIZE)
+        return fail(PA_ERR_METADATA, "slot out of range (token " + std::to_string(i) + ")");
+      if (!seen.insert(s).second)
+        return fail(PA_ERR_METADATA, "duplicate slot (token " + std::to_string(i) + ")");
+    }
+  }
+  return ok();
+}
+
+pa_status pa_validate_metadata(const int32_t* block_tables,
+                               int32_t max_blocks_per_seq,
+                               const int32_t* seq_lens,
+                               const int32_t* query_start_loc,
+                               int32_t num_seqs, int64_t num_q_tokens,
+                               int32_t max_query_len, int32_t max_seq_len,
+                               int64_t num_blocks, const int64_t* slot_mapping,
+                               int64_t num_slots) {
+  if (num_seqs < 0 || max_blocks_per_seq < 0 || num_slots < 0)
+    return fail(PA_ERR_SHAPE, "validate: negative size");
+  if (num_seqs > 0 && (!block_tables || !seq_lens || !query_start_loc))
+    return fail(PA_ERR_NULL, "validate: NULL pointer");
+  std::vector<int32_t> bt((size_t)num_seqs * max_blocks_per_seq);
+  std::vector<int32_t> sl(num_seqs), qsl(num_seqs + 1);
+  std::vector<int64_t> sm(slot_mapping ? num_slots : 0);
+  hipError_t e = hipSuccess;
+  if (num_seqs > 0) {
+    if (!bt.empty())
+      e = hipMemcpy(bt.data(), block_tables, bt.size() * 4, hipMemcpyDeviceToHost);
+    if (e == hipSuccess)
+      e = hipMemcpy(sl.data(), seq_lens, sl.size() * 4, hipMemcpyDeviceToHost);
+    if (e == hipSuccess)
+      e = hipMemcpy(qsl.data(), query_start_loc, qsl.size() * 4, hipMemcpyDeviceToHost);
+  }
+  if (e == hipSuccess && !sm.empty())
+    e = hipMemcpy(sm.data(), slot_mapping, sm.size() * 8, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "validate: copy to host");
+  return pa_validate_metadata_host(bt.data(), max_blocks_per_seq, sl.data(),
+                                   qsl.data(), num_seqs, num_q_tokens,
+                                   max_query_len, max_seq_len, num_blocks,
+                                   sm.empty() ? nullptr : sm.data(),
+                                   (int64_t)sm.size());
+}
+
+}  // extern "C"

@@ -1,0 +1,158 @@
+// Internal declarations shared by the HIP kernels and the C-ABI host code of
+// libpa.so.  gfx950 (CDNA4) only: 64-lane wavefronts, bf16 MFMA.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kBlock = 16;  // tokens per KV block
+
+// Work decomposition of pa_attend (see attend.hip).
+constexpr int kSplitDecode = 512;    // logical tokens per decode split
+constexpr int kSplitPrefill = 2048;  // logical tokens per prefill split
+// A prefill request is split along its keys only if it has fewer than this
+// many (q-tile x kv-head) work units on its own.
+constexpr int kPrefillUnsplitUnits = 512;
+constexpr int kDecodeColTiles = 1;   // 16 MFMA columns: up to 16/G tokens
+constexpr int kPrefillColTiles = 2;  // 32 MFMA columns: 32/G tokens
+constexpr int kMaxGroup = 16;        // query heads per kv head
+constexpr int kAttendThreads = 256;  // 4 independent waves per workgroup
+constexpr int kAttendWavesPerSimd = 2;
+
+enum ItemKind : int { kKindDecode = 0, kKindPrefill = 1 };
+
+// One unit of attention work for one kv head: a tile of consecutive query
+// tokens of one request against one logical key range of that request.
+struct WorkItem {
+  int32_t seq;      // request index b
+  int32_t tok0;     // global index of the tile's first query token
+  int32_t ntok;     // tokens in the tile
+  int32_t kind;     // ItemKind
+  int32_t kv0;      // first logical key (multiple of 32)
+  int32_t kv1;      // one past the last logical key
+  int32_t split;    // split index of this key range
+  int32_t pbase;    // partial slot of (tile token 0, split 0); -1 if unsplit
+};
+static_assert(sizeof(WorkItem) == 32, "WorkItem is two 16-byte loads");
+
+// Per query token: where its split-K partial results live.
+struct TokenSplit {
+  int32_t pbase;   // partial slot of split 0 (slot of split s = pbase + s)
+  int32_t nsplit;  // number of splits; 1 = written directly to out
+};
+
+// Workspace header, at offset 0 of the workspace.
+struct PlanHeader {
+  uint32_t work_counter;  // dynamic work queue head (zeroed by the plan)
+  uint32_t num_work;      // items * num_kv_heads
+  uint32_t num_items;
+  uint32_t error;         // bit0: capacity exceeded, bit1: bad request skipped
+};
+
+// Byte offsets of the workspace sections.
+struct WorkspaceLayout {
+  size_t items;         // WorkItem[max_items]
+  size_t token_split;   // TokenSplit[num_q_tokens]
+  size_t part_ml;       // float2[max_partials * Hq]  (running max, sum)
+  size_t part_acc;      // float[max_partials * Hq * D]
+  size_t total;
+  int64_t max_items;
+  int64_t max_partials;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Tokens per decode tile / prefill tile for group size G (<= 16).
+inline __host__ __device__ int decode_tile_tokens(int G) {
+  return (16 * kDecodeColTiles) / G;
+}
+inline __host__ __device__ int prefill_tile_tokens(int G) {
+  return (16 * kPrefillColTiles) / G;
+}
+
+inline WorkspaceLayout workspace_layout(int32_t num_seqs, int64_t num_q_tokens,
+                                        int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t max_query_len,
+                                        int32_t max_seq_len) {
+  WorkspaceLayout w{};
+  const int G = num_q_heads / num_kv_heads;
+  const int tq_d = decode_tile_tokens(G);
+  const int tq_p = prefill_tile_tokens(G);
+  const int64_t L = max_seq_len > 0 ? max_seq_len : 1;
+  const int64_t B = num_seqs;
+  const int64_t T = num_q_tokens;
+  const int64_t sd = cdiv64(L, kSplitDecode);
+  const int64_t sp = cdiv64(L, kSplitPrefill);
+  // decode-kind requests: one tile each; prefill-kind: <= T/tq_p + B tiles.
+  int64_t dec_tiles = B;
+  int64_t pre_tiles = (max_query_len > tq_d) ? (T / tq_p + B) : 0;
+  w.max_items = dec_tiles * sd + pre_tiles * sp;
+  if (w.max_items < 1) w.max_items = 1;
+  // partial slots: decode tokens <= min(T, B*tq_d), prefill tokens <= T
+  int64_t dec_tok = T < B * tq_d ? T : B * tq_d;
+  int64_t pre_tok = (max_query_len > tq_d) ? T : 0;
+  w.max_partials = dec_tok * sd + pre_tok * sp;
+  if (w.max_partials < 1) w.max_partials = 1;
+  size_t off = align256(sizeof(PlanHeader));
+  w.items = off;
+  off = align256(off + sizeof(WorkItem) * (size_t)w.max_items);
+  w.token_split = off;
+  off = align256(off + sizeof(TokenSplit) * (size_t)(T > 0 ? T : 1));
+  w.part_ml = off;
+  off = align256(off + sizeof(float) * 2 * (size_t)w.max_partials * num_q_heads);
+  w.part_acc = off;
+  off = align256(off + sizeof(float) * (size_t)w.max_partials * num_q_heads *
+                           (size_t)head_dim);
+  w.total = off;
+  return w;
+}
+
+// ---- launchers (defined in the .hip files) ---------------------------------
+
+hipError_t launch_write_kv(const uint16_t* k, const uint16_t* v,
+                           int64_t k_stride, int64_t v_stride,
+                           const int64_t* slot_mapping, int64_t num_tokens,
+                           int num_kv_heads, int head_dim, uint16_t* k_cache,
+                           uint16_t* v_cache, int64_t num_blocks,
+                           hipStream_t stream);
+
+hipError_t launch_gather_kv(const uint16_t* k_cache, const uint16_t* v_cache,
+                            int64_t num_blocks, const int32_t* block_tables,
+                            int32_t bt_stride, const int32_t* seq_lens,
+                            const int64_t* kv_start, int32_t num_seqs,
+                            int64_t total_rows, int num_kv_heads, int head_dim,
+                            uint16_t* k_out, uint16_t* v_out,
+                            hipStream_t stream);
+
+struct AttendArgs {
+  const uint16_t* q;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  int64_t num_blocks;
+  const int32_t* block_tables;
+  int32_t bt_stride;
+  const int32_t* seq_lens;
+  const int32_t* qsl;
+  int32_t num_seqs;
+  int64_t num_q_tokens;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t max_query_len;
+  int32_t max_seq_len;
+  float scale;
+  uint16_t* out;
+  void* workspace;
+  WorkspaceLayout ws;
+  int num_cus;
+};
+
+hipError_t launch_attend(const AttendArgs& a, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,168 @@
+"""C-ABI checks that need no GPU: libpa.so loads, exports every function
+include/pa.h declares, rejects bad arguments before touching the device, and
+its host-side metadata validator flags invalid content."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import workloads as W
+from paged_kv_cache_varlen_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        import paged_kv_cache_varlen_amd._build as b
+        b.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.pa_abi_version() == 1
+    assert lib.pa_status_string(0) == b"ok"
+    assert lib.pa_status_string(4) == b"workspace too small"
+
+
+def test_workspace_size(lib):
+    a = lib.pa_attend_workspace_size(64, 64, 32, 8, 128, 1, 4096)
+    b = lib.pa_attend_workspace_size(64, 64, 32, 8, 128, 1, 8192)
+    assert 0 < a < b
+    assert lib.pa_attend_workspace_size(64, 64, 32, 8, 96, 1, 4096) == 0   # head_dim
+    assert lib.pa_attend_workspace_size(64, 64, 30, 8, 128, 1, 4096) == 0  # Hq % Hkv
+    assert lib.pa_attend_workspace_size(64, 64, 64, 2, 128, 1, 4096) == 0  # G > 16
+    assert lib.pa_attend_workspace_size(-1, 64, 32, 8, 128, 1, 4096) == 0
+
+
+FAKE = 1 << 20  # a non-NULL, 256-aligned pointer value: never dereferenced
+
+
+def attend_args(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, nb=10, bt=FAKE, mb=4, sl=FAKE, qsl=FAKE,
+             B=2, T=2, Hq=8, Hkv=2, D=128, mq=1, ms=64, scale=0.1, out=FAKE,
+             ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(over)
+    return [a[k] for k in ("q", "k", "v", "nb", "bt", "mb", "sl", "qsl", "B", "T",
+                           "Hq", "Hkv", "D", "mq", "ms", "scale", "out", "ws",
+                           "wsb", "stream")]
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), _lib.PA_ERR_NULL),
+    (dict(out=None), _lib.PA_ERR_NULL),
+    (dict(D=96), _lib.PA_ERR_UNSUPPORTED),
+    (dict(Hq=6, Hkv=4), _lib.PA_ERR_SHAPE),
+    (dict(Hq=64, Hkv=2), _lib.PA_ERR_UNSUPPORTED),
+    (dict(T=-1), _lib.PA_ERR_SHAPE),
+    (dict(ws=None), _lib.PA_ERR_WORKSPACE),
+    (dict(wsb=100), _lib.PA_ERR_WORKSPACE),
+    (dict(ws=FAKE + 16), _lib.PA_ERR_WORKSPACE),
+    (dict(q=FAKE + 2), _lib.PA_ERR_SHAPE),
+])
+def test_attend_rejects_bad_arguments(lib, over, status):
+    assert lib.pa_attend(*attend_args(**over)) == status
+    assert lib.pa_last_error() != b""
+
+
+def test_attend_empty_batch_is_ok(lib):
+    assert lib.pa_attend(*attend_args(T=0, q=None, out=None)) == _lib.PA_OK
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, FAKE, 256, 256, FAKE, 4, 2, 96, FAKE, FAKE, 8, None), _lib.PA_ERR_UNSUPPORTED),
+    ((None, FAKE, 256, 256, FAKE, 4, 2, 128, FAKE, FAKE, 8, None), _lib.PA_ERR_NULL),
+    ((FAKE, FAKE, 100, 256, FAKE, 4, 2, 128, FAKE, FAKE, 8, None), _lib.PA_ERR_SHAPE),
+    ((FAKE, FAKE, 256, 256, FAKE, -4, 2, 128, FAKE, FAKE, 8, None), _lib.PA_ERR_SHAPE),
+    ((FAKE, FAKE, 256, 256, FAKE, 0, 2, 128, None, None, 8, None), _lib.PA_OK),
+])
+def test_write_kv_argument_checks(lib, args, status):
+    assert lib.pa_write_kv(*args) == status
+
+
+def test_gather_argument_checks(lib):
+    st = lib.pa_gather_kv(None, FAKE, 8, FAKE, 4, FAKE, FAKE, 2, 10, 2, 64, FAKE,
+                          FAKE, None)
+    assert st == _lib.PA_ERR_NULL
+    st = lib.pa_gather_kv(FAKE, FAKE, 8, FAKE, 4, FAKE, FAKE, 2, 10, 2, 80, FAKE,
+                          FAKE, None)
+    assert st == _lib.PA_ERR_UNSUPPORTED
+
+
+# ---- host metadata validator ---------------------------------------------------------
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def validate(lib, w, bt=None, sl=None, qsl=None, slots=None, mq=None, ms=None,
+             nb=None):
+    bt = np.ascontiguousarray(w.block_tables if bt is None else bt, np.int32)
+    sl = np.ascontiguousarray(w.seq_lens if sl is None else sl, np.int32)
+    qsl = np.ascontiguousarray(w.query_start_loc if qsl is None else qsl, np.int32)
+    slots = np.ascontiguousarray(w.new_slots if slots is None else slots, np.int64)
+    return lib.pa_validate_metadata_host(
+        _p(bt), bt.shape[1], _p(sl), _p(qsl), sl.shape[0], int(qsl[-1]),
+        w.max_query_len if mq is None else mq, w.max_seq_len if ms is None else ms,
+        w.num_blocks if nb is None else nb, _p(slots), slots.shape[0])
+
+
+@pytest.fixture(scope="module")
+def wl():
+    return W.make_workload("v", [1, 17, 40, 33, 64, 5], [1, 1, 7, 33, 3, 0], 8, 2,
+                           64, seed=0)
+
+
+def test_validator_accepts_generated_metadata(lib, wl):
+    assert validate(lib, wl) == _lib.PA_OK
+    allslots = np.concatenate([wl.fill_slots, wl.new_slots])
+    assert validate(lib, wl, slots=allslots) == _lib.PA_OK
+    for k in (1, 2):
+        w = W.make_config(k)
+        assert validate(lib, w, slots=np.concatenate([w.fill_slots, w.new_slots])) == 0
+
+
+def test_validator_rejects_bad_content(lib, wl):
+    M = _lib.PA_ERR_METADATA
+    bt = wl.block_tables.copy()
+    bt[2, 1] = wl.num_blocks
+    assert validate(lib, wl, bt=bt) == M
+    bt = wl.block_tables.copy()
+    bt[4, 0] = -3
+    assert validate(lib, wl, bt=bt) == M
+    sl = wl.seq_lens.copy()
+    sl[3] = 20  # Q = 33 > L
+    assert validate(lib, wl, sl=sl) == M
+    qsl = wl.query_start_loc.copy()
+    qsl[2], qsl[3] = qsl[3], qsl[2]
+    assert validate(lib, wl, qsl=qsl) == M
+    slots = wl.new_slots.copy()
+    slots[1] = slots[0]
+    assert validate(lib, wl, slots=slots) == M
+    slots = wl.new_slots.copy()
+    slots[0] = wl.num_blocks * 16
+    assert validate(lib, wl, slots=slots) == M
+    assert validate(lib, wl, ms=50) == M   # L = 64 > max_seq_len
+    assert validate(lib, wl, mq=3) == M    # Q = 33 > max_query_len
+    bt = wl.block_tables[:, :2].copy()     # row too short for L = 64
+    assert validate(lib, wl, bt=bt) == M
+    assert "request" in lib.pa_last_error().decode()

@@ -19,7 +19,8 @@ What it builds, and where the pages state it:
     equal to the number of tables that hold them (same Aside; "Deep Dive -
     vLLM", "Block pool, prefix cache, and eviction").
 
-Values are N(0, 1) float32 draws from numpy's default_rng rounded to bf16
+Values are N(0, 1) float32 draws from numpy's default_rng (one generator per
+chunk of 2**22 values, keyed by (data seed, tensor, chunk)) rounded to bf16
 (round to nearest even) and carried as uint16 bit patterns.  Workload shapes
 follow the synthetic configurations described in the design notes (Llama-3-8B
 and 70B-class GQA heads, 16-token blocks, decode, mixed chunked-prefill,
@@ -28,9 +29,11 @@ are not available, so these stand in for them.
 """
 from __future__ import annotations
 
+import os
 from collections import Counter
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
-from typing import Dict, List, Optional, Sequence
+from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -57,14 +60,38 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32)
 
 
-def normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
-    """N(0,1) draws rounded to bf16, as uint16 bits."""
+_CHUNK = 1 << 22
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def normal_bf16(key: Tuple[int, ...], shape) -> np.ndarray:
+    """N(0,1) float32 draws rounded to bf16, as uint16 bits.
+
+    Chunk i of 2**22 values comes from np.random.default_rng(key + (i,)), so
+    the result depends only on the key and the shape, not on the number of
+    threads that fill it."""
     n = int(np.prod(shape))
     out = np.empty(n, np.uint16)
-    step = 1 << 24
-    for s in range(0, n, step):
-        e = min(n, s + step)
+
+    def fill(i):
+        s, e = i * _CHUNK, min(n, (i + 1) * _CHUNK)
+        rng = np.random.default_rng(tuple(key) + (i,))
         out[s:e] = f32_to_bf16_bits(rng.standard_normal(e - s, dtype=np.float32))
+
+    nchunks = (n + _CHUNK - 1) // _CHUNK
+    if nchunks <= 1:
+        for i in range(nchunks):
+            fill(i)
+    else:
+        with ThreadPoolExecutor(max_workers=_threads()) as ex:
+            list(ex.map(fill, range(nchunks)))
     return out.reshape(shape)
 
 
@@ -226,7 +253,6 @@ def make_workload(name: str, seq_lens: Sequence[int], query_lens: Sequence[int],
     assert shared_prefix % BLOCK_SIZE == 0
     assert np.all(seq_lens >= shared_prefix)
     seeds = {"data": 1000 + seed, "tables": 3000 + seed}
-    rng_data = np.random.default_rng(seeds["data"])
     rng_tab = np.random.default_rng(seeds["tables"])
 
     nblk = [blocks_needed(int(L)) for L in seq_lens]
@@ -258,24 +284,17 @@ def make_workload(name: str, seq_lens: Sequence[int], query_lens: Sequence[int],
     kv_start = np.zeros(B + 1, np.int64)
     np.cumsum(seq_lens.astype(np.int64), out=kv_start[1:])
     total = int(kv_start[-1])
+    k_dense = normal_bf16((seeds["data"], 0), (total, Hkv, D))
+    v_dense = normal_bf16((seeds["data"], 1), (total, Hkv, D))
     if shared_prefix:
-        pk = normal_bf16(rng_data, (shared_prefix, Hkv, D))
-        pv = normal_bf16(rng_data, (shared_prefix, Hkv, D))
-        k_dense = np.empty((total, Hkv, D), np.uint16)
-        v_dense = np.empty((total, Hkv, D), np.uint16)
-        for b in range(B):
-            s0, L = int(kv_start[b]), int(seq_lens[b])
-            k_dense[s0:s0 + shared_prefix] = pk
-            v_dense[s0:s0 + shared_prefix] = pv
-            rest = L - shared_prefix
-            k_dense[s0 + shared_prefix:s0 + L] = normal_bf16(rng_data, (rest, Hkv, D))
-            v_dense[s0 + shared_prefix:s0 + L] = normal_bf16(rng_data, (rest, Hkv, D))
-    else:
-        k_dense = normal_bf16(rng_data, (total, Hkv, D))
-        v_dense = normal_bf16(rng_data, (total, Hkv, D))
+        # every sequence's first shared_prefix tokens carry sequence 0's K/V
+        for b in range(1, B):
+            s0 = int(kv_start[b])
+            k_dense[s0:s0 + shared_prefix] = k_dense[:shared_prefix]
+            v_dense[s0:s0 + shared_prefix] = v_dense[:shared_prefix]
     qsl = query_start_loc(query_lens)
     T = int(qsl[-1])
-    q = normal_bf16(rng_data, (T, num_q_heads, D))
+    q = normal_bf16((seeds["data"], 2), (T, num_q_heads, D))
 
     fill_rows, fill_slots, new_rows, new_slots = [], [], [], []
     for b in range(B):
