@@ -85,14 +85,15 @@ class Runner:
         self.stream = torch.cuda.current_stream()
 
     def step(self, i, ev=None):
-        pa, u, w = self.pa, self.u, self.w
+        """write_kv + plan + attention for one layer; the events bracket the
+        attention kernel alone."""
+        pa, u = self.pa, self.u
         kc, vc = self.layers[i % len(self.layers)]
         pa.write_kv(u.k_new, u.v_new, u.new_slots, kc, vc)
+        u.plan()
         if ev is not None:
             ev[0].record(self.stream)
-        pa.attend(u.q, kc, vc, u.block_tables, u.seq_lens, u.qsl, w.scale,
-                  w.max_query_len, w.max_seq_len, num_kv_heads=w.num_kv_heads,
-                  out=u.out, workspace=u.workspace)
+        u.attend(k_cache=kc, v_cache=vc, planned=True)
         if ev is not None:
             ev[1].record(self.stream)
 
@@ -182,7 +183,9 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None, "kernel": "pa_attend (plan + attend + merge)",
+            "traffic": None, "kernel": "attend_decode_kernel<128>" if
+            w.max_query_len <= 16 // (w.num_q_heads // w.num_kv_heads)
+            else "attend_mixed_kernel<128>",
             "attend_ms": round(attend_ms, 5),
             "algorithmic_bytes": alg["attend_bytes"]},
     }

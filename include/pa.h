@@ -168,7 +168,8 @@ size_t pa_attend_workspace_size(int32_t num_seqs, int64_t num_q_tokens,
  *   out              device bf16 [num_q_tokens][num_q_heads][head_dim]
  *   workspace        device buffer of >= pa_attend_workspace_size(...) bytes,
  *                    256-byte aligned; contents need no initialisation and
- *                    are scratch after the call
+ *                    hold the work plan and split-K partials after the call.
+ *                    Calls that overlap in time must use distinct workspaces.
  *   num_q_heads % num_kv_heads == 0, num_q_heads/num_kv_heads <= 16,
  *   head_dim 64 or 128.
  *
@@ -189,6 +190,42 @@ pa_status pa_attend(const void *q, const void *k_cache, const void *v_cache,
                     int32_t max_query_len, int32_t max_seq_len, float scale,
                     void *out, void *workspace, size_t workspace_bytes,
                     void *stream);
+
+/*
+ * pa_attend_plan + pa_attend_planned - pa_attend in two calls, so that one
+ * plan serves every layer of a forward step (the metadata is the same for all
+ * layers; "Inside vLLM", Step 4c: the runner builds query_start_loc and the
+ * block tables once per step).
+ *
+ * pa_attend_plan enqueues only the work-plan kernel: it reads the metadata
+ * and writes the work list into `workspace`.  pa_attend_planned enqueues only
+ * the attention kernel over the plan found in `workspace`.  Arguments mean
+ * the same as for pa_attend.  Between the two calls the workspace and the
+ * metadata arrays must not change, and every argument that pa_attend_plan
+ * also takes must be passed with the same value; a plan made for other sizes
+ * is detected on the device and the attention kernel then writes nothing
+ * (out keeps its contents).  pa_attend == pa_attend_plan + pa_attend_planned.
+ */
+pa_status pa_attend_plan(const int32_t *block_tables,
+                         int32_t max_blocks_per_seq, const int32_t *seq_lens,
+                         const int32_t *query_start_loc, int32_t num_seqs,
+                         int64_t num_q_tokens, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim,
+                         int32_t max_query_len, int32_t max_seq_len,
+                         void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+pa_status pa_attend_planned(const void *q, const void *k_cache,
+                            const void *v_cache, int64_t num_blocks,
+                            const int32_t *block_tables,
+                            int32_t max_blocks_per_seq,
+                            const int32_t *seq_lens,
+                            const int32_t *query_start_loc, int32_t num_seqs,
+                            int64_t num_q_tokens, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim,
+                            int32_t max_query_len, int32_t max_seq_len,
+                            float scale, void *out, void *workspace,
+                            size_t workspace_bytes, void *stream);
 
 /*
  * pa_gather_kv - logical gather through the block tables (a checking aid).

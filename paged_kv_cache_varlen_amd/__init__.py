@@ -115,17 +115,8 @@ def alloc_workspace(num_seqs, num_q_tokens, num_q_heads, num_kv_heads, head_dim,
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def attend(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-           block_tables: torch.Tensor, seq_lens: torch.Tensor,
-           query_start_loc: torch.Tensor, scale: float, max_query_len: int,
-           max_seq_len: int, num_kv_heads: Optional[int] = None,
-           out: Optional[torch.Tensor] = None,
-           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Paged varlen causal attention of every query row of a mixed batch.
-
-    q [T][Hq][D] bf16; block_tables [B][max_blocks] int32; seq_lens [B] int32;
-    query_start_loc [B+1] int32; pools from alloc_pool.  Returns out
-    [T][Hq][D] bf16 (written in place when ``out`` is given)."""
+def _attend_args(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
+                 num_kv_heads, out, workspace, max_query_len, max_seq_len):
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
                  (block_tables, "block_tables"), (seq_lens, "seq_lens"),
                  (query_start_loc, "query_start_loc")):
@@ -144,6 +135,8 @@ def attend(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
             raise ValueError("pass num_kv_heads or a [blocks][kv_heads][16*D] pool")
         num_kv_heads = k_cache.shape[1]
     nb = _pool_blocks(k_cache, num_kv_heads, D)
+    if _pool_blocks(v_cache, num_kv_heads, D) != nb:
+        raise ValueError("k_cache and v_cache differ in size")
     if block_tables.dim() != 2 or not block_tables.is_contiguous():
         raise ValueError("block_tables must be contiguous [num_seqs][max_blocks]")
     B = block_tables.shape[0]
@@ -159,14 +152,55 @@ def attend(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     if workspace is None:
         workspace = alloc_workspace(B, T, Hq, num_kv_heads, D, max_query_len,
                                     max_seq_len, device=q.device)
+    return T, Hq, D, num_kv_heads, nb, B, out, workspace
+
+
+def attend(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+           block_tables: torch.Tensor, seq_lens: torch.Tensor,
+           query_start_loc: torch.Tensor, scale: float, max_query_len: int,
+           max_seq_len: int, num_kv_heads: Optional[int] = None,
+           out: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None,
+           planned: bool = False) -> torch.Tensor:
+    """Paged varlen causal attention of every query row of a mixed batch.
+
+    q [T][Hq][D] bf16; block_tables [B][max_blocks] int32; seq_lens [B] int32;
+    query_start_loc [B+1] int32; pools from alloc_pool.  Returns out
+    [T][Hq][D] bf16 (written in place when ``out`` is given).  With
+    planned=True the work plan already in ``workspace`` (from attend_plan with
+    the same metadata) is used and only the attention kernel is enqueued."""
+    T, Hq, D, Hkv, nb, B, out, workspace = _attend_args(
+        q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
+        num_kv_heads, out, workspace, max_query_len, max_seq_len)
     lib = _lib.load()
-    st = lib.pa_attend(_ptr(q), _ptr(k_cache), _ptr(v_cache), nb,
-                       _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens),
-                       _ptr(query_start_loc), B, T, Hq, num_kv_heads, D,
-                       int(max_query_len), int(max_seq_len), float(scale),
-                       _ptr(out), _ptr(workspace), workspace.numel(), _stream(q))
-    _lib.check(st, "pa_attend")
+    fn = lib.pa_attend_planned if planned else lib.pa_attend
+    st = fn(_ptr(q), _ptr(k_cache), _ptr(v_cache), nb, _ptr(block_tables),
+            block_tables.shape[1], _ptr(seq_lens), _ptr(query_start_loc), B, T,
+            Hq, Hkv, D, int(max_query_len), int(max_seq_len), float(scale),
+            _ptr(out), _ptr(workspace), workspace.numel(), _stream(q))
+    _lib.check(st, "pa_attend_planned" if planned else "pa_attend")
     return out
+
+
+def attend_plan(block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                query_start_loc: torch.Tensor, num_q_tokens: int,
+                num_q_heads: int, num_kv_heads: int, head_dim: int,
+                max_query_len: int, max_seq_len: int,
+                workspace: torch.Tensor) -> None:
+    """Enqueue only the work plan of pa_attend into ``workspace``; follow
+    with attend(..., planned=True) for each layer that shares the metadata."""
+    for t, n in ((block_tables, "block_tables"), (seq_lens, "seq_lens"),
+                 (query_start_loc, "query_start_loc"), (workspace, "workspace")):
+        _need_cuda(t, n)
+    B = block_tables.shape[0]
+    lib = _lib.load()
+    st = lib.pa_attend_plan(_ptr(block_tables), block_tables.shape[1],
+                            _ptr(seq_lens), _ptr(query_start_loc), B,
+                            int(num_q_tokens), int(num_q_heads),
+                            int(num_kv_heads), int(head_dim), int(max_query_len),
+                            int(max_seq_len), _ptr(workspace), workspace.numel(),
+                            _stream(workspace))
+    _lib.check(st, "pa_attend_plan")
 
 
 def gather_kv(k_cache: torch.Tensor, v_cache: torch.Tensor,

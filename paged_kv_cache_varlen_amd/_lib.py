@@ -26,6 +26,10 @@ SIGNATURES = {
     "pa_attend_workspace_size": (SZ, [I32, I64, I32, I32, I32, I32, I32]),
     "pa_attend": (STATUS, [P, P, P, I64, P, I32, P, P, I32, I64, I32, I32, I32,
                            I32, I32, F32, P, P, SZ, P]),
+    "pa_attend_plan": (STATUS, [P, I32, P, P, I32, I64, I32, I32, I32, I32, I32,
+                                P, SZ, P]),
+    "pa_attend_planned": (STATUS, [P, P, P, I64, P, I32, P, P, I32, I64, I32,
+                                   I32, I32, I32, I32, F32, P, P, SZ, P]),
     "pa_gather_kv": (STATUS, [P, P, I64, P, I32, P, P, I32, I64, I32, I32, P, P,
                               P]),
     "pa_validate_metadata_host": (STATUS, [P, I32, P, P, I32, I64, I32, I32, I64,

@@ -9,23 +9,33 @@
 // K_j/V_j read from block block_tables[b][j/16], slot j%16, of the kv head
 // h / G shared by the G query heads of its group.
 //
-// Structure (three kernels on one stream, no host synchronisation):
+// Two kernels on one stream, no host synchronisation:
 //   plan    one workgroup turns seq_lens / query_start_loc into a work list of
 //           (request, query tile, logical key range) items, prefill items
-//           first, and zeroes the work-queue head;
+//           first, and zeroes the work-queue head and the arrival counters;
 //   attend  persistent waves pull (item, kv head) units from the queue.  One
-//           wave owns one unit: the query tile's columns (token x head of the
-//           group) are MFMA columns, 16 keys (one block) are MFMA rows, so
-//           every K/V tile is read once for all G heads.  Scores S^T = K Q^T
-//           and the PV product O^T = V^T P^T run on v_mfma_f32_16x16x32_bf16;
-//           the online softmax (running max / sum per column) is fp32 with
-//           wavefront shuffles.  Items whose key range is the whole causal
-//           range write bf16 out directly, split items write fp32 partials;
-//   merge   log-sum-exp combination of the split partials in split order.
+//           wave owns one unit.  The query tile's columns (token x head of
+//           the group) are MFMA columns and the 16 keys of a block are MFMA
+//           rows, so each K/V tile is read once for all G heads of the group.
+//           Scores S^T = K Q^T run on v_mfma_f32_16x16x32_bf16; the online
+//           softmax (running max and sum per column) is fp32, reduced across
+//           the wave with shuffles; O^T = V^T P^T runs on bf16 MFMA with P
+//           taken straight from the score registers.  Units covering a whole
+//           causal range write bf16 out; split units write fp32 partials and
+//           the last split of a tile to arrive merges all of them (log-sum-exp
+//           in split order) into out.
 //
 // Reduction order depends only on (Q_b, L_b) and logical key positions, so
-// results are bitwise independent of physical block ids, of shared blocks and
-// of the rest of the batch.
+// results are bitwise independent of physical block ids, of shared blocks, of
+// which wave ran which unit and of the rest of the batch.
+//
+// The kernel template has two instantiations: a decode-only one (batches whose
+// max_query_len fits a decode tile; fewer registers, more resident waves) and
+// the unified one that serves decode and prefill items of a mixed batch in the
+// same launch.
+#include <mutex>
+#include <vector>
+
 #include "pa_device.h"
 
 namespace pa {
@@ -35,7 +45,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -59,7 +69,7 @@ struct AttendParams {
   uint16_t* out;
   PlanHeader* hdr;
   WorkItem* items;
-  TokenSplit* token_split;
+  uint32_t* counters;
   float2* part_ml;
   float* part_acc;
   int64_t max_items;
@@ -70,19 +80,33 @@ struct AttendParams {
 // plan
 // ---------------------------------------------------------------------------
 
+// Hash of the arguments a plan depends on; the attention kernel runs only on
+// a plan made for its own arguments.
+__device__ __forceinline__ uint32_t plan_signature(const AttendParams& P) {
+  uint32_t h = 2166136261u;
+  const int32_t v[9] = {P.num_seqs, P.num_q_tokens, P.Hq, P.Hkv,
+                        P.max_query_len, P.max_seq_len, P.bt_stride,
+                        (int32_t)P.max_items, (int32_t)P.max_partials};
+#pragma unroll
+  for (int i = 0; i < 9; ++i) h = (h ^ (uint32_t)v[i]) * 16777619u;
+  return h;
+}
+
 constexpr int kPlanThreads = 1024;
+constexpr int kMaxCoop = 64;  // unsplit prefill requests emitted by all threads
 
 struct SeqCounts {
-  int kind;      // -1: nothing to do
+  int kind;         // -1: nothing to do
   int ntiles;
-  int tq;        // tokens per tile
-  int splitlen;  // logical tokens per split (0: unsplit)
+  int tq;           // tokens per tile
+  int splitlen;     // logical tokens per split; 0: unsplit prefill
   int items;
   int partials;
+  int split_tiles;  // tiles with more than one split
 };
 
 __device__ SeqCounts seq_counts(const AttendParams& P, int b) {
-  SeqCounts c{-1, 0, 0, 0, 0, 0};
+  SeqCounts c{-1, 0, 0, 0, 0, 0, 0};
   const int q0 = P.qsl[b], q1 = P.qsl[b + 1];
   const int Q = q1 - q0, L = P.seq_lens[b];
   const bool ok = q0 >= 0 && Q >= 0 && q1 <= P.num_q_tokens && Q <= L &&
@@ -93,8 +117,7 @@ __device__ SeqCounts seq_counts(const AttendParams& P, int b) {
     return c;
   }
   if (Q == 0) return c;
-  const int tq_d = decode_tile_tokens(P.G);
-  if (Q <= tq_d) {
+  if (Q <= decode_tile_tokens(P.G)) {
     c.kind = kKindDecode;
     c.ntiles = 1;
     c.tq = Q;
@@ -102,18 +125,25 @@ __device__ SeqCounts seq_counts(const AttendParams& P, int b) {
     const int ns = (L + kSplitDecode - 1) / kSplitDecode;
     c.items = ns;
     c.partials = ns > 1 ? Q * ns : 0;
+    c.split_tiles = ns > 1 ? 1 : 0;
     return c;
   }
   c.kind = kKindPrefill;
   c.tq = prefill_tile_tokens(P.G);
   c.ntiles = (Q + c.tq - 1) / c.tq;
-  c.splitlen = (c.ntiles * P.Hkv < kPrefillUnsplitUnits) ? kSplitPrefill : 0;
+  if (c.ntiles * P.Hkv >= kPrefillUnsplitUnits) {
+    c.splitlen = 0;
+    c.items = c.ntiles;
+    return c;
+  }
+  c.splitlen = kSplitPrefill;
   for (int t = 0; t < c.ntiles; ++t) {
     const int ntok = min(c.tq, Q - t * c.tq);
     const int pmax1 = L - Q + t * c.tq + ntok;
-    const int ns = c.splitlen ? (pmax1 + c.splitlen - 1) / c.splitlen : 1;
+    const int ns = (pmax1 + c.splitlen - 1) / c.splitlen;
     c.items += ns;
     c.partials += ns > 1 ? ntok * ns : 0;
+    c.split_tiles += ns > 1 ? 1 : 0;
   }
   return c;
 }
@@ -148,105 +178,140 @@ __device__ int block_scan(int x, int* lds, int* total) {
   return res;
 }
 
+__device__ __forceinline__ void put_item(const AttendParams& P, int idx, int b,
+                                         int tok0, int ntok, int kind, int kv0,
+                                         int kv1, int split, int nsplit,
+                                         int pbase, int counter) {
+  WorkItem it;
+  it.seq = b;
+  it.tok0 = tok0;
+  it.ntok = ntok;
+  it.kind = kind;
+  it.kv0 = kv0;
+  it.kv1 = kv1;
+  it.split = split;
+  it.nsplit = nsplit;
+  it.pbase = pbase;
+  it.counter = counter;
+#pragma unroll
+  for (int i = 0; i < 6; ++i) it.pad[i] = 0;
+  P.items[idx] = it;
+}
+
+// Items of one request, emitted by one thread (decode requests and prefill
+// requests with split key ranges, which have few tiles).
 __device__ void emit_seq(const AttendParams& P, int b, const SeqCounts& c,
-                         int ibase, int pbase) {
+                         int ibase, int pbase, int cbase) {
   const int q0 = P.qsl[b];
   const int Q = P.qsl[b + 1] - q0, L = P.seq_lens[b];
   if (c.kind == kKindDecode) {
     const int ns = c.items;
-    const int pb = ns > 1 ? pbase : -1;
-    for (int s = 0; s < ns; ++s) {
-      WorkItem it;
-      it.seq = b;
-      it.tok0 = q0;
-      it.ntok = Q;
-      it.kind = kKindDecode;
-      it.kv0 = s * kSplitDecode;
-      it.kv1 = min(L, (s + 1) * kSplitDecode);
-      it.split = s;
-      it.pbase = pb;
-      P.items[ibase + s] = it;
-    }
-    for (int k = 0; k < Q; ++k)
-      P.token_split[q0 + k] = TokenSplit{pb < 0 ? -1 : pb + k * ns, ns};
+    for (int s = 0; s < ns; ++s)
+      put_item(P, ibase + s, b, q0, Q, kKindDecode, s * kSplitDecode,
+               min(L, (s + 1) * kSplitDecode), s, ns, ns > 1 ? pbase : -1,
+               ns > 1 ? cbase : -1);
     return;
   }
-  // prefill: longest tiles (latest tokens) first
-  int icur = ibase, pcur = pbase;
+  // split prefill: longest tiles (latest tokens) first
+  int icur = ibase, pcur = pbase, ccur = cbase;
   for (int t = c.ntiles - 1; t >= 0; --t) {
     const int ntok = min(c.tq, Q - t * c.tq);
     const int pmax1 = L - Q + t * c.tq + ntok;
-    const int ns = c.splitlen ? (pmax1 + c.splitlen - 1) / c.splitlen : 1;
-    const int span = c.splitlen ? c.splitlen : pmax1;
+    const int ns = (pmax1 + c.splitlen - 1) / c.splitlen;
     const int pb = ns > 1 ? pcur : -1;
-    if (ns > 1) pcur += ntok * ns;
-    for (int s = 0; s < ns; ++s) {
-      WorkItem it;
-      it.seq = b;
-      it.tok0 = q0 + t * c.tq;
-      it.ntok = ntok;
-      it.kind = kKindPrefill;
-      it.kv0 = s * span;
-      it.kv1 = min(pmax1, (s + 1) * span);
-      it.split = s;
-      it.pbase = pb;
-      P.items[icur++] = it;
+    const int cb = ns > 1 ? ccur : -1;
+    if (ns > 1) {
+      pcur += ntok * ns;
+      ccur += 1;
     }
-    for (int k = 0; k < ntok; ++k)
-      P.token_split[q0 + t * c.tq + k] =
-          TokenSplit{pb < 0 ? -1 : pb + k * ns, ns};
+    for (int s = 0; s < ns; ++s)
+      put_item(P, icur++, b, q0 + t * c.tq, ntok, kKindPrefill,
+               s * c.splitlen, min(pmax1, (s + 1) * c.splitlen), s, ns, pb, cb);
   }
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttendParams P) {
   __shared__ int lds[kPlanThreads / 64 + 1];
+  __shared__ int coop_n;
+  __shared__ int coop_b[kMaxCoop];
+  __shared__ int coop_base[kMaxCoop];
   const int tid = threadIdx.x;
   if (tid == 0) {
     P.hdr->work_counter = 0;
     P.hdr->error = 0;
+    P.hdr->signature = plan_signature(P);
+    coop_n = 0;
   }
-  // Tokens of skipped requests keep this record: the merge leaves them alone.
-  for (int t = tid; t < P.num_q_tokens; t += kPlanThreads)
-    P.token_split[t] = TokenSplit{-1, 1};
-  __syncthreads();
-  // sweep 1: total prefill items, so that decode items go after them
-  int pre_total = 0, all_items = 0, all_partials = 0;
+  // sweep 1: totals (prefill items go first, decode items after them)
+  int pre_total = 0, all_items = 0, all_partials = 0, all_split = 0;
   for (int base = 0; base < P.num_seqs; base += kPlanThreads) {
     const int b = base + tid;
-    SeqCounts c{-1, 0, 0, 0, 0, 0};
+    SeqCounts c{-1, 0, 0, 0, 0, 0, 0};
     if (b < P.num_seqs) c = seq_counts(P, b);
-    int t0, t1, t2;
+    int t0, t1, t2, t3;
     block_scan(c.kind == kKindPrefill ? c.items : 0, lds, &t0);
     block_scan(c.items, lds, &t1);
     block_scan(c.partials, lds, &t2);
+    block_scan(c.split_tiles, lds, &t3);
     pre_total += t0;
     all_items += t1;
     all_partials += t2;
+    all_split += t3;
   }
   const bool fits = all_items <= P.max_items && all_partials <= P.max_partials;
+  const int ncounters = fits ? all_split * P.Hkv : 0;
+  for (int i = tid; i < ncounters; i += kPlanThreads) P.counters[i] = 0u;
   // sweep 2: write
-  int pre_carry = 0, dec_carry = 0, part_carry = 0;
+  int pre_carry = 0, dec_carry = 0, part_carry = 0, split_carry = 0;
   for (int base = 0; base < P.num_seqs; base += kPlanThreads) {
     const int b = base + tid;
-    SeqCounts c{-1, 0, 0, 0, 0, 0};
+    SeqCounts c{-1, 0, 0, 0, 0, 0, 0};
     if (b < P.num_seqs) c = seq_counts(P, b);
-    int tp, td, tpart;
+    int tp, td, tpart, tsplit;
     const int ep = block_scan(c.kind == kKindPrefill ? c.items : 0, lds, &tp);
     const int ed = block_scan(c.kind == kKindDecode ? c.items : 0, lds, &td);
     const int epart = block_scan(c.partials, lds, &tpart);
+    const int esplit = block_scan(c.split_tiles, lds, &tsplit);
     if (fits && c.kind >= 0) {
       const int ibase = c.kind == kKindPrefill ? pre_carry + ep
                                                : pre_total + dec_carry + ed;
-      emit_seq(P, b, c, ibase, part_carry + epart);
+      bool self = true;
+      if (c.kind == kKindPrefill && c.splitlen == 0) {
+        const int k = atomicAdd(&coop_n, 1);
+        if (k < kMaxCoop) {
+          coop_b[k] = b;
+          coop_base[k] = ibase;
+          self = false;
+        }
+      }
+      if (self) emit_seq(P, b, c, ibase, part_carry + epart, split_carry + esplit);
     }
     pre_carry += tp;
     dec_carry += td;
     part_carry += tpart;
+    split_carry += tsplit;
+  }
+  __syncthreads();
+  // unsplit prefill requests: every thread emits some of their tiles
+  const int ncoop = min(coop_n, kMaxCoop);
+  for (int k = 0; k < ncoop; ++k) {
+    const int b = coop_b[k];
+    const int q0 = P.qsl[b];
+    const int Q = P.qsl[b + 1] - q0, L = P.seq_lens[b];
+    const int tq = prefill_tile_tokens(P.G);
+    const int ntiles = (Q + tq - 1) / tq;
+    for (int t = tid; t < ntiles; t += kPlanThreads) {
+      const int ntok = min(tq, Q - t * tq);
+      const int pmax1 = L - Q + t * tq + ntok;
+      put_item(P, coop_base[k] + (ntiles - 1 - t), b, q0 + t * tq, ntok,
+               kKindPrefill, 0, pmax1, 0, 1, -1, -1);
+    }
   }
   if (tid == 0) {
     P.hdr->num_items = fits ? (uint32_t)all_items : 0u;
     P.hdr->num_work = fits ? (uint32_t)all_items * (uint32_t)P.Hkv : 0u;
-    if (!fits) P.hdr->error |= 1u;
+    P.hdr->num_counters = (uint32_t)ncounters;
+    if (!fits) atomicOr(&P.hdr->error, 1u);
   }
 }
 
@@ -265,37 +330,27 @@ __device__ __forceinline__ bf16x8 zero8() {
   return z;
 }
 
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int D>
-struct KVPair {
-  bf16x8 k[2][D / 32];  // block a, block b: K rows in MFMA operand order
-  bf16x8 v[2][D / 32];  // V^T rows: lanes' 4 keys at dims d and d + D/2
-};
+__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+      __builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
 
-// One (item, kv head) unit on one wave.  CT = MFMA column tiles of 16;
-// PIPE = 2 keeps the next block pair's loads in flight while the current pair
-// is computed, PIPE = 1 loads and computes one pair at a time.
-template <int D, int CT, int PIPE>
-__device__ __forceinline__ void run_item(const AttendParams& P,
-                                         const WorkItem& it, int kvh,
-                                         int lane) {
-  constexpr int KC = D / 32;  // 32-dim chunks = MFMA k-steps for QK^T
-  constexpr int NT = D / 16;  // 16-dim output tiles for PV
+// Query operand and column positions of a unit.  Column c of tile ct is
+// token c / G, head c % G of the kv head's group; lane (r, g) holds dims
+// 32k + 8g .. +7 of column r for k-step k.
+template <int D, int CT>
+__device__ __forceinline__ void load_query(const AttendParams& P,
+                                           const WorkItem& it, int kvh,
+                                           int lane, int posbase,
+                                           bf16x8 (&qop)[CT][D / 32],
+                                           int (&cpos)[CT]) {
   const int r = lane & 15, g = lane >> 4;
-  const int b = it.seq;
-  const int L = P.seq_lens[b];
-  const int q0 = P.qsl[b];
-  const int Q = P.qsl[b + 1] - q0;
   const int G = P.G;
-  const int posbase = L - Q + (it.tok0 - q0);  // position of tile token 0
   const int ncols = it.ntok * G;
-
-  // Q^T operand: column = (token, head-in-group); lane holds 8 dims.
-  bf16x8 qop[CT][KC];
-  int cpos[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
     const int col = ct * 16 + r;
@@ -307,12 +362,290 @@ __device__ __forceinline__ void run_item(const AttendParams& P,
       const uint16_t* qp =
           P.q + ((int64_t)(it.tok0 + tk) * P.Hq + kvh * G + hh) * D + 8 * g;
 #pragma unroll
-      for (int c = 0; c < KC; ++c) qop[ct][c] = load16(qp + 32 * c);
+      for (int c = 0; c < D / 32; ++c) qop[ct][c] = load16(qp + 32 * c);
     } else {
 #pragma unroll
-      for (int c = 0; c < KC; ++c) qop[ct][c] = zero8();
+      for (int c = 0; c < D / 32; ++c) qop[ct][c] = zero8();
     }
   }
+}
+
+// Online-softmax update of one column tile with N new scores per lane:
+// returns the bf16 probabilities and the rescale factor of the old state.
+template <int N>
+__device__ __forceinline__ void softmax_step(float (&x)[N], float& mrun,
+                                             float& lsum, float& alpha,
+                                             __bf16 (&p)[N]) {
+  float mx = x[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) mx = fmaxf(mx, x[i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float mnew = fmaxf(mrun, mx);
+  const float muse = (mnew == -INFINITY) ? 0.0f : mnew;
+  alpha = __builtin_amdgcn_exp2f(mrun - muse);
+  mrun = mnew;
+  float psum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    p[i] = (__bf16)__builtin_amdgcn_exp2f(x[i] - muse);
+    psum += (float)p[i];
+  }
+  lsum = lsum * alpha + psum;
+}
+
+// End of a unit: direct bf16 output, or partials + arrival count, and the
+// merge by the last split of the tile.
+template <int D, int CT>
+__device__ __forceinline__ void finish_unit(const AttendParams& P,
+                                            const WorkItem& it, int kvh,
+                                            int lane, f32x4 (&acc)[CT][D / 16],
+                                            float (&mrun)[CT],
+                                            float (&lsum)[CT]) {
+  constexpr int NT = D / 16;
+  const int r = lane & 15, g = lane >> 4;
+  const int G = P.G;
+  const int ncols = it.ntok * G;
+  float l[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    l[ct] = lsum[ct];
+    l[ct] += __shfl_xor(l[ct], 16);
+    l[ct] += __shfl_xor(l[ct], 32);
+  }
+  if (it.nsplit == 1) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int col = ct * 16 + r;
+      if (col >= ncols) continue;
+      const int tk = col / G;
+      const int64_t t = it.tok0 + tk;
+      const int h = kvh * G + (col - tk * G);
+      const float inv = 1.0f / l[ct];
+      uint16_t* op = P.out + (t * P.Hq + h) * D + 4 * g;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        bf16x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = (__bf16)(acc[ct][n][i] * inv);
+        *reinterpret_cast<bf16x4*>(op + 16 * n) = o;
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int col = ct * 16 + r;
+    if (col >= ncols) continue;
+    const int tk = col / G;
+    const int h = kvh * G + (col - tk * G);
+    const int64_t slot = (int64_t)it.pbase + (int64_t)tk * it.nsplit + it.split;
+    float* ap = P.part_acc + (slot * P.Hq + h) * D + 4 * g;
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+      *reinterpret_cast<f32x4*>(ap + 16 * n) = acc[ct][n];
+    if (g == 0) P.part_ml[slot * P.Hq + h] = make_float2(mrun[ct], l[ct]);
+  }
+  // release the partials, count the arrival; the last arrival merges
+  __threadfence();
+  uint32_t old = 0;
+  if (lane == 0)
+    old = atomicAdd(&P.counters[(int64_t)it.counter * P.Hkv + kvh], 1u);
+  old = __shfl(old, 0);
+  old = __builtin_amdgcn_readfirstlane(old);
+  if (old != (uint32_t)(it.nsplit - 1)) return;
+  __threadfence();
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int col = ct * 16 + r;
+    if (col >= ncols) continue;
+    const int tk = col / G;
+    const int64_t t = it.tok0 + tk;
+    const int h = kvh * G + (col - tk * G);
+    const int64_t slot0 = (int64_t)it.pbase + (int64_t)tk * it.nsplit;
+    float M = -INFINITY;
+    for (int s = 0; s < it.nsplit; ++s)
+      M = fmaxf(M, P.part_ml[(slot0 + s) * P.Hq + h].x);
+    float den = 0.0f;
+    f32x4 num[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) num[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < it.nsplit; ++s) {
+      const float2 ml = P.part_ml[(slot0 + s) * P.Hq + h];
+      const float w = __builtin_amdgcn_exp2f(ml.x - M);
+      den += w * ml.y;
+      const float* ap = P.part_acc + ((slot0 + s) * P.Hq + h) * D + 4 * g;
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+        num[n] += w * *reinterpret_cast<const f32x4*>(ap + 16 * n);
+    }
+    const float inv = 1.0f / den;
+    uint16_t* op = P.out + (t * P.Hq + h) * D + 4 * g;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      bf16x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = (__bf16)(num[n][i] * inv);
+      *reinterpret_cast<bf16x4*>(op + 16 * n) = o;
+    }
+  }
+}
+
+// Physical block ids of 64 consecutive logical blocks of a unit, one per lane.
+struct BlockIds {
+  int idv = 0;
+  int chunk = -1;
+  __device__ __forceinline__ int get(const int32_t* btrow, int jb0, int jb1,
+                                     int rel, int lane, int64_t maxblk) {
+    const int want = rel >> 6;
+    if (want != chunk) {
+      chunk = want;
+      const int j = jb0 + (want << 6) + lane;
+      int id = j < jb1 ? btrow[j] : 0;
+      id = id < 0 ? 0 : (id > maxblk ? (int)maxblk : id);
+      idv = id;
+    }
+    return __builtin_amdgcn_readlane(idv, rel & 63);
+  }
+};
+
+template <int D>
+struct KVBlock {
+  bf16x8 k[D / 32];  // K rows in MFMA operand order
+  bf16x8 v[D / 32];  // lane's 4 keys at dims d and d + D/2
+};
+
+// Decode path: one block (16 keys) per step, the next block's loads in flight
+// while the current one is computed.  PV on 16x16x16 MFMA: the score
+// registers are its B operand as they stand.
+template <int D, int CT>
+__device__ __forceinline__ void run_decode(const AttendParams& P,
+                                           const WorkItem& it, int kvh,
+                                           int lane) {
+  constexpr int KC = D / 32;
+  constexpr int NT = D / 16;
+  const int g = lane >> 4, r = lane & 15;
+  const int b = it.seq;
+  const int L = P.seq_lens[b];
+  const int q0 = P.qsl[b];
+  const int Q = P.qsl[b + 1] - q0;
+  const int posbase = L - Q + (it.tok0 - q0);
+
+  bf16x8 qop[CT][KC];
+  int cpos[CT];
+  load_query<D, CT>(P, it, kvh, lane, posbase, qop, cpos);
+
+  f32x4 acc[CT][NT];
+  float mrun[CT], lsum[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    mrun[ct] = -INFINITY;
+    lsum[ct] = 0.0f;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[ct][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int jb0 = it.kv0 >> 4;
+  const int jb1 = (it.kv1 + kBlock - 1) >> 4;
+  const int nblk = jb1 - jb0;
+  const int32_t* btrow = P.bt + (int64_t)b * P.bt_stride;
+  const int64_t tile_elems = (int64_t)kBlock * D;
+  BlockIds ids;
+
+  auto issue = [&](KVBlock<D>& buf, int j) {
+    const int id = ids.get(btrow, jb0, jb1, j, lane, P.num_blocks - 1);
+    const int64_t off = ((int64_t)id * P.Hkv + kvh) * tile_elems;
+    const uint16_t* kp = P.k_cache + off;
+    const uint16_t* vp = P.v_cache + off;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) buf.k[c] = load16(kp + c * 512 + lane * 8);
+#pragma unroll
+    for (int c = 0; c < KC; ++c) buf.v[c] = load16(vp + c * 512 + (4 * r + g) * 8);
+  };
+
+  auto compute = [&](KVBlock<D>& buf, int j) {
+    const int kp0 = (jb0 + j) * kBlock;
+    if (kp0 + kBlock > it.kv1) {
+      // keys at or past kv1 may be unwritten pool slots: zero their V so a
+      // 0 weight cannot meet a NaN
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (kp0 + 4 * g + i >= it.kv1) {
+#pragma unroll
+          for (int c = 0; c < KC; ++c) {
+            buf.v[c][i] = (__bf16)0.0f;
+            buf.v[c][i + 4] = (__bf16)0.0f;
+          }
+        }
+      }
+    }
+    const bool need_mask = kp0 + kBlock - 1 > posbase;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < KC; ++c) s = mfma32(buf.k[c], qop[ct][c], s);
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = s[i] * P.scale_log2;
+        if (need_mask && kp0 + 4 * g + i > cpos[ct]) x[i] = -INFINITY;
+      }
+      float alpha;
+      __bf16 p[4];
+      softmax_step<4>(x, mrun[ct], lsum[ct], alpha, p);
+      bf16x4 pop = {p[0], p[1], p[2], p[3]};
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[ct][n] *= alpha;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const bf16x4 vlo = __builtin_shufflevector(buf.v[c], buf.v[c], 0, 1, 2, 3);
+        const bf16x4 vhi = __builtin_shufflevector(buf.v[c], buf.v[c], 4, 5, 6, 7);
+        acc[ct][c] = mfma16(vlo, pop, acc[ct][c]);
+        acc[ct][c + KC] = mfma16(vhi, pop, acc[ct][c + KC]);
+      }
+    }
+  };
+
+  if (nblk > 0) {
+    KVBlock<D> b0, b1;
+    issue(b0, 0);
+    for (int j = 0; j < nblk; j += 2) {
+      if (j + 1 < nblk) issue(b1, j + 1);
+      compute(b0, j);
+      if (j + 1 >= nblk) break;
+      if (j + 2 < nblk) issue(b0, j + 2);
+      compute(b1, j + 1);
+    }
+  }
+  finish_unit<D, CT>(P, it, kvh, lane, acc, mrun, lsum);
+}
+
+template <int D>
+struct KVPair {
+  bf16x8 k[2][D / 32];  // block a, block b: K rows in MFMA operand order
+  bf16x8 v[2][D / 32];  // lane's 4 keys at dims d and d + D/2
+};
+
+// Prefill path: two blocks (32 keys) per step so that PV runs on the
+// full-rate 16x16x32 MFMA (k index 8g+j: block a key 4g+j for j < 4, block b
+// key 4g+j-4 otherwise, matching the two score tiles the lane holds).
+template <int D, int CT>
+__device__ __forceinline__ void run_prefill(const AttendParams& P,
+                                            const WorkItem& it, int kvh,
+                                            int lane) {
+  constexpr int KC = D / 32;
+  constexpr int NT = D / 16;
+  const int r = lane & 15, g = lane >> 4;
+  const int b = it.seq;
+  const int L = P.seq_lens[b];
+  const int q0 = P.qsl[b];
+  const int Q = P.qsl[b + 1] - q0;
+  const int posbase = L - Q + (it.tok0 - q0);
+
+  bf16x8 qop[CT][KC];
+  int cpos[CT];
+  load_query<D, CT>(P, it, kvh, lane, posbase, qop, cpos);
 
   f32x4 acc[CT][NT];
   float mrun[CT], lsum[CT];
@@ -330,43 +663,27 @@ __device__ __forceinline__ void run_item(const AttendParams& P,
   const int npairs = (nblk + 1) >> 1;
   const int32_t* btrow = P.bt + (int64_t)b * P.bt_stride;
   const int64_t tile_elems = (int64_t)kBlock * D;
-  const int64_t maxblk = P.num_blocks - 1;
+  BlockIds ids;
 
-  // Physical block ids of 64 consecutive logical blocks, one per lane.
-  int idv = 0;
-  int chunk = -1;
-  auto ensure_ids = [&](int rel) {
-    const int want = rel >> 6;
-    if (want != chunk) {
-      chunk = want;
-      const int j = jb0 + (want << 6) + lane;
-      int id = j < jb1 ? btrow[j] : 0;
-      id = id < 0 ? 0 : (id > maxblk ? (int)maxblk : id);
-      idv = id;
-    }
-  };
-
-  auto issue = [&](KVPair<D>& buf, int pr) {
+  for (int pr = 0; pr < npairs; ++pr) {
+    KVPair<D> buf;
     const int rel = 2 * pr;
-    ensure_ids(rel);
-    const int ia = __builtin_amdgcn_readlane(idv, rel & 63);
     const bool has_b = rel + 1 < nblk;
-    const int ib = __builtin_amdgcn_readlane(idv, (rel + 1) & 63);
-    const uint16_t* ka = P.k_cache + ((int64_t)ia * P.Hkv + kvh) * tile_elems;
-    const uint16_t* va = P.v_cache + ((int64_t)ia * P.Hkv + kvh) * tile_elems;
+    const int ia = ids.get(btrow, jb0, jb1, rel, lane, P.num_blocks - 1);
+    const int ib = ids.get(btrow, jb0, jb1, rel + 1, lane, P.num_blocks - 1);
+    const int64_t offa = ((int64_t)ia * P.Hkv + kvh) * tile_elems;
 #pragma unroll
-    for (int c = 0; c < KC; ++c) buf.k[0][c] = load16(ka + c * 512 + lane * 8);
+    for (int c = 0; c < KC; ++c) buf.k[0][c] = load16(P.k_cache + offa + c * 512 + lane * 8);
 #pragma unroll
     for (int c = 0; c < KC; ++c)
-      buf.v[0][c] = load16(va + c * 512 + (4 * r + g) * 8);
+      buf.v[0][c] = load16(P.v_cache + offa + c * 512 + (4 * r + g) * 8);
     if (has_b) {
-      const uint16_t* kb = P.k_cache + ((int64_t)ib * P.Hkv + kvh) * tile_elems;
-      const uint16_t* vb = P.v_cache + ((int64_t)ib * P.Hkv + kvh) * tile_elems;
+      const int64_t offb = ((int64_t)ib * P.Hkv + kvh) * tile_elems;
 #pragma unroll
-      for (int c = 0; c < KC; ++c) buf.k[1][c] = load16(kb + c * 512 + lane * 8);
+      for (int c = 0; c < KC; ++c) buf.k[1][c] = load16(P.k_cache + offb + c * 512 + lane * 8);
 #pragma unroll
       for (int c = 0; c < KC; ++c)
-        buf.v[1][c] = load16(vb + c * 512 + (4 * r + g) * 8);
+        buf.v[1][c] = load16(P.v_cache + offb + c * 512 + (4 * r + g) * 8);
     } else {
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
@@ -374,21 +691,15 @@ __device__ __forceinline__ void run_item(const AttendParams& P,
         buf.v[1][c] = zero8();
       }
     }
-  };
-
-  auto compute = [&](KVPair<D>& buf, int pr) {
-    const int kp0 = (jb0 + 2 * pr) * kBlock;  // logical position of key 0 of block a
-    // keys at or past kv1 may be unwritten pool slots: zero their V so that
-    // 0-weight x NaN cannot reach the accumulator.
+    const int kp0 = (jb0 + rel) * kBlock;
     if (kp0 + 2 * kBlock > it.kv1) {
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bool dead = kp0 + 16 * x + 4 * g + i >= it.kv1;
+          if (kp0 + 16 * x + 4 * g + i >= it.kv1) {
 #pragma unroll
-          for (int c = 0; c < KC; ++c) {
-            if (dead) {
+            for (int c = 0; c < KC; ++c) {
               buf.v[x][c][i] = (__bf16)0.0f;
               buf.v[x][c][i + 4] = (__bf16)0.0f;
             }
@@ -401,117 +712,49 @@ __device__ __forceinline__ void run_item(const AttendParams& P,
     for (int ct = 0; ct < CT; ++ct) {
       f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < KC; ++c) sa = mfma(buf.k[0][c], qop[ct][c], sa);
+      for (int c = 0; c < KC; ++c) sa = mfma32(buf.k[0][c], qop[ct][c], sa);
 #pragma unroll
-      for (int c = 0; c < KC; ++c) sb = mfma(buf.k[1][c], qop[ct][c], sb);
+      for (int c = 0; c < KC; ++c) sb = mfma32(buf.k[1][c], qop[ct][c], sb);
       float x[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         x[i] = sa[i] * P.scale_log2;
         x[i + 4] = sb[i] * P.scale_log2;
-      }
-      if (need_mask) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        if (need_mask) {
           const int ka = kp0 + 4 * g + i;
           if (ka > cpos[ct]) x[i] = -INFINITY;
           if (ka + kBlock > cpos[ct]) x[i + 4] = -INFINITY;
         }
       }
-      float mx = x[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrun[ct], mx);
-      const float muse = (mnew == -INFINITY) ? 0.0f : mnew;
-      const float alpha = __builtin_amdgcn_exp2f(mrun[ct] - muse);
-      mrun[ct] = mnew;
+      float alpha;
+      __bf16 p[8];
+      softmax_step<8>(x, mrun[ct], lsum[ct], alpha, p);
       bf16x8 pop;
-      float psum = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const __bf16 pb = (__bf16)__builtin_amdgcn_exp2f(x[i] - muse);
-        pop[i] = pb;
-        psum += (float)pb;
-      }
-      lsum[ct] = lsum[ct] * alpha + psum;
+      for (int i = 0; i < 8; ++i) pop[i] = p[i];
 #pragma unroll
       for (int n = 0; n < NT; ++n) acc[ct][n] *= alpha;
 #pragma unroll
-      for (int n = 0; n < KC; ++n) {
-        const bf16x8 vlo = __builtin_shufflevector(buf.v[0][n], buf.v[1][n], 0,
+      for (int c = 0; c < KC; ++c) {
+        const bf16x8 vlo = __builtin_shufflevector(buf.v[0][c], buf.v[1][c], 0,
                                                    1, 2, 3, 8, 9, 10, 11);
-        acc[ct][n] = mfma(vlo, pop, acc[ct][n]);
-      }
-#pragma unroll
-      for (int n = 0; n < KC; ++n) {
-        const bf16x8 vhi = __builtin_shufflevector(buf.v[0][n], buf.v[1][n], 4,
+        const bf16x8 vhi = __builtin_shufflevector(buf.v[0][c], buf.v[1][c], 4,
                                                    5, 6, 7, 12, 13, 14, 15);
-        acc[ct][n + KC] = mfma(vhi, pop, acc[ct][n + KC]);
+        acc[ct][c] = mfma32(vlo, pop, acc[ct][c]);
+        acc[ct][c + KC] = mfma32(vhi, pop, acc[ct][c + KC]);
       }
-    }
-  };
-
-  if (PIPE == 2) {
-    if (npairs > 0) {
-      KVPair<D> b0, b1;
-      issue(b0, 0);
-      for (int pr = 0; pr < npairs; pr += 2) {
-        if (pr + 1 < npairs) issue(b1, pr + 1);
-        compute(b0, pr);
-        if (pr + 1 >= npairs) break;
-        if (pr + 2 < npairs) issue(b0, pr + 2);
-        compute(b1, pr + 1);
-      }
-    }
-  } else {
-    for (int pr = 0; pr < npairs; ++pr) {
-      KVPair<D> b0;
-      issue(b0, pr);
-      compute(b0, pr);
     }
   }
-
-  // epilogue
-#pragma unroll
-  for (int ct = 0; ct < CT; ++ct) {
-    float l = lsum[ct];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    const int col = ct * 16 + r;
-    if (col >= ncols) continue;
-    const int tk = col / G;
-    const int hh = col - tk * G;
-    const int64_t t = it.tok0 + tk;
-    const int h = kvh * G + hh;
-    if (it.pbase < 0) {
-      const float inv = 1.0f / l;
-      uint16_t* op = P.out + (t * P.Hq + h) * D + 4 * g;
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        bf16x4 o;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = (__bf16)(acc[ct][n][i] * inv);
-        *reinterpret_cast<bf16x4*>(op + 16 * n) = o;
-      }
-    } else {
-      const int ns = P.token_split[t].nsplit;
-      const int64_t slot = (int64_t)it.pbase + (int64_t)tk * ns + it.split;
-      float* ap = P.part_acc + (slot * P.Hq + h) * D + 4 * g;
-#pragma unroll
-      for (int n = 0; n < NT; ++n)
-        *reinterpret_cast<f32x4*>(ap + 16 * n) = acc[ct][n];
-      if (g == 0) P.part_ml[slot * P.Hq + h] = make_float2(mrun[ct], l);
-    }
-  }
+  finish_unit<D, CT>(P, it, kvh, lane, acc, mrun, lsum);
 }
 
-template <int D>
-__global__ __launch_bounds__(kAttendThreads)
-__attribute__((amdgpu_waves_per_eu(kAttendWavesPerSimd, 8)))
-void attend_kernel(AttendParams P) {
+template <int D, bool MIXED>
+__device__ __forceinline__ void attend_body(const AttendParams& P) {
   const int lane = threadIdx.x & 63;
+  if (P.hdr->signature != plan_signature(P)) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(&P.hdr->error, 4u);
+    return;
+  }
   const uint32_t num_work = P.hdr->num_work;
   const uint32_t Hkv = (uint32_t)P.Hkv;
   while (true) {
@@ -522,56 +765,55 @@ void attend_kernel(AttendParams P) {
     if (w >= num_work) break;
     const WorkItem it = P.items[w / Hkv];
     const int kvh = (int)(w % Hkv);
-    if (it.kind == kKindPrefill)
-      run_item<D, kPrefillColTiles, 1>(P, it, kvh, lane);
+    if (MIXED && it.kind == kKindPrefill)
+      run_prefill<D, kPrefillColTiles>(P, it, kvh, lane);
     else
-      run_item<D, kDecodeColTiles, 2>(P, it, kvh, lane);
+      run_decode<D, kDecodeColTiles>(P, it, kvh, lane);
   }
 }
 
-// ---------------------------------------------------------------------------
-// merge
-// ---------------------------------------------------------------------------
-
-// One wave per (token, head); lanes cover head_dim.
+// Decode-only batches: more resident waves than the unified kernel (four per
+// SIMD for head_dim 64, three for 128, where four would spill).
 template <int D>
-__global__ __launch_bounds__(64) void merge_kernel(AttendParams P) {
-  constexpr int PER = D / 64;
-  const int64_t th = blockIdx.x;
-  const int64_t t = th / P.Hq;
-  const int h = (int)(th - t * P.Hq);
-  const TokenSplit ts = P.token_split[t];
-  if (ts.nsplit <= 1 || ts.pbase < 0) return;
-  const int lane = threadIdx.x;
-  float M = -INFINITY;
-  for (int s = 0; s < ts.nsplit; ++s)
-    M = fmaxf(M, P.part_ml[((int64_t)ts.pbase + s) * P.Hq + h].x);
-  float den = 0.0f;
-  float num[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) num[e] = 0.0f;
-  for (int s = 0; s < ts.nsplit; ++s) {
-    const int64_t slot = (int64_t)ts.pbase + s;
-    const float2 ml = P.part_ml[slot * P.Hq + h];
-    const float w = __builtin_amdgcn_exp2f(ml.x - M);
-    den += w * ml.y;
-    const float* ap = P.part_acc + (slot * P.Hq + h) * D;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) num[e] += w * ap[lane * PER + e];
+__global__ __launch_bounds__(kAttendThreads)
+__attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 3, 8)))
+void attend_decode_kernel(AttendParams P) {
+  attend_body<D, false>(P);
+}
+
+// Mixed batches: decode and prefill items in the same launch.
+template <int D>
+__global__ __launch_bounds__(kAttendThreads)
+__attribute__((amdgpu_waves_per_eu(2, 8)))
+void attend_mixed_kernel(AttendParams P) {
+  attend_body<D, true>(P);
+}
+
+// Resident workgroups per CU of a kernel (queried once per device).
+int resident_wgs(const void* fn, int slot) {
+  static std::mutex mu;
+  static std::vector<int> cache;  // [device * 4 + slot]
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1;
+  std::lock_guard<std::mutex> lock(mu);
+  const size_t idx = (size_t)dev * 4 + slot;
+  if (cache.size() <= idx) cache.resize(idx + 1, 0);
+  if (cache[idx] == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kAttendThreads, 0) !=
+            hipSuccess ||
+        n < 1)
+      n = 1;
+    cache[idx] = n;
   }
-  const float inv = 1.0f / den;
-  uint16_t* op = P.out + (t * P.Hq + h) * D;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const __bf16 o = (__bf16)(num[e] * inv);
-    op[lane * PER + e] = *reinterpret_cast<const uint16_t*>(&o);
-  }
+  return cache[idx];
 }
 
 }  // namespace
 
-hipError_t launch_attend(const AttendArgs& a, hipStream_t stream) {
-  if (a.num_q_tokens == 0 || a.num_seqs == 0) return hipSuccess;
+namespace {
+
+AttendParams make_params(const AttendArgs& a) {
   AttendParams P;
   P.q = a.q;
   P.k_cache = a.k_cache;
@@ -593,38 +835,44 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t stream) {
   char* ws = static_cast<char*>(a.workspace);
   P.hdr = reinterpret_cast<PlanHeader*>(ws);
   P.items = reinterpret_cast<WorkItem*>(ws + a.ws.items);
-  P.token_split = reinterpret_cast<TokenSplit*>(ws + a.ws.token_split);
+  P.counters = reinterpret_cast<uint32_t*>(ws + a.ws.counters);
   P.part_ml = reinterpret_cast<float2*>(ws + a.ws.part_ml);
   P.part_acc = reinterpret_cast<float*>(ws + a.ws.part_acc);
   P.max_items = a.ws.max_items;
   P.max_partials = a.ws.max_partials;
+  return P;
+}
 
+}  // namespace
+
+hipError_t launch_plan(const AttendArgs& a, hipStream_t stream) {
+  if (a.num_q_tokens == 0 || a.num_seqs == 0) return hipSuccess;
+  const AttendParams P = make_params(a);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, P);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
 
-  // Persistent grid: enough waves to fill every CU at the kernel's
-  // occupancy, never more than the work-unit bound.
+hipError_t launch_planned(const AttendArgs& a, hipStream_t stream) {
+  if (a.num_q_tokens == 0 || a.num_seqs == 0) return hipSuccess;
+  const AttendParams P = make_params(a);
+  const bool decode_only = a.max_query_len <= decode_tile_tokens(P.G);
+  void (*fn)(AttendParams);
+  int slot;
+  if (a.head_dim == 128) {
+    fn = decode_only ? attend_decode_kernel<128> : attend_mixed_kernel<128>;
+    slot = decode_only ? 0 : 1;
+  } else {
+    fn = decode_only ? attend_decode_kernel<64> : attend_mixed_kernel<64>;
+    slot = decode_only ? 2 : 3;
+  }
+  // Persistent grid: every resident slot of every CU, never more waves than
+  // the work-unit bound.
   const int64_t max_work = a.ws.max_items * a.num_kv_heads;
-  int64_t waves = (int64_t)a.num_cus * 4 * kAttendWavesPerSimd;
-  if (waves > max_work) waves = max_work;
-  const int64_t wgs = (waves + (kAttendThreads / 64) - 1) / (kAttendThreads / 64);
-  if (a.head_dim == 128)
-    hipLaunchKernelGGL(attend_kernel<128>, dim3((unsigned)wgs),
-                       dim3(kAttendThreads), 0, stream, P);
-  else
-    hipLaunchKernelGGL(attend_kernel<64>, dim3((unsigned)wgs),
-                       dim3(kAttendThreads), 0, stream, P);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
-  const int64_t rows = a.num_q_tokens * a.num_q_heads;
-  if (a.head_dim == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, dim3((unsigned)rows), dim3(64), 0,
-                       stream, P);
-  else
-    hipLaunchKernelGGL(merge_kernel<64>, dim3((unsigned)rows), dim3(64), 0,
-                       stream, P);
+  int64_t wgs = (int64_t)a.num_cus * resident_wgs((const void*)fn, slot);
+  const int64_t need = (max_work + (kAttendThreads / 64) - 1) / (kAttendThreads / 64);
+  if (wgs > need) wgs = need;
+  if (wgs < 1) wgs = 1;
+  hipLaunchKernelGGL(fn, dim3((unsigned)wgs), dim3(kAttendThreads), 0, stream, P);
   return hipGetLastError();
 }
 

@@ -125,15 +125,23 @@ size_t pa_attend_workspace_size(int32_t num_seqs, int64_t num_q_tokens,
       .total;
 }
 
-pa_status pa_attend(const void* q, const void* k_cache, const void* v_cache,
-                    int64_t num_blocks, const int32_t* block_tables,
-                    int32_t max_blocks_per_seq, const int32_t* seq_lens,
-                    const int32_t* query_start_loc, int32_t num_seqs,
-                    int64_t num_q_tokens, int32_t num_q_heads,
-                    int32_t num_kv_heads, int32_t head_dim,
-                    int32_t max_query_len, int32_t max_seq_len, float scale,
-                    void* out, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the attention entry points; fills `a`.  With
+// need_tensors = false (planning only) q, the pools and out may be NULL.
+pa_status prepare_attend(const void* q, const void* k_cache,
+                         const void* v_cache, int64_t num_blocks,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* seq_lens, const int32_t* query_start_loc,
+                         int32_t num_seqs, int64_t num_q_tokens,
+                         int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t max_query_len,
+                         int32_t max_seq_len, float scale, void* out,
+                         void* workspace, size_t workspace_bytes,
+                         bool need_tensors, pa::AttendArgs* a, bool* empty) {
+  *empty = false;
   if (num_seqs < 0 || num_q_tokens < 0 || num_blocks < 0 ||
       max_blocks_per_seq < 0 || max_query_len < 0 || max_seq_len < 0)
     return fail(PA_ERR_SHAPE, "pa_attend: negative size");
@@ -141,13 +149,18 @@ pa_status pa_attend(const void* q, const void* k_cache, const void* v_cache,
     return fail(PA_ERR_SHAPE, "pa_attend: num_q_tokens too large");
   pa_status s = check_heads(num_q_heads, num_kv_heads, head_dim);
   if (s != PA_OK) return s;
-  if (num_q_tokens == 0 || num_seqs == 0) return ok();
-  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens ||
-      !query_start_loc || !out)
+  if (num_q_tokens == 0 || num_seqs == 0) {
+    *empty = true;
+    return PA_OK;
+  }
+  if (!block_tables || !seq_lens || !query_start_loc)
+    return fail(PA_ERR_NULL, "pa_attend: NULL metadata pointer");
+  if (need_tensors && (!q || !k_cache || !v_cache || !out))
     return fail(PA_ERR_NULL, "pa_attend: NULL pointer");
-  if (num_blocks == 0 || max_blocks_per_seq == 0)
+  if (max_blocks_per_seq == 0 || (need_tensors && num_blocks == 0))
     return fail(PA_ERR_SHAPE, "pa_attend: empty pool or block table");
-  if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out) & 15)
+  if (need_tensors &&
+      (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out) & 15))
     return fail(PA_ERR_SHAPE, "q, out and the pools must be 16-byte aligned");
   pa::WorkspaceLayout ws =
       pa::workspace_layout(num_seqs, num_q_tokens, num_q_heads, num_kv_heads,
@@ -161,28 +174,99 @@ pa_status pa_attend(const void* q, const void* k_cache, const void* v_cache,
   hipError_t e = hipSuccess;
   const int cus = num_cus_of_current_device(&e);
   if (e != hipSuccess) return hip_fail(e, "pa_attend device query");
+  a->q = static_cast<const uint16_t*>(q);
+  a->k_cache = static_cast<const uint16_t*>(k_cache);
+  a->v_cache = static_cast<const uint16_t*>(v_cache);
+  a->num_blocks = num_blocks;
+  a->block_tables = block_tables;
+  a->bt_stride = max_blocks_per_seq;
+  a->seq_lens = seq_lens;
+  a->qsl = query_start_loc;
+  a->num_seqs = num_seqs;
+  a->num_q_tokens = num_q_tokens;
+  a->num_q_heads = num_q_heads;
+  a->num_kv_heads = num_kv_heads;
+  a->head_dim = head_dim;
+  a->max_query_len = max_query_len;
+  a->max_seq_len = max_seq_len;
+  a->scale = scale;
+  a->out = static_cast<uint16_t*>(out);
+  a->workspace = workspace;
+  a->ws = ws;
+  a->num_cus = cus;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_attend_plan(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* seq_lens, const int32_t* query_start_loc,
+                         int32_t num_seqs, int64_t num_q_tokens,
+                         int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t max_query_len,
+                         int32_t max_seq_len, void* workspace,
+                         size_t workspace_bytes, void* stream) {
   pa::AttendArgs a;
-  a.q = static_cast<const uint16_t*>(q);
-  a.k_cache = static_cast<const uint16_t*>(k_cache);
-  a.v_cache = static_cast<const uint16_t*>(v_cache);
-  a.num_blocks = num_blocks;
-  a.block_tables = block_tables;
-  a.bt_stride = max_blocks_per_seq;
-  a.seq_lens = seq_lens;
-  a.qsl = query_start_loc;
-  a.num_seqs = num_seqs;
-  a.num_q_tokens = num_q_tokens;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.head_dim = head_dim;
-  a.max_query_len = max_query_len;
-  a.max_seq_len = max_seq_len;
-  a.scale = scale;
-  a.out = static_cast<uint16_t*>(out);
-  a.workspace = workspace;
-  a.ws = ws;
-  a.num_cus = cus;
-  e = pa::launch_attend(a, static_cast<hipStream_t>(stream));
+  bool empty;
+  pa_status s = prepare_attend(nullptr, nullptr, nullptr, 0, block_tables,
+                               max_blocks_per_seq, seq_lens, query_start_loc,
+                               num_seqs, num_q_tokens, num_q_heads, num_kv_heads,
+                               head_dim, max_query_len, max_seq_len, 0.0f,
+                               nullptr, workspace, workspace_bytes, false, &a,
+                               &empty);
+  if (s != PA_OK) return s;
+  if (empty) return ok();
+  hipError_t e = pa::launch_plan(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pa_attend_plan launch");
+  return ok();
+}
+
+pa_status pa_attend_planned(const void* q, const void* k_cache,
+                            const void* v_cache, int64_t num_blocks,
+                            const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                            const int32_t* query_start_loc, int32_t num_seqs,
+                            int64_t num_q_tokens, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim,
+                            int32_t max_query_len, int32_t max_seq_len,
+                            float scale, void* out, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  pa::AttendArgs a;
+  bool empty;
+  pa_status s = prepare_attend(q, k_cache, v_cache, num_blocks, block_tables,
+                               max_blocks_per_seq, seq_lens, query_start_loc,
+                               num_seqs, num_q_tokens, num_q_heads, num_kv_heads,
+                               head_dim, max_query_len, max_seq_len, scale, out,
+                               workspace, workspace_bytes, true, &a, &empty);
+  if (s != PA_OK) return s;
+  if (empty) return ok();
+  hipError_t e = pa::launch_planned(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pa_attend_planned launch");
+  return ok();
+}
+
+pa_status pa_attend(const void* q, const void* k_cache, const void* v_cache,
+                    int64_t num_blocks, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                    const int32_t* query_start_loc, int32_t num_seqs,
+                    int64_t num_q_tokens, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim,
+                    int32_t max_query_len, int32_t max_seq_len, float scale,
+                    void* out, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  pa::AttendArgs a;
+  bool empty;
+  pa_status s = prepare_attend(q, k_cache, v_cache, num_blocks, block_tables,
+                               max_blocks_per_seq, seq_lens, query_start_loc,
+                               num_seqs, num_q_tokens, num_q_heads, num_kv_heads,
+                               head_dim, max_query_len, max_seq_len, scale, out,
+                               workspace, workspace_bytes, true, &a, &empty);
+  if (s != PA_OK) return s;
+  if (empty) return ok();
+  hipError_t e = pa::launch_plan(a, static_cast<hipStream_t>(stream));
+  if (e == hipSuccess) e = pa::launch_planned(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "pa_attend launch");
   return ok();
 }

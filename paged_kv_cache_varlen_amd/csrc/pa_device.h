@@ -14,17 +14,16 @@ constexpr int kBlock = 16;  // tokens per KV block
 constexpr int kSplitDecode = 512;    // logical tokens per decode split
 constexpr int kSplitPrefill = 2048;  // logical tokens per prefill split
 // A prefill request is split along its keys only if it has fewer than this
-// many (q-tile x kv-head) work units on its own.
+// many (query tile x kv head) work units on its own.
 constexpr int kPrefillUnsplitUnits = 512;
 constexpr int kDecodeColTiles = 1;   // 16 MFMA columns: up to 16/G tokens
 constexpr int kPrefillColTiles = 2;  // 32 MFMA columns: 32/G tokens
 constexpr int kMaxGroup = 16;        // query heads per kv head
 constexpr int kAttendThreads = 256;  // 4 independent waves per workgroup
-constexpr int kAttendWavesPerSimd = 2;
 
 enum ItemKind : int { kKindDecode = 0, kKindPrefill = 1 };
 
-// One unit of attention work for one kv head: a tile of consecutive query
+// One unit of attention work for all kv heads: a tile of consecutive query
 // tokens of one request against one logical key range of that request.
 struct WorkItem {
   int32_t seq;      // request index b
@@ -34,15 +33,12 @@ struct WorkItem {
   int32_t kv0;      // first logical key (multiple of 32)
   int32_t kv1;      // one past the last logical key
   int32_t split;    // split index of this key range
+  int32_t nsplit;   // splits of this tile (1: output written directly)
   int32_t pbase;    // partial slot of (tile token 0, split 0); -1 if unsplit
+  int32_t counter;  // arrival counter of the tile (x num_kv_heads); -1 if unsplit
+  int32_t pad[6];
 };
-static_assert(sizeof(WorkItem) == 32, "WorkItem is two 16-byte loads");
-
-// Per query token: where its split-K partial results live.
-struct TokenSplit {
-  int32_t pbase;   // partial slot of split 0 (slot of split s = pbase + s)
-  int32_t nsplit;  // number of splits; 1 = written directly to out
-};
+static_assert(sizeof(WorkItem) == 64, "WorkItem is one 64-byte scalar load");
 
 // Workspace header, at offset 0 of the workspace.
 struct PlanHeader {
@@ -50,12 +46,14 @@ struct PlanHeader {
   uint32_t num_work;      // items * num_kv_heads
   uint32_t num_items;
   uint32_t error;         // bit0: capacity exceeded, bit1: bad request skipped
+  uint32_t num_counters;  // split tiles * num_kv_heads
+  uint32_t signature;     // hash of the arguments the plan was made for
 };
 
 // Byte offsets of the workspace sections.
 struct WorkspaceLayout {
   size_t items;         // WorkItem[max_items]
-  size_t token_split;   // TokenSplit[num_q_tokens]
+  size_t counters;      // uint32[max_items * Hkv]  split-tile arrival counters
   size_t part_ml;       // float2[max_partials * Hq]  (running max, sum)
   size_t part_acc;      // float[max_partials * Hq * D]
   size_t total;
@@ -102,8 +100,8 @@ inline WorkspaceLayout workspace_layout(int32_t num_seqs, int64_t num_q_tokens,
   size_t off = align256(sizeof(PlanHeader));
   w.items = off;
   off = align256(off + sizeof(WorkItem) * (size_t)w.max_items);
-  w.token_split = off;
-  off = align256(off + sizeof(TokenSplit) * (size_t)(T > 0 ? T : 1));
+  w.counters = off;
+  off = align256(off + sizeof(uint32_t) * (size_t)w.max_items * num_kv_heads);
   w.part_ml = off;
   off = align256(off + sizeof(float) * 2 * (size_t)w.max_partials * num_q_heads);
   w.part_acc = off;
@@ -153,6 +151,9 @@ struct AttendArgs {
   int num_cus;
 };
 
-hipError_t launch_attend(const AttendArgs& a, hipStream_t stream);
+// Work plan into the workspace (one small kernel).
+hipError_t launch_plan(const AttendArgs& a, hipStream_t stream);
+// Attention over the plan in the workspace (one persistent kernel).
+hipError_t launch_planned(const AttendArgs& a, hipStream_t stream);
 
 }  // namespace pa

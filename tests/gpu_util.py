@@ -64,10 +64,18 @@ class Uploaded:
         pa.write_kv(self.k_new, self.v_new, self.new_slots, self.k_cache,
                     self.v_cache)
 
-    def attend(self, out=None):
+    def attend(self, out=None, k_cache=None, v_cache=None, planned=False):
         w = self.w
-        return pa.attend(self.q, self.k_cache, self.v_cache, self.block_tables,
-                         self.seq_lens, self.qsl, w.scale, w.max_query_len,
-                         w.max_seq_len, num_kv_heads=w.num_kv_heads,
+        return pa.attend(self.q, self.k_cache if k_cache is None else k_cache,
+                         self.v_cache if v_cache is None else v_cache,
+                         self.block_tables, self.seq_lens, self.qsl, w.scale,
+                         w.max_query_len, w.max_seq_len,
+                         num_kv_heads=w.num_kv_heads,
                          out=self.out if out is None else out,
-                         workspace=self.workspace)
+                         workspace=self.workspace, planned=planned)
+
+    def plan(self):
+        w = self.w
+        pa.attend_plan(self.block_tables, self.seq_lens, self.qsl,
+                       w.num_q_tokens, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                       w.max_query_len, w.max_seq_len, self.workspace)

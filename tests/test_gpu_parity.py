@@ -216,6 +216,34 @@ def test_rerun_and_batch_independence_bit_identical():
     assert np.array_equal(c, a[t0:t0 + Q[0]])
 
 
+@pytest.mark.parametrize("name", ["mixed-g4-d128", "mixed-g1-d64"])
+def test_plan_then_planned_equals_attend(name):
+    w = small(name, seed=12)
+    u = Uploaded(w)
+    a = tensor_bits(u.attend()).copy()
+    u.plan()
+    # one plan, several "layers" (here the same pools twice)
+    b1 = tensor_bits(u.attend(out=torch.empty_like(u.q), planned=True)).copy()
+    b2 = tensor_bits(u.attend(out=torch.empty_like(u.q), planned=True)).copy()
+    assert np.array_equal(a, b1) and np.array_equal(a, b2)
+
+
+def test_planned_with_other_sizes_writes_nothing():
+    w = small("mixed-g4-d128", seed=13)
+    u = Uploaded(w)
+    u.plan()
+    out = torch.full_like(u.q, 7.0)
+    ws = pa.alloc_workspace(w.num_seqs, w.num_q_tokens, w.num_q_heads,
+                            w.num_kv_heads, w.head_dim, w.max_query_len,
+                            w.max_seq_len + 512)
+    ws[: u.workspace.numel()].copy_(u.workspace)
+    pa.attend(u.q, u.k_cache, u.v_cache, u.block_tables, u.seq_lens, u.qsl,
+              w.scale, w.max_query_len, w.max_seq_len + 512,
+              num_kv_heads=w.num_kv_heads, out=out, workspace=ws, planned=True)
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
+
+
 def test_empty_batch_is_noop():
     w = small("mixed-g1-d64", seed=10)
     u = Uploaded(w)
