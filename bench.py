@@ -2,8 +2,8 @@
 """Benchmark of one paged-attention layer step on one MI355X.
 
 A step is the whole hot path for one layer over one batch: pa_write_kv of
-the step's new K/V rows, then pa_attend (work plan, unified varlen paged
-attention, split-K merge) over every query row.  Inputs are seeded synthetic
+the step's new K/V rows, then the three kernels of pa_attend (work plan,
+unified varlen paged attention, split-K merge) over every query row.  Inputs are seeded synthetic
 tensors already resident in HBM.  Several copies of the KV pool (one per
 simulated layer, >= 2 GiB in total) are cycled so that no step reads K/V left
 in the caches by the previous one.
@@ -85,17 +85,18 @@ class Runner:
         self.stream = torch.cuda.current_stream()
 
     def step(self, i, ev=None):
-        """write_kv + plan + attention for one layer; the events bracket the
-        attention kernel alone."""
+        """write_kv + plan + attention + merge for one layer; the events
+        bracket the attention kernel alone."""
         pa, u = self.pa, self.u
         kc, vc = self.layers[i % len(self.layers)]
         pa.write_kv(u.k_new, u.v_new, u.new_slots, kc, vc)
         u.plan()
         if ev is not None:
             ev[0].record(self.stream)
-        u.attend(k_cache=kc, v_cache=vc, planned=True)
+        u.attend(k_cache=kc, v_cache=vc, planned=True, merge=False)
         if ev is not None:
             ev[1].record(self.stream)
+        u.merge()
 
     def run(self, steps, warmup):
         torch = self.torch

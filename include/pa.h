@@ -192,19 +192,24 @@ pa_status pa_attend(const void *q, const void *k_cache, const void *v_cache,
                     void *stream);
 
 /*
- * pa_attend_plan + pa_attend_planned - pa_attend in two calls, so that one
- * plan serves every layer of a forward step (the metadata is the same for all
- * layers; "Inside vLLM", Step 4c: the runner builds query_start_loc and the
- * block tables once per step).
+ * pa_attend_plan, pa_attend_planned, pa_attend_merge - pa_attend in three
+ * calls, so that one plan serves every layer of a forward step (the metadata
+ * is the same for all layers; "Inside vLLM", Step 4c: the runner builds
+ * query_start_loc and the block tables once per step), and so that each
+ * kernel can be timed on its own.
  *
- * pa_attend_plan enqueues only the work-plan kernel: it reads the metadata
- * and writes the work list into `workspace`.  pa_attend_planned enqueues only
- * the attention kernel over the plan found in `workspace`.  Arguments mean
- * the same as for pa_attend.  Between the two calls the workspace and the
- * metadata arrays must not change, and every argument that pa_attend_plan
- * also takes must be passed with the same value; a plan made for other sizes
- * is detected on the device and the attention kernel then writes nothing
- * (out keeps its contents).  pa_attend == pa_attend_plan + pa_attend_planned.
+ * pa_attend_plan enqueues the work-plan kernel: it reads the metadata and
+ * writes the work list into `workspace`.  pa_attend_planned enqueues the
+ * attention kernel over the plan found in `workspace`: it writes `out` for
+ * every query row whose keys were not split, and fp32 partial results into
+ * the workspace for the others.  pa_attend_merge enqueues the merge kernel
+ * that combines those partials into `out`; it must follow every
+ * pa_attend_planned on the same stream, before the workspace is reused.
+ * Arguments mean the same as for pa_attend.  Between the calls the workspace
+ * and the metadata arrays must not change, and every size argument must be
+ * passed with the same value to all three; a plan made for other sizes is
+ * detected on the device and the attention kernel then writes nothing (out
+ * keeps its contents).  pa_attend == plan + planned + merge.
  */
 pa_status pa_attend_plan(const int32_t *block_tables,
                          int32_t max_blocks_per_seq, const int32_t *seq_lens,
@@ -226,6 +231,12 @@ pa_status pa_attend_planned(const void *q, const void *k_cache,
                             int32_t max_query_len, int32_t max_seq_len,
                             float scale, void *out, void *workspace,
                             size_t workspace_bytes, void *stream);
+
+pa_status pa_attend_merge(int32_t num_seqs, int64_t num_q_tokens,
+                          int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t max_query_len,
+                          int32_t max_seq_len, void *out, void *workspace,
+                          size_t workspace_bytes, void *stream);
 
 /*
  * pa_gather_kv - logical gather through the block tables (a checking aid).

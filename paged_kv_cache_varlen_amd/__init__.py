@@ -161,14 +161,16 @@ def attend(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
            max_seq_len: int, num_kv_heads: Optional[int] = None,
            out: Optional[torch.Tensor] = None,
            workspace: Optional[torch.Tensor] = None,
-           planned: bool = False) -> torch.Tensor:
+           planned: bool = False, merge: bool = True) -> torch.Tensor:
     """Paged varlen causal attention of every query row of a mixed batch.
 
     q [T][Hq][D] bf16; block_tables [B][max_blocks] int32; seq_lens [B] int32;
     query_start_loc [B+1] int32; pools from alloc_pool.  Returns out
     [T][Hq][D] bf16 (written in place when ``out`` is given).  With
     planned=True the work plan already in ``workspace`` (from attend_plan with
-    the same metadata) is used and only the attention kernel is enqueued."""
+    the same metadata) is used: the attention kernel is enqueued, then (with
+    merge=True, the default) the split-K merge kernel; merge=False leaves the
+    merge to a later attend_merge call."""
     T, Hq, D, Hkv, nb, B, out, workspace = _attend_args(
         q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
         num_kv_heads, out, workspace, max_query_len, max_seq_len)
@@ -179,7 +181,22 @@ def attend(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
             Hq, Hkv, D, int(max_query_len), int(max_seq_len), float(scale),
             _ptr(out), _ptr(workspace), workspace.numel(), _stream(q))
     _lib.check(st, "pa_attend_planned" if planned else "pa_attend")
+    if planned and merge:
+        attend_merge(out, B, Hkv, max_query_len, max_seq_len, workspace)
     return out
+
+
+def attend_merge(out: torch.Tensor, num_seqs: int, num_kv_heads: int,
+                 max_query_len: int, max_seq_len: int,
+                 workspace: torch.Tensor) -> None:
+    """Enqueue the split-K merge after attend(..., planned=True, merge=False)."""
+    _need_cuda(out, "out")
+    T, Hq, D = out.shape
+    st = _lib.load().pa_attend_merge(int(num_seqs), T, Hq, int(num_kv_heads), D,
+                                     int(max_query_len), int(max_seq_len),
+                                     _ptr(out), _ptr(workspace), workspace.numel(),
+                                     _stream(out))
+    _lib.check(st, "pa_attend_merge")
 
 
 def attend_plan(block_tables: torch.Tensor, seq_lens: torch.Tensor,

@@ -9,10 +9,11 @@
 // K_j/V_j read from block block_tables[b][j/16], slot j%16, of the kv head
 // h / G shared by the G query heads of its group.
 //
-// Two kernels on one stream, no host synchronisation:
+// Three kernels on one stream, no host synchronisation:
 //   plan    one workgroup turns seq_lens / query_start_loc into a work list of
 //           (request, query tile, logical key range) items, prefill items
-//           first, and zeroes the work-queue head and the arrival counters;
+//           first, plus the list of tiles whose key range was split, and
+//           zeroes the work-queue head;
 //   attend  persistent waves pull (item, kv head) units from the queue.  One
 //           wave owns one unit.  The query tile's columns (token x head of
 //           the group) are MFMA columns and the 16 keys of a block are MFMA
@@ -21,9 +22,11 @@
 //           softmax (running max and sum per column) is fp32, reduced across
 //           the wave with shuffles; O^T = V^T P^T runs on bf16 MFMA with P
 //           taken straight from the score registers.  Units covering a whole
-//           causal range write bf16 out; split units write fp32 partials and
-//           the last split of a tile to arrive merges all of them (log-sum-exp
-//           in split order) into out.
+//           causal range write bf16 out; split units write fp32 partials;
+//   merge   one wave per (split tile, kv head) combines the partials by
+//           log-sum-exp in split order into bf16 out.  (A separate launch:
+//           the kernel boundary is what makes partials written on one XCD's
+//           L2 visible on another, without device-wide cache flushes.)
 //
 // Reduction order depends only on (Q_b, L_b) and logical key positions, so
 // results are bitwise independent of physical block ids, of shared blocks, of
@@ -69,7 +72,7 @@ struct AttendParams {
   uint16_t* out;
   PlanHeader* hdr;
   WorkItem* items;
-  uint32_t* counters;
+  int4* merge_list;  // per split tile: tok0, ntok, nsplit, pbase
   float2* part_ml;
   float* part_acc;
   int64_t max_items;
@@ -80,19 +83,22 @@ struct AttendParams {
 // plan
 // ---------------------------------------------------------------------------
 
-// Hash of the arguments a plan depends on; the attention kernel runs only on
-// a plan made for its own arguments.
+// Hash of the sizes a plan's workspace layout depends on; the attention and
+// merge kernels run only on a plan made for their own sizes.  (The block
+// table stride is not part of it: every item is checked against the stride
+// of the launch that reads it.)
 __device__ __forceinline__ uint32_t plan_signature(const AttendParams& P) {
   uint32_t h = 2166136261u;
-  const int32_t v[9] = {P.num_seqs, P.num_q_tokens, P.Hq, P.Hkv,
-                        P.max_query_len, P.max_seq_len, P.bt_stride,
-                        (int32_t)P.max_items, (int32_t)P.max_partials};
+  const int32_t v[8] = {P.num_seqs, P.num_q_tokens, P.Hq, P.Hkv,
+                        P.max_query_len, P.max_seq_len, (int32_t)P.max_items,
+                        (int32_t)P.max_partials};
 #pragma unroll
-  for (int i = 0; i < 9; ++i) h = (h ^ (uint32_t)v[i]) * 16777619u;
+  for (int i = 0; i < 8; ++i) h = (h ^ (uint32_t)v[i]) * 16777619u;
   return h;
 }
 
 constexpr int kPlanThreads = 1024;
+static_assert(kSplitDecode / kBlock <= 64, "a decode unit's block ids fit one wave");
 constexpr int kMaxCoop = 64;  // unsplit prefill requests emitted by all threads
 
 struct SeqCounts {
@@ -210,6 +216,7 @@ __device__ void emit_seq(const AttendParams& P, int b, const SeqCounts& c,
       put_item(P, ibase + s, b, q0, Q, kKindDecode, s * kSplitDecode,
                min(L, (s + 1) * kSplitDecode), s, ns, ns > 1 ? pbase : -1,
                ns > 1 ? cbase : -1);
+    if (ns > 1) P.merge_list[cbase] = make_int4(q0, Q, ns, pbase);
     return;
   }
   // split prefill: longest tiles (latest tokens) first
@@ -221,6 +228,7 @@ __device__ void emit_seq(const AttendParams& P, int b, const SeqCounts& c,
     const int pb = ns > 1 ? pcur : -1;
     const int cb = ns > 1 ? ccur : -1;
     if (ns > 1) {
+      P.merge_list[ccur] = make_int4(q0 + t * c.tq, ntok, ns, pcur);
       pcur += ntok * ns;
       ccur += 1;
     }
@@ -259,8 +267,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttendParams P) {
     all_split += t3;
   }
   const bool fits = all_items <= P.max_items && all_partials <= P.max_partials;
-  const int ncounters = fits ? all_split * P.Hkv : 0;
-  for (int i = tid; i < ncounters; i += kPlanThreads) P.counters[i] = 0u;
   // sweep 2: write
   int pre_carry = 0, dec_carry = 0, part_carry = 0, split_carry = 0;
   for (int base = 0; base < P.num_seqs; base += kPlanThreads) {
@@ -310,7 +316,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttendParams P) {
   if (tid == 0) {
     P.hdr->num_items = fits ? (uint32_t)all_items : 0u;
     P.hdr->num_work = fits ? (uint32_t)all_items * (uint32_t)P.Hkv : 0u;
-    P.hdr->num_counters = (uint32_t)ncounters;
+    P.hdr->num_split_tiles = fits ? (uint32_t)all_split : 0u;
     if (!fits) atomicOr(&P.hdr->error, 1u);
   }
 }
@@ -394,8 +400,8 @@ __device__ __forceinline__ void softmax_step(float (&x)[N], float& mrun,
   lsum = lsum * alpha + psum;
 }
 
-// End of a unit: direct bf16 output, or partials + arrival count, and the
-// merge by the last split of the tile.
+// End of a unit: direct bf16 output, or fp32 partials (running max, sum and
+// unnormalised accumulator per column) for the merge kernel.
 template <int D, int CT>
 __device__ __forceinline__ void finish_unit(const AttendParams& P,
                                             const WorkItem& it, int kvh,
@@ -445,49 +451,6 @@ __device__ __forceinline__ void finish_unit(const AttendParams& P,
     for (int n = 0; n < NT; ++n)
       *reinterpret_cast<f32x4*>(ap + 16 * n) = acc[ct][n];
     if (g == 0) P.part_ml[slot * P.Hq + h] = make_float2(mrun[ct], l[ct]);
-  }
-  // release the partials, count the arrival; the last arrival merges
-  __threadfence();
-  uint32_t old = 0;
-  if (lane == 0)
-    old = atomicAdd(&P.counters[(int64_t)it.counter * P.Hkv + kvh], 1u);
-  old = __shfl(old, 0);
-  old = __builtin_amdgcn_readfirstlane(old);
-  if (old != (uint32_t)(it.nsplit - 1)) return;
-  __threadfence();
-#pragma unroll
-  for (int ct = 0; ct < CT; ++ct) {
-    const int col = ct * 16 + r;
-    if (col >= ncols) continue;
-    const int tk = col / G;
-    const int64_t t = it.tok0 + tk;
-    const int h = kvh * G + (col - tk * G);
-    const int64_t slot0 = (int64_t)it.pbase + (int64_t)tk * it.nsplit;
-    float M = -INFINITY;
-    for (int s = 0; s < it.nsplit; ++s)
-      M = fmaxf(M, P.part_ml[(slot0 + s) * P.Hq + h].x);
-    float den = 0.0f;
-    f32x4 num[NT];
-#pragma unroll
-    for (int n = 0; n < NT; ++n) num[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < it.nsplit; ++s) {
-      const float2 ml = P.part_ml[(slot0 + s) * P.Hq + h];
-      const float w = __builtin_amdgcn_exp2f(ml.x - M);
-      den += w * ml.y;
-      const float* ap = P.part_acc + ((slot0 + s) * P.Hq + h) * D + 4 * g;
-#pragma unroll
-      for (int n = 0; n < NT; ++n)
-        num[n] += w * *reinterpret_cast<const f32x4*>(ap + 16 * n);
-    }
-    const float inv = 1.0f / den;
-    uint16_t* op = P.out + (t * P.Hq + h) * D + 4 * g;
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      bf16x4 o;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = (__bf16)(num[n][i] * inv);
-      *reinterpret_cast<bf16x4*>(op + 16 * n) = o;
-    }
   }
 }
 
@@ -547,13 +510,18 @@ __device__ __forceinline__ void run_decode(const AttendParams& P,
 
   const int jb0 = it.kv0 >> 4;
   const int jb1 = (it.kv1 + kBlock - 1) >> 4;
-  const int nblk = jb1 - jb0;
+  const int nblk = jb1 - jb0;  // <= kSplitDecode / 16 <= 64
   const int32_t* btrow = P.bt + (int64_t)b * P.bt_stride;
   const int64_t tile_elems = (int64_t)kBlock * D;
-  BlockIds ids;
+  // All physical block ids of the unit, one per lane, loaded once: inside the
+  // loop every step then issues exactly the same loads, which lets the
+  // compiler wait for the current block only, never for the prefetched one.
+  int idv = 0;
+  if (lane < nblk) idv = btrow[jb0 + lane];
+  idv = idv < 0 ? 0 : (idv >= P.num_blocks ? (int)(P.num_blocks - 1) : idv);
 
   auto issue = [&](KVBlock<D>& buf, int j) {
-    const int id = ids.get(btrow, jb0, jb1, j, lane, P.num_blocks - 1);
+    const int id = __builtin_amdgcn_readlane(idv, j);
     const int64_t off = ((int64_t)id * P.Hkv + kvh) * tile_elems;
     const uint16_t* kp = P.k_cache + off;
     const uint16_t* vp = P.v_cache + off;
@@ -608,15 +576,21 @@ __device__ __forceinline__ void run_decode(const AttendParams& P,
   };
 
   if (nblk > 0) {
+    // Every path into the loop header has exactly one block's loads in
+    // flight (the prefetch is unconditional, clamped to the last block, and
+    // the loop has no early exit), so the compiler's waits stop at the
+    // current block and never drain the prefetch.  With an even block count
+    // the last prefetch re-reads the block just loaded (an L2 hit).
     KVBlock<D> b0, b1;
     issue(b0, 0);
-    for (int j = 0; j < nblk; j += 2) {
-      if (j + 1 < nblk) issue(b1, j + 1);
+    int j = 0;
+    for (; j + 1 < nblk; j += 2) {
+      issue(b1, j + 1);
       compute(b0, j);
-      if (j + 1 >= nblk) break;
-      if (j + 2 < nblk) issue(b0, j + 2);
+      issue(b0, min(j + 2, nblk - 1));
       compute(b1, j + 1);
     }
+    if (j < nblk) compute(b0, j);
   }
   finish_unit<D, CT>(P, it, kvh, lane, acc, mrun, lsum);
 }
@@ -748,6 +722,26 @@ __device__ __forceinline__ void run_prefill(const AttendParams& P,
   finish_unit<D, CT>(P, it, kvh, lane, acc, mrun, lsum);
 }
 
+// A work item read back from the workspace is used only if every index it
+// leads to stays inside the buffers this launch was given (a stale or foreign
+// workspace then costs outputs, never an out-of-bounds access).
+__device__ __forceinline__ bool item_ok(const AttendParams& P,
+                                        const WorkItem& it) {
+  const int cols = it.kind == kKindPrefill ? 16 * kPrefillColTiles
+                                           : 16 * kDecodeColTiles;
+  bool ok = it.seq >= 0 && it.seq < P.num_seqs && it.tok0 >= 0 &&
+            it.ntok >= 1 && it.ntok * P.G <= cols &&
+            it.tok0 + it.ntok <= P.num_q_tokens && it.kv0 >= 0 &&
+            (it.kv0 & 31) == 0 && it.kv1 > it.kv0 && it.kv1 <= P.max_seq_len &&
+            ((it.kv1 + kBlock - 1) / kBlock) <= P.bt_stride &&
+            it.nsplit >= 1 && it.split >= 0 && it.split < it.nsplit;
+  if (it.kind != kKindPrefill) ok = ok && (it.kv1 - it.kv0) <= kSplitDecode;
+  if (it.nsplit > 1)
+    ok = ok && it.pbase >= 0 &&
+         (int64_t)it.pbase + (int64_t)it.ntok * it.nsplit <= P.max_partials;
+  return ok;
+}
+
 template <int D, bool MIXED>
 __device__ __forceinline__ void attend_body(const AttendParams& P) {
   const int lane = threadIdx.x & 63;
@@ -755,7 +749,8 @@ __device__ __forceinline__ void attend_body(const AttendParams& P) {
     if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(&P.hdr->error, 4u);
     return;
   }
-  const uint32_t num_work = P.hdr->num_work;
+  uint32_t num_work = P.hdr->num_work;
+  if ((uint64_t)num_work > (uint64_t)P.max_items * (uint64_t)P.Hkv) num_work = 0;
   const uint32_t Hkv = (uint32_t)P.Hkv;
   while (true) {
     uint32_t w = 0;
@@ -765,6 +760,7 @@ __device__ __forceinline__ void attend_body(const AttendParams& P) {
     if (w >= num_work) break;
     const WorkItem it = P.items[w / Hkv];
     const int kvh = (int)(w % Hkv);
+    if (!item_ok(P, it)) continue;
     if (MIXED && it.kind == kKindPrefill)
       run_prefill<D, kPrefillColTiles>(P, it, kvh, lane);
     else
@@ -787,6 +783,63 @@ __global__ __launch_bounds__(kAttendThreads)
 __attribute__((amdgpu_waves_per_eu(2, 8)))
 void attend_mixed_kernel(AttendParams P) {
   attend_body<D, true>(P);
+}
+
+// ---------------------------------------------------------------------------
+// merge
+// ---------------------------------------------------------------------------
+
+// One wave per (split tile, kv head): for every column of the tile, combine
+// its splits' (m, l, acc) by log-sum-exp in split order; lanes cover the head
+// dimension.
+template <int D>
+__global__ __launch_bounds__(kAttendThreads) void merge_kernel(AttendParams P) {
+  constexpr int PER = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int nwaves = gridDim.x * (kAttendThreads / 64);
+  const int G = P.G;
+  if (P.hdr->signature != plan_signature(P)) return;
+  uint32_t ntiles = P.hdr->num_split_tiles;
+  if ((int64_t)ntiles > P.max_items) ntiles = 0;
+  const uint32_t nunits = ntiles * (uint32_t)P.Hkv;
+  for (uint32_t u = blockIdx.x * (kAttendThreads / 64) + (threadIdx.x >> 6);
+       u < nunits; u += nwaves) {
+    const int4 tile = P.merge_list[u / P.Hkv];  // tok0, ntok, nsplit, pbase
+    const int kvh = (int)(u % P.Hkv);
+    // same rule as for work items: never follow an entry out of bounds
+    if (tile.x < 0 || tile.y < 1 || tile.x + tile.y > P.num_q_tokens ||
+        tile.z < 2 || tile.w < 0 ||
+        (int64_t)tile.w + (int64_t)tile.y * tile.z > P.max_partials)
+      continue;
+    const int ncols = tile.y * G;
+    for (int c = 0; c < ncols; ++c) {
+      const int tk = c / G;
+      const int h = kvh * G + (c - tk * G);
+      const int64_t slot0 = (int64_t)tile.w + (int64_t)tk * tile.z;
+      float M = -INFINITY;
+      for (int s = 0; s < tile.z; ++s)
+        M = fmaxf(M, P.part_ml[(slot0 + s) * P.Hq + h].x);
+      float den = 0.0f;
+      float num[PER];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) num[e] = 0.0f;
+      for (int s = 0; s < tile.z; ++s) {
+        const float2 ml = P.part_ml[(slot0 + s) * P.Hq + h];
+        const float w = __builtin_amdgcn_exp2f(ml.x - M);
+        den += w * ml.y;
+        const float* ap = P.part_acc + ((slot0 + s) * P.Hq + h) * D + lane * PER;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) num[e] += w * ap[e];
+      }
+      const float inv = 1.0f / den;
+      uint16_t* op = P.out + ((int64_t)(tile.x + tk) * P.Hq + h) * D + lane * PER;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const __bf16 o = (__bf16)(num[e] * inv);
+        op[e] = __builtin_bit_cast(uint16_t, o);
+      }
+    }
+  }
 }
 
 // Resident workgroups per CU of a kernel (queried once per device).
@@ -835,7 +888,7 @@ AttendParams make_params(const AttendArgs& a) {
   char* ws = static_cast<char*>(a.workspace);
   P.hdr = reinterpret_cast<PlanHeader*>(ws);
   P.items = reinterpret_cast<WorkItem*>(ws + a.ws.items);
-  P.counters = reinterpret_cast<uint32_t*>(ws + a.ws.counters);
+  P.merge_list = reinterpret_cast<int4*>(ws + a.ws.merge_list);
   P.part_ml = reinterpret_cast<float2*>(ws + a.ws.part_ml);
   P.part_acc = reinterpret_cast<float*>(ws + a.ws.part_acc);
   P.max_items = a.ws.max_items;
@@ -873,6 +926,24 @@ hipError_t launch_planned(const AttendArgs& a, hipStream_t stream) {
   if (wgs > need) wgs = need;
   if (wgs < 1) wgs = 1;
   hipLaunchKernelGGL(fn, dim3((unsigned)wgs), dim3(kAttendThreads), 0, stream, P);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const AttendArgs& a, hipStream_t stream) {
+  if (a.num_q_tokens == 0 || a.num_seqs == 0) return hipSuccess;
+  const AttendParams P = make_params(a);
+  // at most one wave per (split tile, kv head), never more than the resident
+  // waves of the chip
+  int64_t mwaves = a.ws.max_items * a.num_kv_heads;
+  const int64_t cap = (int64_t)a.num_cus * 8 * 4;
+  if (mwaves > cap) mwaves = cap;
+  const int64_t mwgs = (mwaves + (kAttendThreads / 64) - 1) / (kAttendThreads / 64);
+  if (a.head_dim == 128)
+    hipLaunchKernelGGL(merge_kernel<128>, dim3((unsigned)mwgs), dim3(kAttendThreads),
+                       0, stream, P);
+  else
+    hipLaunchKernelGGL(merge_kernel<64>, dim3((unsigned)mwgs), dim3(kAttendThreads),
+                       0, stream, P);
   return hipGetLastError();
 }
 

@@ -1,6 +1,6 @@
 // C ABI of libpa.so: argument checks, workspace sizing and launches.  The
 // operations and their sources are documented in include/pa.h.
-#include "../../include/pa.h"
+#include "pa.h"
 
 #include <hip/hip_runtime_api.h>
 
@@ -247,6 +247,30 @@ pa_status pa_attend_planned(const void* q, const void* k_cache,
   return ok();
 }
 
+pa_status pa_attend_merge(int32_t num_seqs, int64_t num_q_tokens,
+                          int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t max_query_len,
+                          int32_t max_seq_len, void* out, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  pa::AttendArgs a;
+  bool empty;
+  // metadata pointers are not read by the merge: pass placeholders through
+  // the shared checks
+  static const int32_t kNone[2] = {0, 0};
+  pa_status s = prepare_attend(nullptr, nullptr, nullptr, 0, kNone, 1, kNone,
+                               kNone, num_seqs, num_q_tokens, num_q_heads,
+                               num_kv_heads, head_dim, max_query_len,
+                               max_seq_len, 0.0f, out, workspace,
+                               workspace_bytes, false, &a, &empty);
+  if (s != PA_OK) return s;
+  if (empty) return ok();
+  if (!out) return fail(PA_ERR_NULL, "pa_attend_merge: NULL out");
+  if ((uintptr_t)out & 15) return fail(PA_ERR_SHAPE, "out must be 16-byte aligned");
+  hipError_t e = pa::launch_merge(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pa_attend_merge launch");
+  return ok();
+}
+
 pa_status pa_attend(const void* q, const void* k_cache, const void* v_cache,
                     int64_t num_blocks, const int32_t* block_tables,
                     int32_t max_blocks_per_seq, const int32_t* seq_lens,
@@ -267,6 +291,7 @@ pa_status pa_attend(const void* q, const void* k_cache, const void* v_cache,
   if (empty) return ok();
   hipError_t e = pa::launch_plan(a, static_cast<hipStream_t>(stream));
   if (e == hipSuccess) e = pa::launch_planned(a, static_cast<hipStream_t>(stream));
+  if (e == hipSuccess) e = pa::launch_merge(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "pa_attend launch");
   return ok();
 }

@@ -35,7 +35,7 @@ struct WorkItem {
   int32_t split;    // split index of this key range
   int32_t nsplit;   // splits of this tile (1: output written directly)
   int32_t pbase;    // partial slot of (tile token 0, split 0); -1 if unsplit
-  int32_t counter;  // arrival counter of the tile (x num_kv_heads); -1 if unsplit
+  int32_t counter;  // index of the tile in the merge list; -1 if unsplit
   int32_t pad[6];
 };
 static_assert(sizeof(WorkItem) == 64, "WorkItem is one 64-byte scalar load");
@@ -46,14 +46,14 @@ struct PlanHeader {
   uint32_t num_work;      // items * num_kv_heads
   uint32_t num_items;
   uint32_t error;         // bit0: capacity exceeded, bit1: bad request skipped
-  uint32_t num_counters;  // split tiles * num_kv_heads
+  uint32_t num_split_tiles;  // entries of the merge list
   uint32_t signature;     // hash of the arguments the plan was made for
 };
 
 // Byte offsets of the workspace sections.
 struct WorkspaceLayout {
   size_t items;         // WorkItem[max_items]
-  size_t counters;      // uint32[max_items * Hkv]  split-tile arrival counters
+  size_t merge_list;    // int4[max_items]  split tiles: tok0, ntok, nsplit, pbase
   size_t part_ml;       // float2[max_partials * Hq]  (running max, sum)
   size_t part_acc;      // float[max_partials * Hq * D]
   size_t total;
@@ -100,8 +100,8 @@ inline WorkspaceLayout workspace_layout(int32_t num_seqs, int64_t num_q_tokens,
   size_t off = align256(sizeof(PlanHeader));
   w.items = off;
   off = align256(off + sizeof(WorkItem) * (size_t)w.max_items);
-  w.counters = off;
-  off = align256(off + sizeof(uint32_t) * (size_t)w.max_items * num_kv_heads);
+  w.merge_list = off;
+  off = align256(off + 16 * (size_t)w.max_items);
   w.part_ml = off;
   off = align256(off + sizeof(float) * 2 * (size_t)w.max_partials * num_q_heads);
   w.part_acc = off;
@@ -155,5 +155,7 @@ struct AttendArgs {
 hipError_t launch_plan(const AttendArgs& a, hipStream_t stream);
 // Attention over the plan in the workspace (one persistent kernel).
 hipError_t launch_planned(const AttendArgs& a, hipStream_t stream);
+// Split-K merge of the partials the attention kernel left in the workspace.
+hipError_t launch_merge(const AttendArgs& a, hipStream_t stream);
 
 }  // namespace pa

@@ -64,7 +64,8 @@ class Uploaded:
         pa.write_kv(self.k_new, self.v_new, self.new_slots, self.k_cache,
                     self.v_cache)
 
-    def attend(self, out=None, k_cache=None, v_cache=None, planned=False):
+    def attend(self, out=None, k_cache=None, v_cache=None, planned=False,
+               merge=True):
         w = self.w
         return pa.attend(self.q, self.k_cache if k_cache is None else k_cache,
                          self.v_cache if v_cache is None else v_cache,
@@ -72,7 +73,13 @@ class Uploaded:
                          w.max_query_len, w.max_seq_len,
                          num_kv_heads=w.num_kv_heads,
                          out=self.out if out is None else out,
-                         workspace=self.workspace, planned=planned)
+                         workspace=self.workspace, planned=planned, merge=merge)
+
+    def merge(self, out=None):
+        w = self.w
+        pa.attend_merge(self.out if out is None else out, w.num_seqs,
+                        w.num_kv_heads, w.max_query_len, w.max_seq_len,
+                        self.workspace)
 
     def plan(self):
         w = self.w
