@@ -154,34 +154,47 @@ __device__ SeqCounts seq_counts(const AttendParams& P, int b) {
   return c;
 }
 
-// Exclusive scan over the workgroup; *total receives the sum.
-__device__ int block_scan(int x, int* lds, int* total) {
+// Four exclusive scans at once (one set of barriers); tot receives the sums.
+__device__ int4 block_scan4(int4 x, int4* lds, int4* tot) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   constexpr int kWaves = kPlanThreads / 64;
-  int incl = x;
+  int4 incl = x;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
+    const int y0 = __shfl_up(incl.x, off), y1 = __shfl_up(incl.y, off);
+    const int y2 = __shfl_up(incl.z, off), y3 = __shfl_up(incl.w, off);
+    if (lane >= off) {
+      incl.x += y0;
+      incl.y += y1;
+      incl.z += y2;
+      incl.w += y3;
+    }
   }
   if (lane == 63) lds[wid] = incl;
   __syncthreads();
   if (wid == 0) {
-    const int v = lane < kWaves ? lds[lane] : 0;
-    int vi = v;
+    const int4 v = lane < kWaves ? lds[lane] : make_int4(0, 0, 0, 0);
+    int4 vi = v;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(vi, off);
-      if (lane >= off) vi += y;
+      const int y0 = __shfl_up(vi.x, off), y1 = __shfl_up(vi.y, off);
+      const int y2 = __shfl_up(vi.z, off), y3 = __shfl_up(vi.w, off);
+      if (lane >= off) {
+        vi.x += y0;
+        vi.y += y1;
+        vi.z += y2;
+        vi.w += y3;
+      }
     }
-    if (lane < kWaves) lds[lane] = vi - v;
+    if (lane < kWaves) lds[lane] = make_int4(vi.x - v.x, vi.y - v.y, vi.z - v.z, vi.w - v.w);
     if (lane == kWaves - 1) lds[kWaves] = vi;
   }
   __syncthreads();
-  const int res = incl - x + lds[wid];
-  *total = lds[kWaves];
+  const int4 base = lds[wid];
+  *tot = lds[kWaves];
   __syncthreads();
-  return res;
+  return make_int4(incl.x - x.x + base.x, incl.y - x.y + base.y,
+                   incl.z - x.z + base.z, incl.w - x.w + base.w);
 }
 
 __device__ __forceinline__ void put_item(const AttendParams& P, int idx, int b,
@@ -219,12 +232,14 @@ __device__ void emit_seq(const AttendParams& P, int b, const SeqCounts& c,
     if (ns > 1) P.merge_list[cbase] = make_int4(q0, Q, ns, pbase);
     return;
   }
-  // split prefill: longest tiles (latest tokens) first
+  // prefill (split, or unsplit when the workgroup's list was full): longest
+  // tiles (latest tokens) first
   int icur = ibase, pcur = pbase, ccur = cbase;
   for (int t = c.ntiles - 1; t >= 0; --t) {
     const int ntok = min(c.tq, Q - t * c.tq);
     const int pmax1 = L - Q + t * c.tq + ntok;
-    const int ns = (pmax1 + c.splitlen - 1) / c.splitlen;
+    const int span = c.splitlen ? c.splitlen : pmax1;
+    const int ns = (pmax1 + span - 1) / span;
     const int pb = ns > 1 ? pcur : -1;
     const int cb = ns > 1 ? ccur : -1;
     if (ns > 1) {
@@ -233,13 +248,30 @@ __device__ void emit_seq(const AttendParams& P, int b, const SeqCounts& c,
       ccur += 1;
     }
     for (int s = 0; s < ns; ++s)
-      put_item(P, icur++, b, q0 + t * c.tq, ntok, kKindPrefill,
-               s * c.splitlen, min(pmax1, (s + 1) * c.splitlen), s, ns, pb, cb);
+      put_item(P, icur++, b, q0 + t * c.tq, ntok, kKindPrefill, s * span,
+               min(pmax1, (s + 1) * span), s, ns, pb, cb);
   }
 }
 
+// Registers the item bases of request b: emitted now by this thread, or
+// queued for the whole workgroup (unsplit prefill: many tiles).
+__device__ __forceinline__ void place_seq(const AttendParams& P, int b,
+                                          const SeqCounts& c, int ibase,
+                                          int pbase, int cbase, int* coop_n,
+                                          int* coop_b, int* coop_base) {
+  if (c.kind == kKindPrefill && c.splitlen == 0) {
+    const int k = atomicAdd(coop_n, 1);
+    if (k < kMaxCoop) {
+      coop_b[k] = b;
+      coop_base[k] = ibase;
+      return;
+    }
+  }
+  emit_seq(P, b, c, ibase, pbase, cbase);
+}
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttendParams P) {
-  __shared__ int lds[kPlanThreads / 64 + 1];
+  __shared__ int4 lds[kPlanThreads / 64 + 1];
   __shared__ int coop_n;
   __shared__ int coop_b[kMaxCoop];
   __shared__ int coop_base[kMaxCoop];
@@ -250,52 +282,58 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttendParams P) {
     P.hdr->signature = plan_signature(P);
     coop_n = 0;
   }
-  // sweep 1: totals (prefill items go first, decode items after them)
-  int pre_total = 0, all_items = 0, all_partials = 0, all_split = 0;
-  for (int base = 0; base < P.num_seqs; base += kPlanThreads) {
-    const int b = base + tid;
+  // scan lanes: x = prefill items, y = decode items, z = partial slots,
+  // w = split tiles.  Prefill items go first, decode items after them.
+  int4 total;
+  bool fits;
+  if (P.num_seqs <= kPlanThreads) {
+    // one sweep: every request handled by one thread
+    const int b = tid;
     SeqCounts c{-1, 0, 0, 0, 0, 0, 0};
     if (b < P.num_seqs) c = seq_counts(P, b);
-    int t0, t1, t2, t3;
-    block_scan(c.kind == kKindPrefill ? c.items : 0, lds, &t0);
-    block_scan(c.items, lds, &t1);
-    block_scan(c.partials, lds, &t2);
-    block_scan(c.split_tiles, lds, &t3);
-    pre_total += t0;
-    all_items += t1;
-    all_partials += t2;
-    all_split += t3;
-  }
-  const bool fits = all_items <= P.max_items && all_partials <= P.max_partials;
-  // sweep 2: write
-  int pre_carry = 0, dec_carry = 0, part_carry = 0, split_carry = 0;
-  for (int base = 0; base < P.num_seqs; base += kPlanThreads) {
-    const int b = base + tid;
-    SeqCounts c{-1, 0, 0, 0, 0, 0, 0};
-    if (b < P.num_seqs) c = seq_counts(P, b);
-    int tp, td, tpart, tsplit;
-    const int ep = block_scan(c.kind == kKindPrefill ? c.items : 0, lds, &tp);
-    const int ed = block_scan(c.kind == kKindDecode ? c.items : 0, lds, &td);
-    const int epart = block_scan(c.partials, lds, &tpart);
-    const int esplit = block_scan(c.split_tiles, lds, &tsplit);
-    if (fits && c.kind >= 0) {
-      const int ibase = c.kind == kKindPrefill ? pre_carry + ep
-                                               : pre_total + dec_carry + ed;
-      bool self = true;
-      if (c.kind == kKindPrefill && c.splitlen == 0) {
-        const int k = atomicAdd(&coop_n, 1);
-        if (k < kMaxCoop) {
-          coop_b[k] = b;
-          coop_base[k] = ibase;
-          self = false;
-        }
-      }
-      if (self) emit_seq(P, b, c, ibase, part_carry + epart, split_carry + esplit);
+    const int4 mine = make_int4(c.kind == kKindPrefill ? c.items : 0,
+                                c.kind == kKindDecode ? c.items : 0, c.partials,
+                                c.split_tiles);
+    const int4 e = block_scan4(mine, lds, &total);
+    fits = total.x + total.y <= P.max_items && total.z <= P.max_partials;
+    if (fits && c.kind >= 0)
+      place_seq(P, b, c, c.kind == kKindPrefill ? e.x : total.x + e.y, e.z, e.w,
+                &coop_n, coop_b, coop_base);
+  } else {
+    // two sweeps over chunks of requests: totals first, then placement
+    total = make_int4(0, 0, 0, 0);
+    for (int base = 0; base < P.num_seqs; base += kPlanThreads) {
+      const int b = base + tid;
+      SeqCounts c{-1, 0, 0, 0, 0, 0, 0};
+      if (b < P.num_seqs) c = seq_counts(P, b);
+      int4 t;
+      block_scan4(make_int4(c.kind == kKindPrefill ? c.items : 0,
+                            c.kind == kKindDecode ? c.items : 0, c.partials,
+                            c.split_tiles), lds, &t);
+      total.x += t.x;
+      total.y += t.y;
+      total.z += t.z;
+      total.w += t.w;
     }
-    pre_carry += tp;
-    dec_carry += td;
-    part_carry += tpart;
-    split_carry += tsplit;
+    fits = total.x + total.y <= P.max_items && total.z <= P.max_partials;
+    int4 carry = make_int4(0, 0, 0, 0);
+    for (int base = 0; base < P.num_seqs; base += kPlanThreads) {
+      const int b = base + tid;
+      SeqCounts c{-1, 0, 0, 0, 0, 0, 0};
+      if (b < P.num_seqs) c = seq_counts(P, b);
+      int4 t;
+      const int4 e = block_scan4(make_int4(c.kind == kKindPrefill ? c.items : 0,
+                                           c.kind == kKindDecode ? c.items : 0,
+                                           c.partials, c.split_tiles), lds, &t);
+      if (fits && c.kind >= 0)
+        place_seq(P, b, c,
+                  c.kind == kKindPrefill ? carry.x + e.x : total.x + carry.y + e.y,
+                  carry.z + e.z, carry.w + e.w, &coop_n, coop_b, coop_base);
+      carry.x += t.x;
+      carry.y += t.y;
+      carry.z += t.z;
+      carry.w += t.w;
+    }
   }
   __syncthreads();
   // unsplit prefill requests: every thread emits some of their tiles
@@ -314,9 +352,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttendParams P) {
     }
   }
   if (tid == 0) {
+    const int all_items = total.x + total.y;
     P.hdr->num_items = fits ? (uint32_t)all_items : 0u;
     P.hdr->num_work = fits ? (uint32_t)all_items * (uint32_t)P.Hkv : 0u;
-    P.hdr->num_split_tiles = fits ? (uint32_t)all_split : 0u;
+    P.hdr->num_split_tiles = fits ? (uint32_t)total.w : 0u;
     if (!fits) atomicOr(&P.hdr->error, 1u);
   }
 }
@@ -789,12 +828,15 @@ void attend_mixed_kernel(AttendParams P) {
 // merge
 // ---------------------------------------------------------------------------
 
-// One wave per (split tile, kv head): for every column of the tile, combine
-// its splits' (m, l, acc) by log-sum-exp in split order; lanes cover the head
-// dimension.
+// One wave per (split tile, kv head).  Lanes cover (column, 8 dims): a wave
+// merges 64 / (D/8) columns at a time.  Each column's splits are combined by
+// an online log-sum-exp in split order (a fixed order: the result does not
+// depend on timing), with the loads of 8 splits in flight per step.
 template <int D>
 __global__ __launch_bounds__(kAttendThreads) void merge_kernel(AttendParams P) {
-  constexpr int PER = D / 64;
+  constexpr int LPC = D / 8;      // lanes per column
+  constexpr int CPW = 64 / LPC;   // columns per wave pass
+  constexpr int SB = 8;           // splits per step
   const int lane = threadIdx.x & 63;
   const int nwaves = gridDim.x * (kAttendThreads / 64);
   const int G = P.G;
@@ -802,6 +844,8 @@ __global__ __launch_bounds__(kAttendThreads) void merge_kernel(AttendParams P) {
   uint32_t ntiles = P.hdr->num_split_tiles;
   if ((int64_t)ntiles > P.max_items) ntiles = 0;
   const uint32_t nunits = ntiles * (uint32_t)P.Hkv;
+  const int cl = lane / LPC;          // column within the pass
+  const int d0 = (lane % LPC) * 8;    // first of the lane's 8 dims
   for (uint32_t u = blockIdx.x * (kAttendThreads / 64) + (threadIdx.x >> 6);
        u < nunits; u += nwaves) {
     const int4 tile = P.merge_list[u / P.Hkv];  // tok0, ntok, nsplit, pbase
@@ -812,32 +856,53 @@ __global__ __launch_bounds__(kAttendThreads) void merge_kernel(AttendParams P) {
         (int64_t)tile.w + (int64_t)tile.y * tile.z > P.max_partials)
       continue;
     const int ncols = tile.y * G;
-    for (int c = 0; c < ncols; ++c) {
+    const int nsplit = tile.z;
+    for (int c0 = 0; c0 < ncols; c0 += CPW) {
+      const int c = c0 + cl;
+      if (c >= ncols) continue;
       const int tk = c / G;
       const int h = kvh * G + (c - tk * G);
-      const int64_t slot0 = (int64_t)tile.w + (int64_t)tk * tile.z;
-      float M = -INFINITY;
-      for (int s = 0; s < tile.z; ++s)
-        M = fmaxf(M, P.part_ml[(slot0 + s) * P.Hq + h].x);
-      float den = 0.0f;
-      float num[PER];
+      const int64_t slot0 = (int64_t)tile.w + (int64_t)tk * nsplit;
+      float M = -INFINITY, den = 0.0f;
+      f32x4 n0 = {0.f, 0.f, 0.f, 0.f}, n1 = {0.f, 0.f, 0.f, 0.f};
+      for (int s0 = 0; s0 < nsplit; s0 += SB) {
+        float2 ml[SB];
+        f32x4 a0[SB], a1[SB];
 #pragma unroll
-      for (int e = 0; e < PER; ++e) num[e] = 0.0f;
-      for (int s = 0; s < tile.z; ++s) {
-        const float2 ml = P.part_ml[(slot0 + s) * P.Hq + h];
-        const float w = __builtin_amdgcn_exp2f(ml.x - M);
-        den += w * ml.y;
-        const float* ap = P.part_acc + ((slot0 + s) * P.Hq + h) * D + lane * PER;
+        for (int k = 0; k < SB; ++k) {
+          const int sp = s0 + k;
+          if (sp < nsplit) {
+            const int64_t row = (slot0 + sp) * P.Hq + h;
+            ml[k] = P.part_ml[row];
+            const f32x4* ap = reinterpret_cast<const f32x4*>(P.part_acc + row * D + d0);
+            a0[k] = ap[0];
+            a1[k] = ap[1];
+          } else {
+            ml[k] = make_float2(-INFINITY, 0.0f);
+            a0[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+            a1[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+        }
 #pragma unroll
-        for (int e = 0; e < PER; ++e) num[e] += w * ap[e];
+        for (int k = 0; k < SB; ++k) {
+          const float mn = fmaxf(M, ml[k].x);
+          const float mu = (mn == -INFINITY) ? 0.0f : mn;
+          const float c_old = __builtin_amdgcn_exp2f(M - mu);
+          const float c_new = __builtin_amdgcn_exp2f(ml[k].x - mu);
+          den = den * c_old + ml[k].y * c_new;
+          n0 = n0 * c_old + a0[k] * c_new;
+          n1 = n1 * c_old + a1[k] * c_new;
+          M = mn;
+        }
       }
       const float inv = 1.0f / den;
-      uint16_t* op = P.out + ((int64_t)(tile.x + tk) * P.Hq + h) * D + lane * PER;
+      bf16x8 o;
 #pragma unroll
-      for (int e = 0; e < PER; ++e) {
-        const __bf16 o = (__bf16)(num[e] * inv);
-        op[e] = __builtin_bit_cast(uint16_t, o);
+      for (int i = 0; i < 4; ++i) {
+        o[i] = (__bf16)(n0[i] * inv);
+        o[i + 4] = (__bf16)(n1[i] * inv);
       }
+      *reinterpret_cast<bf16x8*>(P.out + ((int64_t)(tile.x + tk) * P.Hq + h) * D + d0) = o;
     }
   }
 }

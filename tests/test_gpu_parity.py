@@ -267,6 +267,37 @@ def test_validate_metadata_on_device():
                              w.max_query_len, w.max_seq_len, w.num_blocks)
 
 
+def test_many_requests_two_sweep_plan():
+    # more requests than the plan's workgroup has threads
+    rng = np.random.default_rng(20)
+    B = 1500
+    L = rng.integers(1, 1200, size=B)
+    Q = np.minimum(L, rng.choice([0, 1, 1, 1, 2, 3], size=B))
+    w = W.make_workload("many", L, Q, 8, 2, 64, seed=21)
+    out = tensor_bits(Uploaded(w).attend())
+    kc, vc = oracle_pool(w)
+    rows = sample_rows(w, 400, seed=22)
+    ref = oracle.attend_rows(w.q, kc, vc, w.block_tables, w.seq_lens,
+                             w.query_start_loc, w.num_kv_heads, w.scale, rows)
+    check_close(out[rows[:, 0], rows[:, 1]], ref, "1500 requests")
+
+
+def test_many_unsplit_prefills():
+    # more unsplit prefill requests than the plan emits cooperatively (64)
+    B = 70
+    L = np.full(B, 1024)
+    Q = np.full(B, 1024)
+    Q[::7] = 1000
+    w = W.make_workload("prefills", L, Q, 16, 16, 64, seed=23)
+    out = tensor_bits(Uploaded(w).attend())
+    assert np.isfinite(to64(out)).all()
+    kc, vc = oracle_pool(w)
+    rows = sample_rows(w, 300, seed=24)
+    ref = oracle.attend_rows(w.q, kc, vc, w.block_tables, w.seq_lens,
+                             w.query_start_loc, w.num_kv_heads, w.scale, rows)
+    check_close(out[rows[:, 0], rows[:, 1]], ref, "70 prefill chunks")
+
+
 # ---- the five synthetic configurations ---------------------------------------------
 
 @pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
