@@ -51,6 +51,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+// block buffers of the decode pipeline (blocks in flight + 1)
+constexpr int kDecodeStages = 3;
 
 struct AttendParams {
   const uint16_t* q;
@@ -98,7 +100,7 @@ __device__ __forceinline__ uint32_t plan_signature(const AttendParams& P) {
 }
 
 constexpr int kPlanThreads = 1024;
-static_assert(kSplitDecode / kBlock <= 64, "a decode unit's block ids fit one wave");
+static_assert(kSplitDecodeLong / kBlock <= 64, "a decode unit's block ids fit one wave");
 constexpr int kMaxCoop = 64;  // unsplit prefill requests emitted by all threads
 
 struct SeqCounts {
@@ -110,6 +112,14 @@ struct SeqCounts {
   int partials;
   int split_tiles;  // tiles with more than one split
 };
+
+// Queue regions: prefill items, then full-length decode splits, then the
+// (shorter) last split of every decode request: longest units first.
+__device__ __forceinline__ int4 scan_lanes(const SeqCounts& c) {
+  const bool dec = c.kind == kKindDecode;
+  return make_int4(c.kind == kKindPrefill ? c.items : 0, dec ? c.items - 1 : 0,
+                   c.partials, c.split_tiles);
+}
 
 __device__ SeqCounts seq_counts(const AttendParams& P, int b) {
   SeqCounts c{-1, 0, 0, 0, 0, 0, 0};
@@ -127,8 +137,8 @@ __device__ SeqCounts seq_counts(const AttendParams& P, int b) {
     c.kind = kKindDecode;
     c.ntiles = 1;
     c.tq = Q;
-    c.splitlen = kSplitDecode;
-    const int ns = (L + kSplitDecode - 1) / kSplitDecode;
+    c.splitlen = L > kLongDecode ? kSplitDecodeLong : kSplitDecode;
+    const int ns = (L + c.splitlen - 1) / c.splitlen;
     c.items = ns;
     c.partials = ns > 1 ? Q * ns : 0;
     c.split_tiles = ns > 1 ? 1 : 0;
@@ -219,15 +229,18 @@ __device__ __forceinline__ void put_item(const AttendParams& P, int idx, int b,
 
 // Items of one request, emitted by one thread (decode requests and prefill
 // requests with split key ranges, which have few tiles).
+// ibase: first item slot (decode: of the full-length splits); ilast: slot of
+// a decode request's last split.
 __device__ void emit_seq(const AttendParams& P, int b, const SeqCounts& c,
-                         int ibase, int pbase, int cbase) {
+                         int ibase, int ilast, int pbase, int cbase) {
   const int q0 = P.qsl[b];
   const int Q = P.qsl[b + 1] - q0, L = P.seq_lens[b];
   if (c.kind == kKindDecode) {
     const int ns = c.items;
+    const int sl = c.splitlen;
     for (int s = 0; s < ns; ++s)
-      put_item(P, ibase + s, b, q0, Q, kKindDecode, s * kSplitDecode,
-               min(L, (s + 1) * kSplitDecode), s, ns, ns > 1 ? pbase : -1,
+      put_item(P, s == ns - 1 ? ilast : ibase + s, b, q0, Q, kKindDecode,
+               s * sl, min(L, (s + 1) * sl), s, ns, ns > 1 ? pbase : -1,
                ns > 1 ? cbase : -1);
     if (ns > 1) P.merge_list[cbase] = make_int4(q0, Q, ns, pbase);
     return;
@@ -257,8 +270,9 @@ __device__ void emit_seq(const AttendParams& P, int b, const SeqCounts& c,
 // queued for the whole workgroup (unsplit prefill: many tiles).
 __device__ __forceinline__ void place_seq(const AttendParams& P, int b,
                                           const SeqCounts& c, int ibase,
-                                          int pbase, int cbase, int* coop_n,
-                                          int* coop_b, int* coop_base) {
+                                          int ilast, int pbase, int cbase,
+                                          int* coop_n, int* coop_b,
+                                          int* coop_base) {
   if (c.kind == kKindPrefill && c.splitlen == 0) {
     const int k = atomicAdd(coop_n, 1);
     if (k < kMaxCoop) {
@@ -267,7 +281,7 @@ __device__ __forceinline__ void place_seq(const AttendParams& P, int b,
       return;
     }
   }
-  emit_seq(P, b, c, ibase, pbase, cbase);
+  emit_seq(P, b, c, ibase, ilast, pbase, cbase);
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttendParams P) {
@@ -284,55 +298,56 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttendParams P) {
   }
   // scan lanes: x = prefill items, y = decode items, z = partial slots,
   // w = split tiles.  Prefill items go first, decode items after them.
-  int4 total;
+  int4 total, total2;
   bool fits;
   if (P.num_seqs <= kPlanThreads) {
     // one sweep: every request handled by one thread
     const int b = tid;
     SeqCounts c{-1, 0, 0, 0, 0, 0, 0};
     if (b < P.num_seqs) c = seq_counts(P, b);
-    const int4 mine = make_int4(c.kind == kKindPrefill ? c.items : 0,
-                                c.kind == kKindDecode ? c.items : 0, c.partials,
-                                c.split_tiles);
-    const int4 e = block_scan4(mine, lds, &total);
-    fits = total.x + total.y <= P.max_items && total.z <= P.max_partials;
+    const int4 e = block_scan4(scan_lanes(c), lds, &total);
+    const int4 e2 = block_scan4(make_int4(c.kind == kKindDecode, 0, 0, 0), lds, &total2);
+    fits = total.x + total.y + total2.x <= P.max_items && total.z <= P.max_partials;
     if (fits && c.kind >= 0)
-      place_seq(P, b, c, c.kind == kKindPrefill ? e.x : total.x + e.y, e.z, e.w,
-                &coop_n, coop_b, coop_base);
+      place_seq(P, b, c, c.kind == kKindPrefill ? e.x : total.x + e.y,
+                total.x + total.y + e2.x, e.z, e.w, &coop_n, coop_b, coop_base);
   } else {
     // two sweeps over chunks of requests: totals first, then placement
     total = make_int4(0, 0, 0, 0);
+    total2 = make_int4(0, 0, 0, 0);
     for (int base = 0; base < P.num_seqs; base += kPlanThreads) {
       const int b = base + tid;
       SeqCounts c{-1, 0, 0, 0, 0, 0, 0};
       if (b < P.num_seqs) c = seq_counts(P, b);
-      int4 t;
-      block_scan4(make_int4(c.kind == kKindPrefill ? c.items : 0,
-                            c.kind == kKindDecode ? c.items : 0, c.partials,
-                            c.split_tiles), lds, &t);
+      int4 t, t2;
+      block_scan4(scan_lanes(c), lds, &t);
+      block_scan4(make_int4(c.kind == kKindDecode, 0, 0, 0), lds, &t2);
       total.x += t.x;
       total.y += t.y;
       total.z += t.z;
       total.w += t.w;
+      total2.x += t2.x;
     }
-    fits = total.x + total.y <= P.max_items && total.z <= P.max_partials;
+    fits = total.x + total.y + total2.x <= P.max_items && total.z <= P.max_partials;
     int4 carry = make_int4(0, 0, 0, 0);
+    int carry_last = 0;
     for (int base = 0; base < P.num_seqs; base += kPlanThreads) {
       const int b = base + tid;
       SeqCounts c{-1, 0, 0, 0, 0, 0, 0};
       if (b < P.num_seqs) c = seq_counts(P, b);
-      int4 t;
-      const int4 e = block_scan4(make_int4(c.kind == kKindPrefill ? c.items : 0,
-                                           c.kind == kKindDecode ? c.items : 0,
-                                           c.partials, c.split_tiles), lds, &t);
+      int4 t, t2;
+      const int4 e = block_scan4(scan_lanes(c), lds, &t);
+      const int4 e2 = block_scan4(make_int4(c.kind == kKindDecode, 0, 0, 0), lds, &t2);
       if (fits && c.kind >= 0)
         place_seq(P, b, c,
                   c.kind == kKindPrefill ? carry.x + e.x : total.x + carry.y + e.y,
-                  carry.z + e.z, carry.w + e.w, &coop_n, coop_b, coop_base);
+                  total.x + total.y + carry_last + e2.x, carry.z + e.z,
+                  carry.w + e.w, &coop_n, coop_b, coop_base);
       carry.x += t.x;
       carry.y += t.y;
       carry.z += t.z;
       carry.w += t.w;
+      carry_last += t2.x;
     }
   }
   __syncthreads();
@@ -352,7 +367,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttendParams P) {
     }
   }
   if (tid == 0) {
-    const int all_items = total.x + total.y;
+    const int all_items = total.x + total.y + total2.x;
     P.hdr->num_items = fits ? (uint32_t)all_items : 0u;
     P.hdr->num_work = fits ? (uint32_t)all_items * (uint32_t)P.Hkv : 0u;
     P.hdr->num_split_tiles = fits ? (uint32_t)total.w : 0u;
@@ -366,6 +381,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttendParams P) {
 
 __device__ __forceinline__ bf16x8 load16(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// Non-temporal load: decode reads each K/V tile once, so it should not
+// displace cached data (the streaming read ceiling is ~10% higher with it).
+__device__ __forceinline__ bf16x8 load16_stream(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p));
 }
 
 __device__ __forceinline__ bf16x8 zero8() {
@@ -517,10 +538,10 @@ struct KVBlock {
   bf16x8 v[D / 32];  // lane's 4 keys at dims d and d + D/2
 };
 
-// Decode path: one block (16 keys) per step, the next block's loads in flight
-// while the current one is computed.  PV on 16x16x16 MFMA: the score
+// Decode path: one block (16 keys) per step, NB-1 later blocks' loads in
+// flight while the current one is computed.  PV on 16x16x16 MFMA: the score
 // registers are its B operand as they stand.
-template <int D, int CT>
+template <int D, int CT, int NB>
 __device__ __forceinline__ void run_decode(const AttendParams& P,
                                            const WorkItem& it, int kvh,
                                            int lane) {
@@ -549,7 +570,7 @@ __device__ __forceinline__ void run_decode(const AttendParams& P,
 
   const int jb0 = it.kv0 >> 4;
   const int jb1 = (it.kv1 + kBlock - 1) >> 4;
-  const int nblk = jb1 - jb0;  // <= kSplitDecode / 16 <= 64
+  const int nblk = jb1 - jb0;  // <= kSplitDecodeLong / 16 <= 64
   const int32_t* btrow = P.bt + (int64_t)b * P.bt_stride;
   const int64_t tile_elems = (int64_t)kBlock * D;
   // All physical block ids of the unit, one per lane, loaded once: inside the
@@ -565,9 +586,9 @@ __device__ __forceinline__ void run_decode(const AttendParams& P,
     const uint16_t* kp = P.k_cache + off;
     const uint16_t* vp = P.v_cache + off;
 #pragma unroll
-    for (int c = 0; c < KC; ++c) buf.k[c] = load16(kp + c * 512 + lane * 8);
+    for (int c = 0; c < KC; ++c) buf.k[c] = load16_stream(kp + c * 512 + lane * 8);
 #pragma unroll
-    for (int c = 0; c < KC; ++c) buf.v[c] = load16(vp + c * 512 + (4 * r + g) * 8);
+    for (int c = 0; c < KC; ++c) buf.v[c] = load16_stream(vp + c * 512 + (4 * r + g) * 8);
   };
 
   auto compute = [&](KVBlock<D>& buf, int j) {
@@ -615,21 +636,26 @@ __device__ __forceinline__ void run_decode(const AttendParams& P,
   };
 
   if (nblk > 0) {
-    // Every path into the loop header has exactly one block's loads in
-    // flight (the prefetch is unconditional, clamped to the last block, and
-    // the loop has no early exit), so the compiler's waits stop at the
-    // current block and never drain the prefetch.  With an even block count
-    // the last prefetch re-reads the block just loaded (an L2 hit).
-    KVBlock<D> b0, b1;
-    issue(b0, 0);
+    // Ring of NB block buffers, NB-1 blocks in flight while one is computed.
+    // Every path into the loop header has the same loads in flight (the
+    // prefetch is unconditional, clamped to the last block, and the loop has
+    // no early exit), so the compiler's waits stop at the block being
+    // computed and never drain the prefetches.  Clamped prefetches past the
+    // end re-read the last block (an L2 hit).
+    KVBlock<D> buf[NB];
+#pragma unroll
+    for (int k = 0; k < NB - 1; ++k) issue(buf[k], min(k, nblk - 1));
     int j = 0;
-    for (; j + 1 < nblk; j += 2) {
-      issue(b1, j + 1);
-      compute(b0, j);
-      issue(b0, min(j + 2, nblk - 1));
-      compute(b1, j + 1);
+    for (; j + NB <= nblk; j += NB) {
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        issue(buf[(k + NB - 1) % NB], min(j + k + NB - 1, nblk - 1));
+        compute(buf[k], j + k);
+      }
     }
-    if (j < nblk) compute(b0, j);
+#pragma unroll
+    for (int k = 0; k < NB - 1; ++k)
+      if (j + k < nblk) compute(buf[k], j + k);
   }
   finish_unit<D, CT>(P, it, kvh, lane, acc, mrun, lsum);
 }
@@ -774,7 +800,7 @@ __device__ __forceinline__ bool item_ok(const AttendParams& P,
             (it.kv0 & 31) == 0 && it.kv1 > it.kv0 && it.kv1 <= P.max_seq_len &&
             ((it.kv1 + kBlock - 1) / kBlock) <= P.bt_stride &&
             it.nsplit >= 1 && it.split >= 0 && it.split < it.nsplit;
-  if (it.kind != kKindPrefill) ok = ok && (it.kv1 - it.kv0) <= kSplitDecode;
+  if (it.kind != kKindPrefill) ok = ok && (it.kv1 - it.kv0) <= kSplitDecodeLong;
   if (it.nsplit > 1)
     ok = ok && it.pbase >= 0 &&
          (int64_t)it.pbase + (int64_t)it.ntok * it.nsplit <= P.max_partials;
@@ -803,15 +829,15 @@ __device__ __forceinline__ void attend_body(const AttendParams& P) {
     if (MIXED && it.kind == kKindPrefill)
       run_prefill<D, kPrefillColTiles>(P, it, kvh, lane);
     else
-      run_decode<D, kDecodeColTiles>(P, it, kvh, lane);
+      run_decode<D, kDecodeColTiles, kDecodeStages>(P, it, kvh, lane);
   }
 }
 
-// Decode-only batches: more resident waves than the unified kernel (four per
-// SIMD for head_dim 64, three for 128, where four would spill).
+// Decode-only batches: registers for the 3-stage pipeline (two waves per
+// SIMD for head_dim 128, four for 64).
 template <int D>
 __global__ __launch_bounds__(kAttendThreads)
-__attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 3, 8)))
+__attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2, 8)))
 void attend_decode_kernel(AttendParams P) {
   attend_body<D, false>(P);
 }

@@ -11,7 +11,12 @@ namespace pa {
 constexpr int kBlock = 16;  // tokens per KV block
 
 // Work decomposition of pa_attend (see attend.hip).
-constexpr int kSplitDecode = 512;    // logical tokens per decode split
+// Decode splits: 512 logical tokens, 1024 for requests longer than
+// kLongDecode (fewer, longer units where there are many anyway).  The split
+// length depends on the request's own length only.
+constexpr int kSplitDecode = 512;
+constexpr int kSplitDecodeLong = 1024;
+constexpr int kLongDecode = 8192;
 constexpr int kSplitPrefill = 2048;  // logical tokens per prefill split
 // A prefill request is split along its keys only if it has fewer than this
 // many (query tile x kv head) work units on its own.
