@@ -12,7 +12,7 @@
  *                its block table.
  *
  * Where the operations are defined:
- *   - "Inside vLLM" (supercharleszhu.github.io), Part 3 Runtime, Aside "KV
+ *   - "vLLM v1 Deep Dive" (supercharleszhu.github.io), Part 3 Runtime, Aside "KV
  *     cache and prefix caching": the pool of fixed-size blocks; slot_mapping
  *     gives, per new token of the flattened batch, the slot
  *     block_id * block_size + offset that its K/V is written to; attention
@@ -21,7 +21,7 @@
  *     prefix + new tokens and a decode query all of its blocks.
  *   - Same page, Step 4c "Mixed batches": query_start_loc is the prefix sum of
  *     per-request scheduled token counts over the flattened batch.
- *   - "vLLM internals study" (anthony-chaudhary.github.io) section 2.1: the
+ *   - "vLLM: An Exhaustive Technical Study for Kernel Engineers" (anthony-chaudhary.github.io) section 2.1: the
  *     block table maps logical block index to physical block id; the write
  *     slot is block number * block_size + block offset.  Section 2.4: query
  *     heads that share one KV head are processed together (GQA).
@@ -128,8 +128,8 @@ const char *pa_last_error(void);
  *                   above)
  *   head_dim        64 or 128
  *
- * Source: "Inside vLLM", Aside "KV cache and prefix caching" (slot_mapping,
- * the phase-agnostic scatter); "vLLM internals study" section 2.1.
+ * Source: "vLLM v1 Deep Dive", Aside "KV cache and prefix caching" (slot_mapping,
+ * the phase-agnostic scatter); "vLLM: An Exhaustive Technical Study" section 2.1.
  */
 pa_status pa_write_kv(const void *k, const void *v, int64_t k_token_stride,
                       int64_t v_token_stride, const int64_t *slot_mapping,
@@ -178,8 +178,8 @@ size_t pa_attend_workspace_size(int32_t num_seqs, int64_t num_q_tokens,
  * independent of physical block ids, of block sharing and of the rest of the
  * batch.
  *
- * Source: "Inside vLLM", Step 4c and the Aside "KV cache and prefix caching";
- * "vLLM internals study" sections 2.1 and 2.4.
+ * Source: "vLLM v1 Deep Dive", Step 4c and the Aside "KV cache and prefix caching";
+ * "vLLM: An Exhaustive Technical Study" sections 2.1 and 2.4.
  */
 pa_status pa_attend(const void *q, const void *k_cache, const void *v_cache,
                     int64_t num_blocks, const int32_t *block_tables,
@@ -194,7 +194,7 @@ pa_status pa_attend(const void *q, const void *k_cache, const void *v_cache,
 /*
  * pa_attend_plan, pa_attend_planned, pa_attend_merge - pa_attend in three
  * calls, so that one plan serves every layer of a forward step (the metadata
- * is the same for all layers; "Inside vLLM", Step 4c: the runner builds
+ * is the same for all layers; "vLLM v1 Deep Dive", Step 4c: the runner builds
  * query_start_loc and the block tables once per step), and so that each
  * kernel can be timed on its own.
  *
@@ -248,7 +248,7 @@ pa_status pa_attend_merge(int32_t num_seqs, int64_t num_q_tokens,
  *
  * Source: "Deep Dive - vLLM" (leetllm.com), "The historical idea: page KV
  * memory" (a kernel follows the table to load the right physical blocks);
- * "vLLM internals study" section 2.1.
+ * "vLLM: An Exhaustive Technical Study" section 2.1.
  */
 pa_status pa_gather_kv(const void *k_cache, const void *v_cache,
                        int64_t num_blocks, const int32_t *block_tables,

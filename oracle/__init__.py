@@ -9,10 +9,10 @@ The arithmetic lives in ``oracle.c`` (plain C, fp64, loops in the order of the
 definitions); this module only compiles it with gcc and marshals numpy arrays.
 bf16 tensors travel as their uint16 bit patterns.
 
-Sources: "Inside vLLM" (supercharleszhu.github.io), Part 3, Step 4c "Mixed
+Sources: "vLLM v1 Deep Dive" (supercharleszhu.github.io), Part 3, Step 4c "Mixed
 batches" (query_start_loc) and the Aside "KV cache and prefix caching"
 (slot_mapping scatter; block_table + varlen causal attention in one launch);
-"vLLM internals study" (anthony-chaudhary.github.io) sections 2.1 (block
+"vLLM: An Exhaustive Technical Study for Kernel Engineers" (anthony-chaudhary.github.io) sections 2.1 (block
 tables, write slot = block number * block_size + offset) and 2.4 (GQA heads
 that share a KV head are processed together).
 """

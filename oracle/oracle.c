@@ -11,7 +11,7 @@
  * become the top half of an IEEE binary32, which converts exactly to binary64).
  *
  * Sources (the pages this build follows):
- *  - "Inside vLLM ... Part 3 Runtime", Aside "KV cache and prefix caching"
+ *  - "vLLM v1 Deep Dive", Part 3 Runtime, Aside "KV cache and prefix caching"
  *    (supercharleszhu.github.io): a forward writes each new token's K/V into
  *    the physical slot block_id*block_size + offset given by slot_mapping, and
  *    reads K/V back per request through its block_table; a prefill query
@@ -19,7 +19,7 @@
  *    of its blocks, one launch for the whole batch.
  *  - Same page, "Step 4c - Mixed batches": query_start_loc is the prefix sum
  *    of per-request scheduled token counts.
- *  - "vLLM internals study" (anthony-chaudhary.github.io) section 2.1
+ *  - "vLLM: An Exhaustive Technical Study for Kernel Engineers" (anthony-chaudhary.github.io) section 2.1
  *    "PagedAttention & the block manager" (block table maps logical block
  *    index to physical block id; write slot = block number * block_size +
  *    offset) and section 2.4 "Attention kernels & backends" (query heads that

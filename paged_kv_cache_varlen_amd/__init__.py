@@ -10,8 +10,8 @@ or a tensor is not on a GPU, the calls raise.
     out = attend(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
                  scale, max_query_len, max_seq_len)
 
-Sources: "Inside vLLM" (supercharleszhu.github.io), Part 3, Step 4c and the
-Aside "KV cache and prefix caching"; "vLLM internals study"
+Sources: "vLLM v1 Deep Dive" (supercharleszhu.github.io), Part 3, Step 4c and the
+Aside "KV cache and prefix caching"; "vLLM: An Exhaustive Technical Study"
 (anthony-chaudhary.github.io) sections 2.1 and 2.4.
 """
 from __future__ import annotations

@@ -1,8 +1,8 @@
 // Paged varlen causal attention over a mixed batch (chunked-prefill chunks and
 // decodes in one launch), gfx950.
 //
-// What is computed ("Inside vLLM", Part 3, Step 4c and the Aside "KV cache and
-// prefix caching"; "vLLM internals study" sections 2.1 and 2.4): for every
+// What is computed ("vLLM v1 Deep Dive", Part 3, Step 4c and the Aside "KV cache and
+// prefix caching"; "vLLM: An Exhaustive Technical Study" sections 2.1 and 2.4): for every
 // query token of request b (its Q_b new tokens are the last Q_b of its L_b
 // tokens, rows query_start_loc[b]..) and every query head h,
 //     out = softmax_j(scale * q.K_j) V_j  over keys j = 0 .. p,  p = L_b - Q_b + i,

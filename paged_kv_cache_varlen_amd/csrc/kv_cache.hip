@@ -2,7 +2,7 @@
 //
 // Scatter ("reshape and cache"): every new token of the flattened batch is
 // written to the physical slot slot_mapping[i] = block_id * 16 + offset
-// ("Inside vLLM", Aside "KV cache and prefix caching"; "vLLM internals study"
+// ("vLLM v1 Deep Dive", Aside "KV cache and prefix caching"; "vLLM: An Exhaustive Technical Study"
 // section 2.1, "Reaching the kernel").  One kernel for prefill chunks and
 // decodes alike: the slot is all it needs.
 //

@@ -7,13 +7,13 @@ attention arithmetic and none of the pool layout.
 
 What it builds, and where the pages state it:
   * query_start_loc: prefix sum of per-request scheduled token counts
-    ("Inside vLLM", Part 3, Step 4c "Mixed batches").
+    ("vLLM v1 Deep Dive", Part 3, Step 4c "Mixed batches").
   * block tables: per request an ordered list of physical block ids, any free
     block backing any logical block, ceil(N / block_size) blocks for N tokens
-    ("vLLM internals study" section 2.1; "Inside the vLLM Engine", "A memory
+    ("vLLM: An Exhaustive Technical Study" section 2.1; "Inside the vLLM Engine", "A memory
     problem wearing a throughput costume").
   * slot_mapping: per written token, block_id * block_size + offset
-    ("Inside vLLM", Aside "KV cache and prefix caching"; "vLLM internals study"
+    ("vLLM v1 Deep Dive", Aside "KV cache and prefix caching"; "vLLM: An Exhaustive Technical Study"
     section 2.1 "Reaching the kernel").
   * shared prefix blocks held by several block tables with a reference count
     equal to the number of tables that hold them (same Aside; "Deep Dive -
