@@ -48,7 +48,51 @@ def parse():
     ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--min-working-set-gib", type=float, default=2.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run 5 plain 1 GiB device-to-device copies (the "
+                         "known-size reference for the HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_probe():
+    """Five 1 GiB torch copies: each reads and writes exactly 2**30 bytes."""
+    import torch
+    src = torch.ones(2**30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_per_copy": 2**30, "copies": 5}))
+    return 0
+
+
+def kernel_source_hash() -> str:
+    """sha256 (first 16 hex) of the attention kernel sources."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_cache_varlen_amd", "csrc")
+    for f in ("attend.hip", "pa_device.h", "kv_cache.hip"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (profiles/hbm_traffic.json), or None when the kernel sources changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256_16") != kernel_source_hash():
+        return None
+    k = t.get("kernels", {}).get("%s|%s" % (kernel, workload))
+    if not k:
+        return None
+    return int(k["fetch_bytes"]) + int(k["write_bytes"])
 
 
 def algorithmic(w):
@@ -158,11 +202,15 @@ def main():
     import workloads as W
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        return copy_probe()
 
     w = W.make_config(args.config)
     alg = algorithmic(w)
     r = Runner(w, args.min_working_set_gib)
     ms_step, attend_ms = r.run(args.steps, args.warmup)
+    kernel = ("attend_decode_kernel<%d>" if w.max_query_len <= 16 // (
+        w.num_q_heads // w.num_kv_heads) else "attend_mixed_kernel<%d>") % w.head_dim
     kv_gbs = alg["kv_bytes"] / (ms_step * 1e-3) / 1e9
     achieved = alg["attend_bytes"] / (attend_ms * 1e-3) / 1e9
     line = {
@@ -184,9 +232,7 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None, "kernel": "attend_decode_kernel<128>" if
-            w.max_query_len <= 16 // (w.num_q_heads // w.num_kv_heads)
-            else "attend_mixed_kernel<128>",
+            "traffic": measured_traffic(kernel, w.name), "kernel": kernel,
             "attend_ms": round(attend_ms, 5),
             "algorithmic_bytes": alg["attend_bytes"]},
     }
