@@ -210,7 +210,7 @@ __device__ int4 block_scan4(int4 x, int4* lds, int4* tot) {
 __device__ __forceinline__ void put_item(const AttendParams& P, int idx, int b,
                                          int tok0, int ntok, int kind, int kv0,
                                          int kv1, int split, int nsplit,
-                                         int pbase, int counter) {
+                                         int pbase, int counter, int posbase) {
   WorkItem it;
   it.seq = b;
   it.tok0 = tok0;
@@ -222,8 +222,9 @@ __device__ __forceinline__ void put_item(const AttendParams& P, int idx, int b,
   it.nsplit = nsplit;
   it.pbase = pbase;
   it.counter = counter;
+  it.posbase = posbase;
 #pragma unroll
-  for (int i = 0; i < 6; ++i) it.pad[i] = 0;
+  for (int i = 0; i < 5; ++i) it.pad[i] = 0;
   P.items[idx] = it;
 }
 
@@ -241,7 +242,7 @@ __device__ void emit_seq(const AttendParams& P, int b, const SeqCounts& c,
     for (int s = 0; s < ns; ++s)
       put_item(P, s == ns - 1 ? ilast : ibase + s, b, q0, Q, kKindDecode,
                s * sl, min(L, (s + 1) * sl), s, ns, ns > 1 ? pbase : -1,
-               ns > 1 ? cbase : -1);
+               ns > 1 ? cbase : -1, L - Q);
     if (ns > 1) P.merge_list[cbase] = make_int4(q0, Q, ns, pbase);
     return;
   }
@@ -262,7 +263,7 @@ __device__ void emit_seq(const AttendParams& P, int b, const SeqCounts& c,
     }
     for (int s = 0; s < ns; ++s)
       put_item(P, icur++, b, q0 + t * c.tq, ntok, kKindPrefill, s * span,
-               min(pmax1, (s + 1) * span), s, ns, pb, cb);
+               min(pmax1, (s + 1) * span), s, ns, pb, cb, L - Q + t * c.tq);
   }
 }
 
@@ -363,7 +364,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttendParams P) {
       const int ntok = min(tq, Q - t * tq);
       const int pmax1 = L - Q + t * tq + ntok;
       put_item(P, coop_base[k] + (ntiles - 1 - t), b, q0 + t * tq, ntok,
-               kKindPrefill, 0, pmax1, 0, 1, -1, -1);
+               kKindPrefill, 0, pmax1, 0, 1, -1, -1, L - Q + t * tq);
     }
   }
   if (tid == 0) {
@@ -549,10 +550,7 @@ __device__ __forceinline__ void run_decode(const AttendParams& P,
   constexpr int NT = D / 16;
   const int g = lane >> 4, r = lane & 15;
   const int b = it.seq;
-  const int L = P.seq_lens[b];
-  const int q0 = P.qsl[b];
-  const int Q = P.qsl[b + 1] - q0;
-  const int posbase = L - Q + (it.tok0 - q0);
+  const int posbase = it.posbase;  // position of the tile's first token
 
   bf16x8 qop[CT][KC];
   int cpos[CT];
@@ -677,10 +675,7 @@ __device__ __forceinline__ void run_prefill(const AttendParams& P,
   constexpr int NT = D / 16;
   const int r = lane & 15, g = lane >> 4;
   const int b = it.seq;
-  const int L = P.seq_lens[b];
-  const int q0 = P.qsl[b];
-  const int Q = P.qsl[b + 1] - q0;
-  const int posbase = L - Q + (it.tok0 - q0);
+  const int posbase = it.posbase;  // position of the tile's first token
 
   bf16x8 qop[CT][KC];
   int cpos[CT];
@@ -817,19 +812,25 @@ __device__ __forceinline__ void attend_body(const AttendParams& P) {
   uint32_t num_work = P.hdr->num_work;
   if ((uint64_t)num_work > (uint64_t)P.max_items * (uint64_t)P.Hkv) num_work = 0;
   const uint32_t Hkv = (uint32_t)P.Hkv;
-  while (true) {
-    uint32_t w = 0;
-    if (lane == 0) w = atomicAdd(&P.hdr->work_counter, 1u);
-    w = __shfl(w, 0);
-    w = __builtin_amdgcn_readfirstlane(w);
+  // Each wave's first unit is its own index (no queue traffic at launch);
+  // units beyond the grid come from the queue, offset by the grid's waves.
+  const uint32_t nwaves = gridDim.x * (kAttendThreads / 64);
+  uint32_t w = __builtin_amdgcn_readfirstlane(blockIdx.x * (kAttendThreads / 64) +
+                                              (threadIdx.x >> 6));
+  for (;; ) {
     if (w >= num_work) break;
     const WorkItem it = P.items[w / Hkv];
     const int kvh = (int)(w % Hkv);
-    if (!item_ok(P, it)) continue;
-    if (MIXED && it.kind == kKindPrefill)
-      run_prefill<D, kPrefillColTiles>(P, it, kvh, lane);
-    else
-      run_decode<D, kDecodeColTiles, kDecodeStages>(P, it, kvh, lane);
+    if (item_ok(P, it)) {
+      if (MIXED && it.kind == kKindPrefill)
+        run_prefill<D, kPrefillColTiles>(P, it, kvh, lane);
+      else
+        run_decode<D, kDecodeColTiles, kDecodeStages>(P, it, kvh, lane);
+    }
+    uint32_t next = 0;
+    if (lane == 0) next = atomicAdd(&P.hdr->work_counter, 1u);
+    next = __shfl(next, 0);
+    w = __builtin_amdgcn_readfirstlane(next) + nwaves;
   }
 }
 

@@ -41,7 +41,8 @@ struct WorkItem {
   int32_t nsplit;   // splits of this tile (1: output written directly)
   int32_t pbase;    // partial slot of (tile token 0, split 0); -1 if unsplit
   int32_t counter;  // index of the tile in the merge list; -1 if unsplit
-  int32_t pad[6];
+  int32_t posbase;  // logical position of the tile's first query token
+  int32_t pad[5];
 };
 static_assert(sizeof(WorkItem) == 64, "WorkItem is one 64-byte scalar load");
 
