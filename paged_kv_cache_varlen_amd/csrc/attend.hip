@@ -51,8 +51,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-// block buffers of the decode pipeline (blocks in flight + 1)
+// block buffers of the decode / prefill pipelines (blocks in flight + 1)
 constexpr int kDecodeStages = 3;
+constexpr int kPrefillStages = 2;
+// one wave in this many starts on the prefill queue of a mixed batch
+constexpr uint32_t kPrefillWaveShare = 1;
 
 struct AttendParams {
   const uint16_t* q;
@@ -293,6 +296,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttendParams P) {
   const int tid = threadIdx.x;
   if (tid == 0) {
     P.hdr->work_counter = 0;
+    P.hdr->prefill_counter = 0;
     P.hdr->error = 0;
     P.hdr->signature = plan_signature(P);
     coop_n = 0;
@@ -371,6 +375,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttendParams P) {
     const int all_items = total.x + total.y + total2.x;
     P.hdr->num_items = fits ? (uint32_t)all_items : 0u;
     P.hdr->num_work = fits ? (uint32_t)all_items * (uint32_t)P.Hkv : 0u;
+    P.hdr->num_prefill_work = fits ? (uint32_t)total.x * (uint32_t)P.Hkv : 0u;
     P.hdr->num_split_tiles = fits ? (uint32_t)total.w : 0u;
     if (!fits) atomicOr(&P.hdr->error, 1u);
   }
@@ -515,37 +520,24 @@ __device__ __forceinline__ void finish_unit(const AttendParams& P,
   }
 }
 
-// Physical block ids of 64 consecutive logical blocks of a unit, one per lane.
-struct BlockIds {
-  int idv = 0;
-  int chunk = -1;
-  __device__ __forceinline__ int get(const int32_t* btrow, int jb0, int jb1,
-                                     int rel, int lane, int64_t maxblk) {
-    const int want = rel >> 6;
-    if (want != chunk) {
-      chunk = want;
-      const int j = jb0 + (want << 6) + lane;
-      int id = j < jb1 ? btrow[j] : 0;
-      id = id < 0 ? 0 : (id > maxblk ? (int)maxblk : id);
-      idv = id;
-    }
-    return __builtin_amdgcn_readlane(idv, rel & 63);
-  }
-};
-
 template <int D>
 struct KVBlock {
   bf16x8 k[D / 32];  // K rows in MFMA operand order
   bf16x8 v[D / 32];  // lane's 4 keys at dims d and d + D/2
 };
 
-// Decode path: one block (16 keys) per step, NB-1 later blocks' loads in
-// flight while the current one is computed.  PV on 16x16x16 MFMA: the score
-// registers are its B operand as they stand.
-template <int D, int CT, int NB>
-__device__ __forceinline__ void run_decode(const AttendParams& P,
-                                           const WorkItem& it, int kvh,
-                                           int lane) {
+// One (item, kv head) unit on one wave: CT column tiles of 16 (query token x
+// head of the group), one block (16 keys) per step with the loads of the next
+// NB-1 blocks in flight while the current one is computed.  Scores on
+// 16x16x32 MFMA, PV on 16x16x16 MFMA whose B operand is the score registers
+// as they stand.  STREAM selects non-temporal K/V loads (decode: every tile is
+// read once) or cached loads (prefill: the tiles of a request are re-read by
+// all of its query tiles).  Block ids come 64 at a time, one per lane; each
+// chunk of 64 blocks runs its own pipeline.
+template <int D, int CT, int NB, bool STREAM>
+__device__ __forceinline__ void run_unit(const AttendParams& P,
+                                         const WorkItem& it, int kvh,
+                                         int lane) {
   constexpr int KC = D / 32;
   constexpr int NT = D / 16;
   const int g = lane >> 4, r = lane & 15;
@@ -568,72 +560,79 @@ __device__ __forceinline__ void run_decode(const AttendParams& P,
 
   const int jb0 = it.kv0 >> 4;
   const int jb1 = (it.kv1 + kBlock - 1) >> 4;
-  const int nblk = jb1 - jb0;  // <= kSplitDecodeLong / 16 <= 64
   const int32_t* btrow = P.bt + (int64_t)b * P.bt_stride;
   const int64_t tile_elems = (int64_t)kBlock * D;
-  // All physical block ids of the unit, one per lane, loaded once: inside the
-  // loop every step then issues exactly the same loads, which lets the
-  // compiler wait for the current block only, never for the prefetched one.
-  int idv = 0;
-  if (lane < nblk) idv = btrow[jb0 + lane];
-  idv = idv < 0 ? 0 : (idv >= P.num_blocks ? (int)(P.num_blocks - 1) : idv);
 
-  auto issue = [&](KVBlock<D>& buf, int j) {
-    const int id = __builtin_amdgcn_readlane(idv, j);
-    const int64_t off = ((int64_t)id * P.Hkv + kvh) * tile_elems;
-    const uint16_t* kp = P.k_cache + off;
-    const uint16_t* vp = P.v_cache + off;
-#pragma unroll
-    for (int c = 0; c < KC; ++c) buf.k[c] = load16_stream(kp + c * 512 + lane * 8);
-#pragma unroll
-    for (int c = 0; c < KC; ++c) buf.v[c] = load16_stream(vp + c * 512 + (4 * r + g) * 8);
-  };
+  for (int c0 = jb0; c0 < jb1; c0 += 64) {
+    const int nblk = min(64, jb1 - c0);
+    // physical ids of this chunk's blocks, one per lane
+    int idv = 0;
+    if (lane < nblk) idv = btrow[c0 + lane];
+    idv = idv < 0 ? 0 : (idv >= P.num_blocks ? (int)(P.num_blocks - 1) : idv);
 
-  auto compute = [&](KVBlock<D>& buf, int j) {
-    const int kp0 = (jb0 + j) * kBlock;
-    if (kp0 + kBlock > it.kv1) {
-      // keys at or past kv1 may be unwritten pool slots: zero their V so a
-      // 0 weight cannot meet a NaN
+    auto issue = [&](KVBlock<D>& buf, int j) {
+      const int id = __builtin_amdgcn_readlane(idv, j);
+      const int64_t off = ((int64_t)id * P.Hkv + kvh) * tile_elems;
+      const uint16_t* kp = P.k_cache + off;
+      const uint16_t* vp = P.v_cache + off;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (kp0 + 4 * g + i >= it.kv1) {
+      for (int c = 0; c < KC; ++c)
+        buf.k[c] = STREAM ? load16_stream(kp + c * 512 + lane * 8)
+                          : load16(kp + c * 512 + lane * 8);
 #pragma unroll
-          for (int c = 0; c < KC; ++c) {
-            buf.v[c][i] = (__bf16)0.0f;
-            buf.v[c][i + 4] = (__bf16)0.0f;
+      for (int c = 0; c < KC; ++c)
+        buf.v[c] = STREAM ? load16_stream(vp + c * 512 + (4 * r + g) * 8)
+                          : load16(vp + c * 512 + (4 * r + g) * 8);
+    };
+
+    auto compute = [&](KVBlock<D>& buf, int j) {
+      const int kp0 = (c0 + j) * kBlock;
+      if (kp0 + kBlock > it.kv1) {
+        // keys at or past kv1 may be unwritten pool slots: zero their V so a
+        // 0 weight cannot meet a NaN
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (kp0 + 4 * g + i >= it.kv1) {
+#pragma unroll
+            for (int c = 0; c < KC; ++c) {
+              buf.v[c][i] = (__bf16)0.0f;
+              buf.v[c][i + 4] = (__bf16)0.0f;
+            }
           }
         }
       }
-    }
-    const bool need_mask = kp0 + kBlock - 1 > posbase;
+      const bool need_mask = kp0 + kBlock - 1 > posbase;
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+      for (int ct = 0; ct < CT; ++ct) {
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < KC; ++c) s = mfma32(buf.k[c], qop[ct][c], s);
-      float x[4];
+        for (int c = 0; c < KC; ++c) sc = mfma32(buf.k[c], qop[ct][c], sc);
+        float x[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[i] = s[i] * P.scale_log2;
-        if (need_mask && kp0 + 4 * g + i > cpos[ct]) x[i] = -INFINITY;
+        for (int i = 0; i < 4; ++i) {
+          x[i] = sc[i] * P.scale_log2;
+          if (need_mask && kp0 + 4 * g + i > cpos[ct]) x[i] = -INFINITY;
+        }
+        float alpha;
+        __bf16 p[4];
+        softmax_step<4>(x, mrun[ct], lsum[ct], alpha, p);
+        bf16x4 pop = {p[0], p[1], p[2], p[3]};
+        // alpha is exactly 1 where the running max did not move: skip the
+        // rescale when that holds for every column of the wave (same bits)
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+          for (int n = 0; n < NT; ++n) acc[ct][n] *= alpha;
+        }
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+          const bf16x4 vlo = __builtin_shufflevector(buf.v[c], buf.v[c], 0, 1, 2, 3);
+          const bf16x4 vhi = __builtin_shufflevector(buf.v[c], buf.v[c], 4, 5, 6, 7);
+          acc[ct][c] = mfma16(vlo, pop, acc[ct][c]);
+          acc[ct][c + KC] = mfma16(vhi, pop, acc[ct][c + KC]);
+        }
       }
-      float alpha;
-      __bf16 p[4];
-      softmax_step<4>(x, mrun[ct], lsum[ct], alpha, p);
-      bf16x4 pop = {p[0], p[1], p[2], p[3]};
-#pragma unroll
-      for (int n = 0; n < NT; ++n) acc[ct][n] *= alpha;
-#pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        const bf16x4 vlo = __builtin_shufflevector(buf.v[c], buf.v[c], 0, 1, 2, 3);
-        const bf16x4 vhi = __builtin_shufflevector(buf.v[c], buf.v[c], 4, 5, 6, 7);
-        acc[ct][c] = mfma16(vlo, pop, acc[ct][c]);
-        acc[ct][c + KC] = mfma16(vhi, pop, acc[ct][c + KC]);
-      }
-    }
-  };
+    };
 
-  if (nblk > 0) {
     // Ring of NB block buffers, NB-1 blocks in flight while one is computed.
     // Every path into the loop header has the same loads in flight (the
     // prefetch is unconditional, clamped to the last block, and the loop has
@@ -654,130 +653,6 @@ __device__ __forceinline__ void run_decode(const AttendParams& P,
 #pragma unroll
     for (int k = 0; k < NB - 1; ++k)
       if (j + k < nblk) compute(buf[k], j + k);
-  }
-  finish_unit<D, CT>(P, it, kvh, lane, acc, mrun, lsum);
-}
-
-template <int D>
-struct KVPair {
-  bf16x8 k[2][D / 32];  // block a, block b: K rows in MFMA operand order
-  bf16x8 v[2][D / 32];  // lane's 4 keys at dims d and d + D/2
-};
-
-// Prefill path: two blocks (32 keys) per step so that PV runs on the
-// full-rate 16x16x32 MFMA (k index 8g+j: block a key 4g+j for j < 4, block b
-// key 4g+j-4 otherwise, matching the two score tiles the lane holds).
-template <int D, int CT>
-__device__ __forceinline__ void run_prefill(const AttendParams& P,
-                                            const WorkItem& it, int kvh,
-                                            int lane) {
-  constexpr int KC = D / 32;
-  constexpr int NT = D / 16;
-  const int r = lane & 15, g = lane >> 4;
-  const int b = it.seq;
-  const int posbase = it.posbase;  // position of the tile's first token
-
-  bf16x8 qop[CT][KC];
-  int cpos[CT];
-  load_query<D, CT>(P, it, kvh, lane, posbase, qop, cpos);
-
-  f32x4 acc[CT][NT];
-  float mrun[CT], lsum[CT];
-#pragma unroll
-  for (int ct = 0; ct < CT; ++ct) {
-    mrun[ct] = -INFINITY;
-    lsum[ct] = 0.0f;
-#pragma unroll
-    for (int n = 0; n < NT; ++n) acc[ct][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  const int jb0 = it.kv0 >> 4;
-  const int jb1 = (it.kv1 + kBlock - 1) >> 4;
-  const int nblk = jb1 - jb0;
-  const int npairs = (nblk + 1) >> 1;
-  const int32_t* btrow = P.bt + (int64_t)b * P.bt_stride;
-  const int64_t tile_elems = (int64_t)kBlock * D;
-  BlockIds ids;
-
-  for (int pr = 0; pr < npairs; ++pr) {
-    KVPair<D> buf;
-    const int rel = 2 * pr;
-    const bool has_b = rel + 1 < nblk;
-    const int ia = ids.get(btrow, jb0, jb1, rel, lane, P.num_blocks - 1);
-    const int ib = ids.get(btrow, jb0, jb1, rel + 1, lane, P.num_blocks - 1);
-    const int64_t offa = ((int64_t)ia * P.Hkv + kvh) * tile_elems;
-#pragma unroll
-    for (int c = 0; c < KC; ++c) buf.k[0][c] = load16(P.k_cache + offa + c * 512 + lane * 8);
-#pragma unroll
-    for (int c = 0; c < KC; ++c)
-      buf.v[0][c] = load16(P.v_cache + offa + c * 512 + (4 * r + g) * 8);
-    if (has_b) {
-      const int64_t offb = ((int64_t)ib * P.Hkv + kvh) * tile_elems;
-#pragma unroll
-      for (int c = 0; c < KC; ++c) buf.k[1][c] = load16(P.k_cache + offb + c * 512 + lane * 8);
-#pragma unroll
-      for (int c = 0; c < KC; ++c)
-        buf.v[1][c] = load16(P.v_cache + offb + c * 512 + (4 * r + g) * 8);
-    } else {
-#pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        buf.k[1][c] = zero8();
-        buf.v[1][c] = zero8();
-      }
-    }
-    const int kp0 = (jb0 + rel) * kBlock;
-    if (kp0 + 2 * kBlock > it.kv1) {
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (kp0 + 16 * x + 4 * g + i >= it.kv1) {
-#pragma unroll
-            for (int c = 0; c < KC; ++c) {
-              buf.v[x][c][i] = (__bf16)0.0f;
-              buf.v[x][c][i + 4] = (__bf16)0.0f;
-            }
-          }
-        }
-      }
-    }
-    const bool need_mask = kp0 + 2 * kBlock - 1 > posbase;
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < KC; ++c) sa = mfma32(buf.k[0][c], qop[ct][c], sa);
-#pragma unroll
-      for (int c = 0; c < KC; ++c) sb = mfma32(buf.k[1][c], qop[ct][c], sb);
-      float x[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[i] = sa[i] * P.scale_log2;
-        x[i + 4] = sb[i] * P.scale_log2;
-        if (need_mask) {
-          const int ka = kp0 + 4 * g + i;
-          if (ka > cpos[ct]) x[i] = -INFINITY;
-          if (ka + kBlock > cpos[ct]) x[i + 4] = -INFINITY;
-        }
-      }
-      float alpha;
-      __bf16 p[8];
-      softmax_step<8>(x, mrun[ct], lsum[ct], alpha, p);
-      bf16x8 pop;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pop[i] = p[i];
-#pragma unroll
-      for (int n = 0; n < NT; ++n) acc[ct][n] *= alpha;
-#pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        const bf16x8 vlo = __builtin_shufflevector(buf.v[0][c], buf.v[1][c], 0,
-                                                   1, 2, 3, 8, 9, 10, 11);
-        const bf16x8 vhi = __builtin_shufflevector(buf.v[0][c], buf.v[1][c], 4,
-                                                   5, 6, 7, 12, 13, 14, 15);
-        acc[ct][c] = mfma32(vlo, pop, acc[ct][c]);
-        acc[ct][c + KC] = mfma32(vhi, pop, acc[ct][c + KC]);
-      }
-    }
   }
   finish_unit<D, CT>(P, it, kvh, lane, acc, mrun, lsum);
 }
@@ -811,26 +686,64 @@ __device__ __forceinline__ void attend_body(const AttendParams& P) {
   }
   uint32_t num_work = P.hdr->num_work;
   if ((uint64_t)num_work > (uint64_t)P.max_items * (uint64_t)P.Hkv) num_work = 0;
+  uint32_t num_pre = P.hdr->num_prefill_work;
+  if (num_pre > num_work) num_pre = num_work;
   const uint32_t Hkv = (uint32_t)P.Hkv;
-  // Each wave's first unit is its own index (no queue traffic at launch);
-  // units beyond the grid come from the queue, offset by the grid's waves.
   const uint32_t nwaves = gridDim.x * (kAttendThreads / 64);
-  uint32_t w = __builtin_amdgcn_readfirstlane(blockIdx.x * (kAttendThreads / 64) +
-                                              (threadIdx.x >> 6));
-  for (;; ) {
-    if (w >= num_work) break;
+  const uint32_t wid = __builtin_amdgcn_readfirstlane(
+      blockIdx.x * (kAttendThreads / 64) + (threadIdx.x >> 6));
+  // Two queues: prefill units [0, num_pre) and decode units [num_pre,
+  // num_work) of the work list.  In a mixed batch one wave in
+  // kPrefillWaveShare starts on prefill, the others on decode, so
+  // compute-bound prefill tiles and bandwidth-bound decode splits share the
+  // CUs; a wave whose queue runs dry moves to the other one.  Each
+  // wave's first unit is assigned by its index (no queue traffic at launch),
+  // later ones come from the queue's counter, offset by the static share.
+  const uint32_t qn[2] = {num_pre, num_work - num_pre};
+  const uint32_t qbase[2] = {0u, num_pre};
+  uint32_t nstatic[2], q, idx;
+  if (MIXED && num_pre > 0) {
+    constexpr uint32_t S = kPrefillWaveShare;  // 1 of every S waves
+    nstatic[0] = (nwaves + S - 1) / S;
+    nstatic[1] = nwaves - nstatic[0];
+    q = (wid % S == 0) ? 0u : 1u;
+    idx = q == 0 ? wid / S : wid - wid / S - 1;
+  } else {
+    nstatic[0] = 0;
+    nstatic[1] = nwaves;
+    q = 1;
+    idx = wid;
+    if (num_pre > 0) {  // cannot happen without prefill items; kept total
+      q = 0;
+      nstatic[0] = nwaves;
+      nstatic[1] = 0;
+    }
+  }
+  uint32_t* const counters[2] = {&P.hdr->prefill_counter, &P.hdr->work_counter};
+  bool switched = false;
+  for (;;) {
+    if (idx >= qn[q]) {
+      // both queues exhausted (or the other one is empty): done
+      if (switched || qn[q ^ 1u] == 0) break;
+      switched = true;
+      q ^= 1u;
+      uint32_t t = 0;
+      if (lane == 0) t = atomicAdd(counters[q], 1u);
+      idx = __builtin_amdgcn_readfirstlane(__shfl(t, 0)) + nstatic[q];
+      continue;
+    }
+    const uint32_t w = qbase[q] + idx;
     const WorkItem it = P.items[w / Hkv];
     const int kvh = (int)(w % Hkv);
     if (item_ok(P, it)) {
       if (MIXED && it.kind == kKindPrefill)
-        run_prefill<D, kPrefillColTiles>(P, it, kvh, lane);
+        run_unit<D, kPrefillColTiles, kPrefillStages, false>(P, it, kvh, lane);
       else
-        run_decode<D, kDecodeColTiles, kDecodeStages>(P, it, kvh, lane);
+        run_unit<D, kDecodeColTiles, kDecodeStages, true>(P, it, kvh, lane);
     }
-    uint32_t next = 0;
-    if (lane == 0) next = atomicAdd(&P.hdr->work_counter, 1u);
-    next = __shfl(next, 0);
-    w = __builtin_amdgcn_readfirstlane(next) + nwaves;
+    uint32_t t = 0;
+    if (lane == 0) t = atomicAdd(counters[q], 1u);
+    idx = __builtin_amdgcn_readfirstlane(__shfl(t, 0)) + nstatic[q];
   }
 }
 

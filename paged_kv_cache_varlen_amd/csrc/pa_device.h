@@ -48,12 +48,14 @@ static_assert(sizeof(WorkItem) == 64, "WorkItem is one 64-byte scalar load");
 
 // Workspace header, at offset 0 of the workspace.
 struct PlanHeader {
-  uint32_t work_counter;  // dynamic work queue head (zeroed by the plan)
-  uint32_t num_work;      // items * num_kv_heads
+  uint32_t work_counter;  // decode queue head (zeroed by the plan)
+  uint32_t num_work;      // items * num_kv_heads (prefill units first)
   uint32_t num_items;
   uint32_t error;         // bit0: capacity exceeded, bit1: bad request skipped
   uint32_t num_split_tiles;  // entries of the merge list
   uint32_t signature;     // hash of the arguments the plan was made for
+  uint32_t prefill_counter;   // prefill queue head (zeroed by the plan)
+  uint32_t num_prefill_work;  // prefill items * num_kv_heads
 };
 
 // Byte offsets of the workspace sections.
