@@ -48,10 +48,12 @@
  *   tile (block n, kv head g) starts at element (n * num_kv_heads + g) * 16 * D.
  *   Inside a tile, for token slot t in [0,16) and dim d in [0,D), H = D/2:
  *     K(t, d) is at ((d / 8) * 16 + t) * 8 + d % 8
- *     V(t, d) is at (((d % H) * 4 + t / 4) * 2 + d / H) * 4 + t % 4
- *   (K: 8-dim chunks of all 16 tokens; V: dims d and d+H of 4 consecutive
- *   tokens side by side.)  Only pa_write_kv, pa_attend and pa_gather_kv are
- *   meant to touch the pools.
+ *     V(t, d) is at ((((d % H) / 16 * 2 + d / H) * 4 + t / 4) * 16 + d % 16)
+ *                   * 4 + t % 4
+ *   (K: 8-dim chunks of all 16 tokens; V: runs of 4 consecutive tokens of
+ *   one dim, 64 runs - 16 dims x 4 token groups - per 512-byte region.)
+ *   Only pa_write_kv, pa_attend and pa_gather_kv are meant to touch the
+ *   pools.
  *
  * Conventions for every call:
  *   - All tensor pointers are DEVICE memory that the caller allocates, owns
@@ -164,7 +166,8 @@ size_t pa_attend_workspace_size(int32_t num_seqs, int64_t num_q_tokens,
  *                    qsl[num_seqs] = num_q_tokens; 0 <= Q_b <= L_b
  *   max_query_len, max_seq_len  host-side upper bounds of Q_b and L_b (used
  *                    for workspace sizing; requests beyond them are skipped)
- *   scale            softmax scale (e.g. 1/sqrt(head_dim))
+ *   scale            softmax scale (e.g. 1/sqrt(head_dim)), finite and > 0
+ *                    (PA_ERR_SHAPE otherwise)
  *   out              device bf16 [num_q_tokens][num_q_heads][head_dim]
  *   workspace        device buffer of >= pa_attend_workspace_size(...) bytes,
  *                    256-byte aligned; contents need no initialisation and

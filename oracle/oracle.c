@@ -68,15 +68,17 @@ static size_t k_index(int64_t n, int64_t g, int64_t t, int64_t d, int64_t Hkv,
 }
 
 /* Element offset of V (block n, kv head g, token slot t, dim d).
- * Inside a tile, with H = D/2: dim d pairs with dim d+H, tokens come in groups
- * of 4; order is [d mod H][t / 4][d / H][t mod 4]. */
+ * Inside a tile, with H = D/2, d = dh*H + 16*c + r (dh < 2, r < 16) and
+ * t = 4*tg + tl: order is [c][dh][tg][r][tl], i.e. 4 consecutive tokens of
+ * one dim are contiguous and 64 such runs form a 512-byte region per
+ * (c, dh). */
 static size_t v_index(int64_t n, int64_t g, int64_t t, int64_t d, int64_t Hkv,
                       int64_t bs, int64_t D) {
   size_t tile = (size_t)((n * Hkv + g) * bs * D);
   int64_t H = D / 2;
-  int64_t dl = d % H, dh = d / H;
+  int64_t dh = d / H, c = (d % H) / 16, r = d % 16;
   int64_t tg = t / 4, tl = t % 4;
-  return tile + (size_t)((((dl * (bs / 4) + tg) * 2 + dh) * 4) + tl);
+  return tile + (size_t)((((c * 2 + dh) * (bs / 4) + tg) * 16 + r) * 4 + tl);
 }
 
 size_t oracle_k_index(int64_t n, int64_t g, int64_t t, int64_t d, int64_t Hkv,

@@ -37,6 +37,7 @@
 // the unified one that serves decode and prefill items of a mixed batch in the
 // same launch.
 #include <mutex>
+#include <type_traits>
 #include <vector>
 
 #include "pa_device.h"
@@ -51,11 +52,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-// block buffers of the decode / prefill pipelines (blocks in flight + 1)
+// block buffers of the decode pipeline (blocks in flight + 1)
 constexpr int kDecodeStages = 3;
-constexpr int kPrefillStages = 2;
-// one wave in this many starts on the prefill queue of a mixed batch
-constexpr uint32_t kPrefillWaveShare = 1;
 
 struct AttendParams {
   const uint16_t* q;
@@ -395,6 +393,13 @@ __device__ __forceinline__ bf16x8 load16_stream(const uint16_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p));
 }
 
+__device__ __forceinline__ bf16x4 load8(const uint16_t* p) {
+  return *reinterpret_cast<const bf16x4*>(p);
+}
+__device__ __forceinline__ bf16x4 load8_stream(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const bf16x4*>(p));
+}
+
 __device__ __forceinline__ bf16x8 zero8() {
   bf16x8 z;
 #pragma unroll
@@ -442,49 +447,75 @@ __device__ __forceinline__ void load_query(const AttendParams& P,
   }
 }
 
-// Online-softmax update of one column tile with N new scores per lane:
-// returns the bf16 probabilities and the rescale factor of the old state.
+// Maximum over the four lanes r, r + 16, r + 32, r + 48, which hold the
+// rows of MFMA column r: two VALU lane swaps (no LDS round trip).
+__device__ __forceinline__ float column_max(float x) {
+  const uint32_t xb = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane32_swap(xb, xb, false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t yb = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane16_swap(yb, yb, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Online-softmax update of one column tile with N new raw scores per lane
+// (q.k; -inf where masked) and c = scale * log2(e).  The running max is kept
+// in the exp2 domain; max(s) * c equals max(s * c) exactly since c > 0.
+// Returns the bf16 probabilities exp2(s * c - m) (one fused multiply-add
+// per score) and the rescale factor of the old state.
 template <int N>
-__device__ __forceinline__ void softmax_step(float (&x)[N], float& mrun,
-                                             float& lsum, float& alpha,
-                                             __bf16 (&p)[N]) {
-  float mx = x[0];
+__device__ __forceinline__ void softmax_step(const float (&s)[N], float c,
+                                             float& mrun, float& lsum,
+                                             float& alpha, __bf16 (&p)[N]) {
+  float mx = s[0];
 #pragma unroll
-  for (int i = 1; i < N; ++i) mx = fmaxf(mx, x[i]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float mnew = fmaxf(mrun, mx);
+  for (int i = 1; i < N; ++i) mx = fmaxf(mx, s[i]);
+  mx = column_max(mx);
+  const float mnew = fmaxf(mrun, mx * c);
   const float muse = (mnew == -INFINITY) ? 0.0f : mnew;
   alpha = __builtin_amdgcn_exp2f(mrun - muse);
   mrun = mnew;
   float psum = 0.0f;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    p[i] = (__bf16)__builtin_amdgcn_exp2f(x[i] - muse);
+    p[i] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -muse));
     psum += (float)p[i];
   }
   lsum = lsum * alpha + psum;
 }
 
+// The same update without the probability sum (computed on the matrix core
+// by the caller).
+template <int N>
+__device__ __forceinline__ void softmax_probs(const float (&s)[N], float c,
+                                              float& mrun, float& alpha,
+                                              __bf16 (&p)[N]) {
+  float mx = s[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) mx = fmaxf(mx, s[i]);
+  mx = column_max(mx);
+  const float mnew = fmaxf(mrun, mx * c);
+  const float muse = (mnew == -INFINITY) ? 0.0f : mnew;
+  alpha = __builtin_amdgcn_exp2f(mrun - muse);
+  mrun = mnew;
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    p[i] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -muse));
+}
+
 // End of a unit: direct bf16 output, or fp32 partials (running max, sum and
-// unnormalised accumulator per column) for the merge kernel.
+// unnormalised accumulator per column) for the merge kernel.  l[ct] is the
+// column's full probability sum (the same in all four lanes of a column).
 template <int D, int CT>
 __device__ __forceinline__ void finish_unit(const AttendParams& P,
                                             const WorkItem& it, int kvh,
                                             int lane, f32x4 (&acc)[CT][D / 16],
                                             float (&mrun)[CT],
-                                            float (&lsum)[CT]) {
+                                            const float (&l)[CT]) {
   constexpr int NT = D / 16;
   const int r = lane & 15, g = lane >> 4;
   const int G = P.G;
   const int ncols = it.ntok * G;
-  float l[CT];
-#pragma unroll
-  for (int ct = 0; ct < CT; ++ct) {
-    l[ct] = lsum[ct];
-    l[ct] += __shfl_xor(l[ct], 16);
-    l[ct] += __shfl_xor(l[ct], 32);
-  }
   if (it.nsplit == 1) {
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
@@ -525,6 +556,16 @@ struct KVBlock {
   bf16x8 k[D / 32];  // K rows in MFMA operand order
   bf16x8 v[D / 32];  // lane's 4 keys at dims d and d + D/2
 };
+
+// V operand of k step c for lane (r, g): keys 4g .. 4g+3 at dims 16c + r
+// (elements 0-3) and D/2 + 16c + r (4-7), two 8-byte reads of the tile.
+template <int D, bool STREAM>
+__device__ __forceinline__ bf16x8 load_v(const uint16_t* vp, int c, int lane) {
+  const uint16_t* lo = vp + (2 * c) * 256 + lane * 4;
+  const bf16x4 a = STREAM ? load8_stream(lo) : load8(lo);
+  const bf16x4 b = STREAM ? load8_stream(lo + 256) : load8(lo + 256);
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
 // One (item, kv head) unit on one wave: CT column tiles of 16 (query token x
 // head of the group), one block (16 keys) per step with the loads of the next
@@ -580,9 +621,7 @@ __device__ __forceinline__ void run_unit(const AttendParams& P,
         buf.k[c] = STREAM ? load16_stream(kp + c * 512 + lane * 8)
                           : load16(kp + c * 512 + lane * 8);
 #pragma unroll
-      for (int c = 0; c < KC; ++c)
-        buf.v[c] = STREAM ? load16_stream(vp + c * 512 + (4 * r + g) * 8)
-                          : load16(vp + c * 512 + (4 * r + g) * 8);
+      for (int c = 0; c < KC; ++c) buf.v[c] = load_v<D, STREAM>(vp, c, lane);
     };
 
     auto compute = [&](KVBlock<D>& buf, int j) {
@@ -610,12 +649,12 @@ __device__ __forceinline__ void run_unit(const AttendParams& P,
         float x[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          x[i] = sc[i] * P.scale_log2;
+          x[i] = sc[i];
           if (need_mask && kp0 + 4 * g + i > cpos[ct]) x[i] = -INFINITY;
         }
         float alpha;
         __bf16 p[4];
-        softmax_step<4>(x, mrun[ct], lsum[ct], alpha, p);
+        softmax_step<4>(x, P.scale_log2, mrun[ct], lsum[ct], alpha, p);
         bf16x4 pop = {p[0], p[1], p[2], p[3]};
         // alpha is exactly 1 where the running max did not move: skip the
         // rescale when that holds for every column of the wave (same bits)
@@ -654,7 +693,307 @@ __device__ __forceinline__ void run_unit(const AttendParams& P,
     for (int k = 0; k < NB - 1; ++k)
       if (j + k < nblk) compute(buf[k], j + k);
   }
-  finish_unit<D, CT>(P, it, kvh, lane, acc, mrun, lsum);
+  float l[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    l[ct] = lsum[ct];
+    l[ct] += __shfl_xor(l[ct], 16);
+    l[ct] += __shfl_xor(l[ct], 32);
+  }
+  finish_unit<D, CT>(P, it, kvh, lane, acc, mrun, l);
+}
+
+// ---- prefill tiles: one workgroup, K/V shared through LDS -------------------
+
+// A prefill tile's kPrefillWaves waves take consecutive token slices of it and
+// read the same keys, so its K/V tiles are fetched once per workgroup into an
+// LDS ring of key-pair stages (2 blocks), kPairStages - 1 pairs ahead of the
+// pair being computed, with direct global-to-LDS loads issued a quarter by
+// each wave.  Two blocks per step let PV run on 16x16x32 MFMA: k slot 8g + j
+// of the pair is key 4g + j of the first block for j < 4 and key 4g + j - 4
+// of the second, matching the score rows the lane holds.
+//
+// Stage layout (bf16 elements, TILE = 16 * D): K of the first block, V of
+// the first, K of the second, V of the second, each a pool tile copied as it
+// is (wave w loads tile w with 1 KiB loads).  K operands are 16-byte LDS
+// reads; a V operand is two 8-byte reads, one from each block's V tile, into
+// adjacent registers.  All are conflict-free.
+constexpr int kPairStages = 4;
+
+template <int D>
+constexpr int pair_stage_elems() {
+  return 4 * kBlock * D;
+}
+template <int D>
+constexpr int prefill_ring_elems() {
+  return kPairStages * pair_stage_elems<D>();
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* l) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint16_t*)l);
+}
+
+__device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const uint16_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Global-to-LDS load: lane i reads 16 bytes at base + voff (bytes, per
+// lane) and writes them to LDS at l + 16 i; base and l are the same for the
+// whole wave.  Written as inline assembly so that the compiler does not
+// track it: it would otherwise wait for every such load before any LDS
+// read, draining the pipeline; the ring protocol below orders them itself.
+// The load reads M0 (its LDS base) and an SGPR pair: five wait states after
+// they are written cover the hazard rules for both.  M0 is restored.
+__device__ __forceinline__ void load16_lds(const uint16_t* base, uint32_t voff,
+                                           uint16_t* l) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 4\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(uniform_ptr(base)), "s"(lds_addr(l))
+      : "memory");
+}
+// Wait until at most N of this wave's vector memory loads are outstanding,
+// then meet the other waves of the workgroup.  (A compiler-level memory
+// barrier as well: LDS reads are not moved across it.)
+template <int N>
+__device__ __forceinline__ void wait_loads_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ bf16x8 lds16(const uint16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ bf16x4 lds8(const uint16_t* p) {
+  return *reinterpret_cast<const bf16x4*>(p);
+}
+
+// Growth of a column's maximum (exp2 domain) below which the running max is
+// kept: probabilities then reach at most 2^kRescaleSlack, far inside bf16
+// and fp32 range, and the accumulators are rescaled only when some column's
+// maximum grows by more than that.
+constexpr float kRescaleSlack = 8.0f;
+
+template <int D>
+__device__ __forceinline__ void run_tile(const AttendParams& P,
+                                         const WorkItem& it, int kvh, int lane,
+                                         int wslot, uint16_t* ring) {
+  constexpr int KC = D / 32;
+  constexpr int NT = D / 16;
+  constexpr int CT = kPrefillColTiles;
+  constexpr int NS = kPairStages;
+  constexpr int TILE = kBlock * D;  // elements of one K or V tile
+  constexpr int LPS = KC;           // 16-byte loads per wave per stage
+  const int g = lane >> 4;
+
+  // this wave's token slice of the tile
+  const int tw = prefill_wave_tokens(P.G);
+  const int wofs = wslot * tw;
+  WorkItem wt = it;
+  wt.tok0 = it.tok0 + wofs;
+  wt.ntok = min(tw, it.ntok - wofs);
+  wt.posbase = it.posbase + wofs;
+  wt.pbase = it.nsplit > 1 ? it.pbase + wofs * it.nsplit : -1;
+  const bool active = wt.ntok > 0;
+  const int wlast = active ? wt.posbase + wt.ntok - 1 : -1;  // causal limit
+
+  bf16x8 qop[CT][KC];
+  int cpos[CT];
+  load_query<D, CT>(P, wt, kvh, lane, wt.posbase, qop, cpos);
+
+  // Per column: reference max mref (exp2 domain; probabilities are
+  // exp2(s * c - mref)), the value subtracted (0 while no key was seen), PV
+  // accumulators and the column sums of P.
+  f32x4 acc[CT][NT], lacc[CT];
+  float mref[CT], msub[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    mref[ct] = -INFINITY;
+    msub[ct] = 0.0f;
+    lacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[ct][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  bf16x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
+
+  const int jb0 = it.kv0 >> 4;
+  const int nblk = ((it.kv1 + kBlock - 1) >> 4) - jb0;
+  const int npairs = (nblk + 1) >> 1;
+  const int32_t* btrow = P.bt + (int64_t)it.seq * P.bt_stride + jb0;
+  // Wave w loads tile w of every stage: K(first), V(first), K(second),
+  // V(second) -- 1 KiB per load, in pool order.
+  const uint16_t* pool = (wslot & 1) ? P.v_cache : P.k_cache;
+  const int half = wslot >> 1;
+
+  // physical ids of 64 blocks (32 pairs) from block 2 * idbase, one per lane
+  auto load_ids = [&](int pr0) {
+    const int jr = min(2 * pr0 + lane, nblk - 1);  // clamped
+    const int id = btrow[jr];
+    return id < 0 ? 0 : (id >= P.num_blocks ? (int)(P.num_blocks - 1) : id);
+  };
+  int idbase = 0;
+  int idv = load_ids(0);
+
+  auto issue = [&](int slot, int pr) {
+    if (pr >= idbase + 32) {  // pairs are issued in order
+      idbase += 32;
+      idv = load_ids(idbase);
+    }
+    const int id = __builtin_amdgcn_readlane(idv, 2 * (pr - idbase) + half);
+    const uint16_t* src = pool + ((int64_t)id * P.Hkv + kvh) * TILE;
+    uint16_t* dst = ring + slot * pair_stage_elems<D>() + wslot * TILE;
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+      load16_lds(src, (uint32_t)(c * 1024 + lane * 16), dst + c * 512);
+  };
+
+  // One pair of blocks.  MASKED: the pair holds keys past some column's
+  // position or past kv1 (the diagonal and the range end); otherwise the
+  // step is straight-line code apart from the rare rescale.
+  auto compute = [&](const uint16_t* st, int kp0, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
+    // scores: each K operand read from LDS just before the MFMAs of all
+    // column tiles that use it (few operand registers live at a time)
+    f32x4 sa[CT], sb[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      sa[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sb[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      // keep the operand reads in step with their MFMAs (register budget).
+      // A real instruction: hazard bookkeeping counts an asm statement as
+      // one wait state.
+      if (c >= 2) asm volatile("s_nop 0" ::: "memory");
+      const bf16x8 ka = lds16(st + c * 512 + lane * 8);
+      const bf16x8 kb = lds16(st + 2 * TILE + c * 512 + lane * 8);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        sa[ct] = mfma32(ka, qop[ct][c], sa[ct]);
+        sb[ct] = mfma32(kb, qop[ct][c], sb[ct]);
+      }
+    }
+    float x[CT][8];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[ct][i] = sa[ct][i];
+        x[ct][i + 4] = sb[ct][i];
+      }
+    }
+    if (MASKED) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kp0 + 4 * g + i;
+          if (key > cpos[ct]) x[ct][i] = -INFINITY;
+          if (key + kBlock > cpos[ct]) x[ct][i + 4] = -INFINITY;
+        }
+      }
+    }
+    float mc[CT];
+    bool grow = false;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      float m = x[ct][0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) m = fmaxf(m, x[ct][i]);
+      mc[ct] = column_max(m) * P.scale_log2;
+      grow = grow || mc[ct] > mref[ct] + kRescaleSlack;
+    }
+    // probabilities and PV; written out on both sides of the (rare) rescale
+    // branch so that the accumulators meet only after the MFMAs
+    auto pv = [&]() {
+      bf16x8 pop[CT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          pop[ct][i] = (__bf16)__builtin_amdgcn_exp2f(
+              __builtin_fmaf(x[ct][i], P.scale_log2, -msub[ct]));
+        lacc[ct] = mfma32(ones, pop[ct], lacc[ct]);
+      }
+#pragma unroll
+      for (int hc = 0; hc < 2 * KC; ++hc) {
+        if (hc >= 2) asm volatile("s_nop 0" ::: "memory");
+        // V operand of dims (hc / KC) * D/2 + 16 (hc % KC) ..: 4 keys of
+        // the first block, then the same keys of the second
+        const uint16_t* va = st + TILE + hc * 256 + lane * 4;
+        bf16x8 v = __builtin_shufflevector(lds8(va), lds8(va + 2 * TILE), 0, 1, 2, 3, 4, 5,
+                                           6, 7);
+        if (MASKED) {
+          // keys at or past kv1 may be unwritten pool slots: zero their V
+          // so a 0 weight cannot meet a NaN
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kp0 + 4 * g + i;
+            if (key >= it.kv1) v[i] = (__bf16)0.0f;
+            if (key + kBlock >= it.kv1) v[i + 4] = (__bf16)0.0f;
+          }
+        }
+        const int n = (hc & 1) * KC + (hc >> 1);  // dim tile of region hc
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) acc[ct][n] = mfma32(v, pop[ct], acc[ct][n]);
+      }
+    };
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      // move the reference to the new max where it grew past the slack;
+      // alpha is exactly 1 for the columns that keep theirs
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const float mnew = mc[ct] > mref[ct] + kRescaleSlack ? mc[ct] : mref[ct];
+        const float alpha =
+            mnew == mref[ct] ? 1.0f : __builtin_amdgcn_exp2f(mref[ct] - mnew);
+        mref[ct] = mnew;
+        msub[ct] = mnew == -INFINITY ? 0.0f : mnew;
+        lacc[ct] *= alpha;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[ct][n] *= alpha;
+      }
+      pv();
+    } else {
+      pv();
+    }
+  };
+
+  // Pair pr lives in stage pr % NS.  Every wave issues the same number of
+  // loads per stage (the prefetch is unconditional, clamped to the last
+  // pair), so after the wait at step pr at most the loads of the NS - 2
+  // later stages are still in flight and stage pr is complete; the barrier
+  // then makes every wave's tile visible and guarantees that stage
+  // (pr - 1) % NS, refilled next, has been read by all waves.
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) issue(s, min(s, npairs - 1));
+  for (int pr = 0; pr < npairs; ++pr) {
+    wait_loads_and_barrier<LPS * (NS - 2)>();
+    issue((pr + NS - 1) % NS, min(pr + NS - 1, npairs - 1));
+    const int kp0 = (jb0 + 2 * pr) * kBlock;
+    const uint16_t* st = ring + (pr % NS) * pair_stage_elems<D>();
+    if (kp0 > wlast) continue;  // past every key this wave's tokens see
+    if (kp0 + 2 * kBlock - 1 <= wt.posbase && kp0 + 2 * kBlock <= it.kv1)
+      compute(st, kp0, std::false_type{});
+    else
+      compute(st, kp0, std::true_type{});
+  }
+  // the ring is free again once every load has landed and every wave is done
+  wait_loads_and_barrier<0>();
+  if (active) {
+    // every row of the all-ones product holds the column sum
+    float l[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) l[ct] = lacc[ct][0];
+    finish_unit<D, CT>(P, wt, kvh, lane, acc, mref, l);
+  }
 }
 
 // A work item read back from the workspace is used only if every index it
@@ -662,10 +1001,10 @@ __device__ __forceinline__ void run_unit(const AttendParams& P,
 // workspace then costs outputs, never an out-of-bounds access).
 __device__ __forceinline__ bool item_ok(const AttendParams& P,
                                         const WorkItem& it) {
-  const int cols = it.kind == kKindPrefill ? 16 * kPrefillColTiles
-                                           : 16 * kDecodeColTiles;
+  const int maxtok = it.kind == kKindPrefill ? prefill_tile_tokens(P.G)
+                                             : decode_tile_tokens(P.G);
   bool ok = it.seq >= 0 && it.seq < P.num_seqs && it.tok0 >= 0 &&
-            it.ntok >= 1 && it.ntok * P.G <= cols &&
+            it.ntok >= 1 && it.ntok <= maxtok &&
             it.tok0 + it.ntok <= P.num_q_tokens && it.kv0 >= 0 &&
             (it.kv0 & 31) == 0 && it.kv1 > it.kv0 && it.kv1 <= P.max_seq_len &&
             ((it.kv1 + kBlock - 1) / kBlock) <= P.bt_stride &&
@@ -678,7 +1017,8 @@ __device__ __forceinline__ bool item_ok(const AttendParams& P,
 }
 
 template <int D, bool MIXED>
-__device__ __forceinline__ void attend_body(const AttendParams& P) {
+__device__ __forceinline__ void attend_body(const AttendParams& P,
+                                            uint16_t* ring) {
   const int lane = threadIdx.x & 63;
   if (P.hdr->signature != plan_signature(P)) {
     if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(&P.hdr->error, 4u);
@@ -689,61 +1029,46 @@ __device__ __forceinline__ void attend_body(const AttendParams& P) {
   uint32_t num_pre = P.hdr->num_prefill_work;
   if (num_pre > num_work) num_pre = num_work;
   const uint32_t Hkv = (uint32_t)P.Hkv;
-  const uint32_t nwaves = gridDim.x * (kAttendThreads / 64);
-  const uint32_t wid = __builtin_amdgcn_readfirstlane(
-      blockIdx.x * (kAttendThreads / 64) + (threadIdx.x >> 6));
-  // Two queues: prefill units [0, num_pre) and decode units [num_pre,
-  // num_work) of the work list.  In a mixed batch one wave in
-  // kPrefillWaveShare starts on prefill, the others on decode, so
-  // compute-bound prefill tiles and bandwidth-bound decode splits share the
-  // CUs; a wave whose queue runs dry moves to the other one.  Each
-  // wave's first unit is assigned by its index (no queue traffic at launch),
-  // later ones come from the queue's counter, offset by the static share.
-  const uint32_t qn[2] = {num_pre, num_work - num_pre};
-  const uint32_t qbase[2] = {0u, num_pre};
-  uint32_t nstatic[2], q, idx;
+  constexpr uint32_t kWpg = kAttendThreads / 64;  // waves per workgroup
+  const uint32_t wslot = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t ndec = num_work - num_pre;  // decode units follow the prefill ones
+  auto claim = [&](uint32_t* counter) {
+    uint32_t t = 0;
+    if (lane == 0) t = atomicAdd(counter, 1u);
+    return __builtin_amdgcn_readfirstlane(__shfl(t, 0));
+  };
+
+  // Prefill units (tile x kv head) go to whole workgroups: workgroup i
+  // starts on unit i, later ones come from the prefill queue.  Workgroups
+  // left without a prefill unit start on the decode units, one per wave; the
+  // others' waves join the decode queue when the prefill queue is empty.
+  uint32_t pre_static = 0;
   if (MIXED && num_pre > 0) {
-    constexpr uint32_t S = kPrefillWaveShare;  // 1 of every S waves
-    nstatic[0] = (nwaves + S - 1) / S;
-    nstatic[1] = nwaves - nstatic[0];
-    q = (wid % S == 0) ? 0u : 1u;
-    idx = q == 0 ? wid / S : wid - wid / S - 1;
-  } else {
-    nstatic[0] = 0;
-    nstatic[1] = nwaves;
-    q = 1;
-    idx = wid;
-    if (num_pre > 0) {  // cannot happen without prefill items; kept total
-      q = 0;
-      nstatic[0] = nwaves;
-      nstatic[1] = 0;
+    __shared__ uint32_t next_unit[2];
+    pre_static = min(gridDim.x, num_pre);
+    uint32_t u = blockIdx.x;
+    int k = 0;
+    while (u < num_pre) {
+      const WorkItem it = P.items[u / Hkv];
+      if (item_ok(P, it) && it.kind == kKindPrefill)
+        run_tile<D>(P, it, (int)(u % Hkv), lane, (int)wslot, ring);
+      if (threadIdx.x == 0)
+        next_unit[k] = atomicAdd(&P.hdr->prefill_counter, 1u) + pre_static;
+      __syncthreads();
+      u = __builtin_amdgcn_readfirstlane(next_unit[k]);
+      k ^= 1;
     }
   }
-  uint32_t* const counters[2] = {&P.hdr->prefill_counter, &P.hdr->work_counter};
-  bool switched = false;
-  for (;;) {
-    if (idx >= qn[q]) {
-      // both queues exhausted (or the other one is empty): done
-      if (switched || qn[q ^ 1u] == 0) break;
-      switched = true;
-      q ^= 1u;
-      uint32_t t = 0;
-      if (lane == 0) t = atomicAdd(counters[q], 1u);
-      idx = __builtin_amdgcn_readfirstlane(__shfl(t, 0)) + nstatic[q];
-      continue;
-    }
-    const uint32_t w = qbase[q] + idx;
+  const uint32_t dec_static = (gridDim.x - pre_static) * kWpg;
+  uint32_t idx = blockIdx.x >= pre_static
+                     ? (blockIdx.x - pre_static) * kWpg + wslot
+                     : claim(&P.hdr->work_counter) + dec_static;
+  while (idx < ndec) {
+    const uint32_t w = num_pre + idx;
     const WorkItem it = P.items[w / Hkv];
-    const int kvh = (int)(w % Hkv);
-    if (item_ok(P, it)) {
-      if (MIXED && it.kind == kKindPrefill)
-        run_unit<D, kPrefillColTiles, kPrefillStages, false>(P, it, kvh, lane);
-      else
-        run_unit<D, kDecodeColTiles, kDecodeStages, true>(P, it, kvh, lane);
-    }
-    uint32_t t = 0;
-    if (lane == 0) t = atomicAdd(counters[q], 1u);
-    idx = __builtin_amdgcn_readfirstlane(__shfl(t, 0)) + nstatic[q];
+    if (item_ok(P, it) && it.kind == kKindDecode)
+      run_unit<D, kDecodeColTiles, kDecodeStages, true>(P, it, (int)(w % Hkv), lane);
+    idx = claim(&P.hdr->work_counter) + dec_static;
   }
 }
 
@@ -753,15 +1078,16 @@ template <int D>
 __global__ __launch_bounds__(kAttendThreads)
 __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2, 8)))
 void attend_decode_kernel(AttendParams P) {
-  attend_body<D, false>(P);
+  attend_body<D, false>(P, nullptr);
 }
 
-// Mixed batches: decode and prefill items in the same launch.
+// Mixed batches: prefill tiles and decode units in the same launch.
 template <int D>
 __global__ __launch_bounds__(kAttendThreads)
 __attribute__((amdgpu_waves_per_eu(2, 8)))
 void attend_mixed_kernel(AttendParams P) {
-  attend_body<D, true>(P);
+  __shared__ __attribute__((aligned(16))) uint16_t ring[prefill_ring_elems<D>()];
+  attend_body<D, true>(P, ring);
 }
 
 // ---------------------------------------------------------------------------

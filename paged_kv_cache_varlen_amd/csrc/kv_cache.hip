@@ -8,14 +8,23 @@
 //
 // Pool tile layout (block n, kv head g), 16*D bf16, H = D/2:
 //   K(t, d) at ((d/8)*16 + t)*8 + d%8      -> 16 bytes per (t, 8-dim chunk)
-//   V(t, d) at (((d%H)*4 + t/4)*2 + d/H)*4 + t%4
-// The attention kernel loads each tile with fully contiguous 1 KiB wave loads
-// that land directly in MFMA operand order.
+//   V(t, d) at ((((d%H)/16*2 + d/H)*4 + t/4)*16 + d%16)*4 + t%4
+//                                          -> 8 bytes per (4 tokens, dim)
+// The attention kernel reads each tile with fully contiguous wave loads
+// (16 bytes per lane for K, 8 for V) that land directly in MFMA operand
+// order.
 #include "pa_device.h"
 
 namespace pa {
 
 namespace {
+
+// Offset of V(t, d) inside a tile.
+template <int D>
+__device__ __forceinline__ int v_offset(int t, int d) {
+  constexpr int H = D / 2;
+  return ((((d % H) / 16 * 2 + d / H) * 4 + (t >> 2)) * 16 + d % 16) * 4 + (t & 3);
+}
 
 // One thread per (token, kv head, 8-dim chunk): a 16-byte K copy and eight
 // 2-byte V stores.  Copies are integer moves: exact bits.
@@ -26,7 +35,6 @@ __global__ __launch_bounds__(256) void write_kv_kernel(
     int64_t num_tokens, int Hkv, uint16_t* __restrict__ k_cache,
     uint16_t* __restrict__ v_cache, int64_t num_slots) {
   constexpr int kChunks = D / 8;
-  constexpr int H = D / 2;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per_token = (int64_t)Hkv * kChunks;
   if (gid >= num_tokens * per_token) return;
@@ -49,8 +57,7 @@ __global__ __launch_bounds__(256) void write_kv_kernel(
   for (int j = 0; j < 8; ++j) {
     const int d = c * 8 + j;
     const uint16_t bits = (uint16_t)(w[j >> 1] >> ((j & 1) * 16));
-    const int off = (((d % H) * 4 + (t >> 2)) * 2 + d / H) * 4 + (t & 3);
-    v_cache[tile + off] = bits;
+    v_cache[tile + v_offset<D>(t, d)] = bits;
   }
 }
 
@@ -63,7 +70,6 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(
     int32_t num_seqs, int64_t total_rows, int Hkv, uint16_t* __restrict__ k_out,
     uint16_t* __restrict__ v_out) {
   constexpr int kChunks = D / 8;
-  constexpr int H = D / 2;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per_row = (int64_t)Hkv * kChunks;
   if (gid >= total_rows * per_row) return;
@@ -91,8 +97,7 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
     const int d = c * 8 + jj;
-    const int off = (((d % H) * 4 + (t >> 2)) * 2 + d / H) * 4 + (t & 3);
-    w[jj >> 1] |= (uint32_t)v_cache[tile + off] << ((jj & 1) * 16);
+    w[jj >> 1] |= (uint32_t)v_cache[tile + v_offset<D>(t, d)] << ((jj & 1) * 16);
   }
   *reinterpret_cast<uint4*>(v_out + dst) = make_uint4(w[0], w[1], w[2], w[3]);
 }

@@ -2,6 +2,8 @@
 // operations and their sources are documented in include/pa.h.
 #include "pa.h"
 
+#include <cfloat>
+
 #include <hip/hip_runtime_api.h>
 
 #include <mutex>
@@ -159,6 +161,8 @@ pa_status prepare_attend(const void* q, const void* k_cache,
     return fail(PA_ERR_NULL, "pa_attend: NULL pointer");
   if (max_blocks_per_seq == 0 || (need_tensors && num_blocks == 0))
     return fail(PA_ERR_SHAPE, "pa_attend: empty pool or block table");
+  if (need_tensors && !(scale > 0.0f && scale <= FLT_MAX))
+    return fail(PA_ERR_SHAPE, "pa_attend: scale must be finite and > 0");
   if (need_tensors &&
       (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out) & 15))
     return fail(PA_ERR_SHAPE, "q, out and the pools must be 16-byte aligned");

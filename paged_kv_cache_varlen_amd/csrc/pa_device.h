@@ -20,11 +20,12 @@ constexpr int kLongDecode = 8192;
 constexpr int kSplitPrefill = 2048;  // logical tokens per prefill split
 // A prefill request is split along its keys only if it has fewer than this
 // many (query tile x kv head) work units on its own.
-constexpr int kPrefillUnsplitUnits = 512;
+constexpr int kPrefillUnsplitUnits = 256;
 constexpr int kDecodeColTiles = 1;   // 16 MFMA columns: up to 16/G tokens
-constexpr int kPrefillColTiles = 2;  // 32 MFMA columns: 32/G tokens
+constexpr int kPrefillColTiles = 2;  // per wave: 32 MFMA columns, 32/G tokens
+constexpr int kPrefillWaves = 4;     // waves sharing one prefill tile's K/V
 constexpr int kMaxGroup = 16;        // query heads per kv head
-constexpr int kAttendThreads = 256;  // 4 independent waves per workgroup
+constexpr int kAttendThreads = 256;  // 4 waves per workgroup
 
 enum ItemKind : int { kKindDecode = 0, kKindPrefill = 1 };
 
@@ -73,12 +74,17 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Tokens per decode tile / prefill tile for group size G (<= 16).
+// Tokens per decode tile / prefill tile for group size G (<= 16).  A
+// prefill tile is split between the kPrefillWaves waves of a workgroup, each
+// taking prefill_wave_tokens consecutive tokens of it.
 inline __host__ __device__ int decode_tile_tokens(int G) {
   return (16 * kDecodeColTiles) / G;
 }
-inline __host__ __device__ int prefill_tile_tokens(int G) {
+inline __host__ __device__ int prefill_wave_tokens(int G) {
   return (16 * kPrefillColTiles) / G;
+}
+inline __host__ __device__ int prefill_tile_tokens(int G) {
+  return kPrefillWaves * prefill_wave_tokens(G);
 }
 
 inline WorkspaceLayout workspace_layout(int32_t num_seqs, int64_t num_q_tokens,

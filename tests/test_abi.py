@@ -78,6 +78,10 @@ def attend_args(**over):
     (dict(wsb=100), _lib.PA_ERR_WORKSPACE),
     (dict(ws=FAKE + 16), _lib.PA_ERR_WORKSPACE),
     (dict(q=FAKE + 2), _lib.PA_ERR_SHAPE),
+    (dict(scale=0.0), _lib.PA_ERR_SHAPE),
+    (dict(scale=-0.125), _lib.PA_ERR_SHAPE),
+    (dict(scale=float("nan")), _lib.PA_ERR_SHAPE),
+    (dict(scale=float("inf")), _lib.PA_ERR_SHAPE),
 ])
 def test_attend_rejects_bad_arguments(lib, over, status):
     assert lib.pa_attend(*attend_args(**over)) == status

@@ -70,6 +70,14 @@ SMALL = {
     "mixed-g8-d128": ([2, 9, 600, 1025, 260], [2, 1, 2, 1, 37], 16, 2, 128),
     "mixed-g7-d64": ([20, 513, 33, 90], [1, 2, 33, 9], 14, 2, 64),
     "mixed-g16-d128": ([40, 1500, 31], [1, 1, 12], 32, 2, 128),
+    # kv head counts with one prefill lane (3, 12) and with eight lanes
+    # sharing a single kv head (1)
+    "mixed-h3-d64": ([300, 45, 2100, 64], [300, 1, 90, 20], 12, 3, 64),
+    "mixed-h12-d64": ([129, 700, 18], [129, 1, 18], 12, 12, 64),
+    "mixed-h1-d128": ([1200, 77, 5], [640, 1, 5], 4, 1, 128),
+    # a prefill tile straddling the 2048-key split boundary: some of its
+    # waves have no keys in the second split
+    "mixed-split-edge": ([2100, 40], [100, 1], 8, 2, 128),
 }
 
 
@@ -136,6 +144,24 @@ def test_attend_small_full_parity(name):
     ref = oracle.attend(w.q, kc, vc, w.block_tables, w.seq_lens,
                         w.query_start_loc, w.num_kv_heads, w.scale)
     check_close(tensor_bits(out), ref, name)
+
+
+@pytest.mark.parametrize("name", ["mixed-g4-d128", "mixed-g7-d64"])
+def test_extreme_logits(name):
+    # q scaled by 32 (exact in bf16): scores span hundreds of units in the
+    # exp2 domain, so any probability computed against a running max that is
+    # not the true column maximum overflows, and a lost max subtraction
+    # shows up as inf/NaN.
+    w = small(name, seed=6)
+    q = W.bf16_bits_to_f32(w.q) * np.float32(32.0)
+    w.q = W.f32_to_bf16_bits(q).reshape(w.q.shape)
+    u = Uploaded(w)
+    out = u.attend()
+    torch.cuda.synchronize()
+    kc, vc = oracle_pool(w)
+    ref = oracle.attend(w.q, kc, vc, w.block_tables, w.seq_lens,
+                        w.query_start_loc, w.num_kv_heads, w.scale)
+    check_close(tensor_bits(out), ref, name + " x32 logits")
 
 
 def test_one_hot_probe_is_exact():
