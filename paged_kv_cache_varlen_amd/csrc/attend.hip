@@ -575,10 +575,14 @@ __device__ __forceinline__ bf16x8 load_v(const uint16_t* vp, int c, int lane) {
 // read once) or cached loads (prefill: the tiles of a request are re-read by
 // all of its query tiles).  Block ids come 64 at a time, one per lane; each
 // chunk of 64 blocks runs its own pipeline.
+// If `counter` is not null, the next queue entry is claimed from it when the
+// load of the unit's last block is issued (its latency then hides behind the
+// last blocks and the output stores) and returned; otherwise 0.
 template <int D, int CT, int NB, bool STREAM>
-__device__ __forceinline__ void run_unit(const AttendParams& P,
-                                         const WorkItem& it, int kvh,
-                                         int lane) {
+__device__ __forceinline__ uint32_t run_unit(const AttendParams& P,
+                                             const WorkItem& it, int kvh,
+                                             int lane,
+                                             uint32_t* counter = nullptr) {
   constexpr int KC = D / 32;
   constexpr int NT = D / 16;
   const int g = lane >> 4, r = lane & 15;
@@ -603,6 +607,8 @@ __device__ __forceinline__ void run_unit(const AttendParams& P,
   const int jb1 = (it.kv1 + kBlock - 1) >> 4;
   const int32_t* btrow = P.bt + (int64_t)b * P.bt_stride;
   const int64_t tile_elems = (int64_t)kBlock * D;
+  uint32_t claim = 0;
+  bool claimed = false;
 
   for (int c0 = jb0; c0 < jb1; c0 += 64) {
     const int nblk = min(64, jb1 - c0);
@@ -612,6 +618,10 @@ __device__ __forceinline__ void run_unit(const AttendParams& P,
     idv = idv < 0 ? 0 : (idv >= P.num_blocks ? (int)(P.num_blocks - 1) : idv);
 
     auto issue = [&](KVBlock<D>& buf, int j) {
+      if (counter != nullptr && !claimed && c0 + j == jb1 - 1) {
+        if (lane == 0) claim = atomicAdd(counter, 1u);
+        claimed = true;
+      }
       const int id = __builtin_amdgcn_readlane(idv, j);
       const int64_t off = ((int64_t)id * P.Hkv + kvh) * tile_elems;
       const uint16_t* kp = P.k_cache + off;
@@ -700,7 +710,12 @@ __device__ __forceinline__ void run_unit(const AttendParams& P,
     l[ct] += __shfl_xor(l[ct], 16);
     l[ct] += __shfl_xor(l[ct], 32);
   }
+  // exactly one claim per call, whatever the loop above did
+  if (counter != nullptr && !claimed) {
+    if (lane == 0) claim = atomicAdd(counter, 1u);
+  }
   finish_unit<D, CT>(P, it, kvh, lane, acc, mrun, l);
+  return __builtin_amdgcn_readfirstlane(__shfl(claim, 0));
 }
 
 // ---- prefill tiles: one workgroup, K/V shared through LDS -------------------
@@ -1048,7 +1063,7 @@ __device__ __forceinline__ void attend_body(const AttendParams& P,
     pre_static = min(gridDim.x, num_pre);
     uint32_t u = blockIdx.x;
     int k = 0;
-    while (u < num_pre) {
+    for (uint32_t pass = 0; u < num_pre && pass <= num_pre; ++pass) {
       const WorkItem it = P.items[u / Hkv];
       if (item_ok(P, it) && it.kind == kKindPrefill)
         run_tile<D>(P, it, (int)(u % Hkv), lane, (int)wslot, ring);
@@ -1063,12 +1078,17 @@ __device__ __forceinline__ void attend_body(const AttendParams& P,
   uint32_t idx = blockIdx.x >= pre_static
                      ? (blockIdx.x - pre_static) * kWpg + wslot
                      : claim(&P.hdr->work_counter) + dec_static;
-  while (idx < ndec) {
+  // Every pass takes one queue entry (one atomic increment), so the loop
+  // ends; the pass bound is a second guarantee of that.
+  for (uint32_t pass = 0; idx < ndec && pass <= ndec; ++pass) {
     const uint32_t w = num_pre + idx;
     const WorkItem it = P.items[w / Hkv];
     if (item_ok(P, it) && it.kind == kKindDecode)
-      run_unit<D, kDecodeColTiles, kDecodeStages, true>(P, it, (int)(w % Hkv), lane);
-    idx = claim(&P.hdr->work_counter) + dec_static;
+      idx = run_unit<D, kDecodeColTiles, kDecodeStages, true>(
+                P, it, (int)(w % Hkv), lane, &P.hdr->work_counter) +
+            dec_static;
+    else
+      idx = claim(&P.hdr->work_counter) + dec_static;
   }
 }
 
