@@ -17,6 +17,9 @@ Prints one JSON line:
            from HIP events on the launch stream;
   mixed_step  mixed chunked-prefill step (1920-token chunk on 1536 cached
            tokens + 128 decodes): tokens/s per layer;
+  prefill_tile  that step's prefill chunk alone: attention TFLOP/s (visible
+           query-key pairs x 4 x head_dim x q heads) against the bf16 MFMA
+           peak;
   cpu_baseline  the CPU oracle (fp64) on the same headline workload.
 
     python bench.py [--steps K] [--warmup W] [--config 2] [--no-mixed]
@@ -44,7 +47,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--config", default="2",
+                    help="workload timed: 1-5, or p for the mixed step's "
+                         "prefill chunk alone")
     ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--min-working-set-gib", type=float, default=2.0)
@@ -159,36 +164,43 @@ class Runner:
         return (t1 - t0) * 1e3 / steps, attend_ms
 
 
-def cpu_baseline(w, budget_s=20.0):
-    """The oracle on the same workload: as many whole sequences as fit the
-    time budget (all heads), scaled to KV GB/s."""
+def cpu_baseline(w, min_s=10.0, max_s=30.0):
+    """The oracle on the same workload, all heads of every sequence, in whole
+    passes over the batch until at least min_s of oracle time (at most max_s,
+    stopping between sequences), scaled to KV GB/s."""
     import oracle
     kc = np.zeros(w.pool_elems(), np.uint16)
     vc = np.zeros(w.pool_elems(), np.uint16)
     oracle.write_kv(kc, vc, w.k_dense[w.fill_rows], w.v_dense[w.fill_rows], w.fill_slots)
     oracle.write_kv(kc, vc, w.k_new, w.v_new, w.new_slots)
     threads = oracle.default_threads()
-    done_seqs, kv_bytes, spent = 0, 0, 0.0
     per_tok = 2 * w.num_kv_heads * w.head_dim * 2
-    order = list(range(w.num_seqs))
-    for b in order:
+    rows = []
+    for b in range(w.num_seqs):
         t0, t1 = int(w.query_start_loc[b]), int(w.query_start_loc[b + 1])
-        rows = np.array([(t, h) for t in range(t0, t1) for h in range(w.num_q_heads)],
-                        np.int64)
-        s = time.perf_counter()
-        oracle.attend_rows(w.q, kc, vc, w.block_tables, w.seq_lens,
-                           w.query_start_loc, w.num_kv_heads, w.scale, rows,
-                           nthreads=threads)
-        spent += time.perf_counter() - s
-        done_seqs += 1
-        kv_bytes += int(w.seq_lens[b]) * per_tok
-        if spent >= budget_s:
+        rows.append(np.array([(t, h) for t in range(t0, t1)
+                              for h in range(w.num_q_heads)], np.int64))
+    done_seqs, kv_bytes, spent = 0, 0, 0.0
+    while spent < min_s:
+        for b in range(w.num_seqs):
+            s = time.perf_counter()
+            oracle.attend_rows(w.q, kc, vc, w.block_tables, w.seq_lens,
+                               w.query_start_loc, w.num_kv_heads, w.scale,
+                               rows[b], nthreads=threads)
+            spent += time.perf_counter() - s
+            done_seqs += 1
+            kv_bytes += int(w.seq_lens[b]) * per_tok
+            if spent >= max_s:
+                break
+        if spent >= max_s:
             break
     return {"value": round(kv_bytes / spent / 1e9, 4), "unit": "GB/s",
             "cores": threads, "kind": "oracle",
-            "sample": "%d of %d sequences of the headline workload, all %d query "
-                      "heads, fp64 C oracle with OpenMP, %.1f s"
-                      % (done_seqs, w.num_seqs, w.num_q_heads, spent)}
+            "sample": "%d sequence attentions (%.1f passes over the %d sequences "
+                      "of the headline workload), all %d query heads, fp64 C "
+                      "oracle with OpenMP, %.1f s"
+                      % (done_seqs, done_seqs / w.num_seqs, w.num_seqs,
+                         w.num_q_heads, spent)}
 
 
 def main():
@@ -205,7 +217,7 @@ def main():
     if args.copy_probe:
         return copy_probe()
 
-    w = W.make_config(args.config)
+    w = W.make_prefill_chunk() if args.config == "p" else W.make_config(int(args.config))
     alg = algorithmic(w)
     r = Runner(w, args.min_working_set_gib)
     ms_step, attend_ms = r.run(args.steps, args.warmup)
@@ -236,10 +248,18 @@ def main():
             "attend_ms": round(attend_ms, 5),
             "algorithmic_bytes": alg["attend_bytes"]},
     }
+    if args.config == "p":
+        # the prefill chunk alone is a dense contraction: priced against MFMA
+        tflops = alg["flops"] / (attend_ms * 1e-3) / 1e12
+        line["roofline"].update({
+            "bound": "mfma", "achieved": round(tflops, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "algorithmic_flops": alg["flops"]})
     del r
     torch.cuda.empty_cache()
 
-    if not args.no_mixed and args.config != 3:
+    if not args.no_mixed and args.config not in ("3", "p"):
         w3 = W.make_config(3)
         a3 = algorithmic(w3)
         r3 = Runner(w3, args.min_working_set_gib)
@@ -250,6 +270,18 @@ def main():
             "kv_read_gbs": round(a3["kv_bytes"] / (ms3 * 1e-3) / 1e9, 2),
             "attend_tflops": round(a3["flops"] / (att3 * 1e-3) / 1e12, 2)}
         del r3
+        torch.cuda.empty_cache()
+        wp = W.make_prefill_chunk()
+        ap = algorithmic(wp)
+        rp = Runner(wp, args.min_working_set_gib)
+        _, attp = rp.run(max(20, args.steps // 4), max(5, args.warmup // 2))
+        tflops = ap["flops"] / (attp * 1e-3) / 1e12
+        line["prefill_tile"] = {
+            "workload": wp.name, "attend_ms": round(attp, 5),
+            "flops": ap["flops"], "tflops": round(tflops, 2),
+            "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+            "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+        del rp
         torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:

@@ -355,6 +355,13 @@ def config_lengths(k: int):
     raise ValueError(k)
 
 
+def make_prefill_chunk() -> Workload:
+    """The prefill request of configuration 3 on its own (1920 new tokens on
+    1536 cached, Llama-3-8B heads), for timing the prefill tiles alone."""
+    return make_workload("llama3-8b-prefill-chunk-1920-on-1536", [1536 + 1920],
+                         [1920], 32, 8, 128, seed=3)
+
+
 def make_config(k: int, shared: bool = True) -> Workload:
     """Synthetic configuration k in 1..5 (seeds 1000+k data, 2000+k lengths,
     3000+k tables)."""
