@@ -54,6 +54,9 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 // block buffers of the decode pipeline (blocks in flight + 1)
 constexpr int kDecodeStages = 3;
+// In a mixed batch, the first 1 / kPrefillWgShare of the workgroups start on
+// prefill tiles and the others on decode units.
+constexpr uint32_t kPrefillWgShare = 2;
 
 struct AttendParams {
   const uint16_t* q;
@@ -962,6 +965,9 @@ __device__ __forceinline__ void run_tile(const AttendParams& P,
       }
     };
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      // (a side effect keeps this a branch: the compiler would otherwise run
+      // the rescale on every step with alpha = 1)
+      asm volatile("s_nop 0");
       // move the reference to the new max where it grew past the slack;
       // alpha is exactly 1 for the columns that keep theirs
 #pragma unroll
@@ -1053,15 +1059,19 @@ __device__ __forceinline__ void attend_body(const AttendParams& P,
     return __builtin_amdgcn_readfirstlane(__shfl(t, 0));
   };
 
-  // Prefill units (tile x kv head) go to whole workgroups: workgroup i
-  // starts on unit i, later ones come from the prefill queue.  Workgroups
-  // left without a prefill unit start on the decode units, one per wave; the
-  // others' waves join the decode queue when the prefill queue is empty.
+  // Prefill units (tile x kv head) go to whole workgroups, decode units to
+  // single waves.  In a mixed batch the first 1 / kPrefillWgShare of the
+  // workgroups start on prefill units (workgroup i on unit i, later ones
+  // from the prefill queue) and then move their waves to the decode queue;
+  // the others start on decode units and, once all of their waves have run
+  // out of them, take the prefill units left.  Compute-bound tiles and
+  // bandwidth-bound decode thus share every CU, and a prefill-only batch
+  // still uses every workgroup.  Every pass of each loop takes one queue
+  // entry (one atomic increment), so the loops end; the pass bounds are a
+  // second guarantee of that.
+  __shared__ uint32_t next_unit[2];
   uint32_t pre_static = 0;
-  if (MIXED && num_pre > 0) {
-    __shared__ uint32_t next_unit[2];
-    pre_static = min(gridDim.x, num_pre);
-    uint32_t u = blockIdx.x;
+  auto prefill_units = [&](uint32_t u) {
     int k = 0;
     for (uint32_t pass = 0; u < num_pre && pass <= num_pre; ++pass) {
       const WorkItem it = P.items[u / Hkv];
@@ -1073,23 +1083,39 @@ __device__ __forceinline__ void attend_body(const AttendParams& P,
       u = __builtin_amdgcn_readfirstlane(next_unit[k]);
       k ^= 1;
     }
-  }
+  };
+  const bool mixed = MIXED && num_pre > 0;
+  if (mixed) pre_static = min(gridDim.x / kPrefillWgShare, num_pre);
   const uint32_t dec_static = (gridDim.x - pre_static) * kWpg;
-  uint32_t idx = blockIdx.x >= pre_static
-                     ? (blockIdx.x - pre_static) * kWpg + wslot
-                     : claim(&P.hdr->work_counter) + dec_static;
-  // Every pass takes one queue entry (one atomic increment), so the loop
-  // ends; the pass bound is a second guarantee of that.
-  for (uint32_t pass = 0; idx < ndec && pass <= ndec; ++pass) {
-    const uint32_t w = num_pre + idx;
-    const WorkItem it = P.items[w / Hkv];
-    if (item_ok(P, it) && it.kind == kKindDecode)
-      idx = run_unit<D, kDecodeColTiles, kDecodeStages, true>(
-                P, it, (int)(w % Hkv), lane, &P.hdr->work_counter) +
-            dec_static;
-    else
-      idx = claim(&P.hdr->work_counter) + dec_static;
+  auto decode_units = [&](uint32_t idx) {
+    for (uint32_t pass = 0; idx < ndec && pass <= ndec; ++pass) {
+      const uint32_t w = num_pre + idx;
+      const WorkItem it = P.items[w / Hkv];
+      if (item_ok(P, it) && it.kind == kKindDecode)
+        idx = run_unit<D, kDecodeColTiles, kDecodeStages, true>(
+                  P, it, (int)(w % Hkv), lane, &P.hdr->work_counter) +
+              dec_static;
+      else
+        idx = claim(&P.hdr->work_counter) + dec_static;
+    }
+  };
+  if (!mixed) {
+    decode_units(blockIdx.x * kWpg + wslot);
+    return;
   }
+  const bool prefill_first = blockIdx.x < pre_static;
+  uint32_t u = blockIdx.x;
+  if (!prefill_first) {
+    // decode first, then (all waves done) the prefill units left
+    decode_units((blockIdx.x - pre_static) * kWpg + wslot);
+    __syncthreads();
+    if (threadIdx.x == 0)
+      next_unit[0] = atomicAdd(&P.hdr->prefill_counter, 1u) + pre_static;
+    __syncthreads();
+    u = __builtin_amdgcn_readfirstlane(next_unit[0]);
+  }
+  prefill_units(u);
+  if (prefill_first) decode_units(claim(&P.hdr->work_counter) + dec_static);
 }
 
 // Decode-only batches: registers for the 3-stage pipeline (two waves per
