@@ -54,9 +54,10 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 // block buffers of the decode pipeline (blocks in flight + 1)
 constexpr int kDecodeStages = 3;
-// In a mixed batch, the first 1 / kPrefillWgShare of the workgroups start on
-// prefill tiles and the others on decode units.
-constexpr uint32_t kPrefillWgShare = 2;
+// In a mixed batch, the first kPrefillWgNum / kPrefillWgDen of the
+// workgroups start on prefill tiles and the others on decode units.
+constexpr uint32_t kPrefillWgNum = 3;
+constexpr uint32_t kPrefillWgDen = 8;
 
 struct AttendParams {
   const uint16_t* q;
@@ -1060,8 +1061,8 @@ __device__ __forceinline__ void attend_body(const AttendParams& P,
   };
 
   // Prefill units (tile x kv head) go to whole workgroups, decode units to
-  // single waves.  In a mixed batch the first 1 / kPrefillWgShare of the
-  // workgroups start on prefill units (workgroup i on unit i, later ones
+  // single waves.  In a mixed batch the first kPrefillWgNum / kPrefillWgDen
+  // of the workgroups start on prefill units (workgroup i on unit i, later ones
   // from the prefill queue) and then move their waves to the decode queue;
   // the others start on decode units and, once all of their waves have run
   // out of them, take the prefill units left.  Compute-bound tiles and
@@ -1085,7 +1086,7 @@ __device__ __forceinline__ void attend_body(const AttendParams& P,
     }
   };
   const bool mixed = MIXED && num_pre > 0;
-  if (mixed) pre_static = min(gridDim.x / kPrefillWgShare, num_pre);
+  if (mixed) pre_static = min(gridDim.x * kPrefillWgNum / kPrefillWgDen, num_pre);
   const uint32_t dec_static = (gridDim.x - pre_static) * kWpg;
   auto decode_units = [&](uint32_t idx) {
     for (uint32_t pass = 0; idx < ndec && pass <= ndec; ++pass) {
