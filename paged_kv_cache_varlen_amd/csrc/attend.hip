@@ -1072,32 +1072,49 @@ __device__ __forceinline__ void attend_body(const AttendParams& P,
   // second guarantee of that.
   __shared__ uint32_t next_unit[2];
   uint32_t pre_static = 0;
+  //
+  // The queue counters are left at zero for the next launch on the same
+  // plan (one plan serves several layers): each queue is claimed exactly a
+  // known number of times per launch -- once per unit processed, plus once
+  // per wave (decode queue) or workgroup (prefill queue) entering it by a
+  // claim -- so the claim that returns the last value is the last access to
+  // that counter in this launch, and it resets the counter.
+  const bool mixed = MIXED && num_pre > 0;
+  if (mixed) pre_static = min(gridDim.x * kPrefillWgNum / kPrefillWgDen, num_pre);
+  const uint32_t dec_static = (gridDim.x - pre_static) * kWpg;
+  const uint32_t dec_claims = ndec + pre_static * kWpg;
+  const uint32_t pre_claims = num_pre + (gridDim.x - pre_static);
+  // one claim on the decode queue by lane 0 (t: the value it returned)
+  auto dec_claimed = [&](uint32_t t) {
+    if (t + 1u == dec_claims && lane == 0) atomicExch(&P.hdr->work_counter, 0u);
+    return t + dec_static;
+  };
+  auto pre_claim = [&]() {  // thread 0 only
+    const uint32_t t = atomicAdd(&P.hdr->prefill_counter, 1u);
+    if (t + 1u == pre_claims) atomicExch(&P.hdr->prefill_counter, 0u);
+    return t + pre_static;
+  };
   auto prefill_units = [&](uint32_t u) {
     int k = 0;
     for (uint32_t pass = 0; u < num_pre && pass <= num_pre; ++pass) {
       const WorkItem it = P.items[u / Hkv];
       if (item_ok(P, it) && it.kind == kKindPrefill)
         run_tile<D>(P, it, (int)(u % Hkv), lane, (int)wslot, ring);
-      if (threadIdx.x == 0)
-        next_unit[k] = atomicAdd(&P.hdr->prefill_counter, 1u) + pre_static;
+      if (threadIdx.x == 0) next_unit[k] = pre_claim();
       __syncthreads();
       u = __builtin_amdgcn_readfirstlane(next_unit[k]);
       k ^= 1;
     }
   };
-  const bool mixed = MIXED && num_pre > 0;
-  if (mixed) pre_static = min(gridDim.x * kPrefillWgNum / kPrefillWgDen, num_pre);
-  const uint32_t dec_static = (gridDim.x - pre_static) * kWpg;
   auto decode_units = [&](uint32_t idx) {
     for (uint32_t pass = 0; idx < ndec && pass <= ndec; ++pass) {
       const uint32_t w = num_pre + idx;
       const WorkItem it = P.items[w / Hkv];
       if (item_ok(P, it) && it.kind == kKindDecode)
-        idx = run_unit<D, kDecodeColTiles, kDecodeStages, true>(
-                  P, it, (int)(w % Hkv), lane, &P.hdr->work_counter) +
-              dec_static;
+        idx = dec_claimed(run_unit<D, kDecodeColTiles, kDecodeStages, true>(
+            P, it, (int)(w % Hkv), lane, &P.hdr->work_counter));
       else
-        idx = claim(&P.hdr->work_counter) + dec_static;
+        idx = dec_claimed(claim(&P.hdr->work_counter));
     }
   };
   if (!mixed) {
@@ -1110,13 +1127,12 @@ __device__ __forceinline__ void attend_body(const AttendParams& P,
     // decode first, then (all waves done) the prefill units left
     decode_units((blockIdx.x - pre_static) * kWpg + wslot);
     __syncthreads();
-    if (threadIdx.x == 0)
-      next_unit[0] = atomicAdd(&P.hdr->prefill_counter, 1u) + pre_static;
+    if (threadIdx.x == 0) next_unit[0] = pre_claim();
     __syncthreads();
     u = __builtin_amdgcn_readfirstlane(next_unit[0]);
   }
   prefill_units(u);
-  if (prefill_first) decode_units(claim(&P.hdr->work_counter) + dec_static);
+  if (prefill_first) decode_units(dec_claimed(claim(&P.hdr->work_counter)));
 }
 
 // Decode-only batches: registers for the 3-stage pipeline (two waves per

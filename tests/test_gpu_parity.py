@@ -254,6 +254,19 @@ def test_plan_then_planned_equals_attend(name):
     assert np.array_equal(a, b1) and np.array_equal(a, b2)
 
 
+@pytest.mark.parametrize("k", [2, 3])
+def test_one_plan_several_launches(k):
+    # more units than resident waves, so most units are claimed from the
+    # work queues: every launch on the same plan must find them ready again
+    w = W.make_config(k)
+    u = Uploaded(w)
+    a = tensor_bits(u.attend()).copy()
+    u.plan()
+    for rep in range(3):
+        b = tensor_bits(u.attend(out=torch.empty_like(u.q), planned=True)).copy()
+        assert np.array_equal(a, b), ("launch", rep)
+
+
 def test_planned_with_other_sizes_writes_nothing():
     w = small("mixed-g4-d128", seed=13)
     u = Uploaded(w)
