@@ -20,6 +20,8 @@ Prints one JSON line:
   prefill_tile  that step's prefill chunk alone: attention TFLOP/s (visible
            query-key pairs x 4 x head_dim x q heads) against the bf16 MFMA
            peak;
+  decode_part  that step's 128 decodes alone: attention kernel GB/s against
+           the HBM peak;
   cpu_baseline  the CPU oracle (fp64) on the same headline workload.
 
     python bench.py [--steps K] [--warmup W] [--config 2] [--no-mixed]
@@ -204,8 +206,18 @@ def cpu_baseline(w, min_s=10.0, max_s=30.0):
                 break
         if spent >= max_s:
             break
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    cpu = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(kv_bytes / spent / 1e9, 4), "unit": "GB/s",
-            "cores": threads, "kind": "oracle",
+            "cores": threads, "kind": "oracle", "cpu": cpu,
+            "os_cpu_count": os.cpu_count(),
             "sample": "%d sequence attentions (%.1f passes over the %d sequences "
                       "of the headline workload), all %d query heads, fp64 C "
                       "oracle with OpenMP, %.1f s"
@@ -292,6 +304,16 @@ def main():
             "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
             "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
         del rp
+        torch.cuda.empty_cache()
+        wd = W.make_decode_part()
+        ad = algorithmic(wd)
+        rd = Runner(wd, args.min_working_set_gib)
+        _, attd = rd.run(max(20, args.steps // 4), max(5, args.warmup // 2))
+        gbs = ad["attend_bytes"] / (attd * 1e-3) / 1e9
+        line["decode_part"] = {
+            "workload": wd.name, "attend_ms": round(attd, 5),
+            "attend_gbs": round(gbs, 2), "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        del rd
         torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:

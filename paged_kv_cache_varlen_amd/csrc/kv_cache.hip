@@ -26,8 +26,12 @@ __device__ __forceinline__ int v_offset(int t, int d) {
   return ((((d % H) / 16 * 2 + d / H) * 4 + (t >> 2)) * 16 + d % 16) * 4 + (t & 3);
 }
 
-// One thread per (token, kv head, 8-dim chunk): a 16-byte K copy and eight
-// 2-byte V stores.  Copies are integer moves: exact bits.
+// One thread per (quad of consecutive new tokens, kv head, 8-dim chunk): a
+// 16-byte K copy per token; for V, when the quad's slots are the four slots
+// 4m .. 4m+3 of one block (a prefill chunk's tokens), one 8-byte run per dim
+// (the layout keeps 4 consecutive tokens of a dim together), otherwise
+// 2-byte stores per token.  Copies are integer moves: exact bits.  Slots
+// outside [0, num_slots) are skipped.
 template <int D>
 __global__ __launch_bounds__(256) void write_kv_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -36,28 +40,60 @@ __global__ __launch_bounds__(256) void write_kv_kernel(
     uint16_t* __restrict__ v_cache, int64_t num_slots) {
   constexpr int kChunks = D / 8;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t per_token = (int64_t)Hkv * kChunks;
-  if (gid >= num_tokens * per_token) return;
-  const int64_t tok = gid / per_token;
-  const int rem = (int)(gid - tok * per_token);
+  const int64_t per_quad = (int64_t)Hkv * kChunks;
+  const int64_t nquads = (num_tokens + 3) >> 2;
+  if (gid >= nquads * per_quad) return;
+  const int64_t quad = gid / per_quad;
+  const int rem = (int)(gid - quad * per_quad);
   const int g = rem / kChunks;
   const int c = rem - g * kChunks;
-  const int64_t s = slots[tok];
-  if (s < 0 || s >= num_slots) return;
-  const int64_t blk = s >> 4;
-  const int t = (int)(s & 15);
-  const int64_t tile = (blk * Hkv + g) * (int64_t)(kBlock * D);
+  const int64_t tok0 = quad * 4;
+  const int ntok = (int)min((int64_t)4, num_tokens - tok0);
 
-  const uint4 kv = *reinterpret_cast<const uint4*>(k + tok * k_stride + g * D + c * 8);
-  *reinterpret_cast<uint4*>(k_cache + tile + ((int64_t)c * 16 + t) * 8) = kv;
-
-  const uint4 vv = *reinterpret_cast<const uint4*>(v + tok * v_stride + g * D + c * 8);
-  const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+  int64_t s[4];
+  uint4 vv[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int d = c * 8 + j;
-    const uint16_t bits = (uint16_t)(w[j >> 1] >> ((j & 1) * 16));
-    v_cache[tile + v_offset<D>(t, d)] = bits;
+  for (int i = 0; i < 4; ++i) {
+    s[i] = -1;
+    if (i < ntok) {
+      s[i] = slots[tok0 + i];
+      vv[i] = *reinterpret_cast<const uint4*>(v + (tok0 + i) * v_stride + g * D + c * 8);
+      const uint4 kv = *reinterpret_cast<const uint4*>(k + (tok0 + i) * k_stride + g * D + c * 8);
+      if (s[i] >= 0 && s[i] < num_slots) {
+        const int64_t tile = ((s[i] >> 4) * Hkv + g) * (int64_t)(kBlock * D);
+        *reinterpret_cast<uint4*>(k_cache + tile + ((int64_t)c * 16 + (s[i] & 15)) * 8) = kv;
+      }
+    }
+  }
+  const bool run = ntok == 4 && s[0] >= 0 && s[3] < num_slots && (s[0] & 3) == 0 &&
+                   s[1] == s[0] + 1 && s[2] == s[0] + 2 && s[3] == s[0] + 3;
+  if (run) {
+    const int64_t tile = ((s[0] >> 4) * Hkv + g) * (int64_t)(kBlock * D);
+    const int t0 = (int)(s[0] & 15);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int d = c * 8 + j;
+      uint32_t lo = 0, hi = 0;  // tokens 0,1 and 2,3 of the run at dim d
+      const int sh = (j & 1) * 16;
+      const uint32_t w0 = (&vv[0].x)[j >> 1] >> sh, w1 = (&vv[1].x)[j >> 1] >> sh;
+      const uint32_t w2 = (&vv[2].x)[j >> 1] >> sh, w3 = (&vv[3].x)[j >> 1] >> sh;
+      lo = (w0 & 0xffffu) | (w1 << 16);
+      hi = (w2 & 0xffffu) | (w3 << 16);
+      *reinterpret_cast<uint2*>(v_cache + tile + v_offset<D>(t0, d)) = make_uint2(lo, hi);
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i >= ntok || s[i] < 0 || s[i] >= num_slots) continue;
+    const int64_t tile = ((s[i] >> 4) * Hkv + g) * (int64_t)(kBlock * D);
+    const int t = (int)(s[i] & 15);
+    const uint32_t w[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int d = c * 8 + j;
+      v_cache[tile + v_offset<D>(t, d)] = (uint16_t)(w[j >> 1] >> ((j & 1) * 16));
+    }
   }
 }
 
@@ -111,7 +147,7 @@ hipError_t launch_write_kv(const uint16_t* k, const uint16_t* v,
                            uint16_t* v_cache, int64_t num_blocks,
                            hipStream_t stream) {
   if (num_tokens == 0) return hipSuccess;
-  const int64_t threads = num_tokens * num_kv_heads * (head_dim / 8);
+  const int64_t threads = ((num_tokens + 3) / 4) * num_kv_heads * (head_dim / 8);
   const dim3 block(256);
   const dim3 grid((unsigned)((threads + 255) / 256));
   const int64_t num_slots = num_blocks * kBlock;

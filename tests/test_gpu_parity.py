@@ -120,6 +120,29 @@ def test_write_kv_strided_rows_and_skips():
     assert np.array_equal(tensor_bits(vc).ravel(), ovc)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_write_kv_runs_and_single_slots(D):
+    # Quads of consecutive tokens: slots 4m..4m+3 of one block (one 8-byte V
+    # store per dim), unaligned, crossing a block edge, with a skipped or an
+    # out-of-range slot, and a partial quad at the tail (per-token stores).
+    slots = np.array([32, 33, 34, 35, 49, 50, 51, 52, 60, 61, 62, 63,
+                      64, 65, -1, 67, 124, 125, 126, 128, 78, 79, 80, 81,
+                      96, 97, 98], np.int64)
+    T, Hkv, nblocks = len(slots), 2, 8
+    rng = np.random.default_rng(7)
+    k = rng.integers(0, 1 << 16, (T, Hkv, D), dtype=np.uint16)
+    v = rng.integers(0, 1 << 16, (T, Hkv, D), dtype=np.uint16)
+    kc, vc = pa.alloc_pool(nblocks, Hkv, D, fill=float("nan"))
+    pa.write_kv(bf16_tensor(k), bf16_tensor(v), i64(slots), kc, vc)
+    torch.cuda.synchronize()
+    okc = np.full(nblocks * Hkv * 16 * D, W.BF16_NAN, np.uint16)
+    ovc = okc.copy()
+    oslots = np.where(slots < nblocks * 16, slots, -1)  # out of range: skipped
+    oracle.write_kv(okc, ovc, k, v, oslots)
+    assert np.array_equal(tensor_bits(kc).ravel(), okc)
+    assert np.array_equal(tensor_bits(vc).ravel(), ovc)
+
+
 @pytest.mark.parametrize("name", ["mixed-g4-d128", "mixed-g1-d64"])
 def test_gather_bit_exact(name):
     w = small(name, seed=3)

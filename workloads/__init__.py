@@ -362,6 +362,14 @@ def make_prefill_chunk() -> Workload:
                          [1920], 32, 8, 128, seed=3)
 
 
+def make_decode_part() -> Workload:
+    """The 128 decode requests of configuration 3 on their own (contexts
+    U[256, 8192], Llama-3-8B heads), for timing the decode part alone."""
+    L, Q = config_lengths(3)
+    return make_workload("llama3-8b-decodes-of-mixed-step-128seq", L[:-1], Q[:-1],
+                         32, 8, 128, seed=3)
+
+
 def make_config(k: int, shared: bool = True) -> Workload:
     """Synthetic configuration k in 1..5 (seeds 1000+k data, 2000+k lengths,
     3000+k tables)."""
