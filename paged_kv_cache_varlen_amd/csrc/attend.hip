@@ -38,6 +38,7 @@
 // same launch.
 #include <mutex>
 #include <type_traits>
+#include <utility>
 #include <vector>
 
 #include "pa_device.h"
@@ -792,6 +793,34 @@ __device__ __forceinline__ bf16x4 lds8(const uint16_t* p) {
   return *reinterpret_cast<const bf16x4*>(p);
 }
 
+// One LDS read of 2 x 8 bytes at addr + 512 O0 and addr + 512 O1 (bytes)
+// into one 16-byte operand.  Inline assembly, so the compiler neither pairs
+// the halves differently nor tracks the read: the caller waits for it
+// (wait_lds_operands) before any use.
+template <int O0, int O1>
+__device__ __forceinline__ bf16x8 lds_read2st64(uint32_t addr) {
+  static_assert(O0 >= 0 && O0 < 256 && O1 >= 0 && O1 < 256, "ds offset range");
+  bf16x8 r;
+  asm volatile("ds_read2st64_b64 %0, %1 offset0:%2 offset1:%3"
+               : "=v"(r)
+               : "v"(addr), "n"(O0), "n"(O1));
+  return r;
+}
+template <int SECOND, int... HC>
+__device__ __forceinline__ void read_v_regions(uint32_t addr, bf16x8* v,
+                                               std::integer_sequence<int, HC...>) {
+  ((v[HC] = lds_read2st64<HC, HC + SECOND>(addr)), ...);
+}
+// Wait for every outstanding LDS read of the wave, then hand the operands
+// read by lds_read2st64 on to the compiler (each tied to a real instruction,
+// so no use can be scheduled before the wait).
+template <int N>
+__device__ __forceinline__ void wait_lds_operands(bf16x8 (&v)[N]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v[0]));
+#pragma unroll
+  for (int i = 1; i < N; ++i) asm volatile("s_nop 0" : "+v"(v[i]));
+}
+
 // Growth of a column's maximum (exp2 domain) below which the running max is
 // kept: probabilities then reach at most 2^kRescaleSlack, far inside bf16
 // and fp32 range, and the accumulators are rescaled only when some column's
@@ -873,14 +902,9 @@ __device__ __forceinline__ void run_tile(const AttendParams& P,
       load16_lds(src, (uint32_t)(c * 1024 + lane * 16), dst + c * 512);
   };
 
-  // One pair of blocks.  MASKED: the pair holds keys past some column's
-  // position or past kv1 (the diagonal and the range end); otherwise the
-  // step is straight-line code apart from the rare rescale.
-  auto compute = [&](const uint16_t* st, int kp0, auto masked) {
-    constexpr bool MASKED = decltype(masked)::value;
-    // scores: each K operand read from LDS just before the MFMAs of all
-    // column tiles that use it (few operand registers live at a time)
-    f32x4 sa[CT], sb[CT];
+  // Scores of one pair of blocks (stage st): sa for the first block, sb
+  // for the second; each K operand feeds the MFMAs of every column tile.
+  auto scores = [&](const uint16_t* st, f32x4 (&sa)[CT], f32x4 (&sb)[CT]) {
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       sa[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -888,10 +912,6 @@ __device__ __forceinline__ void run_tile(const AttendParams& P,
     }
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
-      // keep the operand reads in step with their MFMAs (register budget).
-      // A real instruction: hazard bookkeeping counts an asm statement as
-      // one wait state.
-      if (c >= 2) asm volatile("s_nop 0" ::: "memory");
       const bf16x8 ka = lds16(st + c * 512 + lane * 8);
       const bf16x8 kb = lds16(st + 2 * TILE + c * 512 + lane * 8);
 #pragma unroll
@@ -900,6 +920,25 @@ __device__ __forceinline__ void run_tile(const AttendParams& P,
         sb[ct] = mfma32(kb, qop[ct][c], sb[ct]);
       }
     }
+  };
+
+  // The 2 KC PV operands of the pair in stage st, read in one go: operand
+  // hc holds, for dim (hc / KC) * D/2 + 16 (hc % KC) + lane % 16, keys
+  // 4g .. 4g+3 of the first block, then the same keys of the second (the
+  // rows the score MFMAs left in this lane).  Region hc of a V tile is 512
+  // bytes, and the second block's tile lies 2 TILE elements further.
+  auto read_v = [&](const uint16_t* st, bf16x8 (&vop)[2 * KC]) {
+    const uint32_t a = lds_addr(st + TILE) + (uint32_t)lane * 8;
+    read_v_regions<TILE / 128>(a, vop, std::make_integer_sequence<int, 2 * KC>{});
+  };
+
+  // Softmax and PV of one pair of blocks from its scores.  MASKED: the pair
+  // holds keys past some column's position or past kv1 (the diagonal and
+  // the range end); otherwise the step is straight-line code apart from
+  // the rare rescale.
+  auto softmax_pv = [&](int kp0, const f32x4 (&sa)[CT], const f32x4 (&sb)[CT],
+                        bf16x8 (&vop)[2 * KC], auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
     float x[CT][8];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
@@ -920,51 +959,38 @@ __device__ __forceinline__ void run_tile(const AttendParams& P,
         }
       }
     }
-    float mc[CT];
+    // Each lane checks its own 8 scores of a column against the column's
+    // threshold (c > 0, so max(s) * c exceeds it exactly when some lane's
+    // local max does); the column max across the four lanes of a column is
+    // formed only on the rare step where some column grew.
+    float lm[CT];
     bool grow = false;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       float m = x[ct][0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) m = fmaxf(m, x[ct][i]);
-      mc[ct] = column_max(m) * P.scale_log2;
-      grow = grow || mc[ct] > mref[ct] + kRescaleSlack;
+      lm[ct] = m;
+      grow = grow || m * P.scale_log2 > mref[ct] + kRescaleSlack;
     }
-    // probabilities and PV; written out on both sides of the (rare) rescale
-    // branch so that the accumulators meet only after the MFMAs
-    auto pv = [&]() {
-      bf16x8 pop[CT];
+    // probabilities against the current reference, recomputed below on the
+    // rare step that moves it; the common step is then one straight block
+    // from the scores to the PV MFMAs
+    bf16x8 pop[CT];
+    auto probs = [&]() {
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
           pop[ct][i] = (__bf16)__builtin_amdgcn_exp2f(
               __builtin_fmaf(x[ct][i], P.scale_log2, -msub[ct]));
-        lacc[ct] = mfma32(ones, pop[ct], lacc[ct]);
-      }
-#pragma unroll
-      for (int hc = 0; hc < 2 * KC; ++hc) {
-        if (hc >= 2) asm volatile("s_nop 0" ::: "memory");
-        // V operand of dims (hc / KC) * D/2 + 16 (hc % KC) ..: 4 keys of
-        // the first block, then the same keys of the second
-        const uint16_t* va = st + TILE + hc * 256 + lane * 4;
-        bf16x8 v = __builtin_shufflevector(lds8(va), lds8(va + 2 * TILE), 0, 1, 2, 3, 4, 5,
-                                           6, 7);
-        if (MASKED) {
-          // keys at or past kv1 may be unwritten pool slots: zero their V
-          // so a 0 weight cannot meet a NaN
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = kp0 + 4 * g + i;
-            if (key >= it.kv1) v[i] = (__bf16)0.0f;
-            if (key + kBlock >= it.kv1) v[i + 4] = (__bf16)0.0f;
-          }
-        }
-        const int n = (hc & 1) * KC + (hc >> 1);  // dim tile of region hc
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) acc[ct][n] = mfma32(v, pop[ct], acc[ct][n]);
       }
     };
+    probs();
+    // (pin the common-case probabilities here: the compiler would otherwise
+    // sink them past the branch)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) asm volatile("s_nop 0" ::"v"(pop[ct]));
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
       // (a side effect keeps this a branch: the compiler would otherwise run
       // the rescale on every step with alpha = 1)
@@ -973,7 +999,8 @@ __device__ __forceinline__ void run_tile(const AttendParams& P,
       // alpha is exactly 1 for the columns that keep theirs
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
-        const float mnew = mc[ct] > mref[ct] + kRescaleSlack ? mc[ct] : mref[ct];
+        const float mc = column_max(lm[ct]) * P.scale_log2;
+        const float mnew = mc > mref[ct] + kRescaleSlack ? mc : mref[ct];
         const float alpha =
             mnew == mref[ct] ? 1.0f : __builtin_amdgcn_exp2f(mref[ct] - mnew);
         mref[ct] = mnew;
@@ -982,31 +1009,98 @@ __device__ __forceinline__ void run_tile(const AttendParams& P,
 #pragma unroll
         for (int n = 0; n < NT; ++n) acc[ct][n] *= alpha;
       }
-      pv();
-    } else {
-      pv();
+      probs();
+    }
+    // PV (each accumulator has this one MFMA as its only use in the step,
+    // so it is updated in place)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) lacc[ct] = mfma32(ones, pop[ct], lacc[ct]);
+    wait_lds_operands(vop);
+#pragma unroll
+    for (int hc = 0; hc < 2 * KC; ++hc) {
+      bf16x8 v = vop[hc];
+      if (MASKED) {
+        // keys at or past kv1 may be unwritten pool slots: zero their V
+        // so a 0 weight cannot meet a NaN
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kp0 + 4 * g + i;
+          if (key >= it.kv1) v[i] = (__bf16)0.0f;
+          if (key + kBlock >= it.kv1) v[i + 4] = (__bf16)0.0f;
+        }
+      }
+      const int n = (hc & 1) * KC + (hc >> 1);  // dim tile of region hc
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) acc[ct][n] = mfma32(v, pop[ct], acc[ct][n]);
     }
   };
 
   // Pair pr lives in stage pr % NS.  Every wave issues the same number of
   // loads per stage (the prefetch is unconditional, clamped to the last
-  // pair), so after the wait at step pr at most the loads of the NS - 2
-  // later stages are still in flight and stage pr is complete; the barrier
-  // then makes every wave's tile visible and guarantees that stage
-  // (pr - 1) % NS, refilled next, has been read by all waves.
+  // pair).  Step pr computes the scores of pair pr + 1 and the softmax and
+  // PV of pair pr (whose scores the previous step left), so the matrix
+  // cores have the next pair's score MFMAs to run while the softmax of this
+  // one is on the vector ALUs.  Before step pr a wave waits until only the
+  // loads of pairs pr + 2 .. are in flight, so pair pr + 1 has landed; the
+  // barrier then makes every wave's tiles visible and guarantees that stage
+  // (pr - 1) % NS, refilled next, has been read by all waves (its K at step
+  // pr - 2, its V at step pr - 1).
+  //
+  // The pairs of a wave fall into three runs: pairs every key of which each
+  // of its tokens sees (below the diagonal and the range end), then pairs
+  // that need the mask, then pairs past its last token (the wave only keeps
+  // loading and meeting the others).  One loop per run keeps each loop body
+  // a single path, so the accumulators stay in place across iterations.
+  static_assert(NS >= 4, "the pipelined steps read two stages and refill a third");
+  const int kb = jb0 * kBlock;  // first key of pair 0
+  int nmask_end = 0;            // pairs with kp0 <= wlast
+  if (wlast >= kb) nmask_end = min(npairs, (wlast - kb) / (2 * kBlock) + 1);
+  int nfull = 0;  // pairs with kp0 + 31 <= posbase and kp0 + 32 <= kv1
+  {
+    const int lim = min(wt.posbase + 1, it.kv1) - kb;  // keys below both limits
+    if (lim >= 2 * kBlock) nfull = min(nmask_end, lim / (2 * kBlock));
+  }
+  auto stage = [&](int pr) { return ring + (pr % NS) * pair_stage_elems<D>(); };
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) issue(s, min(s, npairs - 1));
-  for (int pr = 0; pr < npairs; ++pr) {
-    wait_loads_and_barrier<LPS * (NS - 2)>();
+  f32x4 sa[CT], sb[CT];
+  wait_loads_and_barrier<LPS * (NS - 2)>();  // pair 0 has landed
+  if (nmask_end > 0) scores(stage(0), sa, sb);
+  auto step = [&](int pr) {
+    wait_loads_and_barrier<LPS * (NS - 3)>();
     issue((pr + NS - 1) % NS, min(pr + NS - 1, npairs - 1));
-    const int kp0 = (jb0 + 2 * pr) * kBlock;
-    const uint16_t* st = ring + (pr % NS) * pair_stage_elems<D>();
-    if (kp0 > wlast) continue;  // past every key this wave's tokens see
-    if (kp0 + 2 * kBlock - 1 <= wt.posbase && kp0 + 2 * kBlock <= it.kv1)
-      compute(st, kp0, std::false_type{});
-    else
-      compute(st, kp0, std::true_type{});
+  };
+  // (the scores of pair nmask_end, computed by the last step of a wave's
+  // second run, are not used: that stage holds loaded data or a clamped
+  // copy, so the read stays inside the ring)
+  int pr = 0;
+  for (; pr < nfull; ++pr) {
+    bf16x8 vop[2 * KC];
+    read_v(stage(pr), vop);  // complete since the previous step's barrier
+    step(pr);
+    f32x4 na[CT], nb[CT];
+    scores(stage(pr + 1), na, nb);
+    softmax_pv((jb0 + 2 * pr) * kBlock, sa, sb, vop, std::false_type{});
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      sa[ct] = na[ct];
+      sb[ct] = nb[ct];
+    }
   }
+  for (; pr < nmask_end; ++pr) {
+    bf16x8 vop[2 * KC];
+    read_v(stage(pr), vop);  // complete since the previous step's barrier
+    step(pr);
+    f32x4 na[CT], nb[CT];
+    scores(stage(pr + 1), na, nb);
+    softmax_pv((jb0 + 2 * pr) * kBlock, sa, sb, vop, std::true_type{});
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      sa[ct] = na[ct];
+      sb[ct] = nb[ct];
+    }
+  }
+  for (; pr < npairs; ++pr) step(pr);
   // the ring is free again once every load has landed and every wave is done
   wait_loads_and_barrier<0>();
   if (active) {
