@@ -155,7 +155,8 @@ size_t pa_attend_workspace_size(int32_t num_seqs, int64_t num_q_tokens,
  *   q                device bf16 [num_q_tokens][num_q_heads][head_dim],
  *                    rows of request b at query_start_loc[b] ..
  *                    query_start_loc[b+1]-1
- *   k_cache, v_cache device bf16 pools (layout above), num_blocks blocks
+ *   k_cache, v_cache device bf16 pools (layout above), num_blocks blocks;
+ *                    num_blocks * num_kv_heads < 2^32 (PA_ERR_SHAPE otherwise)
  *   block_tables     device int32 [num_seqs][max_blocks_per_seq]; entry j of
  *                    row b is the physical block of logical tokens
  *                    16j .. 16j+15 of request b; entries past ceil(L_b/16) are

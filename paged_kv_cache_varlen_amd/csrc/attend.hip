@@ -761,22 +761,42 @@ __device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
   return (const uint16_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Global-to-LDS load: lane i reads 16 bytes at base + voff (bytes, per
-// lane) and writes them to LDS at l + 16 i; base and l are the same for the
-// whole wave.  Written as inline assembly so that the compiler does not
-// track it: it would otherwise wait for every such load before any LDS
-// read, draining the pipeline; the ring protocol below orders them itself.
-// The load reads M0 (its LDS base) and an SGPR pair: five wait states after
-// they are written cover the hazard rules for both.  M0 is restored.
-__device__ __forceinline__ void load16_lds(const uint16_t* base, uint32_t voff,
-                                           uint16_t* l) {
+// Global-to-LDS copy of N KiB: load c (c < N) has lane i read 16 bytes at
+// base + voff + 1024 c (voff = 16 i) and write them to LDS at
+// l + 1024 c + 16 i (bytes); base and l are the same for the whole wave.
+// The instruction offset moves the global and the LDS address alike, so
+// one M0 value serves all N loads.  Written as inline assembly so that the
+// compiler does not track it: it would otherwise wait for every such load
+// before any LDS read, draining the pipeline; the ring protocol below
+// orders them itself.  The loads read M0 (their LDS base) and an SGPR pair:
+// five wait states after they are written cover the hazard rules for both.
+// M0 is restored.
+template <int N>
+__device__ __forceinline__ void load_lds_kib(const uint16_t* base, uint32_t voff,
+                                             uint32_t l) {
+  static_assert(N == 2 || N == 4, "one 1 KiB load per 8 dims x 16 tokens");
   uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 4\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(uniform_ptr(base)), "s"(lds_addr(l))
-      : "memory");
+  if constexpr (N == 2) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 4\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "global_load_lds_dwordx4 %1, %2 offset:1024\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(uniform_ptr(base)), "s"(l)
+        : "memory");
+  } else {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 4\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "global_load_lds_dwordx4 %1, %2 offset:1024\n\t"
+        "global_load_lds_dwordx4 %1, %2 offset:2048\n\t"
+        "global_load_lds_dwordx4 %1, %2 offset:3072\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(uniform_ptr(base)), "s"(l)
+        : "memory");
+  }
 }
 // Wait until at most N of this wave's vector memory loads are outstanding,
 // then meet the other waves of the workgroup.  (A compiler-level memory
@@ -884,22 +904,24 @@ __device__ __forceinline__ void run_tile(const AttendParams& P,
   auto load_ids = [&](int pr0) {
     const int jr = min(2 * pr0 + lane, nblk - 1);  // clamped
     const int id = btrow[jr];
-    return id < 0 ? 0 : (id >= P.num_blocks ? (int)(P.num_blocks - 1) : id);
+    const int idc = id < 0 ? 0 : (id >= P.num_blocks ? (int)(P.num_blocks - 1) : id);
+    return (int)((uint32_t)idc * (uint32_t)P.Hkv + (uint32_t)kvh);
   };
   int idbase = 0;
   int idv = load_ids(0);
 
+  // LDS byte address of this wave's tile in stage 0 (stage s: + s * stage bytes)
+  const uint32_t ring_lds = lds_addr(ring) + (uint32_t)(wslot * TILE * 2);
   auto issue = [&](int slot, int pr) {
     if (pr >= idbase + 32) {  // pairs are issued in order
       idbase += 32;
       idv = load_ids(idbase);
     }
-    const int id = __builtin_amdgcn_readlane(idv, 2 * (pr - idbase) + half);
-    const uint16_t* src = pool + ((int64_t)id * P.Hkv + kvh) * TILE;
-    uint16_t* dst = ring + slot * pair_stage_elems<D>() + wslot * TILE;
-#pragma unroll
-    for (int c = 0; c < KC; ++c)
-      load16_lds(src, (uint32_t)(c * 1024 + lane * 16), dst + c * 512);
+    // tile index id * Hkv + kvh (below 2^32 for any pool the device holds)
+    const uint32_t tix = (uint32_t)__builtin_amdgcn_readlane(idv, 2 * (pr - idbase) + half);
+    const uint16_t* src = pool + (uint64_t)tix * TILE;
+    load_lds_kib<KC>(src, (uint32_t)lane * 16,
+                     ring_lds + (uint32_t)(slot * pair_stage_elems<D>() * 2));
   };
 
   // Scores of one pair of blocks (stage st): sa for the first block, sb
@@ -922,13 +944,14 @@ __device__ __forceinline__ void run_tile(const AttendParams& P,
     }
   };
 
-  // The 2 KC PV operands of the pair in stage st, read in one go: operand
+  // The 2 KC PV operands of pair pr (in stage pr % NS), read in one go: operand
   // hc holds, for dim (hc / KC) * D/2 + 16 (hc % KC) + lane % 16, keys
   // 4g .. 4g+3 of the first block, then the same keys of the second (the
   // rows the score MFMAs left in this lane).  Region hc of a V tile is 512
   // bytes, and the second block's tile lies 2 TILE elements further.
-  auto read_v = [&](const uint16_t* st, bf16x8 (&vop)[2 * KC]) {
-    const uint32_t a = lds_addr(st + TILE) + (uint32_t)lane * 8;
+  const uint32_t vbase = lds_addr(ring) + (uint32_t)(TILE * 2 + lane * 8);
+  auto read_v = [&](int pr, bf16x8 (&vop)[2 * KC]) {
+    const uint32_t a = vbase + (uint32_t)((pr % NS) * pair_stage_elems<D>() * 2);
     read_v_regions<TILE / 128>(a, vop, std::make_integer_sequence<int, 2 * KC>{});
   };
 
@@ -1076,7 +1099,7 @@ __device__ __forceinline__ void run_tile(const AttendParams& P,
   int pr = 0;
   for (; pr < nfull; ++pr) {
     bf16x8 vop[2 * KC];
-    read_v(stage(pr), vop);  // complete since the previous step's barrier
+    read_v(pr, vop);  // complete since the previous step's barrier
     step(pr);
     f32x4 na[CT], nb[CT];
     scores(stage(pr + 1), na, nb);
@@ -1089,7 +1112,7 @@ __device__ __forceinline__ void run_tile(const AttendParams& P,
   }
   for (; pr < nmask_end; ++pr) {
     bf16x8 vop[2 * KC];
-    read_v(stage(pr), vop);  // complete since the previous step's barrier
+    read_v(pr, vop);  // complete since the previous step's barrier
     step(pr);
     f32x4 na[CT], nb[CT];
     scores(stage(pr + 1), na, nb);

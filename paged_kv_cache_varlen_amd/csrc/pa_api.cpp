@@ -161,6 +161,8 @@ pa_status prepare_attend(const void* q, const void* k_cache,
     return fail(PA_ERR_NULL, "pa_attend: NULL pointer");
   if (max_blocks_per_seq == 0 || (need_tensors && num_blocks == 0))
     return fail(PA_ERR_SHAPE, "pa_attend: empty pool or block table");
+  if (num_blocks > (int64_t)(UINT32_MAX / (uint32_t)num_kv_heads))
+    return fail(PA_ERR_SHAPE, "pa_attend: num_blocks * num_kv_heads must fit in 32 bits");
   if (need_tensors && !(scale > 0.0f && scale <= FLT_MAX))
     return fail(PA_ERR_SHAPE, "pa_attend: scale must be finite and > 0");
   if (need_tensors &&

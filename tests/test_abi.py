@@ -82,6 +82,7 @@ def attend_args(**over):
     (dict(scale=-0.125), _lib.PA_ERR_SHAPE),
     (dict(scale=float("nan")), _lib.PA_ERR_SHAPE),
     (dict(scale=float("inf")), _lib.PA_ERR_SHAPE),
+    (dict(nb=(1 << 31), Hkv=2), _lib.PA_ERR_SHAPE),  # tiles past 2^32
 ])
 def test_attend_rejects_bad_arguments(lib, over, status):
     assert lib.pa_attend(*attend_args(**over)) == status
