@@ -1274,10 +1274,18 @@ void attend_mixed_kernel(AttendParams P) {
 // merge
 // ---------------------------------------------------------------------------
 
-// One wave per (split tile, kv head).  Lanes cover (column, 8 dims): a wave
-// merges 64 / (D/8) columns at a time.  Each column's splits are combined by
-// an online log-sum-exp in split order (a fixed order: the result does not
-// depend on timing), with the loads of 8 splits in flight per step.
+// W waves per (split tile, kv head), W = the passes one token's G columns
+// take (at most 4): the tile's columns of that kv head are dealt to them
+// round-robin, 64 / (D/8) at a time (lanes cover (column, 8 dims)), so a
+// decode request's query heads merge in parallel.  Each column's splits are
+// combined by an online log-sum-exp in split order (a fixed order: the
+// result does not depend on timing), with the loads of 8 splits in flight
+// per step.
+__host__ __device__ inline uint32_t merge_waves_per_head(int G, int D) {
+  const int cpw = 64 / (D / 8);
+  const int w = (G + cpw - 1) / cpw;
+  return (uint32_t)(w < 1 ? 1 : (w > 4 ? 4 : w));
+}
 template <int D>
 __global__ __launch_bounds__(kAttendThreads) void merge_kernel(AttendParams P) {
   constexpr int LPC = D / 8;      // lanes per column
@@ -1289,13 +1297,16 @@ __global__ __launch_bounds__(kAttendThreads) void merge_kernel(AttendParams P) {
   if (P.hdr->signature != plan_signature(P)) return;
   uint32_t ntiles = P.hdr->num_split_tiles;
   if ((int64_t)ntiles > P.max_items) ntiles = 0;
-  const uint32_t nunits = ntiles * (uint32_t)P.Hkv;
+  const uint32_t W = merge_waves_per_head(G, D);
+  const uint32_t per_tile = (uint32_t)P.Hkv * W;
+  const uint32_t nunits = ntiles * per_tile;
   const int cl = lane / LPC;          // column within the pass
   const int d0 = (lane % LPC) * 8;    // first of the lane's 8 dims
   for (uint32_t u = blockIdx.x * (kAttendThreads / 64) + (threadIdx.x >> 6);
        u < nunits; u += nwaves) {
-    const int4 tile = P.merge_list[u / P.Hkv];  // tok0, ntok, nsplit, pbase
-    const int kvh = (int)(u % P.Hkv);
+    const int4 tile = P.merge_list[u / per_tile];  // tok0, ntok, nsplit, pbase
+    const int kvh = (int)((u % per_tile) / W);
+    const int pass0 = (int)(u % W);
     // same rule as for work items: never follow an entry out of bounds
     if (tile.x < 0 || tile.y < 1 || tile.x + tile.y > P.num_q_tokens ||
         tile.z < 2 || tile.w < 0 ||
@@ -1303,7 +1314,7 @@ __global__ __launch_bounds__(kAttendThreads) void merge_kernel(AttendParams P) {
       continue;
     const int ncols = tile.y * G;
     const int nsplit = tile.z;
-    for (int c0 = 0; c0 < ncols; c0 += CPW) {
+    for (int c0 = pass0 * CPW; c0 < ncols; c0 += (int)W * CPW) {
       const int c = c0 + cl;
       if (c >= ncols) continue;
       const int tk = c / G;
@@ -1443,9 +1454,10 @@ hipError_t launch_planned(const AttendArgs& a, hipStream_t stream) {
 hipError_t launch_merge(const AttendArgs& a, hipStream_t stream) {
   if (a.num_q_tokens == 0 || a.num_seqs == 0) return hipSuccess;
   const AttendParams P = make_params(a);
-  // at most one wave per (split tile, kv head), never more than the resident
+  // at most W waves per (split tile, kv head), never more than the resident
   // waves of the chip
-  int64_t mwaves = a.ws.max_items * a.num_kv_heads;
+  int64_t mwaves = a.ws.max_items * a.num_kv_heads *
+                   merge_waves_per_head(a.num_q_heads / a.num_kv_heads, a.head_dim);
   const int64_t cap = (int64_t)a.num_cus * 8 * 4;
   if (mwaves > cap) mwaves = cap;
   const int64_t mwgs = (mwaves + (kAttendThreads / 64) - 1) / (kAttendThreads / 64);
