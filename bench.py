@@ -14,7 +14,8 @@ Prints one JSON line:
            heads, head_dim 128, 16-token blocks) = valid-token K+V bytes per
            step / step time;
   roofline the attention kernel against the 8 TB/s HBM peak, its duration
-           from HIP events on the launch stream;
+           from HIP events on the launch stream; also against this box's
+           measured streaming-read ceiling (measured_ceiling);
   mixed_step  mixed chunked-prefill step (1920-token chunk on 1536 cached
            tokens + 128 decodes): tokens/s per layer;
   prefill_tile  that step's prefill chunk alone: attention TFLOP/s (visible
@@ -54,6 +55,8 @@ def parse():
                          "prefill chunk alone")
     ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming-read ceiling probe")
     ap.add_argument("--min-working-set-gib", type=float, default=2.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run 5 plain 1 GiB device-to-device copies (the "
@@ -176,10 +179,10 @@ class Runner:
         return (t1 - t0) * 1e3 / steps, attend_ms
 
 
-def cpu_baseline(w, min_s=10.0, max_s=30.0):
+def cpu_baseline(w, min_s=10.0, max_s=30.0, min_s1=3.0, max_s1=8.0):
     """The oracle on the same workload, all heads of every sequence, in whole
-    passes over the batch until at least min_s of oracle time (at most max_s,
-    stopping between sequences), scaled to KV GB/s."""
+    sequences until at least min_s of oracle time (at most max_s), scaled to
+    KV GB/s; then the same with one thread on a shorter sample."""
     import oracle
     kc = np.zeros(w.pool_elems(), np.uint16)
     vc = np.zeros(w.pool_elems(), np.uint16)
@@ -192,20 +195,26 @@ def cpu_baseline(w, min_s=10.0, max_s=30.0):
         t0, t1 = int(w.query_start_loc[b]), int(w.query_start_loc[b + 1])
         rows.append(np.array([(t, h) for t in range(t0, t1)
                               for h in range(w.num_q_heads)], np.int64))
-    done_seqs, kv_bytes, spent = 0, 0, 0.0
-    while spent < min_s:
-        for b in range(w.num_seqs):
-            s = time.perf_counter()
-            oracle.attend_rows(w.q, kc, vc, w.block_tables, w.seq_lens,
-                               w.query_start_loc, w.num_kv_heads, w.scale,
-                               rows[b], nthreads=threads)
-            spent += time.perf_counter() - s
-            done_seqs += 1
-            kv_bytes += int(w.seq_lens[b]) * per_tok
-            if spent >= max_s:
+
+    def sample(nthreads, lo, hi):
+        done_seqs, kv_bytes, spent = 0, 0, 0.0
+        while spent < lo:
+            for b in range(w.num_seqs):
+                s = time.perf_counter()
+                oracle.attend_rows(w.q, kc, vc, w.block_tables, w.seq_lens,
+                                   w.query_start_loc, w.num_kv_heads, w.scale,
+                                   rows[b], nthreads=nthreads)
+                spent += time.perf_counter() - s
+                done_seqs += 1
+                kv_bytes += int(w.seq_lens[b]) * per_tok
+                if spent >= hi:
+                    break
+            if spent >= hi:
                 break
-        if spent >= max_s:
-            break
+        return done_seqs, kv_bytes, spent
+
+    done_seqs, kv_bytes, spent = sample(threads, min_s, max_s)
+    seqs1, bytes1, spent1 = sample(1, min_s1, max_s1)
     cpu = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -215,14 +224,55 @@ def cpu_baseline(w, min_s=10.0, max_s=30.0):
                     break
     except OSError:
         pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
     return {"value": round(kv_bytes / spent / 1e9, 4), "unit": "GB/s",
             "cores": threads, "kind": "oracle", "cpu": cpu,
-            "os_cpu_count": os.cpu_count(),
+            "os_cpu_count": os.cpu_count(), "affinity": affinity,
+            "value_1_thread": round(bytes1 / spent1 / 1e9, 4),
             "sample": "%d sequence attentions (%.1f passes over the %d sequences "
                       "of the headline workload), all %d query heads, fp64 C "
-                      "oracle with OpenMP, %.1f s"
+                      "oracle with OpenMP, %.1f s; one thread: %d sequences, %.1f s"
                       % (done_seqs, done_seqs / w.num_seqs, w.num_seqs,
-                         w.num_q_heads, spent)}
+                         w.num_q_heads, spent, seqs1, spent1)}
+
+
+def read_ceiling(torch, gib=4):
+    """Measured streaming-read ceiling of this box: the best of a few grid
+    sizes of the probe kernel (libpa_probe.so) reading a 4 GiB buffer once
+    with 16-byte non-temporal loads; GB/s."""
+    import ctypes
+    path = os.path.join(ROOT, "paged_kv_cache_varlen_amd", "libpa_probe.so")
+    lib = ctypes.CDLL(path)
+    lib.pa_probe_stream_read.restype = ctypes.c_int
+    lib.pa_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                         ctypes.c_int, ctypes.c_void_p]
+    nbytes = gib << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    best = 0.0
+    for per_cu in (8, 16, 32):
+        def launch():
+            rc = lib.pa_probe_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(),
+                                          cus * per_cu, stream.cuda_stream)
+            assert rc == 0, rc
+        for _ in range(2):
+            launch()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(5):
+            launch()
+        b.record(stream)
+        torch.cuda.synchronize()
+        best = max(best, 5 * nbytes / (a.elapsed_time(b) * 1e-3) / 1e9)
+    del buf, sink
+    torch.cuda.empty_cache()
+    return best
 
 
 def main():
@@ -270,6 +320,12 @@ def main():
             "attend_ms": round(attend_ms, 5),
             "algorithmic_bytes": alg["attend_bytes"]},
     }
+    if args.config != "p" and not args.no_ceiling:
+        ceil = read_ceiling(torch)
+        line["roofline"]["measured_ceiling"] = {
+            "gbs": round(ceil, 1), "frac": round(achieved / ceil, 4),
+            "probe": "one pass over 4 GiB with 16-byte non-temporal loads, best of "
+                     "8/16/32 workgroups per CU (libpa_probe.so)"}
     if args.config == "p":
         # the prefill chunk alone is a dense contraction: priced against MFMA
         tflops = alg["flops"] / (attend_ms * 1e-3) / 1e12

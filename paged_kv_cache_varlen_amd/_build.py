@@ -14,6 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpa.so")
+PROBE_LIB = os.path.join(PKG, "libpa_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -45,8 +46,15 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
     os.replace(tmp, LIB)
+    # the streaming-read probe (bench.py's measured ceiling): its own library
+    probe_tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC] + COMMON + ["-shared", os.path.join(CSRC, "read_probe.hip"), "-o", probe_tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for read_probe.hip:\n%s\n%s" % (" ".join(cmd), r.stderr))
+    os.replace(probe_tmp, PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 
