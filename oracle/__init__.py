@@ -72,6 +72,22 @@ def _load():
         lib.oracle_attend_dense.restype = None
         lib.oracle_attend_dense.argtypes = [P, P, P, P, P, I, I, I, I,
                                             ctypes.c_float, I, P, P]
+        lib.oracle_e4m3_decode.restype = ctypes.c_double
+        lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+        lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        lib.oracle_k8_index.restype = ctypes.c_size_t
+        lib.oracle_k8_index.argtypes = [I] * 7
+        lib.oracle_v8_index.restype = ctypes.c_size_t
+        lib.oracle_v8_index.argtypes = [I] * 7
+        lib.oracle_write_kv_fp8.restype = None
+        lib.oracle_write_kv_fp8.argtypes = [P, P, P, P, P, I, I, I, I,
+                                            ctypes.c_float, ctypes.c_float]
+        lib.oracle_attend_fp8.restype = None
+        lib.oracle_attend_fp8.argtypes = [P, P, P, ctypes.c_float, ctypes.c_float,
+                                          P, I, P, P, I, I, I, I, I,
+                                          ctypes.c_float, I, P, I, P, P,
+                                          ctypes.c_int]
         lib.oracle_abi_version.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -201,4 +217,85 @@ def attend_dense(q, k_dense, v_dense, seq_lens, query_start_loc, scale):
     _load().oracle_attend_dense(_p(q), _p(kd), _p(vd), _p(sl), _p(qsl), B, Hq,
                                 Hkv, D, float(scale), maxL, _p(scratch),
                                 _p(out))
+    return out
+
+
+# ---- 8-bit (E4M3) KV cache ------------------------------------------------------
+
+def e4m3_decode(codes) -> np.ndarray:
+    """fp64 values of E4M3 codes (uint8 array)."""
+    lib = _load()
+    c = np.asarray(codes, np.uint8)
+    return np.array([lib.oracle_e4m3_decode(int(b)) for b in c.ravel()],
+                    np.float64).reshape(c.shape)
+
+
+def e4m3_encode(values) -> np.ndarray:
+    """E4M3 codes (uint8) of fp32 values: nearest, ties to even mantissa;
+    |v| >= 448 saturates; NaN -> 0x7f."""
+    lib = _load()
+    v = np.asarray(values, np.float32)
+    return np.array([lib.oracle_e4m3_encode(float(x)) for x in v.ravel()],
+                    np.uint8).reshape(v.shape)
+
+
+def k8_index(n, g, t, d, num_kv_heads, head_dim, block_size=BLOCK_SIZE) -> int:
+    """Byte offset of K(block n, kv head g, slot t, dim d) in an 8-bit pool."""
+    return int(_load().oracle_k8_index(n, g, t, d, num_kv_heads, block_size,
+                                       head_dim))
+
+
+def v8_index(n, g, t, d, num_kv_heads, head_dim, block_size=BLOCK_SIZE) -> int:
+    """Byte offset of V(block n, kv head g, slot t, dim d) in an 8-bit pool."""
+    return int(_load().oracle_v8_index(n, g, t, d, num_kv_heads, block_size,
+                                       head_dim))
+
+
+def write_kv_fp8(k_cache: np.ndarray, v_cache: np.ndarray, k: np.ndarray,
+                 v: np.ndarray, slot_mapping: np.ndarray, k_scale: float,
+                 v_scale: float) -> None:
+    """In-place 8-bit scatter: code of fp32(x) / scale for every element of
+    k, v ([T][Hkv][D] uint16 bf16 bits) at its slot; flat uint8 pools of
+    num_blocks*Hkv*16*D bytes."""
+    assert k_cache.dtype == np.uint8 and k_cache.flags.c_contiguous
+    assert v_cache.dtype == np.uint8 and v_cache.flags.c_contiguous
+    T, Hkv, D = k.shape
+    k = _c(k, np.uint16)
+    v = _c(v, np.uint16)
+    sm = _c(slot_mapping, np.int64)
+    assert sm.shape == (T,)
+    _load().oracle_write_kv_fp8(_p(k_cache), _p(v_cache), _p(k), _p(v), _p(sm),
+                                T, Hkv, BLOCK_SIZE, D, float(k_scale),
+                                float(v_scale))
+
+
+def attend_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tables, seq_lens,
+               query_start_loc, num_kv_heads, scale, rows=None,
+               nthreads=None) -> np.ndarray:
+    """Paged varlen causal attention over 8-bit pools (values decode(code) *
+    scale, fp64): out [T][Hq][D], or [len(rows)][D] for selected (token,
+    head) rows."""
+    q = _c(q, np.uint16)
+    T, Hq, D = q.shape
+    bt = _c(block_tables, np.int32)
+    sl = _c(seq_lens, np.int32)
+    qsl = _c(query_start_loc, np.int32)
+    B = sl.shape[0]
+    assert qsl.shape == (B + 1,) and int(qsl[-1]) == T
+    assert k_cache.dtype == np.uint8 and v_cache.dtype == np.uint8
+    nthreads = nthreads or default_threads()
+    maxL = max(1, int(sl.max()) if B else 1)
+    scratch = np.empty(nthreads * maxL, np.float64)
+    if rows is None:
+        out = np.zeros((T, Hq, D), np.float64)
+        rp, nrows = None, T * Hq
+    else:
+        rows = _c(rows, np.int64).reshape(-1, 2)
+        out = np.zeros((rows.shape[0], D), np.float64)
+        rp, nrows = _p(rows), rows.shape[0]
+    _load().oracle_attend_fp8(_p(q), _p(k_cache), _p(v_cache), float(k_scale),
+                              float(v_scale), _p(bt), bt.shape[1], _p(sl),
+                              _p(qsl), B, Hq, num_kv_heads, BLOCK_SIZE, D,
+                              float(scale), maxL, rp, nrows, _p(scratch),
+                              _p(out), int(nthreads))
     return out

@@ -81,6 +81,88 @@ static size_t v_index(int64_t n, int64_t g, int64_t t, int64_t d, int64_t Hkv,
   return tile + (size_t)((((c * 2 + dh) * (bs / 4) + tg) * 16 + r) * 4 + tl);
 }
 
+/* ---- 8-bit KV cache: E4M3 codes and their tile layout ------------------- */
+
+/* The pages name fp8 (E4M3) KV-cache quantisation with one fp32 scale per
+ * tensor ("Quantization & compute kernels", the KV-cache quantisation axis,
+ * in "vLLM: An Exhaustive Technical Study for Kernel Engineers").  The code
+ * is OCP E4M3 ("E4M3FN"): sign bit, 4 exponent bits with bias 7, 3 mantissa
+ * bits; no infinities; S.1111.111 is NaN; normal values (1 + m/8) * 2^(e-7)
+ * for e = 1..15 (largest finite 1.75 * 2^8 = 448); subnormals (m/8) * 2^-6. */
+double oracle_e4m3_decode(uint8_t b) {
+  int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m / 8.0, -6);
+  else
+    v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+/* Encode one fp32 value: NaN -> 0x7f; magnitudes at or above 448 (and
+ * infinities) saturate to 448; everything else rounds to the nearest code,
+ * ties to the even mantissa.  Exact arithmetic in fp64 (the value is an
+ * fp32, so a / 2^k and its rounding are exact). */
+uint8_t oracle_e4m3_encode(float v) {
+  if (isnan(v)) return 0x7f;
+  uint8_t s = signbit(v) ? 0x80 : 0x00;
+  double a = fabs((double)v);
+  if (a >= 448.0) return s | 0x7e;
+  if (a < ldexp(1.0, -6)) {
+    /* subnormal range: multiples of 2^-9; 8 * 2^-9 is the smallest normal */
+    double m = rint(a / ldexp(1.0, -9)); /* round to nearest, ties to even */
+    return s | (uint8_t)m;               /* m == 8 is code 0x08 = 2^-6 */
+  }
+  int k;
+  frexp(a, &k); /* a = f * 2^k, f in [0.5, 1) */
+  int e = k - 1; /* a in [2^e, 2^(e+1)) */
+  double m = rint((a / ldexp(1.0, e) - 1.0) * 8.0);
+  if (m == 8.0) {
+    m = 0.0;
+    e += 1;
+  }
+  /* a < 448 keeps e + 7 <= 15 and excludes the NaN code */
+  return s | (uint8_t)(((e + 7) << 3) | (int)m);
+}
+
+/* Byte offset of K (block n, kv head g, slot t, dim d) in an 8-bit pool.
+ * Tile (n, g) starts at (n*Hkv + g) * bs * D.  With d = 32c + 8q + j
+ * (q < 4, j < 8) and c = 2p + h: 16-byte units [p][q][t], each holding the
+ * 8 dims of chunk c = 2p and then the 8 dims of chunk 2p + 1. */
+static size_t k8_index(int64_t n, int64_t g, int64_t t, int64_t d, int64_t Hkv,
+                       int64_t bs, int64_t D) {
+  size_t tile = (size_t)((n * Hkv + g) * bs * D);
+  int64_t c = d / 32, q = (d % 32) / 8, j = d % 8;
+  int64_t p = c / 2, h = c % 2;
+  return tile + (size_t)(((p * 4 + q) * bs + t) * 16 + h * 8 + j);
+}
+
+/* Byte offset of V (block n, kv head g, slot t, dim d) in an 8-bit pool.
+ * With H = D/2, d = dh*H + 16c + r (dh < 2, r < 16), c = 2p + cc and
+ * t = 4*tg + tl: 16-byte units [p][tg][r], each holding 4-token runs for
+ * (cc, dh) = (0,0), (0,1), (1,0), (1,1). */
+static size_t v8_index(int64_t n, int64_t g, int64_t t, int64_t d, int64_t Hkv,
+                       int64_t bs, int64_t D) {
+  size_t tile = (size_t)((n * Hkv + g) * bs * D);
+  int64_t H = D / 2;
+  int64_t dh = d / H, c = (d % H) / 16, r = d % 16;
+  int64_t p = c / 2, cc = c % 2;
+  int64_t tg = t / 4, tl = t % 4;
+  return tile +
+         (size_t)(((p * (bs / 4) + tg) * 16 + r) * 16 + (cc * 2 + dh) * 4 + tl);
+}
+
+size_t oracle_k8_index(int64_t n, int64_t g, int64_t t, int64_t d, int64_t Hkv,
+                       int64_t bs, int64_t D) {
+  return k8_index(n, g, t, d, Hkv, bs, D);
+}
+
+size_t oracle_v8_index(int64_t n, int64_t g, int64_t t, int64_t d, int64_t Hkv,
+                       int64_t bs, int64_t D) {
+  return v8_index(n, g, t, d, Hkv, bs, D);
+}
+
 size_t oracle_k_index(int64_t n, int64_t g, int64_t t, int64_t d, int64_t Hkv,
                       int64_t bs, int64_t D) {
   return k_index(n, g, t, d, Hkv, bs, D);
@@ -108,6 +190,31 @@ void oracle_write_kv(uint16_t *k_cache, uint16_t *v_cache, const uint16_t *k,
         size_t src = (size_t)((t * Hkv + g) * D + d);
         k_cache[k_index(n, g, off, d, Hkv, bs, D)] = k[src];
         v_cache[v_index(n, g, off, d, Hkv, bs, D)] = v[src];
+      }
+    }
+  }
+}
+
+/* 8-bit scatter: the same slots as oracle_write_kv; each element x (bf16,
+ * widened exactly to fp32) is stored as the E4M3 code of the fp32 quotient
+ * x / scale (IEEE division, round to nearest). */
+void oracle_write_kv_fp8(uint8_t *k_cache, uint8_t *v_cache, const uint16_t *k,
+                         const uint16_t *v, const int64_t *slot_mapping,
+                         int64_t num_tokens, int64_t Hkv, int64_t bs, int64_t D,
+                         float k_scale, float v_scale) {
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    int64_t s = slot_mapping[t];
+    if (s < 0) continue;
+    int64_t n = s / bs, off = s % bs;
+    for (int64_t g = 0; g < Hkv; ++g) {
+      for (int64_t d = 0; d < D; ++d) {
+        size_t src = (size_t)((t * Hkv + g) * D + d);
+        float kx = (float)bf16_to_double(k[src]);
+        float vx = (float)bf16_to_double(v[src]);
+        float kq = kx / k_scale;
+        float vq = vx / v_scale;
+        k_cache[k8_index(n, g, off, d, Hkv, bs, D)] = oracle_e4m3_encode(kq);
+        v_cache[v8_index(n, g, off, d, Hkv, bs, D)] = oracle_e4m3_encode(vq);
       }
     }
   }
@@ -158,14 +265,22 @@ static void softmax_weighted_sum(const double *s, int64_t p, v_fetch_fn v_at,
   for (int64_t d = 0; d < D; ++d) out[d] /= denom;
 }
 
+/* The pools one attention reads: bf16 (k_cache, v_cache) or 8-bit codes
+ * (k8, v8) whose values are decode(code) * scale, in fp64. */
 typedef struct {
   const uint16_t *k_cache, *v_cache;
+  const uint8_t *k8, *v8;
+  double k_scale, v_scale;
   const int32_t *bt_row;
   int64_t g, Hkv, bs, D;
 } paged_ctx;
 
 static double paged_k(const paged_ctx *c, int64_t j, int64_t d) {
   int64_t n = c->bt_row[j / c->bs];
+  if (c->k8)
+    return oracle_e4m3_decode(
+               c->k8[k8_index(n, c->g, j % c->bs, d, c->Hkv, c->bs, c->D)]) *
+           c->k_scale;
   return bf16_to_double(
       c->k_cache[k_index(n, c->g, j % c->bs, d, c->Hkv, c->bs, c->D)]);
 }
@@ -173,23 +288,29 @@ static double paged_k(const paged_ctx *c, int64_t j, int64_t d) {
 static double paged_v(const void *ctx, int64_t j, int64_t d) {
   const paged_ctx *c = (const paged_ctx *)ctx;
   int64_t n = c->bt_row[j / c->bs];
+  if (c->v8)
+    return oracle_e4m3_decode(
+               c->v8[v8_index(n, c->g, j % c->bs, d, c->Hkv, c->bs, c->D)]) *
+           c->v_scale;
   return bf16_to_double(
       c->v_cache[v_index(n, c->g, j % c->bs, d, c->Hkv, c->bs, c->D)]);
 }
 
-/* One output row: query token t (global index) of sequence b, query head h. */
-static void paged_row(const uint16_t *q, const uint16_t *k_cache,
-                      const uint16_t *v_cache, const int32_t *block_tables,
-                      int64_t bt_stride, const int32_t *seq_lens,
-                      const int32_t *query_start_loc, int64_t b, int64_t t,
-                      int64_t h, int64_t Hq, int64_t Hkv, int64_t bs, int64_t D,
-                      double sigma, double *scores, double *out) {
+/* One output row: query token t (global index) of sequence b, query head h;
+ * pools and layout from *pools (its bt_row and g are set here). */
+static void paged_row(const uint16_t *q, const paged_ctx *pools,
+                      const int32_t *block_tables, int64_t bt_stride,
+                      const int32_t *seq_lens, const int32_t *query_start_loc,
+                      int64_t b, int64_t t, int64_t h, int64_t Hq, double sigma,
+                      double *scores, double *out) {
   int64_t L = seq_lens[b];
   int64_t Q = query_start_loc[b + 1] - query_start_loc[b];
   int64_t i = t - query_start_loc[b];
   int64_t p = L - Q + i; /* position of this query; it sees keys 0..p */
-  paged_ctx c = {k_cache, v_cache, block_tables + b * bt_stride,
-                 h / (Hq / Hkv), Hkv, bs, D};
+  int64_t D = pools->D;
+  paged_ctx c = *pools;
+  c.bt_row = block_tables + b * bt_stride;
+  c.g = h / (Hq / pools->Hkv);
   const uint16_t *qrow = q + (size_t)((t * Hq + h) * D);
   for (int64_t j = 0; j <= p; ++j) {
     double dot = 0.0;
@@ -209,6 +330,33 @@ static int64_t seq_of_token(const int32_t *query_start_loc, int64_t num_seqs,
   return -1;
 }
 
+/* Rows rows[2r] = query token t, rows[2r+1] = query head h (all rows when
+ * rows is NULL: r = t * Hq + h); out[r][d]. */
+static void attend_impl(const uint16_t *q, const paged_ctx *pools,
+                        const int32_t *block_tables, int64_t bt_stride,
+                        const int32_t *seq_lens, const int32_t *query_start_loc,
+                        int64_t num_seqs, int64_t Hq, float scale,
+                        int64_t max_seq_len, const int64_t *rows,
+                        int64_t num_rows, double *scratch, double *out,
+                        int nthreads) {
+  double sigma = (double)scale;
+  int64_t D = pools->D;
+  (void)nthreads;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+  for (int64_t r = 0; r < num_rows; ++r) {
+    int tid = 0;
+#ifdef _OPENMP
+    tid = omp_get_thread_num();
+#endif
+    int64_t t = rows ? rows[2 * r] : r / Hq;
+    int64_t h = rows ? rows[2 * r + 1] : r % Hq;
+    int64_t b = seq_of_token(query_start_loc, num_seqs, t);
+    paged_row(q, pools, block_tables, bt_stride, seq_lens, query_start_loc, b,
+              t, h, Hq, sigma, scratch + (size_t)tid * (size_t)max_seq_len,
+              out + (size_t)(r * D));
+  }
+}
+
 /* out[t][h][d] (fp64) for every query token of every sequence. */
 void oracle_attend(const uint16_t *q, const uint16_t *k_cache,
                    const uint16_t *v_cache, const int32_t *block_tables,
@@ -217,22 +365,10 @@ void oracle_attend(const uint16_t *q, const uint16_t *k_cache,
                    int64_t Hq, int64_t Hkv, int64_t bs, int64_t D, float scale,
                    int64_t max_seq_len, double *scratch, double *out,
                    int nthreads) {
-  int64_t T = query_start_loc[num_seqs];
-  double sigma = (double)scale;
-  (void)nthreads;
-#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
-  for (int64_t r = 0; r < T * Hq; ++r) {
-    int64_t t = r / Hq, h = r % Hq;
-    int tid = 0;
-#ifdef _OPENMP
-    tid = omp_get_thread_num();
-#endif
-    int64_t b = seq_of_token(query_start_loc, num_seqs, t);
-    paged_row(q, k_cache, v_cache, block_tables, bt_stride, seq_lens,
-              query_start_loc, b, t, h, Hq, Hkv, bs, D, sigma,
-              scratch + (size_t)tid * (size_t)max_seq_len,
-              out + (size_t)((t * Hq + h) * D));
-  }
+  paged_ctx pools = {k_cache, v_cache, NULL, NULL, 1.0, 1.0, NULL, 0, Hkv, bs, D};
+  attend_impl(q, &pools, block_tables, bt_stride, seq_lens, query_start_loc,
+              num_seqs, Hq, scale, max_seq_len, NULL,
+              query_start_loc[num_seqs] * Hq, scratch, out, nthreads);
 }
 
 /* Selected rows only: rows[2r] = query token t, rows[2r+1] = query head h;
@@ -245,21 +381,28 @@ void oracle_attend_rows(const uint16_t *q, const uint16_t *k_cache,
                         float scale, int64_t max_seq_len, const int64_t *rows,
                         int64_t num_rows, double *scratch, double *out_rows,
                         int nthreads) {
-  double sigma = (double)scale;
-  (void)nthreads;
-#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
-  for (int64_t r = 0; r < num_rows; ++r) {
-    int tid = 0;
-#ifdef _OPENMP
-    tid = omp_get_thread_num();
-#endif
-    int64_t t = rows[2 * r], h = rows[2 * r + 1];
-    int64_t b = seq_of_token(query_start_loc, num_seqs, t);
-    paged_row(q, k_cache, v_cache, block_tables, bt_stride, seq_lens,
-              query_start_loc, b, t, h, Hq, Hkv, bs, D, sigma,
-              scratch + (size_t)tid * (size_t)max_seq_len,
-              out_rows + (size_t)(r * D));
-  }
+  paged_ctx pools = {k_cache, v_cache, NULL, NULL, 1.0, 1.0, NULL, 0, Hkv, bs, D};
+  attend_impl(q, &pools, block_tables, bt_stride, seq_lens, query_start_loc,
+              num_seqs, Hq, scale, max_seq_len, rows, num_rows, scratch,
+              out_rows, nthreads);
+}
+
+/* The same attention over 8-bit pools: K and V values are
+ * decode(code) * k_scale and decode(code) * v_scale. */
+void oracle_attend_fp8(const uint16_t *q, const uint8_t *k8, const uint8_t *v8,
+                       float k_scale, float v_scale,
+                       const int32_t *block_tables, int64_t bt_stride,
+                       const int32_t *seq_lens, const int32_t *query_start_loc,
+                       int64_t num_seqs, int64_t Hq, int64_t Hkv, int64_t bs,
+                       int64_t D, float scale, int64_t max_seq_len,
+                       const int64_t *rows, int64_t num_rows, double *scratch,
+                       double *out, int nthreads) {
+  paged_ctx pools = {NULL, NULL, k8, v8, (double)k_scale, (double)v_scale,
+                     NULL, 0, Hkv, bs, D};
+  if (!rows) num_rows = query_start_loc[num_seqs] * Hq;
+  attend_impl(q, &pools, block_tables, bt_stride, seq_lens, query_start_loc,
+              num_seqs, Hq, scale, max_seq_len, rows, num_rows, scratch, out,
+              nthreads);
 }
 
 /* Dense form: K/V of sequence b are rows kv_start_b .. kv_start_b + L_b - 1

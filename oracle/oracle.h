@@ -39,5 +39,23 @@ void oracle_attend_dense(const uint16_t *q, const uint16_t *k_dense,
                          const int32_t *query_start_loc, int64_t num_seqs,
                          int64_t Hq, int64_t Hkv, int64_t D, float scale,
                          int64_t max_seq_len, double *scratch, double *out);
+double oracle_e4m3_decode(uint8_t b);
+uint8_t oracle_e4m3_encode(float v);
+size_t oracle_k8_index(int64_t n, int64_t g, int64_t t, int64_t d, int64_t Hkv,
+                       int64_t bs, int64_t D);
+size_t oracle_v8_index(int64_t n, int64_t g, int64_t t, int64_t d, int64_t Hkv,
+                       int64_t bs, int64_t D);
+void oracle_write_kv_fp8(uint8_t *k_cache, uint8_t *v_cache, const uint16_t *k,
+                         const uint16_t *v, const int64_t *slot_mapping,
+                         int64_t num_tokens, int64_t Hkv, int64_t bs, int64_t D,
+                         float k_scale, float v_scale);
+void oracle_attend_fp8(const uint16_t *q, const uint8_t *k8, const uint8_t *v8,
+                       float k_scale, float v_scale,
+                       const int32_t *block_tables, int64_t bt_stride,
+                       const int32_t *seq_lens, const int32_t *query_start_loc,
+                       int64_t num_seqs, int64_t Hq, int64_t Hkv, int64_t bs,
+                       int64_t D, float scale, int64_t max_seq_len,
+                       const int64_t *rows, int64_t num_rows, double *scratch,
+                       double *out, int nthreads);
 int oracle_abi_version(void);
 #endif
