@@ -140,6 +140,38 @@ pa_status pa_write_kv(const void *k, const void *v, int64_t k_token_stride,
                       int64_t num_blocks, void *stream);
 
 /*
+ * pa_write_kv_fp8 - pa_write_kv into 8-bit pools (fp8 E4M3 KV cache).
+ *
+ * Same slots, skips and races as pa_write_kv; each element x (bf16, widened
+ * exactly to fp32) is stored as the E4M3 code of the fp32 quotient
+ * x / k_scale (x / v_scale for V): round to nearest, ties to the even
+ * mantissa; magnitudes at or above 448 and infinities saturate to +-448;
+ * NaN -> 0x7f.  E4M3 is the OCP 8-bit format (sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits, no infinities, S.1111.111 = NaN), the one gfx950
+ * converts in hardware.  A code stands for decode(code) * scale.
+ *
+ *   k_cache, v_cache device uint8 pools of num_blocks * num_kv_heads tiles,
+ *                   each 16 * head_dim bytes; tile (n, g) at byte
+ *                   (n * num_kv_heads + g) * 16 * D, and inside it, H = D/2:
+ *     K(t, d), d = 32c + 8q + j, c = 2p + h:     ((p*4 + q)*16 + t)*16 + h*8 + j
+ *     V(t, d), d = dh*H + 16c + r, c = 2p + cc:  ((p*4 + t/4)*16 + r)*16
+ *                                                 + (2cc + dh)*4 + t%4
+ *   k_scale, v_scale one fp32 scale per pool, finite and > 0 (PA_ERR_SHAPE
+ *                   otherwise)
+ *   other arguments as for pa_write_kv.
+ *
+ * Source: "vLLM: An Exhaustive Technical Study", section 2.8 (the KV-cache
+ * quantisation axis: fp8 E4M3 with an fp32 scale per tensor), with the slot
+ * semantics of pa_write_kv.
+ */
+pa_status pa_write_kv_fp8(const void *k, const void *v, int64_t k_token_stride,
+                          int64_t v_token_stride, const int64_t *slot_mapping,
+                          int64_t num_tokens, int32_t num_kv_heads,
+                          int32_t head_dim, float k_scale, float v_scale,
+                          void *k_cache, void *v_cache, int64_t num_blocks,
+                          void *stream);
+
+/*
  * pa_attend_workspace_size - bytes of device workspace pa_attend needs for a
  * batch within these bounds (work list, per-token split records and split-K
  * partial results).  Returns 0 for invalid arguments.

@@ -96,6 +96,54 @@ def write_kv(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
     _lib.check(st, "pa_write_kv")
 
 
+def alloc_pool_fp8(num_blocks: int, num_kv_heads: int, head_dim: int,
+                   device="cuda", fill: Optional[int] = None
+                   ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Two 8-bit pools (K, V) of E4M3 codes, each uint8
+    [num_blocks][num_kv_heads][16 * head_dim] in the library's 8-bit tile
+    layout; fill: a code byte, or None for uninitialised memory."""
+    shape = (num_blocks, num_kv_heads, BLOCK_SIZE * head_dim)
+    if fill is None:
+        k = torch.empty(shape, dtype=torch.uint8, device=device)
+        v = torch.empty(shape, dtype=torch.uint8, device=device)
+    else:
+        k = torch.full(shape, fill, dtype=torch.uint8, device=device)
+        v = torch.full(shape, fill, dtype=torch.uint8, device=device)
+    return k, v
+
+
+def write_kv_fp8(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                 k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: float,
+                 v_scale: float) -> None:
+    """Scatter k, v ([T][Hkv][D] bf16, rows may be strided) into 8-bit pools:
+    the E4M3 code of fp32(x) / scale per element."""
+    for t, n in ((k, "k"), (v, "v"), (slot_mapping, "slot_mapping"),
+                 (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need_cuda(t, n)
+    _dtype(k, torch.bfloat16, "k")
+    _dtype(v, torch.bfloat16, "v")
+    _dtype(slot_mapping, torch.int64, "slot_mapping")
+    _dtype(k_cache, torch.uint8, "k_cache")
+    _dtype(v_cache, torch.uint8, "v_cache")
+    if k.dim() != 3 or v.shape != k.shape:
+        raise ValueError("k and v must be [num_tokens][num_kv_heads][head_dim]")
+    T, Hkv, D = k.shape
+    for t, n in ((k, "k"), (v, "v")):
+        if t.stride(2) != 1 or t.stride(1) != D:
+            raise ValueError("%s rows must be contiguous [num_kv_heads][head_dim]" % n)
+    if not slot_mapping.is_contiguous() or slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be contiguous [num_tokens]")
+    nb = _pool_blocks(k_cache, Hkv, D)
+    if _pool_blocks(v_cache, Hkv, D) != nb:
+        raise ValueError("k_cache and v_cache differ in size")
+    lib = _lib.load()
+    st = lib.pa_write_kv_fp8(_ptr(k), _ptr(v), k.stride(0), v.stride(0),
+                             _ptr(slot_mapping), T, Hkv, D, float(k_scale),
+                             float(v_scale), _ptr(k_cache), _ptr(v_cache), nb,
+                             _stream(k))
+    _lib.check(st, "pa_write_kv_fp8")
+
+
 def workspace_size(num_seqs: int, num_q_tokens: int, num_q_heads: int,
                    num_kv_heads: int, head_dim: int, max_query_len: int,
                    max_seq_len: int) -> int:

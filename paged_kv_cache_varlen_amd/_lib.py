@@ -23,6 +23,8 @@ SIGNATURES = {
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_write_kv": (STATUS, [P, P, I64, I64, P, I64, I32, I32, P, P, I64, P]),
+    "pa_write_kv_fp8": (STATUS, [P, P, I64, I64, P, I64, I32, I32, F32, F32, P, P,
+                                 I64, P]),
     "pa_attend_workspace_size": (SZ, [I32, I64, I32, I32, I32, I32, I32]),
     "pa_attend": (STATUS, [P, P, P, I64, P, I32, P, P, I32, I64, I32, I32, I32,
                            I32, I32, F32, P, P, SZ, P]),

@@ -115,6 +115,38 @@ pa_status pa_write_kv(const void* k, const void* v, int64_t k_token_stride,
   return ok();
 }
 
+pa_status pa_write_kv_fp8(const void* k, const void* v, int64_t k_token_stride,
+                          int64_t v_token_stride, const int64_t* slot_mapping,
+                          int64_t num_tokens, int32_t num_kv_heads,
+                          int32_t head_dim, float k_scale, float v_scale,
+                          void* k_cache, void* v_cache, int64_t num_blocks,
+                          void* stream) {
+  if (num_tokens < 0 || num_blocks < 0)
+    return fail(PA_ERR_SHAPE, "num_tokens and num_blocks must be >= 0");
+  if (num_kv_heads <= 0) return fail(PA_ERR_SHAPE, "num_kv_heads must be > 0");
+  if (!supported_head_dim(head_dim))
+    return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (!(k_scale > 0.0f && k_scale <= FLT_MAX) || !(v_scale > 0.0f && v_scale <= FLT_MAX))
+    return fail(PA_ERR_SHAPE, "pa_write_kv_fp8: scales must be finite and > 0");
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (k_token_stride < row || v_token_stride < row)
+    return fail(PA_ERR_SHAPE, "token strides must be >= num_kv_heads*head_dim");
+  if ((k_token_stride % 8) || (v_token_stride % 8))
+    return fail(PA_ERR_SHAPE, "token strides must be multiples of 8 elements");
+  if (num_tokens == 0) return ok();
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache)
+    return fail(PA_ERR_NULL, "pa_write_kv_fp8: NULL pointer");
+  if (((uintptr_t)k | (uintptr_t)v | (uintptr_t)k_cache | (uintptr_t)v_cache) & 15)
+    return fail(PA_ERR_SHAPE, "k, v and the pools must be 16-byte aligned");
+  hipError_t e = pa::launch_write_kv8(
+      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+      k_token_stride, v_token_stride, slot_mapping, num_tokens, num_kv_heads,
+      head_dim, k_scale, v_scale, static_cast<uint8_t*>(k_cache),
+      static_cast<uint8_t*>(v_cache), num_blocks, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pa_write_kv_fp8 launch");
+  return ok();
+}
+
 size_t pa_attend_workspace_size(int32_t num_seqs, int64_t num_q_tokens,
                                 int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t max_query_len,

@@ -134,6 +134,13 @@ hipError_t launch_write_kv(const uint16_t* k, const uint16_t* v,
                            uint16_t* v_cache, int64_t num_blocks,
                            hipStream_t stream);
 
+hipError_t launch_write_kv8(const uint16_t* k, const uint16_t* v,
+                            int64_t k_stride, int64_t v_stride,
+                            const int64_t* slot_mapping, int64_t num_tokens,
+                            int num_kv_heads, int head_dim, float k_scale,
+                            float v_scale, uint8_t* k_cache, uint8_t* v_cache,
+                            int64_t num_blocks, hipStream_t stream);
+
 hipError_t launch_gather_kv(const uint16_t* k_cache, const uint16_t* v_cache,
                             int64_t num_blocks, const int32_t* block_tables,
                             int32_t bt_stride, const int32_t* seq_lens,

@@ -26,7 +26,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_and_binding_agree():
@@ -102,6 +102,26 @@ def test_attend_empty_batch_is_ok(lib):
 ])
 def test_write_kv_argument_checks(lib, args, status):
     assert lib.pa_write_kv(*args) == status
+
+
+def _w8(k=FAKE, stride=256, T=4, D=128, ks=0.5, vs=0.25, kc=FAKE):
+    return (k, FAKE, stride, 256, FAKE, T, 2, D, ks, vs, kc, FAKE, 8, None)
+
+
+@pytest.mark.parametrize("args,status", [
+    (_w8(D=96), _lib.PA_ERR_UNSUPPORTED),
+    (_w8(k=None), _lib.PA_ERR_NULL),
+    (_w8(stride=100), _lib.PA_ERR_SHAPE),
+    (_w8(T=-4), _lib.PA_ERR_SHAPE),
+    (_w8(ks=0.0), _lib.PA_ERR_SHAPE),
+    (_w8(vs=-1.0), _lib.PA_ERR_SHAPE),
+    (_w8(ks=float("nan")), _lib.PA_ERR_SHAPE),
+    (_w8(vs=float("inf")), _lib.PA_ERR_SHAPE),
+    (_w8(k=FAKE + 8), _lib.PA_ERR_SHAPE),
+    (_w8(T=0, k=None, kc=None), _lib.PA_OK),
+])
+def test_write_kv_fp8_argument_checks(lib, args, status):
+    assert lib.pa_write_kv_fp8(*args) == status
 
 
 def test_gather_argument_checks(lib):
