@@ -275,6 +275,46 @@ pa_status pa_attend_merge(int32_t num_seqs, int64_t num_q_tokens,
                           size_t workspace_bytes, void *stream);
 
 /*
+ * pa_attend_fp8, pa_attend_planned_fp8 - pa_attend and pa_attend_planned
+ * over 8-bit pools written by pa_write_kv_fp8.
+ *
+ * Same arguments and results as the bf16 calls, with k_cache and v_cache the
+ * uint8 pools (layout with pa_write_kv_fp8) and two more scalars: a K code
+ * stands for decode(code) * k_scale, a V code for decode(code) * v_scale
+ * (decode: the E4M3 value; k_scale, v_scale finite and > 0, PA_ERR_SHAPE
+ * otherwise).  Codes are widened to bf16 exactly (every E4M3 value is a
+ * bf16 value) before the same fp32-accumulating MFMAs as the bf16 path;
+ * k_scale joins the softmax scale and v_scale the output normalisation.
+ * The work plan (pa_attend_plan) and the merge (pa_attend_merge) are the
+ * bf16 path's: the split partials already carry v_scale.
+ *
+ * Source: "vLLM: An Exhaustive Technical Study", section 2.8 (fp8 E4M3
+ * KV cache, one fp32 scale per tensor), with the attention of pa_attend.
+ */
+pa_status pa_attend_fp8(const void *q, const void *k_cache, const void *v_cache,
+                        int64_t num_blocks, const int32_t *block_tables,
+                        int32_t max_blocks_per_seq, const int32_t *seq_lens,
+                        const int32_t *query_start_loc, int32_t num_seqs,
+                        int64_t num_q_tokens, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim,
+                        int32_t max_query_len, int32_t max_seq_len, float scale,
+                        float k_scale, float v_scale, void *out, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+pa_status pa_attend_planned_fp8(const void *q, const void *k_cache,
+                                const void *v_cache, int64_t num_blocks,
+                                const int32_t *block_tables,
+                                int32_t max_blocks_per_seq,
+                                const int32_t *seq_lens,
+                                const int32_t *query_start_loc, int32_t num_seqs,
+                                int64_t num_q_tokens, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim,
+                                int32_t max_query_len, int32_t max_seq_len,
+                                float scale, float k_scale, float v_scale,
+                                void *out, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/*
  * pa_gather_kv - logical gather through the block tables (a checking aid).
  *
  * Writes k_out/v_out, device bf16 [sum_b L_b][num_kv_heads][head_dim]: row

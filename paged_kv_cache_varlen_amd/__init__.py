@@ -170,8 +170,9 @@ def _attend_args(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
                  (query_start_loc, "query_start_loc")):
         _need_cuda(t, n)
     _dtype(q, torch.bfloat16, "q")
-    _dtype(k_cache, torch.bfloat16, "k_cache")
-    _dtype(v_cache, torch.bfloat16, "v_cache")
+    pool_dtype = torch.uint8 if k_cache.dtype == torch.uint8 else torch.bfloat16
+    _dtype(k_cache, pool_dtype, "k_cache")
+    _dtype(v_cache, pool_dtype, "v_cache")
     _dtype(block_tables, torch.int32, "block_tables")
     _dtype(seq_lens, torch.int32, "seq_lens")
     _dtype(query_start_loc, torch.int32, "query_start_loc")
@@ -209,26 +210,33 @@ def attend(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
            max_seq_len: int, num_kv_heads: Optional[int] = None,
            out: Optional[torch.Tensor] = None,
            workspace: Optional[torch.Tensor] = None,
-           planned: bool = False, merge: bool = True) -> torch.Tensor:
+           planned: bool = False, merge: bool = True,
+           k_scale: float = 1.0, v_scale: float = 1.0) -> torch.Tensor:
     """Paged varlen causal attention of every query row of a mixed batch.
 
     q [T][Hq][D] bf16; block_tables [B][max_blocks] int32; seq_lens [B] int32;
-    query_start_loc [B+1] int32; pools from alloc_pool.  Returns out
-    [T][Hq][D] bf16 (written in place when ``out`` is given).  With
-    planned=True the work plan already in ``workspace`` (from attend_plan with
-    the same metadata) is used: the attention kernel is enqueued, then (with
-    merge=True, the default) the split-K merge kernel; merge=False leaves the
-    merge to a later attend_merge call."""
+    query_start_loc [B+1] int32; pools from alloc_pool (bf16) or
+    alloc_pool_fp8 (E4M3 codes standing for code * k_scale, code * v_scale).
+    Returns out [T][Hq][D] bf16 (written in place when ``out`` is given).
+    With planned=True the work plan already in ``workspace`` (from attend_plan
+    with the same metadata) is used: the attention kernel is enqueued, then
+    (with merge=True, the default) the split-K merge kernel; merge=False
+    leaves the merge to a later attend_merge call."""
     T, Hq, D, Hkv, nb, B, out, workspace = _attend_args(
         q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
         num_kv_heads, out, workspace, max_query_len, max_seq_len)
     lib = _lib.load()
-    fn = lib.pa_attend_planned if planned else lib.pa_attend
-    st = fn(_ptr(q), _ptr(k_cache), _ptr(v_cache), nb, _ptr(block_tables),
+    args = [_ptr(q), _ptr(k_cache), _ptr(v_cache), nb, _ptr(block_tables),
             block_tables.shape[1], _ptr(seq_lens), _ptr(query_start_loc), B, T,
-            Hq, Hkv, D, int(max_query_len), int(max_seq_len), float(scale),
-            _ptr(out), _ptr(workspace), workspace.numel(), _stream(q))
-    _lib.check(st, "pa_attend_planned" if planned else "pa_attend")
+            Hq, Hkv, D, int(max_query_len), int(max_seq_len), float(scale)]
+    if k_cache.dtype == torch.uint8:
+        name = "pa_attend_planned_fp8" if planned else "pa_attend_fp8"
+        args += [float(k_scale), float(v_scale)]
+    else:
+        name = "pa_attend_planned" if planned else "pa_attend"
+    st = getattr(lib, name)(*args, _ptr(out), _ptr(workspace), workspace.numel(),
+                            _stream(q))
+    _lib.check(st, name)
     if planned and merge:
         attend_merge(out, B, Hkv, max_query_len, max_seq_len, workspace)
     return out

@@ -33,6 +33,11 @@ SIGNATURES = {
     "pa_attend_planned": (STATUS, [P, P, P, I64, P, I32, P, P, I32, I64, I32,
                                    I32, I32, I32, I32, F32, P, P, SZ, P]),
     "pa_attend_merge": (STATUS, [I32, I64, I32, I32, I32, I32, I32, P, P, SZ, P]),
+    "pa_attend_fp8": (STATUS, [P, P, P, I64, P, I32, P, P, I32, I64, I32, I32, I32,
+                               I32, I32, F32, F32, F32, P, P, SZ, P]),
+    "pa_attend_planned_fp8": (STATUS, [P, P, P, I64, P, I32, P, P, I32, I64, I32,
+                                       I32, I32, I32, I32, F32, F32, F32, P, P, SZ,
+                                       P]),
     "pa_gather_kv": (STATUS, [P, P, I64, P, I32, P, P, I32, I64, I32, I32, P, P,
                               P]),
     "pa_validate_metadata_host": (STATUS, [P, I32, P, P, I32, I64, I32, I32, I64,

@@ -51,6 +51,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 // block buffers of the decode pipeline (blocks in flight + 1)
@@ -76,7 +78,8 @@ struct AttendParams {
   int32_t G;
   int32_t max_query_len;
   int32_t max_seq_len;
-  float scale_log2;  // scale * log2(e): scores live in the exp2 domain
+  float scale_log2;  // scale * k_scale * log2(e): scores live in the exp2 domain
+  float v_scale;     // 8-bit pools: the value of a V code is code * v_scale
   uint16_t* out;
   PlanHeader* hdr;
   WorkItem* items;
@@ -412,6 +415,26 @@ __device__ __forceinline__ bf16x8 zero8() {
   return z;
 }
 
+// 8-bit pools: 16-byte loads of E4M3 codes, and their exact conversion to
+// bf16 operands (every E4M3 value is a bf16 value; the scale is applied
+// outside the MFMAs).
+__device__ __forceinline__ u32x4 load16b(const uint8_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ u32x4 load16b_stream(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+// codes in bytes 0..3 of w (lowest first) -> 4 bf16
+__device__ __forceinline__ bf16x4 e4m3x4_to_bf16(uint32_t w) {
+  const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
+}
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
+  return __builtin_shufflevector(e4m3x4_to_bf16(w0), e4m3x4_to_bf16(w1), 0, 1, 2, 3, 4,
+                                 5, 6, 7);
+}
+
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -511,7 +534,7 @@ __device__ __forceinline__ void softmax_probs(const float (&s)[N], float c,
 // End of a unit: direct bf16 output, or fp32 partials (running max, sum and
 // unnormalised accumulator per column) for the merge kernel.  l[ct] is the
 // column's full probability sum (the same in all four lanes of a column).
-template <int D, int CT>
+template <int D, int CT, bool KV8>
 __device__ __forceinline__ void finish_unit(const AttendParams& P,
                                             const WorkItem& it, int kvh,
                                             int lane, f32x4 (&acc)[CT][D / 16],
@@ -529,7 +552,8 @@ __device__ __forceinline__ void finish_unit(const AttendParams& P,
       const int tk = col / G;
       const int64_t t = it.tok0 + tk;
       const int h = kvh * G + (col - tk * G);
-      const float inv = 1.0f / l[ct];
+      // 8-bit pools: V codes stand for code * v_scale
+      const float inv = (KV8 ? P.v_scale : 1.0f) / l[ct];
       uint16_t* op = P.out + (t * P.Hq + h) * D + 4 * g;
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
@@ -551,7 +575,7 @@ __device__ __forceinline__ void finish_unit(const AttendParams& P,
     float* ap = P.part_acc + (slot * P.Hq + h) * D + 4 * g;
 #pragma unroll
     for (int n = 0; n < NT; ++n)
-      *reinterpret_cast<f32x4*>(ap + 16 * n) = acc[ct][n];
+      *reinterpret_cast<f32x4*>(ap + 16 * n) = KV8 ? acc[ct][n] * P.v_scale : acc[ct][n];
     if (g == 0) P.part_ml[slot * P.Hq + h] = make_float2(mrun[ct], l[ct]);
   }
 }
@@ -561,6 +585,19 @@ struct KVBlock {
   bf16x8 k[D / 32];  // K rows in MFMA operand order
   bf16x8 v[D / 32];  // lane's 4 keys at dims d and d + D/2
 };
+
+// The same block from 8-bit pools: per lane, unit p of K holds the operands
+// of chunks 2p and 2p+1 (8 codes each), unit p of V the 4-key operands of
+// chunks 2p + cc at dims d and d + D/2 (one 32-bit word each, (cc, dh) order
+// (0,0), (0,1), (1,0), (1,1)).
+template <int D>
+struct KVBlock8 {
+  u32x4 k[D / 64];
+  u32x4 v[D / 64];
+};
+
+template <int D, bool KV8>
+using KVBuf = typename std::conditional<KV8, KVBlock8<D>, KVBlock<D>>::type;
 
 // V operand of k step c for lane (r, g): keys 4g .. 4g+3 at dims 16c + r
 // (elements 0-3) and D/2 + 16c + r (4-7), two 8-byte reads of the tile.
@@ -583,7 +620,7 @@ __device__ __forceinline__ bf16x8 load_v(const uint16_t* vp, int c, int lane) {
 // If `counter` is not null, the next queue entry is claimed from it when the
 // load of the unit's last block is issued (its latency then hides behind the
 // last blocks and the output stores) and returned; otherwise 0.
-template <int D, int CT, int NB, bool STREAM>
+template <int D, int CT, int NB, bool STREAM, bool KV8>
 __device__ __forceinline__ uint32_t run_unit(const AttendParams& P,
                                              const WorkItem& it, int kvh,
                                              int lane,
@@ -622,26 +659,61 @@ __device__ __forceinline__ uint32_t run_unit(const AttendParams& P,
     if (lane < nblk) idv = btrow[c0 + lane];
     idv = idv < 0 ? 0 : (idv >= P.num_blocks ? (int)(P.num_blocks - 1) : idv);
 
-    auto issue = [&](KVBlock<D>& buf, int j) {
+    auto issue = [&](KVBuf<D, KV8>& buf, int j) {
       if (counter != nullptr && !claimed && c0 + j == jb1 - 1) {
         if (lane == 0) claim = atomicAdd(counter, 1u);
         claimed = true;
       }
       const int id = __builtin_amdgcn_readlane(idv, j);
       const int64_t off = ((int64_t)id * P.Hkv + kvh) * tile_elems;
-      const uint16_t* kp = P.k_cache + off;
-      const uint16_t* vp = P.v_cache + off;
+      if constexpr (KV8) {
+        // tile_elems bytes per tile; unit p of either pool at p KiB + 16 lane
+        const uint8_t* kp = reinterpret_cast<const uint8_t*>(P.k_cache) + off;
+        const uint8_t* vp = reinterpret_cast<const uint8_t*>(P.v_cache) + off;
 #pragma unroll
-      for (int c = 0; c < KC; ++c)
-        buf.k[c] = STREAM ? load16_stream(kp + c * 512 + lane * 8)
-                          : load16(kp + c * 512 + lane * 8);
+        for (int u = 0; u < D / 64; ++u)
+          buf.k[u] = STREAM ? load16b_stream(kp + u * 1024 + lane * 16)
+                            : load16b(kp + u * 1024 + lane * 16);
 #pragma unroll
-      for (int c = 0; c < KC; ++c) buf.v[c] = load_v<D, STREAM>(vp, c, lane);
+        for (int u = 0; u < D / 64; ++u)
+          buf.v[u] = STREAM ? load16b_stream(vp + u * 1024 + lane * 16)
+                            : load16b(vp + u * 1024 + lane * 16);
+      } else {
+        const uint16_t* kp = P.k_cache + off;
+        const uint16_t* vp = P.v_cache + off;
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+          buf.k[c] = STREAM ? load16_stream(kp + c * 512 + lane * 8)
+                            : load16(kp + c * 512 + lane * 8);
+#pragma unroll
+        for (int c = 0; c < KC; ++c) buf.v[c] = load_v<D, STREAM>(vp, c, lane);
+      }
     };
 
-    auto compute = [&](KVBlock<D>& buf, int j) {
+    auto compute = [&](KVBuf<D, KV8>& buf8, int j) {
       const int kp0 = (c0 + j) * kBlock;
-      if (kp0 + kBlock > it.kv1) {
+      KVBlock<D> buf;
+      if constexpr (KV8) {
+        // keys at or past kv1 may be unwritten pool slots: zero their codes
+        // (code 0 is +0) so a 0 weight cannot meet a NaN
+        uint32_t keep = 0xffffffffu;
+        if (kp0 + kBlock > it.kv1) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (kp0 + 4 * g + i >= it.kv1) keep &= ~(0xffu << (8 * i));
+        }
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+          const u32x4 ku = buf8.k[c >> 1];
+          const u32x4 vu = buf8.v[c >> 1];
+          buf.k[c] = (c & 1) ? e4m3x8_to_bf16(ku[2], ku[3]) : e4m3x8_to_bf16(ku[0], ku[1]);
+          buf.v[c] = (c & 1) ? e4m3x8_to_bf16(vu[2] & keep, vu[3] & keep)
+                             : e4m3x8_to_bf16(vu[0] & keep, vu[1] & keep);
+        }
+      } else {
+        buf = buf8;
+      }
+      if (!KV8 && kp0 + kBlock > it.kv1) {
         // keys at or past kv1 may be unwritten pool slots: zero their V so a
         // 0 weight cannot meet a NaN
 #pragma unroll
@@ -693,7 +765,7 @@ __device__ __forceinline__ uint32_t run_unit(const AttendParams& P,
     // no early exit), so the compiler's waits stop at the block being
     // computed and never drain the prefetches.  Clamped prefetches past the
     // end re-read the last block (an L2 hit).
-    KVBlock<D> buf[NB];
+    KVBuf<D, KV8> buf[NB];
 #pragma unroll
     for (int k = 0; k < NB - 1; ++k) issue(buf[k], min(k, nblk - 1));
     int j = 0;
@@ -719,7 +791,7 @@ __device__ __forceinline__ uint32_t run_unit(const AttendParams& P,
   if (counter != nullptr && !claimed) {
     if (lane == 0) claim = atomicAdd(counter, 1u);
   }
-  finish_unit<D, CT>(P, it, kvh, lane, acc, mrun, l);
+  finish_unit<D, CT, KV8>(P, it, kvh, lane, acc, mrun, l);
   return __builtin_amdgcn_readfirstlane(__shfl(claim, 0));
 }
 
@@ -740,18 +812,24 @@ __device__ __forceinline__ uint32_t run_unit(const AttendParams& P,
 // adjacent registers.  All are conflict-free.
 constexpr int kPairStages = 4;
 
-template <int D>
-constexpr int pair_stage_elems() {
-  return 4 * kBlock * D;
+// Bytes of one K or V pool tile, of a ring stage and of the ring (bf16 or
+// 8-bit pools).
+template <int D, bool KV8>
+constexpr int tile_bytes() {
+  return kBlock * D * (KV8 ? 1 : 2);
 }
-template <int D>
-constexpr int prefill_ring_elems() {
-  return kPairStages * pair_stage_elems<D>();
+template <int D, bool KV8>
+constexpr int pair_stage_bytes() {
+  return 4 * tile_bytes<D, KV8>();
+}
+template <int D, bool KV8>
+constexpr int prefill_ring_bytes() {
+  return kPairStages * pair_stage_bytes<D, KV8>();
 }
 
-__device__ __forceinline__ uint32_t lds_addr(const uint16_t* l) {
+__device__ __forceinline__ uint32_t lds_addr(const void* l) {
   return __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint16_t*)l);
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)l);
 }
 
 __device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
@@ -774,9 +852,17 @@ __device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
 template <int N>
 __device__ __forceinline__ void load_lds_kib(const uint16_t* base, uint32_t voff,
                                              uint32_t l) {
-  static_assert(N == 2 || N == 4, "one 1 KiB load per 8 dims x 16 tokens");
+  static_assert(N == 1 || N == 2 || N == 4, "1, 2 or 4 KiB tiles");
   uint32_t saved;
-  if constexpr (N == 2) {
+  if constexpr (N == 1) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 4\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(uniform_ptr(base)), "s"(l)
+        : "memory");
+  } else if constexpr (N == 2) {
     asm volatile(
         "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 4\n\t"
         "global_load_lds_dwordx4 %1, %2\n\t"
@@ -826,6 +912,22 @@ __device__ __forceinline__ bf16x8 lds_read2st64(uint32_t addr) {
                : "v"(addr), "n"(O0), "n"(O1));
   return r;
 }
+// One 16-byte LDS read at addr + O (bytes), untracked like lds_read2st64.
+template <int O>
+__device__ __forceinline__ u32x4 lds_read_b128(uint32_t addr) {
+  static_assert(O >= 0 && O < 65536, "ds offset range");
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(O));
+  return r;
+}
+// The 2 (D/64) raw 8-bit V units of a pair: units p of the first block's V
+// tile (at addr + 1 KiB p) and of the second's (SECOND bytes further).
+template <int SECOND, int... U>
+__device__ __forceinline__ void read_v8_units(uint32_t addr, u32x4* va, u32x4* vb,
+                                              std::integer_sequence<int, U...>) {
+  ((va[U] = lds_read_b128<U * 1024>(addr)), ...);
+  ((vb[U] = lds_read_b128<SECOND + U * 1024>(addr)), ...);
+}
 template <int SECOND, int... HC>
 __device__ __forceinline__ void read_v_regions(uint32_t addr, bf16x8* v,
                                                std::integer_sequence<int, HC...>) {
@@ -834,8 +936,8 @@ __device__ __forceinline__ void read_v_regions(uint32_t addr, bf16x8* v,
 // Wait for every outstanding LDS read of the wave, then hand the operands
 // read by lds_read2st64 on to the compiler (each tied to a real instruction,
 // so no use can be scheduled before the wait).
-template <int N>
-__device__ __forceinline__ void wait_lds_operands(bf16x8 (&v)[N]) {
+template <typename T, int N>
+__device__ __forceinline__ void wait_lds_operands(T (&v)[N]) {
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v[0]));
 #pragma unroll
   for (int i = 1; i < N; ++i) asm volatile("s_nop 0" : "+v"(v[i]));
@@ -847,16 +949,18 @@ __device__ __forceinline__ void wait_lds_operands(bf16x8 (&v)[N]) {
 // maximum grows by more than that.
 constexpr float kRescaleSlack = 8.0f;
 
-template <int D>
+template <int D, bool KV8>
 __device__ __forceinline__ void run_tile(const AttendParams& P,
                                          const WorkItem& it, int kvh, int lane,
-                                         int wslot, uint16_t* ring) {
+                                         int wslot, uint8_t* ring) {
   constexpr int KC = D / 32;
   constexpr int NT = D / 16;
   constexpr int CT = kPrefillColTiles;
   constexpr int NS = kPairStages;
-  constexpr int TILE = kBlock * D;  // elements of one K or V tile
-  constexpr int LPS = KC;           // 16-byte loads per wave per stage
+  constexpr int TB = tile_bytes<D, KV8>();        // bytes of one K or V tile
+  constexpr int SB = pair_stage_bytes<D, KV8>();  // bytes of one stage
+  constexpr int LPS = TB / 1024;  // 1 KiB loads per wave per stage
+  constexpr int NU = D / 64;      // 8-bit pools: 16-byte units per lane per tile
   const int g = lane >> 4;
 
   // this wave's token slice of the tile
@@ -897,7 +1001,8 @@ __device__ __forceinline__ void run_tile(const AttendParams& P,
   const int32_t* btrow = P.bt + (int64_t)it.seq * P.bt_stride + jb0;
   // Wave w loads tile w of every stage: K(first), V(first), K(second),
   // V(second) -- 1 KiB per load, in pool order.
-  const uint16_t* pool = (wslot & 1) ? P.v_cache : P.k_cache;
+  const uint8_t* pool =
+      reinterpret_cast<const uint8_t*>((wslot & 1) ? P.v_cache : P.k_cache);
   const int half = wslot >> 1;
 
   // physical ids of 64 blocks (32 pairs) from block 2 * idbase, one per lane
@@ -911,7 +1016,7 @@ __device__ __forceinline__ void run_tile(const AttendParams& P,
   int idv = load_ids(0);
 
   // LDS byte address of this wave's tile in stage 0 (stage s: + s * stage bytes)
-  const uint32_t ring_lds = lds_addr(ring) + (uint32_t)(wslot * TILE * 2);
+  const uint32_t ring_lds = lds_addr(ring) + (uint32_t)(wslot * TB);
   auto issue = [&](int slot, int pr) {
     if (pr >= idbase + 32) {  // pairs are issued in order
       idbase += 32;
@@ -919,14 +1024,13 @@ __device__ __forceinline__ void run_tile(const AttendParams& P,
     }
     // tile index id * Hkv + kvh (below 2^32 for any pool the device holds)
     const uint32_t tix = (uint32_t)__builtin_amdgcn_readlane(idv, 2 * (pr - idbase) + half);
-    const uint16_t* src = pool + (uint64_t)tix * TILE;
-    load_lds_kib<KC>(src, (uint32_t)lane * 16,
-                     ring_lds + (uint32_t)(slot * pair_stage_elems<D>() * 2));
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(pool + (uint64_t)tix * TB);
+    load_lds_kib<LPS>(src, (uint32_t)lane * 16, ring_lds + (uint32_t)(slot * SB));
   };
 
   // Scores of one pair of blocks (stage st): sa for the first block, sb
   // for the second; each K operand feeds the MFMAs of every column tile.
-  auto scores = [&](const uint16_t* st, f32x4 (&sa)[CT], f32x4 (&sb)[CT]) {
+  auto scores = [&](const uint8_t* st, f32x4 (&sa)[CT], f32x4 (&sb)[CT]) {
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       sa[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -934,8 +1038,18 @@ __device__ __forceinline__ void run_tile(const AttendParams& P,
     }
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
-      const bf16x8 ka = lds16(st + c * 512 + lane * 8);
-      const bf16x8 kb = lds16(st + 2 * TILE + c * 512 + lane * 8);
+      bf16x8 ka, kb;
+      if constexpr (KV8) {
+        // unit c/2 holds the codes of chunks c (even: bytes 0-7) and c + 1
+        const u32x4 ua = *reinterpret_cast<const u32x4*>(st + (c >> 1) * 1024 + lane * 16);
+        const u32x4 ub =
+            *reinterpret_cast<const u32x4*>(st + 2 * TB + (c >> 1) * 1024 + lane * 16);
+        ka = (c & 1) ? e4m3x8_to_bf16(ua[2], ua[3]) : e4m3x8_to_bf16(ua[0], ua[1]);
+        kb = (c & 1) ? e4m3x8_to_bf16(ub[2], ub[3]) : e4m3x8_to_bf16(ub[0], ub[1]);
+      } else {
+        ka = lds16(reinterpret_cast<const uint16_t*>(st + c * 1024 + lane * 16));
+        kb = lds16(reinterpret_cast<const uint16_t*>(st + 2 * TB + c * 1024 + lane * 16));
+      }
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         sa[ct] = mfma32(ka, qop[ct][c], sa[ct]);
@@ -945,14 +1059,21 @@ __device__ __forceinline__ void run_tile(const AttendParams& P,
   };
 
   // The 2 KC PV operands of pair pr (in stage pr % NS), read in one go: operand
-  // hc holds, for dim (hc / KC) * D/2 + 16 (hc % KC) + lane % 16, keys
-  // 4g .. 4g+3 of the first block, then the same keys of the second (the
-  // rows the score MFMAs left in this lane).  Region hc of a V tile is 512
-  // bytes, and the second block's tile lies 2 TILE elements further.
-  const uint32_t vbase = lds_addr(ring) + (uint32_t)(TILE * 2 + lane * 8);
-  auto read_v = [&](int pr, bf16x8 (&vop)[2 * KC]) {
-    const uint32_t a = vbase + (uint32_t)((pr % NS) * pair_stage_elems<D>() * 2);
-    read_v_regions<TILE / 128>(a, vop, std::make_integer_sequence<int, 2 * KC>{});
+  // hc = 2c + dh holds, for dim dh * D/2 + 16c + lane % 16, keys 4g .. 4g+3
+  // of the first block, then the same keys of the second (the rows the score
+  // MFMAs left in this lane).  bf16: region hc of a V tile is 512 bytes, and
+  // the second block's tile lies 2 tiles further; 8-bit: the reads fetch the
+  // lane's raw units, converted in softmax_pv (operand 4p + w from word w of
+  // unit p of each block).
+  using VRaw = typename std::conditional<KV8, u32x4, bf16x8>::type;
+  constexpr int NV = KV8 ? 2 * NU : 2 * KC;
+  const uint32_t vbase = lds_addr(ring) + (uint32_t)(TB + lane * (KV8 ? 16 : 8));
+  auto read_v = [&](int pr, VRaw (&vraw)[NV]) {
+    const uint32_t a = vbase + (uint32_t)((pr % NS) * SB);
+    if constexpr (KV8)
+      read_v8_units<2 * TB>(a, vraw, vraw + NU, std::make_integer_sequence<int, NU>{});
+    else
+      read_v_regions<TB / 256>(a, vraw, std::make_integer_sequence<int, 2 * KC>{});
   };
 
   // Softmax and PV of one pair of blocks from its scores.  MASKED: the pair
@@ -960,7 +1081,7 @@ __device__ __forceinline__ void run_tile(const AttendParams& P,
   // the range end); otherwise the step is straight-line code apart from
   // the rare rescale.
   auto softmax_pv = [&](int kp0, const f32x4 (&sa)[CT], const f32x4 (&sb)[CT],
-                        bf16x8 (&vop)[2 * KC], auto masked) {
+                        VRaw (&vraw)[NV], auto masked) {
     constexpr bool MASKED = decltype(masked)::value;
     float x[CT][8];
 #pragma unroll
@@ -1038,7 +1159,21 @@ __device__ __forceinline__ void run_tile(const AttendParams& P,
     // so it is updated in place)
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) lacc[ct] = mfma32(ones, pop[ct], lacc[ct]);
-    wait_lds_operands(vop);
+    wait_lds_operands(vraw);
+    bf16x8 vop[2 * KC];
+    if constexpr (KV8) {
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          vop[4 * u + w] = __builtin_shufflevector(e4m3x4_to_bf16(vraw[u][w]),
+                                                   e4m3x4_to_bf16(vraw[NU + u][w]), 0, 1,
+                                                   2, 3, 4, 5, 6, 7);
+      }
+    } else {
+#pragma unroll
+      for (int hc = 0; hc < 2 * KC; ++hc) vop[hc] = vraw[hc];
+    }
 #pragma unroll
     for (int hc = 0; hc < 2 * KC; ++hc) {
       bf16x8 v = vop[hc];
@@ -1083,7 +1218,7 @@ __device__ __forceinline__ void run_tile(const AttendParams& P,
     const int lim = min(wt.posbase + 1, it.kv1) - kb;  // keys below both limits
     if (lim >= 2 * kBlock) nfull = min(nmask_end, lim / (2 * kBlock));
   }
-  auto stage = [&](int pr) { return ring + (pr % NS) * pair_stage_elems<D>(); };
+  auto stage = [&](int pr) { return ring + (pr % NS) * SB; };
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) issue(s, min(s, npairs - 1));
   f32x4 sa[CT], sb[CT];
@@ -1098,7 +1233,7 @@ __device__ __forceinline__ void run_tile(const AttendParams& P,
   // copy, so the read stays inside the ring)
   int pr = 0;
   for (; pr < nfull; ++pr) {
-    bf16x8 vop[2 * KC];
+    VRaw vop[NV];
     read_v(pr, vop);  // complete since the previous step's barrier
     step(pr);
     f32x4 na[CT], nb[CT];
@@ -1111,7 +1246,7 @@ __device__ __forceinline__ void run_tile(const AttendParams& P,
     }
   }
   for (; pr < nmask_end; ++pr) {
-    bf16x8 vop[2 * KC];
+    VRaw vop[NV];
     read_v(pr, vop);  // complete since the previous step's barrier
     step(pr);
     f32x4 na[CT], nb[CT];
@@ -1131,7 +1266,7 @@ __device__ __forceinline__ void run_tile(const AttendParams& P,
     float l[CT];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) l[ct] = lacc[ct][0];
-    finish_unit<D, CT>(P, wt, kvh, lane, acc, mref, l);
+    finish_unit<D, CT, KV8>(P, wt, kvh, lane, acc, mref, l);
   }
 }
 
@@ -1155,9 +1290,9 @@ __device__ __forceinline__ bool item_ok(const AttendParams& P,
   return ok;
 }
 
-template <int D, bool MIXED>
+template <int D, bool MIXED, bool KV8>
 __device__ __forceinline__ void attend_body(const AttendParams& P,
-                                            uint16_t* ring) {
+                                            uint8_t* ring) {
   const int lane = threadIdx.x & 63;
   if (P.hdr->signature != plan_signature(P)) {
     if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(&P.hdr->error, 4u);
@@ -1216,7 +1351,7 @@ __device__ __forceinline__ void attend_body(const AttendParams& P,
     for (uint32_t pass = 0; u < num_pre && pass <= num_pre; ++pass) {
       const WorkItem it = P.items[u / Hkv];
       if (item_ok(P, it) && it.kind == kKindPrefill)
-        run_tile<D>(P, it, (int)(u % Hkv), lane, (int)wslot, ring);
+        run_tile<D, KV8>(P, it, (int)(u % Hkv), lane, (int)wslot, ring);
       if (threadIdx.x == 0) next_unit[k] = pre_claim();
       __syncthreads();
       u = __builtin_amdgcn_readfirstlane(next_unit[k]);
@@ -1228,7 +1363,7 @@ __device__ __forceinline__ void attend_body(const AttendParams& P,
       const uint32_t w = num_pre + idx;
       const WorkItem it = P.items[w / Hkv];
       if (item_ok(P, it) && it.kind == kKindDecode)
-        idx = dec_claimed(run_unit<D, kDecodeColTiles, kDecodeStages, true>(
+        idx = dec_claimed(run_unit<D, kDecodeColTiles, kDecodeStages, true, KV8>(
             P, it, (int)(w % Hkv), lane, &P.hdr->work_counter));
       else
         idx = dec_claimed(claim(&P.hdr->work_counter));
@@ -1254,20 +1389,20 @@ __device__ __forceinline__ void attend_body(const AttendParams& P,
 
 // Decode-only batches: registers for the 3-stage pipeline (two waves per
 // SIMD for head_dim 128, four for 64).
-template <int D>
+template <int D, bool KV8>
 __global__ __launch_bounds__(kAttendThreads)
 __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2, 8)))
 void attend_decode_kernel(AttendParams P) {
-  attend_body<D, false>(P, nullptr);
+  attend_body<D, false, KV8>(P, nullptr);
 }
 
 // Mixed batches: prefill tiles and decode units in the same launch.
-template <int D>
+template <int D, bool KV8>
 __global__ __launch_bounds__(kAttendThreads)
 __attribute__((amdgpu_waves_per_eu(2, 8)))
 void attend_mixed_kernel(AttendParams P) {
-  __shared__ __attribute__((aligned(16))) uint16_t ring[prefill_ring_elems<D>()];
-  attend_body<D, true>(P, ring);
+  __shared__ __attribute__((aligned(16))) uint8_t ring[prefill_ring_bytes<D, KV8>()];
+  attend_body<D, true, KV8>(P, ring);
 }
 
 // ---------------------------------------------------------------------------
@@ -1367,11 +1502,11 @@ __global__ __launch_bounds__(kAttendThreads) void merge_kernel(AttendParams P) {
 // Resident workgroups per CU of a kernel (queried once per device).
 int resident_wgs(const void* fn, int slot) {
   static std::mutex mu;
-  static std::vector<int> cache;  // [device * 4 + slot]
+  static std::vector<int> cache;  // [device * 8 + slot]
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 1;
   std::lock_guard<std::mutex> lock(mu);
-  const size_t idx = (size_t)dev * 4 + slot;
+  const size_t idx = (size_t)dev * 8 + slot;
   if (cache.size() <= idx) cache.resize(idx + 1, 0);
   if (cache[idx] == 0) {
     int n = 0;
@@ -1405,7 +1540,10 @@ AttendParams make_params(const AttendArgs& a) {
   P.G = a.num_q_heads / a.num_kv_heads;
   P.max_query_len = a.max_query_len;
   P.max_seq_len = a.max_seq_len;
-  P.scale_log2 = a.scale * kLog2e;
+  // 8-bit pools: a K code stands for code * k_scale, folded into the score
+  // scale; V's scale is applied to the outputs
+  P.scale_log2 = a.kv8 ? a.scale * a.k_scale * kLog2e : a.scale * kLog2e;
+  P.v_scale = a.kv8 ? a.v_scale : 1.0f;
   P.out = a.out;
   char* ws = static_cast<char*>(a.workspace);
   P.hdr = reinterpret_cast<PlanHeader*>(ws);
@@ -1434,12 +1572,19 @@ hipError_t launch_planned(const AttendArgs& a, hipStream_t stream) {
   void (*fn)(AttendParams);
   int slot;
   if (a.head_dim == 128) {
-    fn = decode_only ? attend_decode_kernel<128> : attend_mixed_kernel<128>;
+    if (a.kv8)
+      fn = decode_only ? attend_decode_kernel<128, true> : attend_mixed_kernel<128, true>;
+    else
+      fn = decode_only ? attend_decode_kernel<128, false> : attend_mixed_kernel<128, false>;
     slot = decode_only ? 0 : 1;
   } else {
-    fn = decode_only ? attend_decode_kernel<64> : attend_mixed_kernel<64>;
+    if (a.kv8)
+      fn = decode_only ? attend_decode_kernel<64, true> : attend_mixed_kernel<64, true>;
+    else
+      fn = decode_only ? attend_decode_kernel<64, false> : attend_mixed_kernel<64, false>;
     slot = decode_only ? 2 : 3;
   }
+  if (a.kv8) slot += 4;
   // Persistent grid: every resident slot of every CU, never more waves than
   // the work-unit bound.
   const int64_t max_work = a.ws.max_items * a.num_kv_heads;

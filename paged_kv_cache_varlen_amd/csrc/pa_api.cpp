@@ -232,6 +232,19 @@ pa_status prepare_attend(const void* q, const void* k_cache,
   a->workspace = workspace;
   a->ws = ws;
   a->num_cus = cus;
+  a->kv8 = false;
+  a->k_scale = 1.0f;
+  a->v_scale = 1.0f;
+  return PA_OK;
+}
+
+// The 8-bit variants: same checks, then the pools' scales.
+pa_status set_fp8(float k_scale, float v_scale, pa::AttendArgs* a) {
+  if (!(k_scale > 0.0f && k_scale <= FLT_MAX) || !(v_scale > 0.0f && v_scale <= FLT_MAX))
+    return fail(PA_ERR_SHAPE, "pa_attend_fp8: scales must be finite and > 0");
+  a->kv8 = true;
+  a->k_scale = k_scale;
+  a->v_scale = v_scale;
   return PA_OK;
 }
 
@@ -331,6 +344,61 @@ pa_status pa_attend(const void* q, const void* k_cache, const void* v_cache,
   if (e == hipSuccess) e = pa::launch_planned(a, static_cast<hipStream_t>(stream));
   if (e == hipSuccess) e = pa::launch_merge(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "pa_attend launch");
+  return ok();
+}
+
+pa_status pa_attend_planned_fp8(const void* q, const void* k_cache,
+                                const void* v_cache, int64_t num_blocks,
+                                const int32_t* block_tables,
+                                int32_t max_blocks_per_seq,
+                                const int32_t* seq_lens,
+                                const int32_t* query_start_loc, int32_t num_seqs,
+                                int64_t num_q_tokens, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim,
+                                int32_t max_query_len, int32_t max_seq_len,
+                                float scale, float k_scale, float v_scale,
+                                void* out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  pa::AttendArgs a;
+  bool empty;
+  pa_status s = prepare_attend(q, k_cache, v_cache, num_blocks, block_tables,
+                               max_blocks_per_seq, seq_lens, query_start_loc,
+                               num_seqs, num_q_tokens, num_q_heads, num_kv_heads,
+                               head_dim, max_query_len, max_seq_len, scale, out,
+                               workspace, workspace_bytes, true, &a, &empty);
+  if (s != PA_OK) return s;
+  if (empty) return ok();
+  s = set_fp8(k_scale, v_scale, &a);
+  if (s != PA_OK) return s;
+  hipError_t e = pa::launch_planned(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pa_attend_planned_fp8 launch");
+  return ok();
+}
+
+pa_status pa_attend_fp8(const void* q, const void* k_cache, const void* v_cache,
+                        int64_t num_blocks, const int32_t* block_tables,
+                        int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                        const int32_t* query_start_loc, int32_t num_seqs,
+                        int64_t num_q_tokens, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim,
+                        int32_t max_query_len, int32_t max_seq_len, float scale,
+                        float k_scale, float v_scale, void* out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  pa::AttendArgs a;
+  bool empty;
+  pa_status s = prepare_attend(q, k_cache, v_cache, num_blocks, block_tables,
+                               max_blocks_per_seq, seq_lens, query_start_loc,
+                               num_seqs, num_q_tokens, num_q_heads, num_kv_heads,
+                               head_dim, max_query_len, max_seq_len, scale, out,
+                               workspace, workspace_bytes, true, &a, &empty);
+  if (s != PA_OK) return s;
+  if (empty) return ok();
+  s = set_fp8(k_scale, v_scale, &a);
+  if (s != PA_OK) return s;
+  hipError_t e = pa::launch_plan(a, static_cast<hipStream_t>(stream));
+  if (e == hipSuccess) e = pa::launch_planned(a, static_cast<hipStream_t>(stream));
+  if (e == hipSuccess) e = pa::launch_merge(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pa_attend_fp8 launch");
   return ok();
 }
 

@@ -170,6 +170,9 @@ struct AttendArgs {
   void* workspace;
   WorkspaceLayout ws;
   int num_cus;
+  bool kv8;        // 8-bit pools: E4M3 codes (k_cache, v_cache are uint8)
+  float k_scale;   // value of a K code: code * k_scale (8-bit pools)
+  float v_scale;   // value of a V code: code * v_scale (8-bit pools)
 };
 
 // Work plan into the workspace (one small kernel).

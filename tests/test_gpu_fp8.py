@@ -102,3 +102,93 @@ def test_write_kv_fp8_strided_rows():
     oracle.write_kv_fp8(okc, ovc, w.k_new, w.v_new, w.new_slots, 0.125, 0.0625)
     assert np.array_equal(u8_bits(kc), okc)
     assert np.array_equal(u8_bits(vc), ovc)
+
+
+# ---- attention over 8-bit pools -----------------------------------------------------
+
+from tests.test_gpu_parity import check_close, sample_rows, to64  # noqa: E402
+from tests.gpu_util import i32, tensor_bits  # noqa: E402
+
+
+def attend8(w, kc, vc, ks, vs, planned=False):
+    bt, sl, qsl = i32(w.block_tables), i32(w.seq_lens), i32(w.query_start_loc)
+    q = bf16_tensor(w.q)
+    ws = pa.alloc_workspace(w.num_seqs, w.num_q_tokens, w.num_q_heads, w.num_kv_heads,
+                            w.head_dim, w.max_query_len, w.max_seq_len)
+    if planned:
+        pa.attend_plan(bt, sl, qsl, w.num_q_tokens, w.num_q_heads, w.num_kv_heads,
+                       w.head_dim, w.max_query_len, w.max_seq_len, ws)
+    out = pa.attend(q, kc, vc, bt, sl, qsl, w.scale, w.max_query_len, w.max_seq_len,
+                    num_kv_heads=w.num_kv_heads, workspace=ws, planned=planned,
+                    k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    return tensor_bits(out)
+
+
+# scales: 1 (codes of N(0,1) data: the 3-bit mantissa, no saturation), the
+# usual amax / 448 choice for N(0,1) data, and a pair that saturates often
+SCALES = [(1.0, 1.0), (0.011, 0.0107), (0.004, 0.0045)]
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+@pytest.mark.parametrize("scales", SCALES)
+def test_attend_fp8_small(name, scales):
+    w = small(name, seed=3)
+    kc, vc = gpu_pool8(w, *scales)
+    got = attend8(w, kc, vc, *scales)
+    okc, ovc = oracle_pool8(w, *scales)
+    ref = oracle.attend_fp8(w.q, okc, ovc, scales[0], scales[1], w.block_tables,
+                            w.seq_lens, w.query_start_loc, w.num_kv_heads, w.scale)
+    check_close(got, ref, "%s fp8 %s" % (name, scales))
+
+
+@pytest.mark.parametrize("name", ["mixed-g4-d128", "mixed-g7-d64", "mixed-split-edge"])
+def test_attend_fp8_planned_equals_unplanned(name):
+    w = small(name, seed=4)
+    kc, vc = gpu_pool8(w, 0.02, 0.03)
+    a = attend8(w, kc, vc, 0.02, 0.03)
+    b = attend8(w, kc, vc, 0.02, 0.03, planned=True)
+    assert np.array_equal(a, b)
+
+
+def test_attend_fp8_block_permutation_is_bit_identical():
+    # outputs depend on logical positions only: a random re-placement of the
+    # physical blocks gives the same bits
+    w = small("mixed-g4-d128", seed=6)
+    kc, vc = gpu_pool8(w, 0.015, 0.012)
+    a = attend8(w, kc, vc, 0.015, 0.012)
+    rng = np.random.default_rng(12)
+    perm = rng.permutation(w.num_blocks)
+    w2 = small("mixed-g4-d128", seed=6)
+    bt = w.block_tables.copy()
+    valid = bt >= 0
+    bt[valid] = perm[bt[valid]]
+    w2.block_tables = bt
+    rel = lambda s: np.where(s >= 0, perm[s // 16] * 16 + s % 16, s)  # noqa: E731
+    w2.fill_slots = rel(w.fill_slots)
+    w2.new_slots = rel(w.new_slots)
+    kc2, vc2 = gpu_pool8(w2, 0.015, 0.012)
+    b = attend8(w2, kc2, vc2, 0.015, 0.012)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 5])
+def test_config_parity_fp8(k):
+    w = W.make_config(k)
+    ks, vs = 0.011, 0.0107
+    kc, vc = gpu_pool8(w, ks, vs)
+    got = attend8(w, kc, vc, ks, vs)
+    assert np.isfinite(to64(got)).all()
+    okc, ovc = oracle_pool8(w, ks, vs)
+    if k <= 2:
+        assert np.array_equal(u8_bits(kc), okc)
+        assert np.array_equal(u8_bits(vc), ovc)
+    if k == 1:
+        ref = oracle.attend_fp8(w.q, okc, ovc, ks, vs, w.block_tables, w.seq_lens,
+                                w.query_start_loc, w.num_kv_heads, w.scale)
+        check_close(got, ref, "config 1 fp8")
+        return
+    rows = sample_rows(w, {2: 192, 3: 192, 5: 64}[k], seed=200 + k)
+    ref = oracle.attend_fp8(w.q, okc, ovc, ks, vs, w.block_tables, w.seq_lens,
+                            w.query_start_loc, w.num_kv_heads, w.scale, rows=rows)
+    check_close(got[rows[:, 0], rows[:, 1]], ref, "config %d fp8 (%d rows)" % (k, len(rows)))
