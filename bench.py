@@ -23,6 +23,9 @@ Prints one JSON line:
            peak;
   decode_part  that step's 128 decodes alone: attention kernel GB/s against
            the HBM peak;
+  fp8_kv   the 8-bit (E4M3) KV cache beside bf16 on the headline decode
+           layer and the 70B-class long-context layer: step time, decode
+           tokens/s, attention GB/s of code bytes;
   cpu_baseline  the CPU oracle (fp64) on the same headline workload.
 
     python bench.py [--steps K] [--warmup W] [--config 2] [--no-mixed]
@@ -124,13 +127,24 @@ def algorithmic(w):
 class Runner:
     """Pools for several simulated layers plus the step's inputs, on the GPU."""
 
-    def __init__(self, w, min_ws_gib):
+    def __init__(self, w, min_ws_gib, fp8=None):
+        """fp8: None for bf16 pools, or (k_scale, v_scale) for 8-bit pools
+        written by pa_write_kv_fp8."""
         import torch
         import paged_kv_cache_varlen_amd as pa
-        from tests.gpu_util import Uploaded
-        self.torch, self.pa, self.w = torch, pa, w
+        from tests.gpu_util import Uploaded, bf16_tensor, i64
+        self.torch, self.pa, self.w, self.fp8 = torch, pa, w, fp8
         base = Uploaded(w, sentinel=False)
-        pool_bytes = 2 * base.k_cache.numel() * 2
+        if fp8 is not None:
+            k8, v8 = pa.alloc_pool_fp8(w.num_blocks, w.num_kv_heads, w.head_dim, fill=0)
+            step = 1 << 18  # bounded host->device staging
+            for s0 in range(0, len(w.fill_rows), step):
+                rows = w.fill_rows[s0:s0 + step]
+                pa.write_kv_fp8(bf16_tensor(w.k_dense[rows]), bf16_tensor(w.v_dense[rows]),
+                                i64(w.fill_slots[s0:s0 + step]), k8, v8, *fp8)
+            pa.write_kv_fp8(base.k_new, base.v_new, base.new_slots, k8, v8, *fp8)
+            base.k_cache, base.v_cache = k8, v8
+        pool_bytes = 2 * base.k_cache.numel() * base.k_cache.element_size()
         n = max(1, min(8, int(np.ceil(min_ws_gib * 2**30 / pool_bytes))))
         self.layers = [(base.k_cache, base.v_cache)]
         for _ in range(n - 1):
@@ -138,13 +152,24 @@ class Runner:
         self.u = base
         self.stream = torch.cuda.current_stream()
 
+    def attend(self, kc, vc):
+        w, u = self.w, self.u
+        scales = {} if self.fp8 is None else dict(k_scale=self.fp8[0], v_scale=self.fp8[1])
+        self.pa.attend(u.q, kc, vc, u.block_tables, u.seq_lens, u.qsl, w.scale,
+                       w.max_query_len, w.max_seq_len, num_kv_heads=w.num_kv_heads,
+                       out=u.out, workspace=u.workspace, planned=True, merge=False,
+                       **scales)
+
     def step(self, i):
         """write_kv + plan + attention + merge for one layer."""
         pa, u = self.pa, self.u
         kc, vc = self.layers[i % len(self.layers)]
-        pa.write_kv(u.k_new, u.v_new, u.new_slots, kc, vc)
+        if self.fp8 is None:
+            pa.write_kv(u.k_new, u.v_new, u.new_slots, kc, vc)
+        else:
+            pa.write_kv_fp8(u.k_new, u.v_new, u.new_slots, kc, vc, *self.fp8)
         u.plan()
-        u.attend(k_cache=kc, v_cache=vc, planned=True, merge=False)
+        self.attend(kc, vc)
         u.merge()
 
     def run(self, steps, warmup):
@@ -172,7 +197,7 @@ class Runner:
         for r in range(runs):
             evs[r][0].record(self.stream)
             for kc, vc in self.layers:
-                self.u.attend(k_cache=kc, v_cache=vc, planned=True, merge=False)
+                self.attend(kc, vc)
             evs[r][1].record(self.stream)
         torch.cuda.synchronize()
         attend_ms = float(np.mean([a.elapsed_time(b) for a, b in evs])) / n
@@ -237,6 +262,33 @@ def cpu_baseline(w, min_s=10.0, max_s=30.0, min_s1=3.0, max_s1=8.0):
                       "oracle with OpenMP, %.1f s; one thread: %d sequences, %.1f s"
                       % (done_seqs, done_seqs / w.num_seqs, w.num_seqs,
                          w.num_q_heads, spent, seqs1, spent1)}
+
+
+FP8_SCALES = (0.011, 0.0107)  # amax / 448 for N(0,1) bf16 data
+
+
+def fp8_runs(args, W):
+    """8-bit (E4M3) KV cache on the headline decode layer and the 70B-class
+    long-context layer: the step's tokens/s and the attention kernel's GB/s of
+    code bytes, beside the same workload on bf16 pools."""
+    import torch
+    out = {"scales": list(FP8_SCALES), "format": "OCP E4M3, one fp32 scale per pool"}
+    for key, w in (("decode_8b", W.make_config(2)), ("decode_70b_32k", W.make_config(5))):
+        alg = algorithmic(w)
+        res = {"workload": w.name}
+        for kind, fp8 in (("bf16", None), ("fp8", FP8_SCALES)):
+            r = Runner(w, args.min_working_set_gib, fp8=fp8)
+            ms, att = r.run(max(20, args.steps // 4), max(5, args.warmup // 2))
+            kv = alg["kv_bytes"] / (2 if fp8 else 1)
+            res[kind] = {"ms_per_step": round(ms, 5), "attend_ms": round(att, 5),
+                         "decode_tokens_per_s": round(w.num_q_tokens / (ms * 1e-3), 1),
+                         "attend_kv_gbs": round(kv / (att * 1e-3) / 1e9, 2),
+                         "hbm_peak_frac": round(kv / (att * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            del r
+            torch.cuda.empty_cache()
+        res["step_speedup"] = round(res["bf16"]["ms_per_step"] / res["fp8"]["ms_per_step"], 3)
+        out[key] = res
+    return out
 
 
 def read_ceiling(torch, gib=4):
@@ -371,6 +423,7 @@ def main():
             "attend_gbs": round(gbs, 2), "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4)}
         del rd
         torch.cuda.empty_cache()
+        line["fp8_kv"] = fp8_runs(args, W)
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)

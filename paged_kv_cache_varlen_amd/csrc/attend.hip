@@ -1388,10 +1388,11 @@ __device__ __forceinline__ void attend_body(const AttendParams& P,
 }
 
 // Decode-only batches: registers for the 3-stage pipeline (two waves per
-// SIMD for head_dim 128, four for 64).
+// SIMD for head_dim 128, four for 64; three for 128 with 8-bit pools, whose
+// blocks take half the registers).
 template <int D, bool KV8>
 __global__ __launch_bounds__(kAttendThreads)
-__attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2, 8)))
+__attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : (KV8 ? 3 : 2), 8)))
 void attend_decode_kernel(AttendParams P) {
   attend_body<D, false, KV8>(P, nullptr);
 }
