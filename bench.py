@@ -345,8 +345,8 @@ def main():
     alg = algorithmic(w)
     r = Runner(w, args.min_working_set_gib)
     ms_step, attend_ms = r.run(args.steps, args.warmup)
-    kernel = ("attend_decode_kernel<%d>" if w.max_query_len <= 16 // (
-        w.num_q_heads // w.num_kv_heads) else "attend_mixed_kernel<%d>") % w.head_dim
+    kernel = ("attend_decode_kernel<%d, false>" if w.max_query_len <= 16 // (
+        w.num_q_heads // w.num_kv_heads) else "attend_mixed_kernel<%d, false>") % w.head_dim
     kv_gbs = alg["kv_bytes"] / (ms_step * 1e-3) / 1e9
     achieved = alg["attend_bytes"] / (attend_ms * 1e-3) / 1e9
     line = {
