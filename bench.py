@@ -26,6 +26,9 @@ Prints one JSON line:
   fp8_kv   the 8-bit (E4M3) KV cache beside bf16 on the headline decode
            layer and the 70B-class long-context layer: step time, decode
            tokens/s, attention GB/s of code bytes;
+  shared_prefix  256 decodes sharing a 2048-token prefix: plain paged
+           attention beside shared-prefix (cascade) attention, GB/s of the
+           logical and of the unique K/V bytes;
   cpu_baseline  the CPU oracle (fp64) on the same headline workload.
 
     python bench.py [--steps K] [--warmup W] [--config 2] [--no-mixed]
@@ -60,6 +63,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the streaming-read ceiling probe")
+    ap.add_argument("--cascade", action="store_true",
+                    help="time the workload's shared-prefix attention calls "
+                         "(config 4: the 2048-token prefix attended once)")
     ap.add_argument("--min-working-set-gib", type=float, default=2.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run 5 plain 1 GiB device-to-device copies (the "
@@ -127,14 +133,21 @@ def algorithmic(w):
 class Runner:
     """Pools for several simulated layers plus the step's inputs, on the GPU."""
 
-    def __init__(self, w, min_ws_gib, fp8=None):
+    def __init__(self, w, min_ws_gib, fp8=None, cascade=None):
         """fp8: None for bf16 pools, or (k_scale, v_scale) for 8-bit pools
-        written by pa_write_kv_fp8."""
+        written by pa_write_kv_fp8.  cascade: None, or the shared prefix
+        length for shared-prefix attention (plan, attention and merge of the
+        shared-prefix calls)."""
         import torch
         import paged_kv_cache_varlen_amd as pa
         from tests.gpu_util import Uploaded, bf16_tensor, i64
         self.torch, self.pa, self.w, self.fp8 = torch, pa, w, fp8
+        self.cascade = cascade
         base = Uploaded(w, sentinel=False)
+        if cascade is not None:
+            base.workspace = pa.alloc_workspace(
+                w.num_seqs, w.num_q_tokens, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                w.max_query_len, w.max_seq_len, cascade=True)
         if fp8 is not None:
             k8, v8 = pa.alloc_pool_fp8(w.num_blocks, w.num_kv_heads, w.head_dim, fill=0)
             step = 1 << 18  # bounded host->device staging
@@ -158,7 +171,18 @@ class Runner:
         self.pa.attend(u.q, kc, vc, u.block_tables, u.seq_lens, u.qsl, w.scale,
                        w.max_query_len, w.max_seq_len, num_kv_heads=w.num_kv_heads,
                        out=u.out, workspace=u.workspace, planned=True, merge=False,
-                       **scales)
+                       common_prefix_len=self.cascade, **scales)
+
+    def plan(self):
+        w, u = self.w, self.u
+        self.pa.attend_plan(u.block_tables, u.seq_lens, u.qsl, w.num_q_tokens,
+                            w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_query_len,
+                            w.max_seq_len, u.workspace, common_prefix_len=self.cascade)
+
+    def merge(self):
+        w, u = self.w, self.u
+        self.pa.attend_merge(u.out, w.num_seqs, w.num_kv_heads, w.max_query_len,
+                             w.max_seq_len, u.workspace, cascade=self.cascade is not None)
 
     def step(self, i):
         """write_kv + plan + attention + merge for one layer."""
@@ -168,9 +192,9 @@ class Runner:
             pa.write_kv(u.k_new, u.v_new, u.new_slots, kc, vc)
         else:
             pa.write_kv_fp8(u.k_new, u.v_new, u.new_slots, kc, vc, *self.fp8)
-        u.plan()
+        self.plan()
         self.attend(kc, vc)
-        u.merge()
+        self.merge()
 
     def run(self, steps, warmup):
         """Time `steps` whole steps (nothing but the step's own launches
@@ -193,7 +217,7 @@ class Runner:
         runs = max(1, steps // n)
         evs = [(torch.cuda.Event(enable_timing=True),
                 torch.cuda.Event(enable_timing=True)) for _ in range(runs)]
-        self.u.plan()
+        self.plan()
         for r in range(runs):
             evs[r][0].record(self.stream)
             for kc, vc in self.layers:
@@ -291,6 +315,38 @@ def fp8_runs(args, W):
     return out
 
 
+def unique_kv_bytes(w):
+    """K+V bytes of the distinct tokens a shared-prefix batch holds: the
+    prefix once, then every request's own tokens."""
+    C = int(w.shared_prefix)
+    toks = C + int((w.seq_lens.astype(np.int64) - C).sum())
+    return toks * 2 * w.num_kv_heads * w.head_dim * 2
+
+
+def shared_prefix_runs(args, W):
+    """The shared-prefix decode layer (256 requests, 2048-token prefix): plain
+    paged attention and shared-prefix attention, whole step and attention
+    kernel, with the attention's GB/s of logical (per request) and unique
+    K/V bytes."""
+    import torch
+    w = W.make_config(4)
+    alg = algorithmic(w)
+    uniq = unique_kv_bytes(w)
+    out = {"workload": w.name, "prefix_tokens": int(w.shared_prefix),
+           "logical_kv_bytes": alg["kv_bytes"], "unique_kv_bytes": uniq}
+    for kind, casc in (("plain", None), ("cascade", int(w.shared_prefix))):
+        r = Runner(w, args.min_working_set_gib, cascade=casc)
+        ms, att = r.run(max(20, args.steps // 4), max(5, args.warmup // 2))
+        out[kind] = {"ms_per_step": round(ms, 5), "attend_ms": round(att, 5),
+                     "decode_tokens_per_s": round(w.num_q_tokens / (ms * 1e-3), 1),
+                     "attend_logical_gbs": round(alg["kv_bytes"] / (att * 1e-3) / 1e9, 2),
+                     "attend_unique_gbs": round(uniq / (att * 1e-3) / 1e9, 2)}
+        del r
+        torch.cuda.empty_cache()
+    out["step_speedup"] = round(out["plain"]["ms_per_step"] / out["cascade"]["ms_per_step"], 3)
+    return out
+
+
 def read_ceiling(torch, gib=4):
     """Measured streaming-read ceiling of this box: the best of a few grid
     sizes of the probe kernel (libpa_probe.so) reading a 4 GiB buffer once
@@ -343,11 +399,19 @@ def main():
 
     w = W.make_prefill_chunk() if args.config == "p" else W.make_config(int(args.config))
     alg = algorithmic(w)
-    r = Runner(w, args.min_working_set_gib)
+    casc = int(w.shared_prefix) if args.cascade else None
+    if args.cascade and not casc:
+        print("--cascade needs a workload with a shared prefix (config 4)", file=sys.stderr)
+        return 2
+    r = Runner(w, args.min_working_set_gib, cascade=casc)
     ms_step, attend_ms = r.run(args.steps, args.warmup)
-    kernel = ("attend_decode_kernel<%d, false>" if w.max_query_len <= 16 // (
+    kernel = ("attend_decode_kernel<%d, false>" if casc is None and w.max_query_len <= 16 // (
         w.num_q_heads // w.num_kv_heads) else "attend_mixed_kernel<%d, false>") % w.head_dim
     kv_gbs = alg["kv_bytes"] / (ms_step * 1e-3) / 1e9
+    if casc:
+        # shared-prefix attention reads the prefix once: its algorithmic
+        # bytes are the distinct tokens' K/V (plus the same q, out, metadata)
+        alg["attend_bytes"] += unique_kv_bytes(w) - alg["kv_bytes"]
     achieved = alg["attend_bytes"] / (attend_ms * 1e-3) / 1e9
     line = {
         "metric": "paged-attn KV read GB/s (% HBM peak) + mixed-step tokens/s per layer",
@@ -363,7 +427,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16 q/K/V, seeded block tables)",
-        "config": dict(W.Workload.describe(w), layers_cycled=len(r.layers)),
+        "config": dict(W.Workload.describe(w), layers_cycled=len(r.layers),
+                       **({"shared_prefix_attention": casc} if casc else {})),
         "decode_tokens_per_s": round(w.num_q_tokens / (ms_step * 1e-3), 1),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
@@ -424,6 +489,7 @@ def main():
         del rd
         torch.cuda.empty_cache()
         line["fp8_kv"] = fp8_runs(args, W)
+        line["shared_prefix"] = shared_prefix_runs(args, W)
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)

@@ -315,6 +315,129 @@ pa_status pa_attend_planned_fp8(const void *q, const void *k_cache,
                                 size_t workspace_bytes, void *stream);
 
 /*
+ * Shared-prefix (cascade) attention: pa_attend for a batch whose requests all
+ * begin with the same common_prefix_len keys.  The prefix is attended once
+ * for every query token of the batch (tiles of consecutive query tokens of
+ * all requests against the prefix's blocks, read once instead of once per
+ * request) and each request's own keys separately; the two results of every
+ * row are combined by the split-K merge (log-sum-exp renormalisation).
+ * Source: "vLLM: An Exhaustive Technical Study", section 2.3 (cascade
+ * attention: the shared prefix computed once, merged with each request's
+ * suffix by log-sum-exp renormalisation; metadata common_prefix_len).
+ *
+ * Result: the same attention as pa_attend (one more split point per row, so
+ * equal up to fp32 rounding order, within the same tolerance of the exact
+ * result).  The reduction order of a row depends only on its request's
+ * (Q_b, L_b), its logical key positions and common_prefix_len.
+ *
+ * Requirements on the batch (content; check with pa_validate_cascade_host):
+ *   - every request b holds the prefix and queries only past it:
+ *     seq_lens[b] - Q_b >= common_prefix_len (requests that break this are
+ *     skipped: their rows are not written, PA_OK is still returned);
+ *   - the prefix's whole blocks are the same in every table: the prefix is
+ *     read through request 0's row.
+ * The library shares the largest multiple of 32 keys not above
+ * common_prefix_len (0: plain pa_attend through the shared-prefix path);
+ * 0 <= common_prefix_len <= max_seq_len (PA_ERR_SHAPE otherwise).
+ *
+ * pa_attend_cascade_workspace_size - workspace bytes of the shared-prefix
+ *   calls (the pa_attend workspace plus a prefix section for up to 8 prefix
+ *   key ranges per query token).  0 for invalid arguments.
+ * pa_attend_cascade, pa_attend_cascade_fp8 - plan + attention + merge, over
+ *   bf16 or 8-bit pools (arguments as pa_attend / pa_attend_fp8 plus
+ *   common_prefix_len).
+ * pa_attend_plan_cascade, pa_attend_planned_cascade(_fp8),
+ *   pa_attend_merge_cascade - the same in three calls, as pa_attend_plan,
+ *   pa_attend_planned(_fp8) and pa_attend_merge (one plan for every layer).
+ *   A shared-prefix plan is run only by these calls and a plain plan only by
+ *   the plain ones (the other kind is detected on the device and nothing is
+ *   written).
+ * All of them: workspace >= pa_attend_cascade_workspace_size(...) bytes
+ * (PA_ERR_WORKSPACE otherwise); other arguments and errors as pa_attend.
+ */
+size_t pa_attend_cascade_workspace_size(int32_t num_seqs, int64_t num_q_tokens,
+                                        int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t max_query_len,
+                                        int32_t max_seq_len);
+
+pa_status pa_attend_cascade(const void *q, const void *k_cache,
+                            const void *v_cache, int64_t num_blocks,
+                            const int32_t *block_tables,
+                            int32_t max_blocks_per_seq, const int32_t *seq_lens,
+                            const int32_t *query_start_loc, int32_t num_seqs,
+                            int64_t num_q_tokens, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim,
+                            int32_t max_query_len, int32_t max_seq_len,
+                            int32_t common_prefix_len, float scale, void *out,
+                            void *workspace, size_t workspace_bytes,
+                            void *stream);
+
+pa_status pa_attend_cascade_fp8(const void *q, const void *k_cache,
+                                const void *v_cache, int64_t num_blocks,
+                                const int32_t *block_tables,
+                                int32_t max_blocks_per_seq,
+                                const int32_t *seq_lens,
+                                const int32_t *query_start_loc, int32_t num_seqs,
+                                int64_t num_q_tokens, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim,
+                                int32_t max_query_len, int32_t max_seq_len,
+                                int32_t common_prefix_len, float scale,
+                                float k_scale, float v_scale, void *out,
+                                void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+pa_status pa_attend_plan_cascade(const int32_t *block_tables,
+                                 int32_t max_blocks_per_seq,
+                                 const int32_t *seq_lens,
+                                 const int32_t *query_start_loc, int32_t num_seqs,
+                                 int64_t num_q_tokens, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t max_query_len, int32_t max_seq_len,
+                                 int32_t common_prefix_len, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
+pa_status pa_attend_planned_cascade(const void *q, const void *k_cache,
+                                    const void *v_cache, int64_t num_blocks,
+                                    const int32_t *block_tables,
+                                    int32_t max_blocks_per_seq,
+                                    const int32_t *seq_lens,
+                                    const int32_t *query_start_loc,
+                                    int32_t num_seqs, int64_t num_q_tokens,
+                                    int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t max_query_len,
+                                    int32_t max_seq_len, float scale, void *out,
+                                    void *workspace, size_t workspace_bytes,
+                                    void *stream);
+
+pa_status pa_attend_planned_cascade_fp8(
+    const void *q, const void *k_cache, const void *v_cache, int64_t num_blocks,
+    const int32_t *block_tables, int32_t max_blocks_per_seq,
+    const int32_t *seq_lens, const int32_t *query_start_loc, int32_t num_seqs,
+    int64_t num_q_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t max_query_len, int32_t max_seq_len, float scale,
+    float k_scale, float v_scale, void *out, void *workspace,
+    size_t workspace_bytes, void *stream);
+
+pa_status pa_attend_merge_cascade(int32_t num_seqs, int64_t num_q_tokens,
+                                  int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t max_query_len,
+                                  int32_t max_seq_len, void *out, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/*
+ * pa_validate_cascade_host - host check of the shared-prefix requirements
+ * above on HOST arrays: PA_ERR_METADATA (detail in pa_last_error()) when a
+ * request has seq_lens[b] - Q_b < common_prefix_len, or when one of the
+ * first common_prefix_len / 16 block-table entries of a request differs from
+ * request 0's (or the row is shorter than that).
+ */
+pa_status pa_validate_cascade_host(const int32_t *block_tables,
+                                   int32_t max_blocks_per_seq,
+                                   const int32_t *seq_lens,
+                                   const int32_t *query_start_loc,
+                                   int32_t num_seqs, int32_t common_prefix_len);
+
+/*
  * pa_gather_kv - logical gather through the block tables (a checking aid).
  *
  * Writes k_out/v_out, device bf16 [sum_b L_b][num_kv_heads][head_dim]: row

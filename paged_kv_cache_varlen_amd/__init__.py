@@ -146,25 +146,30 @@ def write_kv_fp8(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
 
 def workspace_size(num_seqs: int, num_q_tokens: int, num_q_heads: int,
                    num_kv_heads: int, head_dim: int, max_query_len: int,
-                   max_seq_len: int) -> int:
-    n = _lib.load().pa_attend_workspace_size(num_seqs, num_q_tokens, num_q_heads,
-                                            num_kv_heads, head_dim,
-                                            max_query_len, max_seq_len)
+                   max_seq_len: int, cascade: bool = False) -> int:
+    """Workspace bytes of pa_attend (cascade=True: of the shared-prefix calls,
+    which add a prefix section)."""
+    name = "pa_attend_cascade_workspace_size" if cascade else "pa_attend_workspace_size"
+    n = getattr(_lib.load(), name)(num_seqs, num_q_tokens, num_q_heads,
+                                   num_kv_heads, head_dim, max_query_len,
+                                   max_seq_len)
     if n == 0:
-        raise ValueError("invalid arguments for pa_attend_workspace_size")
+        raise ValueError("invalid arguments for " + name)
     return int(n)
 
 
 def alloc_workspace(num_seqs, num_q_tokens, num_q_heads, num_kv_heads, head_dim,
-                    max_query_len, max_seq_len, device="cuda") -> torch.Tensor:
+                    max_query_len, max_seq_len, device="cuda",
+                    cascade: bool = False) -> torch.Tensor:
     n = workspace_size(num_seqs, num_q_tokens, num_q_heads, num_kv_heads,
-                       head_dim, max_query_len, max_seq_len)
+                       head_dim, max_query_len, max_seq_len, cascade=cascade)
     # torch's caching allocator returns 512-byte aligned blocks
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def _attend_args(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
-                 num_kv_heads, out, workspace, max_query_len, max_seq_len):
+                 num_kv_heads, out, workspace, max_query_len, max_seq_len,
+                 cascade=False):
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
                  (block_tables, "block_tables"), (seq_lens, "seq_lens"),
                  (query_start_loc, "query_start_loc")):
@@ -200,7 +205,7 @@ def _attend_args(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
             raise ValueError("out must be contiguous and shaped like q")
     if workspace is None:
         workspace = alloc_workspace(B, T, Hq, num_kv_heads, D, max_query_len,
-                                    max_seq_len, device=q.device)
+                                    max_seq_len, device=q.device, cascade=cascade)
     return T, Hq, D, num_kv_heads, nb, B, out, workspace
 
 
@@ -211,7 +216,8 @@ def attend(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
            out: Optional[torch.Tensor] = None,
            workspace: Optional[torch.Tensor] = None,
            planned: bool = False, merge: bool = True,
-           k_scale: float = 1.0, v_scale: float = 1.0) -> torch.Tensor:
+           k_scale: float = 1.0, v_scale: float = 1.0,
+           common_prefix_len: Optional[int] = None) -> torch.Tensor:
     """Paged varlen causal attention of every query row of a mixed batch.
 
     q [T][Hq][D] bf16; block_tables [B][max_blocks] int32; seq_lens [B] int32;
@@ -221,59 +227,97 @@ def attend(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     With planned=True the work plan already in ``workspace`` (from attend_plan
     with the same metadata) is used: the attention kernel is enqueued, then
     (with merge=True, the default) the split-K merge kernel; merge=False
-    leaves the merge to a later attend_merge call."""
+    leaves the merge to a later attend_merge call.
+
+    common_prefix_len (shared-prefix attention): every request's first
+    common_prefix_len keys are the same blocks (request 0's table is the one
+    read) and every query lies past them; the prefix is then attended once
+    for the whole batch and merged with each request's own keys.  Needs a
+    workspace from alloc_workspace(..., cascade=True) (allocated here when
+    none is given); with planned=True the plan must come from
+    attend_plan(..., common_prefix_len=...)."""
+    cascade = common_prefix_len is not None
     T, Hq, D, Hkv, nb, B, out, workspace = _attend_args(
         q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
-        num_kv_heads, out, workspace, max_query_len, max_seq_len)
+        num_kv_heads, out, workspace, max_query_len, max_seq_len, cascade)
     lib = _lib.load()
     args = [_ptr(q), _ptr(k_cache), _ptr(v_cache), nb, _ptr(block_tables),
             block_tables.shape[1], _ptr(seq_lens), _ptr(query_start_loc), B, T,
-            Hq, Hkv, D, int(max_query_len), int(max_seq_len), float(scale)]
-    if k_cache.dtype == torch.uint8:
-        name = "pa_attend_planned_fp8" if planned else "pa_attend_fp8"
+            Hq, Hkv, D, int(max_query_len), int(max_seq_len)]
+    if cascade and not planned:
+        args.append(int(common_prefix_len))
+    args.append(float(scale))
+    fp8 = k_cache.dtype == torch.uint8
+    if fp8:
         args += [float(k_scale), float(v_scale)]
-    else:
-        name = "pa_attend_planned" if planned else "pa_attend"
+    name = "pa_attend" + ("_planned" if planned else "") + ("_cascade" if cascade else "") \
+        + ("_fp8" if fp8 else "")
     st = getattr(lib, name)(*args, _ptr(out), _ptr(workspace), workspace.numel(),
                             _stream(q))
     _lib.check(st, name)
     if planned and merge:
-        attend_merge(out, B, Hkv, max_query_len, max_seq_len, workspace)
+        attend_merge(out, B, Hkv, max_query_len, max_seq_len, workspace,
+                     cascade=cascade)
     return out
 
 
 def attend_merge(out: torch.Tensor, num_seqs: int, num_kv_heads: int,
                  max_query_len: int, max_seq_len: int,
-                 workspace: torch.Tensor) -> None:
+                 workspace: torch.Tensor, cascade: bool = False) -> None:
     """Enqueue the split-K merge after attend(..., planned=True, merge=False)."""
     _need_cuda(out, "out")
     T, Hq, D = out.shape
-    st = _lib.load().pa_attend_merge(int(num_seqs), T, Hq, int(num_kv_heads), D,
-                                     int(max_query_len), int(max_seq_len),
-                                     _ptr(out), _ptr(workspace), workspace.numel(),
-                                     _stream(out))
-    _lib.check(st, "pa_attend_merge")
+    name = "pa_attend_merge_cascade" if cascade else "pa_attend_merge"
+    st = getattr(_lib.load(), name)(int(num_seqs), T, Hq, int(num_kv_heads), D,
+                                    int(max_query_len), int(max_seq_len),
+                                    _ptr(out), _ptr(workspace), workspace.numel(),
+                                    _stream(out))
+    _lib.check(st, name)
 
 
 def attend_plan(block_tables: torch.Tensor, seq_lens: torch.Tensor,
                 query_start_loc: torch.Tensor, num_q_tokens: int,
                 num_q_heads: int, num_kv_heads: int, head_dim: int,
                 max_query_len: int, max_seq_len: int,
-                workspace: torch.Tensor) -> None:
+                workspace: torch.Tensor,
+                common_prefix_len: Optional[int] = None) -> None:
     """Enqueue only the work plan of pa_attend into ``workspace``; follow
-    with attend(..., planned=True) for each layer that shares the metadata."""
+    with attend(..., planned=True) for each layer that shares the metadata
+    (with common_prefix_len: a shared-prefix plan, run by
+    attend(..., planned=True, common_prefix_len=...))."""
     for t, n in ((block_tables, "block_tables"), (seq_lens, "seq_lens"),
                  (query_start_loc, "query_start_loc"), (workspace, "workspace")):
         _need_cuda(t, n)
     B = block_tables.shape[0]
     lib = _lib.load()
-    st = lib.pa_attend_plan(_ptr(block_tables), block_tables.shape[1],
-                            _ptr(seq_lens), _ptr(query_start_loc), B,
-                            int(num_q_tokens), int(num_q_heads),
-                            int(num_kv_heads), int(head_dim), int(max_query_len),
-                            int(max_seq_len), _ptr(workspace), workspace.numel(),
+    args = [_ptr(block_tables), block_tables.shape[1], _ptr(seq_lens),
+            _ptr(query_start_loc), B, int(num_q_tokens), int(num_q_heads),
+            int(num_kv_heads), int(head_dim), int(max_query_len), int(max_seq_len)]
+    if common_prefix_len is None:
+        name = "pa_attend_plan"
+    else:
+        name = "pa_attend_plan_cascade"
+        args.append(int(common_prefix_len))
+    st = getattr(lib, name)(*args, _ptr(workspace), workspace.numel(),
                             _stream(workspace))
-    _lib.check(st, "pa_attend_plan")
+    _lib.check(st, name)
+
+
+def validate_cascade(block_tables, seq_lens, query_start_loc,
+                     common_prefix_len: int) -> None:
+    """Host check of a shared-prefix batch (every query past the prefix, the
+    prefix's whole blocks the same in every table); raises PAError.  Takes
+    host arrays (numpy or CPU tensors)."""
+    import numpy as np
+    bt = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
+    sl = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    qsl = np.ascontiguousarray(np.asarray(query_start_loc, dtype=np.int32))
+    if bt.ndim != 2 or sl.shape != (bt.shape[0],) or qsl.shape != (bt.shape[0] + 1,):
+        raise ValueError("block_tables [B][max_blocks], seq_lens [B], query_start_loc [B+1]")
+    st = _lib.load().pa_validate_cascade_host(
+        bt.ctypes.data, bt.shape[1], sl.ctypes.data, qsl.ctypes.data, bt.shape[0],
+        int(common_prefix_len))
+    _lib.check(st, "pa_validate_cascade_host")
 
 
 def gather_kv(k_cache: torch.Tensor, v_cache: torch.Tensor,

@@ -38,6 +38,23 @@ SIGNATURES = {
     "pa_attend_planned_fp8": (STATUS, [P, P, P, I64, P, I32, P, P, I32, I64, I32,
                                        I32, I32, I32, I32, F32, F32, F32, P, P, SZ,
                                        P]),
+    "pa_attend_cascade_workspace_size": (SZ, [I32, I64, I32, I32, I32, I32, I32]),
+    "pa_attend_plan_cascade": (STATUS, [P, I32, P, P, I32, I64, I32, I32, I32, I32,
+                                        I32, I32, P, SZ, P]),
+    "pa_attend_planned_cascade": (STATUS, [P, P, P, I64, P, I32, P, P, I32, I64,
+                                           I32, I32, I32, I32, I32, F32, P, P, SZ,
+                                           P]),
+    "pa_attend_planned_cascade_fp8": (STATUS, [P, P, P, I64, P, I32, P, P, I32, I64,
+                                               I32, I32, I32, I32, I32, F32, F32,
+                                               F32, P, P, SZ, P]),
+    "pa_attend_merge_cascade": (STATUS, [I32, I64, I32, I32, I32, I32, I32, P, P, SZ,
+                                         P]),
+    "pa_attend_cascade": (STATUS, [P, P, P, I64, P, I32, P, P, I32, I64, I32, I32,
+                                   I32, I32, I32, I32, F32, P, P, SZ, P]),
+    "pa_attend_cascade_fp8": (STATUS, [P, P, P, I64, P, I32, P, P, I32, I64, I32,
+                                       I32, I32, I32, I32, I32, F32, F32, F32, P, P,
+                                       SZ, P]),
+    "pa_validate_cascade_host": (STATUS, [P, I32, P, P, I32, I32]),
     "pa_gather_kv": (STATUS, [P, P, I64, P, I32, P, P, I32, I64, I32, I32, P, P,
                               P]),
     "pa_validate_metadata_host": (STATUS, [P, I32, P, P, I32, I64, I32, I32, I64,

@@ -88,6 +88,13 @@ struct AttendParams {
   float* part_acc;
   int64_t max_items;
   int64_t max_partials;
+  // shared-prefix section (null / 0 unless the workspace holds one)
+  WorkItem* pitems;
+  float2* pre_ml;
+  float* pre_acc;
+  int64_t max_pre_items;
+  int64_t max_pre_partials;
+  int32_t prefix_len;  // plan: keys every request shares (0: none)
 };
 
 // ---------------------------------------------------------------------------
@@ -100,11 +107,11 @@ struct AttendParams {
 // of the launch that reads it.)
 __device__ __forceinline__ uint32_t plan_signature(const AttendParams& P) {
   uint32_t h = 2166136261u;
-  const int32_t v[8] = {P.num_seqs, P.num_q_tokens, P.Hq, P.Hkv,
+  const int32_t v[9] = {P.num_seqs, P.num_q_tokens, P.Hq, P.Hkv,
                         P.max_query_len, P.max_seq_len, (int32_t)P.max_items,
-                        (int32_t)P.max_partials};
+                        (int32_t)P.max_partials, (int32_t)P.max_pre_items};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) h = (h ^ (uint32_t)v[i]) * 16777619u;
+  for (int i = 0; i < 9; ++i) h = (h ^ (uint32_t)v[i]) * 16777619u;
   return h;
 }
 
@@ -142,21 +149,31 @@ __device__ SeqCounts seq_counts(const AttendParams& P, int b) {
     return c;
   }
   if (Q == 0) return c;
+  // With a shared prefix of C keys (cascade plan) the request's own items
+  // cover keys C .. and every tile merges, since the prefix items add
+  // partials to each of its tokens; its queries must all lie past the prefix.
+  const int C = P.prefix_len;
+  const bool casc = C > 0;
+  if (L - Q < C) {
+    atomicOr(&P.hdr->error, 2u);
+    return c;
+  }
   if (Q <= decode_tile_tokens(P.G)) {
     c.kind = kKindDecode;
     c.ntiles = 1;
     c.tq = Q;
-    c.splitlen = L > kLongDecode ? kSplitDecodeLong : kSplitDecode;
-    const int ns = (L + c.splitlen - 1) / c.splitlen;
+    c.splitlen = L - C > kLongDecode ? kSplitDecodeLong : kSplitDecode;
+    const int ns = (L - C + c.splitlen - 1) / c.splitlen;
+    const bool part = casc || ns > 1;
     c.items = ns;
-    c.partials = ns > 1 ? Q * ns : 0;
-    c.split_tiles = ns > 1 ? 1 : 0;
+    c.partials = part ? Q * ns : 0;
+    c.split_tiles = part ? 1 : 0;
     return c;
   }
   c.kind = kKindPrefill;
   c.tq = prefill_tile_tokens(P.G);
   c.ntiles = (Q + c.tq - 1) / c.tq;
-  if (c.ntiles * P.Hkv >= kPrefillUnsplitUnits) {
+  if (!casc && c.ntiles * P.Hkv >= kPrefillUnsplitUnits) {
     c.splitlen = 0;
     c.items = c.ntiles;
     return c;
@@ -165,10 +182,11 @@ __device__ SeqCounts seq_counts(const AttendParams& P, int b) {
   for (int t = 0; t < c.ntiles; ++t) {
     const int ntok = min(c.tq, Q - t * c.tq);
     const int pmax1 = L - Q + t * c.tq + ntok;
-    const int ns = (pmax1 + c.splitlen - 1) / c.splitlen;
+    const int ns = (pmax1 - C + c.splitlen - 1) / c.splitlen;
+    const bool part = casc || ns > 1;
     c.items += ns;
-    c.partials += ns > 1 ? ntok * ns : 0;
-    c.split_tiles += ns > 1 ? 1 : 0;
+    c.partials += part ? ntok * ns : 0;
+    c.split_tiles += part ? 1 : 0;
   }
   return c;
 }
@@ -216,7 +234,7 @@ __device__ int4 block_scan4(int4 x, int4* lds, int4* tot) {
                    incl.z - x.z + base.z, incl.w - x.w + base.w);
 }
 
-__device__ __forceinline__ void put_item(const AttendParams& P, int idx, int b,
+__device__ __forceinline__ void put_item(WorkItem* dst, int idx, int b,
                                          int tok0, int ntok, int kind, int kv0,
                                          int kv1, int split, int nsplit,
                                          int pbase, int counter, int posbase) {
@@ -234,7 +252,7 @@ __device__ __forceinline__ void put_item(const AttendParams& P, int idx, int b,
   it.posbase = posbase;
 #pragma unroll
   for (int i = 0; i < 5; ++i) it.pad[i] = 0;
-  P.items[idx] = it;
+  dst[idx] = it;
 }
 
 // Items of one request, emitted by one thread (decode requests and prefill
@@ -245,14 +263,16 @@ __device__ void emit_seq(const AttendParams& P, int b, const SeqCounts& c,
                          int ibase, int ilast, int pbase, int cbase) {
   const int q0 = P.qsl[b];
   const int Q = P.qsl[b + 1] - q0, L = P.seq_lens[b];
+  const int C = P.prefix_len;  // first key of the request's own items
   if (c.kind == kKindDecode) {
     const int ns = c.items;
     const int sl = c.splitlen;
+    const bool part = C > 0 || ns > 1;
     for (int s = 0; s < ns; ++s)
-      put_item(P, s == ns - 1 ? ilast : ibase + s, b, q0, Q, kKindDecode,
-               s * sl, min(L, (s + 1) * sl), s, ns, ns > 1 ? pbase : -1,
-               ns > 1 ? cbase : -1, L - Q);
-    if (ns > 1) P.merge_list[cbase] = make_int4(q0, Q, ns, pbase);
+      put_item(P.items, s == ns - 1 ? ilast : ibase + s, b, q0, Q, kKindDecode,
+               C + s * sl, min(L, C + (s + 1) * sl), s, ns, part ? pbase : -1,
+               part ? cbase : -1, L - Q);
+    if (part) P.merge_list[cbase] = make_int4(q0, Q, ns, pbase);
     return;
   }
   // prefill (split, or unsplit when the workgroup's list was full): longest
@@ -262,17 +282,18 @@ __device__ void emit_seq(const AttendParams& P, int b, const SeqCounts& c,
     const int ntok = min(c.tq, Q - t * c.tq);
     const int pmax1 = L - Q + t * c.tq + ntok;
     const int span = c.splitlen ? c.splitlen : pmax1;
-    const int ns = (pmax1 + span - 1) / span;
-    const int pb = ns > 1 ? pcur : -1;
-    const int cb = ns > 1 ? ccur : -1;
-    if (ns > 1) {
+    const int ns = (pmax1 - C + span - 1) / span;
+    const bool part = C > 0 || ns > 1;
+    const int pb = part ? pcur : -1;
+    const int cb = part ? ccur : -1;
+    if (part) {
       P.merge_list[ccur] = make_int4(q0 + t * c.tq, ntok, ns, pcur);
       pcur += ntok * ns;
       ccur += 1;
     }
     for (int s = 0; s < ns; ++s)
-      put_item(P, icur++, b, q0 + t * c.tq, ntok, kKindPrefill, s * span,
-               min(pmax1, (s + 1) * span), s, ns, pb, cb, L - Q + t * c.tq);
+      put_item(P.items, icur++, b, q0 + t * c.tq, ntok, kKindPrefill, C + s * span,
+               min(pmax1, C + (s + 1) * span), s, ns, pb, cb, L - Q + t * c.tq);
   }
 }
 
@@ -305,7 +326,22 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttendParams P) {
     P.hdr->prefill_counter = 0;
     P.hdr->error = 0;
     P.hdr->signature = plan_signature(P);
+    P.hdr->num_prefix_work = 0;
+    P.hdr->prefix_splits = 0;
     coop_n = 0;
+  }
+  // A shared prefix is read through request 0's table: it must hold it, and
+  // the prefix section must exist.  Otherwise the plan is empty.
+  if (P.prefix_len > 0 &&
+      (P.pitems == nullptr || P.prefix_len > P.seq_lens[0] || P.prefix_len > P.max_seq_len)) {
+    if (tid == 0) {
+      P.hdr->num_items = 0;
+      P.hdr->num_work = 0;
+      P.hdr->num_prefill_work = 0;
+      P.hdr->num_split_tiles = 0;
+      P.hdr->error = 2u;
+    }
+    return;
   }
   // scan lanes: x = prefill items, y = decode items, z = partial slots,
   // w = split tiles.  Prefill items go first, decode items after them.
@@ -373,11 +409,32 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttendParams P) {
     for (int t = tid; t < ntiles; t += kPlanThreads) {
       const int ntok = min(tq, Q - t * tq);
       const int pmax1 = L - Q + t * tq + ntok;
-      put_item(P, coop_base[k] + (ntiles - 1 - t), b, q0 + t * tq, ntok,
+      put_item(P.items, coop_base[k] + (ntiles - 1 - t), b, q0 + t * tq, ntok,
                kKindPrefill, 0, pmax1, 0, 1, -1, -1, L - Q + t * tq);
     }
   }
+  // Shared prefix: tiles of tq consecutive tokens of the whole batch x
+  // prefix key ranges of span keys (a multiple of 32); the partial of
+  // (token t, range s) sits at slot t * npre + s of the prefix section.
+  int npre = 0, ntp = 0;
+  if (P.prefix_len > 0 && fits) {
+    const int C = P.prefix_len;
+    npre = min(kMaxPrefixSplits, max(1, (C + kPrefixSplitKeys - 1) / kPrefixSplitKeys));
+    const int span = ((C + npre - 1) / npre + 31) & ~31;
+    npre = (C + span - 1) / span;
+    const int tq = prefill_tile_tokens(P.G);
+    ntp = (P.num_q_tokens + tq - 1) / tq;
+    if ((int64_t)ntp * npre > P.max_pre_items) npre = ntp = 0;  // (not reached)
+    for (int i = tid; i < ntp * npre; i += kPlanThreads) {
+      const int t = i / npre, s = i - t * npre;
+      const int tok0 = t * tq;
+      put_item(P.pitems, i, 0, tok0, min(tq, P.num_q_tokens - tok0), kKindPrefix,
+               s * span, min(C, (s + 1) * span), s, npre, tok0 * npre, -1, C);
+    }
+  }
   if (tid == 0) {
+    P.hdr->num_prefix_work = (uint32_t)(ntp * npre) * (uint32_t)P.Hkv;
+    P.hdr->prefix_splits = (uint32_t)npre;
     const int all_items = total.x + total.y + total2.x;
     P.hdr->num_items = fits ? (uint32_t)all_items : 0u;
     P.hdr->num_work = fits ? (uint32_t)all_items * (uint32_t)P.Hkv : 0u;
@@ -544,7 +601,7 @@ __device__ __forceinline__ void finish_unit(const AttendParams& P,
   const int r = lane & 15, g = lane >> 4;
   const int G = P.G;
   const int ncols = it.ntok * G;
-  if (it.nsplit == 1) {
+  if (it.pbase < 0) {
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       const int col = ct * 16 + r;
@@ -572,11 +629,13 @@ __device__ __forceinline__ void finish_unit(const AttendParams& P,
     const int tk = col / G;
     const int h = kvh * G + (col - tk * G);
     const int64_t slot = (int64_t)it.pbase + (int64_t)tk * it.nsplit + it.split;
-    float* ap = P.part_acc + (slot * P.Hq + h) * D + 4 * g;
+    // shared-prefix items write the prefix section
+    const bool pre = it.kind == kKindPrefix;
+    float* ap = (pre ? P.pre_acc : P.part_acc) + (slot * P.Hq + h) * D + 4 * g;
 #pragma unroll
     for (int n = 0; n < NT; ++n)
       *reinterpret_cast<f32x4*>(ap + 16 * n) = KV8 ? acc[ct][n] * P.v_scale : acc[ct][n];
-    if (g == 0) P.part_ml[slot * P.Hq + h] = make_float2(mrun[ct], l[ct]);
+    if (g == 0) (pre ? P.pre_ml : P.part_ml)[slot * P.Hq + h] = make_float2(mrun[ct], l[ct]);
   }
 }
 
@@ -970,7 +1029,7 @@ __device__ __forceinline__ void run_tile(const AttendParams& P,
   wt.tok0 = it.tok0 + wofs;
   wt.ntok = min(tw, it.ntok - wofs);
   wt.posbase = it.posbase + wofs;
-  wt.pbase = it.nsplit > 1 ? it.pbase + wofs * it.nsplit : -1;
+  wt.pbase = it.pbase >= 0 ? it.pbase + wofs * it.nsplit : -1;
   const bool active = wt.ntok > 0;
   const int wlast = active ? wt.posbase + wt.ntok - 1 : -1;  // causal limit
 
@@ -1275,18 +1334,19 @@ __device__ __forceinline__ void run_tile(const AttendParams& P,
 // workspace then costs outputs, never an out-of-bounds access).
 __device__ __forceinline__ bool item_ok(const AttendParams& P,
                                         const WorkItem& it) {
-  const int maxtok = it.kind == kKindPrefill ? prefill_tile_tokens(P.G)
-                                             : decode_tile_tokens(P.G);
+  const int maxtok = it.kind == kKindDecode ? decode_tile_tokens(P.G)
+                                            : prefill_tile_tokens(P.G);
   bool ok = it.seq >= 0 && it.seq < P.num_seqs && it.tok0 >= 0 &&
             it.ntok >= 1 && it.ntok <= maxtok &&
             it.tok0 + it.ntok <= P.num_q_tokens && it.kv0 >= 0 &&
             (it.kv0 & 31) == 0 && it.kv1 > it.kv0 && it.kv1 <= P.max_seq_len &&
             ((it.kv1 + kBlock - 1) / kBlock) <= P.bt_stride &&
             it.nsplit >= 1 && it.split >= 0 && it.split < it.nsplit;
-  if (it.kind != kKindPrefill) ok = ok && (it.kv1 - it.kv0) <= kSplitDecodeLong;
-  if (it.nsplit > 1)
-    ok = ok && it.pbase >= 0 &&
-         (int64_t)it.pbase + (int64_t)it.ntok * it.nsplit <= P.max_partials;
+  if (it.kind == kKindDecode) ok = ok && (it.kv1 - it.kv0) <= kSplitDecodeLong;
+  if (it.nsplit > 1) ok = ok && it.pbase >= 0;
+  if (it.pbase >= 0)
+    ok = ok && (int64_t)it.pbase + (int64_t)it.ntok * it.nsplit <=
+                   (it.kind == kKindPrefix ? P.max_pre_partials : P.max_partials);
   return ok;
 }
 
@@ -1302,10 +1362,14 @@ __device__ __forceinline__ void attend_body(const AttendParams& P,
   if ((uint64_t)num_work > (uint64_t)P.max_items * (uint64_t)P.Hkv) num_work = 0;
   uint32_t num_pre = P.hdr->num_prefill_work;
   if (num_pre > num_work) num_pre = num_work;
+  // shared-prefix units (their own item list) come first in the prefill queue
+  uint32_t num_pfx = P.pitems != nullptr ? P.hdr->num_prefix_work : 0u;
+  if ((uint64_t)num_pfx > (uint64_t)P.max_pre_items * (uint64_t)P.Hkv) num_pfx = 0;
   const uint32_t Hkv = (uint32_t)P.Hkv;
   constexpr uint32_t kWpg = kAttendThreads / 64;  // waves per workgroup
   const uint32_t wslot = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t ndec = num_work - num_pre;  // decode units follow the prefill ones
+  const uint32_t nq = num_pfx + num_pre;     // units of the prefill queue
   auto claim = [&](uint32_t* counter) {
     uint32_t t = 0;
     if (lane == 0) t = atomicAdd(counter, 1u);
@@ -1331,11 +1395,11 @@ __device__ __forceinline__ void attend_body(const AttendParams& P,
   // per wave (decode queue) or workgroup (prefill queue) entering it by a
   // claim -- so the claim that returns the last value is the last access to
   // that counter in this launch, and it resets the counter.
-  const bool mixed = MIXED && num_pre > 0;
-  if (mixed) pre_static = min(gridDim.x * kPrefillWgNum / kPrefillWgDen, num_pre);
+  const bool mixed = MIXED && nq > 0;
+  if (mixed) pre_static = min(gridDim.x * kPrefillWgNum / kPrefillWgDen, nq);
   const uint32_t dec_static = (gridDim.x - pre_static) * kWpg;
   const uint32_t dec_claims = ndec + pre_static * kWpg;
-  const uint32_t pre_claims = num_pre + (gridDim.x - pre_static);
+  const uint32_t pre_claims = nq + (gridDim.x - pre_static);
   // one claim on the decode queue by lane 0 (t: the value it returned)
   auto dec_claimed = [&](uint32_t t) {
     if (t + 1u == dec_claims && lane == 0) atomicExch(&P.hdr->work_counter, 0u);
@@ -1348,10 +1412,12 @@ __device__ __forceinline__ void attend_body(const AttendParams& P,
   };
   auto prefill_units = [&](uint32_t u) {
     int k = 0;
-    for (uint32_t pass = 0; u < num_pre && pass <= num_pre; ++pass) {
-      const WorkItem it = P.items[u / Hkv];
-      if (item_ok(P, it) && it.kind == kKindPrefill)
-        run_tile<D, KV8>(P, it, (int)(u % Hkv), lane, (int)wslot, ring);
+    for (uint32_t pass = 0; u < nq && pass <= nq; ++pass) {
+      const bool pfx = u < num_pfx;
+      const uint32_t w = pfx ? u : u - num_pfx;
+      const WorkItem it = pfx ? P.pitems[w / Hkv] : P.items[w / Hkv];
+      if (item_ok(P, it) && it.kind == (pfx ? kKindPrefix : kKindPrefill))
+        run_tile<D, KV8>(P, it, (int)(w % Hkv), lane, (int)wslot, ring);
       if (threadIdx.x == 0) next_unit[k] = pre_claim();
       __syncthreads();
       u = __builtin_amdgcn_readfirstlane(next_unit[k]);
@@ -1433,6 +1499,12 @@ __global__ __launch_bounds__(kAttendThreads) void merge_kernel(AttendParams P) {
   if (P.hdr->signature != plan_signature(P)) return;
   uint32_t ntiles = P.hdr->num_split_tiles;
   if ((int64_t)ntiles > P.max_items) ntiles = 0;
+  // shared-prefix plans: every listed token first combines its npre prefix
+  // partials (slots t * npre + s of the prefix section), then its own
+  int npre = P.pre_ml != nullptr ? (int)P.hdr->prefix_splits : 0;
+  if (npre < 0 || npre > kMaxPrefixSplits ||
+      (int64_t)P.num_q_tokens * npre > P.max_pre_partials)
+    ntiles = 0;
   const uint32_t W = merge_waves_per_head(G, D);
   const uint32_t per_tile = (uint32_t)P.Hkv * W;
   const uint32_t nunits = ntiles * per_tile;
@@ -1445,11 +1517,12 @@ __global__ __launch_bounds__(kAttendThreads) void merge_kernel(AttendParams P) {
     const int pass0 = (int)(u % W);
     // same rule as for work items: never follow an entry out of bounds
     if (tile.x < 0 || tile.y < 1 || tile.x + tile.y > P.num_q_tokens ||
-        tile.z < 2 || tile.w < 0 ||
+        tile.z < (npre > 0 ? 1 : 2) || tile.w < 0 ||
         (int64_t)tile.w + (int64_t)tile.y * tile.z > P.max_partials)
       continue;
     const int ncols = tile.y * G;
     const int nsplit = tile.z;
+    const int nall = npre + nsplit;
     for (int c0 = pass0 * CPW; c0 < ncols; c0 += (int)W * CPW) {
       const int c = c0 + cl;
       if (c >= ncols) continue;
@@ -1458,16 +1531,19 @@ __global__ __launch_bounds__(kAttendThreads) void merge_kernel(AttendParams P) {
       const int64_t slot0 = (int64_t)tile.w + (int64_t)tk * nsplit;
       float M = -INFINITY, den = 0.0f;
       f32x4 n0 = {0.f, 0.f, 0.f, 0.f}, n1 = {0.f, 0.f, 0.f, 0.f};
-      for (int s0 = 0; s0 < nsplit; s0 += SB) {
+      for (int s0 = 0; s0 < nall; s0 += SB) {
         float2 ml[SB];
         f32x4 a0[SB], a1[SB];
 #pragma unroll
         for (int k = 0; k < SB; ++k) {
           const int sp = s0 + k;
-          if (sp < nsplit) {
-            const int64_t row = (slot0 + sp) * P.Hq + h;
-            ml[k] = P.part_ml[row];
-            const f32x4* ap = reinterpret_cast<const f32x4*>(P.part_acc + row * D + d0);
+          if (sp < nall) {
+            const bool pre = sp < npre;
+            const int64_t row =
+                (pre ? (int64_t)(tile.x + tk) * npre + sp : slot0 + (sp - npre)) * P.Hq + h;
+            ml[k] = (pre ? P.pre_ml : P.part_ml)[row];
+            const f32x4* ap =
+                reinterpret_cast<const f32x4*>((pre ? P.pre_acc : P.part_acc) + row * D + d0);
             a0[k] = ap[0];
             a1[k] = ap[1];
           } else {
@@ -1554,6 +1630,12 @@ AttendParams make_params(const AttendArgs& a) {
   P.part_acc = reinterpret_cast<float*>(ws + a.ws.part_acc);
   P.max_items = a.ws.max_items;
   P.max_partials = a.ws.max_partials;
+  P.pitems = a.cascade ? reinterpret_cast<WorkItem*>(ws + a.ws.pre_items) : nullptr;
+  P.pre_ml = a.cascade ? reinterpret_cast<float2*>(ws + a.ws.pre_ml) : nullptr;
+  P.pre_acc = a.cascade ? reinterpret_cast<float*>(ws + a.ws.pre_acc) : nullptr;
+  P.max_pre_items = a.cascade ? a.ws.max_pre_items : 0;
+  P.max_pre_partials = a.cascade ? a.ws.max_pre_partials : 0;
+  P.prefix_len = a.cascade ? a.prefix_len : 0;
   return P;
 }
 
@@ -1569,7 +1651,8 @@ hipError_t launch_plan(const AttendArgs& a, hipStream_t stream) {
 hipError_t launch_planned(const AttendArgs& a, hipStream_t stream) {
   if (a.num_q_tokens == 0 || a.num_seqs == 0) return hipSuccess;
   const AttendParams P = make_params(a);
-  const bool decode_only = a.max_query_len <= decode_tile_tokens(P.G);
+  // (a shared-prefix plan has prefill-kind tiles even in a decode batch)
+  const bool decode_only = !a.cascade && a.max_query_len <= decode_tile_tokens(P.G);
   void (*fn)(AttendParams);
   int slot;
   if (a.head_dim == 128) {
@@ -1588,7 +1671,8 @@ hipError_t launch_planned(const AttendArgs& a, hipStream_t stream) {
   if (a.kv8) slot += 4;
   // Persistent grid: every resident slot of every CU, never more waves than
   // the work-unit bound.
-  const int64_t max_work = a.ws.max_items * a.num_kv_heads;
+  const int64_t max_work =
+      (a.ws.max_items + (a.cascade ? a.ws.max_pre_items : 0)) * a.num_kv_heads;
   int64_t wgs = (int64_t)a.num_cus * resident_wgs((const void*)fn, slot);
   const int64_t need = (max_work + (kAttendThreads / 64) - 1) / (kAttendThreads / 64);
   if (wgs > need) wgs = need;

@@ -159,6 +159,18 @@ size_t pa_attend_workspace_size(int32_t num_seqs, int64_t num_q_tokens,
       .total;
 }
 
+size_t pa_attend_cascade_workspace_size(int32_t num_seqs, int64_t num_q_tokens,
+                                        int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t max_query_len,
+                                        int32_t max_seq_len) {
+  if (num_seqs < 0 || num_q_tokens < 0 || max_query_len < 0 || max_seq_len < 0)
+    return 0;
+  if (check_heads(num_q_heads, num_kv_heads, head_dim) != PA_OK) return 0;
+  return pa::workspace_layout(num_seqs, num_q_tokens, num_q_heads, num_kv_heads,
+                              head_dim, max_query_len, max_seq_len)
+      .cascade_total;
+}
+
 }  // extern "C"
 
 namespace {
@@ -174,7 +186,8 @@ pa_status prepare_attend(const void* q, const void* k_cache,
                          int32_t head_dim, int32_t max_query_len,
                          int32_t max_seq_len, float scale, void* out,
                          void* workspace, size_t workspace_bytes,
-                         bool need_tensors, pa::AttendArgs* a, bool* empty) {
+                         bool need_tensors, pa::AttendArgs* a, bool* empty,
+                         int32_t prefix_len = -1) {
   *empty = false;
   if (num_seqs < 0 || num_q_tokens < 0 || num_blocks < 0 ||
       max_blocks_per_seq < 0 || max_query_len < 0 || max_seq_len < 0)
@@ -203,10 +216,18 @@ pa_status prepare_attend(const void* q, const void* k_cache,
   pa::WorkspaceLayout ws =
       pa::workspace_layout(num_seqs, num_q_tokens, num_q_heads, num_kv_heads,
                            head_dim, max_query_len, max_seq_len);
-  if (!workspace || workspace_bytes < ws.total)
+  // shared-prefix calls (prefix_len >= 0): the workspace also holds the
+  // prefix section; the plan shares the largest multiple of 32 keys not above
+  // common_prefix_len (every key range then covers whole pairs of blocks)
+  const bool cascade = prefix_len >= 0;
+  if (cascade && prefix_len > max_seq_len)
+    return fail(PA_ERR_SHAPE, "common_prefix_len must be in [0, max_seq_len]");
+  const size_t need = cascade ? ws.cascade_total : ws.total;
+  if (!workspace || workspace_bytes < need)
     return fail(PA_ERR_WORKSPACE,
-                "pa_attend: workspace needs " + std::to_string(ws.total) +
-                    " bytes, got " + std::to_string(workspace_bytes));
+                std::string(cascade ? "shared-prefix attention" : "pa_attend") +
+                    ": workspace needs " + std::to_string(need) + " bytes, got " +
+                    std::to_string(workspace_bytes));
   if ((uintptr_t)workspace & 255)
     return fail(PA_ERR_WORKSPACE, "pa_attend: workspace must be 256-byte aligned");
   hipError_t e = hipSuccess;
@@ -232,20 +253,25 @@ pa_status prepare_attend(const void* q, const void* k_cache,
   a->workspace = workspace;
   a->ws = ws;
   a->num_cus = cus;
+  a->cascade = cascade;
+  a->prefix_len = cascade ? (prefix_len & ~31) : 0;
   a->kv8 = false;
   a->k_scale = 1.0f;
   a->v_scale = 1.0f;
   return PA_OK;
 }
 
-// The 8-bit variants: same checks, then the pools' scales.
-pa_status set_fp8(float k_scale, float v_scale, pa::AttendArgs* a) {
+// The 8-bit variants: the pools' scales are checked before anything else.
+pa_status check_fp8(float k_scale, float v_scale) {
   if (!(k_scale > 0.0f && k_scale <= FLT_MAX) || !(v_scale > 0.0f && v_scale <= FLT_MAX))
-    return fail(PA_ERR_SHAPE, "pa_attend_fp8: scales must be finite and > 0");
+    return fail(PA_ERR_SHAPE, "8-bit pools: scales must be finite and > 0");
+  return PA_OK;
+}
+
+void set_fp8(float k_scale, float v_scale, pa::AttendArgs* a) {
   a->kv8 = true;
   a->k_scale = k_scale;
   a->v_scale = v_scale;
-  return PA_OK;
 }
 
 }  // namespace
@@ -359,6 +385,7 @@ pa_status pa_attend_planned_fp8(const void* q, const void* k_cache,
                                 float scale, float k_scale, float v_scale,
                                 void* out, void* workspace,
                                 size_t workspace_bytes, void* stream) {
+  if (check_fp8(k_scale, v_scale) != PA_OK) return PA_ERR_SHAPE;
   pa::AttendArgs a;
   bool empty;
   pa_status s = prepare_attend(q, k_cache, v_cache, num_blocks, block_tables,
@@ -368,8 +395,7 @@ pa_status pa_attend_planned_fp8(const void* q, const void* k_cache,
                                workspace, workspace_bytes, true, &a, &empty);
   if (s != PA_OK) return s;
   if (empty) return ok();
-  s = set_fp8(k_scale, v_scale, &a);
-  if (s != PA_OK) return s;
+  set_fp8(k_scale, v_scale, &a);
   hipError_t e = pa::launch_planned(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "pa_attend_planned_fp8 launch");
   return ok();
@@ -384,6 +410,7 @@ pa_status pa_attend_fp8(const void* q, const void* k_cache, const void* v_cache,
                         int32_t max_query_len, int32_t max_seq_len, float scale,
                         float k_scale, float v_scale, void* out, void* workspace,
                         size_t workspace_bytes, void* stream) {
+  if (check_fp8(k_scale, v_scale) != PA_OK) return PA_ERR_SHAPE;
   pa::AttendArgs a;
   bool empty;
   pa_status s = prepare_attend(q, k_cache, v_cache, num_blocks, block_tables,
@@ -393,12 +420,195 @@ pa_status pa_attend_fp8(const void* q, const void* k_cache, const void* v_cache,
                                workspace, workspace_bytes, true, &a, &empty);
   if (s != PA_OK) return s;
   if (empty) return ok();
-  s = set_fp8(k_scale, v_scale, &a);
-  if (s != PA_OK) return s;
+  set_fp8(k_scale, v_scale, &a);
   hipError_t e = pa::launch_plan(a, static_cast<hipStream_t>(stream));
   if (e == hipSuccess) e = pa::launch_planned(a, static_cast<hipStream_t>(stream));
   if (e == hipSuccess) e = pa::launch_merge(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "pa_attend_fp8 launch");
+  return ok();
+}
+
+// ---- shared-prefix (cascade) attention --------------------------------------
+
+pa_status pa_attend_plan_cascade(const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq,
+                                 const int32_t* seq_lens,
+                                 const int32_t* query_start_loc, int32_t num_seqs,
+                                 int64_t num_q_tokens, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t max_query_len, int32_t max_seq_len,
+                                 int32_t common_prefix_len, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  pa::AttendArgs a;
+  bool empty;
+  pa_status s = prepare_attend(nullptr, nullptr, nullptr, 0, block_tables,
+                               max_blocks_per_seq, seq_lens, query_start_loc,
+                               num_seqs, num_q_tokens, num_q_heads, num_kv_heads,
+                               head_dim, max_query_len, max_seq_len, 0.0f,
+                               nullptr, workspace, workspace_bytes, false, &a,
+                               &empty, common_prefix_len < 0 ? INT32_MAX : common_prefix_len);
+  if (s != PA_OK) return s;
+  if (empty) return ok();
+  hipError_t e = pa::launch_plan(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pa_attend_plan_cascade launch");
+  return ok();
+}
+
+namespace {
+
+// Attention (and optionally plan and merge) over a shared-prefix workspace.
+pa_status cascade_call(const void* q, const void* k_cache, const void* v_cache,
+                       int64_t num_blocks, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                       const int32_t* query_start_loc, int32_t num_seqs,
+                       int64_t num_q_tokens, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t head_dim,
+                       int32_t max_query_len, int32_t max_seq_len,
+                       int32_t common_prefix_len, float scale, bool kv8,
+                       float k_scale, float v_scale, void* out, void* workspace,
+                       size_t workspace_bytes, void* stream, bool plan_and_merge,
+                       const char* what) {
+  if (kv8 && check_fp8(k_scale, v_scale) != PA_OK) return PA_ERR_SHAPE;
+  pa::AttendArgs a;
+  bool empty;
+  pa_status s = prepare_attend(q, k_cache, v_cache, num_blocks, block_tables,
+                               max_blocks_per_seq, seq_lens, query_start_loc,
+                               num_seqs, num_q_tokens, num_q_heads, num_kv_heads,
+                               head_dim, max_query_len, max_seq_len, scale, out,
+                               workspace, workspace_bytes, true, &a, &empty,
+                               common_prefix_len < 0 ? INT32_MAX : common_prefix_len);
+  if (s != PA_OK) return s;
+  if (empty) return ok();
+  if (kv8) set_fp8(k_scale, v_scale, &a);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = plan_and_merge ? pa::launch_plan(a, st) : hipSuccess;
+  if (e == hipSuccess) e = pa::launch_planned(a, st);
+  if (e == hipSuccess && plan_and_merge) e = pa::launch_merge(a, st);
+  if (e != hipSuccess) return hip_fail(e, what);
+  return ok();
+}
+
+}  // namespace
+
+pa_status pa_attend_planned_cascade(const void* q, const void* k_cache,
+                                    const void* v_cache, int64_t num_blocks,
+                                    const int32_t* block_tables,
+                                    int32_t max_blocks_per_seq,
+                                    const int32_t* seq_lens,
+                                    const int32_t* query_start_loc,
+                                    int32_t num_seqs, int64_t num_q_tokens,
+                                    int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t max_query_len,
+                                    int32_t max_seq_len, float scale, void* out,
+                                    void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  return cascade_call(q, k_cache, v_cache, num_blocks, block_tables,
+                      max_blocks_per_seq, seq_lens, query_start_loc, num_seqs,
+                      num_q_tokens, num_q_heads, num_kv_heads, head_dim,
+                      max_query_len, max_seq_len, 0, scale, false, 1.0f, 1.0f,
+                      out, workspace, workspace_bytes, stream, false,
+                      "pa_attend_planned_cascade launch");
+}
+
+pa_status pa_attend_planned_cascade_fp8(
+    const void* q, const void* k_cache, const void* v_cache, int64_t num_blocks,
+    const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* seq_lens, const int32_t* query_start_loc, int32_t num_seqs,
+    int64_t num_q_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t max_query_len, int32_t max_seq_len, float scale,
+    float k_scale, float v_scale, void* out, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  return cascade_call(q, k_cache, v_cache, num_blocks, block_tables,
+                      max_blocks_per_seq, seq_lens, query_start_loc, num_seqs,
+                      num_q_tokens, num_q_heads, num_kv_heads, head_dim,
+                      max_query_len, max_seq_len, 0, scale, true, k_scale,
+                      v_scale, out, workspace, workspace_bytes, stream, false,
+                      "pa_attend_planned_cascade_fp8 launch");
+}
+
+pa_status pa_attend_merge_cascade(int32_t num_seqs, int64_t num_q_tokens,
+                                  int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t max_query_len,
+                                  int32_t max_seq_len, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  pa::AttendArgs a;
+  bool empty;
+  static const int32_t kNone[2] = {0, 0};
+  pa_status s = prepare_attend(nullptr, nullptr, nullptr, 0, kNone, 1, kNone,
+                               kNone, num_seqs, num_q_tokens, num_q_heads,
+                               num_kv_heads, head_dim, max_query_len,
+                               max_seq_len, 0.0f, out, workspace,
+                               workspace_bytes, false, &a, &empty, 0);
+  if (s != PA_OK) return s;
+  if (empty) return ok();
+  if (!out) return fail(PA_ERR_NULL, "pa_attend_merge_cascade: NULL out");
+  if ((uintptr_t)out & 15) return fail(PA_ERR_SHAPE, "out must be 16-byte aligned");
+  hipError_t e = pa::launch_merge(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pa_attend_merge_cascade launch");
+  return ok();
+}
+
+pa_status pa_attend_cascade(const void* q, const void* k_cache,
+                            const void* v_cache, int64_t num_blocks,
+                            const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                            const int32_t* query_start_loc, int32_t num_seqs,
+                            int64_t num_q_tokens, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim,
+                            int32_t max_query_len, int32_t max_seq_len,
+                            int32_t common_prefix_len, float scale, void* out,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  return cascade_call(q, k_cache, v_cache, num_blocks, block_tables,
+                      max_blocks_per_seq, seq_lens, query_start_loc, num_seqs,
+                      num_q_tokens, num_q_heads, num_kv_heads, head_dim,
+                      max_query_len, max_seq_len, common_prefix_len, scale, false,
+                      1.0f, 1.0f, out, workspace, workspace_bytes, stream, true,
+                      "pa_attend_cascade launch");
+}
+
+pa_status pa_attend_cascade_fp8(const void* q, const void* k_cache,
+                                const void* v_cache, int64_t num_blocks,
+                                const int32_t* block_tables,
+                                int32_t max_blocks_per_seq,
+                                const int32_t* seq_lens,
+                                const int32_t* query_start_loc, int32_t num_seqs,
+                                int64_t num_q_tokens, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim,
+                                int32_t max_query_len, int32_t max_seq_len,
+                                int32_t common_prefix_len, float scale,
+                                float k_scale, float v_scale, void* out,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return cascade_call(q, k_cache, v_cache, num_blocks, block_tables,
+                      max_blocks_per_seq, seq_lens, query_start_loc, num_seqs,
+                      num_q_tokens, num_q_heads, num_kv_heads, head_dim,
+                      max_query_len, max_seq_len, common_prefix_len, scale, true,
+                      k_scale, v_scale, out, workspace, workspace_bytes, stream,
+                      true, "pa_attend_cascade_fp8 launch");
+}
+
+pa_status pa_validate_cascade_host(const int32_t* block_tables,
+                                   int32_t max_blocks_per_seq,
+                                   const int32_t* seq_lens,
+                                   const int32_t* query_start_loc,
+                                   int32_t num_seqs, int32_t common_prefix_len) {
+  if (num_seqs < 0 || max_blocks_per_seq < 0 || common_prefix_len < 0)
+    return fail(PA_ERR_SHAPE, "validate: negative size");
+  if (num_seqs > 0 && (!block_tables || !seq_lens || !query_start_loc))
+    return fail(PA_ERR_NULL, "validate: NULL pointer");
+  const int64_t nshared = common_prefix_len / PA_BLOCK_SIZE;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const std::string at = " (request " + std::to_string(b) + ")";
+    const int64_t Q = (int64_t)query_start_loc[b + 1] - query_start_loc[b];
+    if ((int64_t)seq_lens[b] - Q < common_prefix_len)
+      return fail(PA_ERR_METADATA, "a query lies inside the shared prefix" + at);
+    if (nshared > max_blocks_per_seq)
+      return fail(PA_ERR_METADATA, "block table row shorter than the shared prefix");
+    for (int64_t j = 0; j < nshared; ++j)
+      if (block_tables[(int64_t)b * max_blocks_per_seq + j] != block_tables[j])
+        return fail(PA_ERR_METADATA, "shared prefix block differs from request 0's" + at);
+  }
   return ok();
 }
 

@@ -26,8 +26,15 @@ constexpr int kPrefillColTiles = 2;  // per wave: 32 MFMA columns, 32/G tokens
 constexpr int kPrefillWaves = 4;     // waves sharing one prefill tile's K/V
 constexpr int kMaxGroup = 16;        // query heads per kv head
 constexpr int kAttendThreads = 256;  // 4 waves per workgroup
+// Shared-prefix (cascade) plans: the common prefix is cut into at most
+// kMaxPrefixSplits key ranges of about kPrefixSplitKeys keys each.
+constexpr int kMaxPrefixSplits = 8;
+constexpr int kPrefixSplitKeys = 256;
 
-enum ItemKind : int { kKindDecode = 0, kKindPrefill = 1 };
+// kKindPrefix: a tile of consecutive query tokens of the whole batch (any
+// requests) against a key range of the common prefix, read through request
+// 0's block table, writing partials into the prefix section.
+enum ItemKind : int { kKindDecode = 0, kKindPrefill = 1, kKindPrefix = 2 };
 
 // One unit of attention work for all kv heads: a tile of consecutive query
 // tokens of one request against one logical key range of that request.
@@ -39,8 +46,9 @@ struct WorkItem {
   int32_t kv0;      // first logical key (multiple of 32)
   int32_t kv1;      // one past the last logical key
   int32_t split;    // split index of this key range
-  int32_t nsplit;   // splits of this tile (1: output written directly)
-  int32_t pbase;    // partial slot of (tile token 0, split 0); -1 if unsplit
+  int32_t nsplit;   // splits of this tile
+  int32_t pbase;    // partial slot of (tile token 0, split 0); -1: the output
+                    // is written directly (one split, no shared prefix)
   int32_t counter;  // index of the tile in the merge list; -1 if unsplit
   int32_t posbase;  // logical position of the tile's first query token
   int32_t pad[5];
@@ -57,6 +65,8 @@ struct PlanHeader {
   uint32_t signature;     // hash of the arguments the plan was made for
   uint32_t prefill_counter;   // prefill queue head (zeroed by the plan)
   uint32_t num_prefill_work;  // prefill items * num_kv_heads
+  uint32_t num_prefix_work;   // shared-prefix items * num_kv_heads
+  uint32_t prefix_splits;     // key ranges of the shared prefix (0: none)
 };
 
 // Byte offsets of the workspace sections.
@@ -68,6 +78,15 @@ struct WorkspaceLayout {
   size_t total;
   int64_t max_items;
   int64_t max_partials;
+  // Shared-prefix section, after the sections above (their offsets are the
+  // same with or without it): prefix items and per-(token, prefix split)
+  // partials.
+  size_t pre_items;     // WorkItem[max_pre_items]
+  size_t pre_ml;        // float2[max_pre_partials * Hq]
+  size_t pre_acc;       // float[max_pre_partials * Hq * D]
+  size_t cascade_total;
+  int64_t max_pre_items;
+  int64_t max_pre_partials;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -122,6 +141,18 @@ inline WorkspaceLayout workspace_layout(int32_t num_seqs, int64_t num_q_tokens,
   off = align256(off + sizeof(float) * (size_t)w.max_partials * num_q_heads *
                            (size_t)head_dim);
   w.total = off;
+  // prefix tiles span the whole batch: ceil(T / tq_p) tiles x splits
+  w.max_pre_items = cdiv64(T, tq_p) * kMaxPrefixSplits;
+  if (w.max_pre_items < 1) w.max_pre_items = 1;
+  w.max_pre_partials = (T > 0 ? T : 1) * kMaxPrefixSplits;
+  w.pre_items = off;
+  off = align256(off + sizeof(WorkItem) * (size_t)w.max_pre_items);
+  w.pre_ml = off;
+  off = align256(off + sizeof(float) * 2 * (size_t)w.max_pre_partials * num_q_heads);
+  w.pre_acc = off;
+  off = align256(off + sizeof(float) * (size_t)w.max_pre_partials * num_q_heads *
+                           (size_t)head_dim);
+  w.cascade_total = off;
   return w;
 }
 
@@ -170,6 +201,8 @@ struct AttendArgs {
   void* workspace;
   WorkspaceLayout ws;
   int num_cus;
+  bool cascade;    // the workspace holds the shared-prefix section
+  int32_t prefix_len;  // plan: keys shared by every request (multiple of 32)
   bool kv8;        // 8-bit pools: E4M3 codes (k_cache, v_cache are uint8)
   float k_scale;   // value of a K code: code * k_scale (8-bit pools)
   float v_scale;   // value of a V code: code * v_scale (8-bit pools)

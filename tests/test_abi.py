@@ -191,3 +191,83 @@ def test_validator_rejects_bad_content(lib, wl):
     bt = wl.block_tables[:, :2].copy()     # row too short for L = 64
     assert validate(lib, wl, bt=bt) == M
     assert "request" in lib.pa_last_error().decode()
+
+
+# ---- shared-prefix (cascade) calls -----------------------------------------------------
+
+def test_cascade_workspace_size(lib):
+    plain = lib.pa_attend_workspace_size(256, 256, 32, 8, 128, 1, 2560)
+    casc = lib.pa_attend_cascade_workspace_size(256, 256, 32, 8, 128, 1, 2560)
+    # the prefix section: up to 8 key ranges per query token, each a float2
+    # and a D-float partial per query head, plus its work items
+    assert casc >= plain + 256 * 8 * 32 * (128 + 2) * 4
+    assert lib.pa_attend_cascade_workspace_size(256, 256, 32, 8, 96, 1, 2560) == 0
+    assert lib.pa_attend_cascade_workspace_size(-1, 256, 32, 8, 128, 1, 2560) == 0
+
+
+def cascade_args(prefix=32, **over):
+    a = attend_args(**over)
+    return a[:15] + [prefix] + a[15:]
+
+
+@pytest.mark.parametrize("prefix,over,status", [
+    (-1, {}, _lib.PA_ERR_SHAPE),
+    (65, {}, _lib.PA_ERR_SHAPE),                     # > max_seq_len
+    (32, dict(q=None), _lib.PA_ERR_NULL),
+    (32, dict(D=96), _lib.PA_ERR_UNSUPPORTED),
+    (32, dict(scale=0.0), _lib.PA_ERR_SHAPE),
+    (32, dict(ws=None), _lib.PA_ERR_WORKSPACE),
+])
+def test_cascade_rejects_bad_arguments(lib, prefix, over, status):
+    assert lib.pa_attend_cascade(*cascade_args(prefix, **over)) == status
+    assert lib.pa_last_error() != b""
+
+
+def test_cascade_needs_the_larger_workspace(lib):
+    plain = lib.pa_attend_workspace_size(2, 2, 8, 2, 128, 1, 64)
+    casc = lib.pa_attend_cascade_workspace_size(2, 2, 8, 2, 128, 1, 64)
+    assert casc > plain
+    assert lib.pa_attend_cascade(*cascade_args(32, wsb=plain)) == _lib.PA_ERR_WORKSPACE
+    assert b"shared-prefix" in lib.pa_last_error()
+    a = attend_args(wsb=plain)
+    # the planned / merge variants check the same size
+    assert lib.pa_attend_planned_cascade(*a) == _lib.PA_ERR_WORKSPACE
+    assert lib.pa_attend_merge_cascade(2, 2, 8, 2, 128, 1, 64, FAKE, FAKE, plain,
+                                       None) == _lib.PA_ERR_WORKSPACE
+    assert lib.pa_attend_plan_cascade(FAKE, 4, FAKE, FAKE, 2, 2, 8, 2, 128, 1, 64, 32,
+                                      FAKE, plain, None) == _lib.PA_ERR_WORKSPACE
+
+
+def test_cascade_fp8_scale_checks(lib):
+    a = cascade_args(32)
+    args = a[:17] + [0.0, 1.0] + a[17:]  # k_scale 0
+    assert lib.pa_attend_cascade_fp8(*args) == _lib.PA_ERR_SHAPE
+
+
+def test_cascade_empty_batch_is_ok(lib):
+    assert lib.pa_attend_cascade(*cascade_args(32, T=0, q=None, out=None)) == _lib.PA_OK
+
+
+def validate_cascade(lib, w, prefix, bt=None, sl=None, qsl=None):
+    bt = np.ascontiguousarray(w.block_tables if bt is None else bt, np.int32)
+    sl = np.ascontiguousarray(w.seq_lens if sl is None else sl, np.int32)
+    qsl = np.ascontiguousarray(w.query_start_loc if qsl is None else qsl, np.int32)
+    return lib.pa_validate_cascade_host(_p(bt), bt.shape[1], _p(sl), _p(qsl),
+                                        bt.shape[0], prefix)
+
+
+def test_cascade_validator(lib):
+    M = _lib.PA_ERR_METADATA
+    w = W.make_workload("c", [100, 90, 300, 80], [1, 20, 200, 6], 8, 2, 64, seed=1,
+                        shared_prefix=64)
+    assert validate_cascade(lib, w, 64) == _lib.PA_OK
+    assert validate_cascade(lib, w, 70) == _lib.PA_OK   # L - Q >= 70 everywhere
+    assert validate_cascade(lib, w, 71) == M            # request 1: L - Q = 70
+    assert "request 1" in lib.pa_last_error().decode()
+    bt = w.block_tables.copy()
+    bt[2, 3] = w.num_blocks - 1                         # differs inside the prefix
+    assert validate_cascade(lib, w, 64, bt=bt) == M
+    assert validate_cascade(lib, w, 48, bt=bt) == _lib.PA_OK  # block 3 not shared
+    u = W.make_workload("u", [100, 90], [1, 20], 8, 2, 64, seed=1, shared_prefix=64,
+                        shared=False)                  # private copies: other ids
+    assert validate_cascade(lib, u, 64) == M
