@@ -61,6 +61,9 @@ constexpr int kDecodeStages = 3;
 // workgroups start on prefill tiles and the others on decode units.
 constexpr uint32_t kPrefillWgNum = 3;
 constexpr uint32_t kPrefillWgDen = 8;
+// With shared-prefix units in the queue: kPrefixWgNum / kPrefixWgDen.
+constexpr uint32_t kPrefixWgNum = 1;
+constexpr uint32_t kPrefixWgDen = 8;
 
 struct AttendParams {
   const uint16_t* q;
@@ -82,6 +85,7 @@ struct AttendParams {
   float v_scale;     // 8-bit pools: the value of a V code is code * v_scale
   uint16_t* out;
   PlanHeader* hdr;
+  uint32_t* dec_counters;  // kDecodeShards decode queue heads
   WorkItem* items;
   int4* merge_list;  // per split tile: tok0, ntok, nsplit, pbase
   float2* part_ml;
@@ -321,8 +325,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttendParams P) {
   __shared__ int coop_b[kMaxCoop];
   __shared__ int coop_base[kMaxCoop];
   const int tid = threadIdx.x;
+  if (tid < kDecodeShards) P.dec_counters[tid * kCounterStride] = 0;
   if (tid == 0) {
-    P.hdr->work_counter = 0;
     P.hdr->prefill_counter = 0;
     P.hdr->error = 0;
     P.hdr->signature = plan_signature(P);
@@ -1396,13 +1400,29 @@ __device__ __forceinline__ void attend_body(const AttendParams& P,
   // claim -- so the claim that returns the last value is the last access to
   // that counter in this launch, and it resets the counter.
   const bool mixed = MIXED && nq > 0;
-  if (mixed) pre_static = min(gridDim.x * kPrefillWgNum / kPrefillWgDen, nq);
-  const uint32_t dec_static = (gridDim.x - pre_static) * kWpg;
-  const uint32_t dec_claims = ndec + pre_static * kWpg;
+  if (mixed)
+    pre_static = min(num_pfx > 0 ? gridDim.x * kPrefixWgNum / kPrefixWgDen
+                                 : gridDim.x * kPrefillWgNum / kPrefillWgDen,
+                     nq);
+  // The decode queue is split into S shards: shard s holds decode units
+  // s, s + S, s + 2S, ... (each shard a like share of the longest-first
+  // order) and is served by the workgroups b = s (mod S) from a counter of
+  // its own, so that claims meet on S addresses instead of one.  Within a
+  // shard, units are numbered locally (unit s + S * k is local index k); the
+  // shard's decode-first waves start on local units 0 .. dec_static - 1.
+  const uint32_t S = min((uint32_t)kDecodeShards, gridDim.x);
+  const uint32_t shard = blockIdx.x % S;
+  uint32_t* const dctr = P.dec_counters + shard * kCounterStride;
+  const uint32_t n_s = ndec > shard ? (ndec - shard + S - 1) / S : 0u;
+  const uint32_t wg_s = (gridDim.x - shard + S - 1) / S;  // workgroups of the shard
+  const uint32_t pf_s =                                   // of them prefill-first
+      pre_static > shard ? min(wg_s, (pre_static - shard + S - 1) / S) : 0u;
+  const uint32_t dec_static = (wg_s - pf_s) * kWpg;
+  const uint32_t dec_claims = n_s + pf_s * kWpg;
   const uint32_t pre_claims = nq + (gridDim.x - pre_static);
-  // one claim on the decode queue by lane 0 (t: the value it returned)
+  // one claim on the shard's counter by lane 0 (t: the value it returned)
   auto dec_claimed = [&](uint32_t t) {
-    if (t + 1u == dec_claims && lane == 0) atomicExch(&P.hdr->work_counter, 0u);
+    if (t + 1u == dec_claims && lane == 0) atomicExch(dctr, 0u);
     return t + dec_static;
   };
   auto pre_claim = [&]() {  // thread 0 only
@@ -1424,33 +1444,34 @@ __device__ __forceinline__ void attend_body(const AttendParams& P,
       k ^= 1;
     }
   };
-  auto decode_units = [&](uint32_t idx) {
-    for (uint32_t pass = 0; idx < ndec && pass <= ndec; ++pass) {
-      const uint32_t w = num_pre + idx;
+  auto decode_units = [&](uint32_t k) {  // k: local index in the shard
+    for (uint32_t pass = 0; k < n_s && pass <= n_s; ++pass) {
+      const uint32_t w = num_pre + shard + S * k;
       const WorkItem it = P.items[w / Hkv];
       if (item_ok(P, it) && it.kind == kKindDecode)
-        idx = dec_claimed(run_unit<D, kDecodeColTiles, kDecodeStages, true, KV8>(
-            P, it, (int)(w % Hkv), lane, &P.hdr->work_counter));
+        k = dec_claimed(run_unit<D, kDecodeColTiles, kDecodeStages, true, KV8>(
+            P, it, (int)(w % Hkv), lane, dctr));
       else
-        idx = dec_claimed(claim(&P.hdr->work_counter));
+        k = dec_claimed(claim(dctr));
     }
   };
+  const uint32_t static_k = (blockIdx.x / S - pf_s) * kWpg + wslot;
   if (!mixed) {
-    decode_units(blockIdx.x * kWpg + wslot);
+    decode_units(static_k);
     return;
   }
   const bool prefill_first = blockIdx.x < pre_static;
   uint32_t u = blockIdx.x;
   if (!prefill_first) {
     // decode first, then (all waves done) the prefill units left
-    decode_units((blockIdx.x - pre_static) * kWpg + wslot);
+    decode_units(static_k);
     __syncthreads();
     if (threadIdx.x == 0) next_unit[0] = pre_claim();
     __syncthreads();
     u = __builtin_amdgcn_readfirstlane(next_unit[0]);
   }
   prefill_units(u);
-  if (prefill_first) decode_units(dec_claimed(claim(&P.hdr->work_counter)));
+  if (prefill_first) decode_units(dec_claimed(claim(dctr)));
 }
 
 // Decode-only batches: registers for the 3-stage pipeline (two waves per
@@ -1624,6 +1645,7 @@ AttendParams make_params(const AttendArgs& a) {
   P.out = a.out;
   char* ws = static_cast<char*>(a.workspace);
   P.hdr = reinterpret_cast<PlanHeader*>(ws);
+  P.dec_counters = reinterpret_cast<uint32_t*>(ws + a.ws.counters);
   P.items = reinterpret_cast<WorkItem*>(ws + a.ws.items);
   P.merge_list = reinterpret_cast<int4*>(ws + a.ws.merge_list);
   P.part_ml = reinterpret_cast<float2*>(ws + a.ws.part_ml);

@@ -26,6 +26,10 @@ constexpr int kPrefillColTiles = 2;  // per wave: 32 MFMA columns, 32/G tokens
 constexpr int kPrefillWaves = 4;     // waves sharing one prefill tile's K/V
 constexpr int kMaxGroup = 16;        // query heads per kv head
 constexpr int kAttendThreads = 256;  // 4 waves per workgroup
+// The decode queue is served from kDecodeShards counters, kCounterStride
+// words (4 KiB) apart, so that claims spread over several memory channels.
+constexpr int kDecodeShards = 8;
+constexpr int kCounterStride = 1024;
 // Shared-prefix (cascade) plans: the common prefix is cut into at most
 // kMaxPrefixSplits key ranges of about kPrefixSplitKeys keys each.
 constexpr int kMaxPrefixSplits = 8;
@@ -57,7 +61,6 @@ static_assert(sizeof(WorkItem) == 64, "WorkItem is one 64-byte scalar load");
 
 // Workspace header, at offset 0 of the workspace.
 struct PlanHeader {
-  uint32_t work_counter;  // decode queue head (zeroed by the plan)
   uint32_t num_work;      // items * num_kv_heads (prefill units first)
   uint32_t num_items;
   uint32_t error;         // bit0: capacity exceeded, bit1: bad request skipped
@@ -71,6 +74,7 @@ struct PlanHeader {
 
 // Byte offsets of the workspace sections.
 struct WorkspaceLayout {
+  size_t counters;      // uint32[kDecodeShards * kCounterStride] decode queue heads
   size_t items;         // WorkItem[max_items]
   size_t merge_list;    // int4[max_items]  split tiles: tok0, ntok, nsplit, pbase
   size_t part_ml;       // float2[max_partials * Hq]  (running max, sum)
@@ -130,7 +134,9 @@ inline WorkspaceLayout workspace_layout(int32_t num_seqs, int64_t num_q_tokens,
   int64_t pre_tok = (max_query_len > tq_d) ? T : 0;
   w.max_partials = dec_tok * sd + pre_tok * sp;
   if (w.max_partials < 1) w.max_partials = 1;
-  size_t off = align256(sizeof(PlanHeader));
+  size_t off = 4096;  // the header, then the counters on their own pages
+  w.counters = off;
+  off += sizeof(uint32_t) * kDecodeShards * kCounterStride;
   w.items = off;
   off = align256(off + sizeof(WorkItem) * (size_t)w.max_items);
   w.merge_list = off;
