@@ -433,7 +433,8 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(kernel, w.name), "kernel": kernel,
+            "traffic": measured_traffic(kernel, w.name + (" shared-prefix" if casc else "")),
+            "kernel": kernel,
             "attend_ms": round(attend_ms, 5),
             "algorithmic_bytes": alg["attend_bytes"]},
     }

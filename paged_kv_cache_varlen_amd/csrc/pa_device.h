@@ -33,7 +33,7 @@ constexpr int kCounterStride = 1024;
 // Shared-prefix (cascade) plans: the common prefix is cut into at most
 // kMaxPrefixSplits key ranges of about kPrefixSplitKeys keys each.
 constexpr int kMaxPrefixSplits = 8;
-constexpr int kPrefixSplitKeys = 256;
+constexpr int kPrefixSplitKeys = 2048;
 
 // kKindPrefix: a tile of consecutive query tokens of the whole batch (any
 // requests) against a key range of the common prefix, read through request
