@@ -88,6 +88,10 @@ def _load():
                                           P, I, P, P, I, I, I, I, I,
                                           ctypes.c_float, I, P, I, P, P,
                                           ctypes.c_int]
+        lib.oracle_copy_blocks.restype = None
+        lib.oracle_copy_blocks.argtypes = [P, P, I, I, P, I]
+        lib.oracle_expand_block_tables.restype = None
+        lib.oracle_expand_block_tables.argtypes = [P, I, I, I, P]
         lib.oracle_abi_version.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -298,4 +302,27 @@ def attend_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tables, seq_lens,
                               _p(qsl), B, Hq, num_kv_heads, BLOCK_SIZE, D,
                               float(scale), maxL, rp, nrows, _p(scratch),
                               _p(out), int(nthreads))
+    return out
+
+
+# ---- copy-on-write and larger blocks ----------------------------------------------
+
+def copy_blocks(k_cache: np.ndarray, v_cache: np.ndarray, block_bytes: int,
+                mapping) -> None:
+    """In-place copy-on-write block copies over the pools' bytes (any dtype,
+    C-contiguous): mapping [n][2] of (src, dst) block ids, applied in order."""
+    assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+    assert k_cache.nbytes == v_cache.nbytes and k_cache.nbytes % block_bytes == 0
+    m = _c(mapping, np.int64).reshape(-1, 2)
+    _load().oracle_copy_blocks(_p(k_cache), _p(v_cache), int(block_bytes),
+                               k_cache.nbytes // int(block_bytes), _p(m), m.shape[0])
+
+
+def expand_block_tables(block_tables, block_size: int) -> np.ndarray:
+    """Tables of block_size-token blocks (a multiple of 16) -> 16-token ids."""
+    bt = _c(block_tables, np.int32)
+    R = int(block_size) // BLOCK_SIZE
+    out = np.empty((bt.shape[0], bt.shape[1] * R), np.int32)
+    _load().oracle_expand_block_tables(_p(bt), bt.shape[0], bt.shape[1],
+                                       int(block_size), _p(out))
     return out

@@ -243,6 +243,46 @@ void oracle_gather_kv(const uint16_t *k_cache, const uint16_t *v_cache,
   }
 }
 
+/* ---- copy-on-write and larger blocks ------------------------------------ */
+
+/* Copy-on-write ("vLLM: An Exhaustive Technical Study", section 2.1: a block
+ * held by several requests is duplicated when one of them writes into it).
+ * For each pair (src, dst) = (mapping[2i], mapping[2i+1]), in order, every
+ * byte of block src is copied to block dst in both pools (a block is
+ * block_bytes bytes: all kv heads, K or V).  Pairs naming a block outside
+ * [0, num_blocks), or the same block twice, are skipped. */
+void oracle_copy_blocks(uint8_t *k_cache, uint8_t *v_cache, int64_t block_bytes,
+                        int64_t num_blocks, const int64_t *mapping,
+                        int64_t num_pairs) {
+  for (int64_t i = 0; i < num_pairs; ++i) {
+    int64_t src = mapping[2 * i], dst = mapping[2 * i + 1];
+    if (src < 0 || dst < 0 || src >= num_blocks || dst >= num_blocks || src == dst)
+      continue;
+    for (int64_t b = 0; b < block_bytes; ++b) {
+      k_cache[dst * block_bytes + b] = k_cache[src * block_bytes + b];
+      v_cache[dst * block_bytes + b] = v_cache[src * block_bytes + b];
+    }
+  }
+}
+
+/* Tables of bs-token blocks (bs = R * 16) in 16-token block ids.  With
+ * block size bs, token t of a request is written to slot
+ * table[t / bs] * bs + t % bs (same section); read as a pool of 16-token
+ * blocks, that slot lies in 16-token block slot / 16.  So 16-token block j of
+ * the request (tokens 16j .. 16j+15) is out[j] = slot(16j) / 16.  Entries
+ * < 0 stay -1. */
+void oracle_expand_block_tables(const int32_t *in, int64_t num_seqs,
+                                int64_t in_stride, int64_t bs, int32_t *out) {
+  int64_t R = bs / 16, out_stride = in_stride * R;
+  for (int64_t b = 0; b < num_seqs; ++b) {
+    for (int64_t j = 0; j < out_stride; ++j) {
+      int64_t t = 16 * j;
+      int64_t n = in[b * in_stride + t / bs];
+      out[b * out_stride + j] = n < 0 ? -1 : (int32_t)((n * bs + t % bs) / 16);
+    }
+  }
+}
+
 /* ---- attention ---------------------------------------------------------- */
 
 /* Softmax-weighted sum over keys 0..p of one (query row, head), given the

@@ -57,5 +57,10 @@ void oracle_attend_fp8(const uint16_t *q, const uint8_t *k8, const uint8_t *v8,
                        int64_t D, float scale, int64_t max_seq_len,
                        const int64_t *rows, int64_t num_rows, double *scratch,
                        double *out, int nthreads);
+void oracle_copy_blocks(uint8_t *k_cache, uint8_t *v_cache, int64_t block_bytes,
+                        int64_t num_blocks, const int64_t *mapping,
+                        int64_t num_pairs);
+void oracle_expand_block_tables(const int32_t *in, int64_t num_seqs,
+                                int64_t in_stride, int64_t bs, int32_t *out);
 int oracle_abi_version(void);
 #endif
