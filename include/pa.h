@@ -438,6 +438,52 @@ pa_status pa_validate_cascade_host(const int32_t *block_tables,
                                    int32_t num_seqs, int32_t common_prefix_len);
 
 /*
+ * pa_copy_blocks - the block copy of copy-on-write: for each pair
+ * (src, dst) = (block_mapping[2i], block_mapping[2i+1]), copy every byte of
+ * block src to block dst in both pools (all kv heads, K and V).
+ *
+ *   k_cache, v_cache  device pools of num_blocks blocks: bf16 pools
+ *                     (elem_bytes 2, pa_write_kv) or 8-bit pools (elem_bytes
+ *                     1, pa_write_kv_fp8); one block is
+ *                     num_kv_heads * 16 * head_dim * elem_bytes bytes
+ *   block_mapping     device int64 [num_pairs][2]
+ * A pair naming a block outside [0, num_blocks), or the same block twice, is
+ * skipped.  A block that is the destination of one pair and the source of
+ * another in the same call, or the destination of two pairs, gives undefined
+ * contents.  Asynchronous on `stream`; call it before writing the step's new
+ * tokens into the copies.
+ *
+ * Source: "vLLM: An Exhaustive Technical Study", section 2.1 (blocks shared
+ * by reference count, a block duplicated when a request writes into one whose
+ * count is above 1).
+ */
+pa_status pa_copy_blocks(void *k_cache, void *v_cache, int64_t num_blocks,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t elem_bytes,
+                         const int64_t *block_mapping, int64_t num_pairs,
+                         void *stream);
+
+/*
+ * pa_expand_block_tables - pools with larger blocks.  A block of
+ * block_size = R * 16 tokens (R = 1, 2, 4, ...) is stored as R consecutive
+ * 16-token blocks of the pool: block n holds the 16-token blocks
+ * n*R .. n*R + R-1, so a pool of N such blocks is a pool of N*R 16-token
+ * blocks, and slot_mapping values (n * block_size + offset) are the same
+ * numbers for pa_write_kv.  This call turns block tables of block_size-token
+ * ids into the 16-token tables pa_attend reads:
+ *   out[b][j] = block_tables[b][j / R] * R + j % R,  j < max_blocks_per_seq * R
+ * (entries < 0 stay -1).  out: device int32 [num_seqs][max_blocks_per_seq * R].
+ * Block sizes below 16 (8) are not supported: the kernels' 16-key MFMA tiles
+ * would then span two physical blocks.
+ *
+ * Source: "vLLM: An Exhaustive Technical Study", section 2.1 (block sizes 8,
+ * 16, 32 and larger per platform; the write slot is
+ * block number * block_size + offset).
+ */
+pa_status pa_expand_block_tables(const int32_t *block_tables, int32_t num_seqs,
+                                 int32_t max_blocks_per_seq, int32_t block_size,
+                                 int32_t *out, void *stream);
+
+/*
  * pa_gather_kv - logical gather through the block tables (a checking aid).
  *
  * Writes k_out/v_out, device bf16 [sum_b L_b][num_kv_heads][head_dim]: row

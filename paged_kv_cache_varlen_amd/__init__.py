@@ -320,6 +320,43 @@ def validate_cascade(block_tables, seq_lens, query_start_loc,
     _lib.check(st, "pa_validate_cascade_host")
 
 
+def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor,
+                block_mapping: torch.Tensor, num_kv_heads: int, head_dim: int) -> None:
+    """Copy-on-write block copies: block_mapping int64 [n][2] of (src, dst)
+    block ids; every kv head of both pools (bf16 or 8-bit) is copied."""
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache"), (block_mapping, "block_mapping")):
+        _need_cuda(t, n)
+    _dtype(block_mapping, torch.int64, "block_mapping")
+    if block_mapping.dim() != 2 or block_mapping.shape[1] != 2 or not block_mapping.is_contiguous():
+        raise ValueError("block_mapping must be contiguous [n][2] (src, dst)")
+    if k_cache.dtype != v_cache.dtype or k_cache.dtype not in (torch.bfloat16, torch.uint8):
+        raise ValueError("pools must both be bf16 or both uint8 (8-bit)")
+    nb = _pool_blocks(k_cache, num_kv_heads, head_dim)
+    if _pool_blocks(v_cache, num_kv_heads, head_dim) != nb:
+        raise ValueError("k_cache and v_cache differ in size")
+    st = _lib.load().pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), nb, num_kv_heads,
+                                    head_dim, k_cache.element_size(), _ptr(block_mapping),
+                                    block_mapping.shape[0], _stream(k_cache))
+    _lib.check(st, "pa_copy_blocks")
+
+
+def expand_block_tables(block_tables: torch.Tensor, block_size: int) -> torch.Tensor:
+    """Block tables of block_size-token blocks (a multiple of 16) -> the
+    16-token block tables attend() reads (block n = 16-token blocks
+    n*R .. n*R+R-1, R = block_size // 16)."""
+    _need_cuda(block_tables, "block_tables")
+    _dtype(block_tables, torch.int32, "block_tables")
+    if block_tables.dim() != 2 or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be contiguous [num_seqs][max_blocks]")
+    B, M = block_tables.shape
+    R = max(1, int(block_size) // BLOCK_SIZE)
+    out = torch.empty((B, M * R), dtype=torch.int32, device=block_tables.device)
+    st = _lib.load().pa_expand_block_tables(_ptr(block_tables), B, M, int(block_size),
+                                            _ptr(out), _stream(block_tables))
+    _lib.check(st, "pa_expand_block_tables")
+    return out
+
+
 def gather_kv(k_cache: torch.Tensor, v_cache: torch.Tensor,
               block_tables: torch.Tensor, seq_lens: torch.Tensor,
               kv_start: torch.Tensor, total_rows: int, num_kv_heads: int,

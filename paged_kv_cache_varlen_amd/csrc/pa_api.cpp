@@ -612,6 +612,50 @@ pa_status pa_validate_cascade_host(const int32_t* block_tables,
   return ok();
 }
 
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, int64_t num_blocks,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t elem_bytes,
+                         const int64_t* block_mapping, int64_t num_pairs,
+                         void* stream) {
+  if (num_blocks < 0 || num_pairs < 0)
+    return fail(PA_ERR_SHAPE, "pa_copy_blocks: negative size");
+  if (num_kv_heads <= 0) return fail(PA_ERR_SHAPE, "num_kv_heads must be > 0");
+  if (!supported_head_dim(head_dim))
+    return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (elem_bytes != 1 && elem_bytes != 2)
+    return fail(PA_ERR_SHAPE, "elem_bytes must be 2 (bf16 pools) or 1 (8-bit pools)");
+  if (num_pairs > (int64_t)1 << 30)
+    return fail(PA_ERR_SHAPE, "pa_copy_blocks: too many pairs in one call");
+  if (num_pairs == 0) return ok();
+  if (!k_cache || !v_cache || !block_mapping)
+    return fail(PA_ERR_NULL, "pa_copy_blocks: NULL pointer");
+  if (((uintptr_t)k_cache | (uintptr_t)v_cache) & 15)
+    return fail(PA_ERR_SHAPE, "the pools must be 16-byte aligned");
+  const int64_t block_bytes = (int64_t)num_kv_heads * PA_BLOCK_SIZE * head_dim * elem_bytes;
+  hipError_t e = pa::launch_copy_blocks(k_cache, v_cache, block_bytes, num_blocks,
+                                        block_mapping, num_pairs,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pa_copy_blocks launch");
+  return ok();
+}
+
+pa_status pa_expand_block_tables(const int32_t* block_tables, int32_t num_seqs,
+                                 int32_t max_blocks_per_seq, int32_t block_size,
+                                 int32_t* out, void* stream) {
+  if (num_seqs < 0 || max_blocks_per_seq < 0)
+    return fail(PA_ERR_SHAPE, "pa_expand_block_tables: negative size");
+  if (block_size < PA_BLOCK_SIZE || block_size % PA_BLOCK_SIZE != 0 || block_size > (1 << 16))
+    return fail(PA_ERR_UNSUPPORTED, "block_size must be a multiple of 16 (at most 65536)");
+  const int R = block_size / PA_BLOCK_SIZE;
+  if ((int64_t)max_blocks_per_seq * R > INT32_MAX)
+    return fail(PA_ERR_SHAPE, "pa_expand_block_tables: expanded rows too long");
+  if (num_seqs == 0 || max_blocks_per_seq == 0) return ok();
+  if (!block_tables || !out) return fail(PA_ERR_NULL, "pa_expand_block_tables: NULL pointer");
+  hipError_t e = pa::launch_expand_tables(block_tables, max_blocks_per_seq, num_seqs, R,
+                                          out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pa_expand_block_tables launch");
+  return ok();
+}
+
 pa_status pa_gather_kv(const void* k_cache, const void* v_cache,
                        int64_t num_blocks, const int32_t* block_tables,
                        int32_t max_blocks_per_seq, const int32_t* seq_lens,

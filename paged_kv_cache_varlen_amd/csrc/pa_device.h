@@ -186,6 +186,17 @@ hipError_t launch_gather_kv(const uint16_t* k_cache, const uint16_t* v_cache,
                             uint16_t* k_out, uint16_t* v_out,
                             hipStream_t stream);
 
+// Copy-on-write: copy whole blocks (every kv head) of both pools, for the
+// (src, dst) pairs of `mapping`; block_bytes = bytes of one block in a pool.
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, int64_t block_bytes,
+                              int64_t num_blocks, const int64_t* mapping,
+                              int64_t num_pairs, hipStream_t stream);
+
+// Block tables of R * 16-token blocks -> tables of 16-token block ids.
+hipError_t launch_expand_tables(const int32_t* in, int32_t in_stride,
+                                int32_t num_seqs, int R, int32_t* out,
+                                hipStream_t stream);
+
 struct AttendArgs {
   const uint16_t* q;
   const uint16_t* k_cache;

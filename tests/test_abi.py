@@ -271,3 +271,20 @@ def test_cascade_validator(lib):
     u = W.make_workload("u", [100, 90], [1, 20], 8, 2, 64, seed=1, shared_prefix=64,
                         shared=False)                  # private copies: other ids
     assert validate_cascade(lib, u, 64) == M
+
+
+def test_copy_blocks_argument_checks(lib):
+    assert lib.pa_copy_blocks(FAKE, FAKE, 8, 2, 128, 2, FAKE, 0, None) == _lib.PA_OK
+    assert lib.pa_copy_blocks(FAKE, FAKE, 8, 2, 128, 3, FAKE, 1, None) == _lib.PA_ERR_SHAPE
+    assert lib.pa_copy_blocks(FAKE, FAKE, 8, 2, 96, 2, FAKE, 1, None) == _lib.PA_ERR_UNSUPPORTED
+    assert lib.pa_copy_blocks(None, FAKE, 8, 2, 128, 2, FAKE, 1, None) == _lib.PA_ERR_NULL
+    assert lib.pa_copy_blocks(FAKE + 8, FAKE, 8, 2, 128, 2, FAKE, 1, None) == _lib.PA_ERR_SHAPE
+    assert lib.pa_copy_blocks(FAKE, FAKE, 8, 2, 128, 2, FAKE, -1, None) == _lib.PA_ERR_SHAPE
+
+
+def test_expand_block_tables_argument_checks(lib):
+    assert lib.pa_expand_block_tables(FAKE, 4, 8, 24, FAKE, None) == _lib.PA_ERR_UNSUPPORTED
+    assert lib.pa_expand_block_tables(FAKE, 4, 8, 8, FAKE, None) == _lib.PA_ERR_UNSUPPORTED
+    assert lib.pa_expand_block_tables(None, 4, 8, 32, FAKE, None) == _lib.PA_ERR_NULL
+    assert lib.pa_expand_block_tables(FAKE, 0, 8, 32, FAKE, None) == _lib.PA_OK
+    assert lib.pa_expand_block_tables(FAKE, 4, 1 << 30, 64, FAKE, None) == _lib.PA_ERR_SHAPE
