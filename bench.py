@@ -29,6 +29,7 @@ Prints one JSON line:
   shared_prefix  256 decodes sharing a 2048-token prefix: plain paged
            attention beside shared-prefix (cascade) attention, GB/s of the
            logical and of the unique K/V bytes;
+  block_copy  copy-on-write block copies (4096 pairs) on the headline pool;
   cpu_baseline  the CPU oracle (fp64) on the same headline workload.
 
     python bench.py [--steps K] [--warmup W] [--config 2] [--no-mixed]
@@ -63,6 +64,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the streaming-read ceiling probe")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time the workload over 8-bit (E4M3) pools")
     ap.add_argument("--cascade", action="store_true",
                     help="time the workload's shared-prefix attention calls "
                          "(config 4: the 2048-token prefix attended once)")
@@ -347,6 +350,33 @@ def shared_prefix_runs(args, W):
     return out
 
 
+def block_copy_run(W):
+    """Copy-on-write block copies on the headline decode layer's pool: 4096
+    random (src, dst) pairs, every kv head of both pools; GB/s of bytes read
+    plus written."""
+    import torch
+    import paged_kv_cache_varlen_amd as pa
+    w = W.make_config(2)
+    kc, vc = pa.alloc_pool(w.num_blocks, w.num_kv_heads, w.head_dim, fill=0.0)
+    rng = np.random.default_rng(7)
+    ids = rng.permutation(w.num_blocks)[:8192]
+    mapping = torch.from_numpy(ids.reshape(2, 4096).T.copy().astype(np.int64)).cuda()
+    n = 20
+    for _ in range(3):
+        pa.copy_blocks(kc, vc, mapping, w.num_kv_heads, w.head_dim)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n):
+        pa.copy_blocks(kc, vc, mapping, w.num_kv_heads, w.head_dim)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / n
+    moved = 4096 * 2 * 2 * w.num_kv_heads * 16 * w.head_dim * 2
+    return {"pairs": 4096, "block_bytes_per_pool": w.num_kv_heads * 16 * w.head_dim * 2,
+            "ms": round(ms, 5), "gbs": round(moved / (ms * 1e-3) / 1e9, 1),
+            "hbm_peak_frac": round(moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def read_ceiling(torch, gib=4):
     """Measured streaming-read ceiling of this box: the best of a few grid
     sizes of the probe kernel (libpa_probe.so) reading a 4 GiB buffer once
@@ -403,15 +433,21 @@ def main():
     if args.cascade and not casc:
         print("--cascade needs a workload with a shared prefix (config 4)", file=sys.stderr)
         return 2
-    r = Runner(w, args.min_working_set_gib, cascade=casc)
+    r = Runner(w, args.min_working_set_gib, fp8=FP8_SCALES if args.fp8 else None,
+               cascade=casc)
     ms_step, attend_ms = r.run(args.steps, args.warmup)
-    kernel = ("attend_decode_kernel<%d, false>" if casc is None and w.max_query_len <= 16 // (
-        w.num_q_heads // w.num_kv_heads) else "attend_mixed_kernel<%d, false>") % w.head_dim
+    kernel = ("attend_decode_kernel<%d, %s>" if casc is None and w.max_query_len <= 16 // (
+        w.num_q_heads // w.num_kv_heads) else "attend_mixed_kernel<%d, %s>") % (
+        w.head_dim, "true" if args.fp8 else "false")
     kv_gbs = alg["kv_bytes"] / (ms_step * 1e-3) / 1e9
     if casc:
         # shared-prefix attention reads the prefix once: its algorithmic
         # bytes are the distinct tokens' K/V (plus the same q, out, metadata)
         alg["attend_bytes"] += unique_kv_bytes(w) - alg["kv_bytes"]
+    if args.fp8:
+        # 8-bit pools: one byte per K or V element
+        alg["attend_bytes"] -= alg["kv_bytes"] // 2
+        alg["kv_bytes"] //= 2
     achieved = alg["attend_bytes"] / (attend_ms * 1e-3) / 1e9
     line = {
         "metric": "paged-attn KV read GB/s (% HBM peak) + mixed-step tokens/s per layer",
@@ -425,7 +461,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "e4m3 K/V codes, bf16 q/out" if args.fp8 else "bf16",
         "data": "synthetic (seeded N(0,1) bf16 q/K/V, seeded block tables)",
         "config": dict(W.Workload.describe(w), layers_cycled=len(r.layers),
                        **({"shared_prefix_attention": casc} if casc else {})),
@@ -433,7 +469,8 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(kernel, w.name + (" shared-prefix" if casc else "")),
+            "traffic": measured_traffic(kernel, w.name + (" shared-prefix" if casc else "")
+                                        + (" fp8" if args.fp8 else "")),
             "kernel": kernel,
             "attend_ms": round(attend_ms, 5),
             "algorithmic_bytes": alg["attend_bytes"]},
@@ -491,6 +528,7 @@ def main():
         torch.cuda.empty_cache()
         line["fp8_kv"] = fp8_runs(args, W)
         line["shared_prefix"] = shared_prefix_runs(args, W)
+        line["block_copy"] = block_copy_run(W)
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
