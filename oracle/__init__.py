@@ -92,6 +92,13 @@ def _load():
         lib.oracle_copy_blocks.argtypes = [P, P, I, I, P, I]
         lib.oracle_expand_block_tables.restype = None
         lib.oracle_expand_block_tables.argtypes = [P, I, I, I, P]
+        lib.oracle_mla_index.restype = ctypes.c_size_t
+        lib.oracle_mla_index.argtypes = [I, I, I]
+        lib.oracle_mla_write_kv.restype = None
+        lib.oracle_mla_write_kv.argtypes = [P, P, P, I]
+        lib.oracle_mla_decode.restype = None
+        lib.oracle_mla_decode.argtypes = [P, P, P, I, P, P, I, I, ctypes.c_float, P,
+                                          ctypes.c_int]
         lib.oracle_abi_version.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -325,4 +332,41 @@ def expand_block_tables(block_tables, block_size: int) -> np.ndarray:
     out = np.empty((bt.shape[0], bt.shape[1] * R), np.int32)
     _load().oracle_expand_block_tables(_p(bt), bt.shape[0], bt.shape[1],
                                        int(block_size), _p(out))
+    return out
+
+
+# ---- MLA latent cache ------------------------------------------------------------
+
+MLA_BLOCK = 64
+MLA_DL = 576   # latent (512) + rotary (64) dims cached per token
+MLA_DV = 512   # latent dims summed into the output
+
+
+def mla_index(n, t, d) -> int:
+    """Flat element offset of dim d of token t of block n in an MLA cache."""
+    return int(_load().oracle_mla_index(n, t, d))
+
+
+def mla_write_kv(cache: np.ndarray, kv: np.ndarray, slot_mapping) -> None:
+    """In-place scatter of kv ([T][576] uint16 bits) into the MLA cache."""
+    assert cache.dtype == np.uint16 and cache.flags.c_contiguous
+    kv = _c(kv, np.uint16)
+    sm = _c(slot_mapping, np.int64)
+    assert kv.shape == (sm.shape[0], MLA_DL)
+    _load().oracle_mla_write_kv(_p(cache), _p(kv), _p(sm), sm.shape[0])
+
+
+def mla_decode(q, cache, block_tables, seq_lens, query_start_loc, scale,
+               nthreads=None) -> np.ndarray:
+    """MLA attention (fp64): q [T][Hq][576] uint16 bits -> [T][Hq][512]."""
+    q = _c(q, np.uint16)
+    T, Hq, Dl = q.shape
+    assert Dl == MLA_DL
+    bt = _c(block_tables, np.int32)
+    sl = _c(seq_lens, np.int32)
+    qsl = _c(query_start_loc, np.int32)
+    out = np.zeros((T, Hq, MLA_DV), np.float64)
+    _load().oracle_mla_decode(_p(q), _p(cache), _p(bt), bt.shape[1], _p(sl), _p(qsl),
+                              sl.shape[0], Hq, float(scale), _p(out),
+                              nthreads or default_threads())
     return out

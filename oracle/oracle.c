@@ -37,6 +37,7 @@
  *    V tile of 16*D bf16 each, permuted inside the tile).
  */
 #include <math.h>
+#include <stdlib.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <string.h>
@@ -279,6 +280,88 @@ void oracle_expand_block_tables(const int32_t *in, int64_t num_seqs,
       int64_t t = 16 * j;
       int64_t n = in[b * in_stride + t / bs];
       out[b * out_stride + j] = n < 0 ? -1 : (int32_t)((n * bs + t % bs) / 16);
+    }
+  }
+}
+
+/* ---- MLA latent cache ----------------------------------------------------- */
+
+/* Multi-head latent attention ("vLLM: An Exhaustive Technical Study",
+ * section 2.4, the MLA paragraph): one latent vector per token, shared by all
+ * query heads, of MLA_DL = 512 latent + 64 rotary dims, in blocks of 64
+ * tokens; decode attends MQA-style on the latent.  Reading: a query head's
+ * score of token j is scale * (its 576-dim query . token j's 576-dim cached
+ * vector), and its output is the softmax-weighted sum of the first
+ * MLA_DV = 512 (latent) dims of those vectors.
+ *
+ * Cache layout (the library's choice, documented with the C ABI): block n
+ * holds 64 * 576 bf16; token t, dim d of the block sits at
+ * (((t / 16) * 18 + d / 32) * 16 + t % 16) * 32 + d % 32. */
+#define MLA_BS 64
+#define MLA_DL 576
+#define MLA_DV 512
+
+static size_t mla_index(int64_t n, int64_t t, int64_t d) {
+  return (size_t)(n * MLA_BS * MLA_DL +
+                  (((t / 16) * (MLA_DL / 32) + d / 32) * 16 + t % 16) * 32 + d % 32);
+}
+
+size_t oracle_mla_index(int64_t n, int64_t t, int64_t d) { return mla_index(n, t, d); }
+
+/* For each token i with slot s = slot_mapping[i] >= 0: block s / 64, offset
+ * s % 64; copy the bits of kv[i][0..575] there. */
+void oracle_mla_write_kv(uint16_t *cache, const uint16_t *kv,
+                         const int64_t *slot_mapping, int64_t num_tokens) {
+  for (int64_t i = 0; i < num_tokens; ++i) {
+    int64_t s = slot_mapping[i];
+    if (s < 0) continue;
+    for (int64_t d = 0; d < MLA_DL; ++d)
+      cache[mla_index(s / MLA_BS, s % MLA_BS, d)] = kv[i * MLA_DL + d];
+  }
+}
+
+/* out[t][h][e] (fp64) for every query token t of every request b: query i of
+ * the request's Q = qsl[b+1] - qsl[b] tokens sits at p = L - Q + i and sees
+ * tokens 0..p; token j's vector is read from block block_tables[b][j / 64],
+ * offset j % 64. */
+void oracle_mla_decode(const uint16_t *q, const uint16_t *cache,
+                       const int32_t *block_tables, int64_t bt_stride,
+                       const int32_t *seq_lens, const int32_t *query_start_loc,
+                       int64_t num_seqs, int64_t Hq, float scale, double *out,
+                       int nthreads) {
+  const double sigma = (double)scale;
+  for (int64_t b = 0; b < num_seqs; ++b) {
+    int64_t q0 = query_start_loc[b], Q = query_start_loc[b + 1] - q0;
+    int64_t L = seq_lens[b];
+    int64_t rows = Q * Hq;
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic)
+    for (int64_t r = 0; r < rows; ++r) {
+      int64_t i = r / Hq, h = r % Hq, t = q0 + i, p = L - Q + i;
+      double *s = (double *)malloc(sizeof(double) * (size_t)(p + 1));
+      double m = -INFINITY;
+      for (int64_t j = 0; j <= p; ++j) {
+        int64_t n = block_tables[b * bt_stride + j / MLA_BS];
+        double acc = 0.0;
+        for (int64_t d = 0; d < MLA_DL; ++d)
+          acc += bf16_to_double(q[(t * Hq + h) * MLA_DL + d]) *
+                 bf16_to_double(cache[mla_index(n, j % MLA_BS, d)]);
+        s[j] = sigma * acc;
+        if (s[j] > m) m = s[j];
+      }
+      double den = 0.0;
+      for (int64_t j = 0; j <= p; ++j) {
+        s[j] = exp(s[j] - m);
+        den += s[j];
+      }
+      for (int64_t e = 0; e < MLA_DV; ++e) {
+        double num = 0.0;
+        for (int64_t j = 0; j <= p; ++j) {
+          int64_t n = block_tables[b * bt_stride + j / MLA_BS];
+          num += s[j] * bf16_to_double(cache[mla_index(n, j % MLA_BS, e)]);
+        }
+        out[(t * Hq + h) * MLA_DV + e] = num / den;
+      }
+      free(s);
     }
   }
 }

@@ -62,5 +62,13 @@ void oracle_copy_blocks(uint8_t *k_cache, uint8_t *v_cache, int64_t block_bytes,
                         int64_t num_pairs);
 void oracle_expand_block_tables(const int32_t *in, int64_t num_seqs,
                                 int64_t in_stride, int64_t bs, int32_t *out);
+size_t oracle_mla_index(int64_t n, int64_t t, int64_t d);
+void oracle_mla_write_kv(uint16_t *cache, const uint16_t *kv,
+                         const int64_t *slot_mapping, int64_t num_tokens);
+void oracle_mla_decode(const uint16_t *q, const uint16_t *cache,
+                       const int32_t *block_tables, int64_t bt_stride,
+                       const int32_t *seq_lens, const int32_t *query_start_loc,
+                       int64_t num_seqs, int64_t Hq, float scale, double *out,
+                       int nthreads);
 int oracle_abi_version(void);
 #endif
