@@ -484,6 +484,55 @@ pa_status pa_expand_block_tables(const int32_t *block_tables, int32_t num_seqs,
                                  int32_t *out, void *stream);
 
 /*
+ * Multi-head latent attention (MLA) over a paged latent cache.
+ *
+ * Source: "vLLM: An Exhaustive Technical Study", section 2.4 (the MLA
+ * paragraph): one low-rank latent vector cached per token, shared by every
+ * query head and attended MQA-style in decode; 512 latent + 64 decoupled
+ * rotary dims = 576 cached values per token; blocks of 64 tokens.
+ * Reading: a query head supplies a 576-dim query (its latent-space part
+ * and its rotary part); its score of token j is scale * (query . cached vector
+ * j), and its output is the softmax-weighted sum of the first 512 (latent)
+ * dims of the cached vectors -- the up- and output projections around this
+ * step are the caller's.  Causal as pa_attend: query i of a request's Q new
+ * tokens sits at L - Q + i and sees tokens 0 .. L - Q + i.
+ *
+ * Cache: bf16, num_blocks blocks of 64 * 576 elements; token t (0..63), dim d
+ * of a block sit at element (((t / 16) * 18 + d / 32) * 16 + t % 16) * 32 + d % 32.
+ * slot = block * 64 + offset.
+ *
+ * pa_mla_write_kv - scatter kv (device bf16, row i of 576 values at
+ *   kv + i * kv_token_stride elements; stride a multiple of 8) into the cache
+ *   at slot_mapping[i] (device int64; < 0 or >= num_blocks * 64: skipped).
+ * pa_mla_workspace_size - workspace bytes of pa_mla_decode (split partials);
+ *   0 for invalid arguments.
+ * pa_mla_decode - q device bf16 [num_q_tokens][num_q_heads][576], out device
+ *   bf16 [num_q_tokens][num_q_heads][512]; block_tables of 64-token block ids
+ *   [num_seqs][max_blocks_per_seq]; seq_lens, query_start_loc as pa_attend;
+ *   num_q_heads a multiple of 16, at most 128, and max_seq_len at most
+ *   262144 (PA_ERR_UNSUPPORTED otherwise);
+ *   workspace >= pa_mla_workspace_size(...) bytes, 256-byte aligned.  A
+ *   request whose metadata is out of bounds is skipped (its rows unwritten).
+ */
+#define PA_MLA_BLOCK_SIZE 64
+#define PA_MLA_DIM 576
+#define PA_MLA_LATENT 512
+
+size_t pa_mla_workspace_size(int64_t num_q_tokens, int32_t num_q_heads,
+                             int32_t max_seq_len);
+
+pa_status pa_mla_write_kv(const void *kv, int64_t kv_token_stride,
+                          const int64_t *slot_mapping, int64_t num_tokens, void *cache,
+                          int64_t num_blocks, void *stream);
+
+pa_status pa_mla_decode(const void *q, const void *cache, int64_t num_blocks,
+                        const int32_t *block_tables, int32_t max_blocks_per_seq,
+                        const int32_t *seq_lens, const int32_t *query_start_loc,
+                        int32_t num_seqs, int64_t num_q_tokens, int32_t num_q_heads,
+                        int32_t max_seq_len, float scale, void *out, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/*
  * pa_gather_kv - logical gather through the block tables (a checking aid).
  *
  * Writes k_out/v_out, device bf16 [sum_b L_b][num_kv_heads][head_dim]: row

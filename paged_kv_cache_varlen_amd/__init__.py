@@ -357,6 +357,77 @@ def expand_block_tables(block_tables: torch.Tensor, block_size: int) -> torch.Te
     return out
 
 
+MLA_BLOCK_SIZE = 64
+MLA_DIM = 576
+MLA_LATENT = 512
+
+
+def alloc_mla_cache(num_blocks: int, device="cuda",
+                    fill: Optional[float] = None) -> torch.Tensor:
+    """A latent cache: bf16 [num_blocks][64 * 576] in the library's layout."""
+    shape = (num_blocks, MLA_BLOCK_SIZE * MLA_DIM)
+    if fill is None:
+        return torch.empty(shape, dtype=torch.bfloat16, device=device)
+    return torch.full(shape, fill, dtype=torch.bfloat16, device=device)
+
+
+def mla_write_kv(kv: torch.Tensor, slot_mapping: torch.Tensor,
+                 cache: torch.Tensor) -> None:
+    """Scatter kv [T][576] bf16 (rows may be strided) into the latent cache
+    at slot_mapping (int64, block * 64 + offset; < 0 skipped)."""
+    for t, n in ((kv, "kv"), (slot_mapping, "slot_mapping"), (cache, "cache")):
+        _need_cuda(t, n)
+    _dtype(kv, torch.bfloat16, "kv")
+    _dtype(cache, torch.bfloat16, "cache")
+    _dtype(slot_mapping, torch.int64, "slot_mapping")
+    if kv.dim() != 2 or kv.shape[1] != MLA_DIM or kv.stride(1) != 1:
+        raise ValueError("kv must be [T][576] with unit stride along the dims")
+    if not cache.is_contiguous() or cache.numel() % (MLA_BLOCK_SIZE * MLA_DIM):
+        raise ValueError("cache must be contiguous [num_blocks][64 * 576]")
+    nb = cache.numel() // (MLA_BLOCK_SIZE * MLA_DIM)
+    st = _lib.load().pa_mla_write_kv(_ptr(kv), kv.stride(0), _ptr(slot_mapping),
+                                     kv.shape[0], _ptr(cache), nb, _stream(kv))
+    _lib.check(st, "pa_mla_write_kv")
+
+
+def mla_workspace(num_q_tokens: int, num_q_heads: int, max_seq_len: int,
+                  device="cuda") -> torch.Tensor:
+    n = _lib.load().pa_mla_workspace_size(num_q_tokens, num_q_heads, max_seq_len)
+    if n == 0:
+        raise ValueError("invalid arguments for pa_mla_workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def mla_decode(q: torch.Tensor, cache: torch.Tensor, block_tables: torch.Tensor,
+               seq_lens: torch.Tensor, query_start_loc: torch.Tensor, scale: float,
+               max_seq_len: int, out: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """MLA attention of q [T][Hq][576] bf16 over the latent cache (64-token
+    block tables) -> out [T][Hq][512] bf16."""
+    for t, n in ((q, "q"), (cache, "cache"), (block_tables, "block_tables"),
+                 (seq_lens, "seq_lens"), (query_start_loc, "query_start_loc")):
+        _need_cuda(t, n)
+    _dtype(q, torch.bfloat16, "q")
+    _dtype(cache, torch.bfloat16, "cache")
+    _dtype(block_tables, torch.int32, "block_tables")
+    if q.dim() != 3 or q.shape[2] != MLA_DIM or not q.is_contiguous():
+        raise ValueError("q must be contiguous [T][Hq][576]")
+    T, Hq, _ = q.shape
+    B = block_tables.shape[0]
+    nb = cache.numel() // (MLA_BLOCK_SIZE * MLA_DIM)
+    if out is None:
+        out = torch.empty((T, Hq, MLA_LATENT), dtype=torch.bfloat16, device=q.device)
+    if workspace is None:
+        workspace = mla_workspace(T, Hq, max_seq_len, device=q.device)
+    st = _lib.load().pa_mla_decode(_ptr(q), _ptr(cache), nb, _ptr(block_tables),
+                                   block_tables.shape[1], _ptr(seq_lens),
+                                   _ptr(query_start_loc), B, T, Hq, int(max_seq_len),
+                                   float(scale), _ptr(out), _ptr(workspace),
+                                   workspace.numel(), _stream(q))
+    _lib.check(st, "pa_mla_decode")
+    return out
+
+
 def gather_kv(k_cache: torch.Tensor, v_cache: torch.Tensor,
               block_tables: torch.Tensor, seq_lens: torch.Tensor,
               kv_start: torch.Tensor, total_rows: int, num_kv_heads: int,

@@ -18,7 +18,7 @@ PROBE_LIB = os.path.join(PKG, "libpa_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["kv_cache.hip", "blocks.hip", "attend.hip", "pa_api.cpp"]
+SOURCES = ["kv_cache.hip", "blocks.hip", "mla.hip", "attend.hip", "pa_api.cpp"]
 # Packed-FP32 VALU forms are kept out of the generated code on purpose.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -57,6 +57,10 @@ SIGNATURES = {
     "pa_validate_cascade_host": (STATUS, [P, I32, P, P, I32, I32]),
     "pa_copy_blocks": (STATUS, [P, P, I64, I32, I32, I32, P, I64, P]),
     "pa_expand_block_tables": (STATUS, [P, I32, I32, I32, P, P]),
+    "pa_mla_workspace_size": (SZ, [I64, I32, I32]),
+    "pa_mla_write_kv": (STATUS, [P, I64, P, I64, P, I64, P]),
+    "pa_mla_decode": (STATUS, [P, P, I64, P, I32, P, P, I32, I64, I32, I32, F32, P, P, SZ,
+                               P]),
     "pa_gather_kv": (STATUS, [P, P, I64, P, I32, P, P, I32, I64, I32, I32, P, P,
                               P]),
     "pa_validate_metadata_host": (STATUS, [P, I32, P, P, I32, I64, I32, I32, I64,

@@ -1,0 +1,296 @@
+// Multi-head latent attention (MLA) over a paged latent cache: one 576-dim
+// vector per token (512 latent + 64 rotary dims) shared by every query head,
+// in blocks of 64 tokens; decode attends MQA-style on the latent.
+//
+// Cache layout: block n holds 64 * 576 bf16; token t, dim d of the block is
+// element (((t / 16) * 18 + d / 32) * 16 + t % 16) * 32 + d % 32, so one
+// 16-token x 32-dim piece is 1 KiB contiguous: a wave loads the score operand
+// of 16 keys for one 32-dim k step with one 16-byte load per lane.
+//
+// Decode (mla_decode_kernel): one workgroup of two waves per (query token,
+// key split, group of 16 query heads).  For each 16 keys, wave w loads the
+// 9 of the 18 32-dim chunks it owns (latent chunks 8w .. 8w+7 and one rotary
+// chunk), computes its share of S^T = K Q^T against the 16 heads, and takes
+// the other wave's share through LDS; both then run the same online softmax,
+// and wave w accumulates output dims 256w .. 256w+255.  The PV product needs each lane to
+// hold 4 consecutive keys of one dim, while the cache rows hold consecutive
+// dims of one key: an MFMA against a 0/1 selection matrix moves a 16-key x
+// 16-dim piece of the key operand into that form (exact: every product is
+// x * 1 or x * 0 and the sums have one nonzero term), so the latent is stored
+// and read once.
+#include "pa_device.h"
+
+namespace pa {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kKc = kMlaDim / 32;      // 18 score k steps
+constexpr int kLatC = kMlaLatent / 32;  // 16 latent chunks of 32 dims
+constexpr int kMlaThreads = 128;        // two waves
+constexpr int kChunks = kLatC / 2 + 1;  // score k steps per wave
+
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+      __builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+// Maximum over the four lanes r, r+16, r+32, r+48 (the rows of MFMA column r).
+__device__ __forceinline__ float column_max(float x) {
+  const uint32_t xb = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane32_swap(xb, xb, false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t yb = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane16_swap(yb, yb, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Request of query token t: the last b with qsl[b] <= t (qsl non-decreasing).
+__device__ __forceinline__ int request_of(const int32_t* qsl, int num_seqs, int t) {
+  int lo = 0, hi = num_seqs;  // answer in [lo, hi)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (qsl[mid] <= t) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Keys token t sees (0 when its request's metadata is out of bounds).
+__device__ __forceinline__ int visible_keys(const MlaParams& P, int t, int* b_out) {
+  const int b = request_of(P.qsl, P.num_seqs, t);
+  const int q0 = P.qsl[b], q1 = P.qsl[b + 1], L = P.seq_lens[b];
+  *b_out = b;
+  if (q0 < 0 || t < q0 || t >= q1 || q1 - q0 > L || L > P.max_seq_len ||
+      (L + kMlaBlock - 1) / kMlaBlock > P.bt_stride)
+    return 0;
+  return L - (q1 - t) + 1;  // query t - q0 sits at L - Q + (t - q0)
+}
+
+__global__ __launch_bounds__(256) void mla_write_kv_kernel(
+    const uint16_t* __restrict__ kv, int64_t stride, const int64_t* __restrict__ slots,
+    int64_t num_tokens, uint16_t* __restrict__ cache, int64_t num_blocks) {
+  // thread: (token, 8-dim piece); 72 pieces per token
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= num_tokens * (kMlaDim / 8)) return;
+  const int64_t tok = i / (kMlaDim / 8);
+  const int d = (int)(i - tok * (kMlaDim / 8)) * 8;
+  const int64_t s = slots[tok];
+  if (s < 0 || s >= num_blocks * kMlaBlock) return;
+  const int64_t n = s / kMlaBlock;
+  const int t = (int)(s - n * kMlaBlock);
+  const int64_t off = n * (int64_t)kMlaBlock * kMlaDim +
+                      (((t >> 4) * kKc + (d >> 5)) * 16 + (t & 15)) * 32 + (d & 31);
+  *reinterpret_cast<uint4*>(cache + off) =
+      *reinterpret_cast<const uint4*>(kv + tok * stride + d);
+}
+
+__global__ __launch_bounds__(kMlaThreads, 2) void mla_decode_kernel(MlaParams P) {
+  // partial scores of the two waves, two tiles deep
+  __shared__ f32x4 sx[2][2][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int nhg = P.Hq / 16;
+  const int unit = blockIdx.x;
+  const int hg = unit % nhg;
+  const int s = (unit / nhg) % P.max_splits;
+  const int t = unit / nhg / P.max_splits;
+  int b;
+  const int nvis = visible_keys(P, t, &b);
+  const int nsplit = (nvis + P.split - 1) / P.split;
+  if (s >= nsplit) return;
+  const int k0 = s * P.split, k1 = min(nvis, k0 + P.split);
+
+  // Wave w owns latent chunks 8w .. 8w+7 (its output dims) and rotary chunk
+  // 16 + w: kChunks of the 18 score k steps.  Its query operands: lane (r, g)
+  // of chunk c holds dims 32c + 8g .. +7 of head r.
+  auto chunk = [&](int i) { return i < kLatC / 2 ? (kLatC / 2) * w + i : kLatC + w; };
+  const uint16_t* qp = P.q + ((int64_t)t * P.Hq + hg * 16 + r) * kMlaDim + 8 * g;
+  bf16x8 qop[kChunks];
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i)
+    qop[i] = *reinterpret_cast<const bf16x8*>(qp + 32 * chunk(i));
+  // 0/1 selection operands: E_j[k][n] = 1 where k = 16j + n (lane (r, g)
+  // holds rows 8g .. 8g+7 of column r)
+  bf16x8 sel[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sel[j][i] = (__bf16)((8 * g + i == 16 * j + r) ? 1.0f : 0.0f);
+
+  // block ids of the split (at most 64), one per lane
+  const int jb0 = k0 / kMlaBlock;
+  const int nblk = (k1 + kMlaBlock - 1) / kMlaBlock - jb0;
+  int idv = 0;
+  if (lane < nblk) idv = P.bt[(int64_t)b * P.bt_stride + jb0 + lane];
+  idv = idv < 0 ? 0 : (idv >= P.num_blocks ? (int)(P.num_blocks - 1) : idv);
+
+  f32x4 acc[kLatC];  // this wave's 8 latent chunks x 2 dim tiles of 16
+#pragma unroll
+  for (int k = 0; k < kLatC; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mrun = -INFINITY, lsum = 0.0f;
+  const float c2 = P.scale_log2;
+
+  const int ntiles = (k1 - k0 + 15) / 16;  // 16-key tiles of the split
+  auto load_tile = [&](bf16x8 (&kop)[kChunks], int tile) {
+    const int key = k0 + 16 * tile;
+    const int id = __builtin_amdgcn_readlane(idv, (key / kMlaBlock) - jb0);
+    // the piece of (16-key tile, chunk) is [16 tokens][32 dims]: lane (r, g)
+    // reads token r, dims 8g .. 8g+7
+    const uint16_t* base = P.cache + (int64_t)id * kMlaBlock * kMlaDim +
+                           ((key % kMlaBlock) >> 4) * kKc * 512 + r * 32 + g * 8;
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i)
+      kop[i] = __builtin_nontemporal_load(
+          reinterpret_cast<const bf16x8*>(base + chunk(i) * 512));
+  };
+  auto compute = [&](const bf16x8 (&kop)[kChunks], int tile) {
+    const int key0 = k0 + 16 * tile;
+    // this wave's share of the scores, then the other wave's through LDS
+    // (a + b == b + a in IEEE arithmetic: both waves hold the same sum)
+    f32x4 part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) part = mfma32(kop[i], qop[i], part);
+    sx[tile & 1][w][lane] = part;
+    __syncthreads();
+    const f32x4 sc = part + sx[tile & 1][w ^ 1][lane];
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = (key0 + 4 * g + i < k1) ? sc[i] : -INFINITY;
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mx = column_max(mx);
+    const float mnew = fmaxf(mrun, mx * c2);
+    const float muse = (mnew == -INFINITY) ? 0.0f : mnew;
+    const float alpha = __builtin_amdgcn_exp2f(mrun - muse);
+    mrun = mnew;
+    bf16x4 p;
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(x[i], c2, -muse));
+      psum += (float)p[i];
+    }
+    lsum = lsum * alpha + psum;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+      for (int k = 0; k < kLatC; ++k) acc[k] *= alpha;
+    }
+    // keys past the split end may be unwritten slots: their V rows are zeroed
+    // (a 0 weight must not meet a NaN)
+#pragma unroll
+    for (int cc = 0; cc < kLatC / 2; ++cc) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const f32x4 tv = mfma32(kop[cc], sel[j], f32x4{0.f, 0.f, 0.f, 0.f});
+        bf16x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          v[i] = (key0 + 4 * g + i < k1) ? (__bf16)tv[i] : (__bf16)0.0f;
+        acc[2 * cc + j] = mfma16(v, p, acc[2 * cc + j]);
+      }
+    }
+  };
+  // two tiles in flight: the loads of tile i+1 are issued before tile i is
+  // computed (the last prefetch repeats the last tile); both waves run the
+  // same number of steps (one barrier each)
+  bf16x8 ka[kChunks], kb[kChunks];
+  load_tile(ka, 0);
+  for (int i = 0; i < ntiles; i += 2) {
+    load_tile(kb, min(i + 1, ntiles - 1));
+    compute(ka, i);
+    load_tile(ka, min(i + 2, ntiles - 1));
+    if (i + 1 < ntiles) compute(kb, i + 1);
+  }
+
+  float l = lsum;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  const int h = hg * 16 + r;
+  if (nsplit == 1) {
+    const float inv = 1.0f / l;
+    uint16_t* op = P.out + ((int64_t)t * P.Hq + h) * kMlaLatent + 256 * w + 4 * g;
+#pragma unroll
+    for (int k = 0; k < kLatC; ++k) {
+      bf16x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = (__bf16)(acc[k][i] * inv);
+      *reinterpret_cast<bf16x4*>(op + 16 * k) = o;
+    }
+    return;
+  }
+  const int64_t row = ((int64_t)t * P.Hq + h) * P.max_splits + s;
+  float* ap = P.part_acc + row * kMlaLatent + 256 * w + 4 * g;
+#pragma unroll
+  for (int k = 0; k < kLatC; ++k) *reinterpret_cast<f32x4*>(ap + 16 * k) = acc[k];
+  if (w == 0 && g == 0) P.part_ml[row] = make_float2(mrun, l);
+}
+
+// One wave per (query token, head) whose keys were split: online log-sum-exp
+// over its splits in order; lane i holds dims 8i .. 8i+7.
+__global__ __launch_bounds__(256) void mla_merge_kernel(MlaParams P) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row0 = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row0 >= (int64_t)P.num_q_tokens * P.Hq) return;
+  const int t = (int)(row0 / P.Hq);
+  int b;
+  const int nvis = visible_keys(P, t, &b);
+  const int nsplit = (nvis + P.split - 1) / P.split;
+  if (nsplit < 2 || nsplit > P.max_splits) return;
+  float M = -INFINITY, den = 0.0f;
+  f32x4 n0 = {0.f, 0.f, 0.f, 0.f}, n1 = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < nsplit; ++s) {
+    const int64_t row = row0 * P.max_splits + s;
+    const float2 ml = P.part_ml[row];
+    const f32x4* ap = reinterpret_cast<const f32x4*>(P.part_acc + row * kMlaLatent + 8 * lane);
+    const f32x4 a0 = ap[0], a1 = ap[1];
+    const float mn = fmaxf(M, ml.x);
+    const float mu = (mn == -INFINITY) ? 0.0f : mn;
+    const float c_old = __builtin_amdgcn_exp2f(M - mu);
+    const float c_new = __builtin_amdgcn_exp2f(ml.x - mu);
+    den = den * c_old + ml.y * c_new;
+    n0 = n0 * c_old + a0 * c_new;
+    n1 = n1 * c_old + a1 * c_new;
+    M = mn;
+  }
+  const float inv = 1.0f / den;
+  bf16x8 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[i] = (__bf16)(n0[i] * inv);
+    o[i + 4] = (__bf16)(n1[i] * inv);
+  }
+  *reinterpret_cast<bf16x8*>(P.out + row0 * kMlaLatent + 8 * lane) = o;
+}
+
+}  // namespace
+
+hipError_t launch_mla_write_kv(const uint16_t* kv, int64_t stride, const int64_t* slots,
+                               int64_t num_tokens, uint16_t* cache, int64_t num_blocks,
+                               hipStream_t stream) {
+  const int64_t n = num_tokens * (kMlaDim / 8);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(mla_write_kv_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     stream, kv, stride, slots, num_tokens, cache, num_blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_decode(const MlaParams& P, hipStream_t stream) {
+  if (P.num_q_tokens == 0 || P.num_seqs == 0) return hipSuccess;
+  const int64_t units = (int64_t)P.num_q_tokens * P.max_splits * (P.Hq / 16);
+  hipLaunchKernelGGL(mla_decode_kernel, dim3((unsigned)units), dim3(kMlaThreads), 0,
+                     stream, P);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || P.max_splits < 2) return e;
+  const int64_t rows = (int64_t)P.num_q_tokens * P.Hq;
+  hipLaunchKernelGGL(mla_merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
+                     stream, P);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -656,6 +656,97 @@ pa_status pa_expand_block_tables(const int32_t* block_tables, int32_t num_seqs,
   return ok();
 }
 
+// ---- multi-head latent attention ----------------------------------------
+
+static_assert(pa::kMlaDim == PA_MLA_DIM && pa::kMlaLatent == PA_MLA_LATENT &&
+                  pa::kMlaBlock == PA_MLA_BLOCK_SIZE,
+              "MLA sizes of the header and the kernels agree");
+
+size_t pa_mla_workspace_size(int64_t num_q_tokens, int32_t num_q_heads,
+                             int32_t max_seq_len) {
+  if (num_q_tokens < 0 || num_q_heads <= 0 || num_q_heads % 16 != 0 || max_seq_len < 0)
+    return 0;
+  return pa::mla_layout(num_q_tokens, num_q_heads, max_seq_len).total;
+}
+
+pa_status pa_mla_write_kv(const void* kv, int64_t kv_token_stride,
+                          const int64_t* slot_mapping, int64_t num_tokens, void* cache,
+                          int64_t num_blocks, void* stream) {
+  if (num_tokens < 0 || num_blocks < 0)
+    return fail(PA_ERR_SHAPE, "pa_mla_write_kv: negative size");
+  if (num_tokens == 0) return ok();
+  if (!kv || !slot_mapping || !cache) return fail(PA_ERR_NULL, "pa_mla_write_kv: NULL pointer");
+  if (kv_token_stride < PA_MLA_DIM || kv_token_stride % 8 != 0)
+    return fail(PA_ERR_SHAPE, "kv_token_stride must be >= 576 and a multiple of 8");
+  if (((uintptr_t)kv | (uintptr_t)cache) & 15)
+    return fail(PA_ERR_SHAPE, "kv and the cache must be 16-byte aligned");
+  hipError_t e = pa::launch_mla_write_kv(static_cast<const uint16_t*>(kv), kv_token_stride,
+                                         slot_mapping, num_tokens,
+                                         static_cast<uint16_t*>(cache), num_blocks,
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pa_mla_write_kv launch");
+  return ok();
+}
+
+pa_status pa_mla_decode(const void* q, const void* cache, int64_t num_blocks,
+                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                        const int32_t* seq_lens, const int32_t* query_start_loc,
+                        int32_t num_seqs, int64_t num_q_tokens, int32_t num_q_heads,
+                        int32_t max_seq_len, float scale, void* out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0 || num_q_tokens < 0 || num_blocks < 0 || max_blocks_per_seq < 0 ||
+      max_seq_len < 0)
+    return fail(PA_ERR_SHAPE, "pa_mla_decode: negative size");
+  if (num_q_heads <= 0 || num_q_heads % 16 != 0 || num_q_heads > 128)
+    return fail(PA_ERR_UNSUPPORTED, "num_q_heads must be a multiple of 16, at most 128");
+  if (num_q_tokens > INT32_MAX / 2)
+    return fail(PA_ERR_SHAPE, "pa_mla_decode: num_q_tokens too large");
+  if (max_seq_len > (1 << 18))
+    return fail(PA_ERR_UNSUPPORTED, "pa_mla_decode: max_seq_len above 262144");
+  if (num_q_tokens == 0 || num_seqs == 0) return ok();
+  if (!q || !cache || !block_tables || !seq_lens || !query_start_loc || !out)
+    return fail(PA_ERR_NULL, "pa_mla_decode: NULL pointer");
+  if (max_blocks_per_seq == 0 || num_blocks == 0 || max_seq_len == 0)
+    return fail(PA_ERR_SHAPE, "pa_mla_decode: empty cache, block table or max_seq_len");
+  if (!(scale > 0.0f && scale <= FLT_MAX))
+    return fail(PA_ERR_SHAPE, "pa_mla_decode: scale must be finite and > 0");
+  if (((uintptr_t)q | (uintptr_t)cache | (uintptr_t)out) & 15)
+    return fail(PA_ERR_SHAPE, "q, out and the cache must be 16-byte aligned");
+  const pa::MlaLayout m = pa::mla_layout(num_q_tokens, num_q_heads, max_seq_len);
+  if ((int64_t)num_q_tokens * m.max_splits * (num_q_heads / 16) > INT32_MAX)
+    return fail(PA_ERR_SHAPE, "pa_mla_decode: too many (token, split) units");
+  if (m.max_splits > 1) {
+    if (!workspace || workspace_bytes < m.total)
+      return fail(PA_ERR_WORKSPACE, "pa_mla_decode: workspace needs " +
+                                        std::to_string(m.total) + " bytes, got " +
+                                        std::to_string(workspace_bytes));
+    if ((uintptr_t)workspace & 255)
+      return fail(PA_ERR_WORKSPACE, "pa_mla_decode: workspace must be 256-byte aligned");
+  }
+  pa::MlaParams P;
+  P.q = static_cast<const uint16_t*>(q);
+  P.cache = static_cast<const uint16_t*>(cache);
+  P.num_blocks = num_blocks;
+  P.bt = block_tables;
+  P.bt_stride = max_blocks_per_seq;
+  P.seq_lens = seq_lens;
+  P.qsl = query_start_loc;
+  P.num_seqs = num_seqs;
+  P.num_q_tokens = (int32_t)num_q_tokens;
+  P.Hq = num_q_heads;
+  P.max_seq_len = max_seq_len;
+  P.split = m.split;
+  P.max_splits = m.max_splits;
+  P.scale_log2 = scale * 1.4426950408889634f;
+  P.out = static_cast<uint16_t*>(out);
+  char* ws = static_cast<char*>(workspace);
+  P.part_ml = m.max_splits > 1 ? reinterpret_cast<float2*>(ws + m.part_ml) : nullptr;
+  P.part_acc = m.max_splits > 1 ? reinterpret_cast<float*>(ws + m.part_acc) : nullptr;
+  hipError_t e = pa::launch_mla_decode(P, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pa_mla_decode launch");
+  return ok();
+}
+
 pa_status pa_gather_kv(const void* k_cache, const void* v_cache,
                        int64_t num_blocks, const int32_t* block_tables,
                        int32_t max_blocks_per_seq, const int32_t* seq_lens,

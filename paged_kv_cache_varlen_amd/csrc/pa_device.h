@@ -197,6 +197,62 @@ hipError_t launch_expand_tables(const int32_t* in, int32_t in_stride,
                                 int32_t num_seqs, int R, int32_t* out,
                                 hipStream_t stream);
 
+// ---- multi-head latent attention (mla.hip) --------------------------------
+
+constexpr int kMlaBlock = 64;    // tokens per latent-cache block
+constexpr int kMlaDim = 576;     // cached dims per token (latent + rotary)
+constexpr int kMlaLatent = 512;  // latent dims (the output)
+
+struct MlaParams {
+  const uint16_t* q;      // [T][Hq][576]
+  const uint16_t* cache;  // [num_blocks][64 * 576]
+  int64_t num_blocks;
+  const int32_t* bt;
+  int32_t bt_stride;
+  const int32_t* seq_lens;
+  const int32_t* qsl;
+  int32_t num_seqs;
+  int32_t num_q_tokens;
+  int32_t Hq;
+  int32_t max_seq_len;
+  int32_t split;       // keys per split (a multiple of 64)
+  int32_t max_splits;  // splits of a max_seq_len-key token
+  float scale_log2;
+  uint16_t* out;       // [T][Hq][512]
+  float2* part_ml;     // [T][Hq][max_splits]
+  float* part_acc;     // [T][Hq][max_splits][512]
+};
+
+// Key split of the MLA decode: at least 256 keys, at most 64 splits (and at
+// most 64 blocks, one block id per lane: max_seq_len <= 262144).
+struct MlaLayout {
+  int32_t split;
+  int32_t max_splits;
+  size_t part_ml;
+  size_t part_acc;
+  size_t total;
+};
+inline MlaLayout mla_layout(int64_t num_q_tokens, int32_t num_q_heads,
+                            int32_t max_seq_len) {
+  MlaLayout m{};
+  const int64_t L = max_seq_len > 0 ? max_seq_len : 1;
+  int64_t split = (cdiv64(L, 64) + kMlaBlock - 1) / kMlaBlock * kMlaBlock;
+  if (split < 256) split = 256;
+  m.split = (int32_t)split;
+  m.max_splits = (int32_t)cdiv64(L, split);
+  const size_t rows = (size_t)num_q_tokens * num_q_heads * m.max_splits;
+  m.part_ml = 0;
+  m.part_acc = align256(sizeof(float) * 2 * rows);
+  m.total = align256(m.part_acc + sizeof(float) * kMlaLatent * rows);
+  return m;
+}
+
+hipError_t launch_mla_write_kv(const uint16_t* kv, int64_t stride, const int64_t* slots,
+                               int64_t num_tokens, uint16_t* cache, int64_t num_blocks,
+                               hipStream_t stream);
+// Decode kernel, then (keys split) the merge kernel.
+hipError_t launch_mla_decode(const MlaParams& P, hipStream_t stream);
+
 struct AttendArgs {
   const uint16_t* q;
   const uint16_t* k_cache;
