@@ -30,6 +30,7 @@ Prints one JSON line:
            attention beside shared-prefix (cascade) attention, GB/s of the
            logical and of the unique K/V bytes;
   block_copy  copy-on-write block copies (4096 pairs) on the headline pool;
+  mla_decode  MLA latent decode, 64 requests, 16 and 128 query heads;
   cpu_baseline  the CPU oracle (fp64) on the same headline workload.
 
     python bench.py [--steps K] [--warmup W] [--config 2] [--no-mixed]
@@ -377,6 +378,78 @@ def block_copy_run(W):
             "hbm_peak_frac": round(moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def mla_case(name, L, Hq, seed):
+    """One MLA decode step: requests of lengths L, one query token each, Hq
+    heads, a latent cache of 64-token blocks in a seeded random order."""
+    rng = np.random.default_rng(seed)
+    L = np.asarray(L, np.int32)
+    nblk = (L + 63) // 64
+    nb = int(nblk.sum() * 1.1) + 1
+    perm = rng.permutation(nb)
+    tables = np.full((len(L), int(nblk.max())), -1, np.int32)
+    pos = 0
+    for b, n in enumerate(nblk):
+        tables[b, :n] = perm[pos:pos + n]
+        pos += int(n)
+    return dict(name=name, L=L, Hq=Hq, nb=nb, tables=tables,
+                qsl=np.arange(len(L) + 1, dtype=np.int32))
+
+
+def mla_runs(args):
+    """MLA latent decode (DeepSeek-V3-shaped: 576 cached values per token,
+    512 latent dims out) on 64 requests of U[128, 4096] tokens: 16 query
+    heads (one tensor-parallel share of 128) and all 128 heads.  Attention
+    kernels (decode + merge) timed with HIP events over back-to-back
+    launches on cycled cache copies; GB/s of the latent bytes the step must
+    read and TFLOP/s of the scores and weighted sums."""
+    import torch
+    import paged_kv_cache_varlen_amd as pa
+    from tests.gpu_util import bf16_tensor, i32
+    rng = np.random.default_rng(2024)
+    L = rng.integers(128, 4096, size=64, endpoint=True).astype(np.int32)
+    out = {"latent_dims": 576, "out_dims": 512, "block_size": 64}
+    for key, Hq in (("h16", 16), ("h128", 128)):
+        c = mla_case("deepseek-v3-mla-decode-64seq-%s" % key, L, Hq, seed=7)
+        T = len(L)
+        cache_bytes = c["nb"] * 64 * 576 * 2
+        ncopies = max(1, min(8, int(np.ceil(args.min_working_set_gib * 2**30 / cache_bytes))))
+        caches = [pa.alloc_mla_cache(c["nb"], fill=0.0) for _ in range(ncopies)]
+        for cc in caches:
+            cc.normal_()
+        q = torch.randn((T, Hq, 576), device="cuda").to(torch.bfloat16)
+        o = torch.empty((T, Hq, 512), dtype=torch.bfloat16, device="cuda")
+        ws = pa.mla_workspace(T, Hq, int(L.max()))
+        bt, sl, qsl = i32(c["tables"]), i32(L), i32(c["qsl"])
+        scale = float(1 / np.sqrt(192.0))
+        run = lambda cc: pa.mla_decode(q, cc, bt, sl, qsl, scale, int(L.max()), out=o,
+                                       workspace=ws)
+        for i in range(10):
+            run(caches[i % ncopies])
+        torch.cuda.synchronize()
+        reps = max(4, args.steps // (4 * ncopies))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            for cc in caches:
+                run(cc)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / (reps * ncopies)
+        lat = int(L.sum()) * 576 * 2
+        byts = lat + T * Hq * (576 + 512) * 2 + int(((L + 63) // 64).sum()) * 4
+        flops = int(L.sum()) * Hq * (576 + 512) * 2
+        out[key] = {"workload": c["name"], "num_q_heads": Hq, "ms": round(ms, 5),
+                    "latent_gbs": round(lat / (ms * 1e-3) / 1e9, 1),
+                    "algorithmic_gbs": round(byts / (ms * 1e-3) / 1e9, 1),
+                    "hbm_peak_frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                    "mfma_peak_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "decode_tokens_per_s": round(T / (ms * 1e-3), 1)}
+        del caches
+        torch.cuda.empty_cache()
+    return out
+
+
 def read_ceiling(torch, gib=4):
     """Measured streaming-read ceiling of this box: the best of a few grid
     sizes of the probe kernel (libpa_probe.so) reading a 4 GiB buffer once
@@ -529,6 +602,7 @@ def main():
         line["fp8_kv"] = fp8_runs(args, W)
         line["shared_prefix"] = shared_prefix_runs(args, W)
         line["block_copy"] = block_copy_run(W)
+        line["mla_decode"] = mla_runs(args)
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)

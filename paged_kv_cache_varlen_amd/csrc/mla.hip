@@ -7,12 +7,12 @@
 // 16-token x 32-dim piece is 1 KiB contiguous: a wave loads the score operand
 // of 16 keys for one 32-dim k step with one 16-byte load per lane.
 //
-// Decode (mla_decode_kernel): one workgroup of two waves per (query token,
+// Decode (mla_decode_kernel): one workgroup of four waves per (query token,
 // key split, group of 16 query heads).  For each 16 keys, wave w loads the
-// 9 of the 18 32-dim chunks it owns (latent chunks 8w .. 8w+7 and one rotary
-// chunk), computes its share of S^T = K Q^T against the 16 heads, and takes
-// the other wave's share through LDS; both then run the same online softmax,
-// and wave w accumulates output dims 256w .. 256w+255.  The PV product needs each lane to
+// 32-dim chunks it owns (latent chunks 4w .. 4w+3, and one rotary chunk for
+// w < 2), computes its share of S^T = K Q^T against the 16 heads, and adds
+// the other waves' shares through LDS; all run the same online softmax, and
+// wave w accumulates output dims 128w .. 128w+127.  The PV product needs each lane to
 // hold 4 consecutive keys of one dim, while the cache rows hold consecutive
 // dims of one key: an MFMA against a 0/1 selection matrix moves a 16-key x
 // 16-dim piece of the key operand into that form (exact: every product is
@@ -31,8 +31,10 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kKc = kMlaDim / 32;      // 18 score k steps
 constexpr int kLatC = kMlaLatent / 32;  // 16 latent chunks of 32 dims
-constexpr int kMlaThreads = 128;        // two waves
-constexpr int kChunks = kLatC / 2 + 1;  // score k steps per wave
+constexpr int kMlaWaves = 4;
+constexpr int kMlaThreads = 64 * kMlaWaves;
+constexpr int kOwn = kLatC / kMlaWaves;  // latent chunks per wave
+constexpr int kMlaStages = 4;            // 16-key tiles in flight + 1
 
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -52,12 +54,28 @@ __device__ __forceinline__ float column_max(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// Request of query token t: the last b with qsl[b] <= t (qsl non-decreasing).
+// Workgroup barrier after this wave's LDS writes have completed.  Unlike
+// __syncthreads() (a release/acquire fence, which also waits for every global
+// load in flight) it leaves the tile prefetches in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Request of query token t: the last b with qsl[b] <= t (qsl non-decreasing,
+// qsl[0] = 0).  The wave's 64 lanes test 64 evenly spaced candidates per
+// round (one load each, in parallel): one round up to 64 requests, two up to
+// 4096.
 __device__ __forceinline__ int request_of(const int32_t* qsl, int num_seqs, int t) {
-  int lo = 0, hi = num_seqs;  // answer in [lo, hi)
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (qsl[mid] <= t) lo = mid; else hi = mid;
+  const int lane = threadIdx.x & 63;
+  int lo = 0, n = num_seqs;  // answer in [lo, lo + n)
+  while (n > 1) {
+    const int stride = (n + 63) / 64;
+    const int bi = lo + lane * stride;
+    const bool le = lane * stride < n && qsl[bi] <= t;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(le);
+    const int k = m ? 63 - __builtin_clzll(m) : 0;
+    lo += k * stride;
+    n = min(stride, n - k * stride);
   }
   return lo;
 }
@@ -92,30 +110,39 @@ __global__ __launch_bounds__(256) void mla_write_kv_kernel(
 }
 
 __global__ __launch_bounds__(kMlaThreads, 2) void mla_decode_kernel(MlaParams P) {
-  // partial scores of the two waves, two tiles deep
-  __shared__ f32x4 sx[2][2][64];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // partial scores of the waves, two tiles deep
+  __shared__ f32x4 sx[2][kMlaWaves][64];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
+  // Workgroup -> (unit u = (token, split), head group): workgroups are
+  // dealt to the 8 XCDs round-robin, so the head groups of one unit get
+  // indices with the same residue mod 8 (one XCD, one L2) and follow each
+  // other there.
   const int nhg = P.Hq / 16;
-  const int unit = blockIdx.x;
-  const int hg = unit % nhg;
-  const int s = (unit / nhg) % P.max_splits;
-  const int t = unit / nhg / P.max_splits;
+  const int rest = blockIdx.x >> 3;
+  const int hg = rest % nhg;
+  const int u = (rest / nhg) * 8 + (blockIdx.x & 7);
+  if (u >= P.num_q_tokens * P.max_splits) return;
+  const int s = u % P.max_splits;
+  const int t = u / P.max_splits;
   int b;
   const int nvis = visible_keys(P, t, &b);
   const int nsplit = (nvis + P.split - 1) / P.split;
   if (s >= nsplit) return;
   const int k0 = s * P.split, k1 = min(nvis, k0 + P.split);
 
-  // Wave w owns latent chunks 8w .. 8w+7 (its output dims) and rotary chunk
-  // 16 + w: kChunks of the 18 score k steps.  Its query operands: lane (r, g)
-  // of chunk c holds dims 32c + 8g .. +7 of head r.
-  auto chunk = [&](int i) { return i < kLatC / 2 ? (kLatC / 2) * w + i : kLatC + w; };
+  // Wave w owns latent chunks kOwn * w .. kOwn * w + kOwn - 1 (its output
+  // dims) and, for w < 2, rotary chunk 16 + w: its share of the 18 score k
+  // steps.  Its query operands: lane (r, g) of chunk c holds dims
+  // 32c + 8g .. +7 of head r.
+  const bool rot = w < kMlaDim / 32 - kLatC;
+  auto chunk = [&](int i) { return i < kOwn ? kOwn * w + i : kLatC + w; };
   const uint16_t* qp = P.q + ((int64_t)t * P.Hq + hg * 16 + r) * kMlaDim + 8 * g;
-  bf16x8 qop[kChunks];
+  bf16x8 qop[kOwn + 1];
 #pragma unroll
-  for (int i = 0; i < kChunks; ++i)
-    qop[i] = *reinterpret_cast<const bf16x8*>(qp + 32 * chunk(i));
+  for (int i = 0; i < kOwn + 1; ++i)
+    if (i < kOwn || rot) qop[i] = *reinterpret_cast<const bf16x8*>(qp + 32 * chunk(i));
   // 0/1 selection operands: E_j[k][n] = 1 where k = 16j + n (lane (r, g)
   // holds rows 8g .. 8g+7 of column r)
   bf16x8 sel[2];
@@ -131,35 +158,43 @@ __global__ __launch_bounds__(kMlaThreads, 2) void mla_decode_kernel(MlaParams P)
   if (lane < nblk) idv = P.bt[(int64_t)b * P.bt_stride + jb0 + lane];
   idv = idv < 0 ? 0 : (idv >= P.num_blocks ? (int)(P.num_blocks - 1) : idv);
 
-  f32x4 acc[kLatC];  // this wave's 8 latent chunks x 2 dim tiles of 16
+  f32x4 acc[2 * kOwn];  // this wave's latent chunks x 2 dim tiles of 16
 #pragma unroll
-  for (int k = 0; k < kLatC; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < 2 * kOwn; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
   float mrun = -INFINITY, lsum = 0.0f;
   const float c2 = P.scale_log2;
 
   const int ntiles = (k1 - k0 + 15) / 16;  // 16-key tiles of the split
-  auto load_tile = [&](bf16x8 (&kop)[kChunks], int tile) {
+  typedef bf16x8 Tile[kOwn + 1];
+  auto load_tile = [&](Tile& kop, int tile) {
     const int key = k0 + 16 * tile;
     const int id = __builtin_amdgcn_readlane(idv, (key / kMlaBlock) - jb0);
     // the piece of (16-key tile, chunk) is [16 tokens][32 dims]: lane (r, g)
     // reads token r, dims 8g .. 8g+7
     const uint16_t* base = P.cache + (int64_t)id * kMlaBlock * kMlaDim +
                            ((key % kMlaBlock) >> 4) * kKc * 512 + r * 32 + g * 8;
+    // one head group: every tile is read once (non-temporal); several: the
+    // other groups' workgroups on this XCD read it again from L2
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i)
-      kop[i] = __builtin_nontemporal_load(
-          reinterpret_cast<const bf16x8*>(base + chunk(i) * 512));
+    for (int i = 0; i < kOwn + 1; ++i)
+      if (i < kOwn || rot) {
+        const bf16x8* src = reinterpret_cast<const bf16x8*>(base + chunk(i) * 512);
+        kop[i] = nhg == 1 ? __builtin_nontemporal_load(src) : *src;
+      }
   };
-  auto compute = [&](const bf16x8 (&kop)[kChunks], int tile) {
+  auto compute = [&](const Tile& kop, int tile) {
     const int key0 = k0 + 16 * tile;
-    // this wave's share of the scores, then the other wave's through LDS
-    // (a + b == b + a in IEEE arithmetic: both waves hold the same sum)
+    // this wave's share of the scores; every wave then adds the shares of
+    // all waves in the same order, so all hold the same sums
     f32x4 part = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i) part = mfma32(kop[i], qop[i], part);
+    for (int i = 0; i < kOwn; ++i) part = mfma32(kop[i], qop[i], part);
+    if (rot) part = mfma32(kop[kOwn], qop[kOwn], part);
     sx[tile & 1][w][lane] = part;
-    __syncthreads();
-    const f32x4 sc = part + sx[tile & 1][w ^ 1][lane];
+    lds_barrier();
+    f32x4 sc = sx[tile & 1][0][lane];
+#pragma unroll
+    for (int v = 1; v < kMlaWaves; ++v) sc += sx[tile & 1][v][lane];
     float x[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = (key0 + 4 * g + i < k1) ? sc[i] : -INFINITY;
@@ -179,12 +214,12 @@ __global__ __launch_bounds__(kMlaThreads, 2) void mla_decode_kernel(MlaParams P)
     lsum = lsum * alpha + psum;
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
-      for (int k = 0; k < kLatC; ++k) acc[k] *= alpha;
+      for (int k = 0; k < 2 * kOwn; ++k) acc[k] *= alpha;
     }
     // keys past the split end may be unwritten slots: their V rows are zeroed
     // (a 0 weight must not meet a NaN)
 #pragma unroll
-    for (int cc = 0; cc < kLatC / 2; ++cc) {
+    for (int cc = 0; cc < kOwn; ++cc) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const f32x4 tv = mfma32(kop[cc], sel[j], f32x4{0.f, 0.f, 0.f, 0.f});
@@ -196,27 +231,31 @@ __global__ __launch_bounds__(kMlaThreads, 2) void mla_decode_kernel(MlaParams P)
       }
     }
   };
-  // two tiles in flight: the loads of tile i+1 are issued before tile i is
-  // computed (the last prefetch repeats the last tile); both waves run the
-  // same number of steps (one barrier each)
-  bf16x8 ka[kChunks], kb[kChunks];
-  load_tile(ka, 0);
-  for (int i = 0; i < ntiles; i += 2) {
-    load_tile(kb, min(i + 1, ntiles - 1));
-    compute(ka, i);
-    load_tile(ka, min(i + 2, ntiles - 1));
-    if (i + 1 < ntiles) compute(kb, i + 1);
+  // Ring of kMlaStages tiles: the loads of tile i + kMlaStages - 1 are issued
+  // before tile i is computed (prefetches past the end repeat the last tile);
+  // every wave runs the same steps (one barrier each).
+  Tile ring[kMlaStages];
+#pragma unroll
+  for (int k = 0; k < kMlaStages - 1; ++k) load_tile(ring[k], min(k, ntiles - 1));
+  for (int i = 0; i < ntiles; i += kMlaStages) {
+#pragma unroll
+    for (int k = 0; k < kMlaStages; ++k) {
+      load_tile(ring[(k + kMlaStages - 1) % kMlaStages],
+                min(i + k + kMlaStages - 1, ntiles - 1));
+      if (i + k < ntiles) compute(ring[k], i + k);
+    }
   }
 
   float l = lsum;
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
   const int h = hg * 16 + r;
+  const int dim0 = 32 * kOwn * w + 4 * g;
   if (nsplit == 1) {
     const float inv = 1.0f / l;
-    uint16_t* op = P.out + ((int64_t)t * P.Hq + h) * kMlaLatent + 256 * w + 4 * g;
+    uint16_t* op = P.out + ((int64_t)t * P.Hq + h) * kMlaLatent + dim0;
 #pragma unroll
-    for (int k = 0; k < kLatC; ++k) {
+    for (int k = 0; k < 2 * kOwn; ++k) {
       bf16x4 o;
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[i] = (__bf16)(acc[k][i] * inv);
@@ -225,9 +264,9 @@ __global__ __launch_bounds__(kMlaThreads, 2) void mla_decode_kernel(MlaParams P)
     return;
   }
   const int64_t row = ((int64_t)t * P.Hq + h) * P.max_splits + s;
-  float* ap = P.part_acc + row * kMlaLatent + 256 * w + 4 * g;
+  float* ap = P.part_acc + row * kMlaLatent + dim0;
 #pragma unroll
-  for (int k = 0; k < kLatC; ++k) *reinterpret_cast<f32x4*>(ap + 16 * k) = acc[k];
+  for (int k = 0; k < 2 * kOwn; ++k) *reinterpret_cast<f32x4*>(ap + 16 * k) = acc[k];
   if (w == 0 && g == 0) P.part_ml[row] = make_float2(mrun, l);
 }
 
@@ -282,8 +321,9 @@ hipError_t launch_mla_write_kv(const uint16_t* kv, int64_t stride, const int64_t
 
 hipError_t launch_mla_decode(const MlaParams& P, hipStream_t stream) {
   if (P.num_q_tokens == 0 || P.num_seqs == 0) return hipSuccess;
-  const int64_t units = (int64_t)P.num_q_tokens * P.max_splits * (P.Hq / 16);
-  hipLaunchKernelGGL(mla_decode_kernel, dim3((unsigned)units), dim3(kMlaThreads), 0,
+  const int64_t units = (int64_t)P.num_q_tokens * P.max_splits;
+  const int64_t wgs = (units + 7) / 8 * 8 * (P.Hq / 16);
+  hipLaunchKernelGGL(mla_decode_kernel, dim3((unsigned)wgs), dim3(kMlaThreads), 0,
                      stream, P);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || P.max_splits < 2) return e;

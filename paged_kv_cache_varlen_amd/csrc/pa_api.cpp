@@ -713,7 +713,7 @@ pa_status pa_mla_decode(const void* q, const void* cache, int64_t num_blocks,
   if (((uintptr_t)q | (uintptr_t)cache | (uintptr_t)out) & 15)
     return fail(PA_ERR_SHAPE, "q, out and the cache must be 16-byte aligned");
   const pa::MlaLayout m = pa::mla_layout(num_q_tokens, num_q_heads, max_seq_len);
-  if ((int64_t)num_q_tokens * m.max_splits * (num_q_heads / 16) > INT32_MAX)
+  if (((int64_t)num_q_tokens * m.max_splits + 7) / 8 * 8 * (num_q_heads / 16) > INT32_MAX)
     return fail(PA_ERR_SHAPE, "pa_mla_decode: too many (token, split) units");
   if (m.max_splits > 1) {
     if (!workspace || workspace_bytes < m.total)

@@ -223,8 +223,10 @@ struct MlaParams {
   float* part_acc;     // [T][Hq][max_splits][512]
 };
 
-// Key split of the MLA decode: at least 256 keys, at most 64 splits (and at
-// most 64 blocks, one block id per lane: max_seq_len <= 262144).
+// Key split of the MLA decode: at most 64 splits (and at most 64 blocks, one
+// block id per lane: max_seq_len <= 262144); at least 512 keys for 16 heads
+// (longer streams per workgroup), 256 for more heads (more workgroups share
+// each tile through L2).
 struct MlaLayout {
   int32_t split;
   int32_t max_splits;
@@ -237,7 +239,8 @@ inline MlaLayout mla_layout(int64_t num_q_tokens, int32_t num_q_heads,
   MlaLayout m{};
   const int64_t L = max_seq_len > 0 ? max_seq_len : 1;
   int64_t split = (cdiv64(L, 64) + kMlaBlock - 1) / kMlaBlock * kMlaBlock;
-  if (split < 256) split = 256;
+  const int64_t min_split = num_q_heads > 16 ? 256 : 512;
+  if (split < min_split) split = min_split;
   m.split = (int32_t)split;
   m.max_splits = (int32_t)cdiv64(L, split);
   const size_t rows = (size_t)num_q_tokens * num_q_heads * m.max_splits;
