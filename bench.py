@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the streaming-read ceiling probe")
+    ap.add_argument("--mla", action="store_true",
+                    help="only the MLA latent decode sub-run (one JSON line)")
     ap.add_argument("--fp8", action="store_true",
                     help="time the workload over 8-bit (E4M3) pools")
     ap.add_argument("--cascade", action="store_true",
@@ -499,6 +501,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_probe:
         return copy_probe()
+    if args.mla:
+        print(json.dumps({"mla_decode": mla_runs(args)}))
+        return 0
 
     w = W.make_prefill_chunk() if args.config == "p" else W.make_config(int(args.config))
     alg = algorithmic(w)
