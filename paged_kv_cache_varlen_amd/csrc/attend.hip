@@ -41,20 +41,13 @@
 #include <utility>
 #include <vector>
 
+#include "mfma_util.h"
 #include "pa_device.h"
 
 namespace pa {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr float kLog2e = 1.4426950408889634f;
 // block buffers of the decode pipeline (blocks in flight + 1)
 constexpr int kDecodeStages = 3;
 // In a mixed batch, the first kPrefillWgNum / kPrefillWgDen of the
@@ -496,14 +489,6 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
                                  5, 6, 7);
 }
 
-__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-      __builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
-}
 
 // Query operand and column positions of a unit.  Column c of tile ct is
 // token c / G, head c % G of the kv head's group; lane (r, g) holds dims
@@ -536,16 +521,6 @@ __device__ __forceinline__ void load_query(const AttendParams& P,
   }
 }
 
-// Maximum over the four lanes r, r + 16, r + 32, r + 48, which hold the
-// rows of MFMA column r: two VALU lane swaps (no LDS round trip).
-__device__ __forceinline__ float column_max(float x) {
-  const uint32_t xb = __float_as_uint(x);
-  const auto a = __builtin_amdgcn_permlane32_swap(xb, xb, false, false);
-  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const uint32_t yb = __float_as_uint(y);
-  const auto b = __builtin_amdgcn_permlane16_swap(yb, yb, false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
 
 // Online-softmax update of one column tile with N new raw scores per lane
 // (q.k; -inf where masked) and c = scale * log2(e).  The running max is kept

@@ -18,16 +18,13 @@
 // 16-dim piece of the key operand into that form (exact: every product is
 // x * 1 or x * 0 and the sums have one nonzero term), so the latent is stored
 // and read once.
+#include "mfma_util.h"
 #include "pa_device.h"
 
 namespace pa {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kKc = kMlaDim / 32;      // 18 score k steps
 constexpr int kLatC = kMlaLatent / 32;  // 16 latent chunks of 32 dims
@@ -36,23 +33,6 @@ constexpr int kMlaThreads = 64 * kMlaWaves;
 constexpr int kOwn = kLatC / kMlaWaves;  // latent chunks per wave
 constexpr int kMlaStages = 4;            // 16-key tiles in flight + 1
 
-__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-      __builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
-}
-
-// Maximum over the four lanes r, r+16, r+32, r+48 (the rows of MFMA column r).
-__device__ __forceinline__ float column_max(float x) {
-  const uint32_t xb = __float_as_uint(x);
-  const auto a = __builtin_amdgcn_permlane32_swap(xb, xb, false, false);
-  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const uint32_t yb = __float_as_uint(y);
-  const auto b = __builtin_amdgcn_permlane16_swap(yb, yb, false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
 
 // Workgroup barrier after this wave's LDS writes have completed.  Unlike
 // __syncthreads() (a release/acquire fence, which also waits for every global
