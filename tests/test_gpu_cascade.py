@@ -15,7 +15,7 @@ import torch
 import oracle
 import paged_kv_cache_varlen_amd as pa
 import workloads as W
-from tests.gpu_util import Uploaded, bf16_tensor, i32, tensor_bits
+from tests.gpu_util import Uploaded, bf16_tensor, i32, i64, tensor_bits
 from tests.test_gpu_fp8 import gpu_pool8, oracle_pool8
 from tests.test_gpu_parity import check_close, oracle_pool, sample_rows, to64
 
@@ -253,3 +253,57 @@ def test_config4_cascade_fp8():
     ref = oracle.attend_fp8(w.q, okc, ovc, ks, vs, w.block_tables, w.seq_lens,
                             w.query_start_loc, w.num_kv_heads, w.scale, rows=rows)
     check_close(got[rows[:, 0], rows[:, 1]], ref, "config 4 cascade fp8")
+
+
+def test_cascade_fp8_planned_equals_unplanned():
+    w, C = casc("casc-mixed-g4-d128", seed=10)
+    u = Uploaded(w)
+    kc, vc = gpu_pool8(w, 0.02, 0.03)
+    a = run_cascade(u, C, k_cache=kc, v_cache=vc, scales=(0.02, 0.03))
+    b = run_cascade(u, C, k_cache=kc, v_cache=vc, scales=(0.02, 0.03), planned=True,
+                    ws=cascade_ws(w))
+    assert np.array_equal(a, b)
+
+
+def test_cascade_with_larger_blocks():
+    # 32-token blocks: an 8-block (256-token) prefix held by every request,
+    # private suffix blocks; the pool read through expanded 16-token tables
+    rng = np.random.default_rng(12)
+    bs, C, Hq, Hkv, D = 32, 256, 16, 4, 128
+    L = np.array([C + 1, C + 40, C + 300, C + 77], np.int32)
+    Q = np.array([1, 20, 1, 5], np.int32)
+    nb32 = C // bs + sum(-(-(int(x) - C) // bs) for x in L) + 3
+    perm = [int(x) for x in rng.permutation(nb32)]
+    prefix_ids, pos = perm[:C // bs], C // bs
+    tables = np.full((len(L), -(-int(L.max()) // bs)), -1, np.int32)
+    for b, x in enumerate(L):
+        n = -(-(int(x) - C) // bs)
+        tables[b, :C // bs] = prefix_ids
+        tables[b, C // bs:C // bs + n] = perm[pos:pos + n]
+        pos += n
+    kv_start = np.concatenate([[0], np.cumsum(L)])
+    kd = W.normal_bf16((12, 0), (int(L.sum()), Hkv, D))
+    vd = W.normal_bf16((12, 1), (int(L.sum()), Hkv, D))
+    for b in range(1, len(L)):  # every request's first C tokens are request 0's
+        kd[kv_start[b]:kv_start[b] + C] = kd[:C]
+        vd[kv_start[b]:kv_start[b] + C] = vd[:C]
+    rows, slots = [], []
+    for b in range(len(L)):
+        first = 0 if b == 0 else C  # the shared blocks are written once
+        pos_b = np.arange(first, int(L[b]))
+        rows.append(kv_start[b] + pos_b)
+        slots.append(W.slots_for(tables[b], pos_b, bs))
+    rows, slots = np.concatenate(rows), np.concatenate(slots)
+    kc, vc = pa.alloc_pool(nb32 * (bs // 16), Hkv, D, fill=float("nan"))
+    pa.write_kv(bf16_tensor(kd[rows]), bf16_tensor(vd[rows]), i64(slots), kc, vc)
+    t16 = pa.expand_block_tables(i32(tables), bs)
+    qsl = W.query_start_loc(Q)
+    q = W.normal_bf16((12, 2), (int(Q.sum()), Hq, D))
+    scale = float(np.float32(1 / np.sqrt(D)))
+    ws = pa.alloc_workspace(len(L), int(Q.sum()), Hq, Hkv, D, int(Q.max()), int(L.max()),
+                            cascade=True)
+    out = pa.attend(bf16_tensor(q), kc, vc, t16, i32(L), i32(qsl), scale, int(Q.max()),
+                    int(L.max()), num_kv_heads=Hkv, workspace=ws, common_prefix_len=C)
+    torch.cuda.synchronize()
+    ref = oracle.attend_dense(q, kd, vd, L, qsl, scale)
+    check_close(tensor_bits(out), ref, "shared prefix over 32-token blocks")
