@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark of one paged-attention layer step on one MI355X.
 
-A step is the whole hot path for one layer over one batch: pa_write_kv of
-the step's new K/V rows, then the three kernels of pa_attend (work plan,
-unified varlen paged attention, split-K merge) over every query row.  Inputs are seeded synthetic
+A step is the whole hot path for one layer over one batch: the scatter of
+the step's new K/V rows and the work plan in one launch (pa_write_kv_plan),
+then unified varlen paged attention and the split-K merge over every query
+row.  Inputs are seeded synthetic
 tensors already resident in HBM.  Several copies of the KV pool (one per
 simulated layer, >= 2 GiB in total) are cycled so that no step reads K/V left
 in the caches by the previous one.
@@ -191,14 +192,15 @@ class Runner:
                              w.max_seq_len, u.workspace, cascade=self.cascade is not None)
 
     def step(self, i):
-        """write_kv + plan + attention + merge for one layer."""
-        pa, u = self.pa, self.u
+        """write_kv + plan (one fused launch) + attention + merge for one
+        layer."""
+        w, u = self.w, self.u
         kc, vc = self.layers[i % len(self.layers)]
-        if self.fp8 is None:
-            pa.write_kv(u.k_new, u.v_new, u.new_slots, kc, vc)
-        else:
-            pa.write_kv_fp8(u.k_new, u.v_new, u.new_slots, kc, vc, *self.fp8)
-        self.plan()
+        ks, vs = (None, None) if self.fp8 is None else self.fp8
+        self.pa.write_kv_plan(u.k_new, u.v_new, u.new_slots, kc, vc, u.block_tables,
+                              u.seq_lens, u.qsl, w.num_q_tokens, w.num_q_heads,
+                              w.max_query_len, w.max_seq_len, u.workspace,
+                              common_prefix_len=self.cascade, k_scale=ks, v_scale=vs)
         self.attend(kc, vc)
         self.merge()
 
@@ -517,7 +519,6 @@ def main():
     kernel = ("attend_decode_kernel<%d, %s>" if casc is None and w.max_query_len <= 16 // (
         w.num_q_heads // w.num_kv_heads) else "attend_mixed_kernel<%d, %s>") % (
         w.head_dim, "true" if args.fp8 else "false")
-    kv_gbs = alg["kv_bytes"] / (ms_step * 1e-3) / 1e9
     if casc:
         # shared-prefix attention reads the prefix once: its algorithmic
         # bytes are the distinct tokens' K/V (plus the same q, out, metadata)
@@ -526,6 +527,8 @@ def main():
         # 8-bit pools: one byte per K or V element
         alg["attend_bytes"] -= alg["kv_bytes"] // 2
         alg["kv_bytes"] //= 2
+    # the line's value: the K/V bytes the step reads (8-bit codes with --fp8)
+    kv_gbs = alg["kv_bytes"] / (ms_step * 1e-3) / 1e9
     achieved = alg["attend_bytes"] / (attend_ms * 1e-3) / 1e9
     line = {
         "metric": "paged-attn KV read GB/s (% HBM peak) + mixed-step tokens/s per layer",

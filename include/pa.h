@@ -425,6 +425,57 @@ pa_status pa_attend_merge_cascade(int32_t num_seqs, int64_t num_q_tokens,
                                   size_t workspace_bytes, void *stream);
 
 /*
+ * pa_write_kv_plan, pa_write_kv_plan_fp8 - pa_write_kv (pa_write_kv_fp8) and
+ * pa_attend_plan (pa_attend_plan_cascade) of the same step in one launch.
+ *
+ * A step scatters its new K/V and plans its attention before the first
+ * layer's attention runs ("vLLM v1 Deep Dive", Step 4c: the runner prepares
+ * the step's metadata once; "vLLM: An Exhaustive Technical Study" section
+ * 2.1: the new tokens are cached before attention reads them).  The two do
+ * not depend on each other: one workgroup of the launch writes the plan
+ * while the others scatter, saving one kernel launch per step.
+ *
+ * Arguments: the scatter's (k, v, strides, slot_mapping, num_new_tokens,
+ * the scales for the 8-bit variant, k_cache, v_cache, num_blocks) exactly
+ * as pa_write_kv / pa_write_kv_fp8 take them, num_new_tokens in the place of
+ * num_tokens; then the plan's, exactly as pa_attend_plan takes them.
+ * num_kv_heads and head_dim serve both.  common_prefix_len < 0: a plain plan
+ * (workspace >= pa_attend_workspace_size(...)), run by pa_attend_planned(_fp8);
+ * common_prefix_len >= 0: a shared-prefix plan as pa_attend_plan_cascade
+ * makes it (workspace >= pa_attend_cascade_workspace_size(...)), run by
+ * pa_attend_planned_cascade(_fp8).
+ *
+ * Results, skips and races: those of the two calls it replaces; the call
+ * checks both argument sets first and enqueues nothing if either is
+ * invalid (the errors of pa_write_kv(_fp8) and pa_attend_plan(_cascade)).
+ * With num_new_tokens == 0 it is the plan alone; with nothing to plan
+ * (num_seqs == 0 or num_q_tokens == 0) it is the scatter alone.
+ */
+pa_status pa_write_kv_plan(const void *k, const void *v, int64_t k_token_stride,
+                           int64_t v_token_stride, const int64_t *slot_mapping,
+                           int64_t num_new_tokens, void *k_cache, void *v_cache,
+                           int64_t num_blocks, const int32_t *block_tables,
+                           int32_t max_blocks_per_seq, const int32_t *seq_lens,
+                           const int32_t *query_start_loc, int32_t num_seqs,
+                           int64_t num_q_tokens, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim,
+                           int32_t max_query_len, int32_t max_seq_len,
+                           int32_t common_prefix_len, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+pa_status pa_write_kv_plan_fp8(const void *k, const void *v, int64_t k_token_stride,
+                               int64_t v_token_stride, const int64_t *slot_mapping,
+                               int64_t num_new_tokens, float k_scale, float v_scale,
+                               void *k_cache, void *v_cache, int64_t num_blocks,
+                               const int32_t *block_tables, int32_t max_blocks_per_seq,
+                               const int32_t *seq_lens, const int32_t *query_start_loc,
+                               int32_t num_seqs, int64_t num_q_tokens,
+                               int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t max_query_len,
+                               int32_t max_seq_len, int32_t common_prefix_len,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * pa_validate_cascade_host - host check of the shared-prefix requirements
  * above on HOST arrays: PA_ERR_METADATA (detail in pa_last_error()) when a
  * request has seq_lens[b] - Q_b < common_prefix_len, or when one of the

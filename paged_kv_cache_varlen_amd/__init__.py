@@ -67,17 +67,16 @@ def _pool_blocks(cache: torch.Tensor, num_kv_heads: int, head_dim: int) -> int:
     return cache.numel() // per_block
 
 
-def write_kv(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
-             k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
-    """Scatter k, v ([T][Hkv][D] bf16, rows may be strided) into their slots."""
+def _scatter_args(k, v, slot_mapping, k_cache, v_cache, pool_dtype):
+    """Checks of a scatter's tensors; returns (T, Hkv, D, num_blocks)."""
     for t, n in ((k, "k"), (v, "v"), (slot_mapping, "slot_mapping"),
                  (k_cache, "k_cache"), (v_cache, "v_cache")):
         _need_cuda(t, n)
     _dtype(k, torch.bfloat16, "k")
     _dtype(v, torch.bfloat16, "v")
     _dtype(slot_mapping, torch.int64, "slot_mapping")
-    _dtype(k_cache, torch.bfloat16, "k_cache")
-    _dtype(v_cache, torch.bfloat16, "v_cache")
+    _dtype(k_cache, pool_dtype, "k_cache")
+    _dtype(v_cache, pool_dtype, "v_cache")
     if k.dim() != 3 or v.shape != k.shape:
         raise ValueError("k and v must be [num_tokens][num_kv_heads][head_dim]")
     T, Hkv, D = k.shape
@@ -89,6 +88,13 @@ def write_kv(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
     nb = _pool_blocks(k_cache, Hkv, D)
     if _pool_blocks(v_cache, Hkv, D) != nb:
         raise ValueError("k_cache and v_cache differ in size")
+    return T, Hkv, D, nb
+
+
+def write_kv(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+             k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
+    """Scatter k, v ([T][Hkv][D] bf16, rows may be strided) into their slots."""
+    T, Hkv, D, nb = _scatter_args(k, v, slot_mapping, k_cache, v_cache, torch.bfloat16)
     lib = _lib.load()
     st = lib.pa_write_kv(_ptr(k), _ptr(v), k.stride(0), v.stride(0),
                          _ptr(slot_mapping), T, Hkv, D, _ptr(k_cache),
@@ -117,25 +123,7 @@ def write_kv_fp8(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
                  v_scale: float) -> None:
     """Scatter k, v ([T][Hkv][D] bf16, rows may be strided) into 8-bit pools:
     the E4M3 code of fp32(x) / scale per element."""
-    for t, n in ((k, "k"), (v, "v"), (slot_mapping, "slot_mapping"),
-                 (k_cache, "k_cache"), (v_cache, "v_cache")):
-        _need_cuda(t, n)
-    _dtype(k, torch.bfloat16, "k")
-    _dtype(v, torch.bfloat16, "v")
-    _dtype(slot_mapping, torch.int64, "slot_mapping")
-    _dtype(k_cache, torch.uint8, "k_cache")
-    _dtype(v_cache, torch.uint8, "v_cache")
-    if k.dim() != 3 or v.shape != k.shape:
-        raise ValueError("k and v must be [num_tokens][num_kv_heads][head_dim]")
-    T, Hkv, D = k.shape
-    for t, n in ((k, "k"), (v, "v")):
-        if t.stride(2) != 1 or t.stride(1) != D:
-            raise ValueError("%s rows must be contiguous [num_kv_heads][head_dim]" % n)
-    if not slot_mapping.is_contiguous() or slot_mapping.shape != (T,):
-        raise ValueError("slot_mapping must be contiguous [num_tokens]")
-    nb = _pool_blocks(k_cache, Hkv, D)
-    if _pool_blocks(v_cache, Hkv, D) != nb:
-        raise ValueError("k_cache and v_cache differ in size")
+    T, Hkv, D, nb = _scatter_args(k, v, slot_mapping, k_cache, v_cache, torch.uint8)
     lib = _lib.load()
     st = lib.pa_write_kv_fp8(_ptr(k), _ptr(v), k.stride(0), v.stride(0),
                              _ptr(slot_mapping), T, Hkv, D, float(k_scale),
@@ -301,6 +289,37 @@ def attend_plan(block_tables: torch.Tensor, seq_lens: torch.Tensor,
     st = getattr(lib, name)(*args, _ptr(workspace), workspace.numel(),
                             _stream(workspace))
     _lib.check(st, name)
+
+
+def write_kv_plan(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                  k_cache: torch.Tensor, v_cache: torch.Tensor,
+                  block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                  query_start_loc: torch.Tensor, num_q_tokens: int, num_q_heads: int,
+                  max_query_len: int, max_seq_len: int, workspace: torch.Tensor,
+                  common_prefix_len: Optional[int] = None,
+                  k_scale: Optional[float] = None,
+                  v_scale: Optional[float] = None) -> None:
+    """write_kv (write_kv_fp8 for uint8 pools, with the scales) and
+    attend_plan of the same step in one launch."""
+    fp8 = k_cache.dtype == torch.uint8
+    T, Hkv, D, nb = _scatter_args(k, v, slot_mapping, k_cache, v_cache,
+                                  torch.uint8 if fp8 else torch.bfloat16)
+    for t, n in ((block_tables, "block_tables"), (seq_lens, "seq_lens"),
+                 (query_start_loc, "query_start_loc"), (workspace, "workspace")):
+        _need_cuda(t, n)
+    if fp8 and (k_scale is None or v_scale is None):
+        raise ValueError("8-bit pools need k_scale and v_scale")
+    lib = _lib.load()
+    scatter = [_ptr(k), _ptr(v), k.stride(0), v.stride(0), _ptr(slot_mapping), T]
+    if fp8:
+        scatter += [float(k_scale), float(v_scale)]
+    plan = [_ptr(k_cache), _ptr(v_cache), nb, _ptr(block_tables), block_tables.shape[1],
+            _ptr(seq_lens), _ptr(query_start_loc), block_tables.shape[0],
+            int(num_q_tokens), int(num_q_heads), Hkv, D, int(max_query_len),
+            int(max_seq_len), -1 if common_prefix_len is None else int(common_prefix_len),
+            _ptr(workspace), workspace.numel(), _stream(k)]
+    name = "pa_write_kv_plan_fp8" if fp8 else "pa_write_kv_plan"
+    _lib.check(getattr(lib, name)(*scatter, *plan), name)
 
 
 def validate_cascade(block_tables, seq_lens, query_start_loc,

@@ -47,6 +47,11 @@ SIGNATURES = {
     "pa_attend_planned_cascade_fp8": (STATUS, [P, P, P, I64, P, I32, P, P, I32, I64,
                                                I32, I32, I32, I32, I32, F32, F32,
                                                F32, P, P, SZ, P]),
+    "pa_write_kv_plan": (STATUS, [P, P, I64, I64, P, I64, P, P, I64, P, I32, P, P,
+                                  I32, I64, I32, I32, I32, I32, I32, I32, P, SZ, P]),
+    "pa_write_kv_plan_fp8": (STATUS, [P, P, I64, I64, P, I64, F32, F32, P, P, I64, P,
+                                      I32, P, P, I32, I64, I32, I32, I32, I32, I32,
+                                      I32, P, SZ, P]),
     "pa_attend_merge_cascade": (STATUS, [I32, I64, I32, I32, I32, I32, I32, P, P, SZ,
                                          P]),
     "pa_attend_cascade": (STATUS, [P, P, P, I64, P, I32, P, P, I32, I64, I32, I32,

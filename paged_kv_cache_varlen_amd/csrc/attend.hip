@@ -41,6 +41,7 @@
 #include <utility>
 #include <vector>
 
+#include "kv_scatter.h"
 #include "mfma_util.h"
 #include "pa_device.h"
 
@@ -312,7 +313,8 @@ __device__ __forceinline__ void place_seq(const AttendParams& P, int b,
   emit_seq(P, b, c, ibase, ilast, pbase, cbase);
 }
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttendParams P) {
+// The work plan, run by one workgroup of kPlanThreads threads.
+__device__ void plan_body(const AttendParams& P) {
   __shared__ int4 lds[kPlanThreads / 64 + 1];
   __shared__ int coop_n;
   __shared__ int coop_b[kMaxCoop];
@@ -439,6 +441,34 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttendParams P) {
     P.hdr->num_split_tiles = fits ? (uint32_t)total.w : 0u;
     if (!fits) atomicOr(&P.hdr->error, 1u);
   }
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttendParams P) {
+  plan_body(P);
+}
+
+// The scatter of a step's new K/V and the work plan in one launch:
+// workgroup 0 plans, the others scatter with their first S.per_block threads
+// (the rest exit at once).  The two are independent (the plan reads only the
+// metadata, the scatter writes only pool slots); both must be complete
+// before attention reads the pools, which stream order gives.
+template <int D, bool KV8>
+__global__ __launch_bounds__(kPlanThreads) void write_plan_kernel(AttendParams P,
+                                                                  ScatterArgs S) {
+  if (blockIdx.x == 0) {
+    plan_body(P);
+    return;
+  }
+  if ((int)threadIdx.x >= S.per_block) return;
+  const int64_t gid = (int64_t)(blockIdx.x - 1) * S.per_block + threadIdx.x;
+  if constexpr (KV8)
+    write_kv8_thread<D>(gid, S.k, S.v, S.k_stride, S.v_stride, S.slots, S.num_tokens,
+                        S.Hkv, S.k_scale, S.v_scale, static_cast<uint8_t*>(S.k_cache),
+                        static_cast<uint8_t*>(S.v_cache), S.num_slots);
+  else
+    write_kv_thread<D>(gid, S.k, S.v, S.k_stride, S.v_stride, S.slots, S.num_tokens,
+                       S.Hkv, static_cast<uint16_t*>(S.k_cache),
+                       static_cast<uint16_t*>(S.v_cache), S.num_slots);
 }
 
 // ---------------------------------------------------------------------------
@@ -1642,6 +1672,32 @@ hipError_t launch_plan(const AttendArgs& a, hipStream_t stream) {
   if (a.num_q_tokens == 0 || a.num_seqs == 0) return hipSuccess;
   const AttendParams P = make_params(a);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, P);
+  return hipGetLastError();
+}
+
+hipError_t launch_write_plan(const AttendArgs& a, const ScatterArgs& s,
+                             hipStream_t stream) {
+  if (a.num_q_tokens == 0 || a.num_seqs == 0) return hipErrorInvalidValue;
+  if (s.num_tokens == 0) return launch_plan(a, stream);
+  const AttendParams P = make_params(a);
+  // scatter threads: one per (quad of new tokens, kv head, 16-byte unit).
+  // A decode step's scatter is small and its V stores are scattered 1- or
+  // 2-byte writes, limited per CU: spread it over every CU (whole waves,
+  // at most kPlanThreads per workgroup).
+  const int64_t units = a.kv8 ? a.head_dim / 4 : a.head_dim / 8;
+  const int64_t threads = ((s.num_tokens + 3) / 4) * s.Hkv * units;
+  const int64_t cus = a.num_cus > 0 ? a.num_cus : 1;
+  int64_t per = ((threads + cus - 1) / cus + 63) / 64 * 64;
+  per = per < 64 ? 64 : (per > kPlanThreads ? kPlanThreads : per);
+  ScatterArgs sc = s;
+  sc.per_block = (int)per;
+  const dim3 grid((unsigned)(1 + (threads + per - 1) / per));
+  void (*fn)(AttendParams, ScatterArgs);
+  if (a.head_dim == 128)
+    fn = a.kv8 ? write_plan_kernel<128, true> : write_plan_kernel<128, false>;
+  else
+    fn = a.kv8 ? write_plan_kernel<64, true> : write_plan_kernel<64, false>;
+  hipLaunchKernelGGL(fn, grid, dim3(kPlanThreads), 0, stream, P, sc);
   return hipGetLastError();
 }
 

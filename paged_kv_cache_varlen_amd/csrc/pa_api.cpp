@@ -86,11 +86,17 @@ const char* pa_status_string(int status) {
 
 const char* pa_last_error(void) { return g_last_error.c_str(); }
 
-pa_status pa_write_kv(const void* k, const void* v, int64_t k_token_stride,
-                      int64_t v_token_stride, const int64_t* slot_mapping,
-                      int64_t num_tokens, int32_t num_kv_heads,
-                      int32_t head_dim, void* k_cache, void* v_cache,
-                      int64_t num_blocks, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the scatter entry points (the 8-bit scales are checked by
+// the caller, first).
+pa_status check_scatter(const char* name, const void* k, const void* v,
+                        int64_t k_token_stride, int64_t v_token_stride,
+                        const int64_t* slot_mapping, int64_t num_tokens,
+                        int32_t num_kv_heads, int32_t head_dim, const void* k_cache,
+                        const void* v_cache, int64_t num_blocks) {
   if (num_tokens < 0 || num_blocks < 0)
     return fail(PA_ERR_SHAPE, "num_tokens and num_blocks must be >= 0");
   if (num_kv_heads <= 0) return fail(PA_ERR_SHAPE, "num_kv_heads must be > 0");
@@ -101,11 +107,34 @@ pa_status pa_write_kv(const void* k, const void* v, int64_t k_token_stride,
     return fail(PA_ERR_SHAPE, "token strides must be >= num_kv_heads*head_dim");
   if ((k_token_stride % 8) || (v_token_stride % 8))
     return fail(PA_ERR_SHAPE, "token strides must be multiples of 8 elements");
-  if (num_tokens == 0) return ok();
+  if (num_tokens == 0) return PA_OK;
   if (!k || !v || !slot_mapping || !k_cache || !v_cache)
-    return fail(PA_ERR_NULL, "pa_write_kv: NULL pointer");
+    return fail(PA_ERR_NULL, std::string(name) + ": NULL pointer");
   if (((uintptr_t)k | (uintptr_t)v | (uintptr_t)k_cache | (uintptr_t)v_cache) & 15)
     return fail(PA_ERR_SHAPE, "k, v and the pools must be 16-byte aligned");
+  return PA_OK;
+}
+
+// The 8-bit variants: the pools' scales are checked before anything else.
+pa_status check_fp8(float k_scale, float v_scale) {
+  if (!(k_scale > 0.0f && k_scale <= FLT_MAX) || !(v_scale > 0.0f && v_scale <= FLT_MAX))
+    return fail(PA_ERR_SHAPE, "8-bit pools: scales must be finite and > 0");
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_write_kv(const void* k, const void* v, int64_t k_token_stride,
+                      int64_t v_token_stride, const int64_t* slot_mapping,
+                      int64_t num_tokens, int32_t num_kv_heads,
+                      int32_t head_dim, void* k_cache, void* v_cache,
+                      int64_t num_blocks, void* stream) {
+  pa_status s = check_scatter("pa_write_kv", k, v, k_token_stride, v_token_stride,
+                              slot_mapping, num_tokens, num_kv_heads, head_dim, k_cache,
+                              v_cache, num_blocks);
+  if (s != PA_OK || num_tokens == 0) return s == PA_OK ? ok() : s;
   hipError_t e = pa::launch_write_kv(
       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
       k_token_stride, v_token_stride, slot_mapping, num_tokens, num_kv_heads,
@@ -121,23 +150,12 @@ pa_status pa_write_kv_fp8(const void* k, const void* v, int64_t k_token_stride,
                           int32_t head_dim, float k_scale, float v_scale,
                           void* k_cache, void* v_cache, int64_t num_blocks,
                           void* stream) {
-  if (num_tokens < 0 || num_blocks < 0)
-    return fail(PA_ERR_SHAPE, "num_tokens and num_blocks must be >= 0");
-  if (num_kv_heads <= 0) return fail(PA_ERR_SHAPE, "num_kv_heads must be > 0");
-  if (!supported_head_dim(head_dim))
-    return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
-  if (!(k_scale > 0.0f && k_scale <= FLT_MAX) || !(v_scale > 0.0f && v_scale <= FLT_MAX))
-    return fail(PA_ERR_SHAPE, "pa_write_kv_fp8: scales must be finite and > 0");
-  const int64_t row = (int64_t)num_kv_heads * head_dim;
-  if (k_token_stride < row || v_token_stride < row)
-    return fail(PA_ERR_SHAPE, "token strides must be >= num_kv_heads*head_dim");
-  if ((k_token_stride % 8) || (v_token_stride % 8))
-    return fail(PA_ERR_SHAPE, "token strides must be multiples of 8 elements");
-  if (num_tokens == 0) return ok();
-  if (!k || !v || !slot_mapping || !k_cache || !v_cache)
-    return fail(PA_ERR_NULL, "pa_write_kv_fp8: NULL pointer");
-  if (((uintptr_t)k | (uintptr_t)v | (uintptr_t)k_cache | (uintptr_t)v_cache) & 15)
-    return fail(PA_ERR_SHAPE, "k, v and the pools must be 16-byte aligned");
+  pa_status s = check_fp8(k_scale, v_scale);
+  if (s != PA_OK) return s;
+  s = check_scatter("pa_write_kv_fp8", k, v, k_token_stride, v_token_stride,
+                    slot_mapping, num_tokens, num_kv_heads, head_dim, k_cache, v_cache,
+                    num_blocks);
+  if (s != PA_OK || num_tokens == 0) return s == PA_OK ? ok() : s;
   hipError_t e = pa::launch_write_kv8(
       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
       k_token_stride, v_token_stride, slot_mapping, num_tokens, num_kv_heads,
@@ -258,13 +276,6 @@ pa_status prepare_attend(const void* q, const void* k_cache,
   a->kv8 = false;
   a->k_scale = 1.0f;
   a->v_scale = 1.0f;
-  return PA_OK;
-}
-
-// The 8-bit variants: the pools' scales are checked before anything else.
-pa_status check_fp8(float k_scale, float v_scale) {
-  if (!(k_scale > 0.0f && k_scale <= FLT_MAX) || !(v_scale > 0.0f && v_scale <= FLT_MAX))
-    return fail(PA_ERR_SHAPE, "8-bit pools: scales must be finite and > 0");
   return PA_OK;
 }
 
@@ -452,6 +463,112 @@ pa_status pa_attend_plan_cascade(const int32_t* block_tables,
   hipError_t e = pa::launch_plan(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "pa_attend_plan_cascade launch");
   return ok();
+}
+
+// ---- scatter + plan in one launch -------------------------------------------
+
+namespace {
+
+pa_status write_plan_call(const char* name, bool kv8, const void* k, const void* v,
+                          int64_t k_token_stride, int64_t v_token_stride,
+                          const int64_t* slot_mapping, int64_t num_new_tokens,
+                          float k_scale, float v_scale, void* k_cache, void* v_cache,
+                          int64_t num_blocks, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                          const int32_t* query_start_loc, int32_t num_seqs,
+                          int64_t num_q_tokens, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t max_query_len,
+                          int32_t max_seq_len, int32_t common_prefix_len,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  pa_status s = kv8 ? check_fp8(k_scale, v_scale) : PA_OK;
+  if (s != PA_OK) return s;
+  s = check_scatter(name, k, v, k_token_stride, v_token_stride, slot_mapping,
+                    num_new_tokens, num_kv_heads, head_dim, k_cache, v_cache, num_blocks);
+  if (s != PA_OK) return s;
+  pa::AttendArgs a;
+  bool empty;
+  s = prepare_attend(nullptr, nullptr, nullptr, num_blocks, block_tables,
+                     max_blocks_per_seq, seq_lens, query_start_loc, num_seqs,
+                     num_q_tokens, num_q_heads, num_kv_heads, head_dim, max_query_len,
+                     max_seq_len, 0.0f, nullptr, workspace, workspace_bytes, false, &a,
+                     &empty, common_prefix_len < 0 ? -1 : common_prefix_len);
+  if (s != PA_OK) return s;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (empty) {
+    // nothing to plan: the scatter alone
+    if (num_new_tokens == 0) return ok();
+    e = kv8 ? pa::launch_write_kv8(static_cast<const uint16_t*>(k),
+                                   static_cast<const uint16_t*>(v), k_token_stride,
+                                   v_token_stride, slot_mapping, num_new_tokens,
+                                   num_kv_heads, head_dim, k_scale, v_scale,
+                                   static_cast<uint8_t*>(k_cache),
+                                   static_cast<uint8_t*>(v_cache), num_blocks, st)
+            : pa::launch_write_kv(static_cast<const uint16_t*>(k),
+                                  static_cast<const uint16_t*>(v), k_token_stride,
+                                  v_token_stride, slot_mapping, num_new_tokens,
+                                  num_kv_heads, head_dim, static_cast<uint16_t*>(k_cache),
+                                  static_cast<uint16_t*>(v_cache), num_blocks, st);
+  } else {
+    a.kv8 = kv8;
+    pa::ScatterArgs sc;
+    sc.k = static_cast<const uint16_t*>(k);
+    sc.v = static_cast<const uint16_t*>(v);
+    sc.k_stride = k_token_stride;
+    sc.v_stride = v_token_stride;
+    sc.slots = slot_mapping;
+    sc.num_tokens = num_new_tokens;
+    sc.Hkv = num_kv_heads;
+    sc.k_scale = k_scale;
+    sc.v_scale = v_scale;
+    sc.k_cache = k_cache;
+    sc.v_cache = v_cache;
+    sc.num_slots = num_blocks * pa::kBlock;
+    sc.per_block = 0;  // chosen by the launcher
+    e = pa::launch_write_plan(a, sc, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, (std::string(name) + " launch").c_str());
+  return ok();
+}
+
+}  // namespace
+
+pa_status pa_write_kv_plan(const void* k, const void* v, int64_t k_token_stride,
+                           int64_t v_token_stride, const int64_t* slot_mapping,
+                           int64_t num_new_tokens, void* k_cache, void* v_cache,
+                           int64_t num_blocks, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                           const int32_t* query_start_loc, int32_t num_seqs,
+                           int64_t num_q_tokens, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim,
+                           int32_t max_query_len, int32_t max_seq_len,
+                           int32_t common_prefix_len, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return write_plan_call("pa_write_kv_plan", false, k, v, k_token_stride, v_token_stride,
+                         slot_mapping, num_new_tokens, 1.0f, 1.0f, k_cache, v_cache,
+                         num_blocks, block_tables, max_blocks_per_seq, seq_lens,
+                         query_start_loc, num_seqs, num_q_tokens, num_q_heads,
+                         num_kv_heads, head_dim, max_query_len, max_seq_len,
+                         common_prefix_len, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_write_kv_plan_fp8(const void* k, const void* v, int64_t k_token_stride,
+                               int64_t v_token_stride, const int64_t* slot_mapping,
+                               int64_t num_new_tokens, float k_scale, float v_scale,
+                               void* k_cache, void* v_cache, int64_t num_blocks,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* seq_lens, const int32_t* query_start_loc,
+                               int32_t num_seqs, int64_t num_q_tokens,
+                               int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t max_query_len,
+                               int32_t max_seq_len, int32_t common_prefix_len,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  return write_plan_call("pa_write_kv_plan_fp8", true, k, v, k_token_stride,
+                         v_token_stride, slot_mapping, num_new_tokens, k_scale, v_scale,
+                         k_cache, v_cache, num_blocks, block_tables, max_blocks_per_seq,
+                         seq_lens, query_start_loc, num_seqs, num_q_tokens, num_q_heads,
+                         num_kv_heads, head_dim, max_query_len, max_seq_len,
+                         common_prefix_len, workspace, workspace_bytes, stream);
 }
 
 namespace {

@@ -286,6 +286,28 @@ struct AttendArgs {
 
 // Work plan into the workspace (one small kernel).
 hipError_t launch_plan(const AttendArgs& a, hipStream_t stream);
+
+// The scatter's arguments for the fused scatter + plan launch (the pools as
+// bf16 or, with AttendArgs::kv8, as 8-bit codes with their scales).
+struct ScatterArgs {
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t k_stride;     // elements between consecutive tokens of k
+  int64_t v_stride;
+  const int64_t* slots;
+  int64_t num_tokens;
+  int Hkv;
+  float k_scale;
+  float v_scale;
+  void* k_cache;
+  void* v_cache;
+  int64_t num_slots;    // num_blocks * 16
+  int per_block;        // scatter threads per workgroup (set by the launcher)
+};
+// Scatter of the new K/V and the work plan in one launch (a non-empty plan;
+// without new tokens, the plan alone).
+hipError_t launch_write_plan(const AttendArgs& a, const ScatterArgs& s,
+                             hipStream_t stream);
 // Attention over the plan in the workspace (one persistent kernel).
 hipError_t launch_planned(const AttendArgs& a, hipStream_t stream);
 // Split-K merge of the partials the attention kernel left in the workspace.

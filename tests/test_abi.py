@@ -124,6 +124,47 @@ def test_write_kv_fp8_argument_checks(lib, args, status):
     assert lib.pa_write_kv_fp8(*args) == status
 
 
+def _wp(k=FAKE, D=128, T=4, C=-1, wsb=1 << 30, bt=FAKE, fp8=None):
+    """pa_write_kv_plan(_fp8) arguments: 4 new tokens, 2 requests of 8 query
+    tokens over 2 kv heads, a workspace of wsb bytes."""
+    scatter = [k, FAKE, 256, 256, FAKE, T]
+    if fp8 is not None:
+        scatter += list(fp8)
+    return tuple(scatter + [FAKE, FAKE, 8, bt, 4, FAKE, FAKE, 2, 8, 4, 2, D, 4, 60, C,
+                            FAKE, wsb, None])
+
+
+@pytest.mark.parametrize("args,status", [
+    (_wp(D=96), _lib.PA_ERR_UNSUPPORTED),
+    (_wp(k=None), _lib.PA_ERR_NULL),
+    (_wp(T=-1), _lib.PA_ERR_SHAPE),
+    (_wp(bt=None), _lib.PA_ERR_NULL),
+    (_wp(wsb=64), _lib.PA_ERR_WORKSPACE),
+    (_wp(C=61), _lib.PA_ERR_SHAPE),
+])
+def test_write_kv_plan_argument_checks(lib, args, status):
+    assert lib.pa_write_kv_plan(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    (_wp(fp8=(0.0, 1.0)), _lib.PA_ERR_SHAPE),
+    (_wp(fp8=(1.0, float("nan"))), _lib.PA_ERR_SHAPE),
+    (_wp(fp8=(1.0, 1.0), D=96), _lib.PA_ERR_UNSUPPORTED),
+    (_wp(fp8=(1.0, 1.0), wsb=64), _lib.PA_ERR_WORKSPACE),
+])
+def test_write_kv_plan_fp8_argument_checks(lib, args, status):
+    assert lib.pa_write_kv_plan_fp8(*args) == status
+
+
+def test_write_kv_plan_workspace_sizes(lib):
+    # a plain plan needs the plain workspace, a shared-prefix plan the larger one
+    plain = lib.pa_attend_workspace_size(2, 8, 4, 2, 128, 4, 60)
+    casc = lib.pa_attend_cascade_workspace_size(2, 8, 4, 2, 128, 4, 60)
+    assert 0 < plain < casc
+    assert lib.pa_write_kv_plan(*_wp(C=32, wsb=plain)) == _lib.PA_ERR_WORKSPACE
+    assert lib.pa_write_kv_plan(*_wp(C=-1, wsb=plain - 1)) == _lib.PA_ERR_WORKSPACE
+
+
 def test_gather_argument_checks(lib):
     st = lib.pa_gather_kv(None, FAKE, 8, FAKE, 4, FAKE, FAKE, 2, 10, 2, 64, FAKE,
                           FAKE, None)

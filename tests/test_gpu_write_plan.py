@@ -1,0 +1,130 @@
+"""GPU parity of the fused scatter + work plan (pa_write_kv_plan(_fp8)).
+
+The call replaces pa_write_kv (pa_write_kv_fp8) and pa_attend_plan
+(pa_attend_plan_cascade) of the same step, so its bars are theirs: every pool
+byte equal to the oracle's scatter, and attention over the fused call's plan
+bit-identical to pa_attend over the separately written pools (the plan is
+the same work list, so the same kernels produce the same bits), which is
+itself within the attention tolerance of the fp64 oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_varlen_amd as pa
+from tests.gpu_util import Uploaded, bf16_tensor, i32, i64, tensor_bits
+from tests.test_gpu_cascade import casc, cascade_ws, oracle_ref, run_cascade
+from tests.test_gpu_fp8 import attend8, gpu_pool8, oracle_pool8, u8_bits
+from tests.test_gpu_parity import check_close, oracle_pool, small
+
+pytestmark = pytest.mark.gpu
+
+
+def fused(u, k_cache, v_cache, ws, common_prefix_len=None, scales=(None, None)):
+    w = u.w
+    pa.write_kv_plan(u.k_new, u.v_new, u.new_slots, k_cache, v_cache, u.block_tables,
+                     u.seq_lens, u.qsl, w.num_q_tokens, w.num_q_heads, w.max_query_len,
+                     w.max_seq_len, ws, common_prefix_len=common_prefix_len,
+                     k_scale=scales[0], v_scale=scales[1])
+
+
+@pytest.mark.parametrize("name", ["mixed-g4-d128", "mixed-g1-d64", "mixed-h3-d64",
+                                  "mixed-g16-d128", "mixed-split-edge"])
+def test_fused_bf16_equals_separate_calls(name):
+    w = small(name, seed=21)
+    u = Uploaded(w, write_new=False)
+    fused(u, u.k_cache, u.v_cache, u.workspace)
+    got = tensor_bits(u.attend(out=torch.empty_like(u.q), planned=True)).copy()
+    torch.cuda.synchronize()
+    kc, vc = oracle_pool(w)
+    assert np.array_equal(tensor_bits(u.k_cache).ravel(), kc)
+    assert np.array_equal(tensor_bits(u.v_cache).ravel(), vc)
+    ref = Uploaded(w)
+    want = tensor_bits(ref.attend()).copy()
+    assert np.array_equal(got, want)
+    check_close(got, oracle.attend(w.q, kc, vc, w.block_tables, w.seq_lens,
+                                   w.query_start_loc, w.num_kv_heads, w.scale), name)
+
+
+@pytest.mark.parametrize("name", ["mixed-g4-d128", "mixed-g1-d64", "mixed-h3-d64"])
+def test_fused_fp8_equals_separate_calls(name):
+    w = small(name, seed=22)
+    scales = (0.011, 0.0107)
+    # pools holding every token but the new ones, then the fused call
+    kc, vc = pa.alloc_pool_fp8(w.num_blocks, w.num_kv_heads, w.head_dim, fill=0x7F)
+    if len(w.fill_rows):
+        pa.write_kv_fp8(bf16_tensor(w.k_dense[w.fill_rows]),
+                        bf16_tensor(w.v_dense[w.fill_rows]), i64(w.fill_slots), kc, vc,
+                        *scales)
+    u = Uploaded(w, write_new=False)
+    fused(u, kc, vc, u.workspace, scales=scales)
+    got = tensor_bits(pa.attend(u.q, kc, vc, u.block_tables, u.seq_lens, u.qsl, w.scale,
+                                w.max_query_len, w.max_seq_len,
+                                num_kv_heads=w.num_kv_heads, out=torch.empty_like(u.q),
+                                workspace=u.workspace, planned=True,
+                                k_scale=scales[0], v_scale=scales[1])).copy()
+    torch.cuda.synchronize()
+    okc, ovc = oracle_pool8(w, *scales)
+    assert np.array_equal(u8_bits(kc), okc)
+    assert np.array_equal(u8_bits(vc), ovc)
+    rk, rv = gpu_pool8(w, *scales)
+    assert np.array_equal(got, attend8(w, rk, rv, *scales))
+
+
+@pytest.mark.parametrize("name", ["casc-decode-g4-d128", "casc-mixed-g4-d128",
+                                  "casc-g8-d64-p48"])
+def test_fused_shared_prefix_plan(name):
+    w, C = casc(name, seed=23)
+    u = Uploaded(w, write_new=False)
+    ws = cascade_ws(w)
+    fused(u, u.k_cache, u.v_cache, ws, common_prefix_len=C)
+    got = tensor_bits(pa.attend(u.q, u.k_cache, u.v_cache, u.block_tables, u.seq_lens,
+                                u.qsl, w.scale, w.max_query_len, w.max_seq_len,
+                                num_kv_heads=w.num_kv_heads, out=torch.empty_like(u.q),
+                                workspace=ws, planned=True,
+                                common_prefix_len=C)).copy()
+    torch.cuda.synchronize()
+    kc, vc = oracle_pool(w)
+    assert np.array_equal(tensor_bits(u.k_cache).ravel(), kc)
+    assert np.array_equal(tensor_bits(u.v_cache).ravel(), vc)
+    assert np.array_equal(got, run_cascade(Uploaded(w), C))
+    check_close(got, oracle_ref(w), name)
+
+
+def test_fused_without_new_tokens_is_the_plan():
+    w = small("mixed-g4-d128", seed=24)
+    u = Uploaded(w)
+    none = torch.empty((0, w.num_kv_heads, w.head_dim), dtype=torch.bfloat16,
+                       device="cuda")
+    pa.write_kv_plan(none, none, i64(np.zeros(0, np.int64)), u.k_cache, u.v_cache,
+                     u.block_tables, u.seq_lens, u.qsl, w.num_q_tokens, w.num_q_heads,
+                     w.max_query_len, w.max_seq_len, u.workspace)
+    got = tensor_bits(u.attend(out=torch.empty_like(u.q), planned=True)).copy()
+    want = tensor_bits(Uploaded(w).attend()).copy()
+    assert np.array_equal(got, want)
+
+
+def test_fused_with_nothing_to_plan_is_the_scatter():
+    w = small("mixed-g1-d64", seed=25)
+    u = Uploaded(w, write_new=False)
+    empty_qsl = i32(np.zeros(1, np.int32))
+    pa.write_kv_plan(u.k_new, u.v_new, u.new_slots, u.k_cache, u.v_cache,
+                     u.block_tables[:0], u.seq_lens[:0], empty_qsl, 0, w.num_q_heads,
+                     0, 0, u.workspace)
+    torch.cuda.synchronize()
+    kc, vc = oracle_pool(w)
+    assert np.array_equal(tensor_bits(u.k_cache).ravel(), kc)
+    assert np.array_equal(tensor_bits(u.v_cache).ravel(), vc)
+
+
+def test_fused_plan_serves_several_layers():
+    # a forward step: the fused call writes the first layer's
+    # new tokens and plans; every other layer reuses the plan
+    w = small("mixed-g8-d128", seed=26)
+    u = Uploaded(w, write_new=False)
+    fused(u, u.k_cache, u.v_cache, u.workspace)
+    a = tensor_bits(u.attend(out=torch.empty_like(u.q), planned=True)).copy()
+    b = tensor_bits(u.attend(out=torch.empty_like(u.q), planned=True)).copy()
+    assert np.array_equal(a, b)
+    assert np.array_equal(a, tensor_bits(Uploaded(w).attend()))
