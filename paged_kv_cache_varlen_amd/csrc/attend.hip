@@ -695,7 +695,7 @@ __device__ __forceinline__ uint32_t run_unit(const AttendParams& P,
                                              uint32_t* counter = nullptr) {
   constexpr int KC = D / 32;
   constexpr int NT = D / 16;
-  const int g = lane >> 4, r = lane & 15;
+  const int g = lane >> 4;
   const int b = it.seq;
   const int posbase = it.posbase;  // position of the tile's first token
 
