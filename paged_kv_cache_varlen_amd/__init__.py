@@ -155,20 +155,32 @@ def alloc_workspace(num_seqs, num_q_tokens, num_q_heads, num_kv_heads, head_dim,
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+def _metadata_args(block_tables, seq_lens, query_start_loc) -> int:
+    """Checks of a step's metadata tensors; returns the number of requests."""
+    for t, n in ((block_tables, "block_tables"), (seq_lens, "seq_lens"),
+                 (query_start_loc, "query_start_loc")):
+        _need_cuda(t, n)
+        _dtype(t, torch.int32, n)
+    if block_tables.dim() != 2 or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be contiguous [num_seqs][max_blocks]")
+    B = block_tables.shape[0]
+    if seq_lens.shape != (B,) or query_start_loc.shape != (B + 1,):
+        raise ValueError("seq_lens must be [B] and query_start_loc [B+1]")
+    if not (seq_lens.is_contiguous() and query_start_loc.is_contiguous()):
+        raise ValueError("seq_lens and query_start_loc must be contiguous")
+    return B
+
+
 def _attend_args(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
                  num_kv_heads, out, workspace, max_query_len, max_seq_len,
                  cascade=False):
-    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
-                 (block_tables, "block_tables"), (seq_lens, "seq_lens"),
-                 (query_start_loc, "query_start_loc")):
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _need_cuda(t, n)
     _dtype(q, torch.bfloat16, "q")
     pool_dtype = torch.uint8 if k_cache.dtype == torch.uint8 else torch.bfloat16
     _dtype(k_cache, pool_dtype, "k_cache")
     _dtype(v_cache, pool_dtype, "v_cache")
-    _dtype(block_tables, torch.int32, "block_tables")
-    _dtype(seq_lens, torch.int32, "seq_lens")
-    _dtype(query_start_loc, torch.int32, "query_start_loc")
+    B = _metadata_args(block_tables, seq_lens, query_start_loc)
     if q.dim() != 3 or not q.is_contiguous():
         raise ValueError("q must be contiguous [num_q_tokens][num_q_heads][head_dim]")
     T, Hq, D = q.shape
@@ -179,11 +191,6 @@ def _attend_args(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
     nb = _pool_blocks(k_cache, num_kv_heads, D)
     if _pool_blocks(v_cache, num_kv_heads, D) != nb:
         raise ValueError("k_cache and v_cache differ in size")
-    if block_tables.dim() != 2 or not block_tables.is_contiguous():
-        raise ValueError("block_tables must be contiguous [num_seqs][max_blocks]")
-    B = block_tables.shape[0]
-    if seq_lens.shape != (B,) or query_start_loc.shape != (B + 1,):
-        raise ValueError("seq_lens must be [B] and query_start_loc [B+1]")
     if out is None:
         out = torch.empty_like(q)
     else:
@@ -273,10 +280,8 @@ def attend_plan(block_tables: torch.Tensor, seq_lens: torch.Tensor,
     with attend(..., planned=True) for each layer that shares the metadata
     (with common_prefix_len: a shared-prefix plan, run by
     attend(..., planned=True, common_prefix_len=...))."""
-    for t, n in ((block_tables, "block_tables"), (seq_lens, "seq_lens"),
-                 (query_start_loc, "query_start_loc"), (workspace, "workspace")):
-        _need_cuda(t, n)
-    B = block_tables.shape[0]
+    B = _metadata_args(block_tables, seq_lens, query_start_loc)
+    _need_cuda(workspace, "workspace")
     lib = _lib.load()
     args = [_ptr(block_tables), block_tables.shape[1], _ptr(seq_lens),
             _ptr(query_start_loc), B, int(num_q_tokens), int(num_q_heads),
@@ -304,9 +309,8 @@ def write_kv_plan(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
     fp8 = k_cache.dtype == torch.uint8
     T, Hkv, D, nb = _scatter_args(k, v, slot_mapping, k_cache, v_cache,
                                   torch.uint8 if fp8 else torch.bfloat16)
-    for t, n in ((block_tables, "block_tables"), (seq_lens, "seq_lens"),
-                 (query_start_loc, "query_start_loc"), (workspace, "workspace")):
-        _need_cuda(t, n)
+    B = _metadata_args(block_tables, seq_lens, query_start_loc)
+    _need_cuda(workspace, "workspace")
     if fp8 and (k_scale is None or v_scale is None):
         raise ValueError("8-bit pools need k_scale and v_scale")
     lib = _lib.load()
@@ -314,9 +318,9 @@ def write_kv_plan(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
     if fp8:
         scatter += [float(k_scale), float(v_scale)]
     plan = [_ptr(k_cache), _ptr(v_cache), nb, _ptr(block_tables), block_tables.shape[1],
-            _ptr(seq_lens), _ptr(query_start_loc), block_tables.shape[0],
-            int(num_q_tokens), int(num_q_heads), Hkv, D, int(max_query_len),
-            int(max_seq_len), -1 if common_prefix_len is None else int(common_prefix_len),
+            _ptr(seq_lens), _ptr(query_start_loc), B, int(num_q_tokens), int(num_q_heads),
+            Hkv, D, int(max_query_len), int(max_seq_len),
+            -1 if common_prefix_len is None else int(common_prefix_len),
             _ptr(workspace), workspace.numel(), _stream(k)]
     name = "pa_write_kv_plan_fp8" if fp8 else "pa_write_kv_plan"
     _lib.check(getattr(lib, name)(*scatter, *plan), name)
