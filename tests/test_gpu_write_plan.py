@@ -134,11 +134,11 @@ def test_binding_rejects_metadata_of_other_types():
     # int32 metadata only: an int64 seq_lens read as int32 would be other lengths
     w = small("mixed-g1-d64", seed=27)
     u = Uploaded(w, write_new=False)
-    with pytest.raises(ValueError):
+    with pytest.raises(TypeError):
         pa.write_kv_plan(u.k_new, u.v_new, u.new_slots, u.k_cache, u.v_cache,
                          u.block_tables, u.seq_lens.to(torch.int64), u.qsl, w.num_q_tokens,
                          w.num_q_heads, w.max_query_len, w.max_seq_len, u.workspace)
-    with pytest.raises(ValueError):
+    with pytest.raises(TypeError):
         pa.attend_plan(u.block_tables.to(torch.int64), u.seq_lens, u.qsl, w.num_q_tokens,
                        w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_query_len,
                        w.max_seq_len, u.workspace)
