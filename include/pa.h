@@ -9,7 +9,9 @@
  *   pa_attend    varlen causal attention of every query token of a mixed batch
  *                (chunked-prefill chunks and single-token decodes together, one
  *                call) over each request's cached + new tokens, read through
- *                its block table.
+ *                its block table;
+ *   pa_write_kv_plan  the scatter and attention's work plan of a step in one
+ *                launch (then pa_attend_planned + pa_attend_merge per layer).
  *
  * Where the operations are defined:
  *   - "vLLM v1 Deep Dive" (supercharleszhu.github.io), Part 3 Runtime, Aside "KV
