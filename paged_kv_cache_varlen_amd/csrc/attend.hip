@@ -963,9 +963,6 @@ __device__ __forceinline__ void wait_loads_and_barrier() {
 __device__ __forceinline__ bf16x8 lds16(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
-__device__ __forceinline__ bf16x4 lds8(const uint16_t* p) {
-  return *reinterpret_cast<const bf16x4*>(p);
-}
 
 // One LDS read of 2 x 8 bytes at addr + 512 O0 and addr + 512 O1 (bytes)
 // into one 16-byte operand.  Inline assembly, so the compiler neither pairs
@@ -1502,13 +1499,34 @@ void attend_mixed_kernel(AttendParams P) {
 // merge
 // ---------------------------------------------------------------------------
 
-// W waves per (split tile, kv head), W = the passes one token's G columns
+// Online log-sum-exp state of one column over the lane's 8 dims: running
+// max M (log2 domain), denominator and the two 4-dim numerator halves.
+struct MergeState {
+  float M, den;
+  f32x4 n0, n1;
+};
+
+// Folds one partial (running max m, sum l, accumulator a0|a1) into st.
+__device__ __forceinline__ void merge_fold(MergeState& st, float m, float l, f32x4 a0,
+                                           f32x4 a1) {
+  const float mn = fmaxf(st.M, m);
+  const float mu = (mn == -INFINITY) ? 0.0f : mn;
+  const float c_old = __builtin_amdgcn_exp2f(st.M - mu);
+  const float c_new = __builtin_amdgcn_exp2f(m - mu);
+  st.den = st.den * c_old + l * c_new;
+  st.n0 = st.n0 * c_old + a0 * c_new;
+  st.n1 = st.n1 * c_old + a1 * c_new;
+  st.M = mn;
+}
+
+// W passes per (split tile, kv head), W = the passes one token's G columns
 // take (at most 4): the tile's columns of that kv head are dealt to them
-// round-robin, 64 / (D/8) at a time (lanes cover (column, 8 dims)), so a
-// decode request's query heads merge in parallel.  Each column's splits are
-// combined by an online log-sum-exp in split order (a fixed order: the
-// result does not depend on timing), with the loads of 8 splits in flight
-// per step.
+// round-robin, 64 / (D/8) at a time (lanes cover (column, 8 dims)).  One
+// workgroup per (split tile, kv head, pass): its 4 waves fold consecutive
+// quarters of each column's partials (a shared prefix's first, then the
+// tile's own splits, in split order, 8 loads in flight per lane), and wave 0
+// folds the 4 wave states in wave order: a fixed order, so the result does
+// not depend on timing, and a long chain of splits is 4 chains of a quarter.
 __host__ __device__ inline uint32_t merge_waves_per_head(int G, int D) {
   const int cpw = 64 / (D / 8);
   const int w = (G + cpw - 1) / cpw;
@@ -1519,8 +1537,10 @@ __global__ __launch_bounds__(kAttendThreads) void merge_kernel(AttendParams P) {
   constexpr int LPC = D / 8;      // lanes per column
   constexpr int CPW = 64 / LPC;   // columns per wave pass
   constexpr int SB = 8;           // splits per step
+  constexpr int NW = kAttendThreads / 64;
+  __shared__ float4 wstate[NW - 1][3][64];  // waves 1..: (M, den), n0, n1 per lane
   const int lane = threadIdx.x & 63;
-  const int nwaves = gridDim.x * (kAttendThreads / 64);
+  const int wave = threadIdx.x >> 6;
   const int G = P.G;
   if (P.hdr->signature != plan_signature(P)) return;
   uint32_t ntiles = P.hdr->num_split_tiles;
@@ -1536,12 +1556,12 @@ __global__ __launch_bounds__(kAttendThreads) void merge_kernel(AttendParams P) {
   const uint32_t nunits = ntiles * per_tile;
   const int cl = lane / LPC;          // column within the pass
   const int d0 = (lane % LPC) * 8;    // first of the lane's 8 dims
-  for (uint32_t u = blockIdx.x * (kAttendThreads / 64) + (threadIdx.x >> 6);
-       u < nunits; u += nwaves) {
+  for (uint32_t u = blockIdx.x; u < nunits; u += gridDim.x) {
     const int4 tile = P.merge_list[u / per_tile];  // tok0, ntok, nsplit, pbase
     const int kvh = (int)((u % per_tile) / W);
     const int pass0 = (int)(u % W);
     // same rule as for work items: never follow an entry out of bounds
+    // (the same decision in every wave of the workgroup)
     if (tile.x < 0 || tile.y < 1 || tile.x + tile.y > P.num_q_tokens ||
         tile.z < (npre > 0 ? 1 : 2) || tile.w < 0 ||
         (int64_t)tile.w + (int64_t)tile.y * tile.z > P.max_partials)
@@ -1549,55 +1569,64 @@ __global__ __launch_bounds__(kAttendThreads) void merge_kernel(AttendParams P) {
     const int ncols = tile.y * G;
     const int nsplit = tile.z;
     const int nall = npre + nsplit;
+    const int s_lo = wave * nall / NW, s_hi = (wave + 1) * nall / NW;
     for (int c0 = pass0 * CPW; c0 < ncols; c0 += (int)W * CPW) {
       const int c = c0 + cl;
-      if (c >= ncols) continue;
-      const int tk = c / G;
+      const bool valid = c < ncols;
+      const int tk = valid ? c / G : 0;
       const int h = kvh * G + (c - tk * G);
+      const int64_t tok = (int64_t)(tile.x + tk);
       const int64_t slot0 = (int64_t)tile.w + (int64_t)tk * nsplit;
-      float M = -INFINITY, den = 0.0f;
-      f32x4 n0 = {0.f, 0.f, 0.f, 0.f}, n1 = {0.f, 0.f, 0.f, 0.f};
-      for (int s0 = 0; s0 < nall; s0 += SB) {
-        float2 ml[SB];
-        f32x4 a0[SB], a1[SB];
+      MergeState st{-INFINITY, 0.0f, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      if (valid) {
+        for (int s0 = s_lo; s0 < s_hi; s0 += SB) {
+          float2 ml[SB];
+          f32x4 a0[SB], a1[SB];
 #pragma unroll
-        for (int k = 0; k < SB; ++k) {
-          const int sp = s0 + k;
-          if (sp < nall) {
-            const bool pre = sp < npre;
-            const int64_t row =
-                (pre ? (int64_t)(tile.x + tk) * npre + sp : slot0 + (sp - npre)) * P.Hq + h;
-            ml[k] = (pre ? P.pre_ml : P.part_ml)[row];
-            const f32x4* ap =
-                reinterpret_cast<const f32x4*>((pre ? P.pre_acc : P.part_acc) + row * D + d0);
-            a0[k] = ap[0];
-            a1[k] = ap[1];
-          } else {
-            ml[k] = make_float2(-INFINITY, 0.0f);
-            a0[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-            a1[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int k = 0; k < SB; ++k) {
+            const int sp = s0 + k;
+            if (sp < s_hi) {
+              const bool pre = sp < npre;
+              const int64_t row = (pre ? tok * npre + sp : slot0 + (sp - npre)) * P.Hq + h;
+              ml[k] = (pre ? P.pre_ml : P.part_ml)[row];
+              const f32x4* ap = reinterpret_cast<const f32x4*>(
+                  (pre ? P.pre_acc : P.part_acc) + row * D + d0);
+              a0[k] = ap[0];
+              a1[k] = ap[1];
+            } else {
+              ml[k] = make_float2(-INFINITY, 0.0f);
+              a0[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+              a1[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
           }
-        }
 #pragma unroll
-        for (int k = 0; k < SB; ++k) {
-          const float mn = fmaxf(M, ml[k].x);
-          const float mu = (mn == -INFINITY) ? 0.0f : mn;
-          const float c_old = __builtin_amdgcn_exp2f(M - mu);
-          const float c_new = __builtin_amdgcn_exp2f(ml[k].x - mu);
-          den = den * c_old + ml[k].y * c_new;
-          n0 = n0 * c_old + a0[k] * c_new;
-          n1 = n1 * c_old + a1[k] * c_new;
-          M = mn;
+          for (int k = 0; k < SB; ++k) merge_fold(st, ml[k].x, ml[k].y, a0[k], a1[k]);
         }
       }
-      const float inv = 1.0f / den;
-      bf16x8 o;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        o[i] = (__bf16)(n0[i] * inv);
-        o[i + 4] = (__bf16)(n1[i] * inv);
+      if (wave > 0) {
+        wstate[wave - 1][0][lane] = make_float4(st.M, st.den, 0.0f, 0.0f);
+        wstate[wave - 1][1][lane] = make_float4(st.n0[0], st.n0[1], st.n0[2], st.n0[3]);
+        wstate[wave - 1][2][lane] = make_float4(st.n1[0], st.n1[1], st.n1[2], st.n1[3]);
       }
-      *reinterpret_cast<bf16x8*>(P.out + ((int64_t)(tile.x + tk) * P.Hq + h) * D + d0) = o;
+      __syncthreads();
+      if (wave == 0 && valid) {
+#pragma unroll
+        for (int w = 0; w < NW - 1; ++w) {
+          const float4 md = wstate[w][0][lane], x0 = wstate[w][1][lane],
+                       x1 = wstate[w][2][lane];
+          merge_fold(st, md.x, md.y, f32x4{x0.x, x0.y, x0.z, x0.w},
+                     f32x4{x1.x, x1.y, x1.z, x1.w});
+        }
+        const float inv = 1.0f / st.den;
+        bf16x8 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o[i] = (__bf16)(st.n0[i] * inv);
+          o[i + 4] = (__bf16)(st.n1[i] * inv);
+        }
+        *reinterpret_cast<bf16x8*>(P.out + (tok * P.Hq + h) * D + d0) = o;
+      }
+      __syncthreads();  // wstate is rewritten by the next pass
     }
   }
 }
@@ -1737,13 +1766,13 @@ hipError_t launch_planned(const AttendArgs& a, hipStream_t stream) {
 hipError_t launch_merge(const AttendArgs& a, hipStream_t stream) {
   if (a.num_q_tokens == 0 || a.num_seqs == 0) return hipSuccess;
   const AttendParams P = make_params(a);
-  // at most W waves per (split tile, kv head), never more than the resident
-  // waves of the chip
-  int64_t mwaves = a.ws.max_items * a.num_kv_heads *
-                   merge_waves_per_head(a.num_q_heads / a.num_kv_heads, a.head_dim);
-  const int64_t cap = (int64_t)a.num_cus * 8 * 4;
-  if (mwaves > cap) mwaves = cap;
-  const int64_t mwgs = (mwaves + (kAttendThreads / 64) - 1) / (kAttendThreads / 64);
+  // one workgroup per (split tile, kv head, pass), at most 8 per CU (the
+  // workgroups stride over the units)
+  int64_t mwgs = a.ws.max_items * a.num_kv_heads *
+                 merge_waves_per_head(a.num_q_heads / a.num_kv_heads, a.head_dim);
+  const int64_t cap = (int64_t)a.num_cus * 8;
+  if (mwgs > cap) mwgs = cap;
+  if (mwgs < 1) mwgs = 1;
   if (a.head_dim == 128)
     hipLaunchKernelGGL(merge_kernel<128>, dim3((unsigned)mwgs), dim3(kAttendThreads),
                        0, stream, P);
