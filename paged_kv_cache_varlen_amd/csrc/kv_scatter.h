@@ -30,7 +30,8 @@ __device__ __forceinline__ int v_offset(int t, int d) {
   return ((((d % H) / 16 * 2 + d / H) * 4 + (t >> 2)) * 16 + d % 16) * 4 + (t & 3);
 }
 
-// One thread per (quad of consecutive new tokens, kv head, 8-dim chunk): a
+// Scatter thread gid (0 <= gid < ceil(T/4) * Hkv * D/8; larger gids do
+// nothing), one per (quad of consecutive new tokens, kv head, 8-dim chunk): a
 // 16-byte K copy per token; for V, when the quad's slots are the four slots
 // 4m .. 4m+3 of one block (a prefill chunk's tokens), one 8-byte run per dim
 // (the layout keeps 4 consecutive tokens of a dim together), otherwise
@@ -143,8 +144,9 @@ __device__ __forceinline__ uint32_t e4m3_pair(float a, float b) {
   return w;
 }
 
-// One thread per (quad of consecutive new tokens, kv head, 16-byte unit u of
-// the D/4 units a quad fills in each pool).  K: unit u belongs to token
+// 8-bit scatter thread gid (0 <= gid < ceil(T/4) * Hkv * D/4; larger gids
+// do nothing), one per (quad of consecutive new tokens, kv head, 16-byte
+// unit u of the D/4 units a quad fills in each pool).  K: unit u belongs to token
 // u / (D/16) of the quad (its own slot); V: unit u = (p, r) holds the quad's
 // 4 tokens for 4 dims, one 16-byte store when the quad fills slots
 // 4m .. 4m+3 of one block, single-byte stores per token otherwise.  Slots
