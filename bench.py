@@ -97,7 +97,7 @@ def kernel_source_hash() -> str:
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_varlen_amd", "csrc")
-    for f in ("attend.hip", "pa_device.h", "kv_cache.hip"):
+    for f in ("attend.hip", "pa_device.h", "kv_cache.hip", "kv_scatter.h", "mfma_util.h"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

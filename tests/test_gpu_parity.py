@@ -277,6 +277,19 @@ def test_plan_then_planned_equals_attend(name):
     assert np.array_equal(a, b1) and np.array_equal(a, b2)
 
 
+@pytest.mark.parametrize("Hq,Hkv,D", [(8, 2, 128), (16, 8, 64)])
+def test_long_chains_of_splits(Hq, Hkv, D):
+    # 137, 3 and 79 splits of 512 keys (chains not divisible by the merge
+    # workgroup's 4 waves) beside a chunk: every row against the oracle
+    w = W.make_workload("long-splits", [70000, 1500, 40000, 900], [1, 1, 1, 37], Hq, Hkv, D,
+                        seed=15)
+    out = tensor_bits(Uploaded(w).attend())
+    kc, vc = oracle_pool(w)
+    ref = oracle.attend(w.q, kc, vc, w.block_tables, w.seq_lens, w.query_start_loc,
+                        w.num_kv_heads, w.scale)
+    check_close(out, ref, "long chains of splits")
+
+
 @pytest.mark.parametrize("k", [2, 3])
 def test_one_plan_several_launches(k):
     # more units than resident waves, so most units are claimed from the
