@@ -46,6 +46,9 @@ CASES = {
     "spec-decode-h16": ([40, 300, 129], [3, 4, 2], 16, None),
     "decode-h128": ([130, 600], [1, 1], 128, None),
     "long-h16": ([5000, 3], [1, 1], 16, None),
+    # chunked prefill through the latent path: chunks of 64 and 96 new tokens
+    # (causal over their cached prefix) beside decodes
+    "prefill-chunks-h16": ([700, 96, 1200, 5], [64, 96, 1, 1], 16, None),
 }
 
 
