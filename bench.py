@@ -241,7 +241,8 @@ class Runner:
         w, u = self.w, self.u
         self.pa.attend_plan(u.block_tables, u.seq_lens, u.qsl, w.num_q_tokens,
                             w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_query_len,
-                            w.max_seq_len, u.workspace, common_prefix_len=self.cascade)
+                            w.max_seq_len, u.workspace, common_prefix_len=self.cascade,
+                            fp8=self.fp8 is not None)
 
     def merge(self):
         w, u = self.w, self.u

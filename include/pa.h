@@ -258,6 +258,24 @@ pa_status pa_attend_plan(const int32_t *block_tables,
                          void *workspace, size_t workspace_bytes,
                          void *stream);
 
+/*
+ * pa_attend_plan_fp8 - pa_attend_plan for attention over 8-bit pools
+ * (pa_attend_planned_fp8).  Same arguments, checks and errors.  A plain
+ * plan of either call is valid for either pool type; this one, for batches
+ * of decodes only (max_query_len at most 16 / (num_q_heads / num_kv_heads)),
+ * splits requests of up to 8192 keys into ranges of 384 keys instead of 512:
+ * 8-bit units read half the bytes, and the shorter ranges balance the launch
+ * better.  pa_attend_fp8 and pa_write_kv_plan_fp8 plan the same way.
+ */
+pa_status pa_attend_plan_fp8(const int32_t *block_tables,
+                             int32_t max_blocks_per_seq, const int32_t *seq_lens,
+                             const int32_t *query_start_loc, int32_t num_seqs,
+                             int64_t num_q_tokens, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim,
+                             int32_t max_query_len, int32_t max_seq_len,
+                             void *workspace, size_t workspace_bytes,
+                             void *stream);
+
 pa_status pa_attend_planned(const void *q, const void *k_cache,
                             const void *v_cache, int64_t num_blocks,
                             const int32_t *block_tables,

@@ -275,11 +275,12 @@ def attend_plan(block_tables: torch.Tensor, seq_lens: torch.Tensor,
                 num_q_heads: int, num_kv_heads: int, head_dim: int,
                 max_query_len: int, max_seq_len: int,
                 workspace: torch.Tensor,
-                common_prefix_len: Optional[int] = None) -> None:
+                common_prefix_len: Optional[int] = None, fp8: bool = False) -> None:
     """Enqueue only the work plan of pa_attend into ``workspace``; follow
     with attend(..., planned=True) for each layer that shares the metadata
     (with common_prefix_len: a shared-prefix plan, run by
-    attend(..., planned=True, common_prefix_len=...))."""
+    attend(..., planned=True, common_prefix_len=...); fp8=True: the plan
+    pa_attend_fp8 makes for 8-bit pools)."""
     B = _metadata_args(block_tables, seq_lens, query_start_loc)
     _need_cuda(workspace, "workspace")
     lib = _lib.load()
@@ -287,7 +288,7 @@ def attend_plan(block_tables: torch.Tensor, seq_lens: torch.Tensor,
             _ptr(query_start_loc), B, int(num_q_tokens), int(num_q_heads),
             int(num_kv_heads), int(head_dim), int(max_query_len), int(max_seq_len)]
     if common_prefix_len is None:
-        name = "pa_attend_plan"
+        name = "pa_attend_plan_fp8" if fp8 else "pa_attend_plan"
     else:
         name = "pa_attend_plan_cascade"
         args.append(int(common_prefix_len))

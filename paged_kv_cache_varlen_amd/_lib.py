@@ -30,6 +30,8 @@ SIGNATURES = {
                            I32, I32, F32, P, P, SZ, P]),
     "pa_attend_plan": (STATUS, [P, I32, P, P, I32, I64, I32, I32, I32, I32, I32,
                                 P, SZ, P]),
+    "pa_attend_plan_fp8": (STATUS, [P, I32, P, P, I32, I64, I32, I32, I32, I32, I32,
+                                    P, SZ, P]),
     "pa_attend_planned": (STATUS, [P, P, P, I64, P, I32, P, P, I32, I64, I32,
                                    I32, I32, I32, I32, F32, P, P, SZ, P]),
     "pa_attend_merge": (STATUS, [I32, I64, I32, I32, I32, I32, I32, P, P, SZ, P]),

@@ -93,6 +93,7 @@ struct AttendParams {
   int64_t max_pre_items;
   int64_t max_pre_partials;
   int32_t prefix_len;  // plan: keys every request shares (0: none)
+  int32_t split_decode;  // plan: key range of a decode split (requests <= kLongDecode)
 };
 
 // ---------------------------------------------------------------------------
@@ -160,7 +161,7 @@ __device__ SeqCounts seq_counts(const AttendParams& P, int b) {
     c.kind = kKindDecode;
     c.ntiles = 1;
     c.tq = Q;
-    c.splitlen = L - C > kLongDecode ? kSplitDecodeLong : kSplitDecode;
+    c.splitlen = L - C > kLongDecode ? kSplitDecodeLong : P.split_decode;
     const int ns = (L - C + c.splitlen - 1) / c.splitlen;
     const bool part = casc || ns > 1;
     c.items = ns;
@@ -1692,6 +1693,8 @@ AttendParams make_params(const AttendArgs& a) {
   P.max_pre_items = a.cascade ? a.ws.max_pre_items : 0;
   P.max_pre_partials = a.cascade ? a.ws.max_pre_partials : 0;
   P.prefix_len = a.cascade ? a.prefix_len : 0;
+  P.split_decode = (a.kv8 && !a.cascade && a.max_query_len <= decode_tile_tokens(P.G))
+                       ? kSplitDecode8 : kSplitDecode;
   return P;
 }
 

@@ -311,6 +311,29 @@ pa_status pa_attend_plan(const int32_t* block_tables, int32_t max_blocks_per_seq
   return ok();
 }
 
+pa_status pa_attend_plan_fp8(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* seq_lens, const int32_t* query_start_loc,
+                             int32_t num_seqs, int64_t num_q_tokens,
+                             int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t max_query_len,
+                             int32_t max_seq_len, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  pa::AttendArgs a;
+  bool empty;
+  pa_status s = prepare_attend(nullptr, nullptr, nullptr, 0, block_tables,
+                               max_blocks_per_seq, seq_lens, query_start_loc,
+                               num_seqs, num_q_tokens, num_q_heads, num_kv_heads,
+                               head_dim, max_query_len, max_seq_len, 0.0f,
+                               nullptr, workspace, workspace_bytes, false, &a,
+                               &empty);
+  if (s != PA_OK) return s;
+  if (empty) return ok();
+  a.kv8 = true;  // the plan's key ranges only; no scales are involved
+  hipError_t e = pa::launch_plan(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pa_attend_plan_fp8 launch");
+  return ok();
+}
+
 pa_status pa_attend_planned(const void* q, const void* k_cache,
                             const void* v_cache, int64_t num_blocks,
                             const int32_t* block_tables,

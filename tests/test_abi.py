@@ -156,6 +156,14 @@ def test_write_kv_plan_fp8_argument_checks(lib, args, status):
     assert lib.pa_write_kv_plan_fp8(*args) == status
 
 
+def test_attend_plan_fp8_argument_checks(lib):
+    ws = lib.pa_attend_workspace_size(2, 8, 4, 2, 128, 4, 60)
+    args = (FAKE, 4, FAKE, FAKE, 2, 8, 4, 2, 128, 4, 60, FAKE)
+    assert lib.pa_attend_plan_fp8(*args, ws - 1, None) == _lib.PA_ERR_WORKSPACE
+    assert lib.pa_attend_plan_fp8(None, *args[1:], ws, None) == _lib.PA_ERR_NULL
+    assert lib.pa_attend_plan_fp8(*args[:8], 96, *args[9:], ws, None) == _lib.PA_ERR_UNSUPPORTED
+
+
 def test_write_kv_plan_workspace_sizes(lib):
     # a plain plan needs the plain workspace, a shared-prefix plan the larger one
     plain = lib.pa_attend_workspace_size(2, 8, 4, 2, 128, 4, 60)

@@ -110,14 +110,14 @@ from tests.test_gpu_parity import check_close, sample_rows, to64  # noqa: E402
 from tests.gpu_util import i32, tensor_bits  # noqa: E402
 
 
-def attend8(w, kc, vc, ks, vs, planned=False):
+def attend8(w, kc, vc, ks, vs, planned=False, fp8_plan=True):
     bt, sl, qsl = i32(w.block_tables), i32(w.seq_lens), i32(w.query_start_loc)
     q = bf16_tensor(w.q)
     ws = pa.alloc_workspace(w.num_seqs, w.num_q_tokens, w.num_q_heads, w.num_kv_heads,
                             w.head_dim, w.max_query_len, w.max_seq_len)
     if planned:
         pa.attend_plan(bt, sl, qsl, w.num_q_tokens, w.num_q_heads, w.num_kv_heads,
-                       w.head_dim, w.max_query_len, w.max_seq_len, ws)
+                       w.head_dim, w.max_query_len, w.max_seq_len, ws, fp8=fp8_plan)
     out = pa.attend(q, kc, vc, bt, sl, qsl, w.scale, w.max_query_len, w.max_seq_len,
                     num_kv_heads=w.num_kv_heads, workspace=ws, planned=planned,
                     k_scale=ks, v_scale=vs)
@@ -192,3 +192,22 @@ def test_config_parity_fp8(k):
     ref = oracle.attend_fp8(w.q, okc, ovc, ks, vs, w.block_tables, w.seq_lens,
                             w.query_start_loc, w.num_kv_heads, w.scale, rows=rows)
     check_close(got[rows[:, 0], rows[:, 1]], ref, "config %d fp8 (%d rows)" % (k, len(rows)))
+
+
+@pytest.mark.parametrize("k", [2])
+def test_plain_plan_serves_8bit_pools(k):
+    # decode-only batches over 8-bit pools are planned with 384-key ranges;
+    # the bf16 plan (512-key ranges) is valid too: both within the tolerance
+    # of the oracle on the same codes
+    w = W.make_config(k)
+    scales = (0.011, 0.0107)
+    kc, vc = gpu_pool8(w, *scales)
+    a = attend8(w, kc, vc, *scales, planned=True, fp8_plan=False)
+    b = attend8(w, kc, vc, *scales, planned=True, fp8_plan=True)
+    assert not np.array_equal(a, b)  # other splits, other rounding
+    okc, ovc = oracle_pool8(w, *scales)
+    rows = sample_rows(w, 192, seed=3)
+    ref = oracle.attend_fp8(w.q, okc, ovc, *scales, w.block_tables, w.seq_lens,
+                            w.query_start_loc, w.num_kv_heads, w.scale, rows=rows)
+    for bits, what in ((a, "bf16 plan"), (b, "8-bit plan")):
+        check_close(bits[rows[:, 0], rows[:, 1]], ref, what)
