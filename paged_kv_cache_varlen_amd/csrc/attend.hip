@@ -117,6 +117,8 @@ __device__ __forceinline__ uint32_t plan_signature(const AttendParams& P) {
 constexpr int kPlanThreads = 1024;
 static_assert(kSplitDecodeLong / kBlock <= 64, "a decode unit's block ids fit one wave");
 constexpr int kMaxCoop = 64;  // unsplit prefill requests emitted by all threads
+constexpr int kLastBuckets = 16;    // queue order of the decode requests' last splits:
+constexpr int kLastBucketKeys = 64; // by length, 64-key buckets, longest first
 
 struct SeqCounts {
   int kind;         // -1: nothing to do
@@ -320,6 +322,7 @@ __device__ void plan_body(const AttendParams& P) {
   __shared__ int coop_n;
   __shared__ int coop_b[kMaxCoop];
   __shared__ int coop_base[kMaxCoop];
+  __shared__ int last_cnt[kLastBuckets];
   const int tid = threadIdx.x;
   if (tid < kDecodeShards) P.dec_counters[tid * kCounterStride] = 0;
   if (tid == 0) {
@@ -355,9 +358,34 @@ __device__ void plan_body(const AttendParams& P) {
     const int4 e = block_scan4(scan_lanes(c), lds, &total);
     const int4 e2 = block_scan4(make_int4(c.kind == kKindDecode, 0, 0, 0), lds, &total2);
     fits = total.x + total.y + total2.x <= P.max_items && total.z <= P.max_partials;
+    // The decode requests' last splits (1 .. split keys each) go last in the
+    // queue, longest first (16 buckets of 64 keys, any order within one), so
+    // that the launch ends on its shortest units.  Where a unit sits in the
+    // queue does not change what it computes.
+    if (tid < kLastBuckets) last_cnt[tid] = 0;
+    __syncthreads();
+    int bk = 0, rank = 0;
+    if (c.kind == kKindDecode) {
+      const int own = P.seq_lens[b] - P.prefix_len;
+      const int rem = own - (c.items - 1) * c.splitlen;  // keys of the last split
+      bk = min(kLastBuckets - 1, max(0, (kLastBucketKeys * kLastBuckets - rem) / kLastBucketKeys));
+      rank = atomicAdd(&last_cnt[bk], 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int acc = 0;
+      for (int i = 0; i < kLastBuckets; ++i) {
+        const int n = last_cnt[i];
+        last_cnt[i] = acc;
+        acc += n;
+      }
+    }
+    __syncthreads();
     if (fits && c.kind >= 0)
       place_seq(P, b, c, c.kind == kKindPrefill ? e.x : total.x + e.y,
-                total.x + total.y + e2.x, e.z, e.w, &coop_n, coop_b, coop_base);
+                total.x + total.y + last_cnt[bk] + rank, e.z, e.w, &coop_n, coop_b,
+                coop_base);
+    (void)e2;
   } else {
     // two sweeps over chunks of requests: totals first, then placement
     total = make_int4(0, 0, 0, 0);
