@@ -192,6 +192,14 @@ __device__ SeqCounts seq_counts(const AttendParams& P, int b) {
   return c;
 }
 
+// Queue bucket of a decode request's last split: longest first, 64 keys a
+// bucket.
+__device__ __forceinline__ int last_bucket(const AttendParams& P, int b, const SeqCounts& c) {
+  const int own = P.seq_lens[b] - P.prefix_len;
+  const int rem = own - (c.items - 1) * c.splitlen;  // keys of the last split
+  return min(kLastBuckets - 1, max(0, (kLastBucketKeys * kLastBuckets - rem) / kLastBucketKeys));
+}
+
 // Four exclusive scans at once (one set of barriers); tot receives the sums.
 __device__ int4 block_scan4(int4 x, int4* lds, int4* tot) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -366,9 +374,7 @@ __device__ void plan_body(const AttendParams& P) {
     __syncthreads();
     int bk = 0, rank = 0;
     if (c.kind == kKindDecode) {
-      const int own = P.seq_lens[b] - P.prefix_len;
-      const int rem = own - (c.items - 1) * c.splitlen;  // keys of the last split
-      bk = min(kLastBuckets - 1, max(0, (kLastBucketKeys * kLastBuckets - rem) / kLastBucketKeys));
+      bk = last_bucket(P, b, c);
       rank = atomicAdd(&last_cnt[bk], 1);
     }
     __syncthreads();
@@ -387,13 +393,17 @@ __device__ void plan_body(const AttendParams& P) {
                 coop_base);
     (void)e2;
   } else {
-    // two sweeps over chunks of requests: totals first, then placement
+    // two sweeps over chunks of requests: totals (and the last splits'
+    // bucket counts) first, then placement
     total = make_int4(0, 0, 0, 0);
     total2 = make_int4(0, 0, 0, 0);
+    if (tid < kLastBuckets) last_cnt[tid] = 0;
+    __syncthreads();
     for (int base = 0; base < P.num_seqs; base += kPlanThreads) {
       const int b = base + tid;
       SeqCounts c{-1, 0, 0, 0, 0, 0, 0};
       if (b < P.num_seqs) c = seq_counts(P, b);
+      if (c.kind == kKindDecode) atomicAdd(&last_cnt[last_bucket(P, b, c)], 1);
       int4 t, t2;
       block_scan4(scan_lanes(c), lds, &t);
       block_scan4(make_int4(c.kind == kKindDecode, 0, 0, 0), lds, &t2);
@@ -404,25 +414,34 @@ __device__ void plan_body(const AttendParams& P) {
       total2.x += t2.x;
     }
     fits = total.x + total.y + total2.x <= P.max_items && total.z <= P.max_partials;
+    __syncthreads();
+    if (tid == 0) {  // bucket counts -> first slot of each bucket
+      int acc = 0;
+      for (int i = 0; i < kLastBuckets; ++i) {
+        const int n = last_cnt[i];
+        last_cnt[i] = acc;
+        acc += n;
+      }
+    }
+    __syncthreads();
     int4 carry = make_int4(0, 0, 0, 0);
-    int carry_last = 0;
     for (int base = 0; base < P.num_seqs; base += kPlanThreads) {
       const int b = base + tid;
       SeqCounts c{-1, 0, 0, 0, 0, 0, 0};
       if (b < P.num_seqs) c = seq_counts(P, b);
-      int4 t, t2;
+      int4 t;
       const int4 e = block_scan4(scan_lanes(c), lds, &t);
-      const int4 e2 = block_scan4(make_int4(c.kind == kKindDecode, 0, 0, 0), lds, &t2);
+      // next free slot of the request's bucket (any order within a bucket)
+      const int last = c.kind == kKindDecode ? atomicAdd(&last_cnt[last_bucket(P, b, c)], 1) : 0;
       if (fits && c.kind >= 0)
         place_seq(P, b, c,
                   c.kind == kKindPrefill ? carry.x + e.x : total.x + carry.y + e.y,
-                  total.x + total.y + carry_last + e2.x, carry.z + e.z,
+                  total.x + total.y + last, carry.z + e.z,
                   carry.w + e.w, &coop_n, coop_b, coop_base);
       carry.x += t.x;
       carry.y += t.y;
       carry.z += t.z;
       carry.w += t.w;
-      carry_last += t2.x;
     }
   }
   __syncthreads();
