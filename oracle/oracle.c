@@ -182,11 +182,14 @@ size_t oracle_v_index(int64_t n, int64_t g, int64_t t, int64_t d, int64_t Hkv,
 void oracle_write_kv(uint16_t *k_cache, uint16_t *v_cache, const uint16_t *k,
                      const uint16_t *v, const int64_t *slot_mapping,
                      int64_t num_tokens, int64_t Hkv, int64_t bs, int64_t D) {
-  for (int64_t t = 0; t < num_tokens; ++t) {
-    int64_t s = slot_mapping[t];
-    if (s < 0) continue;
-    int64_t n = s / bs, off = s % bs;
-    for (int64_t g = 0; g < Hkv; ++g) {
+  /* kv heads write disjoint tiles, so they run in parallel; within a head the
+   * tokens are applied in order (a repeated slot keeps the last token). */
+#pragma omp parallel for schedule(static)
+  for (int64_t g = 0; g < Hkv; ++g) {
+    for (int64_t t = 0; t < num_tokens; ++t) {
+      int64_t s = slot_mapping[t];
+      if (s < 0) continue;
+      int64_t n = s / bs, off = s % bs;
       for (int64_t d = 0; d < D; ++d) {
         size_t src = (size_t)((t * Hkv + g) * D + d);
         k_cache[k_index(n, g, off, d, Hkv, bs, D)] = k[src];
@@ -203,11 +206,13 @@ void oracle_write_kv_fp8(uint8_t *k_cache, uint8_t *v_cache, const uint16_t *k,
                          const uint16_t *v, const int64_t *slot_mapping,
                          int64_t num_tokens, int64_t Hkv, int64_t bs, int64_t D,
                          float k_scale, float v_scale) {
-  for (int64_t t = 0; t < num_tokens; ++t) {
-    int64_t s = slot_mapping[t];
-    if (s < 0) continue;
-    int64_t n = s / bs, off = s % bs;
-    for (int64_t g = 0; g < Hkv; ++g) {
+  /* kv heads in parallel, tokens in order within a head (as above) */
+#pragma omp parallel for schedule(static)
+  for (int64_t g = 0; g < Hkv; ++g) {
+    for (int64_t t = 0; t < num_tokens; ++t) {
+      int64_t s = slot_mapping[t];
+      if (s < 0) continue;
+      int64_t n = s / bs, off = s % bs;
       for (int64_t d = 0; d < D; ++d) {
         size_t src = (size_t)((t * Hkv + g) * D + d);
         float kx = (float)bf16_to_double(k[src]);

@@ -12,6 +12,7 @@ import torch
 import oracle
 import paged_kv_cache_varlen_amd as pa
 import workloads as W
+from tests import configs
 from tests.gpu_util import bf16_tensor, i64
 from tests.test_gpu_parity import SMALL, small
 
@@ -172,42 +173,80 @@ def test_attend_fp8_block_permutation_is_bit_identical():
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("k", [1, 2, 3, 5])
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
 def test_config_parity_fp8(k):
-    w = W.make_config(k)
-    ks, vs = 0.011, 0.0107
+    # full size: every pool byte against the oracle's 8-bit scatter and every
+    # output row against the oracle's attention over the same codes
+    w = configs.workload(k)
+    ks, vs = configs.FP8_SCALES
     kc, vc = gpu_pool8(w, ks, vs)
     got = attend8(w, kc, vc, ks, vs)
-    assert np.isfinite(to64(got)).all()
-    okc, ovc = oracle_pool8(w, ks, vs)
-    if k <= 2:
-        assert np.array_equal(u8_bits(kc), okc)
-        assert np.array_equal(u8_bits(vc), ovc)
-    if k == 1:
-        ref = oracle.attend_fp8(w.q, okc, ovc, ks, vs, w.block_tables, w.seq_lens,
-                                w.query_start_loc, w.num_kv_heads, w.scale)
-        check_close(got, ref, "config 1 fp8")
-        return
-    rows = sample_rows(w, {2: 192, 3: 192, 5: 64}[k], seed=200 + k)
-    ref = oracle.attend_fp8(w.q, okc, ovc, ks, vs, w.block_tables, w.seq_lens,
-                            w.query_start_loc, w.num_kv_heads, w.scale, rows=rows)
-    check_close(got[rows[:, 0], rows[:, 1]], ref, "config %d fp8 (%d rows)" % (k, len(rows)))
+    okc, ovc = configs.pool8(k)
+    assert np.array_equal(u8_bits(kc), okc)
+    assert np.array_equal(u8_bits(vc), ovc)
+    del kc, vc
+    torch.cuda.empty_cache()
+    check_close(got, configs.attend8(k), "config %d fp8 (all %d rows)" % (k, got.shape[0] * got.shape[1]))
 
 
 @pytest.mark.parametrize("k", [2])
 def test_plain_plan_serves_8bit_pools(k):
     # decode-only batches over 8-bit pools are planned with 384-key ranges;
     # the bf16 plan (512-key ranges) is valid too: both within the tolerance
-    # of the oracle on the same codes
-    w = W.make_config(k)
-    scales = (0.011, 0.0107)
+    # of the oracle on the same codes, every output row
+    w = configs.workload(k)
+    scales = configs.FP8_SCALES
     kc, vc = gpu_pool8(w, *scales)
     a = attend8(w, kc, vc, *scales, planned=True, fp8_plan=False)
     b = attend8(w, kc, vc, *scales, planned=True, fp8_plan=True)
     assert not np.array_equal(a, b)  # other splits, other rounding
-    okc, ovc = oracle_pool8(w, *scales)
-    rows = sample_rows(w, 192, seed=3)
-    ref = oracle.attend_fp8(w.q, okc, ovc, *scales, w.block_tables, w.seq_lens,
-                            w.query_start_loc, w.num_kv_heads, w.scale, rows=rows)
+    ref = configs.attend8(k)
     for bits, what in ((a, "bf16 plan"), (b, "8-bit plan")):
-        check_close(bits[rows[:, 0], rows[:, 1]], ref, what)
+        check_close(bits, ref, what)
+
+
+# ---- 8-bit decode-only plans (384-key ranges) ---------------------------------------
+
+DEC8 = {
+    # name: (seq_lens, query_lens, Hq, Hkv, D); max_query_len <= 16 / G, so
+    # these are planned with the 8-bit plan's 384-key decode ranges
+    "dec8-g4-edges": ([383, 384, 385, 767, 768, 769, 1151, 1152, 1153, 8191, 8192,
+                       8193, 9000, 1, 2, 31, 32, 33], [1] * 18, 32, 8, 128),
+    "dec8-g4-q4": ([4, 5, 384, 388, 770, 1155, 2000, 8192, 8196, 7],
+                   [4, 1, 4, 3, 2, 4, 1, 4, 2, 4], 32, 8, 128),
+    "dec8-g1-q16-d64": ([16, 400, 769, 1536, 8190, 8200, 20],
+                        [16, 16, 9, 1, 16, 5, 13], 4, 4, 64),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DEC8))
+def test_attend_fp8_decode_plan(name):
+    L, Q, Hq, Hkv, D = DEC8[name]
+    w = W.make_workload(name, L, Q, Hq, Hkv, D, seed=31)
+    scales = (0.02, 0.017)
+    kc, vc = gpu_pool8(w, *scales)
+    a = attend8(w, kc, vc, *scales)
+    b = attend8(w, kc, vc, *scales, planned=True)
+    assert np.array_equal(a, b)
+    okc, ovc = oracle_pool8(w, *scales)
+    ref = oracle.attend_fp8(w.q, okc, ovc, *scales, w.block_tables, w.seq_lens,
+                            w.query_start_loc, w.num_kv_heads, w.scale)
+    check_close(a, ref, name)
+
+
+def test_attend_fp8_decode_plan_many_requests():
+    # more requests than the plan's workgroup has threads: the two-sweep plan
+    # with its bucketed last splits, every output row
+    rng = np.random.default_rng(32)
+    B = 1100
+    L = rng.integers(1, 2400, size=B)
+    Q = np.minimum(L, rng.integers(1, 3, size=B))
+    w = W.make_workload("dec8-many", L, Q, 16, 2, 128, seed=33)
+    scales = (0.011, 0.0107)
+    kc, vc = gpu_pool8(w, *scales)
+    got = attend8(w, kc, vc, *scales, planned=True)
+    okc, ovc = oracle_pool8(w, *scales)
+    ref = oracle.attend_fp8(w.q, okc, ovc, *scales, w.block_tables, w.seq_lens,
+                            w.query_start_loc, w.num_kv_heads, w.scale)
+    check_close(got, ref, "1100 requests fp8")

@@ -12,6 +12,7 @@ import torch
 import oracle
 import paged_kv_cache_varlen_amd as pa
 import workloads as W
+from tests import configs
 from tests.gpu_util import Uploaded, bf16_tensor, i32, i64, tensor_bits
 
 pytestmark = pytest.mark.gpu
@@ -351,10 +352,9 @@ def test_many_requests_two_sweep_plan():
     w = W.make_workload("many", L, Q, 8, 2, 64, seed=21)
     out = tensor_bits(Uploaded(w).attend())
     kc, vc = oracle_pool(w)
-    rows = sample_rows(w, 400, seed=22)
-    ref = oracle.attend_rows(w.q, kc, vc, w.block_tables, w.seq_lens,
-                             w.query_start_loc, w.num_kv_heads, w.scale, rows)
-    check_close(out[rows[:, 0], rows[:, 1]], ref, "1500 requests")
+    ref = oracle.attend(w.q, kc, vc, w.block_tables, w.seq_lens, w.query_start_loc,
+                        w.num_kv_heads, w.scale)
+    check_close(out, ref, "1500 requests (all rows)")
 
 
 def test_many_unsplit_prefills():
@@ -375,32 +375,24 @@ def test_many_unsplit_prefills():
 
 # ---- the five synthetic configurations ---------------------------------------------
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
 def test_config_parity(k):
-    w = W.make_config(k)
+    # full size: every pool element bit-exact against the oracle's scatter
+    # (cached tokens and this step's new tokens; NaN wherever nothing was
+    # written) and every output row within tolerance of the oracle
+    w = configs.workload(k)
     u = Uploaded(w)
     out = u.attend()
     torch.cuda.synchronize()
     got = tensor_bits(out)
-    assert np.isfinite(to64(got)).all()
-    if k <= 2:
-        # pool bit-exact against the oracle's scatter
-        kc, vc = oracle_pool(w)
-        assert np.array_equal(tensor_bits(u.k_cache).ravel(), kc)
-        assert np.array_equal(tensor_bits(u.v_cache).ravel(), vc)
-    else:
-        kc, vc = oracle_pool(w)
-    if k == 1:
-        ref = oracle.attend(w.q, kc, vc, w.block_tables, w.seq_lens,
-                            w.query_start_loc, w.num_kv_heads, w.scale)
-        check_close(got, ref, "config 1")
-        return
-    rows = sample_rows(w, {2: 256, 3: 256, 4: 256, 5: 96}[k], seed=100 + k)
-    ref = oracle.attend_rows(w.q, kc, vc, w.block_tables, w.seq_lens,
-                             w.query_start_loc, w.num_kv_heads, w.scale, rows)
-    check_close(got[rows[:, 0], rows[:, 1]], ref, "config %d (%d rows)" % (k, len(rows)))
+    kc, vc = configs.pool(k)
+    assert np.array_equal(tensor_bits(u.k_cache).ravel(), kc)
+    assert np.array_equal(tensor_bits(u.v_cache).ravel(), vc)
+    del u
+    torch.cuda.empty_cache()
+    check_close(got, configs.attend(k), "config %d (all %d rows)" % (k, got.shape[0] * got.shape[1]))
     if k == 4:
-        del u
-        wu = W.make_config(4, shared=False)
+        wu = configs.workload(4, shared=False)
         gu = tensor_bits(Uploaded(wu).attend())
         assert np.array_equal(got, gu)

@@ -13,6 +13,7 @@ import torch
 
 import oracle
 import paged_kv_cache_varlen_amd as pa
+import workloads as W
 from tests.gpu_util import Uploaded, bf16_tensor, i32, i64, tensor_bits
 from tests.test_gpu_cascade import casc, cascade_ws, oracle_ref, run_cascade
 from tests.test_gpu_fp8 import attend8, gpu_pool8, oracle_pool8, u8_bits
@@ -142,3 +143,56 @@ def test_binding_rejects_metadata_of_other_types():
         pa.attend_plan(u.block_tables.to(torch.int64), u.seq_lens, u.qsl, w.num_q_tokens,
                        w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_query_len,
                        w.max_seq_len, u.workspace)
+
+
+# ---- the plan's work list, read back ------------------------------------------------
+
+# Internal workspace layout of a plain plan: the plan header at byte 0 (num_work,
+# num_items, error, ... as uint32), then 8 decode-queue counters 4 KiB apart
+# from byte 4096, then the work items (16 int32 each: seq, tok0, ntok, kind, kv0,
+# kv1, split, nsplit, pbase, counter, posbase, pad) from byte 4096 + 32 KiB.
+ITEMS_OFFSET = 4096 + 8 * 4096
+
+
+@pytest.mark.parametrize("B,fp8", [(700, False), (700, True), (1500, False), (1500, True)])
+def test_plan_items_partition_every_request(B, fp8):
+    # one sweep (<= 1024 requests) and two sweeps, bf16 and 8-bit plans: every
+    # slot in [0, num_items) holds exactly one valid item (the workspace is
+    # filled with 0xff first, so a slot left unwritten is seen), and the items
+    # of each request cover its keys 0 .. L-1 once, in ranges of the plan's
+    # split length
+    rng = np.random.default_rng(40 + B)
+    L = rng.integers(1, 9500, size=B)
+    Q = np.minimum(L, rng.integers(1, 3, size=B))
+    w = W.make_workload("plan-%d" % B, L, Q, 16, 2, 64, seed=41)
+    bt, sl, qsl = i32(w.block_tables), i32(w.seq_lens), i32(w.query_start_loc)
+    ws = pa.alloc_workspace(w.num_seqs, w.num_q_tokens, w.num_q_heads, w.num_kv_heads,
+                            w.head_dim, w.max_query_len, w.max_seq_len)
+    ws.fill_(0xFF)
+    pa.attend_plan(bt, sl, qsl, w.num_q_tokens, w.num_q_heads, w.num_kv_heads,
+                   w.head_dim, w.max_query_len, w.max_seq_len, ws, fp8=fp8)
+    torch.cuda.synchronize()
+    raw = ws.cpu().numpy()
+    hdr = raw[:64].view(np.uint32)
+    num_work, num_items, err = int(hdr[0]), int(hdr[1]), int(hdr[2])
+    assert err == 0
+    assert num_work == num_items * w.num_kv_heads
+    items = raw[ITEMS_OFFSET:ITEMS_OFFSET + 64 * num_items].view(np.int32).reshape(-1, 16)
+    seq, tok0, ntok, kind, kv0, kv1, split, nsplit = (items[:, i] for i in range(8))
+    assert np.all((seq >= 0) & (seq < B)), "unwritten or foreign slot"
+    assert np.all(kind == 0) and np.all(kv1 > kv0)
+    qs = w.query_start_loc
+    assert np.array_equal(tok0, qs[seq]) and np.array_equal(ntok, Q[seq])
+    order = np.lexsort((kv0, seq))
+    seq, kv0, kv1, split, nsplit = seq[order], kv0[order], kv1[order], split[order], nsplit[order]
+    counts = np.bincount(seq, minlength=B)
+    assert np.array_equal(counts, nsplit[np.searchsorted(seq, np.arange(B))])
+    first = np.searchsorted(seq, np.arange(B))
+    for b in range(B):
+        s0 = first[b]
+        r0, r1 = kv0[s0:s0 + counts[b]], kv1[s0:s0 + counts[b]]
+        assert r0[0] == 0 and r1[-1] == L[b]
+        assert np.array_equal(r0[1:], r1[:-1]), b
+        assert np.array_equal(split[s0:s0 + counts[b]], np.arange(counts[b]))
+        span = 1024 if L[b] > 8192 else (384 if fp8 else 512)
+        assert np.all(r1[:-1] - r0[:-1] == span), b
