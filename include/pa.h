@@ -230,6 +230,40 @@ pa_status pa_attend(const void *q, const void *k_cache, const void *v_cache,
                     void *stream);
 
 /*
+ * pa_attend_noalloc - pa_attend for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments, results and errors as pa_attend,
+ * without the workspace.  Its work plan and split-K partials live in a
+ * static device array of PA_NOALLOC_SCRATCH_BYTES (64 MiB) inside the
+ * library, one per device, allocated with the library's code when it is
+ * loaded on the device and held until the process ends.  The call allocates
+ * and frees nothing.
+ *
+ * Limit: batches whose pa_attend_workspace_size(...) exceeds
+ * PA_NOALLOC_SCRATCH_BYTES are rejected with PA_ERR_WORKSPACE before
+ * anything is enqueued (e.g. 64 decodes of up to 4096 tokens with 32 q heads
+ * of 128 dims need 11.3 MiB; 16 x 32768-token decodes with 64 q heads, 44 MiB;
+ * a 2048-token mixed step, more than the limit: use pa_attend there).
+ *
+ * Every call on a device shares that device's array, and the array keeps
+ * the last call's plan and partials: calls that overlap in time on one
+ * device (several streams, several host threads) race and give undefined
+ * outputs; order them on one stream.  Nothing in the array needs to start
+ * at zero: each call's plan kernel writes the header and queue counters its
+ * attention kernel reads.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (((size_t)64) << 20)
+
+pa_status pa_attend_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                            int64_t num_blocks, const int32_t *block_tables,
+                            int32_t max_blocks_per_seq, const int32_t *seq_lens,
+                            const int32_t *query_start_loc, int32_t num_seqs,
+                            int64_t num_q_tokens, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim,
+                            int32_t max_query_len, int32_t max_seq_len, float scale,
+                            void *out, void *stream);
+
+/*
  * pa_attend_plan, pa_attend_planned, pa_attend_merge - pa_attend in three
  * calls, so that one plan serves every layer of a forward step (the metadata
  * is the same for all layers; "vLLM v1 Deep Dive", Step 4c: the runner builds

@@ -28,6 +28,8 @@ SIGNATURES = {
     "pa_attend_workspace_size": (SZ, [I32, I64, I32, I32, I32, I32, I32]),
     "pa_attend": (STATUS, [P, P, P, I64, P, I32, P, P, I32, I64, I32, I32, I32,
                            I32, I32, F32, P, P, SZ, P]),
+    "pa_attend_noalloc": (STATUS, [P, P, P, I64, P, I32, P, P, I32, I64, I32, I32,
+                                   I32, I32, I32, F32, P, P]),
     "pa_attend_plan": (STATUS, [P, I32, P, P, I32, I64, I32, I32, I32, I32, I32,
                                 P, SZ, P]),
     "pa_attend_plan_fp8": (STATUS, [P, I32, P, P, I32, I64, I32, I32, I32, I32, I32,

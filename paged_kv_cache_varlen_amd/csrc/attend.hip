@@ -1813,6 +1813,32 @@ hipError_t launch_planned(const AttendArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// The workspace of pa_attend_noalloc: a file-scope device array, one copy per
+// device, allocated with the code object when it is loaded on that device.
+// In host code its name stands for a host-side placeholder, not a device
+// address: scratch_address() looks up the current device's copy, and only
+// that address is ever handed to a kernel.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+hipError_t scratch_address(void** ptr) {
+  static std::mutex mu;
+  static std::vector<void*> cache;  // [device]
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)cache.size() <= dev) cache.resize(dev + 1, nullptr);
+  if (cache[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr || ((uintptr_t)p & 255)) return hipErrorInvalidSymbol;
+    cache[dev] = p;
+  }
+  *ptr = cache[dev];
+  return hipSuccess;
+}
+
 hipError_t launch_merge(const AttendArgs& a, hipStream_t stream) {
   if (a.num_q_tokens == 0 || a.num_seqs == 0) return hipSuccess;
   const AttendParams P = make_params(a);

@@ -407,6 +407,53 @@ pa_status pa_attend(const void* q, const void* k_cache, const void* v_cache,
   return ok();
 }
 
+static_assert(PA_NOALLOC_SCRATCH_BYTES == pa::kStaticScratchBytes,
+              "pa.h states the static scratch size");
+
+pa_status pa_attend_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                            int64_t num_blocks, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                            const int32_t* query_start_loc, int32_t num_seqs,
+                            int64_t num_q_tokens, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim,
+                            int32_t max_query_len, int32_t max_seq_len, float scale,
+                            void* out, void* stream) {
+  // sizes first: a batch whose workspace exceeds the static scratch is
+  // rejected before any device call (invalid sizes fall through to the
+  // checks of prepare_attend, which report them)
+  const size_t need = pa_attend_workspace_size(num_seqs, num_q_tokens, num_q_heads,
+                                               num_kv_heads, head_dim, max_query_len,
+                                               max_seq_len);
+  if (need > pa::kStaticScratchBytes)
+    return fail(PA_ERR_WORKSPACE,
+                "pa_attend_noalloc: these sizes need " + std::to_string(need) +
+                    " bytes of workspace; the static scratch holds " +
+                    std::to_string(pa::kStaticScratchBytes) +
+                    " (call pa_attend with a workspace instead)");
+  // every argument check of pa_attend, against a workspace of the scratch's
+  // size; the scratch's device address is bound once they have passed (the
+  // placeholder is never dereferenced)
+  pa::AttendArgs a;
+  bool empty;
+  void* const placeholder = reinterpret_cast<void*>(uintptr_t(256));
+  pa_status s = prepare_attend(q, k_cache, v_cache, num_blocks, block_tables,
+                               max_blocks_per_seq, seq_lens, query_start_loc,
+                               num_seqs, num_q_tokens, num_q_heads, num_kv_heads,
+                               head_dim, max_query_len, max_seq_len, scale, out,
+                               placeholder, pa::kStaticScratchBytes, true, &a, &empty);
+  if (s != PA_OK) return s;
+  if (empty) return ok();
+  void* ws = nullptr;
+  hipError_t e = pa::scratch_address(&ws);
+  if (e != hipSuccess) return hip_fail(e, "pa_attend_noalloc scratch lookup");
+  a.workspace = ws;
+  e = pa::launch_plan(a, static_cast<hipStream_t>(stream));
+  if (e == hipSuccess) e = pa::launch_planned(a, static_cast<hipStream_t>(stream));
+  if (e == hipSuccess) e = pa::launch_merge(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pa_attend_noalloc launch");
+  return ok();
+}
+
 pa_status pa_attend_planned_fp8(const void* q, const void* k_cache,
                                 const void* v_cache, int64_t num_blocks,
                                 const int32_t* block_tables,

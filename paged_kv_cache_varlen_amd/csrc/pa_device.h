@@ -315,6 +315,13 @@ hipError_t launch_write_plan(const AttendArgs& a, const ScatterArgs& s,
                              hipStream_t stream);
 // Attention over the plan in the workspace (one persistent kernel).
 hipError_t launch_planned(const AttendArgs& a, hipStream_t stream);
+
+// Bytes of the static device scratch that serves as pa_attend_noalloc's
+// workspace (one array per device, held until the process ends).
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+// Device address of the current device's scratch array (looked up once per
+// device with hipGetSymbolAddress, then cached).
+hipError_t scratch_address(void** ptr);
 // Split-K merge of the partials the attention kernel left in the workspace.
 hipError_t launch_merge(const AttendArgs& a, hipStream_t stream);
 

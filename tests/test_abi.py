@@ -89,6 +89,34 @@ def test_attend_rejects_bad_arguments(lib, over, status):
     assert lib.pa_last_error() != b""
 
 
+def noalloc_args(**over):
+    a = attend_args(**over)
+    return a[:17] + a[19:]  # no workspace arguments
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), _lib.PA_ERR_NULL),
+    (dict(D=96), _lib.PA_ERR_UNSUPPORTED),
+    (dict(Hq=6, Hkv=4), _lib.PA_ERR_SHAPE),
+    (dict(scale=0.0), _lib.PA_ERR_SHAPE),
+    (dict(q=FAKE + 2), _lib.PA_ERR_SHAPE),
+    # bounds whose workspace exceeds the static scratch (64 MiB)
+    (dict(B=129, T=2048, Hq=32, Hkv=8, mq=1920, ms=8192, mb=512), _lib.PA_ERR_WORKSPACE),
+])
+def test_attend_noalloc_rejects_bad_arguments(lib, over, status):
+    # host checks only: every one of these returns before any device call
+    assert lib.pa_attend_noalloc(*noalloc_args(**over)) == status
+    assert lib.pa_last_error() != b""
+
+
+def test_attend_noalloc_scratch_limit(lib):
+    # the documented examples: decode batches that fit, a mixed step that does not
+    limit = 64 << 20
+    assert lib.pa_attend_workspace_size(64, 64, 32, 8, 128, 1, 4096) <= limit
+    assert lib.pa_attend_workspace_size(16, 16, 64, 8, 128, 1, 32768) <= limit
+    assert lib.pa_attend_workspace_size(129, 2048, 32, 8, 128, 1920, 8192) > limit
+
+
 def test_attend_empty_batch_is_ok(lib):
     assert lib.pa_attend(*attend_args(T=0, q=None, out=None)) == _lib.PA_OK
 
