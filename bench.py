@@ -4,16 +4,17 @@
 A step is the whole hot path for one layer over one batch: the scatter of
 the step's new K/V rows and the work plan in one launch (pa_write_kv_plan),
 then unified varlen paged attention and the split-K merge over every query
-row.  Inputs are seeded synthetic
-tensors already resident in HBM.  Several copies of the KV pool (one per
-simulated layer, >= 2 GiB in total) are cycled so that no step reads K/V left
-in the caches by the previous one.
+row.  Inputs are seeded synthetic tensors already resident in HBM.  Several
+copies of the KV pool (one per simulated layer, >= 2 GiB in total) are
+cycled so that no step reads K/V left in the caches by the previous one.
 
 Prints one JSON line:
-  value    paged-attention KV read GB/s of the headline workload (Llama-3-8B
-           decode layer: 64 sequences, contexts U[128, 4096], 32 q / 8 kv
-           heads, head_dim 128, 16-token blocks) = valid-token K+V bytes per
-           step / step time;
+  value    paged-attention KV read GB/s of the headline workload (70B-class
+           long-context decode layer: 16 requests x 32768 tokens, 64 q / 8 kv
+           heads, head_dim 128, 16-token blocks, a 2.1 GB pool, plus the
+           scatter of the step's 16 new tokens) = valid-token K+V bytes per
+           step / mean step time; step_ms gives the median and p10/p90 of
+           single steps (HIP events between steps);
   roofline the attention kernel against the 8 TB/s HBM peak, its duration
            from HIP events on the launch stream; also against this box's
            measured streaming-read ceiling (measured_ceiling);
@@ -24,17 +25,22 @@ Prints one JSON line:
            peak;
   decode_part  that step's 128 decodes alone: attention kernel GB/s against
            the HBM peak;
-  fp8_kv   the 8-bit (E4M3) KV cache beside bf16 on the headline decode
-           layer and the 70B-class long-context layer: step time, decode
-           tokens/s, attention GB/s of code bytes;
+  decode_8b  the Llama-3-8B decode layer (64 requests, U[128, 4096]) step
+           and attention kernel;
+  tiny_decode  the 4-request latency case (microseconds per step);
+  fp8_kv   the 8-bit (E4M3) KV cache beside bf16 on the 8B decode layer and
+           the 70B-class long-context layer: step time, decode tokens/s,
+           attention GB/s of code bytes;
   shared_prefix  256 decodes sharing a 2048-token prefix: plain paged
            attention beside shared-prefix (cascade) attention, GB/s of the
            logical and of the unique K/V bytes;
-  block_copy  copy-on-write block copies (4096 pairs) on the headline pool;
+  block_copy  copy-on-write block copies (4096 pairs) on the 8B layer's pool;
   mla_decode  MLA latent decode, 64 requests, 16 and 128 query heads;
-  cpu_baseline  the CPU oracle (fp64) on the same headline workload.
+  cpu_baseline  the CPU oracle (fp64) on a bounded sample of the headline
+           workload, all host threads and one thread; per_config: the same
+           for every synthetic configuration.
 
-    python bench.py [--steps K] [--warmup W] [--config 2] [--no-mixed]
+    python bench.py [--steps K] [--warmup W] [--config 5] [--no-mixed]
                     [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -59,9 +65,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="2",
-                    help="workload timed: 1-5, or p for the mixed step's "
-                         "prefill chunk alone")
+    ap.add_argument("--config", default="5",
+                    help="workload timed: 1-5, p for the mixed step's prefill "
+                         "chunk alone, d for its 128 decodes alone")
     ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true",
@@ -259,12 +265,13 @@ class Runner:
 
     def run(self, steps, warmup):
         """Time `steps` whole steps (nothing but the step's own launches
-        between the synchronisations); then the attention kernel's average
-        launch duration: HIP events on the launch stream around runs of
-        back-to-back launches, one per layer pool, on one plan (as a forward
-        pass runs the layers).  An event record costs a few µs of dispatch gap
-        on each side, so events stay out of the step timing and are amortised
-        over a run of launches."""
+        between the synchronisations): their mean; then `steps` single steps
+        with a HIP event recorded between consecutive steps (median, p10,
+        p90); then the attention kernel's launch duration: HIP events on the
+        launch stream around runs of back-to-back launches, one per layer
+        pool, on one plan (as a forward pass runs the layers).  An event
+        record costs a few µs of dispatch gap, so the mean step comes from
+        the event-free loop and the kernel's from runs of launches."""
         torch = self.torch
         for i in range(warmup):
             self.step(i)
@@ -274,8 +281,15 @@ class Runner:
             self.step(i)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(self.stream)
+        for i in range(steps):
+            self.step(i)
+            ev[i + 1].record(self.stream)
+        torch.cuda.synchronize()
+        single = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
         n = len(self.layers)
-        runs = max(1, steps // n)
+        runs = max(5, steps // n)
         evs = [(torch.cuda.Event(enable_timing=True),
                 torch.cuda.Event(enable_timing=True)) for _ in range(runs)]
         self.plan()
@@ -287,46 +301,19 @@ class Runner:
                     raise RuntimeError(self.pa._lib.load().pa_last_error())
             evs[r][1].record(self.stream)
         torch.cuda.synchronize()
-        attend_ms = float(np.mean([a.elapsed_time(b) for a, b in evs])) / n
-        return (t1 - t0) * 1e3 / steps, attend_ms
+        per_launch = np.array([a.elapsed_time(b) for a, b in evs]) / n
+        return {"ms_per_step": (t1 - t0) * 1e3 / steps, "step_ms": percentiles(single),
+                "attend_ms": float(per_launch.mean()), "attend_pct": percentiles(per_launch)}
 
 
-def cpu_baseline(w, min_s=10.0, max_s=30.0, min_s1=3.0, max_s1=8.0):
-    """The oracle on the same workload, all heads of every sequence, in whole
-    sequences until at least min_s of oracle time (at most max_s), scaled to
-    KV GB/s; then the same with one thread on a shorter sample."""
-    import oracle
-    kc = np.zeros(w.pool_elems(), np.uint16)
-    vc = np.zeros(w.pool_elems(), np.uint16)
-    oracle.write_kv(kc, vc, w.k_dense[w.fill_rows], w.v_dense[w.fill_rows], w.fill_slots)
-    oracle.write_kv(kc, vc, w.k_new, w.v_new, w.new_slots)
-    threads = oracle.default_threads()
-    per_tok = 2 * w.num_kv_heads * w.head_dim * 2
-    rows = []
-    for b in range(w.num_seqs):
-        t0, t1 = int(w.query_start_loc[b]), int(w.query_start_loc[b + 1])
-        rows.append(np.array([(t, h) for t in range(t0, t1)
-                              for h in range(w.num_q_heads)], np.int64))
+def percentiles(x):
+    """Median, p10 and p90 of a sample of durations (ms), and its size."""
+    x = np.asarray(x, np.float64)
+    return {"median": round(float(np.median(x)), 5), "p10": round(float(np.percentile(x, 10)), 5),
+            "p90": round(float(np.percentile(x, 90)), 5), "n": int(x.size)}
 
-    def sample(nthreads, lo, hi):
-        done_seqs, kv_bytes, spent = 0, 0, 0.0
-        while spent < lo:
-            for b in range(w.num_seqs):
-                s = time.perf_counter()
-                oracle.attend_rows(w.q, kc, vc, w.block_tables, w.seq_lens,
-                                   w.query_start_loc, w.num_kv_heads, w.scale,
-                                   rows[b], nthreads=nthreads)
-                spent += time.perf_counter() - s
-                done_seqs += 1
-                kv_bytes += int(w.seq_lens[b]) * per_tok
-                if spent >= hi:
-                    break
-            if spent >= hi:
-                break
-        return done_seqs, kv_bytes, spent
 
-    done_seqs, kv_bytes, spent = sample(threads, min_s, max_s)
-    seqs1, bytes1, spent1 = sample(1, min_s1, max_s1)
+def host_description():
     cpu = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -340,18 +327,106 @@ def cpu_baseline(w, min_s=10.0, max_s=30.0, min_s1=3.0, max_s1=8.0):
         affinity = len(os.sched_getaffinity(0))
     except (AttributeError, OSError):
         affinity = None
-    return {"value": round(kv_bytes / spent / 1e9, 4), "unit": "GB/s",
-            "cores": threads, "kind": "oracle", "cpu": cpu,
-            "os_cpu_count": os.cpu_count(), "affinity": affinity,
-            "value_1_thread": round(bytes1 / spent1 / 1e9, 4),
-            "sample": "%d sequence attentions (%.1f passes over the %d sequences "
-                      "of the headline workload), all %d query heads, fp64 C "
-                      "oracle with OpenMP, %.1f s; one thread: %d sequences, %.1f s"
-                      % (done_seqs, done_seqs / w.num_seqs, w.num_seqs,
-                         w.num_q_heads, spent, seqs1, spent1)}
+    return {"cpu": cpu, "os_cpu_count": os.cpu_count(), "affinity": affinity}
+
+
+def oracle_sample(w, nthreads, min_s, max_s, seed=0):
+    """The CPU oracle (fp64 C, OpenMP over rows) on workload w's own pools,
+    over (query token, head) output rows in a seeded random order, in batches
+    of 16 rows per thread, until at least min_s (at most max_s) of oracle
+    time.  Returns the rows done, the time, and the visible query-key pairs
+    and K/V bytes they stand for (a row of a query at position p reads p + 1
+    keys; its share of the K/V bytes is (p + 1) * 2 * head_dim * 2 / G, the
+    kv head's tokens being read once for its G query heads)."""
+    import oracle
+    kc = np.zeros(w.pool_elems(), np.uint16)
+    vc = np.zeros(w.pool_elems(), np.uint16)
+    oracle.write_kv(kc, vc, w.k_dense[w.fill_rows], w.v_dense[w.fill_rows], w.fill_slots)
+    oracle.write_kv(kc, vc, w.k_new, w.v_new, w.new_slots)
+    T, Hq = w.num_q_tokens, w.num_q_heads
+    G = Hq // w.num_kv_heads
+    qsl = w.query_start_loc.astype(np.int64)
+    seq = np.searchsorted(qsl, np.arange(T), side="right") - 1
+    pos = (w.seq_lens[seq].astype(np.int64) - (qsl[seq + 1] - qsl[seq]) +
+           (np.arange(T) - qsl[seq]))
+    order = np.random.default_rng(seed).permutation(T * Hq)
+    batch = min(16 * nthreads, order.size)
+    done, spent, pairs = 0, 0.0, 0
+    while spent < min_s:
+        # (a workload with fewer rows than the time bound needs is passed
+        # over again, in the same order)
+        idx = np.take(order, np.arange(done, done + batch), mode="wrap")
+        rows = np.stack([idx // Hq, idx % Hq], axis=1).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.attend_rows(w.q, kc, vc, w.block_tables, w.seq_lens, w.query_start_loc,
+                           w.num_kv_heads, w.scale, rows, nthreads=nthreads)
+        spent += time.perf_counter() - t0
+        done += idx.size
+        pairs += int((pos[idx // Hq] + 1).sum())
+        if spent >= max_s:
+            break
+    kv_bytes = pairs * 2 * w.head_dim * 2 / G
+    return {"rows": done, "seconds": spent, "pairs": pairs, "kv_bytes": kv_bytes}
+
+
+def cpu_baseline(w, min_s=10.0, max_s=30.0, min_s1=3.0, max_s1=8.0):
+    """The oracle on a bounded sample of the headline workload, all host
+    threads and then one thread, scaled to KV GB/s (the value's unit)."""
+    import oracle
+    threads = oracle.default_threads()
+    allt = oracle_sample(w, threads, min_s, max_s)
+    one = oracle_sample(w, 1, min_s1, max_s1, seed=1)
+    total_rows = w.num_q_tokens * w.num_q_heads
+    return dict({"value": round(allt["kv_bytes"] / allt["seconds"] / 1e9, 4), "unit": "GB/s",
+                 "cores": threads, "kind": "oracle",
+                 "value_1_thread": round(one["kv_bytes"] / one["seconds"] / 1e9, 4),
+                 "sample": "%d (query token, head) output rows (%.2f passes over the %d "
+                           "rows of the headline workload, in a seeded random order), "
+                           "fp64 C oracle with OpenMP over rows, %d threads, %.1f s; one "
+                           "thread: %d rows, %.1f s" % (allt["rows"], allt["rows"] / total_rows,
+                                                        total_rows, threads, allt["seconds"],
+                                                        one["rows"], one["seconds"])},
+                **host_description())
+
+
+def cpu_per_config(workloads, min_s=1.0, max_s=6.0, min_s1=1.0, max_s1=4.0):
+    """The oracle on every synthetic configuration: KV GB/s and visible
+    query-key pairs per second with all host threads and with one thread,
+    on bounded row samples, and the time the whole configuration would take
+    at those rates."""
+    import oracle
+    threads = oracle.default_threads()
+    out = {}
+    for k, w in workloads:
+        G = w.num_q_heads // w.num_kv_heads
+        alg = algorithmic(w)
+        total_pairs = alg["pairs_per_head"] * w.num_q_heads
+        res = {"workload": w.name, "threads": threads}
+        for key, n, lo, hi in (("all_threads", threads, min_s, max_s), ("one_thread", 1, min_s1, max_s1)):
+            r = oracle_sample(w, n, lo, hi, seed=k)
+            rate = r["pairs"] / r["seconds"]
+            res[key] = {"kv_gbs": round(r["kv_bytes"] / r["seconds"] / 1e9, 4),
+                        "pairs_per_s": round(rate, 1), "rows": r["rows"],
+                        "seconds": round(r["seconds"], 2),
+                        "full_config_s": round(total_pairs / rate, 2)}
+        res["kv_bytes_per_pair"] = round(2 * w.head_dim * 2 / G, 2)
+        out[str(k)] = res
+    return out
 
 
 FP8_SCALES = (0.011, 0.0107)  # amax / 448 for N(0,1) bf16 data
+
+_WORKLOADS = {}
+
+
+def config(W, k):
+    """Synthetic configuration k (1-5; "p": the mixed step's prefill chunk
+    alone, "d": its 128 decodes alone), built once per run."""
+    k = str(k)
+    if k not in _WORKLOADS:
+        _WORKLOADS[k] = (W.make_prefill_chunk() if k == "p" else
+                         W.make_decode_part() if k == "d" else W.make_config(int(k)))
+    return _WORKLOADS[k]
 
 
 def fp8_runs(args, W):
@@ -360,14 +435,16 @@ def fp8_runs(args, W):
     code bytes, beside the same workload on bf16 pools."""
     import torch
     out = {"scales": list(FP8_SCALES), "format": "OCP E4M3, one fp32 scale per pool"}
-    for key, w in (("decode_8b", W.make_config(2)), ("decode_70b_32k", W.make_config(5))):
+    for key, w in (("decode_8b", config(W, 2)), ("decode_70b_32k", config(W, 5))):
         alg = algorithmic(w)
         res = {"workload": w.name}
         for kind, fp8 in (("bf16", None), ("fp8", FP8_SCALES)):
             r = Runner(w, args.min_working_set_gib, fp8=fp8)
-            ms, att = r.run(max(20, args.steps // 4), max(5, args.warmup // 2))
+            t = r.run(max(20, args.steps // 4), max(5, args.warmup // 2))
+            ms, att = t["ms_per_step"], t["attend_ms"]
             kv = alg["kv_bytes"] / (2 if fp8 else 1)
-            res[kind] = {"ms_per_step": round(ms, 5), "attend_ms": round(att, 5),
+            res[kind] = {"ms_per_step": round(ms, 5), "step_ms": t["step_ms"],
+                         "attend_ms": round(att, 5),
                          "decode_tokens_per_s": round(w.num_q_tokens / (ms * 1e-3), 1),
                          "attend_kv_gbs": round(kv / (att * 1e-3) / 1e9, 2),
                          "hbm_peak_frac": round(kv / (att * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -392,15 +469,17 @@ def shared_prefix_runs(args, W):
     kernel, with the attention's GB/s of logical (per request) and unique
     K/V bytes."""
     import torch
-    w = W.make_config(4)
+    w = config(W, 4)
     alg = algorithmic(w)
     uniq = unique_kv_bytes(w)
     out = {"workload": w.name, "prefix_tokens": int(w.shared_prefix),
            "logical_kv_bytes": alg["kv_bytes"], "unique_kv_bytes": uniq}
     for kind, casc in (("plain", None), ("cascade", int(w.shared_prefix))):
         r = Runner(w, args.min_working_set_gib, cascade=casc)
-        ms, att = r.run(max(20, args.steps // 4), max(5, args.warmup // 2))
-        out[kind] = {"ms_per_step": round(ms, 5), "attend_ms": round(att, 5),
+        t = r.run(max(20, args.steps // 4), max(5, args.warmup // 2))
+        ms, att = t["ms_per_step"], t["attend_ms"]
+        out[kind] = {"ms_per_step": round(ms, 5), "step_ms": t["step_ms"],
+                     "attend_ms": round(att, 5),
                      "decode_tokens_per_s": round(w.num_q_tokens / (ms * 1e-3), 1),
                      "attend_logical_gbs": round(alg["kv_bytes"] / (att * 1e-3) / 1e9, 2),
                      "attend_unique_gbs": round(uniq / (att * 1e-3) / 1e9, 2)}
@@ -411,12 +490,12 @@ def shared_prefix_runs(args, W):
 
 
 def block_copy_run(W):
-    """Copy-on-write block copies on the headline decode layer's pool: 4096
-    random (src, dst) pairs, every kv head of both pools; GB/s of bytes read
-    plus written."""
+    """Copy-on-write block copies on the 8B decode layer's pool: 4096 random
+    (src, dst) pairs, every kv head of both pools; GB/s of bytes read plus
+    written."""
     import torch
     import paged_kv_cache_varlen_amd as pa
-    w = W.make_config(2)
+    w = config(W, 2)
     kc, vc = pa.alloc_pool(w.num_blocks, w.num_kv_heads, w.head_dim, fill=0.0)
     rng = np.random.default_rng(7)
     ids = rng.permutation(w.num_blocks)[:8192]
@@ -545,6 +624,32 @@ def read_ceiling(torch, gib=4):
     return best
 
 
+def decode_kernel_name(w, fp8, cascade):
+    """The attention kernel a launch over workload w runs (as the trace names it)."""
+    G = w.num_q_heads // w.num_kv_heads
+    decode = cascade is None and w.max_query_len <= 16 // G
+    return ("attend_decode_kernel<%d, %s>" if decode else "attend_mixed_kernel<%d, %s>") % (
+        w.head_dim, "true" if fp8 else "false")
+
+
+def sub_run(args, w, **kw):
+    """A workload's step and attention kernel, with the kernel's GB/s and
+    TFLOP/s of algorithmic bytes and flops."""
+    import torch
+    alg = algorithmic(w)
+    r = Runner(w, args.min_working_set_gib, **kw)
+    t = r.run(max(20, args.steps // 4), max(5, args.warmup // 2))
+    del r
+    torch.cuda.empty_cache()
+    att = t["attend_ms"] * 1e-3
+    gbs = alg["attend_bytes"] / att / 1e9
+    return alg, t, {"workload": w.name, "ms_per_step": round(t["ms_per_step"], 5),
+                    "step_ms": t["step_ms"], "attend_ms": round(t["attend_ms"], 5),
+                    "attend_pct": t["attend_pct"], "attend_gbs": round(gbs, 2),
+                    "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
+                    "attend_tflops": round(alg["flops"] / att / 1e12, 2)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -562,7 +667,7 @@ def main():
         print(json.dumps({"mla_decode": mla_runs(args)}))
         return 0
 
-    w = W.make_prefill_chunk() if args.config == "p" else W.make_config(int(args.config))
+    w = config(W, args.config)
     alg = algorithmic(w)
     casc = int(w.shared_prefix) if args.cascade else None
     if args.cascade and not casc:
@@ -570,10 +675,9 @@ def main():
         return 2
     r = Runner(w, args.min_working_set_gib, fp8=FP8_SCALES if args.fp8 else None,
                cascade=casc)
-    ms_step, attend_ms = r.run(args.steps, args.warmup)
-    kernel = ("attend_decode_kernel<%d, %s>" if casc is None and w.max_query_len <= 16 // (
-        w.num_q_heads // w.num_kv_heads) else "attend_mixed_kernel<%d, %s>") % (
-        w.head_dim, "true" if args.fp8 else "false")
+    t = r.run(args.steps, args.warmup)
+    ms_step, attend_ms = t["ms_per_step"], t["attend_ms"]
+    kernel = decode_kernel_name(w, args.fp8, casc)
     if casc:
         # shared-prefix attention reads the prefix once: its algorithmic
         # bytes are the distinct tokens' K/V (plus the same q, out, metadata)
@@ -594,6 +698,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "step_ms": t["step_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -609,6 +714,7 @@ def main():
                                         + (" fp8" if args.fp8 else "")),
             "kernel": kernel,
             "attend_ms": round(attend_ms, 5),
+            "attend_pct": t["attend_pct"],
             "algorithmic_bytes": alg["attend_bytes"]},
     }
     if args.config != "p" and not args.no_ceiling:
@@ -628,40 +734,36 @@ def main():
     del r
     torch.cuda.empty_cache()
 
-    if not args.no_mixed and args.config not in ("3", "p"):
-        w3 = W.make_config(3)
-        a3 = algorithmic(w3)
-        r3 = Runner(w3, args.min_working_set_gib)
-        ms3, att3 = r3.run(max(20, args.steps // 4), max(5, args.warmup // 2))
-        line["mixed_step"] = {
-            "workload": w3.name, "tokens_per_s_per_layer": round(w3.num_q_tokens / (ms3 * 1e-3), 1),
-            "ms_per_step": round(ms3, 5), "attend_ms": round(att3, 5),
-            "kv_read_gbs": round(a3["kv_bytes"] / (ms3 * 1e-3) / 1e9, 2),
-            "attend_tflops": round(a3["flops"] / (att3 * 1e-3) / 1e12, 2)}
-        del r3
-        torch.cuda.empty_cache()
-        wp = W.make_prefill_chunk()
-        ap = algorithmic(wp)
-        rp = Runner(wp, args.min_working_set_gib)
-        _, attp = rp.run(max(20, args.steps // 4), max(5, args.warmup // 2))
-        tflops = ap["flops"] / (attp * 1e-3) / 1e12
+    if not args.no_mixed and args.config not in ("3", "p", "d"):
+        w3 = config(W, 3)
+        a3, t3, res = sub_run(args, w3)
+        res["tokens_per_s_per_layer"] = round(w3.num_q_tokens / (t3["ms_per_step"] * 1e-3), 1)
+        res["kv_read_gbs"] = round(a3["kv_bytes"] / (t3["ms_per_step"] * 1e-3) / 1e9, 2)
+        res["traffic"] = measured_traffic(decode_kernel_name(w3, False, None), w3.name)
+        line["mixed_step"] = res
+        ap, tp, res = sub_run(args, config(W, "p"))
+        tflops = ap["flops"] / (tp["attend_ms"] * 1e-3) / 1e12
         line["prefill_tile"] = {
-            "workload": wp.name, "attend_ms": round(attp, 5),
-            "flops": ap["flops"], "tflops": round(tflops, 2),
+            "workload": res["workload"], "attend_ms": res["attend_ms"],
+            "attend_pct": res["attend_pct"], "flops": ap["flops"], "tflops": round(tflops, 2),
             "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
             "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
-        del rp
-        torch.cuda.empty_cache()
-        wd = W.make_decode_part()
-        ad = algorithmic(wd)
-        rd = Runner(wd, args.min_working_set_gib)
-        _, attd = rd.run(max(20, args.steps // 4), max(5, args.warmup // 2))
-        gbs = ad["attend_bytes"] / (attd * 1e-3) / 1e9
-        line["decode_part"] = {
-            "workload": wd.name, "attend_ms": round(attd, 5),
-            "attend_gbs": round(gbs, 2), "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4)}
-        del rd
-        torch.cuda.empty_cache()
+        _, _, res = sub_run(args, config(W, "d"))
+        line["decode_part"] = res
+        if args.config != "2":
+            w2 = config(W, 2)
+            a2, t2, res = sub_run(args, w2)
+            res["decode_tokens_per_s"] = round(w2.num_q_tokens / (t2["ms_per_step"] * 1e-3), 1)
+            res["kv_read_gbs"] = round(a2["kv_bytes"] / (t2["ms_per_step"] * 1e-3) / 1e9, 2)
+            res["traffic"] = measured_traffic(decode_kernel_name(w2, False, None), w2.name)
+            line["decode_8b"] = res
+        if args.config != "1":
+            _, t1, res = sub_run(args, config(W, 1))
+            line["tiny_decode"] = {"workload": res["workload"],
+                                   "us_per_step": round(t1["ms_per_step"] * 1e3, 2),
+                                   "step_us": {k: (round(v * 1e3, 2) if k != "n" else v)
+                                               for k, v in t1["step_ms"].items()},
+                                   "attend_us": round(t1["attend_ms"] * 1e3, 2)}
         line["fp8_kv"] = fp8_runs(args, W)
         line["shared_prefix"] = shared_prefix_runs(args, W)
         line["block_copy"] = block_copy_run(W)
@@ -669,6 +771,9 @@ def main():
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
+        if not args.no_mixed:
+            line["cpu_baseline"]["per_config"] = cpu_per_config(
+                [(k, config(W, k)) for k in (1, 2, 3, 4, 5)])
     print(json.dumps(line))
     return 0
 
