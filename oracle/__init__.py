@@ -136,11 +136,13 @@ def v_index(n, g, t, d, num_kv_heads, head_dim, block_size=BLOCK_SIZE) -> int:
 # ---- scatter / gather -------------------------------------------------------
 
 def write_kv(k_cache: np.ndarray, v_cache: np.ndarray, k: np.ndarray,
-             v: np.ndarray, slot_mapping: np.ndarray) -> None:
+             v: np.ndarray, slot_mapping: np.ndarray,
+             block_size: int = BLOCK_SIZE) -> None:
     """In-place scatter of k, v ([T][Hkv][D] uint16 bits) into the pools.
 
-    ``k_cache``/``v_cache`` are flat uint16 arrays of num_blocks*Hkv*16*D
-    elements (any shape, C-contiguous)."""
+    ``k_cache``/``v_cache`` are flat uint16 arrays of
+    num_blocks*Hkv*block_size*D elements (any shape, C-contiguous); slot s
+    is offset s % block_size of block s // block_size."""
     assert k_cache.dtype == np.uint16 and k_cache.flags.c_contiguous
     assert v_cache.dtype == np.uint16 and v_cache.flags.c_contiguous
     T, Hkv, D = k.shape
@@ -149,19 +151,20 @@ def write_kv(k_cache: np.ndarray, v_cache: np.ndarray, k: np.ndarray,
     sm = _c(slot_mapping, np.int64)
     assert sm.shape == (T,)
     _load().oracle_write_kv(_p(k_cache), _p(v_cache), _p(k), _p(v), _p(sm), T,
-                            Hkv, BLOCK_SIZE, D)
+                            Hkv, int(block_size), D)
 
 
 def gather_kv(k_cache, v_cache, block_tables, seq_lens, num_kv_heads,
-              head_dim):
-    """Logical gather: dense ([sum L][Hkv][D] uint16) K and V."""
+              head_dim, block_size=BLOCK_SIZE):
+    """Logical gather: dense ([sum L][Hkv][D] uint16) K and V; table entry j
+    of a request names the block of its tokens j*block_size ..."""
     bt = _c(block_tables, np.int32)
     sl = _c(seq_lens, np.int32)
     total = int(sl.sum())
     ko = np.empty((total, num_kv_heads, head_dim), np.uint16)
     vo = np.empty_like(ko)
     _load().oracle_gather_kv(_p(k_cache), _p(v_cache), _p(bt), bt.shape[1],
-                             _p(sl), sl.shape[0], num_kv_heads, BLOCK_SIZE,
+                             _p(sl), sl.shape[0], num_kv_heads, int(block_size),
                              head_dim, _p(ko), _p(vo))
     return ko, vo
 
@@ -169,8 +172,9 @@ def gather_kv(k_cache, v_cache, block_tables, seq_lens, num_kv_heads,
 # ---- attention ----------------------------------------------------------------
 
 def attend(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
-           num_kv_heads, scale, nthreads=None) -> np.ndarray:
-    """fp64 out [T][Hq][D] of paged varlen causal attention."""
+           num_kv_heads, scale, nthreads=None, block_size=BLOCK_SIZE) -> np.ndarray:
+    """fp64 out [T][Hq][D] of paged varlen causal attention (pools and tables
+    of block_size-token blocks)."""
     q = _c(q, np.uint16)
     T, Hq, D = q.shape
     bt = _c(block_tables, np.int32)
@@ -183,14 +187,15 @@ def attend(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
     scratch = np.empty(nthreads * maxL, np.float64)
     out = np.zeros((T, Hq, D), np.float64)
     _load().oracle_attend(_p(q), _p(k_cache), _p(v_cache), _p(bt), bt.shape[1],
-                          _p(sl), _p(qsl), B, Hq, num_kv_heads, BLOCK_SIZE, D,
+                          _p(sl), _p(qsl), B, Hq, num_kv_heads, int(block_size), D,
                           float(scale), maxL, _p(scratch), _p(out),
                           int(nthreads))
     return out
 
 
 def attend_rows(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
-                num_kv_heads, scale, rows, nthreads=None) -> np.ndarray:
+                num_kv_heads, scale, rows, nthreads=None,
+                block_size=BLOCK_SIZE) -> np.ndarray:
     """fp64 out for selected (token, head) rows only: [len(rows)][D]."""
     q = _c(q, np.uint16)
     T, Hq, D = q.shape
@@ -205,7 +210,7 @@ def attend_rows(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
     out = np.zeros((rows.shape[0], D), np.float64)
     _load().oracle_attend_rows(_p(q), _p(k_cache), _p(v_cache), _p(bt),
                                bt.shape[1], _p(sl), _p(qsl), B, Hq,
-                               num_kv_heads, BLOCK_SIZE, D, float(scale), maxL,
+                               num_kv_heads, int(block_size), D, float(scale), maxL,
                                _p(rows), rows.shape[0], _p(scratch), _p(out),
                                int(nthreads))
     return out

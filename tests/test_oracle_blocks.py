@@ -93,3 +93,83 @@ def test_copy_on_write_then_write():
     ko, _ = oracle.gather_kv(kc, vc, tables, np.array([21, 21], np.int32), Hkv, D)
     assert np.array_equal(ko[:20], prompt) and np.array_equal(ko[21:41], prompt)
     assert np.array_equal(ko[20], t0[0]) and np.array_equal(ko[41], t1[0])
+
+
+# ---- 8-token blocks ---------------------------------------------------------------------
+
+def _golden_rows(golden_dir, name):
+    import os
+    with open(os.path.join(golden_dir, name)) as f:
+        return [ln for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+def test_golden_pool_layout_bs8(golden_dir):
+    # offsets of the 8-token tile layout worked out by hand
+    for row in _golden_rows(golden_dir, "pool_layout_bs8.txt"):
+        Hkv, D, n, g, t, d, ko, vo = map(int, row.split())
+        assert oracle.k_index(n, g, t, d, Hkv, D, block_size=8) == ko
+        assert oracle.v_index(n, g, t, d, Hkv, D, block_size=8) == vo
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_pool_layout_bs8_is_a_tile_permutation(D):
+    Hkv = 3
+    for n, g in [(0, 0), (2, 1), (5, 2)]:
+        base = (n * Hkv + g) * 8 * D
+        ks = sorted(oracle.k_index(n, g, t, d, Hkv, D, block_size=8) - base
+                    for t in range(8) for d in range(D))
+        vs = sorted(oracle.v_index(n, g, t, d, Hkv, D, block_size=8) - base
+                    for t in range(8) for d in range(D))
+        assert ks == list(range(8 * D))
+        assert vs == list(range(8 * D))
+
+
+def _bs8_workload(seed, **kw):
+    return W.make_workload("bs8", [1, 8, 9, 16, 17, 40, 100, 333], [1, 1, 9, 3, 1, 40, 7, 20],
+                           8, 2, 64, seed=seed, block_size=8, **kw)
+
+
+def test_bs8_accounting():
+    # ceil(L / 8) blocks per request, at most 7 slots of the last one unused
+    w = _bs8_workload(1)
+    nblk = (w.seq_lens + 7) // 8
+    assert np.array_equal((w.block_tables >= 0).sum(axis=1), nblk)
+    assert int(nblk.sum()) == 1 + 1 + 2 + 2 + 3 + 5 + 13 + 42
+    assert np.all(nblk * 8 - w.seq_lens <= 7)
+    assert w.pool_elems() == w.num_blocks * 2 * 8 * 64
+
+
+def test_bs8_scatter_gather_round_trip():
+    w = _bs8_workload(2)
+    kc = np.full(w.pool_elems(), W.BF16_NAN, np.uint16)
+    vc = kc.copy()
+    oracle.write_kv(kc, vc, w.k_dense[w.fill_rows], w.v_dense[w.fill_rows], w.fill_slots,
+                    block_size=8)
+    oracle.write_kv(kc, vc, w.k_new, w.v_new, w.new_slots, block_size=8)
+    kd, vd = oracle.gather_kv(kc, vc, w.block_tables, w.seq_lens, w.num_kv_heads,
+                              w.head_dim, block_size=8)
+    assert np.array_equal(kd, w.k_dense) and np.array_equal(vd, w.v_dense)
+    written = int(w.seq_lens.sum()) * w.num_kv_heads * w.head_dim
+    assert int((kc != W.BF16_NAN).sum()) == written
+
+
+def test_bs8_attention_equals_dense_and_16_token_blocks():
+    # the same requests and values in 8-token and in 16-token blocks (and
+    # contiguous): one logical order, so the fp64 results are identical
+    w8 = _bs8_workload(3)
+    w16 = W.make_workload("bs16", w8.seq_lens, w8.query_lens, 8, 2, 64, seed=3)
+    assert np.array_equal(w8.k_dense, w16.k_dense) and np.array_equal(w8.q, w16.q)
+    outs = []
+    for w in (w8, w16):
+        kc = np.full(w.pool_elems(), W.BF16_NAN, np.uint16)
+        vc = kc.copy()
+        oracle.write_kv(kc, vc, w.k_dense[w.fill_rows], w.v_dense[w.fill_rows],
+                        w.fill_slots, block_size=w.block_size)
+        oracle.write_kv(kc, vc, w.k_new, w.v_new, w.new_slots, block_size=w.block_size)
+        outs.append(oracle.attend(w.q, kc, vc, w.block_tables, w.seq_lens,
+                                  w.query_start_loc, w.num_kv_heads, w.scale,
+                                  block_size=w.block_size))
+    dense = oracle.attend_dense(w8.q, w8.k_dense, w8.v_dense, w8.seq_lens,
+                                w8.query_start_loc, w8.scale)
+    assert np.array_equal(outs[0], outs[1])
+    assert np.array_equal(outs[0], dense)

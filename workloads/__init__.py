@@ -30,7 +30,7 @@ are not available, so these stand in for them.
 from __future__ import annotations
 
 import os
-from collections import Counter
+from collections import deque
 from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 from typing import Dict, List, Optional, Sequence, Tuple
@@ -127,40 +127,53 @@ def slots_for(block_row: Sequence[int], positions: np.ndarray,
 
 
 class BlockPool:
-    """Refcounted pool of physical block ids (test fixture, host only).
+    """Physical block ids with a reference count each (host-side test fixture).
 
-    Free ids are handed out in a seeded random order so that block tables are
-    "a seeded random permutation of free blocks"."""
+    Free ids wait in a queue filled in a seeded random order, so that block
+    tables are "a seeded random permutation of free blocks"; a block held by
+    several tables (a shared prefix) counts one reference per table and
+    rejoins the queue when its last holder lets it go.  The idea follows
+    "Deep Dive - vLLM", section "Block pool, prefix cache, and eviction"."""
 
     def __init__(self, num_blocks: int, rng: np.random.Generator):
         self.num_blocks = int(num_blocks)
-        self.free: List[int] = [int(i) for i in rng.permutation(self.num_blocks)]
-        self.refs: Counter = Counter()
+        self.ref_count = np.zeros(self.num_blocks, np.int64)
+        self.free_ids = deque(int(i) for i in rng.permutation(self.num_blocks))
 
     def allocate(self, n: int) -> List[int]:
-        if n > len(self.free):
-            raise MemoryError("No free KV block")
-        got, self.free = self.free[:n], self.free[n:]
-        for b in got:
-            assert self.refs[b] == 0
-            self.refs[b] = 1
+        """n blocks from the head of the free queue, each held once."""
+        if len(self.free_ids) < n:
+            raise MemoryError("KV block pool exhausted: %d blocks requested, %d free"
+                              % (n, len(self.free_ids)))
+        got = [self.free_ids.popleft() for _ in range(n)]
+        self.ref_count[got] += 1
         return got
 
     def share(self, blocks: Sequence[int]) -> List[int]:
-        for b in blocks:
-            assert self.refs[b] > 0
-            self.refs[b] += 1
-        return list(blocks)
+        """One more holder for blocks that are already held."""
+        ids = np.asarray(list(blocks), np.int64)
+        if ids.size and int(self.ref_count[ids].min()) < 1:
+            raise ValueError("cannot share a block that nobody holds")
+        np.add.at(self.ref_count, ids, 1)
+        return [int(b) for b in ids]
 
     def release(self, blocks: Sequence[int]) -> None:
-        for b in reversed(list(blocks)):
-            self.refs[b] -= 1
-            assert self.refs[b] >= 0
-            if self.refs[b] == 0:
-                self.free.append(b)
+        """One holder fewer for each block; a block nobody holds any more
+        rejoins the free queue."""
+        for b in blocks:
+            if self.ref_count[b] < 1:
+                raise ValueError("block %d is not held" % b)
+            self.ref_count[b] -= 1
+            if self.ref_count[b] == 0:
+                self.free_ids.append(int(b))
+
+    @property
+    def refs(self) -> Dict[int, int]:
+        """Reference count of every held block."""
+        return {int(b): int(self.ref_count[b]) for b in np.flatnonzero(self.ref_count)}
 
     def used(self) -> int:
-        return sum(1 for v in self.refs.values() if v > 0)
+        return int(np.count_nonzero(self.ref_count))
 
 
 # ---- workloads ---------------------------------------------------------------------
@@ -188,6 +201,7 @@ class Workload:
     refs: Dict[int, int] = field(default_factory=dict)
     seeds: Dict[str, int] = field(default_factory=dict)
     shared_prefix: int = 0
+    block_size: int = BLOCK_SIZE  # tokens per physical block (table entry)
 
     @property
     def num_seqs(self) -> int:
@@ -214,7 +228,7 @@ class Workload:
         return self.v_dense[self.new_rows]
 
     def pool_elems(self) -> int:
-        return self.num_blocks * self.num_kv_heads * BLOCK_SIZE * self.head_dim
+        return self.num_blocks * self.num_kv_heads * self.block_size * self.head_dim
 
     def kv_bytes_read(self) -> int:
         """K+V bytes of the valid tokens that attention reads (logical)."""
@@ -226,7 +240,7 @@ class Workload:
             "workload": self.name, "num_seqs": self.num_seqs,
             "num_q_tokens": self.num_q_tokens, "num_q_heads": self.num_q_heads,
             "num_kv_heads": self.num_kv_heads, "head_dim": self.head_dim,
-            "block_size": BLOCK_SIZE, "num_blocks": self.num_blocks,
+            "block_size": self.block_size, "num_blocks": self.num_blocks,
             "max_seq_len": self.max_seq_len, "max_query_len": self.max_query_len,
             "sum_seq_len": int(self.seq_lens.astype(np.int64).sum()),
             "seeds": dict(self.seeds)}
@@ -236,7 +250,8 @@ def make_workload(name: str, seq_lens: Sequence[int], query_lens: Sequence[int],
                   num_q_heads: int, num_kv_heads: int, head_dim: int, seed: int,
                   num_blocks: Optional[int] = None, slack: float = 0.10,
                   shared_prefix: int = 0, shared: bool = True,
-                  table_width: Optional[int] = None) -> Workload:
+                  table_width: Optional[int] = None,
+                  block_size: int = BLOCK_SIZE) -> Workload:
     """Build one step's inputs.
 
     seq_lens include this step's query_lens tokens, which are the last
@@ -244,19 +259,21 @@ def make_workload(name: str, seq_lens: Sequence[int], query_lens: Sequence[int],
     block size), the first shared_prefix logical tokens of every sequence hold
     the same K/V; with shared=True their blocks are allocated once and held by
     every table (ref_cnt = number of sequences), otherwise every sequence gets
-    private copies (the unshared twin)."""
+    private copies (the unshared twin).  block_size: tokens per physical
+    block (16 by default; the tables, slots and pool size follow it)."""
     seq_lens = np.asarray(seq_lens, np.int32)
     query_lens = np.asarray(query_lens, np.int32)
     B = seq_lens.shape[0]
     assert query_lens.shape == (B,)
     assert np.all(query_lens >= 0) and np.all(query_lens <= seq_lens)
-    assert shared_prefix % BLOCK_SIZE == 0
+    bs = int(block_size)
+    assert shared_prefix % bs == 0
     assert np.all(seq_lens >= shared_prefix)
     seeds = {"data": 1000 + seed, "tables": 3000 + seed}
     rng_tab = np.random.default_rng(seeds["tables"])
 
-    nblk = [blocks_needed(int(L)) for L in seq_lens]
-    pref_blocks = shared_prefix // BLOCK_SIZE
+    nblk = [blocks_needed(int(L), bs) for L in seq_lens]
+    pref_blocks = shared_prefix // bs
     if shared_prefix and shared:
         need = pref_blocks + sum(n - pref_blocks for n in nblk)
     else:
@@ -304,12 +321,12 @@ def make_workload(name: str, seq_lens: Sequence[int], query_lens: Sequence[int],
             first = shared_prefix  # the shared blocks are written once, by seq 0
         cached = np.arange(first, L - Q, dtype=np.int64)
         fill_rows.append(s0 + cached)
-        fill_slots.append(slots_for(tables[b], cached))
+        fill_slots.append(slots_for(tables[b], cached, bs))
         newp = np.arange(L - Q, L, dtype=np.int64)
         new_rows.append(s0 + newp)
-        new_slots.append(slots_for(tables[b], newp))
+        new_slots.append(slots_for(tables[b], newp, bs))
     cat = (lambda xs: np.concatenate(xs) if xs else np.zeros(0, np.int64))
-    refs = {int(k): int(v) for k, v in pool.refs.items() if v > 0}
+    refs = pool.refs
     return Workload(
         name=name, num_q_heads=num_q_heads, num_kv_heads=Hkv, head_dim=D,
         num_blocks=int(num_blocks), scale=float(np.float32(1.0 / np.sqrt(D))),
@@ -319,7 +336,7 @@ def make_workload(name: str, seq_lens: Sequence[int], query_lens: Sequence[int],
         fill_slots=cat(fill_slots).astype(np.int64),
         new_rows=cat(new_rows).astype(np.int64),
         new_slots=cat(new_slots).astype(np.int64), refs=refs, seeds=seeds,
-        shared_prefix=int(shared_prefix))
+        shared_prefix=int(shared_prefix), block_size=bs)
 
 
 # ---- the five synthetic step configurations ------------------------------------------
