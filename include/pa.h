@@ -577,8 +577,7 @@ pa_status pa_copy_blocks(void *k_cache, void *v_cache, int64_t num_blocks,
  * ids into the 16-token tables pa_attend reads:
  *   out[b][j] = block_tables[b][j / R] * R + j % R,  j < max_blocks_per_seq * R
  * (entries < 0 stay -1).  out: device int32 [num_seqs][max_blocks_per_seq * R].
- * Block sizes below 16 (8) are not supported: the kernels' 16-key MFMA tiles
- * would then span two physical blocks.
+ * (8-token blocks have calls of their own: pa_write_kv_bs, pa_attend_bs.)
  *
  * Source: "vLLM: An Exhaustive Technical Study", section 2.1 (block sizes 8,
  * 16, 32 and larger per platform; the write slot is
@@ -656,6 +655,52 @@ pa_status pa_gather_kv(const void *k_cache, const void *v_cache,
                        int64_t total_rows, int32_t num_kv_heads,
                        int32_t head_dim, void *k_out, void *v_out,
                        void *stream);
+
+/*
+ * Pools of 8-token blocks (bf16): pa_write_kv_bs, pa_attend_bs,
+ * pa_gather_kv_bs.
+ *
+ * The pages offer block sizes 8, 16 and 32 ("vLLM: An Exhaustive Technical
+ * Study", section 2.1, the --block-size choices; the write slot is
+ * block number * block_size + offset).  These calls take block_size = 8 or
+ * 16; with 16 they are pa_write_kv, pa_attend and pa_gather_kv (larger
+ * blocks: 16-token pools and pa_expand_block_tables).  With 8, a pool is
+ * num_blocks x num_kv_heads tiles of 8 * head_dim bf16, tile (n, g) at
+ * element (n * num_kv_heads + g) * 8 * D, and inside it, H = D/2:
+ *     K(t, d) at ((d / 8) * 8 + t) * 8 + d % 8
+ *     V(t, d) at ((((d % H) / 16 * 2 + d / H) * 2 + t / 4) * 16 + d % 16)
+ *                * 4 + t % 4
+ * (the 16-token tile's formulas with 8 token slots); slot s is offset s % 8
+ * of block s / 8, and entry j of a block-table row names the block of
+ * tokens 8j .. 8j+7 (ceil(L_b / 8) entries used).  Attention gathers each
+ * 16-key step from two 8-token blocks; results are identical to pa_attend's
+ * over the same tokens in 16-token blocks (same work decomposition, same
+ * reduction order).  Arguments, workspace (pa_attend_workspace_size), checks
+ * and errors otherwise as the block-size-16 calls; a block_size other than
+ * 8 or 16 is PA_ERR_UNSUPPORTED.  8-bit pools of 8-token blocks are not
+ * supported.
+ */
+pa_status pa_write_kv_bs(const void *k, const void *v, int64_t k_token_stride,
+                         int64_t v_token_stride, const int64_t *slot_mapping,
+                         int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                         void *k_cache, void *v_cache, int64_t num_blocks,
+                         int32_t block_size, void *stream);
+
+pa_status pa_attend_bs(const void *q, const void *k_cache, const void *v_cache,
+                       int64_t num_blocks, int32_t block_size,
+                       const int32_t *block_tables, int32_t max_blocks_per_seq,
+                       const int32_t *seq_lens, const int32_t *query_start_loc,
+                       int32_t num_seqs, int64_t num_q_tokens, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t max_query_len,
+                       int32_t max_seq_len, float scale, void *out, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+pa_status pa_gather_kv_bs(const void *k_cache, const void *v_cache, int64_t num_blocks,
+                          int32_t block_size, const int32_t *block_tables,
+                          int32_t max_blocks_per_seq, const int32_t *seq_lens,
+                          const int64_t *kv_start, int32_t num_seqs, int64_t total_rows,
+                          int32_t num_kv_heads, int32_t head_dim, void *k_out,
+                          void *v_out, void *stream);
 
 /*
  * pa_validate_metadata_host - check the CONTENT of one step's metadata, all

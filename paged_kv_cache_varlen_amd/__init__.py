@@ -45,11 +45,12 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
 
 
 def alloc_pool(num_blocks: int, num_kv_heads: int, head_dim: int,
-               device="cuda", fill: Optional[float] = None
+               device="cuda", fill: Optional[float] = None, block_size: int = BLOCK_SIZE
                ) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Two bf16 pools (K, V), each [num_blocks][num_kv_heads][16 * head_dim]
-    in the library's tile layout."""
-    shape = (num_blocks, num_kv_heads, BLOCK_SIZE * head_dim)
+    """Two bf16 pools (K, V), each [num_blocks][num_kv_heads][block_size *
+    head_dim] in the library's tile layout (block_size 16, or 8 for the
+    *_bs calls)."""
+    shape = (num_blocks, num_kv_heads, int(block_size) * head_dim)
     if fill is None:
         k = torch.empty(shape, dtype=torch.bfloat16, device=device)
         v = torch.empty(shape, dtype=torch.bfloat16, device=device)
@@ -59,15 +60,16 @@ def alloc_pool(num_blocks: int, num_kv_heads: int, head_dim: int,
     return k, v
 
 
-def _pool_blocks(cache: torch.Tensor, num_kv_heads: int, head_dim: int) -> int:
-    per_block = num_kv_heads * BLOCK_SIZE * head_dim
+def _pool_blocks(cache: torch.Tensor, num_kv_heads: int, head_dim: int,
+                 block_size: int = BLOCK_SIZE) -> int:
+    per_block = num_kv_heads * int(block_size) * head_dim
     if not cache.is_contiguous() or cache.numel() % per_block:
         raise ValueError("pool must be contiguous with a multiple of "
-                         "num_kv_heads*16*head_dim elements")
+                         "num_kv_heads*block_size*head_dim elements")
     return cache.numel() // per_block
 
 
-def _scatter_args(k, v, slot_mapping, k_cache, v_cache, pool_dtype):
+def _scatter_args(k, v, slot_mapping, k_cache, v_cache, pool_dtype, block_size=BLOCK_SIZE):
     """Checks of a scatter's tensors; returns (T, Hkv, D, num_blocks)."""
     for t, n in ((k, "k"), (v, "v"), (slot_mapping, "slot_mapping"),
                  (k_cache, "k_cache"), (v_cache, "v_cache")):
@@ -85,21 +87,27 @@ def _scatter_args(k, v, slot_mapping, k_cache, v_cache, pool_dtype):
             raise ValueError("%s rows must be contiguous [num_kv_heads][head_dim]" % n)
     if not slot_mapping.is_contiguous() or slot_mapping.shape != (T,):
         raise ValueError("slot_mapping must be contiguous [num_tokens]")
-    nb = _pool_blocks(k_cache, Hkv, D)
-    if _pool_blocks(v_cache, Hkv, D) != nb:
+    nb = _pool_blocks(k_cache, Hkv, D, block_size)
+    if _pool_blocks(v_cache, Hkv, D, block_size) != nb:
         raise ValueError("k_cache and v_cache differ in size")
     return T, Hkv, D, nb
 
 
 def write_kv(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
-             k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
-    """Scatter k, v ([T][Hkv][D] bf16, rows may be strided) into their slots."""
-    T, Hkv, D, nb = _scatter_args(k, v, slot_mapping, k_cache, v_cache, torch.bfloat16)
+             k_cache: torch.Tensor, v_cache: torch.Tensor,
+             block_size: int = BLOCK_SIZE) -> None:
+    """Scatter k, v ([T][Hkv][D] bf16, rows may be strided) into their slots
+    (pools of block_size-token blocks: 16, or 8 through pa_write_kv_bs)."""
+    T, Hkv, D, nb = _scatter_args(k, v, slot_mapping, k_cache, v_cache, torch.bfloat16,
+                                  block_size)
     lib = _lib.load()
-    st = lib.pa_write_kv(_ptr(k), _ptr(v), k.stride(0), v.stride(0),
-                         _ptr(slot_mapping), T, Hkv, D, _ptr(k_cache),
-                         _ptr(v_cache), nb, _stream(k))
-    _lib.check(st, "pa_write_kv")
+    args = [_ptr(k), _ptr(v), k.stride(0), v.stride(0), _ptr(slot_mapping), T, Hkv, D,
+            _ptr(k_cache), _ptr(v_cache), nb]
+    if block_size == BLOCK_SIZE:
+        st, name = lib.pa_write_kv(*args, _stream(k)), "pa_write_kv"
+    else:
+        st, name = lib.pa_write_kv_bs(*args, int(block_size), _stream(k)), "pa_write_kv_bs"
+    _lib.check(st, name)
 
 
 def alloc_pool_fp8(num_blocks: int, num_kv_heads: int, head_dim: int,
@@ -173,7 +181,7 @@ def _metadata_args(block_tables, seq_lens, query_start_loc) -> int:
 
 def _attend_args(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
                  num_kv_heads, out, workspace, max_query_len, max_seq_len,
-                 cascade=False):
+                 cascade=False, block_size=BLOCK_SIZE):
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _need_cuda(t, n)
     _dtype(q, torch.bfloat16, "q")
@@ -188,8 +196,8 @@ def _attend_args(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
         if k_cache.dim() != 3:
             raise ValueError("pass num_kv_heads or a [blocks][kv_heads][16*D] pool")
         num_kv_heads = k_cache.shape[1]
-    nb = _pool_blocks(k_cache, num_kv_heads, D)
-    if _pool_blocks(v_cache, num_kv_heads, D) != nb:
+    nb = _pool_blocks(k_cache, num_kv_heads, D, block_size)
+    if _pool_blocks(v_cache, num_kv_heads, D, block_size) != nb:
         raise ValueError("k_cache and v_cache differ in size")
     if out is None:
         out = torch.empty_like(q)
@@ -212,7 +220,8 @@ def attend(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
            workspace: Optional[torch.Tensor] = None,
            planned: bool = False, merge: bool = True,
            k_scale: float = 1.0, v_scale: float = 1.0,
-           common_prefix_len: Optional[int] = None) -> torch.Tensor:
+           common_prefix_len: Optional[int] = None,
+           block_size: int = BLOCK_SIZE) -> torch.Tensor:
     """Paged varlen causal attention of every query row of a mixed batch.
 
     q [T][Hq][D] bf16; block_tables [B][max_blocks] int32; seq_lens [B] int32;
@@ -230,12 +239,25 @@ def attend(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     for the whole batch and merged with each request's own keys.  Needs a
     workspace from alloc_workspace(..., cascade=True) (allocated here when
     none is given); with planned=True the plan must come from
-    attend_plan(..., common_prefix_len=...)."""
+    attend_plan(..., common_prefix_len=...).
+
+    block_size: 16, or 8 (bf16 pools of 8-token blocks from alloc_pool(...,
+    block_size=8), tables of 8-token ids; pa_attend_bs, not planned)."""
     cascade = common_prefix_len is not None
     T, Hq, D, Hkv, nb, B, out, workspace = _attend_args(
         q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
-        num_kv_heads, out, workspace, max_query_len, max_seq_len, cascade)
+        num_kv_heads, out, workspace, max_query_len, max_seq_len, cascade, block_size)
     lib = _lib.load()
+    if block_size != BLOCK_SIZE:
+        if planned or cascade or k_cache.dtype == torch.uint8:
+            raise ValueError("block_size != 16: bf16 pools, plain pa_attend_bs only")
+        st = lib.pa_attend_bs(_ptr(q), _ptr(k_cache), _ptr(v_cache), nb, int(block_size),
+                              _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens),
+                              _ptr(query_start_loc), B, T, Hq, Hkv, D, int(max_query_len),
+                              int(max_seq_len), float(scale), _ptr(out), _ptr(workspace),
+                              workspace.numel(), _stream(q))
+        _lib.check(st, "pa_attend_bs")
+        return out
     args = [_ptr(q), _ptr(k_cache), _ptr(v_cache), nb, _ptr(block_tables),
             block_tables.shape[1], _ptr(seq_lens), _ptr(query_start_loc), B, T,
             Hq, Hkv, D, int(max_query_len), int(max_seq_len)]
@@ -455,23 +477,30 @@ def mla_decode(q: torch.Tensor, cache: torch.Tensor, block_tables: torch.Tensor,
 def gather_kv(k_cache: torch.Tensor, v_cache: torch.Tensor,
               block_tables: torch.Tensor, seq_lens: torch.Tensor,
               kv_start: torch.Tensor, total_rows: int, num_kv_heads: int,
-              head_dim: int) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Logical gather through the block tables: dense [sum L][Hkv][D] K, V."""
+              head_dim: int, block_size: int = BLOCK_SIZE) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Logical gather through the block tables: dense [sum L][Hkv][D] K, V
+    (pools of block_size-token blocks: 16, or 8 through pa_gather_kv_bs)."""
     for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache"),
                  (block_tables, "block_tables"), (seq_lens, "seq_lens"),
                  (kv_start, "kv_start")):
         _need_cuda(t, n)
     _dtype(kv_start, torch.int64, "kv_start")
-    nb = _pool_blocks(k_cache, num_kv_heads, head_dim)
+    nb = _pool_blocks(k_cache, num_kv_heads, head_dim, block_size)
     B = block_tables.shape[0]
     ko = torch.empty((total_rows, num_kv_heads, head_dim), dtype=torch.bfloat16,
                      device=k_cache.device)
     vo = torch.empty_like(ko)
     lib = _lib.load()
-    st = lib.pa_gather_kv(_ptr(k_cache), _ptr(v_cache), nb, _ptr(block_tables),
-                          block_tables.shape[1], _ptr(seq_lens), _ptr(kv_start),
-                          B, total_rows, num_kv_heads, head_dim, _ptr(ko),
-                          _ptr(vo), _stream(k_cache))
+    if block_size == BLOCK_SIZE:
+        st = lib.pa_gather_kv(_ptr(k_cache), _ptr(v_cache), nb, _ptr(block_tables),
+                              block_tables.shape[1], _ptr(seq_lens), _ptr(kv_start),
+                              B, total_rows, num_kv_heads, head_dim, _ptr(ko),
+                              _ptr(vo), _stream(k_cache))
+    else:
+        st = lib.pa_gather_kv_bs(_ptr(k_cache), _ptr(v_cache), nb, int(block_size),
+                                 _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens),
+                                 _ptr(kv_start), B, total_rows, num_kv_heads, head_dim,
+                                 _ptr(ko), _ptr(vo), _stream(k_cache))
     _lib.check(st, "pa_gather_kv")
     return ko, vo
 

@@ -72,6 +72,11 @@ SIGNATURES = {
                                P]),
     "pa_gather_kv": (STATUS, [P, P, I64, P, I32, P, P, I32, I64, I32, I32, P, P,
                               P]),
+    "pa_write_kv_bs": (STATUS, [P, P, I64, I64, P, I64, I32, I32, P, P, I64, I32, P]),
+    "pa_attend_bs": (STATUS, [P, P, P, I64, I32, P, I32, P, P, I32, I64, I32, I32, I32,
+                              I32, I32, F32, P, P, SZ, P]),
+    "pa_gather_kv_bs": (STATUS, [P, P, I64, I32, P, I32, P, P, I32, I64, I32, I32, P, P,
+                                 P]),
     "pa_validate_metadata_host": (STATUS, [P, I32, P, P, I32, I64, I32, I32, I64,
                                            P, I64]),
     "pa_validate_metadata": (STATUS, [P, I32, P, P, I32, I64, I32, I32, I64, P,

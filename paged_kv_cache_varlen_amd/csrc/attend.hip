@@ -94,6 +94,7 @@ struct AttendParams {
   int64_t max_pre_partials;
   int32_t prefix_len;  // plan: keys every request shares (0: none)
   int32_t split_decode;  // plan: key range of a decode split (requests <= kLongDecode)
+  int32_t bs_shift;    // log2 of the tokens per block-table entry (4, or 3)
 };
 
 // ---------------------------------------------------------------------------
@@ -106,11 +107,11 @@ struct AttendParams {
 // of the launch that reads it.)
 __device__ __forceinline__ uint32_t plan_signature(const AttendParams& P) {
   uint32_t h = 2166136261u;
-  const int32_t v[9] = {P.num_seqs, P.num_q_tokens, P.Hq, P.Hkv,
-                        P.max_query_len, P.max_seq_len, (int32_t)P.max_items,
-                        (int32_t)P.max_partials, (int32_t)P.max_pre_items};
+  const int32_t v[10] = {P.num_seqs, P.num_q_tokens, P.Hq, P.Hkv,
+                         P.max_query_len, P.max_seq_len, (int32_t)P.max_items,
+                         (int32_t)P.max_partials, (int32_t)P.max_pre_items, P.bs_shift};
 #pragma unroll
-  for (int i = 0; i < 9; ++i) h = (h ^ (uint32_t)v[i]) * 16777619u;
+  for (int i = 0; i < 10; ++i) h = (h ^ (uint32_t)v[i]) * 16777619u;
   return h;
 }
 
@@ -144,7 +145,7 @@ __device__ SeqCounts seq_counts(const AttendParams& P, int b) {
   const int Q = q1 - q0, L = P.seq_lens[b];
   const bool ok = q0 >= 0 && Q >= 0 && q1 <= P.num_q_tokens && Q <= L &&
                   L <= P.max_seq_len && Q <= P.max_query_len &&
-                  ((L + kBlock - 1) / kBlock) <= P.bt_stride;
+                  ((L + (1 << P.bs_shift) - 1) >> P.bs_shift) <= P.bt_stride;
   if (!ok) {
     atomicOr(&P.hdr->error, 2u);
     return c;
@@ -736,11 +737,16 @@ __device__ __forceinline__ bf16x8 load_v(const uint16_t* vp, int c, int lane) {
 // If `counter` is not null, the next queue entry is claimed from it when the
 // load of the unit's last block is issued (its latency then hides behind the
 // last blocks and the output stores) and returned; otherwise 0.
-template <int D, int CT, int NB, bool STREAM, bool KV8>
+// BS8: the pools hold 8-token blocks (block-table entries name 8 tokens), so
+// each 16-key step reads two pool tiles: lanes of tokens 0-7 (K) and of key
+// groups 0-1 (V) from the first, the others from the second; the operands
+// land in the same registers as from one 16-token tile.
+template <int D, int CT, int NB, bool STREAM, bool KV8, bool BS8 = false>
 __device__ __forceinline__ uint32_t run_unit(const AttendParams& P,
                                              const WorkItem& it, int kvh,
                                              int lane,
                                              uint32_t* counter = nullptr) {
+  static_assert(!(KV8 && BS8), "8-token blocks: bf16 pools only");
   constexpr int KC = D / 32;
   constexpr int NT = D / 16;
   const int g = lane >> 4;
@@ -770,9 +776,21 @@ __device__ __forceinline__ uint32_t run_unit(const AttendParams& P,
 
   for (int c0 = jb0; c0 < jb1; c0 += 64) {
     const int nblk = min(64, jb1 - c0);
-    // physical ids of this chunk's blocks, one per lane
-    int idv = 0;
-    if (lane < nblk) idv = btrow[c0 + lane];
+    // physical ids of this chunk's blocks, one per lane (8-token blocks: the
+    // two of each 16-key step; a second block past the range's keys is not
+    // read from the table, the first stands in for it, its keys masked)
+    int idv = 0, idv2 = 0;
+    if constexpr (BS8) {
+      const int j8 = 2 * (c0 + lane);
+      const int nb8 = (it.kv1 + 7) >> 3;
+      if (lane < nblk) {
+        idv = btrow[j8];
+        idv2 = j8 + 1 < nb8 ? btrow[j8 + 1] : idv;
+      }
+      idv2 = idv2 < 0 ? 0 : (idv2 >= P.num_blocks ? (int)(P.num_blocks - 1) : idv2);
+    } else {
+      if (lane < nblk) idv = btrow[c0 + lane];
+    }
     idv = idv < 0 ? 0 : (idv >= P.num_blocks ? (int)(P.num_blocks - 1) : idv);
 
     auto issue = [&](KVBuf<D, KV8>& buf, int j) {
@@ -782,7 +800,26 @@ __device__ __forceinline__ uint32_t run_unit(const AttendParams& P,
       }
       const int id = __builtin_amdgcn_readlane(idv, j);
       const int64_t off = ((int64_t)id * P.Hkv + kvh) * tile_elems;
-      if constexpr (KV8) {
+      if constexpr (BS8) {
+        // tiles of 8 * D elements: K chunk q of token t at (q * 8 + t) * 8,
+        // V region h (512 bytes in a 16-token tile) at h * 128
+        const int id2 = __builtin_amdgcn_readlane(idv2, j);
+        const int64_t offa = ((int64_t)id * P.Hkv + kvh) * (8 * D);
+        const int64_t offb = ((int64_t)id2 * P.Hkv + kvh) * (8 * D);
+        const int r = lane & 15;
+        const uint16_t* kp = P.k_cache + (r < 8 ? offa : offb) + g * 64 + (r & 7) * 8;
+        const uint16_t* vp = P.v_cache + (g < 2 ? offa : offb) + ((g & 1) * 16 + r) * 4;
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+          buf.k[c] = STREAM ? load16_stream(kp + c * 256) : load16(kp + c * 256);
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+          const bf16x4 a = STREAM ? load8_stream(vp + 2 * c * 128) : load8(vp + 2 * c * 128);
+          const bf16x4 b =
+              STREAM ? load8_stream(vp + (2 * c + 1) * 128) : load8(vp + (2 * c + 1) * 128);
+          buf.v[c] = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+      } else if constexpr (KV8) {
         // tile_elems bytes per tile; unit p of either pool at p KiB + 16 lane
         const uint8_t* kp = reinterpret_cast<const uint8_t*>(P.k_cache) + off;
         const uint8_t* vp = reinterpret_cast<const uint8_t*>(P.v_cache) + off;
@@ -1000,6 +1037,41 @@ __device__ __forceinline__ void load_lds_kib(const uint16_t* base, uint32_t voff
         : "memory");
   }
 }
+// Global-to-LDS copy of N KiB with a global address per lane: load c has
+// lane i read 16 bytes at lane_addr - 512 c + 1024 c and write them to LDS at
+// l + 1024 c + 16 i.  (For pools of 8-token blocks: the 16-token tile of a
+// stage is gathered from two pool tiles, in which the data of consecutive
+// KiB of the stage lie 512 bytes apart.)  M0 is set and restored as in
+// load_lds_kib; the addresses are VGPRs, which need no wait states.
+template <int N>
+__device__ __forceinline__ void load_lds_kib_lanes(uint64_t lane_addr, uint32_t l) {
+  static_assert(N == 2 || N == 4, "2 or 4 KiB tiles");
+  uint32_t saved;
+  const uint64_t a1 = lane_addr - 512;
+  if constexpr (N == 2) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 4\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "global_load_lds_dwordx4 %2, off offset:1024\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(lane_addr), "v"(a1), "s"(l)
+        : "memory");
+  } else {
+    const uint64_t a2 = lane_addr - 1024, a3 = lane_addr - 1536;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %5\n\ts_nop 4\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "global_load_lds_dwordx4 %2, off offset:1024\n\t"
+        "global_load_lds_dwordx4 %3, off offset:2048\n\t"
+        "global_load_lds_dwordx4 %4, off offset:3072\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(lane_addr), "v"(a1), "v"(a2), "v"(a3), "s"(l)
+        : "memory");
+  }
+}
+
 // Wait until at most N of this wave's vector memory loads are outstanding,
 // then meet the other waves of the workgroup.  (A compiler-level memory
 // barrier as well: LDS reads are not moved across it.)
@@ -1062,10 +1134,14 @@ __device__ __forceinline__ void wait_lds_operands(T (&v)[N]) {
 // maximum grows by more than that.
 constexpr float kRescaleSlack = 8.0f;
 
-template <int D, bool KV8>
+// BS8: pools of 8-token blocks.  A stage still holds 16-token tiles in the
+// pool's 16-token layout (the compute below is the same); each is gathered
+// from two 8-token pool tiles with per-lane addresses.
+template <int D, bool KV8, bool BS8 = false>
 __device__ __forceinline__ void run_tile(const AttendParams& P,
                                          const WorkItem& it, int kvh, int lane,
                                          int wslot, uint8_t* ring) {
+  static_assert(!(KV8 && BS8), "8-token blocks: bf16 pools only");
   constexpr int KC = D / 32;
   constexpr int NT = D / 16;
   constexpr int CT = kPrefillColTiles;
@@ -1111,34 +1187,60 @@ __device__ __forceinline__ void run_tile(const AttendParams& P,
   const int jb0 = it.kv0 >> 4;
   const int nblk = ((it.kv1 + kBlock - 1) >> 4) - jb0;
   const int npairs = (nblk + 1) >> 1;
-  const int32_t* btrow = P.bt + (int64_t)it.seq * P.bt_stride + jb0;
+  const int32_t* btrow = P.bt + (int64_t)it.seq * P.bt_stride + (BS8 ? 2 * jb0 : jb0);
+  // 8-token blocks of the item's keys, from block 2 * jb0
+  const int nblk8 = BS8 ? ((it.kv1 + 7) >> 3) - 2 * jb0 : 0;
   // Wave w loads tile w of every stage: K(first), V(first), K(second),
   // V(second) -- 1 KiB per load, in pool order.
   const uint8_t* pool =
       reinterpret_cast<const uint8_t*>((wslot & 1) ? P.v_cache : P.k_cache);
   const int half = wslot >> 1;
 
-  // physical ids of 64 blocks (32 pairs) from block 2 * idbase, one per lane
+  // physical ids of 64 blocks (32 pairs; 8-token blocks: 16 pairs) from the
+  // first block of pair idbase, one per lane, clamped to the item's last
+  // block (a clamped copy only fills keys that are masked)
+  constexpr int kPairsPerIds = BS8 ? 16 : 32;
   auto load_ids = [&](int pr0) {
-    const int jr = min(2 * pr0 + lane, nblk - 1);  // clamped
+    const int jr = BS8 ? min(4 * pr0 + lane, nblk8 - 1) : min(2 * pr0 + lane, nblk - 1);
     const int id = btrow[jr];
     const int idc = id < 0 ? 0 : (id >= P.num_blocks ? (int)(P.num_blocks - 1) : id);
     return (int)((uint32_t)idc * (uint32_t)P.Hkv + (uint32_t)kvh);
   };
   int idbase = 0;
   int idv = load_ids(0);
+  // 8-token blocks: this lane's byte offset inside a pool tile of 8 * D and
+  // which of the 16-key group's two blocks it reads (K: token lane % 16 of
+  // 8-dim chunk lane / 16; V: the 8-byte runs of key group (lane / 8) % 4 at
+  // dims lane % 8 * 2 and + 1 of region lane / 32), for the first KiB of the
+  // stage tile; each later KiB lies 512 bytes further
+  constexpr uint32_t TB8 = TB / 2;
+  const bool vwave = (wslot & 1) != 0;
+  const uint32_t lane_off8 = vwave ? (uint32_t)((lane >> 5) * 256 + ((lane >> 3) & 1) * 128 +
+                                                (lane & 7) * 16)
+                                   : (uint32_t)((lane >> 4) * 128 + (lane & 7) * 16);
+  const bool second8 = vwave ? ((lane >> 4) & 1) != 0 : ((lane >> 3) & 1) != 0;
 
   // LDS byte address of this wave's tile in stage 0 (stage s: + s * stage bytes)
   const uint32_t ring_lds = lds_addr(ring) + (uint32_t)(wslot * TB);
   auto issue = [&](int slot, int pr) {
-    if (pr >= idbase + 32) {  // pairs are issued in order
-      idbase += 32;
+    if (pr >= idbase + kPairsPerIds) {  // pairs are issued in order
+      idbase += kPairsPerIds;
       idv = load_ids(idbase);
     }
-    // tile index id * Hkv + kvh (below 2^32 for any pool the device holds)
-    const uint32_t tix = (uint32_t)__builtin_amdgcn_readlane(idv, 2 * (pr - idbase) + half);
-    const uint16_t* src = reinterpret_cast<const uint16_t*>(pool + (uint64_t)tix * TB);
-    load_lds_kib<LPS>(src, (uint32_t)lane * 16, ring_lds + (uint32_t)(slot * SB));
+    if constexpr (BS8) {
+      // tile indices id * Hkv + kvh of the 16-key group's two 8-token blocks
+      const int e = 4 * (pr - idbase) + 2 * half;
+      const uint32_t ta = (uint32_t)__builtin_amdgcn_readlane(idv, e);
+      const uint32_t tb = (uint32_t)__builtin_amdgcn_readlane(idv, e + 1);
+      const uint64_t addr =
+          (uint64_t)(uintptr_t)pool + (uint64_t)(second8 ? tb : ta) * TB8 + lane_off8;
+      load_lds_kib_lanes<LPS>(addr, ring_lds + (uint32_t)(slot * SB));
+    } else {
+      // tile index id * Hkv + kvh (below 2^32 for any pool the device holds)
+      const uint32_t tix = (uint32_t)__builtin_amdgcn_readlane(idv, 2 * (pr - idbase) + half);
+      const uint16_t* src = reinterpret_cast<const uint16_t*>(pool + (uint64_t)tix * TB);
+      load_lds_kib<LPS>(src, (uint32_t)lane * 16, ring_lds + (uint32_t)(slot * SB));
+    }
   };
 
   // Scores of one pair of blocks (stage st): sa for the first block, sb
@@ -1394,7 +1496,7 @@ __device__ __forceinline__ bool item_ok(const AttendParams& P,
             it.ntok >= 1 && it.ntok <= maxtok &&
             it.tok0 + it.ntok <= P.num_q_tokens && it.kv0 >= 0 &&
             (it.kv0 & 31) == 0 && it.kv1 > it.kv0 && it.kv1 <= P.max_seq_len &&
-            ((it.kv1 + kBlock - 1) / kBlock) <= P.bt_stride &&
+            ((it.kv1 + (1 << P.bs_shift) - 1) >> P.bs_shift) <= P.bt_stride &&
             it.nsplit >= 1 && it.split >= 0 && it.split < it.nsplit;
   if (it.kind == kKindDecode) ok = ok && (it.kv1 - it.kv0) <= kSplitDecodeLong;
   if (it.nsplit > 1) ok = ok && it.pbase >= 0;
@@ -1404,7 +1506,7 @@ __device__ __forceinline__ bool item_ok(const AttendParams& P,
   return ok;
 }
 
-template <int D, bool MIXED, bool KV8>
+template <int D, bool MIXED, bool KV8, bool BS8 = false>
 __device__ __forceinline__ void attend_body(const AttendParams& P,
                                             uint8_t* ring) {
   const int lane = threadIdx.x & 63;
@@ -1487,7 +1589,7 @@ __device__ __forceinline__ void attend_body(const AttendParams& P,
       const uint32_t w = pfx ? u : u - num_pfx;
       const WorkItem it = pfx ? P.pitems[w / Hkv] : P.items[w / Hkv];
       if (item_ok(P, it) && it.kind == (pfx ? kKindPrefix : kKindPrefill))
-        run_tile<D, KV8>(P, it, (int)(w % Hkv), lane, (int)wslot, ring);
+        run_tile<D, KV8, BS8>(P, it, (int)(w % Hkv), lane, (int)wslot, ring);
       if (threadIdx.x == 0) next_unit[k] = pre_claim();
       __syncthreads();
       u = __builtin_amdgcn_readfirstlane(next_unit[k]);
@@ -1499,7 +1601,7 @@ __device__ __forceinline__ void attend_body(const AttendParams& P,
       const uint32_t w = num_pre + shard + S * k;
       const WorkItem it = P.items[w / Hkv];
       if (item_ok(P, it) && it.kind == kKindDecode)
-        k = dec_claimed(run_unit<D, kDecodeColTiles, kDecodeStages, true, KV8>(
+        k = dec_claimed(run_unit<D, kDecodeColTiles, kDecodeStages, true, KV8, BS8>(
             P, it, (int)(w % Hkv), lane, dctr));
       else
         k = dec_claimed(claim(dctr));
@@ -1541,6 +1643,22 @@ __attribute__((amdgpu_waves_per_eu(2, 8)))
 void attend_mixed_kernel(AttendParams P) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[prefill_ring_bytes<D, KV8>()];
   attend_body<D, true, KV8>(P, ring);
+}
+
+// The same two kernels over pools of 8-token blocks (bf16).
+template <int D>
+__global__ __launch_bounds__(kAttendThreads)
+__attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2, 8)))
+void attend_decode_bs8_kernel(AttendParams P) {
+  attend_body<D, false, false, true>(P, nullptr);
+}
+
+template <int D>
+__global__ __launch_bounds__(kAttendThreads)
+__attribute__((amdgpu_waves_per_eu(2, 8)))
+void attend_mixed_bs8_kernel(AttendParams P) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[prefill_ring_bytes<D, false>()];
+  attend_body<D, true, false, true>(P, ring);
 }
 
 // ---------------------------------------------------------------------------
@@ -1682,11 +1800,11 @@ __global__ __launch_bounds__(kAttendThreads) void merge_kernel(AttendParams P) {
 // Resident workgroups per CU of a kernel (queried once per device).
 int resident_wgs(const void* fn, int slot) {
   static std::mutex mu;
-  static std::vector<int> cache;  // [device * 8 + slot]
+  static std::vector<int> cache;  // [device * 16 + slot]
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 1;
   std::lock_guard<std::mutex> lock(mu);
-  const size_t idx = (size_t)dev * 8 + slot;
+  const size_t idx = (size_t)dev * 16 + slot;
   if (cache.size() <= idx) cache.resize(idx + 1, 0);
   if (cache[idx] == 0) {
     int n = 0;
@@ -1742,6 +1860,7 @@ AttendParams make_params(const AttendArgs& a) {
   P.prefix_len = a.cascade ? a.prefix_len : 0;
   P.split_decode = (a.kv8 && !a.cascade && a.max_query_len <= decode_tile_tokens(P.G))
                        ? kSplitDecode8 : kSplitDecode;
+  P.bs_shift = a.block_size == 8 ? 3 : 4;
   return P;
 }
 
@@ -1801,6 +1920,13 @@ hipError_t launch_planned(const AttendArgs& a, hipStream_t stream) {
     slot = decode_only ? 2 : 3;
   }
   if (a.kv8) slot += 4;
+  if (a.block_size == 8) {  // bf16 pools of 8-token blocks (checked by the caller)
+    if (a.head_dim == 128)
+      fn = decode_only ? attend_decode_bs8_kernel<128> : attend_mixed_bs8_kernel<128>;
+    else
+      fn = decode_only ? attend_decode_bs8_kernel<64> : attend_mixed_bs8_kernel<64>;
+    slot = 8 + (decode_only ? 0 : 1) + (a.head_dim == 128 ? 0 : 2);
+  }
   // Persistent grid: every resident slot of every CU, never more waves than
   // the work-unit bound.
   const int64_t max_work =

@@ -8,13 +8,14 @@
 // 2.1, "Reaching the kernel").  One body for prefill chunks and decodes
 // alike: the slot is all it needs.
 //
-// Pool tile layout (block n, kv head g), 16*D bf16, H = D/2:
-//   K(t, d) at ((d/8)*16 + t)*8 + d%8      -> 16 bytes per (t, 8-dim chunk)
-//   V(t, d) at ((((d%H)/16*2 + d/H)*4 + t/4)*16 + d%16)*4 + t%4
-//                                          -> 8 bytes per (4 tokens, dim)
+// Pool tile layout (block n, kv head g) of a pool of BS-token blocks (BS = 16,
+// or 8), BS*D bf16, H = D/2:
+//   K(t, d) at ((d/8)*BS + t)*8 + d%8       -> 16 bytes per (t, 8-dim chunk)
+//   V(t, d) at ((((d%H)/16*2 + d/H)*(BS/4) + t/4)*16 + d%16)*4 + t%4
+//                                           -> 8 bytes per (4 tokens, dim)
 // The attention kernel reads each tile with fully contiguous wave loads
 // (16 bytes per lane for K, 8 for V) that land directly in MFMA operand
-// order.
+// order; a 16-key MFMA tile of a pool of 8-token blocks is two such tiles.
 #pragma once
 
 #include "pa_device.h"
@@ -23,11 +24,11 @@ namespace pa {
 
 namespace {
 
-// Offset of V(t, d) inside a tile.
-template <int D>
+// Offset of V(t, d) inside a tile of BS token slots.
+template <int D, int BS = kBlock>
 __device__ __forceinline__ int v_offset(int t, int d) {
   constexpr int H = D / 2;
-  return ((((d % H) / 16 * 2 + d / H) * 4 + (t >> 2)) * 16 + d % 16) * 4 + (t & 3);
+  return ((((d % H) / 16 * 2 + d / H) * (BS / 4) + (t >> 2)) * 16 + d % 16) * 4 + (t & 3);
 }
 
 // Scatter thread gid (0 <= gid < ceil(T/4) * Hkv * D/8; larger gids do
@@ -36,8 +37,9 @@ __device__ __forceinline__ int v_offset(int t, int d) {
 // 4m .. 4m+3 of one block (a prefill chunk's tokens), one 8-byte run per dim
 // (the layout keeps 4 consecutive tokens of a dim together), otherwise
 // 2-byte stores per token.  Copies are integer moves: exact bits.  Slots
-// outside [0, num_slots) are skipped.
-template <int D>
+// outside [0, num_slots) are skipped.  BS: tokens per block of the pool
+// (slot s is offset s % BS of block s / BS).
+template <int D, int BS = kBlock>
 __device__ __forceinline__ void write_kv_thread(
     int64_t gid,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -65,16 +67,16 @@ __device__ __forceinline__ void write_kv_thread(
       vv[i] = *reinterpret_cast<const uint4*>(v + (tok0 + i) * v_stride + g * D + c * 8);
       const uint4 kv = *reinterpret_cast<const uint4*>(k + (tok0 + i) * k_stride + g * D + c * 8);
       if (s[i] >= 0 && s[i] < num_slots) {
-        const int64_t tile = ((s[i] >> 4) * Hkv + g) * (int64_t)(kBlock * D);
-        *reinterpret_cast<uint4*>(k_cache + tile + ((int64_t)c * 16 + (s[i] & 15)) * 8) = kv;
+        const int64_t tile = ((s[i] / BS) * Hkv + g) * (int64_t)(BS * D);
+        *reinterpret_cast<uint4*>(k_cache + tile + ((int64_t)c * BS + (s[i] % BS)) * 8) = kv;
       }
     }
   }
   const bool run = ntok == 4 && s[0] >= 0 && s[3] < num_slots && (s[0] & 3) == 0 &&
                    s[1] == s[0] + 1 && s[2] == s[0] + 2 && s[3] == s[0] + 3;
   if (run) {
-    const int64_t tile = ((s[0] >> 4) * Hkv + g) * (int64_t)(kBlock * D);
-    const int t0 = (int)(s[0] & 15);
+    const int64_t tile = ((s[0] / BS) * Hkv + g) * (int64_t)(BS * D);
+    const int t0 = (int)(s[0] % BS);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int d = c * 8 + j;
@@ -84,20 +86,20 @@ __device__ __forceinline__ void write_kv_thread(
       const uint32_t w2 = (&vv[2].x)[j >> 1] >> sh, w3 = (&vv[3].x)[j >> 1] >> sh;
       lo = (w0 & 0xffffu) | (w1 << 16);
       hi = (w2 & 0xffffu) | (w3 << 16);
-      *reinterpret_cast<uint2*>(v_cache + tile + v_offset<D>(t0, d)) = make_uint2(lo, hi);
+      *reinterpret_cast<uint2*>(v_cache + tile + v_offset<D, BS>(t0, d)) = make_uint2(lo, hi);
     }
     return;
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (i >= ntok || s[i] < 0 || s[i] >= num_slots) continue;
-    const int64_t tile = ((s[i] >> 4) * Hkv + g) * (int64_t)(kBlock * D);
-    const int t = (int)(s[i] & 15);
+    const int64_t tile = ((s[i] / BS) * Hkv + g) * (int64_t)(BS * D);
+    const int t = (int)(s[i] % BS);
     const uint32_t w[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int d = c * 8 + j;
-      v_cache[tile + v_offset<D>(t, d)] = (uint16_t)(w[j >> 1] >> ((j & 1) * 16));
+      v_cache[tile + v_offset<D, BS>(t, d)] = (uint16_t)(w[j >> 1] >> ((j & 1) * 16));
     }
   }
 }

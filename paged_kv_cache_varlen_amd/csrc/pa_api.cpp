@@ -959,6 +959,82 @@ pa_status pa_gather_kv(const void* k_cache, const void* v_cache,
   return ok();
 }
 
+pa_status pa_write_kv_bs(const void* k, const void* v, int64_t k_token_stride,
+                         int64_t v_token_stride, const int64_t* slot_mapping,
+                         int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                         void* k_cache, void* v_cache, int64_t num_blocks,
+                         int32_t block_size, void* stream) {
+  if (block_size != 8 && block_size != 16)
+    return fail(PA_ERR_UNSUPPORTED,
+                "pa_write_kv_bs: block_size must be 8 or 16 (larger blocks: 16-token "
+                "pools, see pa_expand_block_tables)");
+  pa_status s = check_scatter("pa_write_kv_bs", k, v, k_token_stride, v_token_stride,
+                              slot_mapping, num_tokens, num_kv_heads, head_dim, k_cache,
+                              v_cache, num_blocks);
+  if (s != PA_OK || num_tokens == 0) return s == PA_OK ? ok() : s;
+  hipError_t e = pa::launch_write_kv(
+      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), k_token_stride,
+      v_token_stride, slot_mapping, num_tokens, num_kv_heads, head_dim,
+      static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), num_blocks,
+      static_cast<hipStream_t>(stream), block_size);
+  if (e != hipSuccess) return hip_fail(e, "pa_write_kv_bs launch");
+  return ok();
+}
+
+pa_status pa_attend_bs(const void* q, const void* k_cache, const void* v_cache,
+                       int64_t num_blocks, int32_t block_size,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* seq_lens, const int32_t* query_start_loc,
+                       int32_t num_seqs, int64_t num_q_tokens, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t max_query_len,
+                       int32_t max_seq_len, float scale, void* out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (block_size != 8 && block_size != 16)
+    return fail(PA_ERR_UNSUPPORTED,
+                "pa_attend_bs: block_size must be 8 or 16 (larger blocks: 16-token "
+                "pools, see pa_expand_block_tables)");
+  pa::AttendArgs a;
+  bool empty;
+  pa_status s = prepare_attend(q, k_cache, v_cache, num_blocks, block_tables,
+                               max_blocks_per_seq, seq_lens, query_start_loc,
+                               num_seqs, num_q_tokens, num_q_heads, num_kv_heads,
+                               head_dim, max_query_len, max_seq_len, scale, out,
+                               workspace, workspace_bytes, true, &a, &empty);
+  if (s != PA_OK) return s;
+  if (empty) return ok();
+  a.block_size = block_size;
+  hipError_t e = pa::launch_plan(a, static_cast<hipStream_t>(stream));
+  if (e == hipSuccess) e = pa::launch_planned(a, static_cast<hipStream_t>(stream));
+  if (e == hipSuccess) e = pa::launch_merge(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pa_attend_bs launch");
+  return ok();
+}
+
+pa_status pa_gather_kv_bs(const void* k_cache, const void* v_cache, int64_t num_blocks,
+                          int32_t block_size, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                          const int64_t* kv_start, int32_t num_seqs, int64_t total_rows,
+                          int32_t num_kv_heads, int32_t head_dim, void* k_out,
+                          void* v_out, void* stream) {
+  if (block_size != 8 && block_size != 16)
+    return fail(PA_ERR_UNSUPPORTED, "pa_gather_kv_bs: block_size must be 8 or 16");
+  if (num_seqs < 0 || total_rows < 0 || num_blocks < 0 || max_blocks_per_seq < 0)
+    return fail(PA_ERR_SHAPE, "pa_gather_kv_bs: negative size");
+  if (num_kv_heads <= 0) return fail(PA_ERR_SHAPE, "num_kv_heads must be > 0");
+  if (!supported_head_dim(head_dim))
+    return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (total_rows == 0 || num_seqs == 0) return ok();
+  if (!k_cache || !v_cache || !block_tables || !seq_lens || !kv_start || !k_out || !v_out)
+    return fail(PA_ERR_NULL, "pa_gather_kv_bs: NULL pointer");
+  hipError_t e = pa::launch_gather_kv(
+      static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache),
+      num_blocks, block_tables, max_blocks_per_seq, seq_lens, kv_start, num_seqs,
+      total_rows, num_kv_heads, head_dim, static_cast<uint16_t*>(k_out),
+      static_cast<uint16_t*>(v_out), static_cast<hipStream_t>(stream), block_size);
+  if (e != hipSuccess) return hip_fail(e, "pa_gather_kv_bs launch");
+  return ok();
+}
+
 pa_status pa_validate_metadata_host(const int32_t* block_tables,
                                     int32_t max_blocks_per_seq,
                                     const int32_t* seq_lens,

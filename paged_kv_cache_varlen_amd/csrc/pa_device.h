@@ -169,12 +169,13 @@ inline WorkspaceLayout workspace_layout(int32_t num_seqs, int64_t num_q_tokens,
 
 // ---- launchers (defined in the .hip files) ---------------------------------
 
+// block_size: tokens per block of the pools, 16 or 8.
 hipError_t launch_write_kv(const uint16_t* k, const uint16_t* v,
                            int64_t k_stride, int64_t v_stride,
                            const int64_t* slot_mapping, int64_t num_tokens,
                            int num_kv_heads, int head_dim, uint16_t* k_cache,
                            uint16_t* v_cache, int64_t num_blocks,
-                           hipStream_t stream);
+                           hipStream_t stream, int block_size = kBlock);
 
 hipError_t launch_write_kv8(const uint16_t* k, const uint16_t* v,
                             int64_t k_stride, int64_t v_stride,
@@ -189,7 +190,7 @@ hipError_t launch_gather_kv(const uint16_t* k_cache, const uint16_t* v_cache,
                             const int64_t* kv_start, int32_t num_seqs,
                             int64_t total_rows, int num_kv_heads, int head_dim,
                             uint16_t* k_out, uint16_t* v_out,
-                            hipStream_t stream);
+                            hipStream_t stream, int block_size = kBlock);
 
 // Copy-on-write: copy whole blocks (every kv head) of both pools, for the
 // (src, dst) pairs of `mapping`; block_bytes = bytes of one block in a pool.
@@ -287,6 +288,7 @@ struct AttendArgs {
   bool kv8;        // 8-bit pools: E4M3 codes (k_cache, v_cache are uint8)
   float k_scale;   // value of a K code: code * k_scale (8-bit pools)
   float v_scale;   // value of a V code: code * v_scale (8-bit pools)
+  int block_size = kBlock;  // tokens per block-table entry: 16, or 8 (bf16 pools)
 };
 
 // Work plan into the workspace (one small kernel).

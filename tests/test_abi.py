@@ -117,6 +117,31 @@ def test_attend_noalloc_scratch_limit(lib):
     assert lib.pa_attend_workspace_size(129, 2048, 32, 8, 128, 1920, 8192) > limit
 
 
+@pytest.mark.parametrize("bs,status", [(4, _lib.PA_ERR_UNSUPPORTED),
+                                       (32, _lib.PA_ERR_UNSUPPORTED)])
+def test_block_size_calls_reject_other_sizes(lib, bs, status):
+    a = attend_args()
+    assert lib.pa_attend_bs(*(a[:4] + [bs] + a[4:])) == status
+    assert lib.pa_write_kv_bs(FAKE, FAKE, 256, 256, FAKE, 4, 2, 128, FAKE, FAKE, 8, bs,
+                              None) == status
+    assert lib.pa_gather_kv_bs(FAKE, FAKE, 8, bs, FAKE, 4, FAKE, FAKE, 2, 10, 2, 128, FAKE,
+                               FAKE, None) == status
+
+
+def test_block_size_8_argument_checks(lib):
+    # the checks of the block-size-16 calls apply unchanged
+    a = attend_args(D=96)
+    assert lib.pa_attend_bs(*(a[:4] + [8] + a[4:])) == _lib.PA_ERR_UNSUPPORTED
+    a = attend_args(wsb=100)
+    assert lib.pa_attend_bs(*(a[:4] + [8] + a[4:])) == _lib.PA_ERR_WORKSPACE
+    a = attend_args(T=0, q=None, out=None)
+    assert lib.pa_attend_bs(*(a[:4] + [8] + a[4:])) == _lib.PA_OK
+    assert lib.pa_write_kv_bs(None, FAKE, 256, 256, FAKE, 4, 2, 128, FAKE, FAKE, 8, 8,
+                              None) == _lib.PA_ERR_NULL
+    assert lib.pa_write_kv_bs(None, None, 256, 256, None, 0, 2, 128, None, None, 8, 8,
+                              None) == _lib.PA_OK
+
+
 def test_attend_empty_batch_is_ok(lib):
     assert lib.pa_attend(*attend_args(T=0, q=None, out=None)) == _lib.PA_OK
 
