@@ -1074,10 +1074,14 @@ __device__ __forceinline__ void load_lds_kib_lanes(uint64_t lane_addr, uint32_t 
 
 // Wait until at most N of this wave's vector memory loads are outstanding,
 // then meet the other waves of the workgroup.  (A compiler-level memory
-// barrier as well: LDS reads are not moved across it.)
+// barrier as well: LDS reads are not moved across it.)  LDS reads in flight
+// are not waited for: the only ones a wave can have here are of the stage
+// it computes next, which is not refilled at this barrier (every read of the
+// stage that is refilled was consumed, and so waited for, in the previous
+// step).
 template <int N>
 __device__ __forceinline__ void wait_loads_and_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 __device__ __forceinline__ bf16x8 lds16(const uint16_t* p) {
@@ -1927,12 +1931,16 @@ hipError_t launch_planned(const AttendArgs& a, hipStream_t stream) {
       fn = decode_only ? attend_decode_bs8_kernel<64> : attend_mixed_bs8_kernel<64>;
     slot = 8 + (decode_only ? 0 : 1) + (a.head_dim == 128 ? 0 : 2);
   }
-  // Persistent grid: every resident slot of every CU, never more waves than
-  // the work-unit bound.
+  // Persistent grid: every resident slot of every CU, never more workgroups
+  // than the work-unit bound (a decode unit takes one wave, a prefill unit a
+  // whole workgroup: bounding a mixed launch by units per wave left a
+  // prefill-only batch with about one workgroup per CU).
   const int64_t max_work =
       (a.ws.max_items + (a.cascade ? a.ws.max_pre_items : 0)) * a.num_kv_heads;
   int64_t wgs = (int64_t)a.num_cus * resident_wgs((const void*)fn, slot);
-  const int64_t need = (max_work + (kAttendThreads / 64) - 1) / (kAttendThreads / 64);
+  const int64_t need = decode_only
+                           ? (max_work + (kAttendThreads / 64) - 1) / (kAttendThreads / 64)
+                           : max_work;
   if (wgs > need) wgs = need;
   if (wgs < 1) wgs = 1;
   hipLaunchKernelGGL(fn, dim3((unsigned)wgs), dim3(kAttendThreads), 0, stream, P);
