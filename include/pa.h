@@ -608,15 +608,20 @@ pa_status pa_expand_block_tables(const int32_t *block_tables, int32_t num_seqs,
  * pa_mla_write_kv - scatter kv (device bf16, row i of 576 values at
  *   kv + i * kv_token_stride elements; stride a multiple of 8) into the cache
  *   at slot_mapping[i] (device int64; < 0 or >= num_blocks * 64: skipped).
- * pa_mla_workspace_size - workspace bytes of pa_mla_decode (split partials);
- *   0 for invalid arguments.
+ * pa_mla_workspace_size - workspace bytes of pa_mla_decode (per-token
+ *   records and the partial results of tokens whose keys are cut between
+ *   workgroups: at most two per workgroup); 0 for invalid arguments.
  * pa_mla_decode - q device bf16 [num_q_tokens][num_q_heads][576], out device
  *   bf16 [num_q_tokens][num_q_heads][512]; block_tables of 64-token block ids
  *   [num_seqs][max_blocks_per_seq]; seq_lens, query_start_loc as pa_attend;
- *   num_q_heads a multiple of 16, at most 128, and max_seq_len at most
- *   262144 (PA_ERR_UNSUPPORTED otherwise);
+ *   num_q_heads a multiple of 16, at most 128, max_seq_len at most 262144,
+ *   num_seqs at most 262144, num_q_tokens below 2^27 and num_blocks at most
+ *   2^30 (PA_ERR_UNSUPPORTED otherwise); query_start_loc non-decreasing;
  *   workspace >= pa_mla_workspace_size(...) bytes, 256-byte aligned.  A
  *   request whose metadata is out of bounds is skipped (its rows unwritten).
+ *   Two launches: the decode, then (when keys of a token can be cut between
+ *   workgroups) the fold of the pieces; calls sharing a workspace must be
+ *   ordered (one stream).
  */
 #define PA_MLA_BLOCK_SIZE 64
 #define PA_MLA_DIM 576

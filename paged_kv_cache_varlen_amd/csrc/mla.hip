@@ -3,42 +3,248 @@
 // in blocks of 64 tokens; decode attends MQA-style on the latent.
 //
 // Cache layout: block n holds 64 * 576 bf16; token t, dim d of the block is
-// element (((t / 16) * 18 + d / 32) * 16 + t % 16) * 32 + d % 32, so one
-// 16-token x 32-dim piece is 1 KiB contiguous: a wave loads the score operand
-// of 16 keys for one 32-dim k step with one 16-byte load per lane.
+// element (((t / 16) * 18 + d / 32) * 16 + t % 16) * 32 + d % 32.  A 16-token
+// sub-tile is 18 KiB of [32-dim chunk][16 tokens][32 dims] (one KiB piece per
+// chunk), so tokens 32s .. 32s+31 of a block (s = 0, 1) are 36 KiB contiguous.
 //
-// Decode (mla_decode_kernel): one workgroup of four waves per (query token,
-// key split, group of 16 query heads).  For each 16 keys, wave w loads the
-// 32-dim chunks it owns (latent chunks 4w .. 4w+3, and one rotary chunk for
-// w < 2), computes its share of S^T = K Q^T against the 16 heads, and adds
-// the other waves' shares through LDS; all run the same online softmax, and
-// wave w accumulates output dims 128w .. 128w+127.  The PV product needs each lane to
-// hold 4 consecutive keys of one dim, while the cache rows hold consecutive
-// dims of one key: an MFMA against a 0/1 selection matrix moves a 16-key x
-// 16-dim piece of the key operand into that form (exact: every product is
-// x * 1 or x * 0 and the sums have one nonzero term), so the latent is stored
-// and read once.
+// Decode (mla_decode_kernel).  The work is a stream of 32-key stages: the
+// requests in order, each query token of a request in order, the keys that
+// token sees in stages of 32.  The stream is cut into contiguous ranges of
+// R = ceil(stages / gridDim.x) stages, one per workgroup, so every workgroup
+// reads the same latent bytes whatever the mix of lengths; a token whose
+// keys are cut between workgroups leaves one partial result per workgroup,
+// folded by mla_merge_kernel.
+//
+// A workgroup has one wave per 16 query heads (for 16 and 32 heads, one wave
+// per (16 heads, quarter / half of the 512 output dims)).  Its stages pass
+// through a ring of four 36 KiB LDS buffers, filled three stages ahead by
+// global-to-LDS loads that the waves share; each wave then reads the stage
+// from LDS for
+//  - the scores S^T = K Q^T (MFMA 16x16x32, keys x heads): the key operand
+//    is one 16-byte LDS read per lane per 32-dim chunk and 16 keys, the
+//    query operand stays in registers;
+//  - the weighted sum O^T += V^T P^T over 32 keys per MFMA: the V^T operand
+//    (four consecutive keys of one dim per lane, where the cache holds
+//    consecutive dims of one key) comes from the LDS transpose read
+//    ds_read_b64_tr_b16, so the latent is fetched from HBM once and needs
+//    no transposed copy.
+// Each 1 KiB piece of a stage lands in LDS XOR-swizzled: the 16-byte granule
+// of (token k, 8-dim group g) sits at granule g * 16 + (k ^ (12 * (g & 1)))
+// of its piece, which keeps both LDS read patterns free of bank conflicts.
 #include "mfma_util.h"
 #include "pa_device.h"
 
 namespace pa {
-
 namespace {
 
+constexpr int kKc = kMlaDim / 32;              // 18 chunks of 32 dims
+constexpr int kSubBytes = 16 * kMlaDim * 2;    // 18 KiB: 16 tokens
+constexpr int kStageBytes = 2 * kSubBytes;     // 36 KiB: 32 tokens
+constexpr int kPieces = kStageBytes / 1024;    // 1 KiB loads per stage
+constexpr int kRing = 4;                       // LDS stage buffers
+constexpr int64_t kBlockElems = (int64_t)kMlaBlock * kMlaDim;
+// A new maximum is taken only when a score exceeds the one in use by more
+// than this (log2 units): the exponentials stay <= 2^8, and the rescale of
+// the accumulators is skipped for most stages.
+constexpr float kSlack = 8.0f;
 
-constexpr int kKc = kMlaDim / 32;      // 18 score k steps
-constexpr int kLatC = kMlaLatent / 32;  // 16 latent chunks of 32 dims
-constexpr int kMlaWaves = 4;
-constexpr int kMlaThreads = 64 * kMlaWaves;
-constexpr int kOwn = kLatC / kMlaWaves;  // latent chunks per wave
-constexpr int kMlaStages = 4;            // 16-key tiles in flight + 1
+// s_waitcnt lgkmcnt(0) (vmcnt and expcnt not waited), as an immediate the
+// compiler's own wait insertion sees.
+constexpr int kWaitLgkm0 = 0xC07F;
 
+static_assert(kStageBytes == kMlaStageKeys * kMlaDim * 2, "stage = 32 tokens");
 
-// Workgroup barrier after this wave's LDS writes have completed.  Unlike
-// __syncthreads() (a release/acquire fence, which also waits for every global
-// load in flight) it leaves the tile prefetches in flight.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+// Scalar-memory load of a wave-uniform address (tracked by lgkmcnt, not by
+// the vector-memory counter that orders the stage ring).
+template <class T>
+__device__ __forceinline__ T sload(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
+// Stages of tokens that see 1, 2, .., n keys: the sum of ceil(x / 32).
+__device__ __forceinline__ int64_t stage_prefix(int64_t n) {
+  if (n <= 0) return 0;
+  const int64_t m = n / kMlaStageKeys, r = n % kMlaStageKeys;
+  return (m + 1) * (16 * m + r);
+}
+
+// A request's metadata is in bounds: its tokens inside [0, T), Q <= L,
+// L <= max_seq_len and its blocks inside its block-table row.
+__device__ __forceinline__ bool req_ok(const MlaParams& P, int q0, int q1, int L) {
+  return q0 >= 0 && q1 >= q0 && q1 <= P.num_q_tokens && q1 - q0 <= L &&
+         L <= P.max_seq_len && (L + kMlaBlock - 1) / kMlaBlock <= P.bt_stride;
+}
+
+// Stages of request b (vector loads, one request per lane; 0 past the end
+// or out of bounds).  Query i of its Q tokens sees L - Q + 1 + i keys.
+__device__ __forceinline__ int64_t req_stages(const MlaParams& P, int b) {
+  if (b >= P.num_seqs) return 0;
+  const int q0 = P.qsl[b], q1 = P.qsl[b + 1], L = P.seq_lens[b];
+  if (!req_ok(P, q0, q1, L)) return 0;
+  return stage_prefix(L) - stage_prefix(L - (q1 - q0));
+}
+
+__device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)v >> 32), l);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Inclusive prefix sum over the wave's 64 lanes.
+__device__ __forceinline__ int64_t wave_scan(int64_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t u = __shfl_up(v, d);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+
+// Position in the stage stream: request b (metadata q0, Q, L), its token i,
+// stage j of that token's nst stages.  Every field is wave-uniform.
+struct Cursor {
+  int b, q0, Q, L;
+  int i, j, nst;
+};
+
+__device__ __forceinline__ int token_stages(const Cursor& c) {
+  return (c.L - c.Q + 1 + c.i + kMlaStageKeys - 1) / kMlaStageKeys;
+}
+
+// Metadata of the requests b0 .. b0 + 63, one per lane (loaded once), and
+// scalar loads past them.
+struct ReqWindow {
+  int b0, q0, q1, L;
+  __device__ __forceinline__ void get(const MlaParams& P, int b, int& rq0, int& rq1,
+                                      int& rL) const {
+    if (b - b0 < 64) {
+      rq0 = __builtin_amdgcn_readlane(q0, b - b0);
+      rq1 = __builtin_amdgcn_readlane(q1, b - b0);
+      rL = __builtin_amdgcn_readlane(L, b - b0);
+    } else {
+      rq0 = sload(P.qsl + b);
+      rq1 = sload(P.qsl + b + 1);
+      rL = sload(P.seq_lens + b);
+    }
+  }
+};
+
+// Next stage; past a request's last token the next request with tokens whose
+// metadata is in bounds.  Called only while stages remain, which the
+// stream's total guarantees; past num_seqs it stops on a dummy position,
+// never used.
+__device__ __forceinline__ void cursor_next(Cursor& c, const MlaParams& P,
+                                            const ReqWindow& win) {
+  if (++c.j < c.nst) return;
+  c.j = 0;
+  if (++c.i >= c.Q) {
+    c.i = 0;
+    for (;;) {
+      if (++c.b >= P.num_seqs) {
+        c.b = P.num_seqs - 1;
+        c.q0 = 0;
+        c.Q = 1;
+        c.L = 1;
+        break;
+      }
+      int q0, q1, L;
+      win.get(P, c.b, q0, q1, L);
+      if (q1 > q0 && req_ok(P, q0, q1, L)) {
+        c.q0 = q0;
+        c.Q = q1 - q0;
+        c.L = L;
+        break;
+      }
+    }
+  }
+  c.nst = token_stages(c);
+}
+
+// Global-to-LDS copy of one KiB: lane i reads 16 bytes at gaddr + voff and
+// writes them to LDS at laddr + 16 i (non-temporal: streamed once).  Inline
+// assembly, so that the compiler's wait insertion does not track it (it
+// would wait for every such load before any LDS read); the ring waits for
+// them itself.  M0 holds the LDS address; five wait states after writing it
+// and the SGPR address pair cover the hazards; M0 is restored.
+__device__ __forceinline__ void dma_kib(uint64_t gaddr, uint32_t voff, uint32_t laddr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 4\n\t"
+      "global_load_lds_dwordx4 %1, %2 nt\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(gaddr), "s"(laddr)
+      : "memory");
+}
+
+// Entries of a range's stage table: a key stage is block id * 2 + which 32
+// keys of the block (bit 31 clear); a query stage is kQStage | token << 3 |
+// k: the queries of head groups 2k, 2k + 1 of that token (36 KiB, or 18 for
+// a last odd head group), which precede the token's key stages.
+constexpr uint32_t kQStage = 0x80000000u;
+
+// This wave's share of a stage's loads: nl of its `pieces` one-KiB pieces,
+// p0 .. p0 + nl - 1 modulo pieces (past the end they repeat pieces another
+// wave also loads: the same bytes to the same place), so every wave issues
+// exactly nl loads per stage, key stage or query stage.
+__device__ __forceinline__ void dma_stage(const MlaParams& P, uint32_t e, uint32_t lstage,
+                                          uint32_t voff, int p0, int nl) {
+  uint64_t g;
+  int pieces;
+  uint32_t vo;
+  if (e & kQStage) {
+    const int64_t t = (e & ~kQStage) >> 3;
+    const int k = e & 7;
+    g = (uint64_t)(uintptr_t)(P.q + (t * P.Hq + 32 * k) * kMlaDim);
+    pieces = (P.Hq - 32 * k >= 32 ? 2 : 1) * kSubBytes / 1024;
+    vo = (uint32_t)(16 * (threadIdx.x & 63));
+  } else {
+    g = (uint64_t)(uintptr_t)(P.cache + (int64_t)(e >> 1) * kBlockElems) +
+        (uint64_t)(e & 1) * kStageBytes;
+    pieces = kPieces;
+    vo = voff;
+  }
+  for (int x = 0; x < nl; ++x) {
+    int p = p0 + x;
+    while (p >= pieces) p -= pieces;
+    dma_kib(g + (uint64_t)p * 1024, vo, lstage + (uint32_t)p * 1024);
+  }
+}
+
+// Wait until this wave has at most 2 nl (+ extra) ring loads in flight -- the
+// two stages issued after the one about to be read, plus the result stores
+// of a token finished in the last three stages, which count too -- then meet
+// the other waves: after the barrier every wave's share of the stage is in
+// LDS, and every wave has finished reading the buffer that is refilled next.
+// (No LDS read is outstanding here: each was consumed before.)
+#define MLA_WAIT(N) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory")
+template <int EXTRA>
+__device__ __forceinline__ void ring_wait(int nl, bool tail, bool stores) {
+  static_assert(24 + EXTRA <= 63, "vmcnt immediate");
+  if (tail) {
+    MLA_WAIT(0);
+    return;
+  }
+  switch (nl + (stores ? 100 : 0)) {
+    case 5: MLA_WAIT(10); break;
+    case 6: MLA_WAIT(12); break;
+    case 8: MLA_WAIT(16); break;
+    case 9: MLA_WAIT(18); break;
+    case 12: MLA_WAIT(24); break;
+    case 105: MLA_WAIT(10 + EXTRA); break;
+    case 106: MLA_WAIT(12 + EXTRA); break;
+    case 108: MLA_WAIT(16 + EXTRA); break;
+    case 109: MLA_WAIT(18 + EXTRA); break;
+    case 112: MLA_WAIT(24 + EXTRA); break;
+    default: MLA_WAIT(0); break;
+  }
+}
+#undef MLA_WAIT
+
+__device__ __forceinline__ s16x4 lds_read_tr(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
 }
 
 // Request of query token t: the last b with qsl[b] <= t (qsl non-decreasing,
@@ -60,17 +266,6 @@ __device__ __forceinline__ int request_of(const int32_t* qsl, int num_seqs, int 
   return lo;
 }
 
-// Keys token t sees (0 when its request's metadata is out of bounds).
-__device__ __forceinline__ int visible_keys(const MlaParams& P, int t, int* b_out) {
-  const int b = request_of(P.qsl, P.num_seqs, t);
-  const int q0 = P.qsl[b], q1 = P.qsl[b + 1], L = P.seq_lens[b];
-  *b_out = b;
-  if (q0 < 0 || t < q0 || t >= q1 || q1 - q0 > L || L > P.max_seq_len ||
-      (L + kMlaBlock - 1) / kMlaBlock > P.bt_stride)
-    return 0;
-  return L - (q1 - t) + 1;  // query t - q0 sits at L - Q + (t - q0)
-}
-
 __global__ __launch_bounds__(256) void mla_write_kv_kernel(
     const uint16_t* __restrict__ kv, int64_t stride, const int64_t* __restrict__ slots,
     int64_t num_tokens, uint16_t* __restrict__ cache, int64_t num_blocks) {
@@ -89,192 +284,404 @@ __global__ __launch_bounds__(256) void mla_write_kv_kernel(
       *reinterpret_cast<const uint4*>(kv + tok * stride + d);
 }
 
-__global__ __launch_bounds__(kMlaThreads, 2) void mla_decode_kernel(MlaParams P) {
-  // partial scores of the waves, two tiles deep
-  __shared__ f32x4 sx[2][kMlaWaves][64];
+// DQ waves per 16 heads (4, 2 or 1), each with 512 / DQ output dims.
+template <int DQ>
+__global__ __launch_bounds__(DQ == 1 ? 512 : 256) void mla_decode_kernel(MlaParams P) {
+  constexpr int kTiles = kMlaLatent / 16 / DQ;  // 16-dim output tiles per wave
+  // LDS reads are issued at most this many chunks / tiles ahead of their
+  // MFMAs: all of them would not fit in the registers beside the
+  // accumulators (128 of them with one wave per 16 heads)
+  constexpr int kScoreGroup = DQ == 1 ? 3 : 6;
+  constexpr int kPvGroup = DQ == 1 ? 4 : 8;
+  // With DQ waves per 16 heads, wave dq computes the scores over chunks
+  // [c0, c1) only (4 or 5 of 18 for DQ = 4, 9 for DQ = 2) and the partial
+  // sums are added through LDS in a fixed order, so all DQ waves hold the
+  // same scores without each reading the whole key tile.
+  constexpr int kMaxC = (kKc + DQ - 1) / DQ;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * kStageBytes];
+  // the range's stage table (query and key stages in stream order)
+  __shared__ uint32_t stab[kMlaMaxRange];
+  // partial scores of the waves (DQ > 1: 4 waves): [wave][half][lane]
+  __shared__ f32x4 xsc[DQ > 1 ? 4 : 1][2][64];
+
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = blockDim.x >> 6;
+  const int hg = w / DQ, dq = w % DQ;
   const int r = lane & 15, g = lane >> 4;
-  // Workgroup -> (unit u = (token, split), head group): workgroups are
-  // dealt to the 8 XCDs round-robin, so the head groups of one unit get
-  // indices with the same residue mod 8 (one XCD, one L2) and follow each
-  // other there.
-  const int nhg = P.Hq / 16;
-  const int rest = blockIdx.x >> 3;
-  const int hg = rest % nhg;
-  const int u = (rest / nhg) * 8 + (blockIdx.x & 7);
-  if (u >= P.num_q_tokens * P.max_splits) return;
-  const int s = u % P.max_splits;
-  const int t = u / P.max_splits;
-  int b;
-  const int nvis = visible_keys(P, t, &b);
-  const int nsplit = (nvis + P.split - 1) / P.split;
-  if (s >= nsplit) return;
-  const int k0 = s * P.split, k1 = min(nvis, k0 + P.split);
+  const int c0 = kKc * dq / DQ, nc = kKc * (dq + 1) / DQ - c0;  // this wave's score chunks
 
-  // Wave w owns latent chunks kOwn * w .. kOwn * w + kOwn - 1 (its output
-  // dims) and, for w < 2, rotary chunk 16 + w: its share of the 18 score k
-  // steps.  Its query operands: lane (r, g) of chunk c holds dims
-  // 32c + 8g .. +7 of head r.
-  const bool rot = w < kMlaDim / 32 - kLatC;
-  auto chunk = [&](int i) { return i < kOwn ? kOwn * w + i : kLatC + w; };
-  const uint16_t* qp = P.q + ((int64_t)t * P.Hq + hg * 16 + r) * kMlaDim + 8 * g;
-  bf16x8 qop[kOwn + 1];
-#pragma unroll
-  for (int i = 0; i < kOwn + 1; ++i)
-    if (i < kOwn || rot) qop[i] = *reinterpret_cast<const bf16x8*>(qp + 32 * chunk(i));
-  // 0/1 selection operands: E_j[k][n] = 1 where k = 16j + n (lane (r, g)
-  // holds rows 8g .. 8g+7 of column r)
-  bf16x8 sel[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) sel[j][i] = (__bf16)((8 * g + i == 16 * j + r) ? 1.0f : 0.0f);
-
-  // block ids of the split (at most 64), one per lane
-  const int jb0 = k0 / kMlaBlock;
-  const int nblk = (k1 + kMlaBlock - 1) / kMlaBlock - jb0;
-  int idv = 0;
-  if (lane < nblk) idv = P.bt[(int64_t)b * P.bt_stride + jb0 + lane];
-  idv = idv < 0 ? 0 : (idv >= P.num_blocks ? (int)(P.num_blocks - 1) : idv);
-
-  f32x4 acc[2 * kOwn];  // this wave's latent chunks x 2 dim tiles of 16
-#pragma unroll
-  for (int k = 0; k < 2 * kOwn; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mrun = -INFINITY, lsum = 0.0f;
-  const float c2 = P.scale_log2;
-
-  const int ntiles = (k1 - k0 + 15) / 16;  // 16-key tiles of the split
-  typedef bf16x8 Tile[kOwn + 1];
-  auto load_tile = [&](Tile& kop, int tile) {
-    const int key = k0 + 16 * tile;
-    const int id = __builtin_amdgcn_readlane(idv, (key / kMlaBlock) - jb0);
-    // the piece of (16-key tile, chunk) is [16 tokens][32 dims]: lane (r, g)
-    // reads token r, dims 8g .. 8g+7
-    const uint16_t* base = P.cache + (int64_t)id * kMlaBlock * kMlaDim +
-                           ((key % kMlaBlock) >> 4) * kKc * 512 + r * 32 + g * 8;
-    // one head group: every tile is read once (non-temporal); several: the
-    // other groups' workgroups on this XCD read it again from L2
-#pragma unroll
-    for (int i = 0; i < kOwn + 1; ++i)
-      if (i < kOwn || rot) {
-        const bf16x8* src = reinterpret_cast<const bf16x8*>(base + chunk(i) * 512);
-        kop[i] = nhg == 1 ? __builtin_nontemporal_load(src) : *src;
-      }
-  };
-  auto compute = [&](const Tile& kop, int tile) {
-    const int key0 = k0 + 16 * tile;
-    // this wave's share of the scores; every wave then adds the shares of
-    // all waves in the same order, so all hold the same sums
-    f32x4 part = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < kOwn; ++i) part = mfma32(kop[i], qop[i], part);
-    if (rot) part = mfma32(kop[kOwn], qop[kOwn], part);
-    sx[tile & 1][w][lane] = part;
-    lds_barrier();
-    f32x4 sc = sx[tile & 1][0][lane];
-#pragma unroll
-    for (int v = 1; v < kMlaWaves; ++v) sc += sx[tile & 1][v][lane];
-    float x[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = (key0 + 4 * g + i < k1) ? sc[i] : -INFINITY;
-    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    mx = column_max(mx);
-    const float mnew = fmaxf(mrun, mx * c2);
-    const float muse = (mnew == -INFINITY) ? 0.0f : mnew;
-    const float alpha = __builtin_amdgcn_exp2f(mrun - muse);
-    mrun = mnew;
-    bf16x4 p;
-    float psum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(x[i], c2, -muse));
-      psum += (float)p[i];
-    }
-    lsum = lsum * alpha + psum;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-#pragma unroll
-      for (int k = 0; k < 2 * kOwn; ++k) acc[k] *= alpha;
-    }
-    // keys past the split end may be unwritten slots: their V rows are zeroed
-    // (a 0 weight must not meet a NaN)
-#pragma unroll
-    for (int cc = 0; cc < kOwn; ++cc) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const f32x4 tv = mfma32(kop[cc], sel[j], f32x4{0.f, 0.f, 0.f, 0.f});
-        bf16x4 v;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          v[i] = (key0 + 4 * g + i < k1) ? (__bf16)tv[i] : (__bf16)0.0f;
-        acc[2 * cc + j] = mfma16(v, p, acc[2 * cc + j]);
-      }
-    }
-  };
-  // Ring of kMlaStages tiles: the loads of tile i + kMlaStages - 1 are issued
-  // before tile i is computed (prefetches past the end repeat the last tile);
-  // every wave runs the same steps (one barrier each).
-  Tile ring[kMlaStages];
-#pragma unroll
-  for (int k = 0; k < kMlaStages - 1; ++k) load_tile(ring[k], min(k, ntiles - 1));
-  for (int i = 0; i < ntiles; i += kMlaStages) {
-#pragma unroll
-    for (int k = 0; k < kMlaStages; ++k) {
-      load_tile(ring[(k + kMlaStages - 1) % kMlaStages],
-                min(i + k + kMlaStages - 1, ntiles - 1));
-      if (i + k < ntiles) compute(ring[k], i + k);
+  // ---- records of tokens that no in-bounds request holds ----------------
+  // (tokens t = w, w + grid, ..; every other token's record is written by
+  // the workgroup holding its first stage, so each launch writes every
+  // record once)
+  if (P.seg && w == nw - 1) {
+    for (int64_t t = blockIdx.x; t < P.num_q_tokens; t += gridDim.x) {
+      const int b = request_of(P.qsl, P.num_seqs, (int)t);
+      const int q0 = P.qsl[b], q1 = P.qsl[b + 1], L = P.seq_lens[b];
+      if (!(req_ok(P, q0, q1, L) && t >= q0 && t < q1) && lane == 0) P.seg[t] = make_int2(0, 0);
     }
   }
 
-  float l = lsum;
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  const int h = hg * 16 + r;
-  const int dim0 = 32 * kOwn * w + 4 * g;
-  if (nsplit == 1) {
-    const float inv = 1.0f / l;
-    uint16_t* op = P.out + ((int64_t)t * P.Hq + h) * kMlaLatent + dim0;
-#pragma unroll
-    for (int k = 0; k < 2 * kOwn; ++k) {
-      bf16x4 o;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = (__bf16)(acc[k][i] * inv);
-      *reinterpret_cast<bf16x4*>(op + 16 * k) = o;
+  // ---- this workgroup's range [I0, I1) of the stage stream --------------
+  // Each lane totals a contiguous run of C requests; a scan over the lanes
+  // gives the stream length M and the run holding stage I0, whose requests
+  // a second scan walks.  (Every wave computes the same.)
+  const int C = (P.num_seqs + 63) / 64;
+  int64_t tot = 0;
+#pragma unroll 4
+  for (int k = 0; k < C; ++k) tot += req_stages(P, lane * C + k);
+  const int64_t incl = wave_scan(tot);
+  const int64_t M = readlane64(incl, 63);
+  const int64_t R = (M + gridDim.x - 1) / gridDim.x;
+  const int64_t I0 = min((int64_t)blockIdx.x * R, M);
+  const int64_t I1 = min(I0 + R, M);
+  if (I0 >= I1 || I1 - I0 > kMlaMaxRange) return;
+  const int nreal = (int)(I1 - I0);  // key stages of the range
+  const int lam = __builtin_ctzll(__builtin_amdgcn_ballot_w64(incl > I0));
+  int64_t carry = readlane64(incl - tot, lam);
+  int b0 = -1;
+  int64_t s0 = 0;
+  for (int k0 = 0; k0 < C; k0 += 64) {
+    const int64_t it = k0 + lane < C ? req_stages(P, lam * C + k0 + lane) : 0;
+    const int64_t inc = wave_scan(it) + carry;
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(inc > I0);
+    if (hit) {
+      const int x = __builtin_ctzll(hit);
+      b0 = lam * C + k0 + x;
+      s0 = I0 - (readlane64(inc, x) - readlane64(it, x));
+      break;
     }
+    carry = readlane64(inc, 63);
+  }
+  b0 = __builtin_amdgcn_readfirstlane(b0);
+  if (b0 < 0) return;
+
+  ReqWindow win;
+  win.b0 = b0;
+  {
+    const int b = b0 + lane;
+    const bool in = b < P.num_seqs;
+    win.q0 = in ? P.qsl[b] : 0;
+    win.q1 = in ? P.qsl[b + 1] : 0;
+    win.L = in ? P.seq_lens[b] : 0;
+  }
+  Cursor cur;
+  cur.b = b0;
+  {
+    int q0, q1, L;
+    win.get(P, b0, q0, q1, L);
+    cur.q0 = q0;
+    cur.Q = q1 - q0;
+    cur.L = L;
+    // token: the first i whose stages end past s0
+    const int64_t before = stage_prefix(cur.L - cur.Q);
+    int lo = 0, hi = cur.Q - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (stage_prefix(cur.L - cur.Q + 1 + mid) - before > s0)
+        hi = mid;
+      else
+        lo = mid + 1;
+    }
+    cur.i = lo;
+    cur.j = (int)(s0 - (stage_prefix(cur.L - cur.Q + lo) - before));
+    cur.nst = token_stages(cur);
+  }
+
+  // ---- lane constants of the LDS layout ---------------------------------
+  // key operand: lane (r, g) reads token r, dims 8g .. 8g+7 of a chunk
+  const int offK = (g * 16 + (r ^ (12 * (g & 1)))) * 16;
+  // V^T operand: the transpose read gives lane (g, r) element e from the
+  // 8 bytes lane 16g + 4e + r / 4 points at, element r % 4; lane
+  // 16g + 4e + q therefore points at token 4g + e, dims 4q .. 4q+3 of the
+  // 16-dim tile, and lane (r, g) receives tokens 4g .. 4g+3 of dim r.
+  const int vq = lane & 3, ve = (lane >> 2) & 3, vh = vq >> 1;
+  const int offV = (vh * 16 + ((4 * g + ve) ^ (12 * vh))) * 16 + 8 * (vq & 1) +
+                   512 * (dq * kTiles);
+  // ring loads: lane i fetches granule (token (i % 16) ^ (12 (g & 1)), g) of
+  // a key piece (bytes 16 i .. of a query piece)
+  const uint32_t voff = (uint32_t)(((r ^ (12 * (g & 1))) * 64) + g * 16);
+  const int nl = (kPieces + nw - 1) / nw;
+  const int p0 = w * nl;
+  const uint32_t lring =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)ring;
+
+  // ---- the first token's query stages: issued before the table is built -
+  const int qs = (P.Hq + 31) / 32;  // query stages per token
+  const int pre = min(qs, kRing - 1);
+  for (int k = 0; k < pre; ++k)
+    dma_stage(P, kQStage | ((uint32_t)(cur.q0 + cur.i) << 3) | (uint32_t)k,
+              lring + k * kStageBytes, voff, p0, nl);
+
+  // ---- the range's stage table (wave 0; one gather) -----------------------
+  // Token by token: its query stages, then (request - b0) << 13 | stage of
+  // each key stage; then each lane turns its key entries into block ids
+  // with one block-table load each.
+  constexpr int kCap = kMlaMaxRange - 1;  // the last slot holds the count
+  if (w == 0) {
+    Cursor f = cur;
+    int x = 0;
+    for (int done = 0; done < nreal;) {
+      if (x + qs + min(f.nst - f.j, nreal - done) > kCap) {
+        x = -1;  // cannot happen with the launch's grid: it bounds R
+        break;
+      }
+      if (lane < qs) stab[x + lane] = kQStage | ((uint32_t)(f.q0 + f.i) << 3) | (uint32_t)lane;
+      x += qs;
+      const int cnt = min(f.nst - f.j, nreal - done);
+      for (int y = lane; y < cnt; y += 64)
+        stab[x + y] = ((uint32_t)(f.b - b0) << 13) | (uint32_t)(f.j + y);
+      x += cnt;
+      done += cnt;
+      if (done < nreal) {
+        f.j = f.nst - 1;
+        cursor_next(f, P, win);
+      }
+    }
+#pragma unroll 4
+    for (int y = lane; y < x; y += 64) {
+      const uint32_t v = stab[y];
+      if (v & kQStage) continue;
+      const int b = b0 + (int)(v >> 13), j = (int)(v & 8191);
+      int id = P.bt[(int64_t)b * P.bt_stride + (j >> 1)];
+      id = id < 0 ? 0 : (id >= P.num_blocks ? (int)(P.num_blocks - 1) : id);
+      stab[y] = ((uint32_t)id << 1) | (uint32_t)(j & 1);
+    }
+    if (lane == 0) stab[kCap] = (uint32_t)x;
+  }
+  // (an LDS-only barrier: __syncthreads() would also wait for the ring
+  // loads just issued)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  const int n = (int)__builtin_amdgcn_readfirstlane(stab[kCap]);
+  if (n <= 0) {  // (no LDS write of the ring may outlive the workgroup)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     return;
   }
-  const int64_t row = ((int64_t)t * P.Hq + h) * P.max_splits + s;
-  float* ap = P.part_acc + row * kMlaLatent + dim0;
+
+  // ---- rest of the prologue: entries pre .. kRing - 2 ---------------------
+  for (int k = pre; k < kRing - 1 && k < n; ++k)
+    dma_stage(P, __builtin_amdgcn_readfirstlane(stab[k]), lring + k * kStageBytes, voff, p0,
+              nl);
+
+  int stored = 0;         // ring waits left that allow for result stores
+  int done = 0;           // key stages computed
+  bool first_tok = true;  // the piece is of the range's first token
+  const float c2 = P.scale_log2;
+  int it = 0;             // table entry
+  // Before entry `it` is read: wait for it (and meet the other waves), then
+  // refill the buffer every wave has finished with.
+  auto ring_step = [&]() {
+    ring_wait<kTiles>(nl, it + kRing - 2 >= n, stored > 0);
+    if (stored > 0) --stored;
+    if (it + kRing - 1 < n)
+      dma_stage(P, __builtin_amdgcn_readfirstlane(stab[it + kRing - 1]),
+                lring + (uint32_t)((it + kRing - 1) % kRing) * kStageBytes, voff, p0, nl);
+  };
+
+  // One token's piece of the range per pass: its query stages, then its key
+  // stages.  (The query operand lives within a pass.)
+  while (done < nreal) {
+    bf16x8 qop[kMaxC];  // lane (r, g): head 16 hg + r, dims 32 (c0 + i) + 8g .. +7
+    for (int k = 0; k < qs; ++k, ++it) {
+      ring_step();
+      if (k == (hg >> 1)) {
+        // lane (r, g): head 16 (hg % 2) + r, dims 8g .. of each chunk
+        const uint8_t* st = ring + (it % kRing) * kStageBytes + (hg & 1) * kSubBytes +
+                            r * (kMlaDim * 2) + g * 16 + c0 * 64;
 #pragma unroll
-  for (int k = 0; k < 2 * kOwn; ++k) *reinterpret_cast<f32x4*>(ap + 16 * k) = acc[k];
-  if (w == 0 && g == 0) P.part_ml[row] = make_float2(mrun, l);
+        for (int i = 0; i < kMaxC; ++i)
+          if (i < nc) qop[i] = *reinterpret_cast<const bf16x8*>(st + i * 64);
+        // the copies land before the buffer can be refilled
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      }
+    }
+    const int cnt = min(cur.nst - cur.j, nreal - done);
+    f32x4 acc[kTiles];
+#pragma unroll
+    for (int k = 0; k < kTiles; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float mrun = -INFINITY, lsum = 0.0f;
+    for (int ks = 0; ks < cnt; ++ks, ++it) {
+      ring_step();
+      const int j = cur.j + ks;  // stage of the token
+      const uint8_t* st = ring + (it % kRing) * kStageBytes;
+      // scores of the stage's two 16-key halves
+      f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < kMaxC; ++i) {
+        if (i < nc) {
+          const uint8_t* kp = st + (c0 + i) * 1024 + offK;
+          sa = mfma32(*reinterpret_cast<const bf16x8*>(kp), qop[i], sa);
+          sb = mfma32(*reinterpret_cast<const bf16x8*>(kp + kSubBytes), qop[i], sb);
+        }
+        if (i % kScoreGroup == kScoreGroup - 1) __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (DQ > 1) {
+        // add the head group's partial sums in wave order (the same sums in
+        // every wave); the writes land before the barrier, and every wave
+        // has read them before the next stage's barrier
+        xsc[w][0][lane] = sa;
+        xsc[w][1][lane] = sb;
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        const int w0 = hg * DQ;  // the head group's first wave
+        sa = xsc[w0][0][lane];
+        sb = xsc[w0][1][lane];
+#pragma unroll
+        for (int v = 1; v < DQ; ++v) {
+          sa += xsc[w0 + v][0][lane];
+          sb += xsc[w0 + v][1][lane];
+        }
+      }
+      // online softmax over the 32 keys (lane (r, g): keys 4g .. 4g+3 of each
+      // half, head r); keys the token does not see get -inf
+      const int nvis = cur.L - cur.Q + 1 + cur.i;
+      const int key0 = kMlaStageKeys * j + 4 * g;
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        y[e] = key0 + e < nvis ? sa[e] * c2 : -INFINITY;
+        y[4 + e] = key0 + 16 + e < nvis ? sb[e] * c2 : -INFINITY;
+      }
+      float mx = y[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, y[e]);
+      mx = column_max(mx);
+      if (__builtin_amdgcn_ballot_w64(mx > mrun + kSlack) != 0) {
+        const float mnew = fmaxf(mrun, mx);
+        const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);  // 0 on the first stage
+#pragma unroll
+        for (int k = 0; k < kTiles; ++k) acc[k] *= alpha;
+        lsum *= alpha;
+        mrun = mnew;
+      }
+      bf16x8 pp;
+      float ps = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pp[e] = (__bf16)__builtin_amdgcn_exp2f(y[e] - mrun);
+        ps += (float)pp[e];
+      }
+      lsum += ps;
+      // weighted sum; in a stage the token does not see to its end the V rows
+      // of the unseen keys (possibly unwritten slots: a 0 weight must not meet
+      // a NaN) are first zeroed in LDS.  Every wave writes the same zeros, and
+      // its own reads follow its own writes (LDS operations of a wave complete
+      // in order), so no barrier is needed.
+      if (kMlaStageKeys * j + kMlaStageKeys > nvis) {
+        const int kv = nvis - kMlaStageKeys * j;  // keys of the stage it sees
+        uint8_t* sw = ring + (it % kRing) * kStageBytes;
+        for (int q = lane; q < 2 * (kMlaLatent / 32) * 64; q += 64) {
+          const int u = q >> 10, c = (q >> 6) & 15, pos = q & 63;
+          const int key = 16 * u + ((pos & 15) ^ (12 * ((pos >> 4) & 1)));
+          if (key >= kv)
+            *reinterpret_cast<u32x4*>(sw + u * kSubBytes + c * 1024 + pos * 16) =
+                u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < kTiles; ++mt) {
+        // one whole-vector shuffle: assembled element by element, the
+        // operand was compiled to copies of each read's first dword
+        const bf16x8 a = __builtin_shufflevector(
+            __builtin_bit_cast(bf16x4, lds_read_tr(st + 512 * mt + offV)),
+            __builtin_bit_cast(bf16x4, lds_read_tr(st + kSubBytes + 512 * mt + offV)), 0, 1, 2,
+            3, 4, 5, 6, 7);
+        acc[mt] = mfma32(a, pp, acc[mt]);
+        if (mt % kPvGroup == kPvGroup - 1) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    // the token's piece is done: its output, or its partial
+    const bool whole = cur.j == 0 && cur.j + cnt == cur.nst;
+    float l = lsum;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const int t = cur.q0 + cur.i;
+    const int h = hg * 16 + r;
+    const int dim0 = dq * kTiles * 16 + 4 * g;
+    if (whole) {
+      const float inv = 1.0f / l;
+      uint16_t* op = P.out + ((int64_t)t * P.Hq + h) * kMlaLatent + dim0;
+#pragma unroll
+      for (int k = 0; k < kTiles; ++k) {
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (__bf16)(acc[k][e] * inv);
+        *reinterpret_cast<bf16x4*>(op + 16 * k) = o;
+      }
+    } else {
+      // slot 2w: the range's first token; 2w + 1: its last (only these two
+      // can be cut)
+      const int64_t row = (2 * (int64_t)blockIdx.x + (first_tok ? 0 : 1)) * P.Hq + h;
+      float* ap = P.part_acc + row * kMlaLatent + dim0;
+#pragma unroll
+      for (int k = 0; k < kTiles; ++k) *reinterpret_cast<f32x4*>(ap + 16 * k) = acc[k];
+      if (dq == 0 && g == 0) P.part_ml[row] = make_float2(mrun, l);
+    }
+    // the workgroup holding the token's first stage records which workgroups
+    // hold its pieces: this one, then whole ranges, the last one (R stages
+    // each) ending at or after the token's last stage
+    if (cur.j == 0 && threadIdx.x == 0 && P.seg) {
+      const int64_t last = I0 + done + cur.nst - 1;
+      const int pieces = (int)(last / R - blockIdx.x + 1);
+      P.seg[t] = make_int2((int)blockIdx.x, 2 * pieces + (first_tok ? 0 : 1));
+    }
+    stored = kRing - 1;
+    first_tok = false;
+    done += cnt;
+    if (done < nreal) {
+      cur.j = cur.nst - 1;
+      cursor_next(cur, P, win);
+    }
+  }
 }
 
-// One wave per (query token, head) whose keys were split: online log-sum-exp
-// over its splits in order; lane i holds dims 8i .. 8i+7.
+// One wave per (query token, head) whose keys were cut between workgroups:
+// log-sum-exp over the pieces.  The lanes first read the pieces' (max, sum)
+// in parallel (64 pieces per round), then every lane adds its 8 dims of each
+// piece's sums (independent loads); lane i holds dims 8i .. 8i+7.  The decode
+// writes every token's record in every launch ((0, 0) for tokens of
+// out-of-bounds requests), so no stale record is read.
 __global__ __launch_bounds__(256) void mla_merge_kernel(MlaParams P) {
   const int lane = threadIdx.x & 63;
   const int64_t row0 = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row0 >= (int64_t)P.num_q_tokens * P.Hq) return;
-  const int t = (int)(row0 / P.Hq);
-  int b;
-  const int nvis = visible_keys(P, t, &b);
-  const int nsplit = (nvis + P.split - 1) / P.split;
-  if (nsplit < 2 || nsplit > P.max_splits) return;
+  const int t = (int)(row0 / P.Hq), h = (int)(row0 % P.Hq);
+  // pieces: the first in slot 2 w0 + flag (flag: the token was not the
+  // first of w0's range), the others in slots 2 (w0 + s) (their ranges
+  // begin inside the token)
+  const int2 sg = P.seg[t];
+  const int pieces = sg.y >> 1;
+  if (pieces < 2 || sg.x < 0 || sg.x > P.grid - pieces) return;
+  auto row_of = [&](int s) -> int64_t {
+    const int64_t slot = s == 0 ? 2 * (int64_t)sg.x + (sg.y & 1) : 2 * ((int64_t)sg.x + s);
+    return slot * P.Hq + h;
+  };
   float M = -INFINITY, den = 0.0f;
   f32x4 n0 = {0.f, 0.f, 0.f, 0.f}, n1 = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < nsplit; ++s) {
-    const int64_t row = row0 * P.max_splits + s;
-    const float2 ml = P.part_ml[row];
-    const f32x4* ap = reinterpret_cast<const f32x4*>(P.part_acc + row * kMlaLatent + 8 * lane);
-    const f32x4 a0 = ap[0], a1 = ap[1];
-    const float mn = fmaxf(M, ml.x);
-    const float mu = (mn == -INFINITY) ? 0.0f : mn;
-    const float c_old = __builtin_amdgcn_exp2f(M - mu);
-    const float c_new = __builtin_amdgcn_exp2f(ml.x - mu);
-    den = den * c_old + ml.y * c_new;
-    n0 = n0 * c_old + a0 * c_new;
-    n1 = n1 * c_old + a1 * c_new;
+  for (int s0 = 0; s0 < pieces; s0 += 64) {
+    const int cnt = min(64, pieces - s0);
+    float2 ml = make_float2(-INFINITY, 0.0f);
+    if (lane < cnt) ml = P.part_ml[row_of(s0 + lane)];
+    float mx = ml.x;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
+    const float mn = fmaxf(M, mx);  // finite: every piece saw a key
+    const float c_old = __builtin_amdgcn_exp2f(M - mn);
+    const float c = lane < cnt ? __builtin_amdgcn_exp2f(ml.x - mn) : 0.0f;
+    float dl = c * ml.y;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) dl += __shfl_xor(dl, d);
+    den = den * c_old + dl;
+    n0 *= c_old;
+    n1 *= c_old;
+    for (int k = 0; k < cnt; ++k) {
+      const float ck = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(c), k));
+      const f32x4* ap =
+          reinterpret_cast<const f32x4*>(P.part_acc + row_of(s0 + k) * kMlaLatent + 8 * lane);
+      n0 += ap[0] * ck;
+      n1 += ap[1] * ck;
+    }
     M = mn;
   }
   const float inv = 1.0f / den;
@@ -301,12 +708,17 @@ hipError_t launch_mla_write_kv(const uint16_t* kv, int64_t stride, const int64_t
 
 hipError_t launch_mla_decode(const MlaParams& P, hipStream_t stream) {
   if (P.num_q_tokens == 0 || P.num_seqs == 0) return hipSuccess;
-  const int64_t units = (int64_t)P.num_q_tokens * P.max_splits;
-  const int64_t wgs = (units + 7) / 8 * 8 * (P.Hq / 16);
-  hipLaunchKernelGGL(mla_decode_kernel, dim3((unsigned)wgs), dim3(kMlaThreads), 0,
-                     stream, P);
+  const int hgs = P.Hq / 16;  // 1 .. 8
+  const int dq = hgs == 1 ? 4 : (hgs == 2 ? 2 : 1);
+  const dim3 block(64 * hgs * dq), grid((unsigned)P.grid);
+  if (dq == 4)
+    hipLaunchKernelGGL(mla_decode_kernel<4>, grid, block, 0, stream, P);
+  else if (dq == 2)
+    hipLaunchKernelGGL(mla_decode_kernel<2>, grid, block, 0, stream, P);
+  else
+    hipLaunchKernelGGL(mla_decode_kernel<1>, grid, block, 0, stream, P);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || P.max_splits < 2) return e;
+  if (e != hipSuccess || P.grid < 2) return e;
   const int64_t rows = (int64_t)P.num_q_tokens * P.Hq;
   hipLaunchKernelGGL(mla_merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
                      stream, P);

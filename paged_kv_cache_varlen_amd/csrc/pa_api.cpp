@@ -890,6 +890,12 @@ pa_status pa_mla_decode(const void* q, const void* cache, int64_t num_blocks,
     return fail(PA_ERR_SHAPE, "pa_mla_decode: num_q_tokens too large");
   if (max_seq_len > (1 << 18))
     return fail(PA_ERR_UNSUPPORTED, "pa_mla_decode: max_seq_len above 262144");
+  if (num_seqs > pa::kMlaMaxSeqs)
+    return fail(PA_ERR_UNSUPPORTED, "pa_mla_decode: num_seqs above 262144");
+  if (num_q_tokens >= pa::kMlaMaxTokens)
+    return fail(PA_ERR_UNSUPPORTED, "pa_mla_decode: num_q_tokens of 2^27 or more");
+  if (num_blocks > (int64_t(1) << 30))
+    return fail(PA_ERR_UNSUPPORTED, "pa_mla_decode: num_blocks above 2^30");
   if (num_q_tokens == 0 || num_seqs == 0) return ok();
   if (!q || !cache || !block_tables || !seq_lens || !query_start_loc || !out)
     return fail(PA_ERR_NULL, "pa_mla_decode: NULL pointer");
@@ -900,9 +906,9 @@ pa_status pa_mla_decode(const void* q, const void* cache, int64_t num_blocks,
   if (((uintptr_t)q | (uintptr_t)cache | (uintptr_t)out) & 15)
     return fail(PA_ERR_SHAPE, "q, out and the cache must be 16-byte aligned");
   const pa::MlaLayout m = pa::mla_layout(num_q_tokens, num_q_heads, max_seq_len);
-  if (((int64_t)num_q_tokens * m.max_splits + 7) / 8 * 8 * (num_q_heads / 16) > INT32_MAX)
-    return fail(PA_ERR_SHAPE, "pa_mla_decode: too many (token, split) units");
-  if (m.max_splits > 1) {
+  if (((int64_t)num_q_tokens * num_q_heads + 3) / 4 > INT32_MAX)
+    return fail(PA_ERR_SHAPE, "pa_mla_decode: too many (token, head) rows");
+  if (m.grid > 1) {
     if (!workspace || workspace_bytes < m.total)
       return fail(PA_ERR_WORKSPACE, "pa_mla_decode: workspace needs " +
                                         std::to_string(m.total) + " bytes, got " +
@@ -922,13 +928,13 @@ pa_status pa_mla_decode(const void* q, const void* cache, int64_t num_blocks,
   P.num_q_tokens = (int32_t)num_q_tokens;
   P.Hq = num_q_heads;
   P.max_seq_len = max_seq_len;
-  P.split = m.split;
-  P.max_splits = m.max_splits;
+  P.grid = m.grid;
   P.scale_log2 = scale * 1.4426950408889634f;
   P.out = static_cast<uint16_t*>(out);
   char* ws = static_cast<char*>(workspace);
-  P.part_ml = m.max_splits > 1 ? reinterpret_cast<float2*>(ws + m.part_ml) : nullptr;
-  P.part_acc = m.max_splits > 1 ? reinterpret_cast<float*>(ws + m.part_acc) : nullptr;
+  P.seg = m.grid > 1 ? reinterpret_cast<int2*>(ws + m.seg) : nullptr;
+  P.part_ml = m.grid > 1 ? reinterpret_cast<float2*>(ws + m.part_ml) : nullptr;
+  P.part_acc = m.grid > 1 ? reinterpret_cast<float*>(ws + m.part_acc) : nullptr;
   hipError_t e = pa::launch_mla_decode(P, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "pa_mla_decode launch");
   return ok();

@@ -221,21 +221,31 @@ struct MlaParams {
   int32_t num_q_tokens;
   int32_t Hq;
   int32_t max_seq_len;
-  int32_t split;       // keys per split (a multiple of 64)
-  int32_t max_splits;  // splits of a max_seq_len-key token
+  int32_t grid;        // decode workgroups (equal ranges of the stage stream)
   float scale_log2;
   uint16_t* out;       // [T][Hq][512]
-  float2* part_ml;     // [T][Hq][max_splits]
-  float* part_acc;     // [T][Hq][max_splits][512]
+  int2* seg;           // [T]: (first workgroup, 2 * workgroups + slot flag)
+  float2* part_ml;     // [2 grid][Hq]: (running max, sum) of a piece
+  float* part_acc;     // [2 grid][Hq][512]: unnormalised sums of a piece
 };
 
-// Key split of the MLA decode: at most 64 splits (and at most 64 blocks, one
-// block id per lane: max_seq_len <= 262144); at least 512 keys for 16 heads
-// (longer streams per workgroup), 256 for more heads (more workgroups share
-// each tile through L2).
+// The decode's work is a stream of 32-key stages (each query token's keys in
+// stages of 32), cut into ranges of R = ceil(stages / grid) stages, one per
+// workgroup; in a workgroup's table each token of its range also takes
+// ceil(Hq / 32) query stages.  grid: 256 (one 160 KiB-LDS workgroup per
+// compute unit), more when a range's table could exceed kMlaMaxRange - 1
+// entries, never more than the stages there can be.  Only a range's first
+// and last token can be cut, so a workgroup leaves at most two partial
+// results (slots 2w and 2w + 1).  One workgroup sees every stage: no
+// partials (the workspace is then a nominal 256 bytes, never touched).
+constexpr int kMlaStageKeys = 32;
+constexpr int kMlaGridFloor = 256;
+constexpr int kMlaMaxRange = 2048;
+constexpr int kMlaMaxSeqs = 1 << 18;          // request index in a table entry: 18 bits
+constexpr int64_t kMlaMaxTokens = 1 << 27;    // token index in a table entry: 28 bits
 struct MlaLayout {
-  int32_t split;
-  int32_t max_splits;
+  int32_t grid;
+  size_t seg;
   size_t part_ml;
   size_t part_acc;
   size_t total;
@@ -243,16 +253,23 @@ struct MlaLayout {
 inline MlaLayout mla_layout(int64_t num_q_tokens, int32_t num_q_heads,
                             int32_t max_seq_len) {
   MlaLayout m{};
-  const int64_t L = max_seq_len > 0 ? max_seq_len : 1;
-  int64_t split = (cdiv64(L, 64) + kMlaBlock - 1) / kMlaBlock * kMlaBlock;
-  const int64_t min_split = num_q_heads > 16 ? 256 : 512;
-  if (split < min_split) split = min_split;
-  m.split = (int32_t)split;
-  m.max_splits = (int32_t)cdiv64(L, split);
-  const size_t rows = (size_t)num_q_tokens * num_q_heads * m.max_splits;
-  m.part_ml = 0;
-  m.part_acc = align256(sizeof(float) * 2 * rows);
-  m.total = align256(m.part_acc + sizeof(float) * kMlaLatent * rows);
+  const int64_t most = num_q_tokens * cdiv64(max_seq_len > 0 ? max_seq_len : 1, kMlaStageKeys);
+  // a range of R key stages spans at most R tokens: R (1 + query stages)
+  // table entries
+  const int64_t per_stage = 1 + cdiv64(num_q_heads > 0 ? num_q_heads : 16, 32);
+  int64_t grid = cdiv64(most * per_stage, kMlaMaxRange - 1);
+  if (grid < kMlaGridFloor) grid = kMlaGridFloor;
+  if (grid > most) grid = most > 0 ? most : 1;
+  m.grid = (int32_t)grid;
+  if (m.grid == 1) {
+    m.total = 256;
+    return m;
+  }
+  const size_t slots = (size_t)2 * m.grid * num_q_heads;
+  m.seg = 0;
+  m.part_ml = align256(sizeof(int2) * (size_t)num_q_tokens);
+  m.part_acc = align256(m.part_ml + sizeof(float2) * slots);
+  m.total = align256(m.part_acc + sizeof(float) * kMlaLatent * slots);
   return m;
 }
 

@@ -49,6 +49,12 @@ CASES = {
     # chunked prefill through the latent path: chunks of 64 and 96 new tokens
     # (causal over their cached prefix) beside decodes
     "prefill-chunks-h16": ([700, 96, 1200, 5], [64, 96, 1, 1], 16, None),
+    # every workgroup shape: 3 .. 8 waves of 16 heads each
+    "decode-h48": ([33, 300, 2049], [1, 1, 1], 48, None),
+    "spec-decode-h64": ([1000, 64, 65], [2, 1, 4], 64, None),
+    "decode-h80": ([500, 1], [1, 1], 80, None),
+    "decode-h96": ([129, 4096], [1, 1], 96, None),
+    "decode-h112": ([2000, 31, 32], [1, 1, 1], 112, None),
 }
 
 
@@ -85,3 +91,76 @@ def test_mla_decode_repeat_bit_identical_and_table_permutation():
     c = tensor_bits(pa.mla_decode(bf16_tensor(m["q"]), cache2, i32(t2), i32(m["L"]),
                                   i32(m["qsl"]), 0.05, 1000))
     assert np.array_equal(a, c)
+
+
+def per_request_oracle(m, scale, requests):
+    """The oracle over each listed request on its own: {token: [Hq][512]}."""
+    ref = {}
+    cache = oracle_cache(m)
+    for b in requests:
+        t0, t1 = int(m["qsl"][b]), int(m["qsl"][b + 1])
+        o = oracle.mla_decode(m["q"][t0:t1], cache, m["tables"][b:b + 1], m["L"][b:b + 1],
+                              np.array([0, t1 - t0], np.int32), scale)
+        for i in range(t1 - t0):
+            ref[t0 + i] = o[i]
+    return ref
+
+
+def test_mla_many_requests():
+    """300 requests (several per lane in the range search), decodes and 2-3
+    token queries of 1 .. 900 keys."""
+    rng = np.random.default_rng(11)
+    Q = rng.choice([1, 1, 1, 2, 3], size=300)
+    L = np.maximum(rng.integers(1, 900, size=300), Q)
+    m = mla_batch(L, Q, 16, seed=12)
+    scale = float(np.float32(1 / np.sqrt(DL)))
+    cache = gpu_cache(m)
+    out = pa.mla_decode(bf16_tensor(m["q"]), cache, i32(m["tables"]), i32(m["L"]),
+                        i32(m["qsl"]), scale, int(L.max()))
+    torch.cuda.synchronize()
+    ref = oracle.mla_decode(m["q"], oracle_cache(m), m["tables"], m["L"], m["qsl"], scale)
+    check_close(tensor_bits(out), ref, "mla 300 requests")
+
+
+def test_mla_out_of_bounds_requests_skipped_and_stale_records_ignored():
+    """Requests whose metadata is out of bounds (Q > L: request 1 with L = 0;
+    L above max_seq_len: request 4) are skipped: their rows keep what was
+    there; the others match the oracle.  Run after a batch of long requests
+    on the same workspace, each cut into several pieces, whose records of the
+    skipped tokens are stale."""
+    scale = float(np.float32(1 / np.sqrt(DL)))
+    m = mla_batch([900, 2, 1000, 40, 3000], [1, 1, 2, 1, 1], 32, seed=21)
+    T = int(m["qsl"][-1])  # tokens: 0 | 1 | 2, 3 | 4 | 5
+    L_gpu = m["L"].copy()
+    L_gpu[1] = 0
+    ws = pa.mla_workspace(T, 32, 3000)
+    big = mla_batch([3000] * T, [1] * T, 32, seed=22)
+    pa.mla_decode(bf16_tensor(big["q"]), gpu_cache(big), i32(big["tables"]), i32(big["L"]),
+                  i32(big["qsl"]), scale, 3000, workspace=ws)
+    sentinel = 0x7FA1
+    raw = torch.full((T, 32, 512), sentinel, dtype=torch.int16, device="cuda")
+    pa.mla_decode(bf16_tensor(m["q"]), gpu_cache(m), i32(m["tables"]), i32(L_gpu),
+                  i32(m["qsl"]), scale, 1000, out=raw.view(torch.bfloat16), workspace=ws)
+    torch.cuda.synchronize()
+    got = tensor_bits(raw.view(torch.bfloat16))
+    ref = per_request_oracle(m, scale, [0, 2, 3])
+    for t in (0, 2, 3, 4):
+        check_close(got[t], ref[t], "mla in-bounds token %d" % t)
+    for t in (1, 5):
+        assert (got[t] == sentinel).all(), "row of skipped token %d written" % t
+
+
+@pytest.mark.parametrize("Hq", [16, 128])
+def test_mla_headline_workload_full_parity(Hq):
+    """The timed MLA workload: 64 requests of U[128, 4096] keys, one query
+    token each, every output row against the oracle."""
+    rng = np.random.default_rng(2024)
+    L = rng.integers(128, 4096, size=64, endpoint=True).astype(np.int32)
+    m = mla_batch(L, np.ones(64, np.int32), Hq, seed=31)
+    scale = float(np.float32(1 / np.sqrt(192.0)))
+    cache = gpu_cache(m)
+    out = pa.mla_decode(bf16_tensor(m["q"]), cache, i32(m["tables"]), i32(m["L"]),
+                        i32(m["qsl"]), scale, int(L.max()))
+    torch.cuda.synchronize()
+    ref = oracle.mla_decode(m["q"], oracle_cache(m), m["tables"], m["L"], m["qsl"], scale)
+    check_close(tensor_bits(out), ref, "mla 64 x U[128, 4096] h%d" % Hq)
