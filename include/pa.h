@@ -615,8 +615,8 @@ pa_status pa_expand_block_tables(const int32_t *block_tables, int32_t num_seqs,
  *   bf16 [num_q_tokens][num_q_heads][512]; block_tables of 64-token block ids
  *   [num_seqs][max_blocks_per_seq]; seq_lens, query_start_loc as pa_attend;
  *   num_q_heads a multiple of 16, at most 128, max_seq_len at most 262144,
- *   num_seqs at most 262144, num_q_tokens below 2^27 and num_blocks at most
- *   2^30 (PA_ERR_UNSUPPORTED otherwise); query_start_loc non-decreasing;
+ *   num_seqs at most 131072, num_q_tokens below 2^27 and num_blocks at most
+ *   2^29 (PA_ERR_UNSUPPORTED otherwise); query_start_loc non-decreasing;
  *   workspace >= pa_mla_workspace_size(...) bytes, 256-byte aligned.  A
  *   request whose metadata is out of bounds is skipped (its rows unwritten).
  *   Two launches: the decode, then (when keys of a token can be cut between

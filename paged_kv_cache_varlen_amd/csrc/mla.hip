@@ -39,9 +39,18 @@ namespace {
 
 constexpr int kKc = kMlaDim / 32;              // 18 chunks of 32 dims
 constexpr int kSubBytes = 16 * kMlaDim * 2;    // 18 KiB: 16 tokens
-constexpr int kStageBytes = 2 * kSubBytes;     // 36 KiB: 32 tokens
-constexpr int kPieces = kStageBytes / 1024;    // 1 KiB loads per stage
 constexpr int kRing = 4;                       // LDS stage buffers
+// A stage of SK keys (16 or 32): SK / 16 sub-tiles of 18 KiB, kPieces
+// one-KiB loads, 64 / SK stages per block; a range's stage table holds
+// kTable entries.
+template <int SK>
+struct Geo {
+  static constexpr int kSubs = SK / 16;
+  static constexpr int kStageBytes = kSubs * kSubBytes;
+  static constexpr int kPieces = kStageBytes / 1024;
+  static constexpr int kPerBlock = kMlaBlock / SK;
+  static constexpr int kTable = mla_table_entries(SK);
+};
 constexpr int64_t kBlockElems = (int64_t)kMlaBlock * kMlaDim;
 // A new maximum is taken only when a score exceeds the one in use by more
 // than this (log2 units): the exponentials stay <= 2^8, and the rescale of
@@ -52,8 +61,6 @@ constexpr float kSlack = 8.0f;
 // compiler's own wait insertion sees.
 constexpr int kWaitLgkm0 = 0xC07F;
 
-static_assert(kStageBytes == kMlaStageKeys * kMlaDim * 2, "stage = 32 tokens");
-
 // Scalar-memory load of a wave-uniform address (tracked by lgkmcnt, not by
 // the vector-memory counter that orders the stage ring).
 template <class T>
@@ -61,11 +68,12 @@ __device__ __forceinline__ T sload(const T* p) {
   return *(const __attribute__((address_space(4))) T*)p;
 }
 
-// Stages of tokens that see 1, 2, .., n keys: the sum of ceil(x / 32).
+// Stages of tokens that see 1, 2, .., n keys: the sum of ceil(x / SK).
+template <int SK>
 __device__ __forceinline__ int64_t stage_prefix(int64_t n) {
   if (n <= 0) return 0;
-  const int64_t m = n / kMlaStageKeys, r = n % kMlaStageKeys;
-  return (m + 1) * (16 * m + r);
+  const int64_t m = n / SK, r = n % SK;
+  return (m + 1) * (SK / 2 * m + r);
 }
 
 // A request's metadata is in bounds: its tokens inside [0, T), Q <= L,
@@ -77,11 +85,12 @@ __device__ __forceinline__ bool req_ok(const MlaParams& P, int q0, int q1, int L
 
 // Stages of request b (vector loads, one request per lane; 0 past the end
 // or out of bounds).  Query i of its Q tokens sees L - Q + 1 + i keys.
+template <int SK>
 __device__ __forceinline__ int64_t req_stages(const MlaParams& P, int b) {
   if (b >= P.num_seqs) return 0;
   const int q0 = P.qsl[b], q1 = P.qsl[b + 1], L = P.seq_lens[b];
   if (!req_ok(P, q0, q1, L)) return 0;
-  return stage_prefix(L) - stage_prefix(L - (q1 - q0));
+  return stage_prefix<SK>(L) - stage_prefix<SK>(L - (q1 - q0));
 }
 
 __device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
@@ -108,8 +117,9 @@ struct Cursor {
   int i, j, nst;
 };
 
+template <int SK>
 __device__ __forceinline__ int token_stages(const Cursor& c) {
-  return (c.L - c.Q + 1 + c.i + kMlaStageKeys - 1) / kMlaStageKeys;
+  return (c.L - c.Q + 1 + c.i + SK - 1) / SK;
 }
 
 // Metadata of the requests b0 .. b0 + 63, one per lane (loaded once), and
@@ -134,6 +144,7 @@ struct ReqWindow {
 // metadata is in bounds.  Called only while stages remain, which the
 // stream's total guarantees; past num_seqs it stops on a dummy position,
 // never used.
+template <int SK>
 __device__ __forceinline__ void cursor_next(Cursor& c, const MlaParams& P,
                                             const ReqWindow& win) {
   if (++c.j < c.nst) return;
@@ -158,7 +169,7 @@ __device__ __forceinline__ void cursor_next(Cursor& c, const MlaParams& P,
       }
     }
   }
-  c.nst = token_stages(c);
+  c.nst = token_stages<SK>(c);
 }
 
 // Global-to-LDS copy of one KiB: lane i reads 16 bytes at gaddr + voff and
@@ -168,6 +179,13 @@ __device__ __forceinline__ void cursor_next(Cursor& c, const MlaParams& P,
 // them itself.  M0 holds the LDS address; five wait states after writing it
 // and the SGPR address pair cover the hazards; M0 is restored.
 __device__ __forceinline__ void dma_kib(uint64_t gaddr, uint32_t voff, uint32_t laddr) {
+  // (the addresses are wave-uniform; readfirstlane makes that visible, so
+  // that they sit in SGPRs.  It returns an int: each half goes through a
+  // uint32_t, or the low half would be sign-extended into the high one.)
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)gaddr);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(gaddr >> 32));
+  gaddr = ((uint64_t)hi << 32) | lo;
+  laddr = __builtin_amdgcn_readfirstlane(laddr);
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 4\n\t"
@@ -178,16 +196,18 @@ __device__ __forceinline__ void dma_kib(uint64_t gaddr, uint32_t voff, uint32_t 
       : "memory");
 }
 
-// Entries of a range's stage table: a key stage is block id * 2 + which 32
+// Entries of a range's stage table: a key stage is block id * 4 + which SK
 // keys of the block (bit 31 clear); a query stage is kQStage | token << 3 |
-// k: the queries of head groups 2k, 2k + 1 of that token (36 KiB, or 18 for
-// a last odd head group), which precede the token's key stages.
+// k: the queries of heads SK k .. SK k + SK - 1 of that token (SK * 1152
+// bytes, fewer for a last partial group), which precede the token's key
+// stages.
 constexpr uint32_t kQStage = 0x80000000u;
 
 // This wave's share of a stage's loads: nl of its `pieces` one-KiB pieces,
 // p0 .. p0 + nl - 1 modulo pieces (past the end they repeat pieces another
 // wave also loads: the same bytes to the same place), so every wave issues
 // exactly nl loads per stage, key stage or query stage.
+template <int SK>
 __device__ __forceinline__ void dma_stage(const MlaParams& P, uint32_t e, uint32_t lstage,
                                           uint32_t voff, int p0, int nl) {
   uint64_t g;
@@ -196,13 +216,13 @@ __device__ __forceinline__ void dma_stage(const MlaParams& P, uint32_t e, uint32
   if (e & kQStage) {
     const int64_t t = (e & ~kQStage) >> 3;
     const int k = e & 7;
-    g = (uint64_t)(uintptr_t)(P.q + (t * P.Hq + 32 * k) * kMlaDim);
-    pieces = (P.Hq - 32 * k >= 32 ? 2 : 1) * kSubBytes / 1024;
+    g = (uint64_t)(uintptr_t)(P.q + (t * P.Hq + SK * k) * kMlaDim);
+    pieces = min(SK, P.Hq - SK * k) * (kMlaDim * 2) / 1024;
     vo = (uint32_t)(16 * (threadIdx.x & 63));
   } else {
-    g = (uint64_t)(uintptr_t)(P.cache + (int64_t)(e >> 1) * kBlockElems) +
-        (uint64_t)(e & 1) * kStageBytes;
-    pieces = kPieces;
+    g = (uint64_t)(uintptr_t)(P.cache + (int64_t)(e >> 2) * kBlockElems) +
+        (uint64_t)(e & 3) * Geo<SK>::kStageBytes;
+    pieces = Geo<SK>::kPieces;
     vo = voff;
   }
   for (int x = 0; x < nl; ++x) {
@@ -284,10 +304,18 @@ __global__ __launch_bounds__(256) void mla_write_kv_kernel(
       *reinterpret_cast<const uint4*>(kv + tok * stride + d);
 }
 
-// DQ waves per 16 heads (4, 2 or 1), each with 512 / DQ output dims.
-template <int DQ>
-__global__ __launch_bounds__(DQ == 1 ? 512 : 256) void mla_decode_kernel(MlaParams P) {
+// DQ waves per 16 heads (4, 2 or 1), each with 512 / DQ output dims; stages
+// of SK keys (16: 80 KiB of LDS, two workgroups per compute unit; 32: 160
+// KiB, one).
+template <int DQ, int SK>
+__global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_decode_kernel(
+    MlaParams P) {
   constexpr int kTiles = kMlaLatent / 16 / DQ;  // 16-dim output tiles per wave
+  constexpr int kSubs = Geo<SK>::kSubs;
+  constexpr int kStageBytes = Geo<SK>::kStageBytes;
+  constexpr int kPieces = Geo<SK>::kPieces;
+  constexpr int kPerBlock = Geo<SK>::kPerBlock;
+  constexpr int kTable = Geo<SK>::kTable;
   // LDS reads are issued at most this many chunks / tiles ahead of their
   // MFMAs: all of them would not fit in the registers beside the
   // accumulators (128 of them with one wave per 16 heads)
@@ -300,9 +328,9 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256) void mla_decode_kernel(MlaPara
   constexpr int kMaxC = (kKc + DQ - 1) / DQ;
   __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * kStageBytes];
   // the range's stage table (query and key stages in stream order)
-  __shared__ uint32_t stab[kMlaMaxRange];
-  // partial scores of the waves (DQ > 1: 4 waves): [wave][half][lane]
-  __shared__ f32x4 xsc[DQ > 1 ? 4 : 1][2][64];
+  __shared__ uint32_t stab[kTable];
+  // partial scores of the waves (DQ > 1: 4 waves): [wave][sub-tile][lane]
+  __shared__ f32x4 xsc[DQ > 1 ? 4 : 1][kSubs][64];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -329,21 +357,32 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256) void mla_decode_kernel(MlaPara
   // a second scan walks.  (Every wave computes the same.)
   const int C = (P.num_seqs + 63) / 64;
   int64_t tot = 0;
+  int wq0 = 0, wq1 = 0, wL = 0;  // C == 1: lane b's request metadata, kept
+  if (C == 1) {
+    if (lane < P.num_seqs) {
+      wq0 = P.qsl[lane];
+      wq1 = P.qsl[lane + 1];
+      wL = P.seq_lens[lane];
+      if (req_ok(P, wq0, wq1, wL))
+        tot = stage_prefix<SK>(wL) - stage_prefix<SK>(wL - (wq1 - wq0));
+    }
+  } else {
 #pragma unroll 4
-  for (int k = 0; k < C; ++k) tot += req_stages(P, lane * C + k);
+    for (int k = 0; k < C; ++k) tot += req_stages<SK>(P, lane * C + k);
+  }
   const int64_t incl = wave_scan(tot);
   const int64_t M = readlane64(incl, 63);
   const int64_t R = (M + gridDim.x - 1) / gridDim.x;
   const int64_t I0 = min((int64_t)blockIdx.x * R, M);
   const int64_t I1 = min(I0 + R, M);
-  if (I0 >= I1 || I1 - I0 > kMlaMaxRange) return;
+  if (I0 >= I1 || I1 - I0 > kTable) return;
   const int nreal = (int)(I1 - I0);  // key stages of the range
   const int lam = __builtin_ctzll(__builtin_amdgcn_ballot_w64(incl > I0));
   int64_t carry = readlane64(incl - tot, lam);
-  int b0 = -1;
-  int64_t s0 = 0;
-  for (int k0 = 0; k0 < C; k0 += 64) {
-    const int64_t it = k0 + lane < C ? req_stages(P, lam * C + k0 + lane) : 0;
+  int b0 = C == 1 ? lam : -1;
+  int64_t s0 = I0 - carry;
+  for (int k0 = 0; C > 1 && k0 < C; k0 += 64) {
+    const int64_t it = k0 + lane < C ? req_stages<SK>(P, lam * C + k0 + lane) : 0;
     const int64_t inc = wave_scan(it) + carry;
     const uint64_t hit = __builtin_amdgcn_ballot_w64(inc > I0);
     if (hit) {
@@ -358,8 +397,13 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256) void mla_decode_kernel(MlaPara
   if (b0 < 0) return;
 
   ReqWindow win;
-  win.b0 = b0;
-  {
+  if (C == 1) {  // every request is in the scan's registers
+    win.b0 = 0;
+    win.q0 = wq0;
+    win.q1 = wq1;
+    win.L = wL;
+  } else {
+    win.b0 = b0;
     const int b = b0 + lane;
     const bool in = b < P.num_seqs;
     win.q0 = in ? P.qsl[b] : 0;
@@ -375,18 +419,18 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256) void mla_decode_kernel(MlaPara
     cur.Q = q1 - q0;
     cur.L = L;
     // token: the first i whose stages end past s0
-    const int64_t before = stage_prefix(cur.L - cur.Q);
+    const int64_t before = stage_prefix<SK>(cur.L - cur.Q);
     int lo = 0, hi = cur.Q - 1;
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      if (stage_prefix(cur.L - cur.Q + 1 + mid) - before > s0)
+      if (stage_prefix<SK>(cur.L - cur.Q + 1 + mid) - before > s0)
         hi = mid;
       else
         lo = mid + 1;
     }
     cur.i = lo;
-    cur.j = (int)(s0 - (stage_prefix(cur.L - cur.Q + lo) - before));
-    cur.nst = token_stages(cur);
+    cur.j = (int)(s0 - (stage_prefix<SK>(cur.L - cur.Q + lo) - before));
+    cur.nst = token_stages<SK>(cur);
   }
 
   // ---- lane constants of the LDS layout ---------------------------------
@@ -408,17 +452,27 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256) void mla_decode_kernel(MlaPara
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)ring;
 
   // ---- the first token's query stages: issued before the table is built -
-  const int qs = (P.Hq + 31) / 32;  // query stages per token
+  const int qs = (P.Hq + SK - 1) / SK;  // query stages per token
   const int pre = min(qs, kRing - 1);
   for (int k = 0; k < pre; ++k)
-    dma_stage(P, kQStage | ((uint32_t)(cur.q0 + cur.i) << 3) | (uint32_t)k,
+    dma_stage<SK>(P, kQStage | ((uint32_t)(cur.q0 + cur.i) << 3) | (uint32_t)k,
               lring + k * kStageBytes, voff, p0, nl);
+  // and its first key stage (block id read directly; the table's entry is
+  // the same)
+  int pre2 = pre;
+  if (qs < kRing - 1) {
+    int id = sload(P.bt + (int64_t)cur.b * P.bt_stride + cur.j / kPerBlock);
+    id = id < 0 ? 0 : (id >= P.num_blocks ? (int)(P.num_blocks - 1) : id);
+    dma_stage<SK>(P, ((uint32_t)id << 2) | (uint32_t)(cur.j % kPerBlock),
+                  lring + qs * kStageBytes, voff, p0, nl);
+    pre2 = qs + 1;
+  }
 
   // ---- the range's stage table (wave 0; one gather) -----------------------
-  // Token by token: its query stages, then (request - b0) << 13 | stage of
+  // Token by token: its query stages, then (request - b0) << 14 | stage of
   // each key stage; then each lane turns its key entries into block ids
   // with one block-table load each.
-  constexpr int kCap = kMlaMaxRange - 1;  // the last slot holds the count
+  constexpr int kCap = kTable - 1;  // the last slot holds the count
   if (w == 0) {
     Cursor f = cur;
     int x = 0;
@@ -431,22 +485,22 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256) void mla_decode_kernel(MlaPara
       x += qs;
       const int cnt = min(f.nst - f.j, nreal - done);
       for (int y = lane; y < cnt; y += 64)
-        stab[x + y] = ((uint32_t)(f.b - b0) << 13) | (uint32_t)(f.j + y);
+        stab[x + y] = ((uint32_t)(f.b - b0) << 14) | (uint32_t)(f.j + y);
       x += cnt;
       done += cnt;
       if (done < nreal) {
         f.j = f.nst - 1;
-        cursor_next(f, P, win);
+        cursor_next<SK>(f, P, win);
       }
     }
 #pragma unroll 4
     for (int y = lane; y < x; y += 64) {
       const uint32_t v = stab[y];
       if (v & kQStage) continue;
-      const int b = b0 + (int)(v >> 13), j = (int)(v & 8191);
-      int id = P.bt[(int64_t)b * P.bt_stride + (j >> 1)];
+      const int b = b0 + (int)(v >> 14), j = (int)(v & 16383);
+      int id = P.bt[(int64_t)b * P.bt_stride + j / kPerBlock];
       id = id < 0 ? 0 : (id >= P.num_blocks ? (int)(P.num_blocks - 1) : id);
-      stab[y] = ((uint32_t)id << 1) | (uint32_t)(j & 1);
+      stab[y] = ((uint32_t)id << 2) | (uint32_t)(j % kPerBlock);
     }
     if (lane == 0) stab[kCap] = (uint32_t)x;
   }
@@ -459,9 +513,9 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256) void mla_decode_kernel(MlaPara
     return;
   }
 
-  // ---- rest of the prologue: entries pre .. kRing - 2 ---------------------
-  for (int k = pre; k < kRing - 1 && k < n; ++k)
-    dma_stage(P, __builtin_amdgcn_readfirstlane(stab[k]), lring + k * kStageBytes, voff, p0,
+  // ---- rest of the prologue: entries pre2 .. kRing - 2 --------------------
+  for (int k = pre2; k < kRing - 1 && k < n; ++k)
+    dma_stage<SK>(P, __builtin_amdgcn_readfirstlane(stab[k]), lring + k * kStageBytes, voff, p0,
               nl);
 
   int stored = 0;         // ring waits left that allow for result stores
@@ -475,7 +529,7 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256) void mla_decode_kernel(MlaPara
     ring_wait<kTiles>(nl, it + kRing - 2 >= n, stored > 0);
     if (stored > 0) --stored;
     if (it + kRing - 1 < n)
-      dma_stage(P, __builtin_amdgcn_readfirstlane(stab[it + kRing - 1]),
+      dma_stage<SK>(P, __builtin_amdgcn_readfirstlane(stab[it + kRing - 1]),
                 lring + (uint32_t)((it + kRing - 1) % kRing) * kStageBytes, voff, p0, nl);
   };
 
@@ -485,10 +539,11 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256) void mla_decode_kernel(MlaPara
     bf16x8 qop[kMaxC];  // lane (r, g): head 16 hg + r, dims 32 (c0 + i) + 8g .. +7
     for (int k = 0; k < qs; ++k, ++it) {
       ring_step();
-      if (k == (hg >> 1)) {
-        // lane (r, g): head 16 (hg % 2) + r, dims 8g .. of each chunk
-        const uint8_t* st = ring + (it % kRing) * kStageBytes + (hg & 1) * kSubBytes +
-                            r * (kMlaDim * 2) + g * 16 + c0 * 64;
+      if (k == 16 * hg / SK) {
+        // lane (r, g): head 16 hg + r (row (16 hg) % SK + r of the stage),
+        // dims 8g .. of each chunk
+        const uint8_t* st = ring + (it % kRing) * kStageBytes +
+                            (16 * hg % SK + r) * (kMlaDim * 2) + g * 16 + c0 * 64;
 #pragma unroll
         for (int i = 0; i < kMaxC; ++i)
           if (i < nc) qop[i] = *reinterpret_cast<const bf16x8*>(st + i * 64);
@@ -505,14 +560,17 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256) void mla_decode_kernel(MlaPara
       ring_step();
       const int j = cur.j + ks;  // stage of the token
       const uint8_t* st = ring + (it % kRing) * kStageBytes;
-      // scores of the stage's two 16-key halves
-      f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+      // scores of the stage's 16-key sub-tiles
+      f32x4 sc[kSubs];
+#pragma unroll
+      for (int u = 0; u < kSubs; ++u) sc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < kMaxC; ++i) {
         if (i < nc) {
           const uint8_t* kp = st + (c0 + i) * 1024 + offK;
-          sa = mfma32(*reinterpret_cast<const bf16x8*>(kp), qop[i], sa);
-          sb = mfma32(*reinterpret_cast<const bf16x8*>(kp + kSubBytes), qop[i], sb);
+#pragma unroll
+          for (int u = 0; u < kSubs; ++u)
+            sc[u] = mfma32(*reinterpret_cast<const bf16x8*>(kp + u * kSubBytes), qop[i], sc[u]);
         }
         if (i % kScoreGroup == kScoreGroup - 1) __builtin_amdgcn_sched_barrier(0);
       }
@@ -520,31 +578,30 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256) void mla_decode_kernel(MlaPara
         // add the head group's partial sums in wave order (the same sums in
         // every wave); the writes land before the barrier, and every wave
         // has read them before the next stage's barrier
-        xsc[w][0][lane] = sa;
-        xsc[w][1][lane] = sb;
+#pragma unroll
+        for (int u = 0; u < kSubs; ++u) xsc[w][u][lane] = sc[u];
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         const int w0 = hg * DQ;  // the head group's first wave
-        sa = xsc[w0][0][lane];
-        sb = xsc[w0][1][lane];
 #pragma unroll
-        for (int v = 1; v < DQ; ++v) {
-          sa += xsc[w0 + v][0][lane];
-          sb += xsc[w0 + v][1][lane];
+        for (int u = 0; u < kSubs; ++u) {
+          sc[u] = xsc[w0][u][lane];
+#pragma unroll
+          for (int v = 1; v < DQ; ++v) sc[u] += xsc[w0 + v][u][lane];
         }
       }
-      // online softmax over the 32 keys (lane (r, g): keys 4g .. 4g+3 of each
-      // half, head r); keys the token does not see get -inf
+      // online softmax over the stage's keys (lane (r, g): keys 4g .. 4g+3
+      // of each sub-tile, head r); keys the token does not see get -inf
       const int nvis = cur.L - cur.Q + 1 + cur.i;
-      const int key0 = kMlaStageKeys * j + 4 * g;
-      float y[8];
+      const int key0 = SK * j + 4 * g;
+      float y[4 * kSubs];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        y[e] = key0 + e < nvis ? sa[e] * c2 : -INFINITY;
-        y[4 + e] = key0 + 16 + e < nvis ? sb[e] * c2 : -INFINITY;
-      }
+      for (int u = 0; u < kSubs; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          y[4 * u + e] = key0 + 16 * u + e < nvis ? sc[u][e] * c2 : -INFINITY;
       float mx = y[0];
 #pragma unroll
-      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, y[e]);
+      for (int e = 1; e < 4 * kSubs; ++e) mx = fmaxf(mx, y[e]);
       mx = column_max(mx);
       if (__builtin_amdgcn_ballot_w64(mx > mrun + kSlack) != 0) {
         const float mnew = fmaxf(mrun, mx);
@@ -554,12 +611,12 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256) void mla_decode_kernel(MlaPara
         lsum *= alpha;
         mrun = mnew;
       }
-      bf16x8 pp;
+      __bf16 pw[4 * kSubs];
       float ps = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pp[e] = (__bf16)__builtin_amdgcn_exp2f(y[e] - mrun);
-        ps += (float)pp[e];
+      for (int e = 0; e < 4 * kSubs; ++e) {
+        pw[e] = (__bf16)__builtin_amdgcn_exp2f(y[e] - mrun);
+        ps += (float)pw[e];
       }
       lsum += ps;
       // weighted sum; in a stage the token does not see to its end the V rows
@@ -567,10 +624,10 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256) void mla_decode_kernel(MlaPara
       // a NaN) are first zeroed in LDS.  Every wave writes the same zeros, and
       // its own reads follow its own writes (LDS operations of a wave complete
       // in order), so no barrier is needed.
-      if (kMlaStageKeys * j + kMlaStageKeys > nvis) {
-        const int kv = nvis - kMlaStageKeys * j;  // keys of the stage it sees
+      if (SK * j + SK > nvis) {
+        const int kv = nvis - SK * j;  // keys of the stage it sees
         uint8_t* sw = ring + (it % kRing) * kStageBytes;
-        for (int q = lane; q < 2 * (kMlaLatent / 32) * 64; q += 64) {
+        for (int q = lane; q < kSubs * (kMlaLatent / 32) * 64; q += 64) {
           const int u = q >> 10, c = (q >> 6) & 15, pos = q & 63;
           const int key = 16 * u + ((pos & 15) ^ (12 * ((pos >> 4) & 1)));
           if (key >= kv)
@@ -578,16 +635,32 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256) void mla_decode_kernel(MlaPara
                 u32x4{0u, 0u, 0u, 0u};
         }
       }
+      // (operands assembled by whole-vector casts and shuffles: assembled
+      // element by element, the transpose reads' results were compiled to
+      // copies of their first dwords)
+      if constexpr (SK == 32) {
+        bf16x8 pp;
 #pragma unroll
-      for (int mt = 0; mt < kTiles; ++mt) {
-        // one whole-vector shuffle: assembled element by element, the
-        // operand was compiled to copies of each read's first dword
-        const bf16x8 a = __builtin_shufflevector(
-            __builtin_bit_cast(bf16x4, lds_read_tr(st + 512 * mt + offV)),
-            __builtin_bit_cast(bf16x4, lds_read_tr(st + kSubBytes + 512 * mt + offV)), 0, 1, 2,
-            3, 4, 5, 6, 7);
-        acc[mt] = mfma32(a, pp, acc[mt]);
-        if (mt % kPvGroup == kPvGroup - 1) __builtin_amdgcn_sched_barrier(0);
+        for (int e = 0; e < 8; ++e) pp[e] = pw[e];
+#pragma unroll
+        for (int mt = 0; mt < kTiles; ++mt) {
+          const bf16x8 a = __builtin_shufflevector(
+              __builtin_bit_cast(bf16x4, lds_read_tr(st + 512 * mt + offV)),
+              __builtin_bit_cast(bf16x4, lds_read_tr(st + kSubBytes + 512 * mt + offV)), 0, 1,
+              2, 3, 4, 5, 6, 7);
+          acc[mt] = mfma32(a, pp, acc[mt]);
+          if (mt % kPvGroup == kPvGroup - 1) __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+        bf16x4 pp;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pp[e] = pw[e];
+#pragma unroll
+        for (int mt = 0; mt < kTiles; ++mt) {
+          const bf16x4 a = __builtin_bit_cast(bf16x4, lds_read_tr(st + 512 * mt + offV));
+          acc[mt] = mfma16(a, pp, acc[mt]);
+          if (mt % kPvGroup == kPvGroup - 1) __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
 
@@ -611,11 +684,18 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256) void mla_decode_kernel(MlaPara
       }
     } else {
       // slot 2w: the range's first token; 2w + 1: its last (only these two
-      // can be cut)
+      // can be cut).  The piece's normalised output in bf16, its (max, sum)
+      // in fp32.
       const int64_t row = (2 * (int64_t)blockIdx.x + (first_tok ? 0 : 1)) * P.Hq + h;
-      float* ap = P.part_acc + row * kMlaLatent + dim0;
+      uint16_t* ap = P.part_out + row * kMlaLatent + dim0;
+      const float inv = 1.0f / l;
 #pragma unroll
-      for (int k = 0; k < kTiles; ++k) *reinterpret_cast<f32x4*>(ap + 16 * k) = acc[k];
+      for (int k = 0; k < kTiles; ++k) {
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (__bf16)(acc[k][e] * inv);
+        *reinterpret_cast<bf16x4*>(ap + 16 * k) = o;
+      }
       if (dq == 0 && g == 0) P.part_ml[row] = make_float2(mrun, l);
     }
     // the workgroup holding the token's first stage records which workgroups
@@ -631,15 +711,16 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256) void mla_decode_kernel(MlaPara
     done += cnt;
     if (done < nreal) {
       cur.j = cur.nst - 1;
-      cursor_next(cur, P, win);
+      cursor_next<SK>(cur, P, win);
     }
   }
 }
 
 // One wave per (query token, head) whose keys were cut between workgroups:
-// log-sum-exp over the pieces.  The lanes first read the pieces' (max, sum)
-// in parallel (64 pieces per round), then every lane adds its 8 dims of each
-// piece's sums (independent loads); lane i holds dims 8i .. 8i+7.  The decode
+// log-sum-exp over the pieces.  The lanes read the pieces' (max, sum) in
+// parallel (64 pieces per round) along with the outputs of the first four
+// pieces, then every lane adds its 8 dims of each piece's output, weighted;
+// lane i holds dims 8i .. 8i+7.  The decode
 // writes every token's record in every launch ((0, 0) for tokens of
 // out-of-bounds requests), so no stale record is read.
 __global__ __launch_bounds__(256) void mla_merge_kernel(MlaParams P) {
@@ -657,40 +738,56 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaParams P) {
     const int64_t slot = s == 0 ? 2 * (int64_t)sg.x + (sg.y & 1) : 2 * ((int64_t)sg.x + s);
     return slot * P.Hq + h;
   };
+  // out = sum_i w_i o_i / sum_i w_i, w_i = l_i 2^(m_i - M): o_i a piece's
+  // normalised output (bf16), (m_i, l_i) its running max and sum
   float M = -INFINITY, den = 0.0f;
-  f32x4 n0 = {0.f, 0.f, 0.f, 0.f}, n1 = {0.f, 0.f, 0.f, 0.f};
+  float n[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  constexpr int kAhead = 4;  // pieces whose outputs are loaded with the (max, sum) round
   for (int s0 = 0; s0 < pieces; s0 += 64) {
     const int cnt = min(64, pieces - s0);
     float2 ml = make_float2(-INFINITY, 0.0f);
     if (lane < cnt) ml = P.part_ml[row_of(s0 + lane)];
+    // the first pieces' outputs do not depend on the (max, sum) values:
+    // their loads go out in the same round
+    bf16x8 oa[kAhead];
+#pragma unroll
+    for (int k = 0; k < kAhead; ++k)
+      if (k < cnt)
+        oa[k] = *reinterpret_cast<const bf16x8*>(P.part_out + row_of(s0 + k) * kMlaLatent +
+                                                 8 * lane);
     float mx = ml.x;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
     const float mn = fmaxf(M, mx);  // finite: every piece saw a key
     const float c_old = __builtin_amdgcn_exp2f(M - mn);
-    const float c = lane < cnt ? __builtin_amdgcn_exp2f(ml.x - mn) : 0.0f;
-    float dl = c * ml.y;
+    const float wgt = lane < cnt ? ml.y * __builtin_amdgcn_exp2f(ml.x - mn) : 0.0f;
+    float dl = wgt;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) dl += __shfl_xor(dl, d);
     den = den * c_old + dl;
-    n0 *= c_old;
-    n1 *= c_old;
-    for (int k = 0; k < cnt; ++k) {
-      const float ck = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(c), k));
-      const f32x4* ap =
-          reinterpret_cast<const f32x4*>(P.part_acc + row_of(s0 + k) * kMlaLatent + 8 * lane);
-      n0 += ap[0] * ck;
-      n1 += ap[1] * ck;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) n[e] *= c_old;
+#pragma unroll
+    for (int k = 0; k < kAhead; ++k) {
+      if (k < cnt) {
+        const float wk = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wgt), k));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) n[e] += wk * (float)oa[k][e];
+      }
+    }
+    for (int k = kAhead; k < cnt; ++k) {
+      const float wk = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wgt), k));
+      const bf16x8 ok = *reinterpret_cast<const bf16x8*>(P.part_out + row_of(s0 + k) * kMlaLatent +
+                                                         8 * lane);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) n[e] += wk * (float)ok[e];
     }
     M = mn;
   }
   const float inv = 1.0f / den;
   bf16x8 o;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    o[i] = (__bf16)(n0[i] * inv);
-    o[i + 4] = (__bf16)(n1[i] * inv);
-  }
+  for (int e = 0; e < 8; ++e) o[e] = (__bf16)(n[e] * inv);
   *reinterpret_cast<bf16x8*>(P.out + row0 * kMlaLatent + 8 * lane) = o;
 }
 
@@ -711,12 +808,15 @@ hipError_t launch_mla_decode(const MlaParams& P, hipStream_t stream) {
   const int hgs = P.Hq / 16;  // 1 .. 8
   const int dq = hgs == 1 ? 4 : (hgs == 2 ? 2 : 1);
   const dim3 block(64 * hgs * dq), grid((unsigned)P.grid);
+  static_assert(mla_stage_keys(16) == 16 && mla_stage_keys(32) == 16 &&
+                    mla_stage_keys(48) == 32,
+                "the instances below follow the stage size the layout assumes");
   if (dq == 4)
-    hipLaunchKernelGGL(mla_decode_kernel<4>, grid, block, 0, stream, P);
+    hipLaunchKernelGGL((mla_decode_kernel<4, 16>), grid, block, 0, stream, P);
   else if (dq == 2)
-    hipLaunchKernelGGL(mla_decode_kernel<2>, grid, block, 0, stream, P);
+    hipLaunchKernelGGL((mla_decode_kernel<2, 16>), grid, block, 0, stream, P);
   else
-    hipLaunchKernelGGL(mla_decode_kernel<1>, grid, block, 0, stream, P);
+    hipLaunchKernelGGL((mla_decode_kernel<1, 32>), grid, block, 0, stream, P);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || P.grid < 2) return e;
   const int64_t rows = (int64_t)P.num_q_tokens * P.Hq;

@@ -891,11 +891,11 @@ pa_status pa_mla_decode(const void* q, const void* cache, int64_t num_blocks,
   if (max_seq_len > (1 << 18))
     return fail(PA_ERR_UNSUPPORTED, "pa_mla_decode: max_seq_len above 262144");
   if (num_seqs > pa::kMlaMaxSeqs)
-    return fail(PA_ERR_UNSUPPORTED, "pa_mla_decode: num_seqs above 262144");
+    return fail(PA_ERR_UNSUPPORTED, "pa_mla_decode: num_seqs above 131072");
   if (num_q_tokens >= pa::kMlaMaxTokens)
     return fail(PA_ERR_UNSUPPORTED, "pa_mla_decode: num_q_tokens of 2^27 or more");
-  if (num_blocks > (int64_t(1) << 30))
-    return fail(PA_ERR_UNSUPPORTED, "pa_mla_decode: num_blocks above 2^30");
+  if (num_blocks > pa::kMlaMaxBlocks)
+    return fail(PA_ERR_UNSUPPORTED, "pa_mla_decode: num_blocks above 2^29");
   if (num_q_tokens == 0 || num_seqs == 0) return ok();
   if (!q || !cache || !block_tables || !seq_lens || !query_start_loc || !out)
     return fail(PA_ERR_NULL, "pa_mla_decode: NULL pointer");
@@ -934,7 +934,7 @@ pa_status pa_mla_decode(const void* q, const void* cache, int64_t num_blocks,
   char* ws = static_cast<char*>(workspace);
   P.seg = m.grid > 1 ? reinterpret_cast<int2*>(ws + m.seg) : nullptr;
   P.part_ml = m.grid > 1 ? reinterpret_cast<float2*>(ws + m.part_ml) : nullptr;
-  P.part_acc = m.grid > 1 ? reinterpret_cast<float*>(ws + m.part_acc) : nullptr;
+  P.part_out = m.grid > 1 ? reinterpret_cast<uint16_t*>(ws + m.part_out) : nullptr;
   hipError_t e = pa::launch_mla_decode(P, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "pa_mla_decode launch");
   return ok();

@@ -226,39 +226,42 @@ struct MlaParams {
   uint16_t* out;       // [T][Hq][512]
   int2* seg;           // [T]: (first workgroup, 2 * workgroups + slot flag)
   float2* part_ml;     // [2 grid][Hq]: (running max, sum) of a piece
-  float* part_acc;     // [2 grid][Hq][512]: unnormalised sums of a piece
+  uint16_t* part_out;  // [2 grid][Hq][512]: a piece's normalised output (bf16)
 };
 
-// The decode's work is a stream of 32-key stages (each query token's keys in
-// stages of 32), cut into ranges of R = ceil(stages / grid) stages, one per
-// workgroup; in a workgroup's table each token of its range also takes
-// ceil(Hq / 32) query stages.  grid: 256 (one 160 KiB-LDS workgroup per
-// compute unit), more when a range's table could exceed kMlaMaxRange - 1
-// entries, never more than the stages there can be.  Only a range's first
-// and last token can be cut, so a workgroup leaves at most two partial
-// results (slots 2w and 2w + 1).  One workgroup sees every stage: no
+// The decode's work is a stream of stages of SK keys (each query token's
+// keys in stages of SK: 16 for 16 and 32 query heads, 32 for more), cut into
+// ranges of R = ceil(stages / grid) stages, one per workgroup; in a
+// workgroup's table each token of its range also takes ceil(Hq / SK) query
+// stages.  grid: 512 for SK = 16 (80 KiB of LDS per workgroup, two per
+// compute unit), 256 for SK = 32 (160 KiB, one); more when a range's table
+// could exceed its entries, never more than the stages there can be.  Only a
+// range's first and last token can be cut, so a workgroup leaves at most two
+// partial results (slots 2w and 2w + 1).  One workgroup sees every stage: no
 // partials (the workspace is then a nominal 256 bytes, never touched).
-constexpr int kMlaStageKeys = 32;
-constexpr int kMlaGridFloor = 256;
-constexpr int kMlaMaxRange = 2048;
-constexpr int kMlaMaxSeqs = 1 << 18;          // request index in a table entry: 18 bits
-constexpr int64_t kMlaMaxTokens = 1 << 27;    // token index in a table entry: 28 bits
+constexpr int mla_stage_keys(int num_q_heads) { return num_q_heads <= 32 ? 16 : 32; }
+constexpr int mla_table_entries(int stage_keys) { return stage_keys == 16 ? 1024 : 2048; }
+constexpr int kMlaMaxSeqs = 1 << 17;        // request index in a table entry: 17 bits
+constexpr int64_t kMlaMaxTokens = 1 << 27;  // token index in a table entry: 28 bits
+constexpr int64_t kMlaMaxBlocks = 1 << 29;  // block id in a table entry: 29 bits
 struct MlaLayout {
   int32_t grid;
   size_t seg;
   size_t part_ml;
-  size_t part_acc;
+  size_t part_out;
   size_t total;
 };
 inline MlaLayout mla_layout(int64_t num_q_tokens, int32_t num_q_heads,
                             int32_t max_seq_len) {
   MlaLayout m{};
-  const int64_t most = num_q_tokens * cdiv64(max_seq_len > 0 ? max_seq_len : 1, kMlaStageKeys);
+  const int sk = mla_stage_keys(num_q_heads);
+  const int64_t most = num_q_tokens * cdiv64(max_seq_len > 0 ? max_seq_len : 1, sk);
   // a range of R key stages spans at most R tokens: R (1 + query stages)
   // table entries
-  const int64_t per_stage = 1 + cdiv64(num_q_heads > 0 ? num_q_heads : 16, 32);
-  int64_t grid = cdiv64(most * per_stage, kMlaMaxRange - 1);
-  if (grid < kMlaGridFloor) grid = kMlaGridFloor;
+  const int64_t per_stage = 1 + cdiv64(num_q_heads > 0 ? num_q_heads : 16, sk);
+  int64_t grid = cdiv64(most * per_stage, mla_table_entries(sk) - 1);
+  const int64_t floor = sk == 16 ? 512 : 256;
+  if (grid < floor) grid = floor;
   if (grid > most) grid = most > 0 ? most : 1;
   m.grid = (int32_t)grid;
   if (m.grid == 1) {
@@ -268,8 +271,8 @@ inline MlaLayout mla_layout(int64_t num_q_tokens, int32_t num_q_heads,
   const size_t slots = (size_t)2 * m.grid * num_q_heads;
   m.seg = 0;
   m.part_ml = align256(sizeof(int2) * (size_t)num_q_tokens);
-  m.part_acc = align256(m.part_ml + sizeof(float2) * slots);
-  m.total = align256(m.part_acc + sizeof(float) * kMlaLatent * slots);
+  m.part_out = align256(m.part_ml + sizeof(float2) * slots);
+  m.total = align256(m.part_out + sizeof(uint16_t) * kMlaLatent * slots);
   return m;
 }
 
