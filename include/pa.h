@@ -610,7 +610,9 @@ pa_status pa_expand_block_tables(const int32_t *block_tables, int32_t num_seqs,
  *   at slot_mapping[i] (device int64; < 0 or >= num_blocks * 64: skipped).
  * pa_mla_workspace_size - workspace bytes of pa_mla_decode (per-token
  *   records and the partial results of tokens whose keys are cut between
- *   workgroups: at most two per workgroup); 0 for invalid arguments.
+ *   workgroups: at most two per workgroup); 0 for invalid arguments and
+ *   for work beyond one launch (num_q_tokens x max_seq_len above about 2^44
+ *   keys), which pa_mla_decode rejects with PA_ERR_UNSUPPORTED.
  * pa_mla_decode - q device bf16 [num_q_tokens][num_q_heads][576], out device
  *   bf16 [num_q_tokens][num_q_heads][512]; block_tables of 64-token block ids
  *   [num_seqs][max_blocks_per_seq]; seq_lens, query_start_loc as pa_attend;

@@ -7,9 +7,10 @@
 // sub-tile is 18 KiB of [32-dim chunk][16 tokens][32 dims] (one KiB piece per
 // chunk), so tokens 32s .. 32s+31 of a block (s = 0, 1) are 36 KiB contiguous.
 //
-// Decode (mla_decode_kernel).  The work is a stream of 32-key stages: the
-// requests in order, each query token of a request in order, the keys that
-// token sees in stages of 32.  The stream is cut into contiguous ranges of
+// Decode (mla_decode_kernel).  The work is a stream of SK-key stages (SK =
+// 16 for up to 32 heads, 32 for more): the requests in order, each query
+// token of a request in order, then its query stages and the keys that token
+// sees in stages of SK.  The stream is cut into contiguous ranges of
 // R = ceil(stages / gridDim.x) stages, one per workgroup, so every workgroup
 // reads the same latent bytes whatever the mix of lengths; a token whose
 // keys are cut between workgroups leaves one partial result per workgroup,
@@ -17,13 +18,14 @@
 //
 // A workgroup has one wave per 16 query heads (for 16 and 32 heads, one wave
 // per (16 heads, quarter / half of the 512 output dims)).  Its stages pass
-// through a ring of four 36 KiB LDS buffers, filled three stages ahead by
-// global-to-LDS loads that the waves share; each wave then reads the stage
-// from LDS for
+// through a ring of four LDS buffers (18 KiB for SK = 16, two workgroups per
+// CU; 36 KiB for SK = 32), filled three stages ahead by global-to-LDS loads
+// that the waves share; each wave then reads the stage from LDS for
 //  - the scores S^T = K Q^T (MFMA 16x16x32, keys x heads): the key operand
 //    is one 16-byte LDS read per lane per 32-dim chunk and 16 keys, the
 //    query operand stays in registers;
-//  - the weighted sum O^T += V^T P^T over 32 keys per MFMA: the V^T operand
+//  - the weighted sum O^T += V^T P^T (MFMA 16x16x32 over 32 keys, 16x16x16
+//    over 16): the V^T operand
 //    (four consecutive keys of one dim per lane, where the cache holds
 //    consecutive dims of one key) comes from the LDS transpose read
 //    ds_read_b64_tr_b16, so the latent is fetched from HBM once and needs
@@ -83,20 +85,29 @@ __device__ __forceinline__ bool req_ok(const MlaParams& P, int q0, int q1, int L
          L <= P.max_seq_len && (L + kMlaBlock - 1) / kMlaBlock <= P.bt_stride;
 }
 
-// Stages of request b (vector loads, one request per lane; 0 past the end
-// or out of bounds).  Query i of its Q tokens sees L - Q + 1 + i keys.
+// Stream items of request b (vector loads, one request per lane; 0 past the
+// end or out of bounds): per query token, qw head items then its key
+// stages.  Query i of its Q tokens sees L - Q + 1 + i keys.
 template <int SK>
-__device__ __forceinline__ int64_t req_stages(const MlaParams& P, int b) {
+__device__ __forceinline__ int64_t req_items(const MlaParams& P, int b, int qw) {
   if (b >= P.num_seqs) return 0;
   const int q0 = P.qsl[b], q1 = P.qsl[b + 1], L = P.seq_lens[b];
   if (!req_ok(P, q0, q1, L)) return 0;
-  return stage_prefix<SK>(L) - stage_prefix<SK>(L - (q1 - q0));
+  return (int64_t)(q1 - q0) * qw + stage_prefix<SK>(L) - stage_prefix<SK>(L - (q1 - q0));
 }
 
 __device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
   const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, l);
   const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)v >> 32), l);
   return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Range of workgroup b of a grid of g: with g = 8 q + r, the workgroups
+// b = x (mod 8) (those of XCD x) take ranges x q + min(x, r) + b / 8 onward,
+// a bijection of [0, g).
+__device__ __forceinline__ int xcd_range(int b, int g) {
+  const int x = b & 7, q = g >> 3, r = g & 7;
+  return x * q + min(x, r) + (b >> 3);
 }
 
 // Inclusive prefix sum over the wave's 64 lanes.
@@ -327,10 +338,14 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_dec
   // same scores without each reading the whole key tile.
   constexpr int kMaxC = (kKc + DQ - 1) / DQ;
   __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * kStageBytes];
-  // the range's stage table (query and key stages in stream order)
+  // the range's stage table (query and key stages in stream order; its
+  // last two slots hold the entry count and the key-stage count)
   __shared__ uint32_t stab[kTable];
   // partial scores of the waves (DQ > 1: 4 waves): [wave][sub-tile][lane]
   __shared__ f32x4 xsc[DQ > 1 ? 4 : 1][kSubs][64];
+  // two workgroups per compute unit with 16-key stages: at most 80 KiB each
+  static_assert(sizeof(ring) + sizeof(stab) + sizeof(xsc) <= (SK == 16 ? 81920u : 163840u),
+                "LDS of the decode workgroup");
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -351,10 +366,14 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_dec
     }
   }
 
-  // ---- this workgroup's range [I0, I1) of the stage stream --------------
-  // Each lane totals a contiguous run of C requests; a scan over the lanes
-  // gives the stream length M and the run holding stage I0, whose requests
-  // a second scan walks.  (Every wave computes the same.)
+  // ---- this workgroup's range [I0, I1) of the item stream ---------------
+  // The stream: per query token, qw head items (the cost of its query
+  // stages and of switching tokens, in key-stage times), then its key
+  // stages.  Each lane totals a contiguous run of C requests; a scan over
+  // the lanes gives the stream length M and the run holding item I0, whose
+  // requests a second scan walks.  (Every wave computes the same.)
+  const int qs = (P.Hq + SK - 1) / SK;  // query stages per token
+  const int qw = mla_token_items(P.Hq, SK);
   const int C = (P.num_seqs + 63) / 64;
   int64_t tot = 0;
   int wq0 = 0, wq1 = 0, wL = 0;  // C == 1: lane b's request metadata, kept
@@ -364,25 +383,29 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_dec
       wq1 = P.qsl[lane + 1];
       wL = P.seq_lens[lane];
       if (req_ok(P, wq0, wq1, wL))
-        tot = stage_prefix<SK>(wL) - stage_prefix<SK>(wL - (wq1 - wq0));
+        tot = (int64_t)(wq1 - wq0) * qw + stage_prefix<SK>(wL) -
+              stage_prefix<SK>(wL - (wq1 - wq0));
     }
   } else {
 #pragma unroll 4
-    for (int k = 0; k < C; ++k) tot += req_stages<SK>(P, lane * C + k);
+    for (int k = 0; k < C; ++k) tot += req_items<SK>(P, lane * C + k, qw);
   }
   const int64_t incl = wave_scan(tot);
   const int64_t M = readlane64(incl, 63);
   const int64_t R = (M + gridDim.x - 1) / gridDim.x;
-  const int64_t I0 = min((int64_t)blockIdx.x * R, M);
+  // range rg of workgroup blockIdx.x: workgroups go to the 8 XCDs in turn,
+  // and consecutive ranges (the pieces of one token, which read the same
+  // query) are given to workgroups of one XCD, so that they share its L2
+  const int rg = xcd_range(blockIdx.x, gridDim.x);
+  const int64_t I0 = min((int64_t)rg * R, M);
   const int64_t I1 = min(I0 + R, M);
-  if (I0 >= I1 || I1 - I0 > kTable) return;
-  const int nreal = (int)(I1 - I0);  // key stages of the range
+  if (I0 >= I1 || I1 - I0 > kTable - 2 - qs) return;
   const int lam = __builtin_ctzll(__builtin_amdgcn_ballot_w64(incl > I0));
   int64_t carry = readlane64(incl - tot, lam);
   int b0 = C == 1 ? lam : -1;
   int64_t s0 = I0 - carry;
   for (int k0 = 0; C > 1 && k0 < C; k0 += 64) {
-    const int64_t it = k0 + lane < C ? req_stages<SK>(P, lam * C + k0 + lane) : 0;
+    const int64_t it = k0 + lane < C ? req_items<SK>(P, lam * C + k0 + lane, qw) : 0;
     const int64_t inc = wave_scan(it) + carry;
     const uint64_t hit = __builtin_amdgcn_ballot_w64(inc > I0);
     if (hit) {
@@ -412,24 +435,29 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_dec
   }
   Cursor cur;
   cur.b = b0;
+  int64_t kpos;  // stream index of the current token's first key stage
   {
     int q0, q1, L;
     win.get(P, b0, q0, q1, L);
     cur.q0 = q0;
     cur.Q = q1 - q0;
     cur.L = L;
-    // token: the first i whose stages end past s0
+    // token: the last i whose items start at or before s0 (token i starts
+    // at i qw + its key stages before it)
     const int64_t before = stage_prefix<SK>(cur.L - cur.Q);
     int lo = 0, hi = cur.Q - 1;
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      if (stage_prefix<SK>(cur.L - cur.Q + 1 + mid) - before > s0)
+      if ((int64_t)(mid + 1) * qw + stage_prefix<SK>(cur.L - cur.Q + 1 + mid) - before > s0)
         hi = mid;
       else
         lo = mid + 1;
     }
     cur.i = lo;
-    cur.j = (int)(s0 - (stage_prefix<SK>(cur.L - cur.Q + lo) - before));
+    const int off = (int)(s0 - ((int64_t)lo * qw + stage_prefix<SK>(cur.L - cur.Q + lo) - before));
+    // a range starting among the head items starts the token at stage 0
+    cur.j = off < qw ? 0 : off - qw;
+    kpos = I0 - off + qw;
     cur.nst = token_stages<SK>(cur);
   }
 
@@ -452,46 +480,57 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_dec
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)ring;
 
   // ---- the first token's query stages: issued before the table is built -
-  const int qs = (P.Hq + SK - 1) / SK;  // query stages per token
-  const int pre = min(qs, kRing - 1);
-  for (int k = 0; k < pre; ++k)
-    dma_stage<SK>(P, kQStage | ((uint32_t)(cur.q0 + cur.i) << 3) | (uint32_t)k,
-              lring + k * kStageBytes, voff, p0, nl);
   // and its first key stage (block id read directly; the table's entry is
-  // the same)
-  int pre2 = pre;
-  if (qs < kRing - 1) {
-    int id = sload(P.bt + (int64_t)cur.b * P.bt_stride + cur.j / kPerBlock);
-    id = id < 0 ? 0 : (id >= P.num_blocks ? (int)(P.num_blocks - 1) : id);
-    dma_stage<SK>(P, ((uint32_t)id << 2) | (uint32_t)(cur.j % kPerBlock),
-                  lring + qs * kStageBytes, voff, p0, nl);
-    pre2 = qs + 1;
-  }
+  // the same).  Wave 0, which builds the table, issues its share after it:
+  // its block-id loads would otherwise wait for these loads (the vector
+  // memory counter retires in order).
+  const int pre = min(qs, kRing - 1);
+  const int pre2 = qs < kRing - 1 ? qs + 1 : pre;
+  auto issue_first = [&]() {
+    for (int k = 0; k < pre; ++k)
+      dma_stage<SK>(P, kQStage | ((uint32_t)(cur.q0 + cur.i) << 3) | (uint32_t)k,
+                    lring + k * kStageBytes, voff, p0, nl);
+    if (pre2 > pre) {
+      int id = sload(P.bt + (int64_t)cur.b * P.bt_stride + cur.j / kPerBlock);
+      id = id < 0 ? 0 : (id >= P.num_blocks ? (int)(P.num_blocks - 1) : id);
+      dma_stage<SK>(P, ((uint32_t)id << 2) | (uint32_t)(cur.j % kPerBlock),
+                    lring + qs * kStageBytes, voff, p0, nl);
+    }
+  };
+  if (w != 0) issue_first();
 
   // ---- the range's stage table (wave 0; one gather) -----------------------
-  // Token by token: its query stages, then (request - b0) << 14 | stage of
-  // each key stage; then each lane turns its key entries into block ids
-  // with one block-table load each.
-  constexpr int kCap = kTable - 1;  // the last slot holds the count
+  // Token by token, for each token with key stages in the range: its query
+  // stages, then (request - b0) << 14 | stage of each of those key stages;
+  // then each lane turns its key entries into block ids with one
+  // block-table load each.  At most R + qs entries (a token's query stages
+  // are entries of the range only where its head items are, but the
+  // first's).
+  constexpr int kCap = kTable - 2;  // entries; then the two counts
   if (w == 0) {
     Cursor f = cur;
-    int x = 0;
-    for (int done = 0; done < nreal;) {
-      if (x + qs + min(f.nst - f.j, nreal - done) > kCap) {
-        x = -1;  // cannot happen with the launch's grid: it bounds R
-        break;
+    int64_t fpos = kpos;
+    int x = 0, nk = 0;
+    for (;;) {
+      const int64_t ka = max(I0, fpos), kb = min(I1, fpos + f.nst);
+      if (kb > ka) {
+        const int cnt = (int)(kb - ka), j0 = (int)(ka - fpos);
+        if (x + qs + cnt > kCap) {
+          x = -1;  // cannot happen with the launch's grid: it bounds R
+          break;
+        }
+        if (lane < qs) stab[x + lane] = kQStage | ((uint32_t)(f.q0 + f.i) << 3) | (uint32_t)lane;
+        x += qs;
+        for (int y = lane; y < cnt; y += 64)
+          stab[x + y] = ((uint32_t)(f.b - b0) << 14) | (uint32_t)(j0 + y);
+        x += cnt;
+        nk += cnt;
       }
-      if (lane < qs) stab[x + lane] = kQStage | ((uint32_t)(f.q0 + f.i) << 3) | (uint32_t)lane;
-      x += qs;
-      const int cnt = min(f.nst - f.j, nreal - done);
-      for (int y = lane; y < cnt; y += 64)
-        stab[x + y] = ((uint32_t)(f.b - b0) << 14) | (uint32_t)(f.j + y);
-      x += cnt;
-      done += cnt;
-      if (done < nreal) {
-        f.j = f.nst - 1;
-        cursor_next<SK>(f, P, win);
-      }
+      // the next token's key stages start past its head items
+      fpos += f.nst + qw;
+      if (fpos >= I1) break;
+      f.j = f.nst - 1;
+      cursor_next<SK>(f, P, win);
     }
 #pragma unroll 4
     for (int y = lane; y < x; y += 64) {
@@ -502,13 +541,18 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_dec
       id = id < 0 ? 0 : (id >= P.num_blocks ? (int)(P.num_blocks - 1) : id);
       stab[y] = ((uint32_t)id << 2) | (uint32_t)(j % kPerBlock);
     }
-    if (lane == 0) stab[kCap] = (uint32_t)x;
+    if (lane == 0) {
+      stab[kCap] = (uint32_t)x;
+      stab[kCap + 1] = (uint32_t)nk;
+    }
+    issue_first();
   }
   // (an LDS-only barrier: __syncthreads() would also wait for the ring
   // loads just issued)
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   const int n = (int)__builtin_amdgcn_readfirstlane(stab[kCap]);
-  if (n <= 0) {  // (no LDS write of the ring may outlive the workgroup)
+  const int nreal = (int)__builtin_amdgcn_readfirstlane(stab[kCap + 1]);  // key stages of the range
+  if (n <= 0 || nreal <= 0) {  // (no LDS write of the ring may outlive the workgroup)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     return;
   }
@@ -683,10 +727,10 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_dec
         *reinterpret_cast<bf16x4*>(op + 16 * k) = o;
       }
     } else {
-      // slot 2w: the range's first token; 2w + 1: its last (only these two
+      // slot 2 rg: the range's first token; 2 rg + 1: its last (only these two
       // can be cut).  The piece's normalised output in bf16, its (max, sum)
       // in fp32.
-      const int64_t row = (2 * (int64_t)blockIdx.x + (first_tok ? 0 : 1)) * P.Hq + h;
+      const int64_t row = (2 * (int64_t)rg + (first_tok ? 0 : 1)) * P.Hq + h;
       uint16_t* ap = P.part_out + row * kMlaLatent + dim0;
       const float inv = 1.0f / l;
 #pragma unroll
@@ -698,18 +742,19 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_dec
       }
       if (dq == 0 && g == 0) P.part_ml[row] = make_float2(mrun, l);
     }
-    // the workgroup holding the token's first stage records which workgroups
-    // hold its pieces: this one, then whole ranges, the last one (R stages
-    // each) ending at or after the token's last stage
+    // the workgroup holding the token's first key stage records which
+    // workgroups hold its pieces: this one, then whole ranges, the last one
+    // (R items each) holding the token's last key stage
     if (cur.j == 0 && threadIdx.x == 0 && P.seg) {
-      const int64_t last = I0 + done + cur.nst - 1;
-      const int pieces = (int)(last / R - blockIdx.x + 1);
-      P.seg[t] = make_int2((int)blockIdx.x, 2 * pieces + (first_tok ? 0 : 1));
+      const int64_t last = kpos + cur.nst - 1;
+      const int pieces = (int)(last / R - rg + 1);
+      P.seg[t] = make_int2(rg, 2 * pieces + (first_tok ? 0 : 1));
     }
     stored = kRing - 1;
     first_tok = false;
     done += cnt;
     if (done < nreal) {
+      kpos += cur.nst + qw;
       cur.j = cur.nst - 1;
       cursor_next<SK>(cur, P, win);
     }

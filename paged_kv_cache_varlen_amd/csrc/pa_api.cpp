@@ -853,7 +853,7 @@ size_t pa_mla_workspace_size(int64_t num_q_tokens, int32_t num_q_heads,
                              int32_t max_seq_len) {
   if (num_q_tokens < 0 || num_q_heads <= 0 || num_q_heads % 16 != 0 || max_seq_len < 0)
     return 0;
-  return pa::mla_layout(num_q_tokens, num_q_heads, max_seq_len).total;
+  return pa::mla_layout(num_q_tokens, num_q_heads, max_seq_len).total;  // 0 past kMlaMaxGrid
 }
 
 pa_status pa_mla_write_kv(const void* kv, int64_t kv_token_stride,
@@ -906,6 +906,8 @@ pa_status pa_mla_decode(const void* q, const void* cache, int64_t num_blocks,
   if (((uintptr_t)q | (uintptr_t)cache | (uintptr_t)out) & 15)
     return fail(PA_ERR_SHAPE, "q, out and the cache must be 16-byte aligned");
   const pa::MlaLayout m = pa::mla_layout(num_q_tokens, num_q_heads, max_seq_len);
+  if (m.grid <= 0)
+    return fail(PA_ERR_UNSUPPORTED, "pa_mla_decode: more work than one launch takes");
   if (((int64_t)num_q_tokens * num_q_heads + 3) / 4 > INT32_MAX)
     return fail(PA_ERR_SHAPE, "pa_mla_decode: too many (token, head) rows");
   if (m.grid > 1) {

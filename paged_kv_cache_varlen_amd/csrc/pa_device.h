@@ -221,7 +221,7 @@ struct MlaParams {
   int32_t num_q_tokens;
   int32_t Hq;
   int32_t max_seq_len;
-  int32_t grid;        // decode workgroups (equal ranges of the stage stream)
+  int32_t grid;        // decode workgroups (equal ranges of the item stream)
   float scale_log2;
   uint16_t* out;       // [T][Hq][512]
   int2* seg;           // [T]: (first workgroup, 2 * workgroups + slot flag)
@@ -229,21 +229,30 @@ struct MlaParams {
   uint16_t* part_out;  // [2 grid][Hq][512]: a piece's normalised output (bf16)
 };
 
-// The decode's work is a stream of stages of SK keys (each query token's
-// keys in stages of SK: 16 for 16 and 32 query heads, 32 for more), cut into
-// ranges of R = ceil(stages / grid) stages, one per workgroup; in a
-// workgroup's table each token of its range also takes ceil(Hq / SK) query
-// stages.  grid: 512 for SK = 16 (80 KiB of LDS per workgroup, two per
-// compute unit), 256 for SK = 32 (160 KiB, one); more when a range's table
-// could exceed its entries, never more than the stages there can be.  Only a
-// range's first and last token can be cut, so a workgroup leaves at most two
-// partial results (slots 2w and 2w + 1).  One workgroup sees every stage: no
-// partials (the workspace is then a nominal 256 bytes, never touched).
+// The decode's work is a stream of items: per query token, qw head items
+// (its ceil(Hq / SK) query stages and the switch to it, costed in key-stage
+// times) and then its keys in stages of SK (16 for 16 and 32 query heads, 32
+// for more).  The stream is cut into ranges of R = ceil(items / grid) items,
+// one per workgroup; a workgroup's table holds, for each token with key
+// stages in its range, the query stages and those key stages: at most
+// R + ceil(Hq / SK) entries (and two counts).  grid: 512 for SK = 16 (80 KiB of LDS per
+// workgroup, two per compute unit), 256 for SK = 32 (160 KiB, one); more
+// when a range's table could exceed its entries, never more than the items
+// there can be.  Only a range's first and last token can be cut, so a
+// workgroup leaves at most two partial results (slots 2 rg and 2 rg + 1 of
+// its range rg).  One workgroup sees every item: no partials (the workspace
+// is then a nominal 256 bytes, never touched).
 constexpr int mla_stage_keys(int num_q_heads) { return num_q_heads <= 32 ? 16 : 32; }
 constexpr int mla_table_entries(int stage_keys) { return stage_keys == 16 ? 1024 : 2048; }
+// Head items per query token (measured: a token switch costs about its
+// query stages plus two 16-key stages, or one 32-key stage).
+__host__ __device__ constexpr int mla_token_items(int num_q_heads, int stage_keys) {
+  return (num_q_heads + stage_keys - 1) / stage_keys + (stage_keys == 16 ? 2 : 1);
+}
 constexpr int kMlaMaxSeqs = 1 << 17;        // request index in a table entry: 17 bits
 constexpr int64_t kMlaMaxTokens = 1 << 27;  // token index in a table entry: 28 bits
 constexpr int64_t kMlaMaxBlocks = 1 << 29;  // block id in a table entry: 29 bits
+constexpr int64_t kMlaMaxGrid = 1 << 30;    // decode workgroups of one launch
 struct MlaLayout {
   int32_t grid;
   size_t seg;
@@ -255,14 +264,17 @@ inline MlaLayout mla_layout(int64_t num_q_tokens, int32_t num_q_heads,
                             int32_t max_seq_len) {
   MlaLayout m{};
   const int sk = mla_stage_keys(num_q_heads);
-  const int64_t most = num_q_tokens * cdiv64(max_seq_len > 0 ? max_seq_len : 1, sk);
-  // a range of R key stages spans at most R tokens: R (1 + query stages)
-  // table entries
-  const int64_t per_stage = 1 + cdiv64(num_q_heads > 0 ? num_q_heads : 16, sk);
-  int64_t grid = cdiv64(most * per_stage, mla_table_entries(sk) - 1);
+  const int hq = num_q_heads > 0 ? num_q_heads : 16;
+  const int64_t most =
+      num_q_tokens * (cdiv64(max_seq_len > 0 ? max_seq_len : 1, sk) + mla_token_items(hq, sk));
+  // a range of R items has at most R + qs table entries (the table's last
+  // two slots hold counts)
+  const int64_t qs = cdiv64(hq, sk);
+  int64_t grid = cdiv64(most, mla_table_entries(sk) - 2 - qs);
   const int64_t floor = sk == 16 ? 512 : 256;
   if (grid < floor) grid = floor;
   if (grid > most) grid = most > 0 ? most : 1;
+  if (grid > kMlaMaxGrid) return m;  // grid 0: more work than one launch takes
   m.grid = (int32_t)grid;
   if (m.grid == 1) {
     m.total = 256;

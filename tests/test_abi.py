@@ -390,3 +390,52 @@ def test_expand_block_tables_argument_checks(lib):
     assert lib.pa_expand_block_tables(None, 4, 8, 32, FAKE, None) == _lib.PA_ERR_NULL
     assert lib.pa_expand_block_tables(FAKE, 0, 8, 32, FAKE, None) == _lib.PA_OK
     assert lib.pa_expand_block_tables(FAKE, 4, 1 << 30, 64, FAKE, None) == _lib.PA_ERR_SHAPE
+
+
+# ---- MLA latent decode --------------------------------------------------------------
+
+FAKE = 4096  # a 256-byte-aligned non-NULL address: every call below fails its checks first
+
+
+def mla_args(**over):
+    a = dict(q=FAKE, cache=FAKE, nb=16, bt=FAKE, mbs=4, sl=FAKE, qsl=FAKE, B=2, T=2, Hq=16,
+             maxL=256, scale=0.07, out=FAKE, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(over)
+    return [a[k] for k in ("q", "cache", "nb", "bt", "mbs", "sl", "qsl", "B", "T", "Hq", "maxL",
+                           "scale", "out", "ws", "wsb", "stream")]
+
+
+def test_mla_workspace_size(lib):
+    small = lib.pa_mla_workspace_size(64, 16, 4096)
+    assert small > 0 and small % 256 == 0
+    # more heads, more partial rows
+    assert lib.pa_mla_workspace_size(64, 128, 4096) > small
+    assert lib.pa_mla_workspace_size(64, 24, 4096) == 0      # not a multiple of 16
+    assert lib.pa_mla_workspace_size(-1, 16, 4096) == 0
+    # more work than one launch's grid: no size, and the decode refuses it
+    assert lib.pa_mla_workspace_size((1 << 27) - 1, 16, 1 << 18) == 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(Hq=24), _lib.PA_ERR_UNSUPPORTED),
+    (dict(Hq=144), _lib.PA_ERR_UNSUPPORTED),
+    (dict(maxL=(1 << 18) + 1), _lib.PA_ERR_UNSUPPORTED),
+    (dict(B=(1 << 17) + 1), _lib.PA_ERR_UNSUPPORTED),
+    (dict(nb=(1 << 29) + 1), _lib.PA_ERR_UNSUPPORTED),
+    (dict(T=(1 << 27) - 1, maxL=1 << 18), _lib.PA_ERR_UNSUPPORTED),   # grid past one launch
+    (dict(q=None), _lib.PA_ERR_NULL),
+    (dict(scale=0.0), _lib.PA_ERR_SHAPE),
+    (dict(q=FAKE + 8), _lib.PA_ERR_SHAPE),                              # 16-byte alignment
+    (dict(ws=None), _lib.PA_ERR_WORKSPACE),
+    (dict(wsb=256), _lib.PA_ERR_WORKSPACE),
+    (dict(ws=FAKE + 16), _lib.PA_ERR_WORKSPACE),                        # 256-byte alignment
+    (dict(T=-1), _lib.PA_ERR_SHAPE),
+])
+def test_mla_decode_rejects_bad_arguments(lib, over, status):
+    assert lib.pa_mla_decode(*mla_args(**over)) == status
+    assert lib.pa_last_error() != b""
+
+
+def test_mla_decode_empty_batch_is_ok(lib):
+    assert lib.pa_mla_decode(*mla_args(T=0)) == _lib.PA_OK
+    assert lib.pa_mla_decode(*mla_args(B=0)) == _lib.PA_OK
