@@ -763,7 +763,7 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_dec
 
 // One wave per (query token, head) whose keys were cut between workgroups:
 // log-sum-exp over the pieces.  The lanes read the pieces' (max, sum) in
-// parallel (64 pieces per round) along with the outputs of the first four
+// parallel (64 pieces per round) along with the outputs of the first eight
 // pieces, then every lane adds its 8 dims of each piece's output, weighted;
 // lane i holds dims 8i .. 8i+7.  The decode
 // writes every token's record in every launch ((0, 0) for tokens of
@@ -787,7 +787,9 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaParams P) {
   // normalised output (bf16), (m_i, l_i) its running max and sum
   float M = -INFINITY, den = 0.0f;
   float n[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  constexpr int kAhead = 4;  // pieces whose outputs are loaded with the (max, sum) round
+  // pieces whose outputs are loaded with the (max, sum) round (a token of
+  // a few requests typically has 4 to 10)
+  constexpr int kAhead = 8;
   for (int s0 = 0; s0 < pieces; s0 += 64) {
     const int cnt = min(64, pieces - s0);
     float2 ml = make_float2(-INFINITY, 0.0f);
@@ -820,6 +822,7 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaParams P) {
         for (int e = 0; e < 8; ++e) n[e] += wk * (float)oa[k][e];
       }
     }
+#pragma unroll 4
     for (int k = kAhead; k < cnt; ++k) {
       const float wk = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wgt), k));
       const bf16x8 ok = *reinterpret_cast<const bf16x8*>(P.part_out + row_of(s0 + k) * kMlaLatent +
