@@ -609,15 +609,17 @@ pa_status pa_expand_block_tables(const int32_t *block_tables, int32_t num_seqs,
  *   kv + i * kv_token_stride elements; stride a multiple of 8) into the cache
  *   at slot_mapping[i] (device int64; < 0 or >= num_blocks * 64: skipped).
  * pa_mla_workspace_size - workspace bytes of pa_mla_decode (per-token
- *   records and the partial results of tokens whose keys are cut between
- *   workgroups: at most two per workgroup); 0 for invalid arguments and
- *   for work beyond one launch (num_q_tokens x max_seq_len above about 2^44
- *   keys), which pa_mla_decode rejects with PA_ERR_UNSUPPORTED.
+ *   records and the partial results of query tokens whose keys are cut
+ *   between workgroups: at most two groups of tokens per workgroup), enough
+ *   for either of the decode's two forms (one query token per work item, or
+ *   groups of 128 / num_q_heads consecutive tokens of a request for 16, 32
+ *   and 64 heads when the batch averages 4 or more query tokens per
+ *   request); 0 for invalid arguments.
  * pa_mla_decode - q device bf16 [num_q_tokens][num_q_heads][576], out device
  *   bf16 [num_q_tokens][num_q_heads][512]; block_tables of 64-token block ids
  *   [num_seqs][max_blocks_per_seq]; seq_lens, query_start_loc as pa_attend;
  *   num_q_heads a multiple of 16, at most 128, max_seq_len at most 262144,
- *   num_seqs at most 131072, num_q_tokens below 2^27 and num_blocks at most
+ *   num_seqs at most 131072, num_q_tokens below 2^25 and num_blocks at most
  *   2^29 (PA_ERR_UNSUPPORTED otherwise); query_start_loc non-decreasing;
  *   workspace >= pa_mla_workspace_size(...) bytes, 256-byte aligned.  A
  *   request whose metadata is out of bounds is skipped (its rows unwritten).

@@ -85,15 +85,39 @@ __device__ __forceinline__ bool req_ok(const MlaParams& P, int q0, int q1, int L
          L <= P.max_seq_len && (L + kMlaBlock - 1) / kMlaBlock <= P.bt_stride;
 }
 
-// Stream items of request b (vector loads, one request per lane; 0 past the
-// end or out of bounds): per query token, qw head items then its key
-// stages.  Query i of its Q tokens sees L - Q + 1 + i keys.
+// Key stages of the first k groups of G query tokens of a request, all full
+// groups, whose k'-th group's last token sees a + k' G keys: the sum of
+// ceil((a + k' G) / SK).  With SK = m G that is floor((c + k') / m),
+// c = floor((a + SK - 1) / G), whose partial sums have a closed form.
 template <int SK>
-__device__ __forceinline__ int64_t req_items(const MlaParams& P, int b, int qw) {
+__device__ __forceinline__ int64_t group_prefix(int64_t k, int64_t a, int G) {
+  const int64_t m = SK / G, c = (a + SK - 1) / G;
+  auto tri = [m](int64_t n) {  // sum_{x < n} floor(x / m)
+    const int64_t q = n / m, r = n % m;
+    return m * q * (q - 1) / 2 + q * r;
+  };
+  return tri(c + k) - tri(c);
+}
+
+// Stream items of a request of Q query tokens and L keys in groups of G:
+// per group, qw head items, then the stages of the keys its last token sees
+// (query i of the Q sees L - Q + 1 + i keys; a last partial group's last
+// token sees L).
+template <int SK>
+__device__ __forceinline__ int64_t items_of(int Q, int L, int G, int qw) {
+  if (Q <= 0) return 0;
+  const int ng = (Q + G - 1) / G;
+  return (int64_t)ng * qw + group_prefix<SK>(ng - 1, L - Q + G, G) + (L + SK - 1) / SK;
+}
+
+// Stream items of request b (vector loads, one request per lane; 0 past the
+// end or out of bounds).
+template <int SK>
+__device__ __forceinline__ int64_t req_items(const MlaParams& P, int b, int qw, int G) {
   if (b >= P.num_seqs) return 0;
   const int q0 = P.qsl[b], q1 = P.qsl[b + 1], L = P.seq_lens[b];
   if (!req_ok(P, q0, q1, L)) return 0;
-  return (int64_t)(q1 - q0) * qw + stage_prefix<SK>(L) - stage_prefix<SK>(L - (q1 - q0));
+  return items_of<SK>(q1 - q0, L, G, qw);
 }
 
 __device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
@@ -121,16 +145,20 @@ __device__ __forceinline__ int64_t wave_scan(int64_t v) {
   return v;
 }
 
-// Position in the stage stream: request b (metadata q0, Q, L), its token i,
-// stage j of that token's nst stages.  Every field is wave-uniform.
+// Position in the stream: request b (metadata q0, Q, L), its group i of
+// ntok query tokens (tokens q0 + G i ..), stage j of the group's nst stages
+// (those of the nvis keys its last token sees).  Every field is
+// wave-uniform.
 struct Cursor {
   int b, q0, Q, L;
-  int i, j, nst;
+  int i, j, nst, ntok, nvis;
 };
 
 template <int SK>
-__device__ __forceinline__ int token_stages(const Cursor& c) {
-  return (c.L - c.Q + 1 + c.i + SK - 1) / SK;
+__device__ __forceinline__ void cursor_group(Cursor& c, int G) {
+  c.ntok = min(G, c.Q - c.i * G);
+  c.nvis = c.L - c.Q + c.i * G + c.ntok;
+  c.nst = (c.nvis + SK - 1) / SK;
 }
 
 // Metadata of the requests b0 .. b0 + 63, one per lane (loaded once), and
@@ -157,10 +185,10 @@ struct ReqWindow {
 // never used.
 template <int SK>
 __device__ __forceinline__ void cursor_next(Cursor& c, const MlaParams& P,
-                                            const ReqWindow& win) {
+                                            const ReqWindow& win, int G) {
   if (++c.j < c.nst) return;
   c.j = 0;
-  if (++c.i >= c.Q) {
+  if (++c.i >= (c.Q + G - 1) / G) {
     c.i = 0;
     for (;;) {
       if (++c.b >= P.num_seqs) {
@@ -180,7 +208,7 @@ __device__ __forceinline__ void cursor_next(Cursor& c, const MlaParams& P,
       }
     }
   }
-  c.nst = token_stages<SK>(c);
+  cursor_group<SK>(c, G);
 }
 
 // Global-to-LDS copy of one KiB: lane i reads 16 bytes at gaddr + voff and
@@ -208,9 +236,10 @@ __device__ __forceinline__ void dma_kib(uint64_t gaddr, uint32_t voff, uint32_t 
 }
 
 // Entries of a range's stage table: a key stage is block id * 4 + which SK
-// keys of the block (bit 31 clear); a query stage is kQStage | token << 3 |
-// k: the queries of heads SK k .. SK k + SK - 1 of that token (SK * 1152
-// bytes, fewer for a last partial group), which precede the token's key
+// keys of the block (bit 31 clear); a query stage is kQStage | t0 << 6 |
+// (ntok - 1) << 3 | k: (token, head) rows SK k .. SK k + SK - 1 of the group
+// of ntok tokens from token t0 (its rows t0 Hq .. are consecutive in q;
+// SK * 1152 bytes, fewer for the last), which precede the group's key
 // stages.
 constexpr uint32_t kQStage = 0x80000000u;
 
@@ -225,10 +254,11 @@ __device__ __forceinline__ void dma_stage(const MlaParams& P, uint32_t e, uint32
   int pieces;
   uint32_t vo;
   if (e & kQStage) {
-    const int64_t t = (e & ~kQStage) >> 3;
+    const int64_t t = (e & ~kQStage) >> 6;
+    const int ntok = (int)((e >> 3) & 7) + 1;
     const int k = e & 7;
     g = (uint64_t)(uintptr_t)(P.q + (t * P.Hq + SK * k) * kMlaDim);
-    pieces = min(SK, P.Hq - SK * k) * (kMlaDim * 2) / 1024;
+    pieces = min(SK, ntok * P.Hq - SK * k) * (kMlaDim * 2) / 1024;
     vo = (uint32_t)(16 * (threadIdx.x & 63));
   } else {
     g = (uint64_t)(uintptr_t)(P.cache + (int64_t)(e >> 2) * kBlockElems) +
@@ -317,10 +347,12 @@ __global__ __launch_bounds__(256) void mla_write_kv_kernel(
 
 // DQ waves per 16 heads (4, 2 or 1), each with 512 / DQ output dims; stages
 // of SK keys (16: 80 KiB of LDS, two workgroups per compute unit; 32: 160
-// KiB, one).
-template <int DQ, int SK>
+// KiB, one).  GRP: groups of P.G query tokens (one wave per 16 of the
+// group's (token, head) rows); otherwise one token per group.
+template <int DQ, int SK, bool GRP>
 __global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_decode_kernel(
     MlaParams P) {
+  static_assert(!GRP || DQ == 1, "groups of tokens: one wave per 16 rows");
   constexpr int kTiles = kMlaLatent / 16 / DQ;  // 16-dim output tiles per wave
   constexpr int kSubs = Geo<SK>::kSubs;
   constexpr int kStageBytes = Geo<SK>::kStageBytes;
@@ -367,13 +399,15 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_dec
   }
 
   // ---- this workgroup's range [I0, I1) of the item stream ---------------
-  // The stream: per query token, qw head items (the cost of its query
-  // stages and of switching tokens, in key-stage times), then its key
-  // stages.  Each lane totals a contiguous run of C requests; a scan over
-  // the lanes gives the stream length M and the run holding item I0, whose
-  // requests a second scan walks.  (Every wave computes the same.)
-  const int qs = (P.Hq + SK - 1) / SK;  // query stages per token
-  const int qw = mla_token_items(P.Hq, SK);
+  // The stream: per group of G query tokens of a request, qw head items (the
+  // cost of its query stages and of switching groups, in key-stage times),
+  // then the key stages of its last token.  Each lane totals a contiguous
+  // run of C requests; a scan over the lanes gives the stream length M and
+  // the run holding item I0, whose requests a second scan walks.  (Every
+  // wave computes the same.)
+  const int G = GRP ? P.G : 1;
+  const int qs = (G * P.Hq + SK - 1) / SK;  // query stages of a full group
+  const int qw = mla_token_items(G * P.Hq, SK);
   const int C = (P.num_seqs + 63) / 64;
   int64_t tot = 0;
   int wq0 = 0, wq1 = 0, wL = 0;  // C == 1: lane b's request metadata, kept
@@ -382,13 +416,11 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_dec
       wq0 = P.qsl[lane];
       wq1 = P.qsl[lane + 1];
       wL = P.seq_lens[lane];
-      if (req_ok(P, wq0, wq1, wL))
-        tot = (int64_t)(wq1 - wq0) * qw + stage_prefix<SK>(wL) -
-              stage_prefix<SK>(wL - (wq1 - wq0));
+      if (req_ok(P, wq0, wq1, wL)) tot = items_of<SK>(wq1 - wq0, wL, G, qw);
     }
   } else {
 #pragma unroll 4
-    for (int k = 0; k < C; ++k) tot += req_items<SK>(P, lane * C + k, qw);
+    for (int k = 0; k < C; ++k) tot += req_items<SK>(P, lane * C + k, qw, G);
   }
   const int64_t incl = wave_scan(tot);
   const int64_t M = readlane64(incl, 63);
@@ -405,7 +437,7 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_dec
   int b0 = C == 1 ? lam : -1;
   int64_t s0 = I0 - carry;
   for (int k0 = 0; C > 1 && k0 < C; k0 += 64) {
-    const int64_t it = k0 + lane < C ? req_items<SK>(P, lam * C + k0 + lane, qw) : 0;
+    const int64_t it = k0 + lane < C ? req_items<SK>(P, lam * C + k0 + lane, qw, G) : 0;
     const int64_t inc = wave_scan(it) + carry;
     const uint64_t hit = __builtin_amdgcn_ballot_w64(inc > I0);
     if (hit) {
@@ -435,30 +467,30 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_dec
   }
   Cursor cur;
   cur.b = b0;
-  int64_t kpos;  // stream index of the current token's first key stage
+  int64_t kpos;  // stream index of the current group's first key stage
   {
     int q0, q1, L;
     win.get(P, b0, q0, q1, L);
     cur.q0 = q0;
     cur.Q = q1 - q0;
     cur.L = L;
-    // token: the last i whose items start at or before s0 (token i starts
-    // at i qw + its key stages before it)
-    const int64_t before = stage_prefix<SK>(cur.L - cur.Q);
-    int lo = 0, hi = cur.Q - 1;
+    // group: the last i whose items start at or before s0 (group i starts
+    // at i qw + the key stages of the groups before it, all full)
+    const int64_t a = cur.L - cur.Q + G;
+    int lo = 0, hi = (cur.Q + G - 1) / G - 1;
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      if ((int64_t)(mid + 1) * qw + stage_prefix<SK>(cur.L - cur.Q + 1 + mid) - before > s0)
+      if ((int64_t)(mid + 1) * qw + group_prefix<SK>(mid + 1, a, G) > s0)
         hi = mid;
       else
         lo = mid + 1;
     }
     cur.i = lo;
-    const int off = (int)(s0 - ((int64_t)lo * qw + stage_prefix<SK>(cur.L - cur.Q + lo) - before));
-    // a range starting among the head items starts the token at stage 0
+    const int off = (int)(s0 - ((int64_t)lo * qw + group_prefix<SK>(lo, a, G)));
+    // a range starting among the head items starts the group at stage 0
     cur.j = off < qw ? 0 : off - qw;
     kpos = I0 - off + qw;
-    cur.nst = token_stages<SK>(cur);
+    cursor_group<SK>(cur, G);
   }
 
   // ---- lane constants of the LDS layout ---------------------------------
@@ -479,31 +511,37 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_dec
   const uint32_t lring =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)ring;
 
-  // ---- the first token's query stages: issued before the table is built -
+  // ---- the first group's query stages: issued before the table is built -
   // and its first key stage (block id read directly; the table's entry is
   // the same).  Wave 0, which builds the table, issues its share after it:
   // its block-id loads would otherwise wait for these loads (the vector
   // memory counter retires in order).
-  const int pre = min(qs, kRing - 1);
-  const int pre2 = qs < kRing - 1 ? qs + 1 : pre;
+  // (query stages of a group, and the table entry of its k-th)
+  auto group_qs = [&](const Cursor& c) { return (c.ntok * P.Hq + SK - 1) / SK; };
+  auto qentry = [&](const Cursor& c, int k) {
+    return kQStage | ((uint32_t)(c.q0 + c.i * G) << 6) | ((uint32_t)(c.ntok - 1) << 3) |
+           (uint32_t)k;
+  };
+  const int qs0 = group_qs(cur);
+  const int pre = min(qs0, kRing - 1);
+  const int pre2 = qs0 < kRing - 1 ? qs0 + 1 : pre;
   auto issue_first = [&]() {
     for (int k = 0; k < pre; ++k)
-      dma_stage<SK>(P, kQStage | ((uint32_t)(cur.q0 + cur.i) << 3) | (uint32_t)k,
-                    lring + k * kStageBytes, voff, p0, nl);
+      dma_stage<SK>(P, qentry(cur, k), lring + k * kStageBytes, voff, p0, nl);
     if (pre2 > pre) {
       int id = sload(P.bt + (int64_t)cur.b * P.bt_stride + cur.j / kPerBlock);
       id = id < 0 ? 0 : (id >= P.num_blocks ? (int)(P.num_blocks - 1) : id);
       dma_stage<SK>(P, ((uint32_t)id << 2) | (uint32_t)(cur.j % kPerBlock),
-                    lring + qs * kStageBytes, voff, p0, nl);
+                    lring + qs0 * kStageBytes, voff, p0, nl);
     }
   };
   if (w != 0) issue_first();
 
   // ---- the range's stage table (wave 0; one gather) -----------------------
-  // Token by token, for each token with key stages in the range: its query
+  // Group by group, for each group with key stages in the range: its query
   // stages, then (request - b0) << 14 | stage of each of those key stages;
   // then each lane turns its key entries into block ids with one
-  // block-table load each.  At most R + qs entries (a token's query stages
+  // block-table load each.  At most R + qs entries (a group's query stages
   // are entries of the range only where its head items are, but the
   // first's).
   constexpr int kCap = kTable - 2;  // entries; then the two counts
@@ -514,23 +552,23 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_dec
     for (;;) {
       const int64_t ka = max(I0, fpos), kb = min(I1, fpos + f.nst);
       if (kb > ka) {
-        const int cnt = (int)(kb - ka), j0 = (int)(ka - fpos);
-        if (x + qs + cnt > kCap) {
+        const int cnt = (int)(kb - ka), j0 = (int)(ka - fpos), qsf = group_qs(f);
+        if (x + qsf + cnt > kCap) {
           x = -1;  // cannot happen with the launch's grid: it bounds R
           break;
         }
-        if (lane < qs) stab[x + lane] = kQStage | ((uint32_t)(f.q0 + f.i) << 3) | (uint32_t)lane;
-        x += qs;
+        if (lane < qsf) stab[x + lane] = qentry(f, lane);
+        x += qsf;
         for (int y = lane; y < cnt; y += 64)
           stab[x + y] = ((uint32_t)(f.b - b0) << 14) | (uint32_t)(j0 + y);
         x += cnt;
         nk += cnt;
       }
-      // the next token's key stages start past its head items
+      // the next group's key stages start past its head items
       fpos += f.nst + qw;
       if (fpos >= I1) break;
       f.j = f.nst - 1;
-      cursor_next<SK>(f, P, win);
+      cursor_next<SK>(f, P, win, G);
     }
 #pragma unroll 4
     for (int y = lane; y < x; y += 64) {
@@ -577,17 +615,25 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_dec
                 lring + (uint32_t)((it + kRing - 1) % kRing) * kStageBytes, voff, p0, nl);
   };
 
-  // One token's piece of the range per pass: its query stages, then its key
-  // stages.  (The query operand lives within a pass.)
+  // The wave's 16 (token, head) rows of a group: rows 16 hg .. 16 hg + 15,
+  // token tw of the group, heads 16 hg - tw Hq .. (one token's heads: Hq is
+  // a multiple of 16).
+  const int vrow = 16 * hg;
+  const int tw = vrow / P.Hq;
+  // One group's piece of the range per pass: its query stages, then its key
+  // stages.  (The query operand lives within a pass.)  A wave whose token is
+  // past a short group's last takes part in the waits and barriers only.
   while (done < nreal) {
-    bf16x8 qop[kMaxC];  // lane (r, g): head 16 hg + r, dims 32 (c0 + i) + 8g .. +7
-    for (int k = 0; k < qs; ++k, ++it) {
+    const bool active = !GRP || tw < cur.ntok;
+    bf16x8 qop[kMaxC];  // lane (r, g): row vrow + r, dims 32 (c0 + i) + 8g .. +7
+    const int qsg = group_qs(cur);
+    for (int k = 0; k < qsg; ++k, ++it) {
       ring_step();
-      if (k == 16 * hg / SK) {
-        // lane (r, g): head 16 hg + r (row (16 hg) % SK + r of the stage),
-        // dims 8g .. of each chunk
+      if (active && k == vrow / SK) {
+        // lane (r, g): row vrow + r (row vrow % SK + r of the stage), dims
+        // 8g .. of each chunk
         const uint8_t* st = ring + (it % kRing) * kStageBytes +
-                            (16 * hg % SK + r) * (kMlaDim * 2) + g * 16 + c0 * 64;
+                            (vrow % SK + r) * (kMlaDim * 2) + g * 16 + c0 * 64;
 #pragma unroll
         for (int i = 0; i < kMaxC; ++i)
           if (i < nc) qop[i] = *reinterpret_cast<const bf16x8*>(st + i * 64);
@@ -600,10 +646,14 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_dec
 #pragma unroll
     for (int k = 0; k < kTiles; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     float mrun = -INFINITY, lsum = 0.0f;
+    // keys the wave's token sees
+    const int nvis = cur.L - cur.Q + 1 + cur.i * G + tw;
     for (int ks = 0; ks < cnt; ++ks, ++it) {
       ring_step();
-      const int j = cur.j + ks;  // stage of the token
+      const int j = cur.j + ks;  // stage of the group
       const uint8_t* st = ring + (it % kRing) * kStageBytes;
+      __bf16 pw[4 * kSubs];
+      if (active) {
       // scores of the stage's 16-key sub-tiles
       f32x4 sc[kSubs];
 #pragma unroll
@@ -634,8 +684,9 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_dec
         }
       }
       // online softmax over the stage's keys (lane (r, g): keys 4g .. 4g+3
-      // of each sub-tile, head r); keys the token does not see get -inf
-      const int nvis = cur.L - cur.Q + 1 + cur.i;
+      // of each sub-tile, row r); keys the token does not see get -inf (in a
+      // group, an earlier token may see none of a stage: its weights are 0
+      // while its maximum is still -inf)
       const int key0 = SK * j + 4 * g;
       float y[4 * kSubs];
 #pragma unroll
@@ -655,21 +706,24 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_dec
         lsum *= alpha;
         mrun = mnew;
       }
-      __bf16 pw[4 * kSubs];
+      const float mref = mrun == -INFINITY ? 0.0f : mrun;
       float ps = 0.0f;
 #pragma unroll
       for (int e = 0; e < 4 * kSubs; ++e) {
-        pw[e] = (__bf16)__builtin_amdgcn_exp2f(y[e] - mrun);
+        pw[e] = (__bf16)__builtin_amdgcn_exp2f(y[e] - mref);
         ps += (float)pw[e];
       }
       lsum += ps;
+      }  // active
       // weighted sum; in a stage the token does not see to its end the V rows
       // of the unseen keys (possibly unwritten slots: a 0 weight must not meet
       // a NaN) are first zeroed in LDS.  Every wave writes the same zeros, and
       // its own reads follow its own writes (LDS operations of a wave complete
       // in order), so no barrier is needed.
-      if (SK * j + SK > nvis) {
-        const int kv = nvis - SK * j;  // keys of the stage it sees
+      // (the keys past what the group's last token sees: the other tokens'
+      // masked keys are written slots)
+      if (SK * j + SK > cur.nvis) {
+        const int kv = cur.nvis - SK * j;  // keys of the stage it sees
         uint8_t* sw = ring + (it % kRing) * kStageBytes;
         for (int q = lane; q < kSubs * (kMlaLatent / 32) * 64; q += 64) {
           const int u = q >> 10, c = (q >> 6) & 15, pos = q & 63;
@@ -682,6 +736,7 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_dec
       // (operands assembled by whole-vector casts and shuffles: assembled
       // element by element, the transpose reads' results were compiled to
       // copies of their first dwords)
+      if (!active) continue;
       if constexpr (SK == 32) {
         bf16x8 pp;
 #pragma unroll
@@ -708,16 +763,18 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_dec
       }
     }
 
-    // the token's piece is done: its output, or its partial
+    // the group's piece is done: the wave's rows of the output, or of its
+    // partial (a token that saw no key of the piece: weight 0, output 0)
     const bool whole = cur.j == 0 && cur.j + cnt == cur.nst;
     float l = lsum;
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
-    const int t = cur.q0 + cur.i;
-    const int h = hg * 16 + r;
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const int t = cur.q0 + cur.i * G + tw;
+    const int h = vrow - tw * P.Hq + r;
     const int dim0 = dq * kTiles * 16 + 4 * g;
-    if (whole) {
-      const float inv = 1.0f / l;
+    if (!active) {
+    } else if (whole) {
       uint16_t* op = P.out + ((int64_t)t * P.Hq + h) * kMlaLatent + dim0;
 #pragma unroll
       for (int k = 0; k < kTiles; ++k) {
@@ -727,12 +784,11 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_dec
         *reinterpret_cast<bf16x4*>(op + 16 * k) = o;
       }
     } else {
-      // slot 2 rg: the range's first token; 2 rg + 1: its last (only these two
-      // can be cut).  The piece's normalised output in bf16, its (max, sum)
-      // in fp32.
-      const int64_t row = (2 * (int64_t)rg + (first_tok ? 0 : 1)) * P.Hq + h;
+      // slot 2 rg: the range's first group; 2 rg + 1: its last (only these
+      // two can be cut), G Hq rows each.  The piece's normalised output in
+      // bf16, its (max, sum) in fp32.
+      const int64_t row = (2 * (int64_t)rg + (first_tok ? 0 : 1)) * (G * P.Hq) + vrow + r;
       uint16_t* ap = P.part_out + row * kMlaLatent + dim0;
-      const float inv = 1.0f / l;
 #pragma unroll
       for (int k = 0; k < kTiles; ++k) {
         bf16x4 o;
@@ -742,21 +798,24 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_dec
       }
       if (dq == 0 && g == 0) P.part_ml[row] = make_float2(mrun, l);
     }
-    // the workgroup holding the token's first key stage records which
-    // workgroups hold its pieces: this one, then whole ranges, the last one
-    // (R items each) holding the token's last key stage
-    if (cur.j == 0 && threadIdx.x == 0 && P.seg) {
+    // the workgroup holding the group's first key stage records, for each of
+    // its tokens, which workgroups hold its pieces (this one, then whole
+    // ranges, the last one (R items each) holding the group's last key
+    // stage) and the token's place in the group; the first wave of each
+    // token writes it
+    if (cur.j == 0 && active && vrow % P.Hq == 0 && dq == 0 && lane == 0 && P.seg) {
       const int64_t last = kpos + cur.nst - 1;
       const int pieces = (int)(last / R - rg + 1);
-      P.seg[t] = make_int2(rg, 2 * pieces + (first_tok ? 0 : 1));
+      P.seg[t] = make_int2(rg, ((2 * pieces + (first_tok ? 0 : 1)) << 3) | tw);
     }
-    stored = kRing - 1;
+    // (the ring waits allow for result stores only where there are some)
+    stored = active ? kRing - 1 : 0;
     first_tok = false;
     done += cnt;
     if (done < nreal) {
       kpos += cur.nst + qw;
       cur.j = cur.nst - 1;
-      cursor_next<SK>(cur, P, win);
+      cursor_next<SK>(cur, P, win, G);
     }
   }
 }
@@ -773,15 +832,16 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaParams P) {
   const int64_t row0 = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row0 >= (int64_t)P.num_q_tokens * P.Hq) return;
   const int t = (int)(row0 / P.Hq), h = (int)(row0 % P.Hq);
-  // pieces: the first in slot 2 w0 + flag (flag: the token was not the
-  // first of w0's range), the others in slots 2 (w0 + s) (their ranges
-  // begin inside the token)
+  // pieces of the token's group: the first in slot 2 w0 + flag (flag: the
+  // group was not the first of w0's range), the others in slots 2 (w0 + s)
+  // (their ranges begin inside the group); the token's rows are those of its
+  // place tw in the group
   const int2 sg = P.seg[t];
-  const int pieces = sg.y >> 1;
-  if (pieces < 2 || sg.x < 0 || sg.x > P.grid - pieces) return;
+  const int pieces = sg.y >> 4, flag = (sg.y >> 3) & 1, tw = sg.y & 7;
+  if (pieces < 2 || sg.x < 0 || sg.x > P.grid - pieces || tw >= P.G) return;
   auto row_of = [&](int s) -> int64_t {
-    const int64_t slot = s == 0 ? 2 * (int64_t)sg.x + (sg.y & 1) : 2 * ((int64_t)sg.x + s);
-    return slot * P.Hq + h;
+    const int64_t slot = s == 0 ? 2 * (int64_t)sg.x + flag : 2 * ((int64_t)sg.x + s);
+    return slot * (P.G * P.Hq) + tw * P.Hq + h;
   };
   // out = sum_i w_i o_i / sum_i w_i, w_i = l_i 2^(m_i - M): o_i a piece's
   // normalised output (bf16), (m_i, l_i) its running max and sum
@@ -805,7 +865,7 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaParams P) {
     float mx = ml.x;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
-    const float mn = fmaxf(M, mx);  // finite: every piece saw a key
+    const float mn = fmaxf(M, mx);  // finite: the group's first piece saw a key of every token
     const float c_old = __builtin_amdgcn_exp2f(M - mn);
     const float wgt = lane < cnt ? ml.y * __builtin_amdgcn_exp2f(ml.x - mn) : 0.0f;
     float dl = wgt;
@@ -859,12 +919,14 @@ hipError_t launch_mla_decode(const MlaParams& P, hipStream_t stream) {
   static_assert(mla_stage_keys(16) == 16 && mla_stage_keys(32) == 16 &&
                     mla_stage_keys(48) == 32,
                 "the instances below follow the stage size the layout assumes");
-  if (dq == 4)
-    hipLaunchKernelGGL((mla_decode_kernel<4, 16>), grid, block, 0, stream, P);
+  if (P.G > 1)  // groups of 128 / Hq tokens: 8 waves of 16 (token, head) rows
+    hipLaunchKernelGGL((mla_decode_kernel<1, 32, true>), grid, dim3(512), 0, stream, P);
+  else if (dq == 4)
+    hipLaunchKernelGGL((mla_decode_kernel<4, 16, false>), grid, block, 0, stream, P);
   else if (dq == 2)
-    hipLaunchKernelGGL((mla_decode_kernel<2, 16>), grid, block, 0, stream, P);
+    hipLaunchKernelGGL((mla_decode_kernel<2, 16, false>), grid, block, 0, stream, P);
   else
-    hipLaunchKernelGGL((mla_decode_kernel<1, 32>), grid, block, 0, stream, P);
+    hipLaunchKernelGGL((mla_decode_kernel<1, 32, false>), grid, block, 0, stream, P);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || P.grid < 2) return e;
   const int64_t rows = (int64_t)P.num_q_tokens * P.Hq;

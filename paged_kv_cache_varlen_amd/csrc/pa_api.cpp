@@ -851,9 +851,10 @@ static_assert(pa::kMlaDim == PA_MLA_DIM && pa::kMlaLatent == PA_MLA_LATENT &&
 
 size_t pa_mla_workspace_size(int64_t num_q_tokens, int32_t num_q_heads,
                              int32_t max_seq_len) {
-  if (num_q_tokens < 0 || num_q_heads <= 0 || num_q_heads % 16 != 0 || max_seq_len < 0)
+  if (num_q_tokens < 0 || num_q_tokens >= pa::kMlaMaxTokens || num_q_heads <= 0 ||
+      num_q_heads % 16 != 0 || max_seq_len < 0)
     return 0;
-  return pa::mla_layout(num_q_tokens, num_q_heads, max_seq_len).total;  // 0 past kMlaMaxGrid
+  return pa::mla_workspace_bytes(num_q_tokens, num_q_heads, max_seq_len);  // 0 past kMlaMaxGrid
 }
 
 pa_status pa_mla_write_kv(const void* kv, int64_t kv_token_stride,
@@ -893,7 +894,7 @@ pa_status pa_mla_decode(const void* q, const void* cache, int64_t num_blocks,
   if (num_seqs > pa::kMlaMaxSeqs)
     return fail(PA_ERR_UNSUPPORTED, "pa_mla_decode: num_seqs above 131072");
   if (num_q_tokens >= pa::kMlaMaxTokens)
-    return fail(PA_ERR_UNSUPPORTED, "pa_mla_decode: num_q_tokens of 2^27 or more");
+    return fail(PA_ERR_UNSUPPORTED, "pa_mla_decode: num_q_tokens of 2^25 or more");
   if (num_blocks > pa::kMlaMaxBlocks)
     return fail(PA_ERR_UNSUPPORTED, "pa_mla_decode: num_blocks above 2^29");
   if (num_q_tokens == 0 || num_seqs == 0) return ok();
@@ -905,7 +906,8 @@ pa_status pa_mla_decode(const void* q, const void* cache, int64_t num_blocks,
     return fail(PA_ERR_SHAPE, "pa_mla_decode: scale must be finite and > 0");
   if (((uintptr_t)q | (uintptr_t)cache | (uintptr_t)out) & 15)
     return fail(PA_ERR_SHAPE, "q, out and the cache must be 16-byte aligned");
-  const pa::MlaLayout m = pa::mla_layout(num_q_tokens, num_q_heads, max_seq_len);
+  const int group = pa::mla_group(num_q_heads, num_q_tokens, num_seqs);
+  const pa::MlaLayout m = pa::mla_layout(num_q_tokens, num_q_heads, max_seq_len, group);
   if (m.grid <= 0)
     return fail(PA_ERR_UNSUPPORTED, "pa_mla_decode: more work than one launch takes");
   if (((int64_t)num_q_tokens * num_q_heads + 3) / 4 > INT32_MAX)
@@ -931,6 +933,7 @@ pa_status pa_mla_decode(const void* q, const void* cache, int64_t num_blocks,
   P.Hq = num_q_heads;
   P.max_seq_len = max_seq_len;
   P.grid = m.grid;
+  P.G = group;
   P.scale_log2 = scale * 1.4426950408889634f;
   P.out = static_cast<uint16_t*>(out);
   char* ws = static_cast<char*>(workspace);

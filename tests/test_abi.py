@@ -408,12 +408,17 @@ def mla_args(**over):
 def test_mla_workspace_size(lib):
     small = lib.pa_mla_workspace_size(64, 16, 4096)
     assert small > 0 and small % 256 == 0
-    # more heads, more partial rows
-    assert lib.pa_mla_workspace_size(64, 128, 4096) > small
+    # more heads, more partial rows (16 heads: enough for the grouped form's
+    # 128 (token, head) rows per slot as well; 48 heads have no grouped form)
+    assert lib.pa_mla_workspace_size(64, 128, 4096) >= small
+    assert lib.pa_mla_workspace_size(64, 48, 4096) < lib.pa_mla_workspace_size(64, 128, 4096)
     assert lib.pa_mla_workspace_size(64, 24, 4096) == 0      # not a multiple of 16
     assert lib.pa_mla_workspace_size(-1, 16, 4096) == 0
-    # more work than one launch's grid: no size, and the decode refuses it
-    assert lib.pa_mla_workspace_size((1 << 27) - 1, 16, 1 << 18) == 0
+    # past the token limit: no size, and the decode refuses it
+    assert lib.pa_mla_workspace_size(1 << 25, 16, 4096) == 0
+    assert lib.pa_mla_workspace_size((1 << 25) - 1, 16, 4096) > 0
+    # enough for the grouped form too (128 (token, head) rows per slot)
+    assert small >= 2 * 256 * 128 * 512 * 2
 
 
 @pytest.mark.parametrize("over,status", [
@@ -422,7 +427,7 @@ def test_mla_workspace_size(lib):
     (dict(maxL=(1 << 18) + 1), _lib.PA_ERR_UNSUPPORTED),
     (dict(B=(1 << 17) + 1), _lib.PA_ERR_UNSUPPORTED),
     (dict(nb=(1 << 29) + 1), _lib.PA_ERR_UNSUPPORTED),
-    (dict(T=(1 << 27) - 1, maxL=1 << 18), _lib.PA_ERR_UNSUPPORTED),   # grid past one launch
+    (dict(T=1 << 25), _lib.PA_ERR_UNSUPPORTED),                        # token index bits
     (dict(q=None), _lib.PA_ERR_NULL),
     (dict(scale=0.0), _lib.PA_ERR_SHAPE),
     (dict(q=FAKE + 8), _lib.PA_ERR_SHAPE),                              # 16-byte alignment

@@ -55,6 +55,15 @@ CASES = {
     "decode-h80": ([500, 1], [1, 1], 80, None),
     "decode-h96": ([129, 4096], [1, 1], 96, None),
     "decode-h112": ([2000, 31, 32], [1, 1, 1], 112, None),
+    # grouped form (a batch averaging 4+ query tokens per request; 16, 32 and
+    # 64 heads): 128 / Hq consecutive tokens of a request per work item.  A
+    # fresh prompt (its first tokens see a handful of keys, so most pieces of
+    # their group hold none of them), short last groups, single-token groups,
+    # a 1-key request, a long context
+    "chunk-h16-fresh": ([200], [200], 16, None),
+    "chunk-h32-ragged": ([700, 300, 77], [37, 120, 5], 32, None),
+    "chunk-h64-mixed": ([2000, 50, 600, 1], [130, 1, 17, 1], 64, None),
+    "chunk-h16-long": ([5000, 64], [100, 64], 16, None),
 }
 
 
