@@ -34,7 +34,7 @@
 // of (token k, 8-dim group g) sits at granule g * 16 + (k ^ (12 * (g & 1)))
 // of its piece, which keeps both LDS read patterns free of bank conflicts.
 #include "mfma_util.h"
-#include "pa_device.h"
+#include "mla_device.h"
 
 namespace pa {
 namespace {

@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "pa_device.h"
+#include "mla_device.h"
 
 namespace {
 
