@@ -533,16 +533,73 @@ def mla_case(name, L, Hq, seed):
                 qsl=np.arange(len(L) + 1, dtype=np.int32))
 
 
+def _mla_time(pa, torch, c, L, qsl, Hq, ncopies, reps):
+    """Mean ms of one pa_mla_decode launch (decode + merge) for case c with
+    query_start_loc qsl, over back-to-back launches on ncopies cache copies;
+    the C-ABI call's arguments are prepared once (the binding's per-call
+    checks cost host time comparable to the kernels) and checked once against
+    the binding's path bit for bit."""
+    from tests.gpu_util import i32
+    from paged_kv_cache_varlen_amd import _lib
+    T = int(qsl[-1])
+    maxL = int(np.max(L))
+    caches = [pa.alloc_mla_cache(c["nb"], fill=0.0) for _ in range(ncopies)]
+    for cc in caches:
+        cc.normal_()
+    q = torch.randn((T, Hq, 576), device="cuda").to(torch.bfloat16)
+    o = torch.empty((T, Hq, 512), dtype=torch.bfloat16, device="cuda")
+    ws = pa.mla_workspace(T, Hq, maxL)
+    bt, sl, qs = i32(c["tables"]), i32(np.asarray(L, np.int32)), i32(np.asarray(qsl, np.int32))
+    scale = float(1 / np.sqrt(192.0))
+    fn = _lib.load().pa_mla_decode
+    stream = torch.cuda.current_stream().cuda_stream
+    prepared = [(q.data_ptr(), cc.data_ptr(), c["nb"], bt.data_ptr(), int(bt.shape[1]),
+                 sl.data_ptr(), qs.data_ptr(), len(L), T, Hq, maxL, scale,
+                 o.data_ptr(), ws.data_ptr(), ws.numel(), stream) for cc in caches]
+
+    def run(i):
+        if fn(*prepared[i % ncopies]) != 0:
+            raise RuntimeError(_lib.load().pa_last_error())
+    pa.mla_decode(q, caches[0], bt, sl, qs, scale, maxL, out=o, workspace=ws)
+    ref = o.clone()
+    o.fill_(float("nan"))
+    run(0)
+    torch.cuda.synchronize()
+    assert torch.equal(ref.view(torch.int16), o.view(torch.int16)), \
+        "prepared MLA call differs from the binding's"
+    for i in range(3 * ncopies):
+        run(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        for i in range(ncopies):
+            run(i)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / (reps * ncopies)
+    del caches
+    torch.cuda.empty_cache()
+    return ms
+
+
+# chunked prefill through the latent path: (name, cached + new tokens per
+# request, new tokens per request, query heads)
+MLA_CHUNKS = (("mla-prefill-chunk-1024-on-1024-h16", [2048], [1024], 16),
+              ("mla-prefill-chunk-1024-on-1024-h128", [2048], [1024], 128),
+              ("mla-prefill-8x512-on-3584-h16", [4096] * 8, [512] * 8, 16))
+
+
 def mla_runs(args):
     """MLA latent decode (DeepSeek-V3-shaped: 576 cached values per token,
     512 latent dims out) on 64 requests of U[128, 4096] tokens: 16 query
     heads (one tensor-parallel share of 128) and all 128 heads.  Attention
     kernels (decode + merge) timed with HIP events over back-to-back
     launches on cycled cache copies; GB/s of the latent bytes the step must
-    read and TFLOP/s of the scores and weighted sums."""
+    read and TFLOP/s of the scores and weighted sums.  Then chunked-prefill
+    batches through the same call (TFLOP/s)."""
     import torch
     import paged_kv_cache_varlen_amd as pa
-    from tests.gpu_util import bf16_tensor, i32
     rng = np.random.default_rng(2024)
     L = rng.integers(128, 4096, size=64, endpoint=True).astype(np.int32)
     out = {"latent_dims": 576, "out_dims": 512, "block_size": 64}
@@ -551,46 +608,8 @@ def mla_runs(args):
         T = len(L)
         cache_bytes = c["nb"] * 64 * 576 * 2
         ncopies = max(1, min(8, int(np.ceil(args.min_working_set_gib * 2**30 / cache_bytes))))
-        caches = [pa.alloc_mla_cache(c["nb"], fill=0.0) for _ in range(ncopies)]
-        for cc in caches:
-            cc.normal_()
-        q = torch.randn((T, Hq, 576), device="cuda").to(torch.bfloat16)
-        o = torch.empty((T, Hq, 512), dtype=torch.bfloat16, device="cuda")
-        ws = pa.mla_workspace(T, Hq, int(L.max()))
-        bt, sl, qsl = i32(c["tables"]), i32(L), i32(c["qsl"])
-        scale = float(1 / np.sqrt(192.0))
-        # the C-ABI call with its arguments prepared once (the binding's
-        # per-call checks cost host time comparable to the kernels), checked
-        # once against the binding's path bit for bit
-        from paged_kv_cache_varlen_amd import _lib
-        fn = _lib.load().pa_mla_decode
-        stream = torch.cuda.current_stream().cuda_stream
-        prepared = [(q.data_ptr(), cc.data_ptr(), c["nb"], bt.data_ptr(), int(bt.shape[1]),
-                     sl.data_ptr(), qsl.data_ptr(), T, T, Hq, int(L.max()), scale,
-                     o.data_ptr(), ws.data_ptr(), ws.numel(), stream) for cc in caches]
-
-        def run(i):
-            if fn(*prepared[i % ncopies]) != 0:
-                raise RuntimeError(_lib.load().pa_last_error())
-        pa.mla_decode(q, caches[0], bt, sl, qsl, scale, int(L.max()), out=o, workspace=ws)
-        ref = o.clone()
-        o.fill_(float("nan"))
-        run(0)
-        torch.cuda.synchronize()
-        assert torch.equal(ref.view(torch.int16), o.view(torch.int16)), \
-            "prepared MLA call differs from the binding's"
-        for i in range(10):
-            run(i)
-        torch.cuda.synchronize()
         reps = max(4, args.steps // (4 * ncopies))
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(reps):
-            for i in range(ncopies):
-                run(i)
-        b.record()
-        torch.cuda.synchronize()
-        ms = a.elapsed_time(b) / (reps * ncopies)
+        ms = _mla_time(pa, torch, c, L, c["qsl"], Hq, ncopies, reps)
         lat = int(L.sum()) * 576 * 2
         byts = lat + T * Hq * (576 + 512) * 2 + int(((L + 63) // 64).sum()) * 4
         flops = int(L.sum()) * Hq * (576 + 512) * 2
@@ -601,8 +620,17 @@ def mla_runs(args):
                     "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
                     "mfma_peak_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                     "decode_tokens_per_s": round(T / (ms * 1e-3), 1)}
-        del caches
-        torch.cuda.empty_cache()
+    chunks = {}
+    for name, Lc, Qc, Hq in MLA_CHUNKS:
+        c = mla_case(name, Lc, Hq, seed=3)
+        qsl = np.concatenate([[0], np.cumsum(Qc)]).astype(np.int32)
+        ms = _mla_time(pa, torch, c, Lc, qsl, Hq, 1, 10)
+        keys = sum(l - qq + 1 + i for l, qq in zip(Lc, Qc) for i in range(qq))
+        flops = keys * Hq * (576 + 512) * 2
+        chunks[name] = {"num_q_heads": Hq, "query_tokens": int(qsl[-1]), "ms": round(ms, 5),
+                        "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                        "mfma_peak_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    out["prefill_chunks"] = chunks
     return out
 
 

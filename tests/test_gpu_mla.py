@@ -131,6 +131,26 @@ def test_mla_many_requests():
     check_close(tensor_bits(out), ref, "mla 300 requests")
 
 
+@pytest.mark.parametrize("Hq", [16, 32, 64])
+def test_mla_grouped_many_requests(Hq):
+    """The grouped form (the batch averages 4+ query tokens per request) over
+    150 requests (several per lane in the range search): 1 .. 13 query
+    tokens each, so full, short and single-token groups, on 1 .. 600 keys."""
+    rng = np.random.default_rng(13 + Hq)
+    Q = rng.integers(1, 14, size=150)
+    Q[:10] = 1
+    L = Q + rng.integers(0, 600, size=150)
+    assert Q.sum() >= 4 * len(Q)
+    m = mla_batch(L, Q, Hq, seed=14)
+    scale = float(np.float32(1 / np.sqrt(DL)))
+    cache = gpu_cache(m)
+    out = pa.mla_decode(bf16_tensor(m["q"]), cache, i32(m["tables"]), i32(m["L"]),
+                        i32(m["qsl"]), scale, int(L.max()))
+    torch.cuda.synchronize()
+    ref = oracle.mla_decode(m["q"], oracle_cache(m), m["tables"], m["L"], m["qsl"], scale)
+    check_close(tensor_bits(out), ref, "mla grouped 150 requests")
+
+
 def test_mla_out_of_bounds_requests_skipped_and_stale_records_ignored():
     """Requests whose metadata is out of bounds (Q > L: request 1 with L = 0;
     L above max_seq_len: request 4) are skipped: their rows keep what was
@@ -157,6 +177,36 @@ def test_mla_out_of_bounds_requests_skipped_and_stale_records_ignored():
         check_close(got[t], ref[t], "mla in-bounds token %d" % t)
     for t in (1, 5):
         assert (got[t] == sentinel).all(), "row of skipped token %d written" % t
+
+
+def test_mla_grouped_out_of_bounds_requests_and_stale_records():
+    """The same in the grouped form (16 heads, groups of 8 tokens): requests
+    1 (L = 0 < Q) and 4 (L above max_seq_len) skipped inside a grouped batch,
+    run after a grouped batch on the same workspace whose records (with the
+    tokens' places in their groups) are stale."""
+    scale = float(np.float32(1 / np.sqrt(DL)))
+    m = mla_batch([900, 2, 1000, 40, 3000], [8, 1, 12, 6, 5], 16, seed=23)
+    T = int(m["qsl"][-1])  # 32 tokens over 5 requests: grouped
+    L_gpu = m["L"].copy()
+    L_gpu[1] = 0
+    ws = pa.mla_workspace(T, 16, 3000)
+    big = mla_batch([3000, 2500], [16, 16], 16, seed=24)
+    pa.mla_decode(bf16_tensor(big["q"]), gpu_cache(big), i32(big["tables"]), i32(big["L"]),
+                  i32(big["qsl"]), scale, 3000, workspace=ws)
+    sentinel = 0x7FA1
+    raw = torch.full((T, 16, 512), sentinel, dtype=torch.int16, device="cuda")
+    pa.mla_decode(bf16_tensor(m["q"]), gpu_cache(m), i32(m["tables"]), i32(L_gpu),
+                  i32(m["qsl"]), scale, 1000, out=raw.view(torch.bfloat16), workspace=ws)
+    torch.cuda.synchronize()
+    got = tensor_bits(raw.view(torch.bfloat16))
+    ref = per_request_oracle(m, scale, [0, 2, 3])
+    q = m["qsl"]
+    for b in (0, 2, 3):
+        for t in range(q[b], q[b + 1]):
+            check_close(got[t], ref[t], "mla grouped in-bounds token %d" % t)
+    for b in (1, 4):
+        for t in range(q[b], q[b + 1]):
+            assert (got[t] == sentinel).all(), "row of skipped token %d written" % t
 
 
 @pytest.mark.parametrize("Hq", [16, 128])
