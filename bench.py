@@ -74,6 +74,9 @@ def parse():
                     help="skip the streaming-read ceiling probe")
     ap.add_argument("--mla", action="store_true",
                     help="only the MLA latent decode sub-run (one JSON line)")
+    ap.add_argument("--no-mla-chunks", action="store_true",
+                    help="leave the MLA chunked-prefill batches out (profiles of "
+                         "the decode workloads alone)")
     ap.add_argument("--fp8", action="store_true",
                     help="time the workload over 8-bit (E4M3) pools")
     ap.add_argument("--cascade", action="store_true",
@@ -620,6 +623,8 @@ def mla_runs(args):
                     "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
                     "mfma_peak_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                     "decode_tokens_per_s": round(T / (ms * 1e-3), 1)}
+    if getattr(args, "no_mla_chunks", False):
+        return out
     chunks = {}
     for name, Lc, Qc, Hq in MLA_CHUNKS:
         c = mla_case(name, Lc, Hq, seed=3)
