@@ -7,17 +7,20 @@
 // sub-tile is 18 KiB of [32-dim chunk][16 tokens][32 dims] (one KiB piece per
 // chunk), so tokens 32s .. 32s+31 of a block (s = 0, 1) are 36 KiB contiguous.
 //
-// Decode (mla_decode_kernel).  The work is a stream of SK-key stages (SK =
-// 16 for up to 32 heads, 32 for more): the requests in order, each query
-// token of a request in order, then its query stages and the keys that token
-// sees in stages of SK.  The stream is cut into contiguous ranges of
-// R = ceil(stages / gridDim.x) stages, one per workgroup, so every workgroup
-// reads the same latent bytes whatever the mix of lengths; a token whose
-// keys are cut between workgroups leaves one partial result per workgroup,
-// folded by mla_merge_kernel.
+// Decode (mla_decode_kernel).  The work is a stream of items: the requests
+// in order, each group of G consecutive query tokens of a request in order
+// (G = 1, or 128 / Hq for batches of multi-token requests with 16, 32 or 64
+// heads), a few head items for the group's query stages, then the keys its
+// last token sees in stages of SK (16 for up to 32 heads with G = 1, else
+// 32).  The stream is cut into contiguous ranges of R = ceil(items /
+// gridDim.x) items, one per workgroup, so every workgroup reads about the
+// same latent bytes whatever the mix of lengths; a group whose keys are cut
+// between workgroups leaves one partial result per workgroup, folded by
+// mla_merge_kernel.
 //
-// A workgroup has one wave per 16 query heads (for 16 and 32 heads, one wave
-// per (16 heads, quarter / half of the 512 output dims)).  Its stages pass
+// A workgroup has one wave per 16 (token, head) rows of a group (for 16 and
+// 32 heads with G = 1, one wave per (16 heads, quarter / half of the 512
+// output dims)).  Its stages pass
 // through a ring of four LDS buffers (18 KiB for SK = 16, two workgroups per
 // CU; 36 KiB for SK = 32), filled three stages ahead by global-to-LDS loads
 // that the waves share; each wave then reads the stage from LDS for
@@ -68,14 +71,6 @@ constexpr int kWaitLgkm0 = 0xC07F;
 template <class T>
 __device__ __forceinline__ T sload(const T* p) {
   return *(const __attribute__((address_space(4))) T*)p;
-}
-
-// Stages of tokens that see 1, 2, .., n keys: the sum of ceil(x / SK).
-template <int SK>
-__device__ __forceinline__ int64_t stage_prefix(int64_t n) {
-  if (n <= 0) return 0;
-  const int64_t m = n / SK, r = n % SK;
-  return (m + 1) * (SK / 2 * m + r);
 }
 
 // A request's metadata is in bounds: its tokens inside [0, T), Q <= L,
@@ -275,10 +270,13 @@ __device__ __forceinline__ void dma_stage(const MlaParams& P, uint32_t e, uint32
 
 // Wait until this wave has at most 2 nl (+ extra) ring loads in flight -- the
 // two stages issued after the one about to be read, plus the result stores
-// of a token finished in the last three stages, which count too -- then meet
+// of a piece finished in the last three stages, which count too -- then meet
 // the other waves: after the barrier every wave's share of the stage is in
 // LDS, and every wave has finished reading the buffer that is refilled next.
-// (No LDS read is outstanding here: each was consumed before.)
+// (The counter retires in order, so the wait covers the stage as long as
+// the allowance is no more than the operations issued after it: `extra` is
+// at most the stores a piece issues, and none where the wave stored none.
+// No LDS read is outstanding here: each was consumed before.)
 #define MLA_WAIT(N) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory")
 template <int EXTRA>
 __device__ __forceinline__ void ring_wait(int nl, bool tail, bool stores) {
@@ -426,7 +424,7 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_dec
   const int64_t M = readlane64(incl, 63);
   const int64_t R = (M + gridDim.x - 1) / gridDim.x;
   // range rg of workgroup blockIdx.x: workgroups go to the 8 XCDs in turn,
-  // and consecutive ranges (the pieces of one token, which read the same
+  // and consecutive ranges (the pieces of one group, which read the same
   // query) are given to workgroups of one XCD, so that they share its L2
   const int rg = xcd_range(blockIdx.x, gridDim.x);
   const int64_t I0 = min((int64_t)rg * R, M);
@@ -602,7 +600,7 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_dec
 
   int stored = 0;         // ring waits left that allow for result stores
   int done = 0;           // key stages computed
-  bool first_tok = true;  // the piece is of the range's first token
+  bool first_tok = true;  // the piece is of the range's first group
   const float c2 = P.scale_log2;
   int it = 0;             // table entry
   // Before entry `it` is read: wait for it (and meet the other waves), then
@@ -654,74 +652,73 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_dec
       const uint8_t* st = ring + (it % kRing) * kStageBytes;
       __bf16 pw[4 * kSubs];
       if (active) {
-      // scores of the stage's 16-key sub-tiles
-      f32x4 sc[kSubs];
+        // scores of the stage's 16-key sub-tiles
+        f32x4 sc[kSubs];
 #pragma unroll
-      for (int u = 0; u < kSubs; ++u) sc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < kSubs; ++u) sc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < kMaxC; ++i) {
-        if (i < nc) {
-          const uint8_t* kp = st + (c0 + i) * 1024 + offK;
+        for (int i = 0; i < kMaxC; ++i) {
+          if (i < nc) {
+            const uint8_t* kp = st + (c0 + i) * 1024 + offK;
 #pragma unroll
-          for (int u = 0; u < kSubs; ++u)
-            sc[u] = mfma32(*reinterpret_cast<const bf16x8*>(kp + u * kSubBytes), qop[i], sc[u]);
+            for (int u = 0; u < kSubs; ++u)
+              sc[u] = mfma32(*reinterpret_cast<const bf16x8*>(kp + u * kSubBytes), qop[i], sc[u]);
+          }
+          if (i % kScoreGroup == kScoreGroup - 1) __builtin_amdgcn_sched_barrier(0);
         }
-        if (i % kScoreGroup == kScoreGroup - 1) __builtin_amdgcn_sched_barrier(0);
-      }
-      if constexpr (DQ > 1) {
-        // add the head group's partial sums in wave order (the same sums in
-        // every wave); the writes land before the barrier, and every wave
-        // has read them before the next stage's barrier
+        if constexpr (DQ > 1) {
+          // add the head group's partial sums in wave order (the same sums in
+          // every wave); the writes land before the barrier, and every wave
+          // has read them before the next stage's barrier
 #pragma unroll
-        for (int u = 0; u < kSubs; ++u) xsc[w][u][lane] = sc[u];
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        const int w0 = hg * DQ;  // the head group's first wave
+          for (int u = 0; u < kSubs; ++u) xsc[w][u][lane] = sc[u];
+          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+          const int w0 = hg * DQ;  // the head group's first wave
 #pragma unroll
-        for (int u = 0; u < kSubs; ++u) {
-          sc[u] = xsc[w0][u][lane];
+          for (int u = 0; u < kSubs; ++u) {
+            sc[u] = xsc[w0][u][lane];
 #pragma unroll
-          for (int v = 1; v < DQ; ++v) sc[u] += xsc[w0 + v][u][lane];
+            for (int v = 1; v < DQ; ++v) sc[u] += xsc[w0 + v][u][lane];
+          }
         }
+        // online softmax over the stage's keys (lane (r, g): keys 4g .. 4g+3
+        // of each sub-tile, row r); keys the token does not see get -inf (in a
+        // group, an earlier token may see none of a stage: its weights are 0
+        // while its maximum is still -inf)
+        const int key0 = SK * j + 4 * g;
+        float y[4 * kSubs];
+#pragma unroll
+        for (int u = 0; u < kSubs; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            y[4 * u + e] = key0 + 16 * u + e < nvis ? sc[u][e] * c2 : -INFINITY;
+        float mx = y[0];
+#pragma unroll
+        for (int e = 1; e < 4 * kSubs; ++e) mx = fmaxf(mx, y[e]);
+        mx = column_max(mx);
+        if (__builtin_amdgcn_ballot_w64(mx > mrun + kSlack) != 0) {
+          const float mnew = fmaxf(mrun, mx);
+          const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);  // 0 on the first stage
+#pragma unroll
+          for (int k = 0; k < kTiles; ++k) acc[k] *= alpha;
+          lsum *= alpha;
+          mrun = mnew;
+        }
+        const float mref = mrun == -INFINITY ? 0.0f : mrun;
+        float ps = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4 * kSubs; ++e) {
+          pw[e] = (__bf16)__builtin_amdgcn_exp2f(y[e] - mref);
+          ps += (float)pw[e];
+        }
+        lsum += ps;
       }
-      // online softmax over the stage's keys (lane (r, g): keys 4g .. 4g+3
-      // of each sub-tile, row r); keys the token does not see get -inf (in a
-      // group, an earlier token may see none of a stage: its weights are 0
-      // while its maximum is still -inf)
-      const int key0 = SK * j + 4 * g;
-      float y[4 * kSubs];
-#pragma unroll
-      for (int u = 0; u < kSubs; ++u)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          y[4 * u + e] = key0 + 16 * u + e < nvis ? sc[u][e] * c2 : -INFINITY;
-      float mx = y[0];
-#pragma unroll
-      for (int e = 1; e < 4 * kSubs; ++e) mx = fmaxf(mx, y[e]);
-      mx = column_max(mx);
-      if (__builtin_amdgcn_ballot_w64(mx > mrun + kSlack) != 0) {
-        const float mnew = fmaxf(mrun, mx);
-        const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);  // 0 on the first stage
-#pragma unroll
-        for (int k = 0; k < kTiles; ++k) acc[k] *= alpha;
-        lsum *= alpha;
-        mrun = mnew;
-      }
-      const float mref = mrun == -INFINITY ? 0.0f : mrun;
-      float ps = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 4 * kSubs; ++e) {
-        pw[e] = (__bf16)__builtin_amdgcn_exp2f(y[e] - mref);
-        ps += (float)pw[e];
-      }
-      lsum += ps;
-      }  // active
-      // weighted sum; in a stage the token does not see to its end the V rows
-      // of the unseen keys (possibly unwritten slots: a 0 weight must not meet
-      // a NaN) are first zeroed in LDS.  Every wave writes the same zeros, and
-      // its own reads follow its own writes (LDS operations of a wave complete
-      // in order), so no barrier is needed.
-      // (the keys past what the group's last token sees: the other tokens'
-      // masked keys are written slots)
+      // weighted sum; in a stage the group's last token does not see to its
+      // end, the V rows of the keys past what it sees (possibly unwritten
+      // slots: a 0 weight must not meet a NaN) are first zeroed in LDS (the
+      // other tokens' masked keys are written slots).  Every wave writes the
+      // same zeros, and its own reads follow its own writes (LDS operations of
+      // a wave complete in order), so no barrier is needed.
       if (SK * j + SK > cur.nvis) {
         const int kv = cur.nvis - SK * j;  // keys of the stage it sees
         uint8_t* sw = ring + (it % kRing) * kStageBytes;
@@ -882,7 +879,6 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaParams P) {
         for (int e = 0; e < 8; ++e) n[e] += wk * (float)oa[k][e];
       }
     }
-#pragma unroll 4
     for (int k = kAhead; k < cnt; ++k) {
       const float wk = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wgt), k));
       const bf16x8 ok = *reinterpret_cast<const bf16x8*>(P.part_out + row_of(s0 + k) * kMlaLatent +
