@@ -81,8 +81,10 @@ def test_mla_decode_parity(name):
     check_close(tensor_bits(out), ref, "mla " + name)
 
 
-def test_mla_decode_repeat_bit_identical_and_table_permutation():
-    m = mla_batch([300, 77, 1000], [1, 2, 1], 16, seed=9)
+@pytest.mark.parametrize("Q", [[1, 2, 1], [40, 77, 9]])
+def test_mla_decode_repeat_bit_identical_and_table_permutation(Q):
+    # [1, 2, 1]: one token per work item; [40, 77, 9]: the grouped form
+    m = mla_batch([300, 77, 1000], Q, 16, seed=9)
     cache = gpu_cache(m)
     args = (bf16_tensor(m["q"]), cache, i32(m["tables"]), i32(m["L"]), i32(m["qsl"]),
             0.05, 1000)
