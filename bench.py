@@ -27,7 +27,8 @@ Prints one JSON line:
            the HBM peak;
   decode_8b  the Llama-3-8B decode layer (64 requests, U[128, 4096]) step
            and attention kernel;
-  tiny_decode  the 4-request latency case (microseconds per step);
+  tiny_decode  the 4-request latency case (microseconds per step, also with
+               the step replayed as a captured HIP graph);
   fp8_kv   the 8-bit (E4M3) KV cache beside bf16 on the 8B decode layer and
            the 70B-class long-context layer: step time, decode tokens/s,
            attention GB/s of code bytes;
@@ -265,6 +266,35 @@ class Runner:
             st = fn(*args)
             if st != 0:
                 raise RuntimeError("%s: %s" % (fn.__name__, self.pa._lib.load().pa_last_error()))
+
+    def graph_run(self, steps):
+        """Layer 0's step (scatter + plan, attention, merge) captured once as a
+        HIP graph (through the binding, on a capture stream) and replayed
+        `steps` times back to back: mean ms per replay.  A replay's output is
+        checked once against the eager step, bit for bit."""
+        torch = self.torch
+        self.step_checked(0)
+        torch.cuda.synchronize()
+        ref = self.u.out.clone()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            self.step_checked(0)
+        torch.cuda.synchronize()
+        self.u.out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ref.view(torch.int16), self.u.out.view(torch.int16)), \
+            "graph replay differs from the eager step"
+        for _ in range(10):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
 
     def run(self, steps, warmup):
         """Time `steps` whole steps (nothing but the step's own launches
@@ -683,13 +713,16 @@ def decode_kernel_name(w, fp8, cascade):
         w.head_dim, "true" if fp8 else "false")
 
 
-def sub_run(args, w, **kw):
+def sub_run(args, w, graph=False, **kw):
     """A workload's step and attention kernel, with the kernel's GB/s and
-    TFLOP/s of algorithmic bytes and flops."""
+    TFLOP/s of algorithmic bytes and flops; graph: also the step replayed as
+    a captured HIP graph (t["graph_ms_per_step"])."""
     import torch
     alg = algorithmic(w)
     r = Runner(w, args.min_working_set_gib, **kw)
     t = r.run(max(20, args.steps // 4), max(5, args.warmup // 2))
+    if graph:
+        t["graph_ms_per_step"] = r.graph_run(max(50, args.steps))
     del r
     torch.cuda.empty_cache()
     att = t["attend_ms"] * 1e-3
@@ -809,9 +842,10 @@ def main():
             res["traffic"] = measured_traffic(decode_kernel_name(w2, False, None), w2.name)
             line["decode_8b"] = res
         if args.config != "1":
-            _, t1, res = sub_run(args, config(W, 1))
+            _, t1, res = sub_run(args, config(W, 1), graph=True)
             line["tiny_decode"] = {"workload": res["workload"],
                                    "us_per_step": round(t1["ms_per_step"] * 1e3, 2),
+                                   "graph_us_per_step": round(t1["graph_ms_per_step"] * 1e3, 2),
                                    "step_us": {k: (round(v * 1e3, 2) if k != "n" else v)
                                                for k, v in t1["step_ms"].items()},
                                    "attend_us": round(t1["attend_ms"] * 1e3, 2)}
