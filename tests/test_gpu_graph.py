@@ -55,3 +55,37 @@ def test_step_graph_replays_match_eager(k):
     step()
     torch.cuda.synchronize()
     assert np.array_equal(tensor_bits(u.out), ref), "eager step after the replays differs"
+
+
+@pytest.mark.parametrize("Q", [[1, 1, 1, 1], [40, 3, 77, 9]])
+def test_mla_graph_replays_match_eager(Q):
+    # the MLA call (decode, then the split merge) in both forms: one token
+    # per work item, and groups of tokens
+    from tests.gpu_util import bf16_tensor, i32
+    from tests.test_gpu_mla import gpu_cache
+    from tests.test_oracle_mla import mla_batch
+    m = mla_batch([900, 77, 2500, 300], Q, 16, seed=31)
+    cache = gpu_cache(m)
+    T, L = int(m["qsl"][-1]), m["L"]
+    q = bf16_tensor(m["q"])
+    out = torch.empty((T, 16, 512), dtype=torch.bfloat16, device="cuda")
+    ws = pa.mla_workspace(T, 16, int(L.max()))
+    args = (q, cache, i32(m["tables"]), i32(L), i32(m["qsl"]), 0.05, int(L.max()))
+
+    def step():
+        pa.mla_decode(*args, out=out, workspace=ws)
+    step()
+    torch.cuda.synchronize()
+    ref = tensor_bits(out).copy()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    torch.cuda.synchronize()
+    for r in range(4):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(tensor_bits(out), ref), "replay %d differs" % r
