@@ -10,7 +10,7 @@
  * them, floating point in fp64.  bf16 inputs are widened exactly (the 16 bits
  * become the top half of an IEEE binary32, which converts exactly to binary64).
  *
- * Sources (the pages this build follows):
+ * Sources (the pages whose definitions these functions write out):
  *  - "vLLM v1 Deep Dive", Part 3 Runtime, Aside "KV cache and prefix caching"
  *    (supercharleszhu.github.io): a forward writes each new token's K/V into
  *    the physical slot block_id*block_size + offset given by slot_mapping, and
