@@ -511,9 +511,11 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_dec
 
   // ---- the first group's query stages: issued before the table is built -
   // and its first key stage (block id read directly; the table's entry is
-  // the same).  Wave 0, which builds the table, issues its share after it:
-  // its block-id loads would otherwise wait for these loads (the vector
-  // memory counter retires in order).
+  // the same), by waves 1 .. nw - 1 only, nle pieces each: wave 0 builds the
+  // table, and its block-id loads would otherwise wait for these loads (the
+  // vector memory counter retires in order).  The ring waits still hold: a
+  // wave that loads nle >= nl pieces of these stages waits for no fewer
+  // loads than it needs, and wave 0 has none of them in flight.
   // (query stages of a group, and the table entry of its k-th)
   auto group_qs = [&](const Cursor& c) { return (c.ntok * P.Hq + SK - 1) / SK; };
   auto qentry = [&](const Cursor& c, int k) {
@@ -523,17 +525,19 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_dec
   const int qs0 = group_qs(cur);
   const int pre = min(qs0, kRing - 1);
   const int pre2 = qs0 < kRing - 1 ? qs0 + 1 : pre;
+  const int nle = nw > 1 ? (kPieces + nw - 2) / (nw - 1) : nl;
+  const int p0e = nw > 1 ? (w - 1) * nle : 0;
   auto issue_first = [&]() {
     for (int k = 0; k < pre; ++k)
-      dma_stage<SK>(P, qentry(cur, k), lring + k * kStageBytes, voff, p0, nl);
+      dma_stage<SK>(P, qentry(cur, k), lring + k * kStageBytes, voff, p0e, nle);
     if (pre2 > pre) {
       int id = sload(P.bt + (int64_t)cur.b * P.bt_stride + cur.j / kPerBlock);
       id = id < 0 ? 0 : (id >= P.num_blocks ? (int)(P.num_blocks - 1) : id);
       dma_stage<SK>(P, ((uint32_t)id << 2) | (uint32_t)(cur.j % kPerBlock),
-                    lring + qs0 * kStageBytes, voff, p0, nl);
+                    lring + qs0 * kStageBytes, voff, p0e, nle);
     }
   };
-  if (w != 0) issue_first();
+  if (w != 0 || nw == 1) issue_first();
 
   // ---- the range's stage table (wave 0; one gather) -----------------------
   // Group by group, for each group with key stages in the range: its query
@@ -581,7 +585,6 @@ __global__ __launch_bounds__(DQ == 1 ? 512 : 256, SK == 16 ? 2 : 1) void mla_dec
       stab[kCap] = (uint32_t)x;
       stab[kCap + 1] = (uint32_t)nk;
     }
-    issue_first();
   }
   // (an LDS-only barrier: __syncthreads() would also wait for the ring
   // loads just issued)
