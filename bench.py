@@ -27,8 +27,7 @@ Prints one JSON line:
            the HBM peak;
   decode_8b  the Llama-3-8B decode layer (64 requests, U[128, 4096]) step
            and attention kernel;
-  tiny_decode  the 4-request latency case (microseconds per step, also with
-               the step replayed as a captured HIP graph);
+  tiny_decode  the 4-request latency case (microseconds per step);
   fp8_kv   the 8-bit (E4M3) KV cache beside bf16 on the 8B decode layer and
            the 70B-class long-context layer: step time, decode tokens/s,
            attention GB/s of code bytes;
@@ -842,10 +841,9 @@ def main():
             res["traffic"] = measured_traffic(decode_kernel_name(w2, False, None), w2.name)
             line["decode_8b"] = res
         if args.config != "1":
-            _, t1, res = sub_run(args, config(W, 1), graph=True)
+            _, t1, res = sub_run(args, config(W, 1))
             line["tiny_decode"] = {"workload": res["workload"],
                                    "us_per_step": round(t1["ms_per_step"] * 1e3, 2),
-                                   "graph_us_per_step": round(t1["graph_ms_per_step"] * 1e3, 2),
                                    "step_us": {k: (round(v * 1e3, 2) if k != "n" else v)
                                                for k, v in t1["step_ms"].items()},
                                    "attend_us": round(t1["attend_ms"] * 1e3, 2)}
