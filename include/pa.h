@@ -277,6 +277,9 @@ pa_status pa_attend_noalloc(const void *q, const void *k_cache, const void *v_ca
  * the workspace for the others.  pa_attend_merge enqueues the merge kernel
  * that combines those partials into `out`; it must follow every
  * pa_attend_planned on the same stream, before the workspace is reused.
+ * When max_seq_len is at most 384 (no request's keys are split at any
+ * length the batch allows) there are no partials and pa_attend_merge
+ * launches nothing.
  * Arguments mean the same as for pa_attend.  Between the calls the workspace
  * and the metadata arrays must not change, and every size argument must be
  * passed with the same value to all three; a plan made for other sizes is

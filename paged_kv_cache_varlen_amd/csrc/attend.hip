@@ -201,10 +201,9 @@ __device__ __forceinline__ int last_bucket(const AttendParams& P, int b, const S
   return min(kLastBuckets - 1, max(0, (kLastBucketKeys * kLastBuckets - rem) / kLastBucketKeys));
 }
 
-// Four exclusive scans at once (one set of barriers); tot receives the sums.
-__device__ int4 block_scan4(int4 x, int4* lds, int4* tot) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  constexpr int kWaves = kPlanThreads / 64;
+// Four inclusive scans at once over the lanes of a wave.
+__device__ __forceinline__ int4 wave_incl_scan4(int4 x) {
+  const int lane = threadIdx.x & 63;
   int4 incl = x;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -217,6 +216,14 @@ __device__ int4 block_scan4(int4 x, int4* lds, int4* tot) {
       incl.w += y3;
     }
   }
+  return incl;
+}
+
+// Four exclusive scans at once (one set of barriers); tot receives the sums.
+__device__ int4 block_scan4(int4 x, int4* lds, int4* tot) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  constexpr int kWaves = kPlanThreads / 64;
+  const int4 incl = wave_incl_scan4(x);
   if (lane == 63) lds[wid] = incl;
   __syncthreads();
   if (wid == 0) {
@@ -325,14 +332,66 @@ __device__ __forceinline__ void place_seq(const AttendParams& P, int b,
   emit_seq(P, b, c, ibase, ilast, pbase, cbase);
 }
 
-// The work plan, run by one workgroup of kPlanThreads threads.
-__device__ void plan_body(const AttendParams& P) {
-  __shared__ int4 lds[kPlanThreads / 64 + 1];
-  __shared__ int coop_n;
-  __shared__ int coop_b[kMaxCoop];
-  __shared__ int coop_base[kMaxCoop];
-  __shared__ int last_cnt[kLastBuckets];
-  const int tid = threadIdx.x;
+// The tiles of an unsplit prefill request b (its first item slot ibase,
+// latest tokens first), thread `first` of `step` threads taking every
+// step-th tile.
+__device__ void emit_tiles_unsplit(const AttendParams& P, int b, int ibase, int first,
+                                   int step) {
+  const int q0 = P.qsl[b];
+  const int Q = P.qsl[b + 1] - q0, L = P.seq_lens[b];
+  const int tq = prefill_tile_tokens(P.G);
+  const int ntiles = (Q + tq - 1) / tq;
+  for (int t = first; t < ntiles; t += step) {
+    const int ntok = min(tq, Q - t * tq);
+    const int pmax1 = L - Q + t * tq + ntok;
+    put_item(P.items, ibase + (ntiles - 1 - t), b, q0 + t * tq, ntok, kKindPrefill, 0,
+             pmax1, 0, 1, -1, -1, L - Q + t * tq);
+  }
+}
+
+// Shared prefix: tiles of tq consecutive tokens of the whole batch x prefix
+// key ranges of span keys (a multiple of 32); the partial of (token t,
+// range s) sits at slot t * npre + s of the prefix section.  Returns
+// (prefix tiles, prefix ranges); (0, 0) without a shared prefix.
+__device__ int2 emit_prefix_items(const AttendParams& P, bool fits, int first, int step) {
+  int npre = 0, ntp = 0;
+  if (P.prefix_len > 0 && fits) {
+    const int C = P.prefix_len;
+    npre = min(kMaxPrefixSplits, max(1, (C + kPrefixSplitKeys - 1) / kPrefixSplitKeys));
+    const int span = ((C + npre - 1) / npre + 31) & ~31;
+    npre = (C + span - 1) / span;
+    const int tq = prefill_tile_tokens(P.G);
+    ntp = (P.num_q_tokens + tq - 1) / tq;
+    if ((int64_t)ntp * npre > P.max_pre_items) npre = ntp = 0;  // (not reached)
+    for (int i = first; i < ntp * npre; i += step) {
+      const int t = i / npre, s = i - t * npre;
+      const int tok0 = t * tq;
+      put_item(P.pitems, i, 0, tok0, min(tq, P.num_q_tokens - tok0), kKindPrefix,
+               s * span, min(C, (s + 1) * span), s, npre, tok0 * npre, -1, C);
+    }
+  }
+  return make_int2(ntp, npre);
+}
+
+// The plan's totals into the header (one thread).  total: prefill items,
+// full decode splits, partial slots, split tiles; ndec: decode requests
+// (one last split each); pre: prefix tiles and ranges.
+__device__ void finish_header(const AttendParams& P, bool fits, int4 total, int ndec,
+                              int2 pre) {
+  P.hdr->num_prefix_work = (uint32_t)(pre.x * pre.y) * (uint32_t)P.Hkv;
+  P.hdr->prefix_splits = (uint32_t)pre.y;
+  const int all_items = total.x + total.y + ndec;
+  P.hdr->num_items = fits ? (uint32_t)all_items : 0u;
+  P.hdr->num_work = fits ? (uint32_t)all_items * (uint32_t)P.Hkv : 0u;
+  P.hdr->num_prefill_work = fits ? (uint32_t)total.x * (uint32_t)P.Hkv : 0u;
+  P.hdr->num_split_tiles = fits ? (uint32_t)total.w : 0u;
+  if (!fits) atomicOr(&P.hdr->error, 1u);
+}
+
+// The header fields every plan starts from, the queue heads zeroed; false
+// (and an empty plan) if a shared prefix cannot be read.  Threads 0 ..
+// kDecodeShards - 1 of the caller take part.
+__device__ bool start_plan(const AttendParams& P, int tid) {
   if (tid < kDecodeShards) P.dec_counters[tid * kCounterStride] = 0;
   if (tid == 0) {
     P.hdr->prefill_counter = 0;
@@ -340,7 +399,6 @@ __device__ void plan_body(const AttendParams& P) {
     P.hdr->signature = plan_signature(P);
     P.hdr->num_prefix_work = 0;
     P.hdr->prefix_splits = 0;
-    coop_n = 0;
   }
   // A shared prefix is read through request 0's table: it must hold it, and
   // the prefix section must exist.  Otherwise the plan is empty.
@@ -353,51 +411,115 @@ __device__ void plan_body(const AttendParams& P) {
       P.hdr->num_split_tiles = 0;
       P.hdr->error = 2u;
     }
+    return false;
+  }
+  return true;
+}
+
+// The plan of a batch of at most 64 requests, built by one wave with request
+// b on lane b: the same queue as plan_body's (prefill items, full decode
+// splits, the decode requests' last splits longest first, any order within
+// a bucket), with wave scans where plan_body needs workgroup barriers.  (For
+// larger batches the workgroup's threads are faster than one wave's chunks
+// of 64.)  cnt: kLastBuckets ints of LDS.
+__device__ void plan_wave(const AttendParams& P, int* cnt) {
+  const int lane = threadIdx.x;
+  if (!start_plan(P, lane)) return;
+  if (lane < kLastBuckets) cnt[lane] = 0;
+  SeqCounts c{-1, 0, 0, 0, 0, 0, 0};
+  if (lane < P.num_seqs) c = seq_counts(P, lane);
+  const int4 x = scan_lanes(c);
+  const int4 incl = wave_incl_scan4(x);
+  const int4 total = make_int4(__shfl(incl.x, 63), __shfl(incl.y, 63), __shfl(incl.z, 63),
+                               __shfl(incl.w, 63));
+  const int4 e = make_int4(incl.x - x.x, incl.y - x.y, incl.z - x.z, incl.w - x.w);
+  // queue slot of each decode request's last split (one wave: its LDS
+  // operations take effect in program order)
+  int bk = -1, rank = 0;
+  if (c.kind == kKindDecode) {
+    bk = last_bucket(P, lane, c);
+    rank = atomicAdd(&cnt[bk], 1);
+  }
+  const int n = lane < kLastBuckets ? cnt[lane] : 0;
+  const int nincl = wave_incl_scan4(make_int4(n, 0, 0, 0)).x;
+  if (lane < kLastBuckets) cnt[lane] = nincl - n;
+  const int ndec = __shfl(nincl, 63);
+  const bool fits = total.x + total.y + ndec <= P.max_items && total.z <= P.max_partials;
+  const bool unsplit = c.kind == kKindPrefill && c.splitlen == 0;
+  if (fits && c.kind >= 0 && !unsplit)
+    emit_seq(P, lane, c, c.kind == kKindPrefill ? e.x : total.x + e.y,
+             total.x + total.y + (bk >= 0 ? cnt[bk] : 0) + rank, e.z, e.w);
+  // unsplit prefill requests (many tiles): the whole wave emits each one's
+  uint64_t um = __ballot(fits && unsplit);
+  while (um) {
+    const int b = __builtin_ctzll(um);
+    um &= um - 1;
+    emit_tiles_unsplit(P, b, __shfl(e.x, b), lane, 64);
+  }
+  const int2 pre = emit_prefix_items(P, fits, lane, 64);
+  if (lane == 0) finish_header(P, fits, total, ndec, pre);
+}
+// Wave 0 of plan_body: the last splits' bucket counts in cnt become each
+// bucket's first slot (an exclusive scan); *ndec receives their sum, the
+// number of decode requests.
+__device__ __forceinline__ void bucket_starts(int* cnt, int* ndec) {
+  const int lane = threadIdx.x & 63;
+  const int n = lane < kLastBuckets ? cnt[lane] : 0;
+  const int incl = wave_incl_scan4(make_int4(n, 0, 0, 0)).x;
+  if (lane < kLastBuckets) cnt[lane] = incl - n;
+  if (lane == 63) *ndec = incl;
+}
+
+// The work plan, run by one workgroup of kPlanThreads threads (one wave of
+// it for batches of at most 64 requests).
+__device__ void plan_body(const AttendParams& P) {
+  __shared__ int4 lds[kPlanThreads / 64 + 1];
+  __shared__ int coop_n;
+  __shared__ int coop_b[kMaxCoop];
+  __shared__ int coop_base[kMaxCoop];
+  __shared__ int last_cnt[kLastBuckets];
+  __shared__ int ndec_sh;
+  const int tid = threadIdx.x;
+  if (P.num_seqs <= 64) {
+    if (tid < 64) plan_wave(P, last_cnt);
     return;
   }
+  if (tid == 0) coop_n = 0;
+  if (!start_plan(P, tid)) return;
   // scan lanes: x = prefill items, y = decode items, z = partial slots,
   // w = split tiles.  Prefill items go first, decode items after them.
-  int4 total, total2;
+  int4 total;
+  int ndec = 0;  // decode requests: one last split each
   bool fits;
   if (P.num_seqs <= kPlanThreads) {
     // one sweep: every request handled by one thread
     const int b = tid;
     SeqCounts c{-1, 0, 0, 0, 0, 0, 0};
     if (b < P.num_seqs) c = seq_counts(P, b);
-    const int4 e = block_scan4(scan_lanes(c), lds, &total);
-    const int4 e2 = block_scan4(make_int4(c.kind == kKindDecode, 0, 0, 0), lds, &total2);
-    fits = total.x + total.y + total2.x <= P.max_items && total.z <= P.max_partials;
     // The decode requests' last splits (1 .. split keys each) go last in the
     // queue, longest first (16 buckets of 64 keys, any order within one), so
     // that the launch ends on its shortest units.  Where a unit sits in the
     // queue does not change what it computes.
     if (tid < kLastBuckets) last_cnt[tid] = 0;
-    __syncthreads();
+    const int4 e = block_scan4(scan_lanes(c), lds, &total);
     int bk = 0, rank = 0;
     if (c.kind == kKindDecode) {
       bk = last_bucket(P, b, c);
       rank = atomicAdd(&last_cnt[bk], 1);
     }
     __syncthreads();
-    if (tid == 0) {
-      int acc = 0;
-      for (int i = 0; i < kLastBuckets; ++i) {
-        const int n = last_cnt[i];
-        last_cnt[i] = acc;
-        acc += n;
-      }
-    }
+    if (tid < 64) bucket_starts(last_cnt, &ndec_sh);
     __syncthreads();
+    ndec = ndec_sh;
+    fits = total.x + total.y + ndec <= P.max_items && total.z <= P.max_partials;
     if (fits && c.kind >= 0)
       place_seq(P, b, c, c.kind == kKindPrefill ? e.x : total.x + e.y,
                 total.x + total.y + last_cnt[bk] + rank, e.z, e.w, &coop_n, coop_b,
                 coop_base);
-    (void)e2;
   } else {
     // two sweeps over chunks of requests: totals (and the last splits'
     // bucket counts) first, then placement
     total = make_int4(0, 0, 0, 0);
-    total2 = make_int4(0, 0, 0, 0);
     if (tid < kLastBuckets) last_cnt[tid] = 0;
     __syncthreads();
     for (int base = 0; base < P.num_seqs; base += kPlanThreads) {
@@ -405,26 +527,18 @@ __device__ void plan_body(const AttendParams& P) {
       SeqCounts c{-1, 0, 0, 0, 0, 0, 0};
       if (b < P.num_seqs) c = seq_counts(P, b);
       if (c.kind == kKindDecode) atomicAdd(&last_cnt[last_bucket(P, b, c)], 1);
-      int4 t, t2;
+      int4 t;
       block_scan4(scan_lanes(c), lds, &t);
-      block_scan4(make_int4(c.kind == kKindDecode, 0, 0, 0), lds, &t2);
       total.x += t.x;
       total.y += t.y;
       total.z += t.z;
       total.w += t.w;
-      total2.x += t2.x;
-    }
-    fits = total.x + total.y + total2.x <= P.max_items && total.z <= P.max_partials;
-    __syncthreads();
-    if (tid == 0) {  // bucket counts -> first slot of each bucket
-      int acc = 0;
-      for (int i = 0; i < kLastBuckets; ++i) {
-        const int n = last_cnt[i];
-        last_cnt[i] = acc;
-        acc += n;
-      }
     }
     __syncthreads();
+    if (tid < 64) bucket_starts(last_cnt, &ndec_sh);  // counts -> first slots
+    __syncthreads();
+    ndec = ndec_sh;
+    fits = total.x + total.y + ndec <= P.max_items && total.z <= P.max_partials;
     int4 carry = make_int4(0, 0, 0, 0);
     for (int base = 0; base < P.num_seqs; base += kPlanThreads) {
       const int b = base + tid;
@@ -448,48 +562,10 @@ __device__ void plan_body(const AttendParams& P) {
   __syncthreads();
   // unsplit prefill requests: every thread emits some of their tiles
   const int ncoop = min(coop_n, kMaxCoop);
-  for (int k = 0; k < ncoop; ++k) {
-    const int b = coop_b[k];
-    const int q0 = P.qsl[b];
-    const int Q = P.qsl[b + 1] - q0, L = P.seq_lens[b];
-    const int tq = prefill_tile_tokens(P.G);
-    const int ntiles = (Q + tq - 1) / tq;
-    for (int t = tid; t < ntiles; t += kPlanThreads) {
-      const int ntok = min(tq, Q - t * tq);
-      const int pmax1 = L - Q + t * tq + ntok;
-      put_item(P.items, coop_base[k] + (ntiles - 1 - t), b, q0 + t * tq, ntok,
-               kKindPrefill, 0, pmax1, 0, 1, -1, -1, L - Q + t * tq);
-    }
-  }
-  // Shared prefix: tiles of tq consecutive tokens of the whole batch x
-  // prefix key ranges of span keys (a multiple of 32); the partial of
-  // (token t, range s) sits at slot t * npre + s of the prefix section.
-  int npre = 0, ntp = 0;
-  if (P.prefix_len > 0 && fits) {
-    const int C = P.prefix_len;
-    npre = min(kMaxPrefixSplits, max(1, (C + kPrefixSplitKeys - 1) / kPrefixSplitKeys));
-    const int span = ((C + npre - 1) / npre + 31) & ~31;
-    npre = (C + span - 1) / span;
-    const int tq = prefill_tile_tokens(P.G);
-    ntp = (P.num_q_tokens + tq - 1) / tq;
-    if ((int64_t)ntp * npre > P.max_pre_items) npre = ntp = 0;  // (not reached)
-    for (int i = tid; i < ntp * npre; i += kPlanThreads) {
-      const int t = i / npre, s = i - t * npre;
-      const int tok0 = t * tq;
-      put_item(P.pitems, i, 0, tok0, min(tq, P.num_q_tokens - tok0), kKindPrefix,
-               s * span, min(C, (s + 1) * span), s, npre, tok0 * npre, -1, C);
-    }
-  }
-  if (tid == 0) {
-    P.hdr->num_prefix_work = (uint32_t)(ntp * npre) * (uint32_t)P.Hkv;
-    P.hdr->prefix_splits = (uint32_t)npre;
-    const int all_items = total.x + total.y + total2.x;
-    P.hdr->num_items = fits ? (uint32_t)all_items : 0u;
-    P.hdr->num_work = fits ? (uint32_t)all_items * (uint32_t)P.Hkv : 0u;
-    P.hdr->num_prefill_work = fits ? (uint32_t)total.x * (uint32_t)P.Hkv : 0u;
-    P.hdr->num_split_tiles = fits ? (uint32_t)total.w : 0u;
-    if (!fits) atomicOr(&P.hdr->error, 1u);
-  }
+  for (int k = 0; k < ncoop; ++k)
+    emit_tiles_unsplit(P, coop_b[k], coop_base[k], tid, kPlanThreads);
+  const int2 pre = emit_prefix_items(P, fits, tid, kPlanThreads);
+  if (tid == 0) finish_header(P, fits, total, ndec, pre);
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttendParams P) {
@@ -1712,6 +1788,14 @@ __global__ __launch_bounds__(kAttendThreads) void merge_kernel(AttendParams P) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int G = P.G;
+  const uint32_t W = merge_waves_per_head(G, D);
+  const uint32_t per_tile = (uint32_t)P.Hkv * W;
+  // the list entry of the workgroup's first unit, loaded beside the header
+  // (any entry within the list's capacity may be read; it is used only if
+  // the header lists it)
+  const uint32_t first_tile = blockIdx.x / per_tile;
+  const int4 tile0 = (int64_t)first_tile < P.max_items ? P.merge_list[first_tile]
+                                                       : make_int4(-1, 0, 0, 0);
   if (P.hdr->signature != plan_signature(P)) return;
   uint32_t ntiles = P.hdr->num_split_tiles;
   if ((int64_t)ntiles > P.max_items) ntiles = 0;
@@ -1721,13 +1805,13 @@ __global__ __launch_bounds__(kAttendThreads) void merge_kernel(AttendParams P) {
   if (npre < 0 || npre > kMaxPrefixSplits ||
       (int64_t)P.num_q_tokens * npre > P.max_pre_partials)
     ntiles = 0;
-  const uint32_t W = merge_waves_per_head(G, D);
-  const uint32_t per_tile = (uint32_t)P.Hkv * W;
   const uint32_t nunits = ntiles * per_tile;
   const int cl = lane / LPC;          // column within the pass
   const int d0 = (lane % LPC) * 8;    // first of the lane's 8 dims
   for (uint32_t u = blockIdx.x; u < nunits; u += gridDim.x) {
-    const int4 tile = P.merge_list[u / per_tile];  // tok0, ntok, nsplit, pbase
+    // tok0, ntok, nsplit, pbase
+    int4 tile = tile0;
+    if (u != blockIdx.x) tile = P.merge_list[u / per_tile];
     const int kvh = (int)((u % per_tile) / W);
     const int pass0 = (int)(u % W);
     // same rule as for work items: never follow an entry out of bounds
@@ -1975,6 +2059,12 @@ hipError_t scratch_address(void** ptr) {
 
 hipError_t launch_merge(const AttendArgs& a, hipStream_t stream) {
   if (a.num_q_tokens == 0 || a.num_seqs == 0) return hipSuccess;
+  // Without a shared prefix, a request of at most min(decode split, prefill
+  // split) keys is one key range, whatever its kind and its batch: a plan
+  // for such lengths has no split tile, and nothing is launched.
+  constexpr int kOneRange = kSplitDecode8 < kSplitDecode ? kSplitDecode8 : kSplitDecode;
+  static_assert(kOneRange <= kSplitPrefill, "decode splits are the shorter ones");
+  if (!a.cascade && a.max_seq_len <= kOneRange) return hipSuccess;
   const AttendParams P = make_params(a);
   // one workgroup per (split tile, kv head, pass), at most 8 per CU (the
   // workgroups stride over the units)
