@@ -28,9 +28,12 @@
 //           the kernel boundary is what makes partials written on one XCD's
 //           L2 visible on another, without device-wide cache flushes.)
 //
-// Reduction order depends only on (Q_b, L_b) and logical key positions, so
-// results are bitwise independent of physical block ids, of shared blocks, of
-// which wave ran which unit and of the rest of the batch.
+// Reduction order depends only on (Q_b, L_b), logical key positions and,
+// for decode requests of more than 8192 keys, the split length the plan
+// chose for the batch's long requests, so results are bitwise independent
+// of physical block ids, of shared blocks and of which wave ran which unit,
+// and a request of at most 8192 keys (or any prefill chunk) also of the
+// rest of the batch.
 //
 // The kernel template has two instantiations: a decode-only one (batches whose
 // max_query_len fits a decode tile; fewer registers, more resident waves) and
@@ -94,6 +97,7 @@ struct AttendParams {
   int64_t max_pre_partials;
   int32_t prefix_len;  // plan: keys every request shares (0: none)
   int32_t split_decode;  // plan: key range of a decode split (requests <= kLongDecode)
+  int32_t long_units;    // plan: long-request decode units wanted (kLongUnitsPerCu per CU)
   int32_t bs_shift;    // log2 of the tokens per block-table entry (4, or 3)
 };
 
@@ -116,7 +120,6 @@ __device__ __forceinline__ uint32_t plan_signature(const AttendParams& P) {
 }
 
 constexpr int kPlanThreads = 1024;
-static_assert(kSplitDecodeLong / kBlock <= 64, "a decode unit's block ids fit one wave");
 constexpr int kMaxCoop = 64;  // unsplit prefill requests emitted by all threads
 constexpr int kLastBuckets = 16;    // queue order of the decode requests' last splits:
 constexpr int kLastBucketKeys = 64; // by length, 64-key buckets, longest first
@@ -139,14 +142,21 @@ __device__ __forceinline__ int4 scan_lanes(const SeqCounts& c) {
                    c.partials, c.split_tiles);
 }
 
-__device__ SeqCounts seq_counts(const AttendParams& P, int b) {
+// A request's metadata is usable: its tokens inside [0, T), Q <= L and
+// <= max_query_len, L <= max_seq_len, its blocks inside its table row.
+__device__ __forceinline__ bool req_ok(const AttendParams& P, int q0, int q1, int L) {
+  const int Q = q1 - q0;
+  return q0 >= 0 && Q >= 0 && q1 <= P.num_q_tokens && Q <= L && L <= P.max_seq_len &&
+         Q <= P.max_query_len && ((L + (1 << P.bs_shift) - 1) >> P.bs_shift) <= P.bt_stride;
+}
+
+// split_long: key range of the splits of decode requests with more than
+// kLongDecode keys of their own (chosen per plan, pick_split_long).
+__device__ SeqCounts seq_counts(const AttendParams& P, int b, int split_long) {
   SeqCounts c{-1, 0, 0, 0, 0, 0, 0};
   const int q0 = P.qsl[b], q1 = P.qsl[b + 1];
   const int Q = q1 - q0, L = P.seq_lens[b];
-  const bool ok = q0 >= 0 && Q >= 0 && q1 <= P.num_q_tokens && Q <= L &&
-                  L <= P.max_seq_len && Q <= P.max_query_len &&
-                  ((L + (1 << P.bs_shift) - 1) >> P.bs_shift) <= P.bt_stride;
-  if (!ok) {
+  if (!req_ok(P, q0, q1, L)) {
     atomicOr(&P.hdr->error, 2u);
     return c;
   }
@@ -164,7 +174,7 @@ __device__ SeqCounts seq_counts(const AttendParams& P, int b) {
     c.kind = kKindDecode;
     c.ntiles = 1;
     c.tq = Q;
-    c.splitlen = L - C > kLongDecode ? kSplitDecodeLong : P.split_decode;
+    c.splitlen = L - C > kLongDecode ? split_long : P.split_decode;
     const int ns = (L - C + c.splitlen - 1) / c.splitlen;
     const bool part = casc || ns > 1;
     c.items = ns;
@@ -191,6 +201,37 @@ __device__ SeqCounts seq_counts(const AttendParams& P, int b) {
     c.split_tiles += part ? 1 : 0;
   }
   return c;
+}
+
+// Units of request b at each candidate long split (1024, 2048, 4096, 8192
+// keys) if it is a usable decode request with more than kLongDecode keys of
+// its own; zeros otherwise.
+__device__ __forceinline__ int4 long_units(const AttendParams& P, int b) {
+  const int q0 = P.qsl[b], q1 = P.qsl[b + 1], L = P.seq_lens[b];
+  const int own = L - P.prefix_len;
+  if (!req_ok(P, q0, q1, L) || q1 == q0 || q1 - q0 > decode_tile_tokens(P.G) ||
+      L - (q1 - q0) < P.prefix_len || own <= kLongDecode)
+    return make_int4(0, 0, 0, 0);
+  return make_int4((own + 1023) >> 10, (own + 2047) >> 11, (own + 4095) >> 12,
+                   (own + 8191) >> 13);
+}
+static_assert(kSplitLongMin == 1024 && kSplitLongMax == 8192, "long_units' candidates");
+
+// The long split of a plan from the batch's totals of long_units: the
+// shortest candidate whose units (x kv heads) number at most P.long_units.
+__device__ __forceinline__ int pick_split_long(const AttendParams& P, int4 tot) {
+  const int64_t want = P.long_units;
+  const int64_t h = P.Hkv;
+  if ((int64_t)tot.x * h <= want) return 1024;
+  if ((int64_t)tot.y * h <= want) return 2048;
+  if ((int64_t)tot.z * h <= want) return 4096;
+  return 8192;
+}
+
+// Whether a plan can hold long decode requests at all (max_seq_len bounds
+// every request's keys).
+__device__ __forceinline__ bool may_have_long(const AttendParams& P) {
+  return P.max_seq_len - P.prefix_len > kLongDecode;
 }
 
 // Queue bucket of a decode request's last split: longest first, 64 keys a
@@ -426,8 +467,15 @@ __device__ void plan_wave(const AttendParams& P, int* cnt) {
   const int lane = threadIdx.x;
   if (!start_plan(P, lane)) return;
   if (lane < kLastBuckets) cnt[lane] = 0;
+  int split_long = kSplitLongMin;
+  if (may_have_long(P)) {
+    const int4 u = lane < P.num_seqs ? long_units(P, lane) : make_int4(0, 0, 0, 0);
+    const int4 ui = wave_incl_scan4(u);
+    split_long = pick_split_long(P, make_int4(__shfl(ui.x, 63), __shfl(ui.y, 63),
+                                              __shfl(ui.z, 63), __shfl(ui.w, 63)));
+  }
   SeqCounts c{-1, 0, 0, 0, 0, 0, 0};
-  if (lane < P.num_seqs) c = seq_counts(P, lane);
+  if (lane < P.num_seqs) c = seq_counts(P, lane, split_long);
   const int4 x = scan_lanes(c);
   const int4 incl = wave_incl_scan4(x);
   const int4 total = make_int4(__shfl(incl.x, 63), __shfl(incl.y, 63), __shfl(incl.z, 63),
@@ -494,8 +542,14 @@ __device__ void plan_body(const AttendParams& P) {
   if (P.num_seqs <= kPlanThreads) {
     // one sweep: every request handled by one thread
     const int b = tid;
+    int split_long = kSplitLongMin;
+    if (may_have_long(P)) {
+      int4 tl;
+      block_scan4(b < P.num_seqs ? long_units(P, b) : make_int4(0, 0, 0, 0), lds, &tl);
+      split_long = pick_split_long(P, tl);
+    }
     SeqCounts c{-1, 0, 0, 0, 0, 0, 0};
-    if (b < P.num_seqs) c = seq_counts(P, b);
+    if (b < P.num_seqs) c = seq_counts(P, b, split_long);
     // The decode requests' last splits (1 .. split keys each) go last in the
     // queue, longest first (16 buckets of 64 keys, any order within one), so
     // that the launch ends on its shortest units.  Where a unit sits in the
@@ -518,14 +572,29 @@ __device__ void plan_body(const AttendParams& P) {
                 coop_base);
   } else {
     // two sweeps over chunks of requests: totals (and the last splits'
-    // bucket counts) first, then placement
+    // bucket counts) first, then placement (and before them, if the batch
+    // can hold long decode requests, one for their split)
+    int split_long = kSplitLongMin;
+    if (may_have_long(P)) {
+      int4 tl = make_int4(0, 0, 0, 0);
+      for (int base = 0; base < P.num_seqs; base += kPlanThreads) {
+        const int b = base + tid;
+        int4 t;
+        block_scan4(b < P.num_seqs ? long_units(P, b) : make_int4(0, 0, 0, 0), lds, &t);
+        tl.x += t.x;
+        tl.y += t.y;
+        tl.z += t.z;
+        tl.w += t.w;
+      }
+      split_long = pick_split_long(P, tl);
+    }
     total = make_int4(0, 0, 0, 0);
     if (tid < kLastBuckets) last_cnt[tid] = 0;
     __syncthreads();
     for (int base = 0; base < P.num_seqs; base += kPlanThreads) {
       const int b = base + tid;
       SeqCounts c{-1, 0, 0, 0, 0, 0, 0};
-      if (b < P.num_seqs) c = seq_counts(P, b);
+      if (b < P.num_seqs) c = seq_counts(P, b, split_long);
       if (c.kind == kKindDecode) atomicAdd(&last_cnt[last_bucket(P, b, c)], 1);
       int4 t;
       block_scan4(scan_lanes(c), lds, &t);
@@ -543,7 +612,7 @@ __device__ void plan_body(const AttendParams& P) {
     for (int base = 0; base < P.num_seqs; base += kPlanThreads) {
       const int b = base + tid;
       SeqCounts c{-1, 0, 0, 0, 0, 0, 0};
-      if (b < P.num_seqs) c = seq_counts(P, b);
+      if (b < P.num_seqs) c = seq_counts(P, b, split_long);
       int4 t;
       const int4 e = block_scan4(scan_lanes(c), lds, &t);
       // next free slot of the request's bucket (any order within a bucket)
@@ -1578,7 +1647,7 @@ __device__ __forceinline__ bool item_ok(const AttendParams& P,
             (it.kv0 & 31) == 0 && it.kv1 > it.kv0 && it.kv1 <= P.max_seq_len &&
             ((it.kv1 + (1 << P.bs_shift) - 1) >> P.bs_shift) <= P.bt_stride &&
             it.nsplit >= 1 && it.split >= 0 && it.split < it.nsplit;
-  if (it.kind == kKindDecode) ok = ok && (it.kv1 - it.kv0) <= kSplitDecodeLong;
+  if (it.kind == kKindDecode) ok = ok && (it.kv1 - it.kv0) <= kSplitLongMax;
   if (it.nsplit > 1) ok = ok && it.pbase >= 0;
   if (it.pbase >= 0)
     ok = ok && (int64_t)it.pbase + (int64_t)it.ntok * it.nsplit <=
@@ -1949,6 +2018,7 @@ AttendParams make_params(const AttendArgs& a) {
   P.split_decode = (a.kv8 && !a.cascade && a.max_query_len <= decode_tile_tokens(P.G))
                        ? kSplitDecode8 : kSplitDecode;
   P.bs_shift = a.block_size == 8 ? 3 : 4;
+  P.long_units = (a.num_cus > 0 ? a.num_cus : 1) * kLongUnitsPerCu;
   return P;
 }
 

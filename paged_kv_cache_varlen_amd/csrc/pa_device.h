@@ -11,16 +11,24 @@ namespace pa {
 constexpr int kBlock = 16;  // tokens per KV block
 
 // Work decomposition of pa_attend (see attend.hip).
-// Decode splits: 512 logical tokens, 1024 for requests longer than
-// kLongDecode (fewer, longer units where there are many anyway).  The split
-// length depends on the request's own length only.
+// Decode splits: 512 logical tokens.  Requests longer than kLongDecode are
+// cut into ranges of 1024, 2048, 4096 or 8192 keys, one length per plan: the
+// shortest for which the batch's long-request units number at most
+// kLongUnitsPerCu per CU (one per SIMD), else 8192.  Measured on MI355X,
+// long ranges streamed as one unbroken pass per SIMD read faster than twice
+// as many shorter units in two rounds (16 x 32768 keys, GQA 8: 351 -> 322 us;
+// 4 to 32 requests of 32768 keys: 81-84% of 8 TB/s), while half a unit per
+// SIMD leaves bandwidth unused.  A short request's split depends on its own
+// length only; a long request's also on the batch's other long requests.
 constexpr int kSplitDecode = 512;
 // 8-bit pools, decode-only batches: their units stream twice as fast, and
 // shorter key ranges balance the launch better (measured: 384 keys, 11%
 // faster attention on the Llama-3-8B decode layer; mixed batches and bf16
 // pools keep 512).
 constexpr int kSplitDecode8 = 384;
-constexpr int kSplitDecodeLong = 1024;
+constexpr int kSplitLongMin = 1024;  // long decode splits: 1024 .. 8192 keys
+constexpr int kSplitLongMax = 8192;
+constexpr int kLongUnitsPerCu = 4;
 constexpr int kLongDecode = 8192;
 constexpr int kSplitPrefill = 2048;  // logical tokens per prefill split
 // A prefill request is split along its keys only if it has fewer than this

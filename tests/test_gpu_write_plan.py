@@ -147,6 +147,20 @@ def test_binding_rejects_metadata_of_other_types():
 
 # ---- the plan's work list, read back ------------------------------------------------
 
+def expected_long_split(L, Q, Hq, Hkv):
+    """Key range of the splits of decode requests of more than 8192 keys: the
+    shortest of 1024, 2048, 4096 whose units (requests' ranges x kv heads)
+    number at most 4 per CU, else 8192."""
+    G = Hq // Hkv
+    own = np.asarray(L, np.int64)[(np.asarray(L) > 8192) & (np.asarray(Q) >= 1) &
+                                  (np.asarray(Q) <= 16 // G)]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for s in (1024, 2048, 4096):
+        if int(((own + s - 1) // s).sum()) * Hkv <= 4 * cus:
+            return s
+    return 8192
+
+
 # Internal workspace layout of a plain plan: the plan header at byte 0 (num_work,
 # num_items, error, ... as uint32), then 8 decode-queue counters 4 KiB apart
 # from byte 4096, then the work items (16 int32 each: seq, tok0, ntok, kind, kv0,
@@ -154,17 +168,12 @@ def test_binding_rejects_metadata_of_other_types():
 ITEMS_OFFSET = 4096 + 8 * 4096
 
 
-@pytest.mark.parametrize("B,fp8", [(700, False), (700, True), (1500, False), (1500, True)])
-def test_plan_items_partition_every_request(B, fp8):
-    # one sweep (<= 1024 requests) and two sweeps, bf16 and 8-bit plans: every
-    # slot in [0, num_items) holds exactly one valid item (the workspace is
-    # filled with 0xff first, so a slot left unwritten is seen), and the items
-    # of each request cover its keys 0 .. L-1 once, in ranges of the plan's
-    # split length
-    rng = np.random.default_rng(40 + B)
-    L = rng.integers(1, 9500, size=B)
-    Q = np.minimum(L, rng.integers(1, 3, size=B))
-    w = W.make_workload("plan-%d" % B, L, Q, 16, 2, 64, seed=41)
+def read_plan(w, fp8):
+    """Plan w into a workspace filled with 0xff, read the work items back and
+    check that every slot in [0, num_items) holds exactly one valid decode item
+    and that each request's items cover its keys 0 .. L-1 once, in split
+    order.  Returns, per request, the lengths of its key ranges."""
+    B, L, Q = w.num_seqs, w.seq_lens, w.query_lens
     bt, sl, qsl = i32(w.block_tables), i32(w.seq_lens), i32(w.query_start_loc)
     ws = pa.alloc_workspace(w.num_seqs, w.num_q_tokens, w.num_q_heads, w.num_kv_heads,
                             w.head_dim, w.max_query_len, w.max_seq_len)
@@ -188,11 +197,53 @@ def test_plan_items_partition_every_request(B, fp8):
     counts = np.bincount(seq, minlength=B)
     assert np.array_equal(counts, nsplit[np.searchsorted(seq, np.arange(B))])
     first = np.searchsorted(seq, np.arange(B))
+    ranges = []
     for b in range(B):
         s0 = first[b]
         r0, r1 = kv0[s0:s0 + counts[b]], kv1[s0:s0 + counts[b]]
         assert r0[0] == 0 and r1[-1] == L[b]
         assert np.array_equal(r0[1:], r1[:-1]), b
         assert np.array_equal(split[s0:s0 + counts[b]], np.arange(counts[b]))
-        span = 1024 if L[b] > 8192 else (384 if fp8 else 512)
-        assert np.all(r1[:-1] - r0[:-1] == span), b
+        ranges.append(r1 - r0)
+    return ranges
+
+
+@pytest.mark.parametrize("B,fp8", [(700, False), (700, True), (1500, False), (1500, True)])
+def test_plan_items_partition_every_request(B, fp8):
+    # one sweep (<= 1024 requests) and two sweeps, bf16 and 8-bit plans: every
+    # slot in [0, num_items) holds exactly one valid item (the workspace is
+    # filled with 0xff first, so a slot left unwritten is seen), and the items
+    # of each request cover its keys 0 .. L-1 once, in ranges of the plan's
+    # split length
+    rng = np.random.default_rng(40 + B)
+    L = rng.integers(1, 9500, size=B)
+    Q = np.minimum(L, rng.integers(1, 3, size=B))
+    w = W.make_workload("plan-%d" % B, L, Q, 16, 2, 64, seed=41)
+    ranges = read_plan(w, fp8)
+    long_split = expected_long_split(L, Q, w.num_q_heads, w.num_kv_heads)
+    for b in range(B):
+        span = long_split if L[b] > 8192 else (384 if fp8 else 512)
+        assert np.all(ranges[b][:-1] == span), b
+
+
+@pytest.mark.parametrize("B,Lr,seed", [(12, 12000, 1), (20, 16384, 2), (40, 16384, 3),
+                                        (3, 12000, 4)])
+def test_long_split_follows_the_batch(B, Lr, seed):
+    # decode batches of requests of more than 8192 keys, one plan sweep: the
+    # plan cuts them into 2048-, 4096- or 8192-key ranges where 1024-key ones
+    # would number more than 4 per CU (on 256 CUs: 12 x 12000 -> 2048,
+    # 20 x 16384 -> 4096, 40 x 16384 -> 8192, 3 x 12000 -> 1024), the last
+    # range shorter; every output row against the oracle
+    rng = np.random.default_rng(seed)
+    L = (Lr - rng.integers(0, 200, size=B)).astype(np.int64)
+    Q = np.ones(B, np.int64)
+    w = W.make_workload("long-%d" % B, L, Q, 8, 8, 64, seed=seed)
+    span = expected_long_split(L, Q, 8, 8)
+    ranges = read_plan(w, False)
+    for b in range(B):
+        assert np.all(ranges[b][:-1] == span) and ranges[b][-1] <= span, b
+    out = tensor_bits(Uploaded(w).attend())
+    kc, vc = oracle_pool(w)
+    ref = oracle.attend(w.q, kc, vc, w.block_tables, w.seq_lens, w.query_start_loc,
+                        w.num_kv_heads, w.scale)
+    check_close(out, ref, "long split %d" % span)
