@@ -97,7 +97,9 @@ struct AttendParams {
   int64_t max_pre_partials;
   int32_t prefix_len;  // plan: keys every request shares (0: none)
   int32_t split_decode;  // plan: key range of a decode split (requests <= kLongDecode)
-  int32_t long_units;    // plan: long-request decode units wanted (kLongUnitsPerCu per CU)
+  int32_t long_units;    // plan: decode units wanted (kLongUnitsPerCu per CU)
+  int32_t* ranges;       // stream plans: first item of each decode range (the workspace's table)
+  int32_t stream_ok;     // plan: stream plans allowed (bf16 pools)
   int32_t bs_shift;    // log2 of the tokens per block-table entry (4, or 3)
 };
 
@@ -120,6 +122,11 @@ __device__ __forceinline__ uint32_t plan_signature(const AttendParams& P) {
 }
 
 constexpr int kPlanThreads = 1024;
+// Without a shared prefix, a request of at most this many keys is one key
+// range whatever its kind and its batch (the shorter of the decode splits).
+constexpr int kOneRangeKeys = kSplitDecode8 < kSplitDecode ? kSplitDecode8 : kSplitDecode;
+static_assert(kOneRangeKeys <= kSplitPrefill && kOneRangeKeys <= kMinRangeKeys,
+              "no split below kOneRangeKeys");
 constexpr int kMaxCoop = 64;  // unsplit prefill requests emitted by all threads
 constexpr int kLastBuckets = 16;    // queue order of the decode requests' last splits:
 constexpr int kLastBucketKeys = 64; // by length, 64-key buckets, longest first
@@ -136,10 +143,53 @@ struct SeqCounts {
 
 // Queue regions: prefill items, then full-length decode splits, then the
 // (shorter) last split of every decode request: longest units first.
-__device__ __forceinline__ int4 scan_lanes(const SeqCounts& c) {
+// (stream plans: every decode item in the decode region, in request order)
+__device__ __forceinline__ int4 scan_lanes(const SeqCounts& c, bool stream = false) {
   const bool dec = c.kind == kKindDecode;
-  return make_int4(c.kind == kKindPrefill ? c.items : 0, dec ? c.items - 1 : 0,
-                   c.partials, c.split_tiles);
+  return make_int4(c.kind == kKindPrefill ? c.items : 0,
+                   dec ? (stream ? c.items : c.items - 1) : 0, c.partials, c.split_tiles);
+}
+
+// Stream plans.  The decode requests' own keys, in request order and in
+// pairs of 32, form one stream of T pairs cut into R ranges of equal length
+// (+-1 pair); each (range, kv head) is one unit of work, and a request's
+// piece in each range it meets is one work item.  Every wave then streams
+// the same number of keys, one long pass, whatever the mix of lengths.  A
+// plan is a stream plan when it has no shared prefix, max_seq_len is above
+// kOneRangeKeys and the batch fills long_units units with ranges of at
+// least kMinRangeKeys keys; otherwise each request is cut into splits of its
+// own (seq_counts) and every split is a unit.
+// Range r holds q + 1 pairs if r < rem, else q (T = R q + rem).
+struct Stream {
+  int T, R, q, rem;  // R = 0: not a stream plan
+};
+__device__ __forceinline__ int range_start(const Stream& st, int r) {
+  return r * st.q + min(r, st.rem);
+}
+__device__ __forceinline__ int range_of(const Stream& st, int x) {  // x in [0, T)
+  const int big = st.rem * (st.q + 1);
+  return x < big ? x / (st.q + 1) : st.rem + (x - big) / st.q;
+}
+__device__ __forceinline__ Stream stream_of(const AttendParams& P, int T) {
+  const int want = min(P.long_units, kMaxStreamUnits) / P.Hkv;
+  // (the pair counts are summed in 32 bits: batches whose bound could pass
+  // 2^31 pairs are not streamed)
+  const bool ok = P.prefix_len == 0 && P.max_seq_len > kOneRangeKeys && P.stream_ok &&
+                  (int64_t)P.max_seq_len * P.num_seqs < ((int64_t)1 << 36) && want >= 1 &&
+                  (int64_t)T >= (int64_t)want * (kMinRangeKeys / 32);
+  return ok ? Stream{T, want, T / want, T % want} : Stream{T, 0, 0, 0};
+}
+// Own 32-key pairs of a decode request (0 for others).
+__device__ __forceinline__ int stream_pairs(const AttendParams& P, int b, const SeqCounts& c) {
+  return c.kind == kKindDecode ? (P.seq_lens[b] - P.prefix_len + 31) >> 5 : 0;
+}
+// A decode request's counts in a stream plan (its pairs [gp, gp + np)).
+__device__ __forceinline__ void stream_counts(const Stream& st, int gp, int np,
+                                              SeqCounts& c) {
+  const int ns = range_of(st, gp + np - 1) - range_of(st, gp) + 1;
+  c.items = ns;
+  c.partials = ns > 1 ? c.tq * ns : 0;
+  c.split_tiles = ns > 1 ? 1 : 0;
 }
 
 // A request's metadata is usable: its tokens inside [0, T), Q <= L and
@@ -355,6 +405,27 @@ __device__ void emit_seq(const AttendParams& P, int b, const SeqCounts& c,
   }
 }
 
+// The items of decode request b in a stream plan (pairs [gp, gp + np)), one
+// per range it meets, in key order; the first item of every range that
+// starts inside the request goes into the range table.
+__device__ void emit_pieces(const AttendParams& P, int b, const SeqCounts& c, const Stream& st,
+                            int gp, int np, int ibase, int pbase, int cbase) {
+  const int q0 = P.qsl[b], Q = c.tq, L = P.seq_lens[b];
+  const int r0 = range_of(st, gp);
+  const int ns = c.items;
+  const bool part = ns > 1;
+  int rs = range_start(st, r0);
+  for (int s = 0; s < ns; ++s) {
+    const int re = range_start(st, r0 + s + 1);
+    const int a = max(gp, rs), e = min(gp + np, re);
+    put_item(P.items, ibase + s, b, q0, Q, kKindDecode, 32 * (a - gp), min(L, 32 * (e - gp)),
+             s, ns, part ? pbase : -1, part ? cbase : -1, L - Q);
+    if (rs >= gp) P.ranges[r0 + s] = ibase + s;
+    rs = re;
+  }
+  if (part) P.merge_list[cbase] = make_int4(q0, Q, ns, pbase);
+}
+
 // Registers the item bases of request b: emitted now by this thread, or
 // queued for the whole workgroup (unsplit prefill: many tiles).
 __device__ __forceinline__ void place_seq(const AttendParams& P, int b,
@@ -418,12 +489,16 @@ __device__ int2 emit_prefix_items(const AttendParams& P, bool fits, int first, i
 // full decode splits, partial slots, split tiles; ndec: decode requests
 // (one last split each); pre: prefix tiles and ranges.
 __device__ void finish_header(const AttendParams& P, bool fits, int4 total, int ndec,
-                              int2 pre) {
+                              int2 pre, const Stream& st) {
   P.hdr->num_prefix_work = (uint32_t)(pre.x * pre.y) * (uint32_t)P.Hkv;
   P.hdr->prefix_splits = (uint32_t)pre.y;
   const int all_items = total.x + total.y + ndec;
+  // stream plans: the decode units are (range, kv head) pairs
+  const int units = st.R > 0 ? total.x + (int)st.R : all_items;
+  if (fits && st.R > 0) P.ranges[st.R] = total.x + total.y;
+  P.hdr->num_ranges = fits ? (uint32_t)st.R : 0u;
   P.hdr->num_items = fits ? (uint32_t)all_items : 0u;
-  P.hdr->num_work = fits ? (uint32_t)all_items * (uint32_t)P.Hkv : 0u;
+  P.hdr->num_work = fits ? (uint32_t)units * (uint32_t)P.Hkv : 0u;
   P.hdr->num_prefill_work = fits ? (uint32_t)total.x * (uint32_t)P.Hkv : 0u;
   P.hdr->num_split_tiles = fits ? (uint32_t)total.w : 0u;
   if (!fits) atomicOr(&P.hdr->error, 1u);
@@ -440,6 +515,7 @@ __device__ bool start_plan(const AttendParams& P, int tid) {
     P.hdr->signature = plan_signature(P);
     P.hdr->num_prefix_work = 0;
     P.hdr->prefix_splits = 0;
+    P.hdr->num_ranges = 0;
   }
   // A shared prefix is read through request 0's table: it must hold it, and
   // the prefix section must exist.  Otherwise the plan is empty.
@@ -476,7 +552,13 @@ __device__ void plan_wave(const AttendParams& P, int* cnt) {
   }
   SeqCounts c{-1, 0, 0, 0, 0, 0, 0};
   if (lane < P.num_seqs) c = seq_counts(P, lane, split_long);
-  const int4 x = scan_lanes(c);
+  // stream partition of the decode requests
+  const int np = stream_pairs(P, lane, c);
+  const int npi = wave_incl_scan4(make_int4(np, 0, 0, 0)).x;
+  const Stream st = stream_of(P, __shfl(npi, 63));
+  const int gp = npi - np;
+  if (st.R > 0 && c.kind == kKindDecode) stream_counts(st, gp, np, c);
+  const int4 x = scan_lanes(c, st.R > 0);
   const int4 incl = wave_incl_scan4(x);
   const int4 total = make_int4(__shfl(incl.x, 63), __shfl(incl.y, 63), __shfl(incl.z, 63),
                                __shfl(incl.w, 63));
@@ -484,7 +566,7 @@ __device__ void plan_wave(const AttendParams& P, int* cnt) {
   // queue slot of each decode request's last split (one wave: its LDS
   // operations take effect in program order)
   int bk = -1, rank = 0;
-  if (c.kind == kKindDecode) {
+  if (c.kind == kKindDecode && st.R == 0) {
     bk = last_bucket(P, lane, c);
     rank = atomicAdd(&cnt[bk], 1);
   }
@@ -494,7 +576,9 @@ __device__ void plan_wave(const AttendParams& P, int* cnt) {
   const int ndec = __shfl(nincl, 63);
   const bool fits = total.x + total.y + ndec <= P.max_items && total.z <= P.max_partials;
   const bool unsplit = c.kind == kKindPrefill && c.splitlen == 0;
-  if (fits && c.kind >= 0 && !unsplit)
+  if (fits && c.kind == kKindDecode && st.R > 0)
+    emit_pieces(P, lane, c, st, gp, np, total.x + e.y, e.z, e.w);
+  else if (fits && c.kind >= 0 && !unsplit)
     emit_seq(P, lane, c, c.kind == kKindPrefill ? e.x : total.x + e.y,
              total.x + total.y + (bk >= 0 ? cnt[bk] : 0) + rank, e.z, e.w);
   // unsplit prefill requests (many tiles): the whole wave emits each one's
@@ -505,7 +589,7 @@ __device__ void plan_wave(const AttendParams& P, int* cnt) {
     emit_tiles_unsplit(P, b, __shfl(e.x, b), lane, 64);
   }
   const int2 pre = emit_prefix_items(P, fits, lane, 64);
-  if (lane == 0) finish_header(P, fits, total, ndec, pre);
+  if (lane == 0) finish_header(P, fits, total, ndec, pre, st);
 }
 // Wave 0 of plan_body: the last splits' bucket counts in cnt become each
 // bucket's first slot (an exclusive scan); *ndec receives their sum, the
@@ -538,6 +622,8 @@ __device__ void plan_body(const AttendParams& P) {
   // w = split tiles.  Prefill items go first, decode items after them.
   int4 total;
   int ndec = 0;  // decode requests: one last split each
+  Stream st{0, 0, 0, 0};  // (stream plans: one sweep only)
+  int np = 0, gp = 0;
   bool fits;
   if (P.num_seqs <= kPlanThreads) {
     // one sweep: every request handled by one thread
@@ -550,14 +636,20 @@ __device__ void plan_body(const AttendParams& P) {
     }
     SeqCounts c{-1, 0, 0, 0, 0, 0, 0};
     if (b < P.num_seqs) c = seq_counts(P, b, split_long);
+    // stream partition of the decode requests
+    np = stream_pairs(P, b, c);
+    int4 tp;
+    gp = block_scan4(make_int4(np, 0, 0, 0), lds, &tp).x;
+    st = stream_of(P, tp.x);
+    if (st.R > 0 && c.kind == kKindDecode) stream_counts(st, gp, np, c);
     // The decode requests' last splits (1 .. split keys each) go last in the
     // queue, longest first (16 buckets of 64 keys, any order within one), so
     // that the launch ends on its shortest units.  Where a unit sits in the
     // queue does not change what it computes.
     if (tid < kLastBuckets) last_cnt[tid] = 0;
-    const int4 e = block_scan4(scan_lanes(c), lds, &total);
+    const int4 e = block_scan4(scan_lanes(c, st.R > 0), lds, &total);
     int bk = 0, rank = 0;
-    if (c.kind == kKindDecode) {
+    if (c.kind == kKindDecode && st.R == 0) {
       bk = last_bucket(P, b, c);
       rank = atomicAdd(&last_cnt[bk], 1);
     }
@@ -566,7 +658,9 @@ __device__ void plan_body(const AttendParams& P) {
     __syncthreads();
     ndec = ndec_sh;
     fits = total.x + total.y + ndec <= P.max_items && total.z <= P.max_partials;
-    if (fits && c.kind >= 0)
+    if (fits && c.kind == kKindDecode && st.R > 0)
+      emit_pieces(P, b, c, st, gp, np, total.x + e.y, e.z, e.w);
+    else if (fits && c.kind >= 0)
       place_seq(P, b, c, c.kind == kKindPrefill ? e.x : total.x + e.y,
                 total.x + total.y + last_cnt[bk] + rank, e.z, e.w, &coop_n, coop_b,
                 coop_base);
@@ -634,7 +728,7 @@ __device__ void plan_body(const AttendParams& P) {
   for (int k = 0; k < ncoop; ++k)
     emit_tiles_unsplit(P, coop_b[k], coop_base[k], tid, kPlanThreads);
   const int2 pre = emit_prefix_items(P, fits, tid, kPlanThreads);
-  if (tid == 0) finish_header(P, fits, total, ndec, pre);
+  if (tid == 0) finish_header(P, fits, total, ndec, pre, st);
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttendParams P) {
@@ -886,11 +980,94 @@ __device__ __forceinline__ bf16x8 load_v(const uint16_t* vp, int c, int lane) {
 // each 16-key step reads two pool tiles: lanes of tokens 0-7 (K) and of key
 // groups 0-1 (V) from the first, the others from the second; the operands
 // land in the same registers as from one 16-token tile.
+__device__ __forceinline__ bool item_ok(const AttendParams& P,
+                                        const WorkItem& it) {
+  const int maxtok = it.kind == kKindDecode ? decode_tile_tokens(P.G)
+                                            : prefill_tile_tokens(P.G);
+  bool ok = it.seq >= 0 && it.seq < P.num_seqs && it.tok0 >= 0 &&
+            it.ntok >= 1 && it.ntok <= maxtok &&
+            it.tok0 + it.ntok <= P.num_q_tokens && it.kv0 >= 0 &&
+            (it.kv0 & 31) == 0 && it.kv1 > it.kv0 && it.kv1 <= P.max_seq_len &&
+            ((it.kv1 + (1 << P.bs_shift) - 1) >> P.bs_shift) <= P.bt_stride &&
+            it.nsplit >= 1 && it.split >= 0 && it.split < it.nsplit;
+  if (it.kind == kKindDecode) ok = ok && (it.kv1 - it.kv0) <= kSplitLongMax;
+  if (it.nsplit > 1) ok = ok && it.pbase >= 0;
+  if (it.pbase >= 0)
+    ok = ok && (int64_t)it.pbase + (int64_t)it.ntok * it.nsplit <=
+                   (it.kind == kKindPrefix ? P.max_pre_partials : P.max_partials);
+  return ok;
+}
+
+// One shard of the decode queue as a wave sees it: local unit k is queue
+// entry base + stride * k (k < n); a claim returning t hands the wave local
+// unit t + first_dynamic, and the claim returning claims - 1 is the shard's
+// last in the launch, which resets the counter for the next launch.
+struct DecodeQueue {
+  uint32_t* counter;
+  uint32_t base, stride, n, first_dynamic, claims;
+  bool unit_items;  // a unit is one item (plans without stream ranges)
+};
+
+// The wave's next unit as run_unit prepares it during the current one: its
+// local index k (>= n: none), its item as 16 dwords on lanes 0..15 once
+// item_ready, and the physical ids of its first 64 blocks, one per lane,
+// once ids_ready.
+struct NextUnit {
+  uint32_t k;
+  int itv;
+  int idv;
+  bool item_ready;
+  bool ids_ready;
+};
+
+// Work item idx as 16 dwords, dword i on lane i (0 on lanes 16..63): a vector
+// load, ordered with the block loads in flight (a scalar load would be waited
+// for by the softmax's cross-lane steps).
+__device__ __forceinline__ int load_item_lanes(const WorkItem* items, uint32_t idx, int lane) {
+  const int32_t* p = reinterpret_cast<const int32_t*>(items + idx);
+  return lane < 16 ? p[lane] : 0;
+}
+
+__device__ __forceinline__ WorkItem item_of_lanes(int v) {
+  WorkItem it;
+  it.seq = __builtin_amdgcn_readlane(v, 0);
+  it.tok0 = __builtin_amdgcn_readlane(v, 1);
+  it.ntok = __builtin_amdgcn_readlane(v, 2);
+  it.kind = __builtin_amdgcn_readlane(v, 3);
+  it.kv0 = __builtin_amdgcn_readlane(v, 4);
+  it.kv1 = __builtin_amdgcn_readlane(v, 5);
+  it.split = __builtin_amdgcn_readlane(v, 6);
+  it.nsplit = __builtin_amdgcn_readlane(v, 7);
+  it.pbase = __builtin_amdgcn_readlane(v, 8);
+  it.counter = __builtin_amdgcn_readlane(v, 9);
+  it.posbase = __builtin_amdgcn_readlane(v, 10);
+#pragma unroll
+  for (int i = 0; i < 5; ++i) it.pad[i] = 0;
+  return it;
+}
+
+// Physical ids of 16-token blocks c0 .. c0 + 63 of a unit (one per lane,
+// lanes past its last block 0), clamped into the pool.
+__device__ __forceinline__ int block_ids(const AttendParams& P, const WorkItem& it, int c0,
+                                         int lane) {
+  const int jb1 = (it.kv1 + kBlock - 1) >> 4;
+  int idv = 0;
+  if (lane < min(64, jb1 - c0)) idv = P.bt[(int64_t)it.seq * P.bt_stride + c0 + lane];
+  return idv < 0 ? 0 : (idv >= P.num_blocks ? (int)(P.num_blocks - 1) : idv);
+}
+
+// One decode item (it, kv head kvh) of a wave.  With next_item < 0 it ends
+// the wave's unit: exactly one claim on the queue, issued with the loads of
+// the item's third block from last, so that its value is back by the time
+// that block is computed; otherwise item next_item of the same unit follows.
+// Either way the next item, then its first block ids, are loaded while the
+// last blocks stream, so that the next call starts on its block loads at
+// once (nx: in, the ids of this item if ready; out, the next one).
 template <int D, int CT, int NB, bool STREAM, bool KV8, bool BS8 = false>
-__device__ __forceinline__ uint32_t run_unit(const AttendParams& P,
-                                             const WorkItem& it, int kvh,
-                                             int lane,
-                                             uint32_t* counter = nullptr) {
+__device__ __forceinline__ void run_unit(const AttendParams& P,
+                                         const WorkItem& it, int kvh,
+                                         int lane, const DecodeQueue& Qd,
+                                         NextUnit& nx, int next_item) {
   static_assert(!(KV8 && BS8), "8-token blocks: bf16 pools only");
   constexpr int KC = D / 32;
   constexpr int NT = D / 16;
@@ -916,8 +1093,36 @@ __device__ __forceinline__ uint32_t run_unit(const AttendParams& P,
   const int jb1 = (it.kv1 + kBlock - 1) >> 4;
   const int32_t* btrow = P.bt + (int64_t)b * P.bt_stride;
   const int64_t tile_elems = (int64_t)kBlock * D;
+  // 8-bit pools: no prefetch (their waves need the registers for more
+  // waves per SIMD, which hide the dequantisation); the claim goes with the
+  // last block's loads and is read at the end
+  constexpr bool kPrefetch = !KV8;
+  const int jclaim = kPrefetch ? max(jb0, jb1 - 3) : jb1 - 1;  // its loads carry the claim
   uint32_t claim = 0;
-  bool claimed = false;
+  bool claimed = next_item >= 0, took = false;
+  const bool have_ids = kPrefetch && !BS8 && nx.ids_ready;
+  const int ids0 = nx.idv;
+  NextUnit next{nx.k, 0, 0, false, false};
+  // the next item: the unit's next one, or the claimed unit's (when a unit
+  // is one item), loaded at once
+  auto take_claim = [&]() {
+    if (next_item >= 0) {
+      if (kPrefetch) {
+        next.itv = load_item_lanes(P.items, (uint32_t)next_item, lane);
+        next.item_ready = true;
+      }
+    } else {
+      const uint32_t t = __builtin_amdgcn_readfirstlane(__shfl(claim, 0));
+      if (t + 1u == Qd.claims && lane == 0) atomicExch(Qd.counter, 0u);
+      next.k = t + Qd.first_dynamic;
+      if (kPrefetch && next.k < Qd.n && Qd.unit_items) {
+        next.itv = load_item_lanes(P.items, (Qd.base + Qd.stride * next.k) / (uint32_t)P.Hkv,
+                                   lane);
+        next.item_ready = true;
+      }
+    }
+    took = true;
+  };
 
   for (int c0 = jb0; c0 < jb1; c0 += 64) {
     const int nblk = min(64, jb1 - c0);
@@ -933,14 +1138,14 @@ __device__ __forceinline__ uint32_t run_unit(const AttendParams& P,
         idv2 = j8 + 1 < nb8 ? btrow[j8 + 1] : idv;
       }
       idv2 = idv2 < 0 ? 0 : (idv2 >= P.num_blocks ? (int)(P.num_blocks - 1) : idv2);
+      idv = idv < 0 ? 0 : (idv >= P.num_blocks ? (int)(P.num_blocks - 1) : idv);
     } else {
-      if (lane < nblk) idv = btrow[c0 + lane];
+      idv = (have_ids && c0 == jb0) ? ids0 : block_ids(P, it, c0, lane);
     }
-    idv = idv < 0 ? 0 : (idv >= P.num_blocks ? (int)(P.num_blocks - 1) : idv);
 
     auto issue = [&](KVBuf<D, KV8>& buf, int j) {
-      if (counter != nullptr && !claimed && c0 + j == jb1 - 1) {
-        if (lane == 0) claim = atomicAdd(counter, 1u);
+      if (!claimed && c0 + j == jclaim) {
+        if (lane == 0) claim = atomicAdd(Qd.counter, 1u);
         claimed = true;
       }
       const int id = __builtin_amdgcn_readlane(idv, j);
@@ -1055,6 +1260,7 @@ __device__ __forceinline__ uint32_t run_unit(const AttendParams& P,
           acc[ct][c + KC] = mfma16(vhi, pop, acc[ct][c + KC]);
         }
       }
+      if (kPrefetch && c0 + j == jclaim && claimed && !took) take_claim();
     };
 
     // Ring of NB block buffers, NB-1 blocks in flight while one is computed.
@@ -1078,6 +1284,20 @@ __device__ __forceinline__ uint32_t run_unit(const AttendParams& P,
     for (int k = 0; k < NB - 1; ++k)
       if (j + k < nblk) compute(buf[k], j + k);
   }
+  // exactly one claim per call, whatever the loop above did
+  if (!claimed) {
+    if (lane == 0) claim = atomicAdd(Qd.counter, 1u);
+    claimed = true;
+  }
+  if (!took) take_claim();
+  // the next unit's first block ids go out before this unit's results
+  if (kPrefetch && next.item_ready && !BS8) {
+    const WorkItem ni = item_of_lanes(next.itv);
+    if (item_ok(P, ni) && ni.kind == kKindDecode) {
+      next.idv = block_ids(P, ni, ni.kv0 >> 4, lane);
+      next.ids_ready = true;
+    }
+  }
   float l[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
@@ -1085,12 +1305,8 @@ __device__ __forceinline__ uint32_t run_unit(const AttendParams& P,
     l[ct] += __shfl_xor(l[ct], 16);
     l[ct] += __shfl_xor(l[ct], 32);
   }
-  // exactly one claim per call, whatever the loop above did
-  if (counter != nullptr && !claimed) {
-    if (lane == 0) claim = atomicAdd(counter, 1u);
-  }
   finish_unit<D, CT, KV8>(P, it, kvh, lane, acc, mrun, l);
-  return __builtin_amdgcn_readfirstlane(__shfl(claim, 0));
+  nx = next;
 }
 
 // ---- prefill tiles: one workgroup, K/V shared through LDS -------------------
@@ -1637,23 +1853,6 @@ __device__ __forceinline__ void run_tile(const AttendParams& P,
 // A work item read back from the workspace is used only if every index it
 // leads to stays inside the buffers this launch was given (a stale or foreign
 // workspace then costs outputs, never an out-of-bounds access).
-__device__ __forceinline__ bool item_ok(const AttendParams& P,
-                                        const WorkItem& it) {
-  const int maxtok = it.kind == kKindDecode ? decode_tile_tokens(P.G)
-                                            : prefill_tile_tokens(P.G);
-  bool ok = it.seq >= 0 && it.seq < P.num_seqs && it.tok0 >= 0 &&
-            it.ntok >= 1 && it.ntok <= maxtok &&
-            it.tok0 + it.ntok <= P.num_q_tokens && it.kv0 >= 0 &&
-            (it.kv0 & 31) == 0 && it.kv1 > it.kv0 && it.kv1 <= P.max_seq_len &&
-            ((it.kv1 + (1 << P.bs_shift) - 1) >> P.bs_shift) <= P.bt_stride &&
-            it.nsplit >= 1 && it.split >= 0 && it.split < it.nsplit;
-  if (it.kind == kKindDecode) ok = ok && (it.kv1 - it.kv0) <= kSplitLongMax;
-  if (it.nsplit > 1) ok = ok && it.pbase >= 0;
-  if (it.pbase >= 0)
-    ok = ok && (int64_t)it.pbase + (int64_t)it.ntok * it.nsplit <=
-                   (it.kind == kKindPrefix ? P.max_pre_partials : P.max_partials);
-  return ok;
-}
 
 template <int D, bool MIXED, bool KV8, bool BS8 = false>
 __device__ __forceinline__ void attend_body(const AttendParams& P,
@@ -1667,6 +1866,17 @@ __device__ __forceinline__ void attend_body(const AttendParams& P,
   if ((uint64_t)num_work > (uint64_t)P.max_items * (uint64_t)P.Hkv) num_work = 0;
   uint32_t num_pre = P.hdr->num_prefill_work;
   if (num_pre > num_work) num_pre = num_work;
+  // stream plans: the decode units are (range, kv head) pairs over a range
+  // table whose entries are item indices in [prefill items, num_items]
+  uint32_t num_items = P.hdr->num_items;
+  if ((int64_t)num_items > P.max_items) num_items = 0;
+  uint32_t nranges = P.hdr->num_ranges;
+  const int num_pre_items = (int)(num_pre / (uint32_t)P.Hkv);
+  if (nranges > (uint32_t)kMaxStreamUnits || (nranges > 0 && P.ranges == nullptr) ||
+      (nranges > 0 && num_pre + nranges * (uint32_t)P.Hkv != num_work)) {
+    nranges = 0;
+    num_work = num_pre;  // (never: the plan writes them together)
+  }
   // shared-prefix units (their own item list) come first in the prefill queue
   uint32_t num_pfx = P.pitems != nullptr ? P.hdr->num_prefix_work : 0u;
   if ((uint64_t)num_pfx > (uint64_t)P.max_pre_items * (uint64_t)P.Hkv) num_pfx = 0;
@@ -1745,15 +1955,47 @@ __device__ __forceinline__ void attend_body(const AttendParams& P,
       k ^= 1;
     }
   };
+  const DecodeQueue dq{dctr, num_pre + shard, S, n_s, dec_static, dec_claims, nranges == 0};
   auto decode_units = [&](uint32_t k) {  // k: local index in the shard
-    for (uint32_t pass = 0; k < n_s && pass <= n_s; ++pass) {
-      const uint32_t w = num_pre + shard + S * k;
-      const WorkItem it = P.items[w / Hkv];
-      if (item_ok(P, it) && it.kind == kKindDecode)
-        k = dec_claimed(run_unit<D, kDecodeColTiles, kDecodeStages, true, KV8, BS8>(
-            P, it, (int)(w % Hkv), lane, dctr));
-      else
-        k = dec_claimed(claim(dctr));
+    NextUnit nx{k, 0, 0, false, false};
+    for (uint32_t pass = 0; nx.k < n_s && pass <= n_s; ++pass) {
+      const uint32_t w = num_pre + shard + S * nx.k;
+      if (nranges == 0) {  // the unit is one item
+        if (!nx.item_ready) nx.itv = load_item_lanes(P.items, w / Hkv, lane);
+        const WorkItem it = item_of_lanes(nx.itv);
+        if (item_ok(P, it) && it.kind == kKindDecode) {
+          run_unit<D, kDecodeColTiles, kDecodeStages, true, KV8, BS8>(P, it, (int)(w % Hkv),
+                                                                       lane, dq, nx, -1);
+        } else {
+          nx.k = dec_claimed(claim(dctr));
+          nx.item_ready = nx.ids_ready = false;
+        }
+        continue;
+      }
+      // stream plans: the unit is the items of range r for kv head kvh
+      const uint32_t d = w - num_pre;
+      const uint32_t r = d / Hkv;
+      const int kvh = (int)(d % Hkv);
+      int i0 = P.ranges[r], i1 = P.ranges[r + 1];
+      if (i0 < num_pre_items || i1 > (int)num_items || i1 <= i0) i1 = i0;  // (never: no items)
+      nx.item_ready = nx.ids_ready = false;
+      bool done = false;
+      for (int i = i0; i < i1; ++i) {
+        if (!nx.item_ready) nx.itv = load_item_lanes(P.items, (uint32_t)i, lane);
+        const WorkItem it = item_of_lanes(nx.itv);
+        const bool last = i + 1 == i1;
+        if (item_ok(P, it) && it.kind == kKindDecode) {
+          run_unit<D, kDecodeColTiles, kDecodeStages, true, KV8, BS8>(P, it, kvh, lane, dq,
+                                                                       nx, last ? -1 : i + 1);
+          done = last;
+        } else {
+          nx.item_ready = nx.ids_ready = false;
+        }
+      }
+      if (!done) {  // the unit's claim, if its last item did not make it
+        nx.k = dec_claimed(claim(dctr));
+        nx.item_ready = nx.ids_ready = false;
+      }
     }
   };
   const uint32_t static_k = (blockIdx.x / S - pf_s) * kWpg + wslot;
@@ -1775,12 +2017,13 @@ __device__ __forceinline__ void attend_body(const AttendParams& P,
   if (prefill_first) decode_units(dec_claimed(claim(dctr)));
 }
 
-// Decode-only batches: registers for the 3-stage pipeline (two waves per
-// SIMD for head_dim 128, four for 64; three for 128 with 8-bit pools, whose
-// blocks take half the registers).
+// Decode-only batches: registers for the 3-stage pipeline and the next
+// item's prefetch (two waves per SIMD for head_dim 128, three for 64; three
+// for 128 with 8-bit pools, whose blocks take half the registers and which
+// do not prefetch).
 template <int D, bool KV8>
 __global__ __launch_bounds__(kAttendThreads)
-__attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : (KV8 ? 3 : 2), 8)))
+__attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : (KV8 ? 3 : 2), 8)))
 void attend_decode_kernel(AttendParams P) {
   attend_body<D, false, KV8>(P, nullptr);
 }
@@ -1797,7 +2040,7 @@ void attend_mixed_kernel(AttendParams P) {
 // The same two kernels over pools of 8-token blocks (bf16).
 template <int D>
 __global__ __launch_bounds__(kAttendThreads)
-__attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2, 8)))
+__attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2, 8)))
 void attend_decode_bs8_kernel(AttendParams P) {
   attend_body<D, false, false, true>(P, nullptr);
 }
@@ -2019,6 +2262,12 @@ AttendParams make_params(const AttendArgs& a) {
                        ? kSplitDecode8 : kSplitDecode;
   P.bs_shift = a.block_size == 8 ? 3 : 4;
   P.long_units = (a.num_cus > 0 ? a.num_cus : 1) * kLongUnitsPerCu;
+  // Stream plans are made for bf16 pools only: an 8-bit unit's
+  // dequantisation needs more than one wave per SIMD to keep up with its
+  // stream (measured: the 8B decode layer 49 -> 72 us as a stream plan).  A
+  // plain plan serves 8-bit launches too, so every launch reads the table.
+  P.ranges = reinterpret_cast<int32_t*>(ws + a.ws.ranges);
+  P.stream_ok = a.kv8 ? 0 : 1;
   return P;
 }
 
@@ -2132,9 +2381,7 @@ hipError_t launch_merge(const AttendArgs& a, hipStream_t stream) {
   // Without a shared prefix, a request of at most min(decode split, prefill
   // split) keys is one key range, whatever its kind and its batch: a plan
   // for such lengths has no split tile, and nothing is launched.
-  constexpr int kOneRange = kSplitDecode8 < kSplitDecode ? kSplitDecode8 : kSplitDecode;
-  static_assert(kOneRange <= kSplitPrefill, "decode splits are the shorter ones");
-  if (!a.cascade && a.max_seq_len <= kOneRange) return hipSuccess;
+  if (!a.cascade && a.max_seq_len <= kOneRangeKeys) return hipSuccess;
   const AttendParams P = make_params(a);
   // one workgroup per (split tile, kv head, pass), at most 8 per CU (the
   // workgroups stride over the units)

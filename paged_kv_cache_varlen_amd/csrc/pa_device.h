@@ -30,6 +30,11 @@ constexpr int kSplitLongMin = 1024;  // long decode splits: 1024 .. 8192 keys
 constexpr int kSplitLongMax = 8192;
 constexpr int kLongUnitsPerCu = 4;
 constexpr int kLongDecode = 8192;
+// Stream partition of a plan's decode requests (see attend.hip): at most
+// kMaxStreamUnits (range, kv head) units, ranges of at least kMinRangeKeys
+// keys.
+constexpr int kMaxStreamUnits = 2048;
+constexpr int kMinRangeKeys = 512;
 constexpr int kSplitPrefill = 2048;  // logical tokens per prefill split
 // A prefill request is split along its keys only if it has fewer than this
 // many (query tile x kv head) work units on its own.
@@ -83,6 +88,7 @@ struct PlanHeader {
   uint32_t num_prefill_work;  // prefill items * num_kv_heads
   uint32_t num_prefix_work;   // shared-prefix items * num_kv_heads
   uint32_t prefix_splits;     // key ranges of the shared prefix (0: none)
+  uint32_t num_ranges;        // stream ranges of the decode items (0: one unit per item)
 };
 
 // Byte offsets of the workspace sections.
@@ -92,6 +98,7 @@ struct WorkspaceLayout {
   size_t merge_list;    // int4[max_items]  split tiles: tok0, ntok, nsplit, pbase
   size_t part_ml;       // float2[max_partials * Hq]  (running max, sum)
   size_t part_acc;      // float[max_partials * Hq * D]
+  size_t ranges;        // int32[kMaxStreamUnits + 1] first item of each stream range
   size_t total;
   int64_t max_items;
   int64_t max_partials;
@@ -140,12 +147,14 @@ inline WorkspaceLayout workspace_layout(int32_t num_seqs, int64_t num_q_tokens,
   // decode-kind requests: one tile each; prefill-kind: <= T/tq_p + B tiles.
   int64_t dec_tiles = B;
   int64_t pre_tiles = (max_query_len > tq_d) ? (T / tq_p + B) : 0;
-  w.max_items = dec_tiles * sd + pre_tiles * sp;
+  // (a decode request cut by stream ranges of at least kMinRangeKeys keys
+  // has at most ceil(L / 384) + 2 pieces)
+  w.max_items = dec_tiles * (sd + 2) + pre_tiles * sp;
   if (w.max_items < 1) w.max_items = 1;
   // partial slots: decode tokens <= min(T, B*tq_d), prefill tokens <= T
   int64_t dec_tok = T < B * tq_d ? T : B * tq_d;
   int64_t pre_tok = (max_query_len > tq_d) ? T : 0;
-  w.max_partials = dec_tok * sd + pre_tok * sp;
+  w.max_partials = dec_tok * (sd + 2) + pre_tok * sp;
   if (w.max_partials < 1) w.max_partials = 1;
   size_t off = 4096;  // the header, then the counters on their own pages
   w.counters = off;
@@ -159,6 +168,8 @@ inline WorkspaceLayout workspace_layout(int32_t num_seqs, int64_t num_q_tokens,
   w.part_acc = off;
   off = align256(off + sizeof(float) * (size_t)w.max_partials * num_q_heads *
                            (size_t)head_dim);
+  w.ranges = off;
+  off = align256(off + sizeof(int32_t) * (size_t)(kMaxStreamUnits + 1));
   w.total = off;
   // prefix tiles span the whole batch: ceil(T / tq_p) tiles x splits
   w.max_pre_items = cdiv64(T, tq_p) * kMaxPrefixSplits;

@@ -193,8 +193,8 @@ def test_config_parity_fp8(k):
 @pytest.mark.parametrize("k", [2])
 def test_plain_plan_serves_8bit_pools(k):
     # decode-only batches over 8-bit pools are planned with 384-key ranges;
-    # the bf16 plan (512-key ranges) is valid too: both within the tolerance
-    # of the oracle on the same codes, every output row
+    # the bf16 plan (here a stream plan) is valid too: both within the
+    # tolerance of the oracle on the same codes, every output row
     w = configs.workload(k)
     scales = configs.FP8_SCALES
     kc, vc = gpu_pool8(w, *scales)

@@ -161,6 +161,32 @@ def expected_long_split(L, Q, Hq, Hkv):
     return 8192
 
 
+def RANGES_OFFSET(w):
+    """Byte offset of the stream range table: the end of the partial
+    accumulators (the layout of pa_attend_workspace_size's sections)."""
+    return stream_table_offset(w.num_seqs, w.num_q_tokens, w.num_q_heads, w.num_kv_heads,
+                               w.head_dim, w.max_query_len, w.max_seq_len)
+
+
+def stream_table_offset(B, T, Hq, Hkv, D, max_q, max_l):
+    al = lambda x: (x + 255) & ~255
+    G = Hq // Hkv
+    tq_d, tq_p = 16 // G, 4 * (32 // G)
+    sd = -(-max(max_l, 1) // 384)
+    sp = -(-max(max_l, 1) // 2048)
+    pre_tiles = (T // tq_p + B) if max_q > tq_d else 0
+    max_items = max(1, B * (sd + 2) + pre_tiles * sp)
+    dec_tok = min(T, B * tq_d)
+    pre_tok = T if max_q > tq_d else 0
+    max_partials = max(1, dec_tok * (sd + 2) + pre_tok * sp)
+    off = 4096 + 4 * 8 * 1024
+    off = al(off + 64 * max_items)
+    off = al(off + 16 * max_items)
+    off = al(off + 8 * max_partials * Hq)
+    off = al(off + 4 * max_partials * Hq * D)
+    return off
+
+
 # Internal workspace layout of a plain plan: the plan header at byte 0 (num_work,
 # num_items, error, ... as uint32), then 8 decode-queue counters 4 KiB apart
 # from byte 4096, then the work items (16 int32 each: seq, tok0, ntok, kind, kv0,
@@ -172,7 +198,10 @@ def read_plan(w, fp8):
     """Plan w into a workspace filled with 0xff, read the work items back and
     check that every slot in [0, num_items) holds exactly one valid decode item
     and that each request's items cover its keys 0 .. L-1 once, in split
-    order.  Returns, per request, the lengths of its key ranges."""
+    order.  For a stream plan (header word 9: the number of stream ranges R),
+    also check the range table: R equal runs of the decode stream (the
+    requests' 32-key pairs in request order), each a run of consecutive items.
+    Returns, per request, the lengths of its key ranges, and R."""
     B, L, Q = w.num_seqs, w.seq_lens, w.query_lens
     bt, sl, qsl = i32(w.block_tables), i32(w.seq_lens), i32(w.query_start_loc)
     ws = pa.alloc_workspace(w.num_seqs, w.num_q_tokens, w.num_q_heads, w.num_kv_heads,
@@ -183,9 +212,9 @@ def read_plan(w, fp8):
     torch.cuda.synchronize()
     raw = ws.cpu().numpy()
     hdr = raw[:64].view(np.uint32)
-    num_work, num_items, err = int(hdr[0]), int(hdr[1]), int(hdr[2])
+    num_work, num_items, err, nranges = int(hdr[0]), int(hdr[1]), int(hdr[2]), int(hdr[9])
     assert err == 0
-    assert num_work == num_items * w.num_kv_heads
+    assert num_work == (nranges if nranges else num_items) * w.num_kv_heads
     items = raw[ITEMS_OFFSET:ITEMS_OFFSET + 64 * num_items].view(np.int32).reshape(-1, 16)
     seq, tok0, ntok, kind, kv0, kv1, split, nsplit = (items[:, i] for i in range(8))
     assert np.all((seq >= 0) & (seq < B)), "unwritten or foreign slot"
@@ -205,7 +234,18 @@ def read_plan(w, fp8):
         assert np.array_equal(r0[1:], r1[:-1]), b
         assert np.array_equal(split[s0:s0 + counts[b]], np.arange(counts[b]))
         ranges.append(r1 - r0)
-    return ranges
+    if nranges:
+        # items in request order (the stream's order), the table R + 1 item
+        # indices from 0 to num_items, every range the same number of pairs +-1
+        assert np.array_equal(order, np.arange(num_items))
+        table = raw[RANGES_OFFSET(w):RANGES_OFFSET(w) + 4 * (nranges + 1)].view(np.int32)
+        assert table[0] == 0 and table[-1] == num_items and np.all(np.diff(table) >= 1)
+        pairs = (kv1 - kv0 + 31) // 32
+        per_range = np.add.reduceat(pairs, table[:-1])
+        total = int(((L + 31) // 32).sum())
+        assert per_range.sum() == total
+        assert per_range.min() >= total // nranges and per_range.max() <= -(-total // nranges)
+    return ranges, nranges
 
 
 @pytest.mark.parametrize("B,fp8", [(700, False), (700, True), (1500, False), (1500, True)])
@@ -219,31 +259,40 @@ def test_plan_items_partition_every_request(B, fp8):
     L = rng.integers(1, 9500, size=B)
     Q = np.minimum(L, rng.integers(1, 3, size=B))
     w = W.make_workload("plan-%d" % B, L, Q, 16, 2, 64, seed=41)
-    ranges = read_plan(w, fp8)
+    ranges, nranges = read_plan(w, fp8)
+    # 700 requests, bf16 plan: one sweep, a stream plan; 8-bit plans and
+    # 1500 requests (two sweeps): splits of each request's own
+    assert (nranges > 0) == (B <= 1024 and not fp8)
+    if nranges:
+        return
     long_split = expected_long_split(L, Q, w.num_q_heads, w.num_kv_heads)
     for b in range(B):
         span = long_split if L[b] > 8192 else (384 if fp8 else 512)
         assert np.all(ranges[b][:-1] == span), b
 
 
-@pytest.mark.parametrize("B,Lr,seed", [(12, 12000, 1), (20, 16384, 2), (40, 16384, 3),
-                                        (3, 12000, 4)])
-def test_long_split_follows_the_batch(B, Lr, seed):
-    # decode batches of requests of more than 8192 keys, one plan sweep: the
-    # plan cuts them into 2048-, 4096- or 8192-key ranges where 1024-key ones
-    # would number more than 4 per CU (on 256 CUs: 12 x 12000 -> 2048,
-    # 20 x 16384 -> 4096, 40 x 16384 -> 8192, 3 x 12000 -> 1024), the last
-    # range shorter; every output row against the oracle
+@pytest.mark.parametrize("B,Lr,seed", [(12, 12000, 1), (40, 16384, 3), (3, 12000, 4),
+                                        (2, 30000, 5)])
+def test_long_requests_stream_or_split(B, Lr, seed):
+    # decode batches of requests of more than 8192 keys: where the batch fills
+    # 4 units per CU with ranges of at least 512 keys it is a stream plan
+    # (12 x 12000 and 40 x 16384 keys over 8 kv heads on 256 CUs), otherwise
+    # each request is cut into splits of the long length the batch picks
+    # (3 x 12000, 2 x 30000: 1024); every output row against the oracle
     rng = np.random.default_rng(seed)
     L = (Lr - rng.integers(0, 200, size=B)).astype(np.int64)
     Q = np.ones(B, np.int64)
     w = W.make_workload("long-%d" % B, L, Q, 8, 8, 64, seed=seed)
-    span = expected_long_split(L, Q, 8, 8)
-    ranges = read_plan(w, False)
-    for b in range(B):
-        assert np.all(ranges[b][:-1] == span) and ranges[b][-1] <= span, b
+    ranges, nranges = read_plan(w, False)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    want = min(4 * cus, 2048) // 8
+    assert (nranges > 0) == (int(((L + 31) // 32).sum()) >= want * 16)
+    if nranges == 0:
+        span = expected_long_split(L, Q, 8, 8)
+        for b in range(B):
+            assert np.all(ranges[b][:-1] == span) and ranges[b][-1] <= span, b
     out = tensor_bits(Uploaded(w).attend())
     kc, vc = oracle_pool(w)
     ref = oracle.attend(w.q, kc, vc, w.block_tables, w.seq_lens, w.query_start_loc,
                         w.num_kv_heads, w.scale)
-    check_close(out, ref, "long split %d" % span)
+    check_close(out, ref, "long requests, %d stream ranges" % nranges)
