@@ -184,12 +184,14 @@ __device__ __forceinline__ int stream_pairs(const AttendParams& P, int b, const 
   return c.kind == kKindDecode ? (P.seq_lens[b] - P.prefix_len + 31) >> 5 : 0;
 }
 // A decode request's counts in a stream plan (its pairs [gp, gp + np)).
-__device__ __forceinline__ void stream_counts(const Stream& st, int gp, int np,
-                                              SeqCounts& c) {
+// (with a shared prefix every decode tile merges, as in seq_counts)
+__device__ __forceinline__ void stream_counts(const AttendParams& P, const Stream& st, int gp,
+                                              int np, SeqCounts& c) {
   const int ns = range_of(st, gp + np - 1) - range_of(st, gp) + 1;
+  const bool part = P.prefix_len > 0 || ns > 1;
   c.items = ns;
-  c.partials = ns > 1 ? c.tq * ns : 0;
-  c.split_tiles = ns > 1 ? 1 : 0;
+  c.partials = part ? c.tq * ns : 0;
+  c.split_tiles = part ? 1 : 0;
 }
 
 // A request's metadata is usable: its tokens inside [0, T), Q <= L and
@@ -408,22 +410,23 @@ __device__ void emit_seq(const AttendParams& P, int b, const SeqCounts& c,
 // The items of decode request b in a stream plan (pairs [gp, gp + np)), one
 // per range it meets, in key order; the first item of every range that
 // starts inside the request goes into the range table.
-__device__ void emit_pieces(const AttendParams& P, int b, const SeqCounts& c, const Stream& st,
-                            int gp, int np, int ibase, int pbase, int cbase) {
-  const int q0 = P.qsl[b], Q = c.tq, L = P.seq_lens[b];
+// Pieces first, first + step, ... of the request (several threads can share
+// a request of many pieces).
+__device__ void emit_pieces(const AttendParams& P, int b, int Q, int ns, const Stream& st,
+                            int gp, int np, int ibase, int pbase, int cbase, int first = 0,
+                            int step = 1) {
+  const int q0 = P.qsl[b], L = P.seq_lens[b];
+  const int C = P.prefix_len;  // first key of the request's own items
   const int r0 = range_of(st, gp);
-  const int ns = c.items;
-  const bool part = ns > 1;
-  int rs = range_start(st, r0);
-  for (int s = 0; s < ns; ++s) {
-    const int re = range_start(st, r0 + s + 1);
+  const bool part = C > 0 || ns > 1;
+  for (int s = first; s < ns; s += step) {
+    const int rs = range_start(st, r0 + s), re = range_start(st, r0 + s + 1);
     const int a = max(gp, rs), e = min(gp + np, re);
-    put_item(P.items, ibase + s, b, q0, Q, kKindDecode, 32 * (a - gp), min(L, 32 * (e - gp)),
-             s, ns, part ? pbase : -1, part ? cbase : -1, L - Q);
+    put_item(P.items, ibase + s, b, q0, Q, kKindDecode, C + 32 * (a - gp),
+             min(L, C + 32 * (e - gp)), s, ns, part ? pbase : -1, part ? cbase : -1, L - Q);
     if (rs >= gp) P.ranges[r0 + s] = ibase + s;
-    rs = re;
   }
-  if (part) P.merge_list[cbase] = make_int4(q0, Q, ns, pbase);
+  if (part && first == 0) P.merge_list[cbase] = make_int4(q0, Q, ns, pbase);
 }
 
 // Registers the item bases of request b: emitted now by this thread, or
@@ -557,7 +560,7 @@ __device__ void plan_wave(const AttendParams& P, int* cnt) {
   const int npi = wave_incl_scan4(make_int4(np, 0, 0, 0)).x;
   const Stream st = stream_of(P, __shfl(npi, 63));
   const int gp = npi - np;
-  if (st.R > 0 && c.kind == kKindDecode) stream_counts(st, gp, np, c);
+  if (st.R > 0 && c.kind == kKindDecode) stream_counts(P, st, gp, np, c);
   const int4 x = scan_lanes(c, st.R > 0);
   const int4 incl = wave_incl_scan4(x);
   const int4 total = make_int4(__shfl(incl.x, 63), __shfl(incl.y, 63), __shfl(incl.z, 63),
@@ -576,9 +579,11 @@ __device__ void plan_wave(const AttendParams& P, int* cnt) {
   const int ndec = __shfl(nincl, 63);
   const bool fits = total.x + total.y + ndec <= P.max_items && total.z <= P.max_partials;
   const bool unsplit = c.kind == kKindPrefill && c.splitlen == 0;
-  if (fits && c.kind == kKindDecode && st.R > 0)
-    emit_pieces(P, lane, c, st, gp, np, total.x + e.y, e.z, e.w);
-  else if (fits && c.kind >= 0 && !unsplit)
+  // (a request of many pieces is emitted by the whole wave, below)
+  const bool many = c.kind == kKindDecode && st.R > 0 && c.items > 8;
+  if (fits && c.kind == kKindDecode && st.R > 0 && !many)
+    emit_pieces(P, lane, c.tq, c.items, st, gp, np, total.x + e.y, e.z, e.w);
+  else if (fits && c.kind >= 0 && !unsplit && !(c.kind == kKindDecode && st.R > 0))
     emit_seq(P, lane, c, c.kind == kKindPrefill ? e.x : total.x + e.y,
              total.x + total.y + (bk >= 0 ? cnt[bk] : 0) + rank, e.z, e.w);
   // unsplit prefill requests (many tiles): the whole wave emits each one's
@@ -587,6 +592,13 @@ __device__ void plan_wave(const AttendParams& P, int* cnt) {
     const int b = __builtin_ctzll(um);
     um &= um - 1;
     emit_tiles_unsplit(P, b, __shfl(e.x, b), lane, 64);
+  }
+  uint64_t mm = __ballot(fits && many);
+  while (mm) {
+    const int b = __builtin_ctzll(mm);
+    mm &= mm - 1;
+    emit_pieces(P, b, __shfl(c.tq, b), __shfl(c.items, b), st, __shfl(gp, b), __shfl(np, b),
+                total.x + __shfl(e.y, b), __shfl(e.z, b), __shfl(e.w, b), lane, 64);
   }
   const int2 pre = emit_prefix_items(P, fits, lane, 64);
   if (lane == 0) finish_header(P, fits, total, ndec, pre, st);
@@ -641,7 +653,7 @@ __device__ void plan_body(const AttendParams& P) {
     int4 tp;
     gp = block_scan4(make_int4(np, 0, 0, 0), lds, &tp).x;
     st = stream_of(P, tp.x);
-    if (st.R > 0 && c.kind == kKindDecode) stream_counts(st, gp, np, c);
+    if (st.R > 0 && c.kind == kKindDecode) stream_counts(P, st, gp, np, c);
     // The decode requests' last splits (1 .. split keys each) go last in the
     // queue, longest first (16 buckets of 64 keys, any order within one), so
     // that the launch ends on its shortest units.  Where a unit sits in the
@@ -659,7 +671,7 @@ __device__ void plan_body(const AttendParams& P) {
     ndec = ndec_sh;
     fits = total.x + total.y + ndec <= P.max_items && total.z <= P.max_partials;
     if (fits && c.kind == kKindDecode && st.R > 0)
-      emit_pieces(P, b, c, st, gp, np, total.x + e.y, e.z, e.w);
+      emit_pieces(P, b, c.tq, c.items, st, gp, np, total.x + e.y, e.z, e.w);
     else if (fits && c.kind >= 0)
       place_seq(P, b, c, c.kind == kKindPrefill ? e.x : total.x + e.y,
                 total.x + total.y + last_cnt[bk] + rank, e.z, e.w, &coop_n, coop_b,
@@ -1289,7 +1301,7 @@ __device__ __forceinline__ void run_unit(const AttendParams& P,
     if (lane == 0) claim = atomicAdd(Qd.counter, 1u);
     claimed = true;
   }
-  if (!took) take_claim();
+  if (kPrefetch && !took) take_claim();
   // the next unit's first block ids go out before this unit's results
   if (kPrefetch && next.item_ready && !BS8) {
     const WorkItem ni = item_of_lanes(next.itv);
@@ -1306,6 +1318,7 @@ __device__ __forceinline__ void run_unit(const AttendParams& P,
     l[ct] += __shfl_xor(l[ct], 32);
   }
   finish_unit<D, CT, KV8>(P, it, kvh, lane, acc, mrun, l);
+  if (!took) take_claim();  // (no prefetch: the claim is read after the stores)
   nx = next;
 }
 
