@@ -97,9 +97,9 @@ struct AttendParams {
   int64_t max_pre_partials;
   int32_t prefix_len;  // plan: keys every request shares (0: none)
   int32_t split_decode;  // plan: key range of a decode split (requests <= kLongDecode)
-  int32_t long_units;    // plan: decode units wanted (kLongUnitsPerCu per CU)
+  int32_t long_units;    // plan: decode units wanted (per CU: kLongUnitsPerCu, 8-bit kUnitsPerCu8)
   int32_t* ranges;       // stream plans: first item of each decode range (the workspace's table)
-  int32_t stream_ok;     // plan: stream plans allowed (bf16 pools)
+  int32_t min_range_pairs;  // plan: shortest stream range, in 32-key pairs
   int32_t bs_shift;    // log2 of the tokens per block-table entry (4, or 3)
 };
 
@@ -157,8 +157,9 @@ __device__ __forceinline__ int4 scan_lanes(const SeqCounts& c, bool stream = fal
 // the same number of keys, one long pass, whatever the mix of lengths.  A
 // plan is a stream plan when it has no shared prefix, max_seq_len is above
 // kOneRangeKeys and the batch fills long_units units with ranges of at
-// least kMinRangeKeys keys; otherwise each request is cut into splits of its
-// own (seq_counts) and every split is a unit.
+// least min_range_pairs pairs (512 keys; 8-bit plans 384); otherwise each
+// request is cut into splits of its own (seq_counts) and every split is a
+// unit.
 // Range r holds q + 1 pairs if r < rem, else q (T = R q + rem).
 struct Stream {
   int T, R, q, rem;  // R = 0: not a stream plan
@@ -174,9 +175,9 @@ __device__ __forceinline__ Stream stream_of(const AttendParams& P, int T) {
   const int want = min(P.long_units, kMaxStreamUnits) / P.Hkv;
   // (the pair counts are summed in 32 bits: batches whose bound could pass
   // 2^31 pairs are not streamed)
-  const bool ok = P.prefix_len == 0 && P.max_seq_len > kOneRangeKeys && P.stream_ok &&
+  const bool ok = P.prefix_len == 0 && P.max_seq_len > kOneRangeKeys &&
                   (int64_t)P.max_seq_len * P.num_seqs < ((int64_t)1 << 36) && want >= 1 &&
-                  (int64_t)T >= (int64_t)want * (kMinRangeKeys / 32);
+                  (int64_t)T >= (int64_t)want * P.min_range_pairs;
   return ok ? Stream{T, want, T / want, T % want} : Stream{T, 0, 0, 0};
 }
 // Own 32-key pairs of a decode request (0 for others).
@@ -579,26 +580,43 @@ __device__ void plan_wave(const AttendParams& P, int* cnt) {
   const int ndec = __shfl(nincl, 63);
   const bool fits = total.x + total.y + ndec <= P.max_items && total.z <= P.max_partials;
   const bool unsplit = c.kind == kKindPrefill && c.splitlen == 0;
+  const bool piece = c.kind == kKindDecode && st.R > 0;
   // (a request of many pieces is emitted by the whole wave, below)
-  const bool many = c.kind == kKindDecode && st.R > 0 && c.items > 8;
-  if (fits && c.kind == kKindDecode && st.R > 0 && !many)
+  const bool many = piece && c.items > 16;
+  if (fits && piece && !many)
     emit_pieces(P, lane, c.tq, c.items, st, gp, np, total.x + e.y, e.z, e.w);
-  else if (fits && c.kind >= 0 && !unsplit && !(c.kind == kKindDecode && st.R > 0))
+  else if (fits && c.kind >= 0 && !unsplit && !piece)
     emit_seq(P, lane, c, c.kind == kKindPrefill ? e.x : total.x + e.y,
              total.x + total.y + (bk >= 0 ? cnt[bk] : 0) + rank, e.z, e.w);
+  // Requests of many pieces: decode item p (p < total.y, in request order)
+  // is piece p - e.y_b of the request b with e.y_b <= p < e.y_b + ns_b, the
+  // last lane whose e.y is at most p (a request without decode items adds
+  // nothing to e.y, so the request that holds p ends its run of equal
+  // values); the lanes take one item each in turn and emit those of such
+  // requests.
+  if (__ballot(fits && many)) {
+    for (int p0 = 0; p0 < total.y; p0 += 64) {
+      const int p = p0 + lane;
+      int b = 0;
+#pragma unroll
+      for (int step = 32; step > 0; step >>= 1) {
+        const int ey = __shfl(e.y, min(b + step, 63));
+        if (b + step < 64 && ey <= p) b += step;
+      }
+      const bool mb = __shfl((int)many, b) != 0;
+      const int Qb = __shfl(c.tq, b), nsb = __shfl(c.items, b);
+      const int gpb = __shfl(gp, b), npb = __shfl(np, b), eyb = __shfl(e.y, b);
+      const int ezb = __shfl(e.z, b), ewb = __shfl(e.w, b);
+      if (p < total.y && mb)
+        emit_pieces(P, b, Qb, nsb, st, gpb, npb, total.x + eyb, ezb, ewb, p - eyb, nsb);
+    }
+  }
   // unsplit prefill requests (many tiles): the whole wave emits each one's
   uint64_t um = __ballot(fits && unsplit);
   while (um) {
     const int b = __builtin_ctzll(um);
     um &= um - 1;
     emit_tiles_unsplit(P, b, __shfl(e.x, b), lane, 64);
-  }
-  uint64_t mm = __ballot(fits && many);
-  while (mm) {
-    const int b = __builtin_ctzll(mm);
-    mm &= mm - 1;
-    emit_pieces(P, b, __shfl(c.tq, b), __shfl(c.items, b), st, __shfl(gp, b), __shfl(np, b),
-                total.x + __shfl(e.y, b), __shfl(e.z, b), __shfl(e.w, b), lane, 64);
   }
   const int2 pre = emit_prefix_items(P, fits, lane, 64);
   if (lane == 0) finish_header(P, fits, total, ndec, pre, st);
@@ -2274,13 +2292,15 @@ AttendParams make_params(const AttendArgs& a) {
   P.split_decode = (a.kv8 && !a.cascade && a.max_query_len <= decode_tile_tokens(P.G))
                        ? kSplitDecode8 : kSplitDecode;
   P.bs_shift = a.block_size == 8 ? 3 : 4;
-  P.long_units = (a.num_cus > 0 ? a.num_cus : 1) * kLongUnitsPerCu;
-  // Stream plans are made for bf16 pools only: an 8-bit unit's
-  // dequantisation needs more than one wave per SIMD to keep up with its
-  // stream (measured: the 8B decode layer 49 -> 72 us as a stream plan).  A
-  // plain plan serves 8-bit launches too, so every launch reads the table.
+  // units wanted: 4 per CU over bf16 pools (one per SIMD), 8 over 8-bit
+  // pools, whose dequantisation needs two waves per SIMD to keep up with
+  // the stream (8B decode layer, 8-bit: 49 -> 72 us with 4 units per CU as a
+  // stream plan, 51 -> 48 us with 8)
+  P.long_units = (a.num_cus > 0 ? a.num_cus : 1) * (a.kv8 ? kUnitsPerCu8 : kLongUnitsPerCu);
+  // (a plan of either kind serves either pool type, so every launch reads
+  // the table)
   P.ranges = reinterpret_cast<int32_t*>(ws + a.ws.ranges);
-  P.stream_ok = a.kv8 ? 0 : 1;
+  P.min_range_pairs = (a.kv8 ? kMinRangeKeys8 : kMinRangeKeys) / 32;
   return P;
 }
 

@@ -28,13 +28,17 @@ constexpr int kSplitDecode = 512;
 constexpr int kSplitDecode8 = 384;
 constexpr int kSplitLongMin = 1024;  // long decode splits: 1024 .. 8192 keys
 constexpr int kSplitLongMax = 8192;
-constexpr int kLongUnitsPerCu = 4;
+constexpr int kLongUnitsPerCu = 4;  // (also the stream units per CU over bf16 pools)
 constexpr int kLongDecode = 8192;
 // Stream partition of a plan's decode requests (see attend.hip): at most
 // kMaxStreamUnits (range, kv head) units, ranges of at least kMinRangeKeys
 // keys.
 constexpr int kMaxStreamUnits = 2048;
 constexpr int kMinRangeKeys = 512;
+// 8-bit pools: twice the units (kUnitsPerCu8 per CU), ranges of at least
+// 384 keys (a request then still has at most ceil(L / 384) + 1 pieces)
+constexpr int kUnitsPerCu8 = 8;
+constexpr int kMinRangeKeys8 = 384;
 constexpr int kSplitPrefill = 2048;  // logical tokens per prefill split
 // A prefill request is split along its keys only if it has fewer than this
 // many (query tile x kv head) work units on its own.

@@ -192,9 +192,9 @@ def test_config_parity_fp8(k):
 
 @pytest.mark.parametrize("k", [2])
 def test_plain_plan_serves_8bit_pools(k):
-    # decode-only batches over 8-bit pools are planned with 384-key ranges;
-    # the bf16 plan (here a stream plan) is valid too: both within the
-    # tolerance of the oracle on the same codes, every output row
+    # the 8-bit plan (here a stream plan of 8 units per CU) and the bf16
+    # plan (4 per CU) cut the batch differently; both serve 8-bit pools,
+    # within the tolerance of the oracle on the same codes, every output row
     w = configs.workload(k)
     scales = configs.FP8_SCALES
     kc, vc = gpu_pool8(w, *scales)

@@ -147,16 +147,16 @@ def test_binding_rejects_metadata_of_other_types():
 
 # ---- the plan's work list, read back ------------------------------------------------
 
-def expected_long_split(L, Q, Hq, Hkv):
+def expected_long_split(L, Q, Hq, Hkv, per_cu=4):
     """Key range of the splits of decode requests of more than 8192 keys: the
     shortest of 1024, 2048, 4096 whose units (requests' ranges x kv heads)
-    number at most 4 per CU, else 8192."""
+    number at most per_cu per CU (4; 8-bit plans 8), else 8192."""
     G = Hq // Hkv
     own = np.asarray(L, np.int64)[(np.asarray(L) > 8192) & (np.asarray(Q) >= 1) &
                                   (np.asarray(Q) <= 16 // G)]
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     for s in (1024, 2048, 4096):
-        if int(((own + s - 1) // s).sum()) * Hkv <= 4 * cus:
+        if int(((own + s - 1) // s).sum()) * Hkv <= per_cu * cus:
             return s
     return 8192
 
@@ -260,12 +260,12 @@ def test_plan_items_partition_every_request(B, fp8):
     Q = np.minimum(L, rng.integers(1, 3, size=B))
     w = W.make_workload("plan-%d" % B, L, Q, 16, 2, 64, seed=41)
     ranges, nranges = read_plan(w, fp8)
-    # 700 requests, bf16 plan: one sweep, a stream plan; 8-bit plans and
-    # 1500 requests (two sweeps): splits of each request's own
-    assert (nranges > 0) == (B <= 1024 and not fp8)
+    # 700 requests: one sweep, a stream plan (bf16: 4 units per CU, 8-bit:
+    # 8); 1500 (two sweeps): splits of each request's own
+    assert (nranges > 0) == (B <= 1024)
     if nranges:
         return
-    long_split = expected_long_split(L, Q, w.num_q_heads, w.num_kv_heads)
+    long_split = expected_long_split(L, Q, w.num_q_heads, w.num_kv_heads, 8 if fp8 else 4)
     for b in range(B):
         span = long_split if L[b] > 8192 else (384 if fp8 else 512)
         assert np.all(ranges[b][:-1] == span), b
