@@ -296,3 +296,35 @@ def test_long_requests_stream_or_split(B, Lr, seed):
     ref = oracle.attend(w.q, kc, vc, w.block_tables, w.seq_lens, w.query_start_loc,
                         w.num_kv_heads, w.scale)
     check_close(out, ref, "long requests, %d stream ranges" % nranges)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("Hq,Hkv,D,seed", [(32, 8, 128, 21), (16, 4, 64, 22)])
+def test_stream_plan_multi_token_decodes(fp8, Hq, Hkv, D, seed):
+    # a stream plan over decodes of 1 to 16/G query tokens (speculative
+    # decoding) with lengths from a few blocks to a few thousand keys, so that
+    # range boundaries fall inside requests, between them and inside a
+    # request's last partial pair; and requests shorter than a range, several
+    # in one range.  The read-back checks the range table; every output row
+    # against the oracle (8-bit: on the same codes)
+    rng = np.random.default_rng(seed)
+    B = 220
+    L = rng.integers(20, 3000, size=B)
+    L[::7] = rng.integers(20, 80, size=len(L[::7]))
+    Q = np.minimum(L, rng.integers(1, 16 // (Hq // Hkv) + 1, size=B))
+    w = W.make_workload("stream-q", L, Q, Hq, Hkv, D, seed=seed)
+    _, nranges = read_plan(w, fp8)
+    assert nranges > 0
+    if not fp8:
+        out = tensor_bits(Uploaded(w).attend())
+        kc, vc = oracle_pool(w)
+        ref = oracle.attend(w.q, kc, vc, w.block_tables, w.seq_lens, w.query_start_loc,
+                            w.num_kv_heads, w.scale)
+    else:
+        scales = (0.011, 0.0107)
+        kc8, vc8 = gpu_pool8(w, *scales)
+        out = attend8(w, kc8, vc8, *scales)
+        okc, ovc = oracle_pool8(w, *scales)
+        ref = oracle.attend_fp8(w.q, okc, ovc, scales[0], scales[1], w.block_tables,
+                                w.seq_lens, w.query_start_loc, w.num_kv_heads, w.scale)
+    check_close(out, ref, "stream plan, multi-token decodes%s" % (" (8-bit)" if fp8 else ""))
