@@ -543,9 +543,26 @@ def block_copy_run(W):
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / n
     moved = 4096 * 2 * 2 * w.num_kv_heads * 16 * w.head_dim * 2
+    # the same bytes as one contiguous device-to-device copy (torch's copy
+    # kernel, timed the same way): what read-plus-write traffic reaches on
+    # this device, the bound of any copy
+    src = torch.empty(moved // 4, dtype=torch.int16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    a.record()
+    for _ in range(n):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms_c = a.elapsed_time(b) / n
+    gbs, gbs_c = moved / (ms * 1e-3) / 1e9, moved / (ms_c * 1e-3) / 1e9
     return {"pairs": 4096, "block_bytes_per_pool": w.num_kv_heads * 16 * w.head_dim * 2,
-            "ms": round(ms, 5), "gbs": round(moved / (ms * 1e-3) / 1e9, 1),
-            "hbm_peak_frac": round(moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            "ms": round(ms, 5), "gbs": round(gbs, 1),
+            "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "contiguous_copy": {"ms": round(ms_c, 5), "gbs": round(gbs_c, 1),
+                                "hbm_peak_frac": round(gbs_c / HBM_PEAK_GBS, 4)},
+            "frac_of_contiguous_copy": round(gbs / gbs_c, 4)}
 
 
 def mla_case(name, L, Hq, seed):

@@ -151,16 +151,22 @@ __device__ __forceinline__ int4 scan_lanes(const SeqCounts& c, bool stream = fal
 }
 
 // Stream plans.  The decode requests' own keys, in request order and in
-// pairs of 32, form one stream of T pairs cut into R ranges of equal length
-// (+-1 pair); each (range, kv head) is one unit of work, and a request's
-// piece in each range it meets is one work item.  Every wave then streams
-// the same number of keys, one long pass, whatever the mix of lengths.  A
-// plan is a stream plan when it has no shared prefix, max_seq_len is above
-// kOneRangeKeys and the batch fills long_units units with ranges of at
-// least min_range_pairs pairs (512 keys; 8-bit plans 384); otherwise each
-// request is cut into splits of its own (seq_counts) and every split is a
-// unit.
+// pairs of 32, form one stream cut into R ranges of equal length (+-1 pair);
+// each (range, kv head) is one unit of work, and a request's piece in each
+// range it meets is one work item.  In the stream every request is preceded
+// by kStartPairs pairs that hold no keys: a request starting inside a range
+// costs its wave a switch of items (the block pipeline drains and fills
+// again), so a range with more request starts gets fewer keys, and every
+// wave's unit takes about the same time whatever the mix of lengths
+// (measured on the 8B-shaped decode layer, bf16 and 8-bit: 2 pairs best of
+// 0 to 4, about 1 us faster than none).  (A range is longer than kStartPairs, so
+// each range still holds at least one item.)  A plan is a stream plan when
+// it has no shared prefix, max_seq_len is above kOneRangeKeys and the batch
+// fills long_units units with ranges of at least min_range_pairs pairs (512
+// keys; 8-bit plans 384); otherwise each request is cut into splits of its
+// own (seq_counts) and every split is a unit.
 // Range r holds q + 1 pairs if r < rem, else q (T = R q + rem).
+constexpr int kStartPairs = 2;
 struct Stream {
   int T, R, q, rem;  // R = 0: not a stream plan
 };
@@ -176,19 +182,22 @@ __device__ __forceinline__ Stream stream_of(const AttendParams& P, int T) {
   // (the pair counts are summed in 32 bits: batches whose bound could pass
   // 2^31 pairs are not streamed)
   const bool ok = P.prefix_len == 0 && P.max_seq_len > kOneRangeKeys &&
-                  (int64_t)P.max_seq_len * P.num_seqs < ((int64_t)1 << 36) && want >= 1 &&
+                  (int64_t)(P.max_seq_len + 64) * P.num_seqs < ((int64_t)1 << 36) &&
+                  want >= 1 &&
                   (int64_t)T >= (int64_t)want * P.min_range_pairs;
   return ok ? Stream{T, want, T / want, T % want} : Stream{T, 0, 0, 0};
 }
 // Own 32-key pairs of a decode request (0 for others).
+// A request's length in the stream: kStartPairs, then its key pairs (its
+// keys start at stream position gp + kStartPairs).
 __device__ __forceinline__ int stream_pairs(const AttendParams& P, int b, const SeqCounts& c) {
-  return c.kind == kKindDecode ? (P.seq_lens[b] - P.prefix_len + 31) >> 5 : 0;
+  return c.kind == kKindDecode ? ((P.seq_lens[b] - P.prefix_len + 31) >> 5) + kStartPairs : 0;
 }
 // A decode request's counts in a stream plan (its pairs [gp, gp + np)).
 // (with a shared prefix every decode tile merges, as in seq_counts)
 __device__ __forceinline__ void stream_counts(const AttendParams& P, const Stream& st, int gp,
                                               int np, SeqCounts& c) {
-  const int ns = range_of(st, gp + np - 1) - range_of(st, gp) + 1;
+  const int ns = range_of(st, gp + np - 1) - range_of(st, gp + kStartPairs) + 1;
   const bool part = P.prefix_len > 0 || ns > 1;
   c.items = ns;
   c.partials = part ? c.tq * ns : 0;
@@ -408,9 +417,10 @@ __device__ void emit_seq(const AttendParams& P, int b, const SeqCounts& c,
   }
 }
 
-// The items of decode request b in a stream plan (pairs [gp, gp + np)), one
-// per range it meets, in key order; the first item of every range that
-// starts inside the request goes into the range table.
+// The items of decode request b in a stream plan (stream positions [gp, gp +
+// np): kStartPairs, then its key pairs), one per range its key pairs meet,
+// in key order; the first item of every range that starts inside the
+// request's positions goes into the range table.
 // Pieces first, first + step, ... of the request (several threads can share
 // a request of many pieces).
 __device__ void emit_pieces(const AttendParams& P, int b, int Q, int ns, const Stream& st,
@@ -418,13 +428,14 @@ __device__ void emit_pieces(const AttendParams& P, int b, int Q, int ns, const S
                             int step = 1) {
   const int q0 = P.qsl[b], L = P.seq_lens[b];
   const int C = P.prefix_len;  // first key of the request's own items
-  const int r0 = range_of(st, gp);
+  const int g1 = gp + kStartPairs;  // stream position of the first key pair
+  const int r0 = range_of(st, g1);
   const bool part = C > 0 || ns > 1;
   for (int s = first; s < ns; s += step) {
     const int rs = range_start(st, r0 + s), re = range_start(st, r0 + s + 1);
-    const int a = max(gp, rs), e = min(gp + np, re);
-    put_item(P.items, ibase + s, b, q0, Q, kKindDecode, C + 32 * (a - gp),
-             min(L, C + 32 * (e - gp)), s, ns, part ? pbase : -1, part ? cbase : -1, L - Q);
+    const int a = max(g1, rs), e = min(gp + np, re);
+    put_item(P.items, ibase + s, b, q0, Q, kKindDecode, C + 32 * (a - g1),
+             min(L, C + 32 * (e - g1)), s, ns, part ? pbase : -1, part ? cbase : -1, L - Q);
     if (rs >= gp) P.ranges[r0 + s] = ibase + s;
   }
   if (part && first == 0) P.merge_list[cbase] = make_int4(q0, Q, ns, pbase);

@@ -192,6 +192,9 @@ def stream_table_offset(B, T, Hq, Hkv, D, max_q, max_l):
 # from byte 4096, then the work items (16 int32 each: seq, tok0, ntok, kind, kv0,
 # kv1, split, nsplit, pbase, counter, posbase, pad) from byte 4096 + 32 KiB.
 ITEMS_OFFSET = 4096 + 8 * 4096
+# Stream positions (of 32 keys each) that stand for a request's start in a
+# stream plan: the cost of a wave's switch to the request's first item.
+START_PAIRS = 2
 
 
 def read_plan(w, fp8):
@@ -199,8 +202,9 @@ def read_plan(w, fp8):
     check that every slot in [0, num_items) holds exactly one valid decode item
     and that each request's items cover its keys 0 .. L-1 once, in split
     order.  For a stream plan (header word 9: the number of stream ranges R),
-    also check the range table: R equal runs of the decode stream (the
-    requests' 32-key pairs in request order), each a run of consecutive items.
+    also check the range table: R equal runs of the decode stream (per
+    request in request order, START_PAIRS pairs for its start, then its
+    32-key pairs), each a run of consecutive items.
     Returns, per request, the lengths of its key ranges, and R."""
     B, L, Q = w.num_seqs, w.seq_lens, w.query_lens
     bt, sl, qsl = i32(w.block_tables), i32(w.seq_lens), i32(w.query_start_loc)
@@ -240,11 +244,21 @@ def read_plan(w, fp8):
         assert np.array_equal(order, np.arange(num_items))
         table = raw[RANGES_OFFSET(w):RANGES_OFFSET(w) + 4 * (nranges + 1)].view(np.int32)
         assert table[0] == 0 and table[-1] == num_items and np.all(np.diff(table) >= 1)
+        # The stream: every request is START_PAIRS pairs with no keys (its
+        # start) followed by its key pairs; range r is positions [s_r,
+        # s_(r+1)) of a cut into equal lengths +-1.  A range's length is the
+        # key pairs of its items plus the start positions that fall in it.
         pairs = (kv1 - kv0 + 31) // 32
         per_range = np.add.reduceat(pairs, table[:-1])
-        total = int(((L + 31) // 32).sum())
-        assert per_range.sum() == total
-        assert per_range.min() >= total // nranges and per_range.max() <= -(-total // nranges)
+        span = (L + 31) // 32 + START_PAIRS
+        total = int(span.sum())
+        q, rem = divmod(total, nranges)
+        bounds = np.arange(nranges + 1) * q + np.minimum(np.arange(nranges + 1), rem)
+        starts = np.concatenate([[0], np.cumsum(span)[:-1]])
+        for k in range(START_PAIRS):
+            per_range = per_range + np.bincount(
+                np.searchsorted(bounds, starts + k, side="right") - 1, minlength=nranges)
+        assert np.array_equal(per_range, np.diff(bounds))
     return ranges, nranges
 
 
@@ -286,7 +300,7 @@ def test_long_requests_stream_or_split(B, Lr, seed):
     ranges, nranges = read_plan(w, False)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     want = min(4 * cus, 2048) // 8
-    assert (nranges > 0) == (int(((L + 31) // 32).sum()) >= want * 16)
+    assert (nranges > 0) == (int(((L + 31) // 32 + START_PAIRS).sum()) >= want * 16)
     if nranges == 0:
         span = expected_long_split(L, Q, 8, 8)
         for b in range(B):
