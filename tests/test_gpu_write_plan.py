@@ -313,6 +313,34 @@ def test_long_requests_stream_or_split(B, Lr, seed):
 
 
 @pytest.mark.parametrize("fp8", [False, True])
+def test_stream_plan_requests_of_many_pieces(fp8):
+    # a stream plan whose requests meet more than 32 ranges each (the plan's
+    # wave emits such a request's pieces, 64 at a time), beside short ones
+    # emitted one lane each: 3 requests of about 60000 keys (bf16: ~44
+    # pieces, one pass; 8-bit: ~87, two) and 5 of a few hundred; every
+    # output row against the oracle
+    rng = np.random.default_rng(23)
+    L = np.array([60000, 300, 58000, 77, 61111, 500, 900, 33], np.int64)
+    Q = np.minimum(L, rng.integers(1, 3, size=len(L)))
+    w = W.make_workload("many-pieces", L, Q, 16, 8, 64, seed=23)
+    ranges, nranges = read_plan(w, fp8)
+    assert nranges > 0 and max(len(r) for r in ranges) > (64 if fp8 else 32)
+    if not fp8:
+        out = tensor_bits(Uploaded(w).attend())
+        kc, vc = oracle_pool(w)
+        ref = oracle.attend(w.q, kc, vc, w.block_tables, w.seq_lens, w.query_start_loc,
+                            w.num_kv_heads, w.scale)
+    else:
+        scales = (0.011, 0.0107)
+        kc8, vc8 = gpu_pool8(w, *scales)
+        out = attend8(w, kc8, vc8, *scales)
+        okc, ovc = oracle_pool8(w, *scales)
+        ref = oracle.attend_fp8(w.q, okc, ovc, scales[0], scales[1], w.block_tables,
+                                w.seq_lens, w.query_start_loc, w.num_kv_heads, w.scale)
+    check_close(out, ref, "stream plan, requests of many pieces%s" % (" (8-bit)" if fp8 else ""))
+
+
+@pytest.mark.parametrize("fp8", [False, True])
 @pytest.mark.parametrize("Hq,Hkv,D,seed", [(32, 8, 128, 21), (16, 4, 64, 22)])
 def test_stream_plan_multi_token_decodes(fp8, Hq, Hkv, D, seed):
     # a stream plan over decodes of 1 to 16/G query tokens (speculative
