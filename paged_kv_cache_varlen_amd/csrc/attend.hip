@@ -2118,19 +2118,25 @@ __device__ __forceinline__ void merge_fold(MergeState& st, float m, float l, f32
 // round-robin, 64 / (D/8) at a time (lanes cover (column, 8 dims)).  One
 // workgroup per (split tile, kv head, pass): its 4 waves fold consecutive
 // quarters of each column's partials (a shared prefix's first, then the
-// tile's own splits, in split order, 8 loads in flight per lane), and wave 0
-// folds the 4 wave states in wave order: a fixed order, so the result does
-// not depend on timing, and a long chain of splits is 4 chains of a quarter.
+// tile's own splits, in split order, two splits' loads in flight per lane),
+// and wave 0 folds the 4 wave states in wave order: a fixed order, so the
+// result does not depend on timing, and a long chain of splits is 4 chains
+// of a quarter.  Two splits per step keep the kernel at 64 registers, eight
+// waves per SIMD, so that a launch of up to 8 workgroups per CU is one
+// round (eight splits per step: 121 registers, four waves per SIMD; measured
+// 7.1 -> 5.1 us on 2040 (tile, kv head) units, 4.1 -> 3.8 us on the 8B
+// decode layer, 7.5 -> 8.3 us on one request of 128 splits).
 __host__ __device__ inline uint32_t merge_waves_per_head(int G, int D) {
   const int cpw = 64 / (D / 8);
   const int w = (G + cpw - 1) / cpw;
   return (uint32_t)(w < 1 ? 1 : (w > 4 ? 4 : w));
 }
 template <int D>
-__global__ __launch_bounds__(kAttendThreads) void merge_kernel(AttendParams P) {
+__global__ __launch_bounds__(kAttendThreads)
+__attribute__((amdgpu_waves_per_eu(8, 8))) void merge_kernel(AttendParams P) {
   constexpr int LPC = D / 8;      // lanes per column
   constexpr int CPW = 64 / LPC;   // columns per wave pass
-  constexpr int SB = 8;           // splits per step
+  constexpr int SB = 2;           // splits per step
   constexpr int NW = kAttendThreads / 64;
   __shared__ float4 wstate[NW - 1][3][64];  // waves 1..: (M, den), n0, n1 per lane
   const int lane = threadIdx.x & 63;
