@@ -2428,8 +2428,11 @@ hipError_t launch_merge(const AttendArgs& a, hipStream_t stream) {
   if (!a.cascade && a.max_seq_len <= kOneRangeKeys) return hipSuccess;
   const AttendParams P = make_params(a);
   // one workgroup per (split tile, kv head, pass), at most 8 per CU (the
-  // workgroups stride over the units)
-  int64_t mwgs = a.ws.max_items * a.num_kv_heads *
+  // workgroups stride over the units); a split tile holds at least one query
+  // token of its own, so there are at most num_q_tokens of them
+  const int64_t max_tiles =
+      a.ws.max_items < a.num_q_tokens ? a.ws.max_items : a.num_q_tokens;
+  int64_t mwgs = max_tiles * a.num_kv_heads *
                  merge_waves_per_head(a.num_q_heads / a.num_kv_heads, a.head_dim);
   const int64_t cap = (int64_t)a.num_cus * 8;
   if (mwgs > cap) mwgs = cap;
