@@ -177,14 +177,16 @@ __device__ __forceinline__ int range_of(const Stream& st, int x) {  // x in [0, 
   const int big = st.rem * (st.q + 1);
   return x < big ? x / (st.q + 1) : st.rem + (x - big) / st.q;
 }
-__device__ __forceinline__ Stream stream_of(const AttendParams& P, int T) {
+// T: stream positions (start positions included), n_req: decode requests
+// with keys; whether to stream is decided on the key pairs alone.
+__device__ __forceinline__ Stream stream_of(const AttendParams& P, int T, int n_req) {
   const int want = min(P.long_units, kMaxStreamUnits) / P.Hkv;
   // (the pair counts are summed in 32 bits: batches whose bound could pass
   // 2^31 pairs are not streamed)
   const bool ok = P.prefix_len == 0 && P.max_seq_len > kOneRangeKeys &&
                   (int64_t)(P.max_seq_len + 64) * P.num_seqs < ((int64_t)1 << 36) &&
                   want >= 1 &&
-                  (int64_t)T >= (int64_t)want * P.min_range_pairs;
+                  (int64_t)T - (int64_t)kStartPairs * n_req >= (int64_t)want * P.min_range_pairs;
   return ok ? Stream{T, want, T / want, T % want} : Stream{T, 0, 0, 0};
 }
 // Own 32-key pairs of a decode request (0 for others).
@@ -573,7 +575,8 @@ __device__ void plan_wave(const AttendParams& P, int* cnt) {
   // stream partition of the decode requests
   const int np = stream_pairs(P, lane, c);
   const int npi = wave_incl_scan4(make_int4(np, 0, 0, 0)).x;
-  const Stream st = stream_of(P, __shfl(npi, 63));
+  const Stream st =
+      stream_of(P, __shfl(npi, 63), __popcll(__ballot(lane < P.num_seqs && np > 0)));
   const int gp = npi - np;
   if (st.R > 0 && c.kind == kKindDecode) stream_counts(P, st, gp, np, c);
   const int4 x = scan_lanes(c, st.R > 0);
@@ -673,8 +676,8 @@ __device__ void plan_body(const AttendParams& P) {
     // stream partition of the decode requests
     np = stream_pairs(P, b, c);
     int4 tp;
-    gp = block_scan4(make_int4(np, 0, 0, 0), lds, &tp).x;
-    st = stream_of(P, tp.x);
+    gp = block_scan4(make_int4(np, np > 0 ? 1 : 0, 0, 0), lds, &tp).x;
+    st = stream_of(P, tp.x, tp.y);
     if (st.R > 0 && c.kind == kKindDecode) stream_counts(P, st, gp, np, c);
     // The decode requests' last splits (1 .. split keys each) go last in the
     // queue, longest first (16 buckets of 64 keys, any order within one), so

@@ -300,7 +300,8 @@ def test_long_requests_stream_or_split(B, Lr, seed):
     ranges, nranges = read_plan(w, False)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     want = min(4 * cus, 2048) // 8
-    assert (nranges > 0) == (int(((L + 31) // 32 + START_PAIRS).sum()) >= want * 16)
+    # (streamed when the key pairs alone fill the units' minimum ranges)
+    assert (nranges > 0) == (int(((L + 31) // 32).sum()) >= want * 16)
     if nranges == 0:
         span = expected_long_split(L, Q, 8, 8)
         for b in range(B):
