@@ -313,6 +313,28 @@ def test_long_requests_stream_or_split(B, Lr, seed):
     check_close(out, ref, "long requests, %d stream ranges" % nranges)
 
 
+def test_stream_decision_counts_keys_only():
+    # 900 one-key decodes beside one of 1000 keys: with their start positions
+    # the stream would fill the units' minimum ranges, with their keys alone
+    # it does not, and the keys decide: no stream ranges (per-request
+    # splits); every output row against the oracle
+    L = np.ones(901, np.int64)
+    L[450] = 1000
+    Q = np.ones(901, np.int64)
+    w = W.make_workload("keys-only", L, Q, 8, 8, 64, seed=24)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    want = min(4 * cus, 2048) // 8
+    pairs = (L + 31) // 32
+    assert pairs.sum() < want * 16 <= (pairs + START_PAIRS).sum()
+    _, nranges = read_plan(w, False)
+    assert nranges == 0
+    out = tensor_bits(Uploaded(w).attend())
+    kc, vc = oracle_pool(w)
+    ref = oracle.attend(w.q, kc, vc, w.block_tables, w.seq_lens, w.query_start_loc,
+                        w.num_kv_heads, w.scale)
+    check_close(out, ref, "one-key decodes beside a long one")
+
+
 @pytest.mark.parametrize("fp8", [False, True])
 def test_stream_plan_requests_of_many_pieces(fp8):
     # a stream plan whose requests meet more than 32 ranges each (the plan's
